@@ -1,0 +1,17 @@
+"""fp64 CPU oracle for the selected-token logprob and the three-way comparison.
+
+TEST INFRASTRUCTURE ONLY. This package is the plain, slow definition that the
+GPU library is checked against. Only tests/, the smoke check in
+__graft_entry__.py and bench.py's CPU-baseline leg may import it; the library
+in rollout_logprob_consistency_amd/ never does, and the two share no code.
+
+Every function cites the passage of the source pages it writes out:
+  [AMD]  "Debugging Logprob Mismatches in LLM Reinforcement Learning"
+  [vLLM] "Fault localization and mismatch bisect" (train-inference-consistency
+         guide)
+  [TII]  "Rollout-Training Mismatch in LLM RL"
+  [VeX]  "Diagnosing Training Inference Mismatch in LLM Reinforcement Learning"
+"""
+
+from .score import bf16_bits_to_f64, score, logits  # noqa: F401
+from .compare import compare, per_token, PAIRS, STAT_FIELDS  # noqa: F401

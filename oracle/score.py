@@ -1,0 +1,83 @@
+"""Selected-token logprob: the plain fp64 definition.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py). Not used by the library.
+
+What is computed, per scored row t (rows are independent):
+
+  [AMD] §"What a Logprob Difference Means": the stored score of token x_t is
+        the natural log of its probability given the prefix, in nats.
+  [AMD] §"Case 2: A and B Stay Close; C Changes": that logprob is the target
+        token's logit minus the log of the sum over the whole vocabulary of the
+        exponentials of the logits, the sum taken as a stable log-sum-exp.
+  [AMD] §"How this differs from a real temperature mismatch": temperature
+        divides every logit before the normaliser is formed; dividing a
+        finished logprob by T is a different (wrong) quantity.
+  [AMD] §"Collect A/B and C": the logits are the LM-head product of the final
+        hidden state; the log-softmax is taken in higher precision than the
+        model's; one global normaliser spans the whole vocabulary.
+  "Training and rollout stop disagreeing ..." (vime / RL-Kernel summary): the
+        normaliser covers the true vocabulary range only, so padded LM-head
+        rows past it take no part.
+
+Precision: the bf16 input bits are widened exactly to fp64; every later
+operation is one fp64 operation. The logit row is an fp64 matrix product
+(library matmul; its rounding, at most about H * 2^-53 relative, is far below
+any tolerance used against it). For memory, the product is formed in blocks of
+vocabulary rows; each logit is still one full dot product over h.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp64, exactly (bf16 is the top half of an fp32)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def logits(x_bits: np.ndarray, w_bits: np.ndarray, v_true: int | None = None,
+           block: int = 8192) -> np.ndarray:
+    """z[t, v] = sum_h x[t, h] * w[v, h] in fp64, for v < v_true."""
+    x = bf16_bits_to_f64(x_bits)
+    V = w_bits.shape[0] if v_true is None else int(v_true)
+    if x.ndim != 2 or w_bits.ndim != 2 or x.shape[1] != w_bits.shape[1]:
+        raise ValueError("expected x [T, H] and w [V, H] with the same H")
+    if not 1 <= V <= w_bits.shape[0]:
+        raise ValueError("v_true must lie in [1, V]")
+    z = np.empty((x.shape[0], V), dtype=np.float64)
+    for v0 in range(0, V, block):
+        v1 = min(V, v0 + block)
+        z[:, v0:v1] = x @ bf16_bits_to_f64(w_bits[v0:v1]).T
+    return z
+
+
+def log_softmax_at(z: np.ndarray, ids: np.ndarray, temperature: float = 1.0):
+    """Return (logprob[t], lse[t]) for logit rows z [T, V], fp64.
+
+    s = z / T;  lse = M + ln sum_v exp(s_v - M) with M = max_v s_v;
+    logprob = s[ids[t]] - lse.
+    """
+    temperature = float(temperature)
+    if not (np.isfinite(temperature) and temperature > 0.0):
+        raise ValueError("temperature must be finite and > 0")
+    ids = np.asarray(ids, dtype=np.int64)
+    if ids.shape != (z.shape[0],):
+        raise ValueError("one target id per row")
+    if ids.size and (ids.min() < 0 or ids.max() >= z.shape[1]):
+        raise ValueError("target id outside the true vocabulary range")
+    s = z / temperature
+    M = s.max(axis=1)
+    S = np.exp(s - M[:, None]).sum(axis=1)
+    lse = M + np.log(S)
+    lp = s[np.arange(z.shape[0]), ids] - lse
+    return lp, lse
+
+
+def score(x_bits: np.ndarray, w_bits: np.ndarray, ids: np.ndarray,
+          temperature: float = 1.0, v_true: int | None = None):
+    """Selected-token logprob of every row: (logprob fp64 [T], lse fp64 [T])."""
+    if x_bits.shape[0] == 0:
+        return np.zeros(0), np.zeros(0)
+    return log_softmax_at(logits(x_bits, w_bits, v_true), ids, temperature)
