@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark: one step = the whole hot path on one batch of synthetic input.
+
+Step = lp_score on the Qwen3-8B-shaped scoring batch (T = 8192 rows =
+16 sequences x 512 response tokens, H = 4096, V = 151 936, bf16 inputs, fp32
+accumulation, temperature 1.0) followed by lp_compare of generation (A),
+the replay scores just produced (B) and trainer scores (C) over those
+16 x 512 tokens. Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "scored tokens/s + % bf16 MFMA peak, H=4096 V=151936; batch-invariance bit-exact"
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_qwen8b_traffic.json")
+SCORE_SRC = os.path.join(ROOT, "rollout_logprob_consistency_amd", "csrc", "score.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def score_source_hash() -> str:
+    return hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()
+
+
+def measured_traffic():
+    """Per-launch HBM bytes from the committed rocprofv3 counter summary, or
+    None if there is none or the kernel source changed since it was taken."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("score_hip_sha256") != score_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        return int(max(n)) if n else 1
+    except Exception:
+        return 1
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-rows", type=int, default=512,
+                    help="rows of the batch the fp64 oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-n", type=int, default=4096,
+                    help="sequences in the comparison bandwidth probe (L = 2304)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the scoring path has no cross-GPU "
+              "exchange and this build runs on a single MI355X (use --gpus 1).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import rollout_logprob_consistency_amd as lp
+    from workloads import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T, H, V, NSEQ, LSEQ = 8192, 4096, 151936, 16, 512
+
+    t0 = time.time()
+    log("bench: generating Qwen3-8B-shaped inputs (seeded, host) ...")
+    w_bits = synth.qwen_weight(H, V)
+    case = synth.qwen_case(T=T, H=H, V=V, w_bits=w_bits)
+    log(f"bench: inputs ready in {time.time() - t0:.1f} s; uploading")
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, w = bf16(case.x_bits), bf16(w_bits)
+    ids = torch.from_numpy(case.ids).to(dev)
+    out = torch.empty(T, dtype=torch.float32, device=dev)
+    ws = torch.empty(lp.score_workspace_bytes(T, H, V), dtype=torch.uint8, device=dev)
+
+    # Comparison inputs: trainer C = a replay of the same rows (bitwise equal
+    # when the scorer is deterministic), generation A = C + N(0, 1e-3).
+    lp.score(x, w, ids, out=out, workspace=ws, check=True)
+    torch.cuda.synchronize()
+    C = out.view(NSEQ, LSEQ).clone()
+    gen = torch.Generator(device=dev).manual_seed(synth.BASE_SEED)
+    A = (C.double() + 1e-3 * torch.randn(C.shape, generator=gen, device=dev,
+                                          dtype=torch.float64)).float()
+    mask = torch.ones((NSEQ, LSEQ), dtype=torch.uint8, device=dev)
+    B = out.view(NSEQ, LSEQ)
+    stats_buf = torch.empty(3 * NSEQ * lp.SEQ_STATS_DTYPE.itemsize, dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        lp.score(x, w, ids, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        lp.compare_raw(A, B, C, mask, out=stats_buf)
+        if ev is not None:
+            ev[2].record()
+
+    log(f"bench: warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    score_ms = [e[0].elapsed_time(e[1]) for e in events]
+    cmp_ms = [e[1].elapsed_time(e[2]) for e in events]
+    score_avg = float(np.mean(score_ms)) / 1e3
+    cmp_avg = float(np.mean(cmp_ms)) / 1e3
+
+    st = lp.stats_from_bytes(stats_buf, NSEQ)
+    assert (st["BC"]["mismatch"] == 0).all(), "replay differs from an identical earlier scoring"
+
+    flops = 2.0 * T * H * V
+    achieved = flops / score_avg / 1e12
+    log(f"bench: lp_score {score_avg * 1e3:.3f} ms avg (min {min(score_ms):.3f}, max "
+        f"{max(score_ms):.3f}) = {achieved:.1f} TFLOP/s = {100 * achieved / PEAK_BF16_TFLOPS:.1f}% "
+        f"of bf16 peak; lp_compare {cmp_avg * 1e6:.1f} us")
+
+    # Comparison bandwidth probe at a size that is not launch-latency bound.
+    sweep = None
+    if args.sweep_n > 0:
+        sc = synth.compare_sweep_case(N=args.sweep_n)
+        tA, tB, tC, tM = (torch.from_numpy(a).to(dev) for a in (sc.A, sc.B, sc.C, sc.mask))
+        sbuf = torch.empty(3 * sc.N * lp.SEQ_STATS_DTYPE.itemsize, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            lp.compare_raw(tA, tB, tC, tM, out=sbuf)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
+        for e in evs:
+            e[0].record()
+            lp.compare_raw(tA, tB, tC, tM, out=sbuf)
+            e[1].record()
+        torch.cuda.synchronize()
+        us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+        nbytes = 13.0 * sc.N * sc.L
+        sweep = {"N": sc.N, "L": sc.L, "us": round(us, 2),
+                 "GBps": round(nbytes / us / 1e3, 1), "bytes_per_token": 13}
+        log(f"bench: lp_compare N={sc.N} L={sc.L}: {us:.1f} us = {nbytes / us / 1e3:.1f} GB/s")
+        del tA, tB, tC, tM
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n = min(args.cpu_rows, T)
+        log(f"bench: timing the fp64 oracle on {n} rows ...")
+        tc = time.perf_counter()
+        oracle.score(case.x_bits[:n], w_bits, case.ids[:n], 1.0)
+        dt = time.perf_counter() - tc
+        cpu = {"value": round(n / dt, 3), "unit": "tokens/s", "cores": blas_threads(),
+               "kind": "oracle",
+               "sample": f"first {n} of the {T} rows (H={H}, V={V}), fp64 numpy/OpenBLAS, "
+                         f"{dt:.1f} s"}
+        log(f"bench: oracle {n / dt:.2f} tokens/s ({dt:.1f} s, {cpu['cores']} threads)")
+
+    traffic = measured_traffic()
+    rec = {
+        "metric": METRIC,
+        "value": round(T * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-8B-shaped selected-token logprob T=8192 (16x512) "
+                               "H=4096 V=151936 temperature 1.0, then three-way compare "
+                               "of the 16x512 scores",
+                   "T": T, "H": H, "V": V, "temperature": 1.0, "accumulate": "fp32",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "kernels": {"lp_score_ms": round(score_avg * 1e3, 4),
+                    "lp_compare_us": round(cmp_avg * 1e6, 2)},
+        "compare_sweep": sweep,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

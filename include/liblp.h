@@ -1,0 +1,170 @@
+/*
+ * liblp: deterministic, batch-invariant selected-token logprobs and the
+ * three-way logprob comparison, for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Every pointer argument is device memory owned by the caller unless
+ * stated otherwise; the library allocates nothing and keeps no global state,
+ * so calls on different streams may run concurrently. Calls enqueue work on
+ * `stream` and return at once; results are valid once the stream has reached
+ * them. Argument errors are returned synchronously before anything is
+ * enqueued. No C++ exception crosses this interface.
+ *
+ * Sources (page titles as published):
+ *   [AMD]  "Debugging Logprob Mismatches in LLM Reinforcement Learning"
+ *   [vLLM] "Fault localization and mismatch bisect" (train-inference-
+ *          consistency guide)
+ *   [TII]  "Rollout-Training Mismatch in LLM RL"
+ *   [RLK]  "Training and rollout stop disagreeing: vime and RL-Kernel hold
+ *          logprobs bitwise identical for 200 steps on AMD MI300X"
+ *   [VeX]  "Diagnosing Training Inference Mismatch in LLM Reinforcement
+ *          Learning"
+ */
+#ifndef LIBLP_H
+#define LIBLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LP_OK = 0,
+  LP_EINVAL = 1,       /* an argument is invalid; nothing was enqueued        */
+  LP_EUNSUPPORTED = 2, /* valid, but a shape/alignment this build does not
+                          handle; nothing was enqueued                        */
+  LP_EHIP = 3          /* a HIP runtime call or kernel launch failed          */
+} lp_status;
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char* lp_status_string(lp_status status);
+
+/* ------------------------------------------------------------------------
+ * Selected-token logprob
+ *
+ * For every row t independently ([AMD] "Case 2: A and B Stay Close; C
+ * Changes"; "How this differs from a real temperature mismatch"; "Collect
+ * A/B and C"; [RLK] true vocabulary range):
+ *
+ *   z[t, v]       = sum_h hidden[t, h] * w[v, h]        (bf16 x bf16, fp32 acc.)
+ *   s[t, v]       = z[t, v] / temperature               for v < V_true
+ *   lse[t]        = log sum_{v < V_true} exp(s[t, v])    (natural log)
+ *   logprob[t]    = s[t, target_ids[t]] - lse[t]         (nats, fp32)
+ *
+ * Rows are assumed already aligned with the tokens they predict (the
+ * prediction after position j scores token j + 1, [AMD] "Align Each Score
+ * With the Token It Predicts"); the binding's align() helper performs that
+ * shift. Full logits are never written to memory.
+ *
+ * Determinism and batch invariance: each row's outputs are a fixed function
+ * of that row's hidden vector, its target id, w, V_true and temperature. The
+ * tile shape, the K (hidden) reduction order and the vocabulary merge order
+ * are compile-time constants: they never depend on T, on the row's position
+ * in the batch, on the other rows, on the stream or on the device occupancy.
+ * There is no split-K and no floating-point atomic.
+ *
+ * Layout:
+ *   hidden_bf16  [T, H] bf16, row stride ldh elements (ldh >= H, ldh % 8 == 0),
+ *                16-byte aligned base.
+ *   w_bf16       [V_rows, H] bf16, contiguous (row stride H), 16-byte aligned:
+ *                the nn.Linear LM-head layout.
+ *   target_ids   [T] int64.
+ *   out_logprob  [T] fp32.
+ *   out_lse      [T] fp32, may be NULL.
+ *   bad_rows     one int32, may be NULL: the library ADDS the number of rows
+ *                whose target id lies outside [0, V_true); the caller sets
+ *                it to 0 beforehand. Such rows get logprob = NaN.
+ *   workspace    at least lp_score_workspace_bytes(T, H, V_rows, V_true)
+ *                bytes, 256-byte aligned; contents on entry are ignored.
+ *
+ * Errors: LP_EINVAL for T < 0, H < 1, V_rows < 1, V_true outside
+ * [1, V_rows], ldh < H, a temperature that is not finite and > 0, a NULL
+ * required pointer, or a workspace that is too small or misaligned.
+ * LP_EUNSUPPORTED for H % 64 != 0, ldh % 8 != 0 or misaligned hidden/w, and
+ * for sizes whose index arithmetic would overflow 32-bit tile counters.
+ * T == 0 is a no-op returning LP_OK.
+ * ------------------------------------------------------------------------ */
+size_t lp_score_workspace_bytes(int64_t T, int64_t H, int64_t V_rows,
+                                int64_t V_true);
+
+lp_status lp_score(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
+                   const int64_t* target_ids, int64_t T, int64_t H,
+                   int64_t V_rows, int64_t V_true, float temperature,
+                   float* out_logprob, float* out_lse, int32_t* bad_rows,
+                   void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Three-way comparison of generation (A), replay (B) and trainer (C) scores
+ *
+ * [AMD] "One Response, Three Scores", "Check Whether the Pattern Extends",
+ * Case 1's compare(); [vLLM] "Per-sequence observation patterns", "Metric
+ * measurement basis", "Compare per-token logprobs"; [TII] sec. 2.1 (TIS);
+ * [VeX] sec. 3 "How TIS takes effect" (token and sequence TIS).
+ *
+ * Pairs, in this order: p = 0: (A, B); p = 1: (B, C); p = 2: (A, C), written
+ * (left, right). Per pair and per sequence n, over the ACTIVE tokens
+ * (mask != 0) i_0 < i_1 < ... with active rank k:
+ *
+ *   valid        number of active tokens
+ *   mismatch     active tokens whose fp32 bit patterns differ (+0.0 and -0.0
+ *                differ, identical NaN bits do not). With atol >= 0, a token
+ *                whose bits differ counts as equal when |left - right| <= atol.
+ *   first_div    smallest active rank k that mismatches, -1 if none
+ *   longest_run  longest run of consecutive active tokens that mismatch;
+ *                inactive positions neither extend nor break a run
+ *   nonfinite    active tokens whose left or right score is not finite; these
+ *                take part in mismatch/first_div/longest_run only
+ *   k3_nonfinite tokens whose k3 term overflows; left out of sum_k3
+ *   delta_i      (double)left - (double)right; d_i = -delta_i
+ *   max_abs      max |delta_i| (0 if none)          -- exact
+ *   sum_abs      sum |delta_i|;  sum_signed = sum delta_i;  sum_d = sum d_i
+ *   sum_k3       sum (expm1(d_i) - d_i)             (Schulman k3, never clipped)
+ *   sum_tok_tis  sum min(exp(d_i), tis_clip)        (token TIS weights)
+ *   seq_tis      min(exp(sum_d), tis_clip)          (sequence TIS weight)
+ *
+ * Integer fields and max_abs are exact. The fp64 sums are taken in a fixed
+ * order, so they are bitwise reproducible run to run and independent of N.
+ *
+ * Layout:
+ *   gen_A, replay_B, train_C  [N, L] fp32, row stride ld elements (ld >= L).
+ *   mask                      [N, L] uint8, same row stride ld.
+ *   out                       [3][N] lp_seq_stats (pair-major), device memory.
+ *   per_token                 NULL, or [3 pairs][3][N][L] fp32 contiguous with
+ *                             values |delta|, k3, min(exp(d), tis_clip) for
+ *                             active finite tokens, 0 for inactive tokens and
+ *                             NaN for active non-finite ones.
+ *
+ * Errors: LP_EINVAL for N < 0, L < 0, ld < L, tis_clip not finite and > 0,
+ * atol NaN, or a NULL required pointer. N == 0 or L == 0 is a no-op (with
+ * L == 0 and N > 0 the stats are still written, all empty).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t valid;
+  int32_t mismatch;
+  int32_t first_div;
+  int32_t longest_run;
+  int32_t nonfinite;
+  int32_t k3_nonfinite;
+  double max_abs;
+  double sum_abs;
+  double sum_signed;
+  double sum_k3;
+  double sum_d;
+  double seq_tis;
+  double sum_tok_tis;
+} lp_seq_stats;
+
+lp_status lp_compare(const float* gen_A, const float* replay_B,
+                     const float* train_C, const uint8_t* mask, int64_t N,
+                     int64_t L, int64_t ld, float tis_clip, float atol,
+                     lp_seq_stats* out, float* per_token, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBLP_H */

@@ -1,0 +1,167 @@
+"""Deterministic, batch-invariant selected-token logprobs and the three-way
+logprob comparison on AMD Instinct MI355X.
+
+Thin binding over the C ABI in include/liblp.h (liblp.so, built in-tree by
+build.py). This module only checks and marshals arguments: it passes device
+pointers and the current HIP stream to the library, and every arithmetic
+step runs in the library's kernels. PyTorch supplies device memory and
+streams.
+
+    score(hidden, w, ids, temperature=1.0, v_true=None)   -> logprob [T] fp32
+    compare(A, B, C, mask, tis_clip=2.0, atol=None)       -> stats per pair
+    align(hidden, input_ids, response_mask)               -> rows, targets, mask
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from ._lib import (EXPORTS, LP_OK, SEQ_STATS_DTYPE, LpError, lib,  # noqa: F401
+                   status_string)
+
+PAIRS = ("AB", "BC", "AC")
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_cuda(name: str, t: torch.Tensor, dtype: torch.dtype):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def score_workspace_bytes(T: int, H: int, V_rows: int, V_true: int | None = None) -> int:
+    return int(lib().lp_score_workspace_bytes(T, H, V_rows, V_rows if V_true is None else V_true))
+
+
+def score(hidden: torch.Tensor, w: torch.Tensor, ids: torch.Tensor,
+          temperature: float = 1.0, v_true: int | None = None, *,
+          out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+          workspace: torch.Tensor | None = None, bad_rows: torch.Tensor | None = None,
+          check: bool = False) -> torch.Tensor:
+    """Selected-token logprob of every row of `hidden` (fp32, nats).
+
+    hidden [T, H] bf16 with unit column stride, w [V, H] bf16 contiguous,
+    ids [T] int64. Rows must already be aligned with their targets (align()).
+    With check=True the call synchronises and raises ValueError if any target
+    id lies outside [0, v_true).
+    """
+    _need_cuda("hidden", hidden, torch.bfloat16)
+    _need_cuda("w", w, torch.bfloat16)
+    _need_cuda("ids", ids, torch.int64)
+    if hidden.dim() != 2 or w.dim() != 2 or ids.dim() != 1:
+        raise ValueError("expected hidden [T, H], w [V, H], ids [T]")
+    if hidden.stride(1) != 1 or not w.is_contiguous() or not ids.is_contiguous():
+        raise ValueError("hidden needs unit column stride; w and ids must be contiguous")
+    T, H = hidden.shape
+    V = w.shape[0]
+    if w.shape[1] != H or ids.shape[0] != T:
+        raise ValueError("shape mismatch between hidden, w and ids")
+    vt = V if v_true is None else int(v_true)
+    dev = hidden.device
+    if out is None:
+        out = torch.empty(T, dtype=torch.float32, device=dev)
+    need = score_workspace_bytes(T, H, V, vt)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if check and bad_rows is None:
+        bad_rows = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = lib().lp_score(_ptr(hidden), hidden.stride(0) if T else H, _ptr(w), _ptr(ids),
+                        T, H, V, vt, float(temperature), _ptr(out), _ptr(lse),
+                        _ptr(bad_rows), _ptr(workspace),
+                        workspace.numel() * workspace.element_size(), _stream(dev))
+    if st != LP_OK:
+        raise LpError(st, "lp_score")
+    if check and int(bad_rows.item()) != 0:
+        raise ValueError(f"{int(bad_rows.item())} row(s) have a target id outside [0, {vt})")
+    return out
+
+
+def compare_raw(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch.Tensor,
+                tis_clip: float = 2.0, atol: float | None = None,
+                per_token: bool = False, out: torch.Tensor | None = None):
+    """Enqueue lp_compare; returns (stats bytes [3*N*80] uint8 device tensor,
+    per-token tensor [3, 3, N, L] fp32 or None). Does not synchronise."""
+    for name, t in (("A", A), ("B", B), ("C", C)):
+        _need_cuda(name, t, torch.float32)
+    _need_cuda("mask", mask, torch.uint8)
+    if not (A.shape == B.shape == C.shape == mask.shape) or A.dim() != 2:
+        raise ValueError("A, B, C and mask must share one [N, L] shape")
+    N, L = A.shape
+    ld = A.stride(0) if N else L
+    for t in (A, B, C, mask):
+        if t.stride(1) != 1 or (N > 1 and t.stride(0) != ld):
+            raise ValueError("A, B, C and mask need unit column stride and one row stride")
+    dev = A.device
+    nbytes = 3 * N * SEQ_STATS_DTYPE.itemsize
+    if out is None:
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    pt = torch.empty((3, 3, N, L), dtype=torch.float32, device=dev) if per_token else None
+    st = lib().lp_compare(_ptr(A), _ptr(B), _ptr(C), _ptr(mask), N, L, max(ld, L),
+                          float(tis_clip), -1.0 if atol is None else float(atol),
+                          _ptr(out), _ptr(pt), _stream(dev))
+    if st != LP_OK:
+        raise LpError(st, "lp_compare")
+    return out, pt
+
+
+def stats_from_bytes(raw: torch.Tensor, N: int) -> dict:
+    """Device stats bytes -> {"AB"|"BC"|"AC": numpy structured array [N]}."""
+    host = raw[: 3 * N * SEQ_STATS_DTYPE.itemsize].cpu().numpy()
+    rec = host.view(SEQ_STATS_DTYPE).reshape(3, N) if N else np.zeros((3, 0), SEQ_STATS_DTYPE)
+    return {p: rec[i] for i, p in enumerate(PAIRS)}
+
+
+def compare(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch.Tensor,
+            tis_clip: float = 2.0, atol: float | None = None, per_token: bool = False,
+            check: bool = True):
+    """Three-way comparison; synchronises and returns per-pair statistics.
+
+    Like the AMD blog's compare(), with check=True it raises ValueError when a
+    sequence has no active token or an active score is non-finite.
+    """
+    raw, pt = compare_raw(A, B, C, mask, tis_clip, atol, per_token)
+    stats = stats_from_bytes(raw, A.shape[0])
+    if check:
+        s = stats["AB"]
+        if np.any(s["valid"] == 0):
+            raise ValueError("a sequence has no active token")
+        for p in PAIRS:
+            if np.any(stats[p]["nonfinite"] > 0):
+                raise ValueError(f"non-finite score on an active token ({p})")
+    return (stats, pt) if per_token else stats
+
+
+def align(hidden: torch.Tensor, input_ids: torch.Tensor, response_mask: torch.Tensor):
+    """Pair every prediction row with the token it predicts.
+
+    The output after position j scores token j + 1, so the first response
+    token is scored by the last prompt position and the mask moves with its
+    target (AMD blog, "Align Each Score With the Token It Predicts").
+    hidden [B, S, H], input_ids [B, S], response_mask [B, S] (0/1) ->
+    rows [B*S, H] (a view), targets [B*S] int64, mask [B*S] uint8, where
+    position j of each sequence targets input_ids[:, j + 1] and the last
+    position has target 0 with mask 0. Every position is scored; apply the
+    mask afterwards to A, B and C alike.
+    """
+    if hidden.dim() != 3 or input_ids.shape != hidden.shape[:2] or \
+            response_mask.shape != input_ids.shape:
+        raise ValueError("expected hidden [B, S, H], input_ids and response_mask [B, S]")
+    if bool((response_mask[:, 0] != 0).any()):
+        raise ValueError("no preceding prediction row for input position zero")
+    B, S, H = hidden.shape
+    targets = torch.zeros_like(input_ids, dtype=torch.int64)
+    targets[:, :-1] = input_ids[:, 1:]
+    mask = torch.zeros((B, S), dtype=torch.uint8, device=response_mask.device)
+    mask[:, :-1] = response_mask[:, 1:] != 0
+    return hidden.reshape(B * S, H), targets.reshape(-1), mask.reshape(-1)

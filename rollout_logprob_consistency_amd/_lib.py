@@ -1,0 +1,66 @@
+"""ctypes declarations of the liblp C ABI (include/liblp.h).
+
+The shared library must have been built in-tree (build.py); importing the
+package without it raises, there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblp.so")
+
+LP_OK, LP_EINVAL, LP_EUNSUPPORTED, LP_EHIP = 0, 1, 2, 3
+
+# Names of every function include/liblp.h declares.
+EXPORTS = ("lp_status_string", "lp_score_workspace_bytes", "lp_score", "lp_compare")
+
+# numpy mirror of `lp_seq_stats` (natural C alignment: 6 int32 then 7 double).
+SEQ_STATS_DTYPE = np.dtype([
+    ("valid", "<i4"), ("mismatch", "<i4"), ("first_div", "<i4"),
+    ("longest_run", "<i4"), ("nonfinite", "<i4"), ("k3_nonfinite", "<i4"),
+    ("max_abs", "<f8"), ("sum_abs", "<f8"), ("sum_signed", "<f8"),
+    ("sum_k3", "<f8"), ("sum_d", "<f8"), ("seq_tis", "<f8"), ("sum_tok_tis", "<f8"),
+], align=True)
+assert SEQ_STATS_DTYPE.itemsize == 80
+
+
+class LpError(RuntimeError):
+    """A non-OK lp_status returned by the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m rollout_logprob_consistency_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    L.lp_status_string.restype = ctypes.c_char_p
+    L.lp_status_string.argtypes = [ctypes.c_int]
+    L.lp_score_workspace_bytes.restype = ctypes.c_size_t
+    L.lp_score_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    L.lp_score.restype = ctypes.c_int
+    L.lp_score.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, f32,
+                           vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.lp_compare.restype = ctypes.c_int
+    L.lp_compare.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, f32, vp, vp, vp]
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().lp_status_string(int(status)).decode()

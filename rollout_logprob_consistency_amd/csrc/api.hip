@@ -1,0 +1,103 @@
+// C-ABI entry points of liblp: argument validation, workspace layout, fixed
+// launch geometry. Every check happens before anything is enqueued.
+#include <math.h>
+#include <stdint.h>
+
+#include <limits>
+
+#include "lp_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+constexpr int64_t kI32Max = std::numeric_limits<int32_t>::max();
+
+}  // namespace
+
+extern "C" {
+
+const char* lp_status_string(lp_status status) {
+  switch (status) {
+    case LP_OK: return "LP_OK: success";
+    case LP_EINVAL: return "LP_EINVAL: invalid argument (nothing was enqueued)";
+    case LP_EUNSUPPORTED:
+      return "LP_EUNSUPPORTED: shape or alignment not supported (nothing was enqueued)";
+    case LP_EHIP: return "LP_EHIP: HIP runtime or kernel launch failure";
+  }
+  return "unknown lp_status";
+}
+
+size_t lp_score_workspace_bytes(int64_t T, int64_t H, int64_t V_rows, int64_t V_true) {
+  (void)H;
+  if (T < 0 || V_rows < 1 || V_true < 1 || V_true > V_rows) return 0;
+  return lp::score_workspace_layout(T, V_true).total;
+}
+
+lp_status lp_score(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
+                   const int64_t* target_ids, int64_t T, int64_t H, int64_t V_rows,
+                   int64_t V_true, float temperature, float* out_logprob, float* out_lse,
+                   int32_t* bad_rows, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  if (T < 0 || H < 1 || V_rows < 1 || V_true < 1 || V_true > V_rows || ldh < H)
+    return LP_EINVAL;
+  if (!(isfinite(temperature) && temperature > 0.0f)) return LP_EINVAL;
+  if (T == 0) return LP_OK;
+  if (!hidden_bf16 || !w_bf16 || !target_ids || !out_logprob || !workspace) return LP_EINVAL;
+  const lp::ScoreWorkspace ws = lp::score_workspace_layout(T, V_true);
+  if (workspace_bytes < ws.total || !aligned(workspace, 256)) return LP_EINVAL;
+  if (H % lp::kTileK != 0 || ldh % 8 != 0) return LP_EUNSUPPORTED;
+  if (!aligned(hidden_bf16, 16) || !aligned(w_bf16, 16)) return LP_EUNSUPPORTED;
+  const int64_t n_vt = (V_true + lp::kTileV - 1) / lp::kTileV;
+  const int64_t n_tt = (T + lp::kTileT - 1) / lp::kTileT;
+  if (T > kI32Max || H > kI32Max || V_rows > kI32Max || n_vt * n_tt > kI32Max)
+    return LP_EUNSUPPORTED;
+
+  lp::ScoreArgs a;
+  a.x = static_cast<const uint16_t*>(hidden_bf16);
+  a.w = static_cast<const uint16_t*>(w_bf16);
+  a.ids = target_ids;
+  a.ldh = ldh;
+  a.T = (int32_t)T;
+  a.H = (int32_t)H;
+  a.V_rows = (int32_t)V_rows;
+  a.V_true = (int32_t)V_true;
+  a.n_vt = (int32_t)n_vt;
+  a.n_tt = (int32_t)n_tt;
+  a.scale2 = (float)(1.4426950408889634 / (double)temperature);
+  char* base = static_cast<char*>(workspace);
+  a.part_m = reinterpret_cast<float*>(base + ws.off_m);
+  a.part_s = reinterpret_cast<float*>(base + ws.off_s);
+  a.tval = reinterpret_cast<float*>(base + ws.off_t);
+  a.out_lp = out_logprob;
+  a.out_lse = out_lse;
+  a.bad_rows = bad_rows;
+  return lp::launch_score(a, stream) == hipSuccess ? LP_OK : LP_EHIP;
+}
+
+lp_status lp_compare(const float* gen_A, const float* replay_B, const float* train_C,
+                     const uint8_t* mask, int64_t N, int64_t L, int64_t ld, float tis_clip,
+                     float atol, lp_seq_stats* out, float* per_token, hipStream_t stream) {
+  if (N < 0 || L < 0 || ld < L) return LP_EINVAL;
+  if (!(isfinite(tis_clip) && tis_clip > 0.0f) || isnan(atol)) return LP_EINVAL;
+  if (N == 0) return LP_OK;
+  if (!out) return LP_EINVAL;
+  if (L > 0 && (!gen_A || !replay_B || !train_C || !mask)) return LP_EINVAL;
+  if (L > kI32Max || N > kI32Max) return LP_EUNSUPPORTED;
+  lp::CompareArgs a;
+  a.A = gen_A;
+  a.B = replay_B;
+  a.C = train_C;
+  a.mask = mask;
+  a.N = N;
+  a.L = L;
+  a.ld = ld;
+  a.tis_clip = (double)tis_clip;
+  a.log_clip = log((double)tis_clip);
+  a.atol = atol < 0.0f ? -1.0 : (double)atol;
+  a.out = out;
+  a.per_token = per_token;
+  return lp::launch_compare(a, stream) == hipSuccess ? LP_OK : LP_EHIP;
+}
+
+}  // extern "C"

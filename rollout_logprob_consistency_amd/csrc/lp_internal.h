@@ -1,0 +1,58 @@
+// Internal launch interface between the C-ABI host code and the kernels.
+// Not installed; the public interface is include/liblp.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "liblp.h"
+
+namespace lp {
+
+// Fixed tile geometry of the selected-token logprob. These never depend on
+// the number of rows: every row is reduced over H and over the vocabulary in
+// the same order whatever batch it is scored in.
+constexpr int kTileV = 256;   // vocabulary rows per workgroup tile
+constexpr int kTileT = 256;   // token rows per workgroup tile
+constexpr int kTileK = 64;    // hidden elements per LDS stage
+
+struct ScoreArgs {
+  const uint16_t* x;      // [T, ldh] bf16 bits
+  const uint16_t* w;      // [V_rows, H] bf16 bits
+  const int64_t* ids;     // [T]
+  int64_t ldh;
+  int32_t T, H, V_rows, V_true;
+  int32_t n_vt, n_tt;     // vocabulary / token tile counts
+  float scale2;           // log2(e) / temperature
+  float* part_m;          // [n_vt][T]  per-tile max (log2 units)
+  float* part_s;          // [n_vt][T]  per-tile sum of exp2(s - max)
+  float* tval;            // [T]        target logit (log2 units)
+  float* out_lp;          // [T]
+  float* out_lse;         // [T] or null
+  int32_t* bad_rows;      // or null
+};
+
+// Workspace layout inside the caller's buffer (offsets in bytes, 256-aligned).
+struct ScoreWorkspace {
+  size_t off_m, off_s, off_t, total;
+};
+ScoreWorkspace score_workspace_layout(int64_t T, int64_t V_true);
+
+hipError_t launch_score(const ScoreArgs& a, hipStream_t stream);
+
+struct CompareArgs {
+  const float* A;
+  const float* B;
+  const float* C;
+  const uint8_t* mask;
+  int64_t N, L, ld;
+  double tis_clip;
+  double log_clip;        // log(tis_clip)
+  double atol;            // < 0: bitwise mode
+  lp_seq_stats* out;      // [3][N]
+  float* per_token;       // [3][3][N][L] or null
+};
+
+hipError_t launch_compare(const CompareArgs& a, hipStream_t stream);
+
+}  // namespace lp

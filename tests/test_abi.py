@@ -1,0 +1,134 @@
+"""The C-ABI library loads, exports every function include/liblp.h declares,
+and rejects invalid arguments before touching a device (CPU only: no call
+here reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "liblp.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from rollout_logprob_consistency_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("liblp.so is not built; run python -m rollout_logprob_consistency_amd.build")
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lp_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(
+        ["lp_status_string", "lp_score_workspace_bytes", "lp_score", "lp_compare"])
+
+
+def test_every_declared_symbol_is_exported(L):
+    from rollout_logprob_consistency_amd import _lib
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (lp_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+    assert set(_lib.EXPORTS) == set(declared_functions())
+
+
+def test_status_strings(L):
+    from rollout_logprob_consistency_amd import status_string
+    for code, word in ((0, "LP_OK"), (1, "LP_EINVAL"), (2, "LP_EUNSUPPORTED"), (3, "LP_EHIP")):
+        assert status_string(code).startswith(word)
+    assert "unknown" in status_string(99)
+
+
+def test_workspace_bytes(L):
+    for T, V in ((64, 4096), (8192, 151936), (1, 1), (300, 1000)):
+        n_vt = -(-V // 256)
+        got = L.lp_score_workspace_bytes(T, 4096, V, V)
+        assert got >= 2 * n_vt * T * 4 + T * 4 and got % 256 == 0
+    assert L.lp_score_workspace_bytes(-1, 64, 10, 10) == 0
+    assert L.lp_score_workspace_bytes(4, 64, 10, 11) == 0
+
+
+P = ctypes.c_void_p(0x10000)   # aligned, never dereferenced: every call below fails validation
+
+
+def score(L, T=4, H=64, V=300, vt=300, temp=1.0, ldh=None, hid=P, w=P, ids=P, out=P,
+          ws=P, wsb=1 << 30):
+    return L.lp_score(hid, H if ldh is None else ldh, w, ids, T, H, V, vt, temp, out,
+                      None, None, ws, wsb, None)
+
+
+def test_score_rejects_bad_arguments(L):
+    EINVAL, EUNSUP = 1, 2
+    nan, inf = float("nan"), float("inf")
+    assert score(L, T=-1) == EINVAL
+    assert score(L, H=0) == EINVAL
+    assert score(L, V=0, vt=0) == EINVAL
+    assert score(L, vt=0) == EINVAL
+    assert score(L, vt=301) == EINVAL
+    assert score(L, ldh=32) == EINVAL
+    for t in (0.0, -1.0, nan, inf):
+        assert score(L, temp=t) == EINVAL
+    for k in ("hid", "w", "ids", "out", "ws"):
+        assert score(L, **{k: None}) == EINVAL
+    assert score(L, wsb=16) == EINVAL
+    assert score(L, ws=ctypes.c_void_p(0x10010)) == EINVAL          # workspace misaligned
+    assert score(L, H=96, ldh=96) == EUNSUP                          # H % 64
+    assert score(L, ldh=68) == EUNSUP                                # ldh % 8
+    assert score(L, hid=ctypes.c_void_p(0x10008)) == EUNSUP          # 16-byte alignment
+    assert score(L, T=0, hid=None, w=None, ids=None, out=None, ws=None) == 0   # empty: no-op
+
+
+def cmp(L, N=2, Lq=5, ld=None, clip=2.0, atol=-1.0, out=P, a=P, m=P):
+    return L.lp_compare(a, P, P, m, N, Lq, Lq if ld is None else ld, clip, atol, out, None, None)
+
+
+def test_compare_rejects_bad_arguments(L):
+    EINVAL = 1
+    assert cmp(L, N=-1) == EINVAL
+    assert cmp(L, Lq=-1) == EINVAL
+    assert cmp(L, ld=3) == EINVAL
+    for c in (0.0, -2.0, float("nan"), float("inf")):
+        assert cmp(L, clip=c) == EINVAL
+    assert cmp(L, atol=float("nan")) == EINVAL
+    assert cmp(L, out=None) == EINVAL
+    assert cmp(L, a=None) == EINVAL
+    assert cmp(L, m=None) == EINVAL
+    assert cmp(L, N=0, out=None, a=None, m=None) == 0                 # empty: no-op
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import rollout_logprob_consistency_amd as lp
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        lp.score(x, x, torch.zeros(4, dtype=torch.int64))
+    a = torch.zeros(2, 3)
+    with pytest.raises(ValueError):
+        lp.compare(a, a, a, torch.ones(2, 3, dtype=torch.uint8))
+
+
+def test_align_shift_on_cpu():
+    import torch
+    import rollout_logprob_consistency_amd as lp
+    B, S, H = 2, 6, 4
+    hidden = torch.arange(B * S * H, dtype=torch.float32).reshape(B, S, H)
+    ids = torch.tensor([[5, 6, 7, 8, 9, 10], [11, 12, 13, 14, 15, 16]])
+    resp = torch.tensor([[0, 0, 0, 1, 1, 1], [0, 0, 1, 1, 0, 0]])
+    rows, tgt, mask = lp.align(hidden, ids, resp)
+    assert rows.shape == (B * S, H) and rows.data_ptr() == hidden.data_ptr()
+    # The output after the last prompt position scores the first response token.
+    assert tgt.tolist() == [6, 7, 8, 9, 10, 0, 12, 13, 14, 15, 16, 0]
+    assert mask.tolist() == [0, 0, 1, 1, 1, 0, 0, 1, 1, 0, 0, 0]
+    with pytest.raises(ValueError):
+        lp.align(hidden, ids, torch.ones_like(ids))

@@ -1,0 +1,160 @@
+"""GPU parity of lp_compare against the oracle: integer statistics and
+max_abs bit-exact, fixed-order fp64 sums to 1e-9 relative. Every call goes
+through the C ABI (liblp.so)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rollout_logprob_consistency_amd as lp
+from workloads import synth
+
+from .gpu_helpers import DEV, SCORE_ATOL, check_stats, dev, gpu_score
+
+pytestmark = pytest.mark.gpu
+
+
+def run(case_or_arrays, tis_clip=2.0, atol=None, per_token=False):
+    if isinstance(case_or_arrays, tuple):
+        A, B, C, M = case_or_arrays
+    else:
+        c = case_or_arrays
+        A, B, C, M = c.A, c.B, c.C, c.mask
+    res = lp.compare(dev(A), dev(B), dev(C), dev(M), tis_clip, atol, per_token, check=False)
+    ref = oracle.compare(A, B, C, M, tis_clip, atol)
+    got = res[0] if per_token else res
+    check_stats(got, ref)
+    return res, ref
+
+
+@pytest.fixture(scope="module")
+def record():
+    return synth.compare_case(N=8, max_resp=2048, prompt=256, seed=0)
+
+
+def with_c(c, C=None, A=None):
+    return (c.A if A is None else A, c.B, c.C if C is None else C, c.mask)
+
+
+def test_baseline_identical(record):
+    got, _ = run(record)
+    assert not got["AB"]["mismatch"].any() and (got["BC"]["first_div"] == -1).all()
+
+
+def test_fault_noise(record):
+    C = synth.noise_scores(record.C, record.mask, 1e-3, seed=11)
+    got, _ = run(with_c(record, C))
+    assert (got["BC"]["mismatch"] > 0).all()
+
+
+@pytest.mark.parametrize("k", [1, -1])
+def test_fault_token_shift(record, k):
+    C = synth.shift_scores(record.C, seq=3, k=k, fill=-5.0)
+    got, _ = run(with_c(record, C))
+    assert got["BC"]["mismatch"][3] > 0
+    assert not np.delete(got["BC"]["mismatch"], 3).any()
+
+
+def test_fault_case1_case2_offsets(record):
+    A = synth.offset_scores(record.A, record.mask, 0.10, first_pos=1)
+    C = synth.offset_scores(record.C, record.mask, 0.10)
+    got, _ = run(with_c(record, C, A))
+    assert (got["AB"]["first_div"][record.resp_len >= 2] == 1).all()
+    assert (got["BC"]["first_div"] == 0).all()
+
+
+def test_fault_stale_weights():
+    # Skipped weight sync: B scored with W, C with W' = bf16(W + N(0, 1e-3)),
+    # both by the oracle (rounded to fp32) so the comparison inputs never come
+    # from the GPU path. The GPU scorer is checked on the same rows too.
+    x, w, w_stale, ids = synth.stale_inputs()
+    N, L = 8, 2304
+    B = oracle.score(x, w, ids)[0].astype(np.float32).reshape(N, L)
+    C = oracle.score(x, w_stale, ids)[0].astype(np.float32).reshape(N, L)
+    rec = synth.compare_case(N=N, max_resp=2048, prompt=256, seed=5, B=B)
+    Cm = rec.C.copy()
+    act = rec.mask != 0
+    Cm[act] = C[act]
+    got, _ = run(with_c(rec, Cm))
+    assert (got["BC"]["mismatch"] > 0).all()
+    rows = np.flatnonzero(act.reshape(-1))[:4096]
+    g = gpu_score(x[rows], w_stale, ids[rows])
+    assert np.max(np.abs(g - C.reshape(-1)[rows])) <= SCORE_ATOL
+
+
+def test_per_token_values(record):
+    C = synth.noise_scores(record.C, record.mask, 1e-3, seed=12)
+    C[0, 300] = np.nan
+    (stats, pt), _ = run(with_c(record, C), per_token=True)
+    ref = oracle.per_token(record.A, record.B, C, record.mask)
+    got = pt.cpu().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[:, 0][fin[:, 0]], ref[:, 0][fin[:, 0]])        # |delta| exact
+    np.testing.assert_allclose(got[fin], ref[fin], rtol=2e-7, atol=1e-30)
+
+
+def test_special_values_and_atol():
+    f = np.float32
+    A = np.array([[0.0, -1.0, np.nan, np.inf, -1000.0, -2.0, -3.0, -4.0]], f)
+    B = np.array([[-0.0, -1.0, np.nan, -1.0, 0.0, -2.0005, -3.0, -4.0]], f)
+    C = np.array([[0.0, -1.5, -1.0, np.inf, -1000.0, -2.0, -3.1, np.nan]], f)
+    M = np.array([[1, 1, 1, 1, 1, 1, 0, 1]], np.uint8)
+    for atol in (None, 1e-3, 0.0):
+        run((A, B, C, M), atol=atol)
+    run((A, B, C, M), tis_clip=1.5)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_masks_with_holes(seed):
+    rng = np.random.default_rng(200 + seed)
+    N, L = 37, int(rng.integers(1, 700))
+    B = np.log(1.0 - rng.random((N, L))).astype(np.float32)
+    A = B.copy(); C = B.copy()
+    for arr in (A, C):
+        sel = rng.random((N, L)) < rng.random()
+        arr[sel] = (arr[sel] + rng.normal(0, 0.01, sel.sum())).astype(np.float32)
+    M = (rng.random((N, L)) < 0.8).astype(np.uint8)
+    M[0] = 0
+    run((A, B, C, M), atol=None if seed else 0.005)
+
+
+def test_strided_rows_and_degenerate_sizes(record):
+    N, L = record.N, record.L
+    pad = 40
+    big = [np.zeros((N, L + pad), a.dtype) for a in (record.A, record.B, record.C, record.mask)]
+    for b, a in zip(big, (record.A, record.B, record.C, record.mask)):
+        b[:, :L] = a
+    views = [dev(b)[:, :L] for b in big]
+    got = lp.compare(*views, check=False)
+    check_stats(got, oracle.compare(record.A, record.B, record.C, record.mask))
+    # N = 0: nothing to do; L = 0: every sequence is empty.
+    z = torch.zeros((0, 5), dtype=torch.float32, device=DEV)
+    lp.compare(z, z, z, torch.zeros((0, 5), dtype=torch.uint8, device=DEV), check=False)
+    e = torch.zeros((3, 0), dtype=torch.float32, device=DEV)
+    got = lp.compare(e, e, e, torch.zeros((3, 0), dtype=torch.uint8, device=DEV), check=False)
+    assert (got["AB"]["valid"] == 0).all() and (got["BC"]["first_div"] == -1).all()
+    with pytest.raises(ValueError):
+        lp.compare(e, e, e, torch.zeros((3, 0), dtype=torch.uint8, device=DEV))
+
+
+def test_results_independent_of_batch_and_repeatable(record):
+    C = synth.noise_scores(record.C, record.mask, 1e-3, seed=13)
+    full = lp.compare(dev(record.A), dev(record.B), dev(C), dev(record.mask), check=False)
+    again = lp.compare(dev(record.A), dev(record.B), dev(C), dev(record.mask), check=False)
+    one = lp.compare(dev(record.A[5:6]), dev(record.B[5:6]), dev(C[5:6]),
+                     dev(record.mask[5:6]), check=False)
+    for p in lp.PAIRS:
+        assert full[p].tobytes() == again[p].tobytes()
+        assert full[p][5:6].tobytes() == one[p].tobytes()
+
+
+def test_large_batch_sampled():
+    c = synth.compare_sweep_case(N=4096)
+    raw, _ = lp.compare_raw(dev(c.A), dev(c.B), dev(c.C), dev(c.mask))
+    got = lp.stats_from_bytes(raw, c.N)
+    seqs = np.random.default_rng(9).choice(c.N, 24, replace=False)
+    ref = oracle.compare(c.A[seqs], c.B[seqs], c.C[seqs], c.mask[seqs])
+    check_stats({p: got[p][seqs] for p in lp.PAIRS}, ref)
+    assert np.array_equal(got["AB"]["valid"], c.mask.sum(axis=1))
