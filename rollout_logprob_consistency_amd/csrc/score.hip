@@ -49,14 +49,17 @@ constexpr int kWaveT = 128;                  // token columns per wave
 constexpr int kSubV = kWaveV / 32;           // MFMA tiles along vocab
 constexpr int kSubT = kWaveT / 32;           // MFMA tiles along tokens
 constexpr int kChunks = kTileK / 8;          // 16-byte chunks per row per stage
-constexpr int kStageU4 = kTileV * kChunks;   // uint4 per operand stage
-constexpr int kLoads = kStageU4 / kThreads;  // 16-byte loads per thread per operand
+constexpr int kStageBytes = kTileV * kTileK * 2;     // one operand stage: 32 KiB
+constexpr int kLoads = kStageBytes / 16 / kThreads;  // 16-byte copies per thread per operand
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
+// lgkmcnt [11:8]); only vmcnt is constrained.
+constexpr int kWaitVm0 = 0x0F70;             // vmcnt(0)
 constexpr int kGroupV = 4;                   // vocab tiles per scheduling group
 constexpr float kLn2 = 0.693147180559945309f;
 
 static_assert(kTileV == kTileT, "A and B stages share one layout");
 static_assert(kTileV == 2 * kWaveV && kTileT == 2 * kWaveT, "2 x 2 waves");
-static_assert(kLoads * kThreads == kStageU4, "stage split");
+static_assert(kLoads * kThreads * 16 == kStageBytes, "stage split");
 
 // Physical 16-byte chunk of logical chunk `c` in tile row `row`.
 __device__ __forceinline__ int swz(int row, int c) {
@@ -66,7 +69,6 @@ __device__ __forceinline__ int swz(int row, int c) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 // Workgroup id -> (vocab tile, token tile). The hardware deals workgroups to
 // the 8 XCDs round-robin; give each XCD a contiguous run of logical tiles, and
@@ -88,54 +90,118 @@ __device__ __forceinline__ void tile_of(int b, int n_vt, int n_tt, int& vt, int&
   tt = r / gv;
 }
 
+// Direct buffer -> LDS copies (buffer_load_dwordx4 ... lds): one 16-byte chunk
+// per lane, the wave's 64 chunks landing contiguously at the LDS address
+// (lane i at byte 16 i); no VGPR round trip.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
+
+// Byte extent of a buffer resource, capped to what num_records can hold.
+__device__ __forceinline__ uint32_t span_bytes(uint64_t n) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(n > 0x7FFFFFF0ull ? 0x7FFFFFF0ull : n));
+}
+
+// Buffer resource from wave-uniform values, built so the compiler keeps it in
+// SGPRs (a resource it cannot prove uniform costs a waterfall loop per load).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const uint64_t pu = ((uint64_t)hi << 32) | lo;
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(pu), 0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
+}
+
+// Enqueue the copies of one K stage of both operands into LDS buffer `buf`.
+__device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t wres, __amdgpu_buffer_rsrc_t xres,
+                                            const uint32_t (&offA)[kLoads],
+                                            const uint32_t (&offB)[kLoads], lds_char* dstA,
+                                            lds_char* dstB, int wave, int koff) {
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int q = 4 * j + wave;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void*)(dstA + q * 1024), 16, offA[j],
+                                             koff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void*)(dstB + q * 1024), 16, offB[j],
+                                             koff, 0, 0);
+  }
+}
+
 __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
-  __shared__ uint4 smem[4 * kStageU4];  // A0 | A1 | B0 | B1  (128 KiB)
+  // LDS: two stages of each operand, 256 rows x 128 B each, the 16-byte chunks
+  // of row r XOR-permuted by f(r) (see swz()). Separate objects, so the
+  // compiler can tell the copies into one stage from the reads of the other.
+  __shared__ __attribute__((aligned(1024))) char sA0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char sA1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char sB0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char sB1[kStageBytes];
   __shared__ float red_m[2][kTileT];
   __shared__ float red_s[2][kTileT];
 
   int vt, tt;
   tile_of(blockIdx.x, a.n_vt, a.n_tt, vt, tt);
+  vt = __builtin_amdgcn_readfirstlane(vt);  // uniform: keep tile state in SGPRs
+  tt = __builtin_amdgcn_readfirstlane(tt);
   const int v0 = vt * kTileV, t0 = tt * kTileT;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
 
-  // Global -> LDS assignment: 16-byte chunk (row, kc) with row = lrow + 32 j.
-  const int lrow = tid >> 3, kc = tid & 7;
-  const uint16_t* pa[kLoads];
-  const uint16_t* pb[kLoads];
-  int woff[kLoads];
+  // ---- Global -> LDS assignment. Per operand and stage, wave w issues 8
+  // copies; copy j fills LDS rows 8q .. 8q+7 (q = 4 j + w), lane i writing
+  // physical chunk (i & 7) of row 8q + (i >> 3), i.e. logical chunk
+  // (i & 7) ^ f(row). Rows past the matrix are clamped (results discarded).
+  // Buffer resources based at the first row of each operand tile: the copies
+  // then take a 32-bit per-lane offset plus a uniform K offset.
+  const char* wtile = reinterpret_cast<const char*>(a.w) + (size_t)v0 * a.H * 2;
+  const char* xtile = reinterpret_cast<const char*>(a.x) + (size_t)t0 * a.ldh * 2;
+  const uint32_t w_span = span_bytes((uint64_t)(a.V_rows - v0) * (uint64_t)a.H * 2);
+  const uint32_t x_span = span_bytes((uint64_t)(a.T - t0 - 1) * (uint64_t)a.ldh * 2 + (uint64_t)a.H * 2);
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc(wtile, w_span);
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc(xtile, x_span);
+  uint32_t offA[kLoads], offB[kLoads];
 #pragma unroll
   for (int j = 0; j < kLoads; ++j) {
-    const int row = lrow + 32 * j;
-    const int rv = min(v0 + row, a.V_rows - 1);
-    const int rt = min(t0 + row, a.T - 1);
-    pa[j] = a.w + (size_t)rv * a.H + kc * 8;
-    pb[j] = a.x + (size_t)rt * a.ldh + kc * 8;
-    woff[j] = row * kChunks + swz(row, kc);
+    const int q = 4 * j + wave;
+    const int row = 8 * q + (lane >> 3);
+    const int c = swz(row, lane & 7);  // XOR permutation is its own inverse
+    const int ra = min(row, a.V_rows - 1 - v0);
+    const int rt = min(row, a.T - 1 - t0);
+    offA[j] = (uint32_t)ra * (uint32_t)(a.H * 2) + c * 16;
+    offB[j] = (uint32_t)rt * (uint32_t)(a.ldh * 2) + c * 16;
   }
+#define ISSUE_STAGE(kt_, buf_)                                                          \
+  issue_stage(wres, xres, offA, offB, (lds_char*)((buf_) ? sA1 : sA0),               \
+              (lds_char*)((buf_) ? sB1 : sB0), wave, (kt_) * (kTileK * 2))
 
-  uint4 ra[kLoads], rb[kLoads];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      ra[j] = *reinterpret_cast<const uint4*>(pa[j] + kt * kTileK);
-      rb[j] = *reinterpret_cast<const uint4*>(pb[j] + kt * kTileK);
-    }
-  };
-  auto swrite = [&](int buf) {
-    uint4* As = smem + buf * kStageU4;
-    uint4* Bs = smem + (2 + buf) * kStageU4;
-#pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      As[woff[j]] = ra[j];
-      Bs[woff[j]] = rb[j];
-    }
-  };
-
-  // Fragment read offsets (uint4 units within a stage) for substep s, tile i.
+  // ---- Fragment reads. Lane l reads row (base + 32 i + (l & 31)), logical
+  // chunk 2 s + (l >> 5). With f(row) = (l & 7) ^ ((l & 31) >> 3) ^ 4 (i & 1)
+  // the physical chunk is 2 (s ^ 2 (i & 1)) ^ c0 with c0 = (l >> 5) ^ f0, so
+  // four addresses per operand cover every (s, i); the rest is immediate.
   const int frow = lane & 31, fhalf = lane >> 5;
+  const int c0 = fhalf ^ ((frow & 7) ^ (frow >> 3));
+  uint32_t rdA[4], rdB[4];
+#pragma unroll
+  for (int sp = 0; sp < 4; ++sp) {
+    rdA[sp] = (uint32_t)((wm * kWaveV + frow) * 128 + (((2 * sp) ^ c0) * 16));
+    rdB[sp] = (uint32_t)((wn * kWaveT + frow) * 128 + (((2 * sp) ^ c0) * 16));
+  }
+  auto read_frags = [&](bf16x8 (&fa)[kSubV], bf16x8 (&fb)[kSubT], int buf, int s)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kSubV; ++i) {
+      const int sp = s ^ (2 * (i & 1));
+      fa[i] = *reinterpret_cast<const bf16x8*>((buf ? sA1 : sA0) + rdA[sp] + i * 4096);
+    }
+#pragma unroll
+    for (int j = 0; j < kSubT; ++j) {
+      const int sp = s ^ (2 * (j & 1));
+      fb[j] = *reinterpret_cast<const bf16x8*>((buf ? sB1 : sB0) + rdB[sp] + j * 4096);
+    }
+  };
 
   f32x16 acc[kSubV][kSubT];
 #pragma unroll
@@ -145,39 +211,65 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = a.H / kTileK;
-  gload(0);
-  swrite(0);
-  __syncthreads();
+  auto mma = [&](const bf16x8 (&fa)[kSubV], const bf16x8 (&fb)[kSubT])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kSubV; ++i)
+#pragma unroll
+      for (int j = 0; j < kSubT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint4* As = smem + cur * kStageU4;
-    const uint4* Bs = smem + (2 + cur) * kStageU4;
-#pragma unroll
-    for (int s = 0; s < kTileK / 16; ++s) {
-      const int ch = 2 * s + fhalf;
-      bf16x8 fa[kSubV], fb[kSubT];
-#pragma unroll
-      for (int i = 0; i < kSubV; ++i) {
-        const int row = wm * kWaveV + i * 32 + frow;
-        fa[i] = as_bf16x8(As[row * kChunks + swz(row, ch)]);
-      }
-#pragma unroll
-      for (int j = 0; j < kSubT; ++j) {
-        const int row = wn * kWaveT + j * 32 + frow;
-        fb[j] = as_bf16x8(Bs[row * kChunks + swz(row, ch)]);
-      }
-#pragma unroll
-      for (int i = 0; i < kSubV; ++i)
-#pragma unroll
-        for (int j = 0; j < kSubT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) swrite(cur ^ 1);
-    __syncthreads();
+  const int nk = a.H / kTileK;
+  bf16x8 fa0[kSubV], fb0[kSubT], fa1[kSubV], fb1[kSubT];
+
+  // Software pipeline over K stages. Phase kt runs between two barriers with
+  // stage kt readable in LDS buffer kt & 1: it first enqueues the copy of
+  // stage kt+1 into the other buffer (freed by the barrier just passed), then
+  // alternates fragment registers so that the LDS reads of substep s+1 are in
+  // flight while the 16 MFMAs of substep s issue; the 16 MFMAs of the last
+  // substep are carried into the next phase, where they cover the latency of
+  // its first reads. Each phase ends with vmcnt(0) + barrier, so no copy is in
+  // flight across the loop back-edge. sched_barrier(0) keeps the compiler
+  // from re-ordering the phases.
+#define PHASE_FENCE() __builtin_amdgcn_sched_barrier(0)
+#define PHASE(kt_, buf_, carry_)                                  \
+  do {                                                            \
+    if ((kt_) + 1 < nk) ISSUE_STAGE((kt_) + 1, (buf_) ^ 1);       \
+    PHASE_FENCE();                                                \
+    read_frags(fa0, fb0, (buf_), 0);                              \
+    PHASE_FENCE();                                                \
+    if (carry_) mma(fa1, fb1);                                    \
+    PHASE_FENCE();                                                \
+    read_frags(fa1, fb1, (buf_), 1);                              \
+    PHASE_FENCE();                                                \
+    mma(fa0, fb0);                                                \
+    PHASE_FENCE();                                                \
+    read_frags(fa0, fb0, (buf_), 2);                              \
+    PHASE_FENCE();                                                \
+    mma(fa1, fb1);                                                \
+    PHASE_FENCE();                                                \
+    read_frags(fa1, fb1, (buf_), 3);                              \
+    PHASE_FENCE();                                                \
+    mma(fa0, fb0);                                                \
+    PHASE_FENCE();                                                \
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);                         \
+    __syncthreads();                                              \
+    PHASE_FENCE();                                                \
+  } while (0)
+
+  ISSUE_STAGE(0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  PHASE(0, 0, false);
+  for (int kt = 1; kt < nk; kt += 2) {
+    PHASE(kt, 1, true);
+    if (kt + 1 < nk) PHASE(kt + 1, 0, true);
   }
+  mma(fa1, fb1);  // last substep of the last stage
+#undef ISSUE_STAGE
+#undef PHASE
+#undef PHASE_FENCE
 
   // ---- Epilogue: per-token online LSE over this wave's 128 vocab rows. ----
   // MFMA 32x32 output layout: lane l holds column (l & 31) and, in register
