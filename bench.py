@@ -69,6 +69,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-n", type=int, default=4096,
                     help="sequences in the comparison bandwidth probe (L = 2304)")
+    ap.add_argument("--mode", choices=("bench", "score", "copy"), default="bench",
+                    help="score: only `steps` lp_score calls on the benchmark batch (for "
+                         "profilers); copy: one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the scoring path has no cross-GPU "
@@ -85,6 +88,15 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     T, H, V, NSEQ, LSEQ = 8192, 4096, 151936, 16, 512
+
+    if args.mode == "copy":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(7)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("bench: copied 1 GiB device to device")
+        return 0
 
     t0 = time.time()
     log("bench: generating Qwen3-8B-shaped inputs (seeded, host) ...")
@@ -111,6 +123,13 @@ def main() -> int:
     mask = torch.ones((NSEQ, LSEQ), dtype=torch.uint8, device=dev)
     B = out.view(NSEQ, LSEQ)
     stats_buf = torch.empty(3 * NSEQ * lp.SEQ_STATS_DTYPE.itemsize, dtype=torch.uint8, device=dev)
+
+    if args.mode == "score":
+        for _ in range(args.steps):
+            lp.score(x, w, ids, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        log(f"bench: {args.steps} lp_score calls done")
+        return 0
 
     def step(ev=None):
         if ev is not None:

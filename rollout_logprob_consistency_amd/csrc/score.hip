@@ -233,29 +233,54 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   // flight across the loop back-edge. sched_barrier(0) keeps the compiler
   // from re-ordering the phases.
 #define PHASE_FENCE() __builtin_amdgcn_sched_barrier(0)
-#define PHASE(kt_, buf_, carry_)                                  \
-  do {                                                            \
-    if ((kt_) + 1 < nk) ISSUE_STAGE((kt_) + 1, (buf_) ^ 1);       \
-    PHASE_FENCE();                                                \
-    read_frags(fa0, fb0, (buf_), 0);                              \
-    PHASE_FENCE();                                                \
-    if (carry_) mma(fa1, fb1);                                    \
-    PHASE_FENCE();                                                \
-    read_frags(fa1, fb1, (buf_), 1);                              \
-    PHASE_FENCE();                                                \
-    mma(fa0, fb0);                                                \
-    PHASE_FENCE();                                                \
-    read_frags(fa0, fb0, (buf_), 2);                              \
-    PHASE_FENCE();                                                \
-    mma(fa1, fb1);                                                \
-    PHASE_FENCE();                                                \
-    read_frags(fa1, fb1, (buf_), 3);                              \
-    PHASE_FENCE();                                                \
-    mma(fa0, fb0);                                                \
-    PHASE_FENCE();                                                \
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);                         \
-    __syncthreads();                                              \
-    PHASE_FENCE();                                                \
+// Interleave hints (sched_group_barrier masks: 0x008 MFMA, 0x020 VMEM read,
+// 0x100 DS read): spread the 8 fragment reads, and the 16 stage copies when
+// present, over the first 8 MFMAs of a group so that neither stalls the
+// matrix pipe.
+#define SGB(mask_, n_) __builtin_amdgcn_sched_group_barrier((mask_), (n_), 0)
+#define MIX_READS()                   \
+  do {                                \
+    _Pragma("unroll") for (int u = 0; u < 8; ++u) { \
+      SGB(0x008, 1);                  \
+      SGB(0x100, 1);                  \
+    }                                 \
+    SGB(0x008, 8);                    \
+  } while (0)
+#define MIX_READS_COPIES()            \
+  do {                                \
+    _Pragma("unroll") for (int u = 0; u < 8; ++u) { \
+      SGB(0x008, 1);                  \
+      SGB(0x020, 2);                  \
+      SGB(0x100, 1);                  \
+    }                                 \
+    SGB(0x008, 8);                    \
+  } while (0)
+#define GROUP(rd_a, rd_b, s_, mm_a, mm_b)   \
+  do {                                      \
+    read_frags(rd_a, rd_b, buf, (s_));      \
+    mma(mm_a, mm_b);                        \
+    MIX_READS();                            \
+    PHASE_FENCE();                          \
+  } while (0)
+// The copy of the next stage is issued unconditionally (branch-free, so it
+// can be interleaved): in the last phase it re-copies the final stage into the
+// idle buffer, which nothing reads; the vmcnt(0) before the barrier drains it.
+#define PHASE(kt_, buf_, carry_)                                            \
+  do {                                                                      \
+    const int buf = (buf_);                                                 \
+    ISSUE_STAGE(min((kt_) + 1, nk - 1), buf ^ 1);                           \
+    read_frags(fa0, fb0, buf, 0);                                           \
+    if (carry_) {                                                           \
+      mma(fa1, fb1);                                                        \
+      MIX_READS_COPIES();                                                   \
+    }                                                                       \
+    PHASE_FENCE();                                                          \
+    GROUP(fa1, fb1, 1, fa0, fb0);                                           \
+    GROUP(fa0, fb0, 2, fa1, fb1);                                           \
+    GROUP(fa1, fb1, 3, fa0, fb0);                                           \
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);                                   \
+    __syncthreads();                                                        \
+    PHASE_FENCE();                                                          \
   } while (0)
 
   ISSUE_STAGE(0, 0);
@@ -269,6 +294,10 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   mma(fa1, fb1);  // last substep of the last stage
 #undef ISSUE_STAGE
 #undef PHASE
+#undef GROUP
+#undef MIX_READS
+#undef MIX_READS_COPIES
+#undef SGB
 #undef PHASE_FENCE
 
   // ---- Epilogue: per-token online LSE over this wave's 128 vocab rows. ----
@@ -344,19 +373,43 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   }
 }
 
-// One thread per token: merge the vocabulary-tile partials in ascending tile
-// order, then logprob = (target - lse) in nats.
-__global__ __launch_bounds__(256) void lse_merge_kernel(ScoreArgs a) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= a.T) return;
+// Merge of the per-tile partials. A workgroup takes 64 consecutive tokens
+// (one per lane, so every partial row is read coalesced) and 8 waves; wave w
+// folds the vocabulary tiles of segment w in ascending order, then the 8
+// segment results are folded in segment order. Segment bounds depend only on
+// the number of vocabulary tiles, so the order is the same for every batch.
+constexpr int kMergeSegs = 8;
+
+__device__ __forceinline__ void lse_fold(float& M, float& S, float m, float s) {
+  const float Mn = fmaxf(M, m);
+  S = S * fast_exp2(M - Mn) + s * fast_exp2(m - Mn);  // exp2(-inf) = 0 on first use
+  M = Mn;
+}
+
+__global__ __launch_bounds__(64 * kMergeSegs) void lse_merge_kernel(ScoreArgs a) {
+  __shared__ float seg_m[kMergeSegs][64];
+  __shared__ float seg_s[kMergeSegs][64];
+  const int lane = threadIdx.x & 63, seg = threadIdx.x >> 6;
+  const int t = blockIdx.x * 64 + lane;
+  const int per = (a.n_vt + kMergeSegs - 1) / kMergeSegs;
+  const int lo = min(a.n_vt, seg * per), hi = min(a.n_vt, lo + per);
   float M = -__builtin_inff(), S = 0.f;
-  for (int vt = 0; vt < a.n_vt; ++vt) {
-    const float m = a.part_m[(size_t)vt * a.T + t];
-    const float s = a.part_s[(size_t)vt * a.T + t];
-    const float Mn = fmaxf(M, m);
-    S = S * fast_exp2(M - Mn) + s * fast_exp2(m - Mn);
-    M = Mn;
+  if (t < a.T) {
+    const float* pm = a.part_m + t;
+    const float* ps = a.part_s + t;
+#pragma unroll 4
+    for (int vt = lo; vt < hi; ++vt)
+      lse_fold(M, S, pm[(size_t)vt * a.T], ps[(size_t)vt * a.T]);
   }
+  seg_m[seg][lane] = M;
+  seg_s[seg][lane] = S;
+  __syncthreads();
+  if (seg != 0 || t >= a.T) return;
+  M = seg_m[0][lane];
+  S = seg_s[0][lane];
+#pragma unroll
+  for (int g = 1; g < kMergeSegs; ++g)  // an empty segment (-inf, 0) folds to a no-op
+    lse_fold(M, S, seg_m[g][lane], seg_s[g][lane]);
   const float lse2 = M + fast_log2(S);
   const int64_t id = a.ids[t];
   const bool ok = id >= 0 && id < a.V_true;
@@ -383,7 +436,7 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(score_tile_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lse_merge_kernel, dim3((a.T + 255) / 256), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(lse_merge_kernel, dim3((a.T + 63) / 64), dim3(64 * kMergeSegs), 0, stream, a);
   return hipGetLastError();
 }
 
