@@ -113,13 +113,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
 }
 
-// Enqueue the copies of one K stage of both operands into LDS buffer `buf`.
+// Enqueue copies j0 <= j < j1 of one K stage of both operands into the LDS
+// stage buffers dstA (W) and dstB (X).
 __device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t wres, __amdgpu_buffer_rsrc_t xres,
                                             const uint32_t (&offA)[kLoads],
                                             const uint32_t (&offB)[kLoads], lds_char* dstA,
-                                            lds_char* dstB, int wave, int koff) {
+                                            lds_char* dstB, int wave, int koff, int j0, int j1) {
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) {
+  for (int j = j0; j < j1; ++j) {
     const int q = 4 * j + wave;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void*)(dstA + q * 1024), 16, offA[j],
                                              koff, 0, 0);
@@ -173,9 +174,10 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
     offA[j] = (uint32_t)ra * (uint32_t)(a.H * 2) + c * 16;
     offB[j] = (uint32_t)rt * (uint32_t)(a.ldh * 2) + c * 16;
   }
-#define ISSUE_STAGE(kt_, buf_)                                                          \
+#define ISSUE_PART(kt_, buf_, j0_, j1_)                                                 \
   issue_stage(wres, xres, offA, offB, (lds_char*)((buf_) ? sA1 : sA0),               \
-              (lds_char*)((buf_) ? sB1 : sB0), wave, (kt_) * (kTileK * 2))
+              (lds_char*)((buf_) ? sB1 : sB0), wave, (kt_) * (kTileK * 2), (j0_), (j1_))
+#define ISSUE_STAGE(kt_, buf_) ISSUE_PART((kt_), (buf_), 0, kLoads)
 
   // ---- Fragment reads. Lane l reads row (base + 32 i + (l & 31)), logical
   // chunk 2 s + (l >> 5). With f(row) = (l & 7) ^ ((l & 31) >> 3) ^ 4 (i & 1)
@@ -224,60 +226,66 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   bf16x8 fa0[kSubV], fb0[kSubT], fa1[kSubV], fb1[kSubT];
 
   // Software pipeline over K stages. Phase kt runs between two barriers with
-  // stage kt readable in LDS buffer kt & 1: it first enqueues the copy of
-  // stage kt+1 into the other buffer (freed by the barrier just passed), then
-  // alternates fragment registers so that the LDS reads of substep s+1 are in
-  // flight while the 16 MFMAs of substep s issue; the 16 MFMAs of the last
-  // substep are carried into the next phase, where they cover the latency of
-  // its first reads. Each phase ends with vmcnt(0) + barrier, so no copy is in
-  // flight across the loop back-edge. sched_barrier(0) keeps the compiler
-  // from re-ordering the phases.
+  // stage kt readable in LDS buffer kt & 1 and four substeps of 16 MFMAs. The
+  // copies of stage kt+1 into the other buffer (freed by the barrier just
+  // passed) are spread one per two MFMAs over the first two substeps: a
+  // 1-KiB copy keeps the CU's address unit busy for several cycles, and
+  // bursts of copies from the four waves (which all leave the barrier
+  // together) would stall their in-order MFMA issue, while copies issued in
+  // the second half of the phase would not land before its end. Fragment
+  // registers alternate per substep so that the LDS reads of substep s+1
+  // (one per two MFMAs) overlap the MFMAs of substep s; the 16 MFMAs of the
+  // last substep are carried into the next phase, where they cover the
+  // latency of its first reads. Each phase ends with vmcnt(0) + barrier, so
+  // no copy is in flight across the loop back-edge. The copy of the next
+  // stage is issued unconditionally (branch-free, so it can be interleaved):
+  // in the last phase it re-copies the final stage into the idle buffer,
+  // which nothing reads. sched_barrier(0) keeps the compiler from re-ordering
+  // the substeps; sched_group_barrier sets the interleave inside one (masks:
+  // 0x008 MFMA, 0x020 VMEM read, 0x100 DS read).
 #define PHASE_FENCE() __builtin_amdgcn_sched_barrier(0)
-// Interleave hints (sched_group_barrier masks: 0x008 MFMA, 0x020 VMEM read,
-// 0x100 DS read): spread the 8 fragment reads, and the 16 stage copies when
-// present, over the first 8 MFMAs of a group so that neither stalls the
-// matrix pipe.
 #define SGB(mask_, n_) __builtin_amdgcn_sched_group_barrier((mask_), (n_), 0)
-#define MIX_READS()                   \
-  do {                                \
-    _Pragma("unroll") for (int u = 0; u < 8; ++u) { \
-      SGB(0x008, 1);                  \
-      SGB(0x100, 1);                  \
-    }                                 \
-    SGB(0x008, 8);                    \
+#define MIX_READS()                                  \
+  do {                                               \
+    _Pragma("unroll") for (int u = 0; u < 8; ++u) {  \
+      SGB(0x008, 1);                                 \
+      SGB(0x100, 1);                                 \
+      SGB(0x008, 1);                                 \
+    }                                                \
   } while (0)
-#define MIX_READS_COPIES()            \
-  do {                                \
-    _Pragma("unroll") for (int u = 0; u < 8; ++u) { \
-      SGB(0x008, 1);                  \
-      SGB(0x020, 2);                  \
-      SGB(0x100, 1);                  \
-    }                                 \
-    SGB(0x008, 8);                    \
+#define MIX_READS_COPIES()                           \
+  do {                                               \
+    _Pragma("unroll") for (int u = 0; u < 8; ++u) {  \
+      SGB(0x008, 1);                                 \
+      SGB(0x020, 1);                                 \
+      SGB(0x100, 1);                                 \
+      SGB(0x008, 1);                                 \
+    }                                                \
   } while (0)
-#define GROUP(rd_a, rd_b, s_, mm_a, mm_b)   \
-  do {                                      \
-    read_frags(rd_a, rd_b, buf, (s_));      \
-    mma(mm_a, mm_b);                        \
-    MIX_READS();                            \
-    PHASE_FENCE();                          \
-  } while (0)
-// The copy of the next stage is issued unconditionally (branch-free, so it
-// can be interleaved): in the last phase it re-copies the final stage into the
-// idle buffer, which nothing reads; the vmcnt(0) before the barrier drains it.
 #define PHASE(kt_, buf_, carry_)                                            \
   do {                                                                      \
     const int buf = (buf_);                                                 \
-    ISSUE_STAGE(min((kt_) + 1, nk - 1), buf ^ 1);                           \
+    const int kc = min((kt_) + 1, nk - 1);                                  \
+    ISSUE_PART(kc, buf ^ 1, 0, kLoads / 2);                                 \
     read_frags(fa0, fb0, buf, 0);                                           \
     if (carry_) {                                                           \
       mma(fa1, fb1);                                                        \
       MIX_READS_COPIES();                                                   \
     }                                                                       \
     PHASE_FENCE();                                                          \
-    GROUP(fa1, fb1, 1, fa0, fb0);                                           \
-    GROUP(fa0, fb0, 2, fa1, fb1);                                           \
-    GROUP(fa1, fb1, 3, fa0, fb0);                                           \
+    ISSUE_PART(kc, buf ^ 1, kLoads / 2, kLoads);                            \
+    read_frags(fa1, fb1, buf, 1);                                           \
+    mma(fa0, fb0);                                                          \
+    MIX_READS_COPIES();                                                     \
+    PHASE_FENCE();                                                          \
+    read_frags(fa0, fb0, buf, 2);                                           \
+    mma(fa1, fb1);                                                          \
+    MIX_READS();                                                            \
+    PHASE_FENCE();                                                          \
+    read_frags(fa1, fb1, buf, 3);                                           \
+    mma(fa0, fb0);                                                          \
+    MIX_READS();                                                            \
+    PHASE_FENCE();                                                          \
     __builtin_amdgcn_s_waitcnt(kWaitVm0);                                   \
     __syncthreads();                                                        \
     PHASE_FENCE();                                                          \
@@ -293,8 +301,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   }
   mma(fa1, fb1);  // last substep of the last stage
 #undef ISSUE_STAGE
+#undef ISSUE_PART
 #undef PHASE
-#undef GROUP
 #undef MIX_READS
 #undef MIX_READS_COPIES
 #undef SGB
