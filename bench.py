@@ -64,7 +64,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-rows", type=int, default=512,
+    ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the batch the fp64 oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-n", type=int, default=4096,
