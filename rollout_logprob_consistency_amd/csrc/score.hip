@@ -316,27 +316,36 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   const bool vtail = v0 + kTileV > a.V_true;
   const int64_t wv_lo = v0 + wm * kWaveV;
 
+  // Rows at or past V_true (only in the last vocabulary tile) become -inf.
+  if (vtail) {
+#pragma unroll
+    for (int i = 0; i < kSubV; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (vlane + 32 * i + 8 * (r >> 2) + (r & 3) >= a.V_true)
+#pragma unroll
+          for (int j = 0; j < kSubT; ++j) acc[i][j][r] = NEG_INF;
+  }
+
 #pragma unroll
   for (int j = 0; j < kSubT; ++j) {
     const int tl = wn * kWaveT + j * 32 + frow;
     const int t = t0 + tl;
-    float m = NEG_INF;
+    // The scale log2(e)/T is positive, so the max of the scaled logits is the
+    // scaled max; the scale is folded into the exp2 argument with one FMA.
+    float mr = NEG_INF;
 #pragma unroll
     for (int i = 0; i < kSubV; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = acc[i][j][r] * a.scale2;
-        if (vtail && vlane + 32 * i + 8 * (r >> 2) + (r & 3) >= a.V_true) x = NEG_INF;
-        acc[i][j][r] = x;
-        m = fmaxf(m, x);
-      }
-    m = fmaxf(m, __shfl_xor(m, 32));
+      for (int r = 0; r < 16; ++r) mr = fmaxf(mr, acc[i][j][r]);
+    mr = fmaxf(mr, __shfl_xor(mr, 32));
+    const float m = mr * a.scale2;
     float s = 0.f;
-    if (m != NEG_INF) {
+    if (mr != NEG_INF) {
 #pragma unroll
       for (int i = 0; i < kSubV; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s += fast_exp2(acc[i][j][r] - m);
+        for (int r = 0; r < 16; ++r) s += fast_exp2(__builtin_fmaf(acc[i][j][r], a.scale2, -m));
     }
     s += __shfl_xor(s, 32);  // s_l + s_{l^32}: identical in both lanes
 
@@ -355,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
               if (i == ti && r == tr) tv = acc[i][j][r];
-          a.tval[t] = tv;
+          a.tval[t] = tv * a.scale2;
         }
       }
     }
