@@ -97,6 +97,8 @@ lp_status lp_compare(const float* gen_A, const float* replay_B, const float* tra
   a.atol = atol < 0.0f ? -1.0 : (double)atol;
   a.out = out;
   a.per_token = per_token;
+  a.vec = ld % 4 == 0 && aligned(gen_A, 16) && aligned(replay_B, 16) && aligned(train_C, 16) &&
+          aligned(mask, 4);
   return lp::launch_compare(a, stream) == hipSuccess ? LP_OK : LP_EHIP;
 }
 

@@ -49,6 +49,7 @@ struct CompareArgs {
   double tis_clip;
   double log_clip;        // log(tis_clip)
   double atol;            // < 0: bitwise mode
+  bool vec;               // rows 16-byte aligned (A, B, C) and 4-byte aligned (mask)
   lp_seq_stats* out;      // [3][N]
   float* per_token;       // [3][3][N][L] or null
 };

@@ -8,7 +8,11 @@ import rollout_logprob_consistency_amd as lp
 
 DEV = "cuda:0"
 INT_FIELDS = ("valid", "mismatch", "first_div", "longest_run", "nonfinite", "k3_nonfinite")
-SUM_FIELDS = ("sum_abs", "sum_signed", "sum_d", "sum_k3", "sum_tok_tis", "seq_tis")
+# fp64 sums in a fixed order: compared at 1e-9 relative, except the two whose
+# per-token terms are evaluated in fp32 for |d| < 0.5 (k3 by its Taylor series,
+# exp(d) by exp2), compared at 1e-6 relative.
+SUM_RTOL = {"sum_abs": 1e-9, "sum_signed": 1e-9, "sum_d": 1e-9, "seq_tis": 1e-9,
+            "sum_k3": 1e-6, "sum_tok_tis": 1e-6}
 # Score tolerance: max |GPU - fp64 oracle| in nats.
 SCORE_ATOL = 1e-3
 
@@ -35,12 +39,12 @@ def gpu_score(x_bits, w_dev_or_bits, ids, temperature=1.0, v_true=None, lse=Fals
     return (out.cpu().numpy(), l.cpu().numpy()) if lse else out.cpu().numpy()
 
 
-def check_stats(gpu: dict, ref: dict, rtol=1e-9):
-    """Integer fields and max_abs exact; fixed-order fp64 sums to rtol."""
+def check_stats(gpu: dict, ref: dict):
+    """Integer fields and max_abs exact; sums to SUM_RTOL."""
     for p in lp.PAIRS:
         g, r = gpu[p], ref[p]
         for f in INT_FIELDS:
             assert np.array_equal(g[f].astype(np.int64), r[f]), (p, f, g[f], r[f])
         assert np.array_equal(g["max_abs"], r["max_abs"]), (p, "max_abs")
-        for f in SUM_FIELDS:
+        for f, rtol in SUM_RTOL.items():
             np.testing.assert_allclose(g[f], r[f], rtol=rtol, atol=1e-12, err_msg=f"{p} {f}")

@@ -1,6 +1,7 @@
 """GPU parity of lp_compare against the oracle: integer statistics and
-max_abs bit-exact, fixed-order fp64 sums to 1e-9 relative. Every call goes
-through the C ABI (liblp.so)."""
+max_abs bit-exact, fixed-order fp64 sums to 1e-9 relative (k3 and token-TIS
+sums, whose small-|d| terms are fp32, to 1e-6). Every call goes through the
+C ABI (liblp.so)."""
 
 import numpy as np
 import pytest
@@ -92,7 +93,7 @@ def test_per_token_values(record):
     assert np.array_equal(np.isnan(got), np.isnan(ref))
     fin = ~np.isnan(ref)
     assert np.array_equal(got[:, 0][fin[:, 0]], ref[:, 0][fin[:, 0]])        # |delta| exact
-    np.testing.assert_allclose(got[fin], ref[fin], rtol=2e-7, atol=1e-30)
+    np.testing.assert_allclose(got[:, 1:][fin[:, 1:]], ref[:, 1:][fin[:, 1:]], rtol=1e-6, atol=1e-30)
 
 
 def test_special_values_and_atol():
@@ -158,3 +159,17 @@ def test_large_batch_sampled():
     ref = oracle.compare(c.A[seqs], c.B[seqs], c.C[seqs], c.mask[seqs])
     check_stats({p: got[p][seqs] for p in lp.PAIRS}, ref)
     assert np.array_equal(got["AB"]["valid"], c.mask.sum(axis=1))
+
+
+def test_vector_and_scalar_paths_agree(record):
+    # Rows whose stride is not a multiple of 4 take the scalar path; it visits
+    # the same positions in the same order as the 16-byte path.
+    C = synth.noise_scores(record.C, record.mask, 1e-3, seed=14)
+    N, L = record.N, record.L
+    vec = lp.compare(dev(record.A), dev(record.B), dev(C), dev(record.mask), check=False)
+    big = [np.zeros((N, L + 1), a.dtype) for a in (record.A, record.B, C, record.mask)]
+    for b, a in zip(big, (record.A, record.B, C, record.mask)):
+        b[:, :L] = a
+    sca = lp.compare(*[dev(b)[:, :L] for b in big], check=False)
+    for p in lp.PAIRS:
+        assert vec[p].tobytes() == sca[p].tobytes(), p
