@@ -173,3 +173,31 @@ def test_vector_and_scalar_paths_agree(record):
     sca = lp.compare(*[dev(b)[:, :L] for b in big], check=False)
     for p in lp.PAIRS:
         assert vec[p].tobytes() == sca[p].tobytes(), p
+
+
+def test_large_differences_and_overflow():
+    # |d| >= 0.5 takes the fp64 exponential; d = 700 stays finite, d beyond
+    # the fp64 overflow threshold of e^d (about 709.78) makes k3 overflow
+    # (counted, never clipped) while the TIS weight clips; d <= -745
+    # underflows e^d to 0.
+    rng = np.random.default_rng(321)
+    N, L = 9, 1000
+    B = (3.0 * np.log(1.0 - rng.random((N, L)))).astype(np.float32)
+    A = B.copy()
+    scale = rng.choice(np.array([0.01, 1.0, 30.0]), (N, L))
+    C = (B + rng.normal(0.0, 1.0, (N, L)) * scale).astype(np.float32)
+    C[0, 0] = B[0, 0] + np.float32(700.0)
+    C[0, 1:40] = B[0, 1:40] + np.linspace(710.0, 720.0, 39, dtype=np.float32)
+    C[1, :40] = B[1, :40] - np.linspace(700.0, 800.0, 40, dtype=np.float32)
+    A[2] = (B[2] + 0.75).astype(np.float32)
+    M = (rng.random((N, L)) < 0.9).astype(np.uint8)
+    for clip in (2.0, 0.5):
+        (stats, pt), _ = run((A, B, C, M), tis_clip=clip, per_token=True)
+        assert stats["BC"]["k3_nonfinite"][0] > 0
+        ref = oracle.per_token(A, B, C, M, clip)
+        got = pt.cpu().numpy()
+        assert np.array_equal(np.isnan(got), np.isnan(ref))
+        fin = ~np.isnan(ref)
+        assert np.array_equal(got[:, 0][fin[:, 0]], ref[:, 0][fin[:, 0]])
+        np.testing.assert_allclose(got[:, 1:][fin[:, 1:]], ref[:, 1:][fin[:, 1:]],
+                                   rtol=1e-6, atol=1e-30)
