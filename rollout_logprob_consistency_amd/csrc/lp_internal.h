@@ -15,6 +15,11 @@ namespace lp {
 constexpr int kTileV = 256;   // vocabulary rows per workgroup tile
 constexpr int kTileT = 256;   // token rows per workgroup tile
 constexpr int kTileK = 64;    // hidden elements per LDS stage
+// Batches of at most this many rows take the streaming kernel (one wave per
+// 128-row half of a vocabulary tile x 32 or 64 tokens, the same per-row
+// arithmetic), which streams W at HBM rate instead of computing 256-token
+// tiles that are mostly padding.
+constexpr int kSkinnyMaxT = 64;
 
 struct ScoreArgs {
   const uint16_t* x;      // [T, ldh] bf16 bits

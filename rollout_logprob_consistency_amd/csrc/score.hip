@@ -48,7 +48,6 @@ constexpr int kWaveV = 128;                  // vocab rows per wave
 constexpr int kWaveT = 128;                  // token columns per wave
 constexpr int kSubV = kWaveV / 32;           // MFMA tiles along vocab
 constexpr int kSubT = kWaveT / 32;           // MFMA tiles along tokens
-constexpr int kChunks = kTileK / 8;          // 16-byte chunks per row per stage
 constexpr int kStageBytes = kTileV * kTileK * 2;     // one operand stage: 32 KiB
 constexpr int kLoads = kStageBytes / 16 / kThreads;  // 16-byte copies per thread per operand
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
@@ -75,16 +74,16 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // order logical tiles in groups of kGroupV vocab tiles with the token tile
 // varying fastest, so the workgroups resident on one XCD share W and X slabs
 // in that XCD's L2.
-__device__ __forceinline__ void tile_of(int b, int n_vt, int n_tt, int& vt, int& tt) {
+__device__ __forceinline__ void tile_of(int b, int n_vt, int n_tt, int group_v, int& vt, int& tt) {
   const int G = n_vt * n_tt;
   const int xcd = b & 7, idx = b >> 3;
   const int per = G >> 3, rem = G & 7;
   const int L = (xcd < rem) ? xcd * (per + 1) + idx
                             : rem * (per + 1) + (xcd - rem) * per + idx;
-  const int group = kGroupV * n_tt;
+  const int group = group_v * n_tt;
   const int g = L / group;
-  const int first = g * kGroupV;
-  const int gv = min(kGroupV, n_vt - first);
+  const int first = g * group_v;
+  const int gv = min(group_v, n_vt - first);
   const int r = L - g * group;
   vt = first + r % gv;
   tt = r / gv;
@@ -129,6 +128,76 @@ __device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t wres, __amdgp
   }
 }
 
+// ---- Epilogue pieces shared by both tile kernels, so that a (token,
+// vocabulary tile) pair goes through the same floating-point operations in the
+// same order whichever kernel scores it. A wave holds kSubV MFMA tiles of 32
+// vocabulary rows for each token column; `v(i, r)` returns the raw accumulator
+// of vocabulary sub-tile i, register r, for the lane's token. MFMA 32x32
+// output layout: lane l holds column (l & 31) and, in register r, row
+// 8 * (r >> 2) + 4 * (l >> 5) + (r & 3).
+
+// Per-token max and sum of exp2 over the wave's 128 rows (lane pair l, l^32).
+// The scale log2(e)/T is positive, so the max of the scaled logits is the
+// scaled max; the scale is folded into the exp2 argument with one FMA.
+template <class Get>
+__device__ __forceinline__ void wave_lse(Get v, float scale2, float& m_out, float& s_out) {
+  const float NEG_INF = -__builtin_inff();
+  float mr = NEG_INF;
+#pragma unroll
+  for (int i = 0; i < kSubV; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mr = fmaxf(mr, v(i, r));
+  mr = fmaxf(mr, __shfl_xor(mr, 32));
+  const float m = mr * scale2;
+  float s = 0.f;
+  if (mr != NEG_INF) {
+#pragma unroll
+    for (int i = 0; i < kSubV; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s += fast_exp2(__builtin_fmaf(v(i, r), scale2, -m));
+  }
+  s += __shfl_xor(s, 32);  // s_l + s_{l^32}: identical in both lanes
+  m_out = m;
+  s_out = s;
+}
+
+// Target gather for token t: exactly one lane of the grid holds (target, t);
+// wv_lo is the first vocabulary row of the wave.
+template <class Get>
+__device__ __forceinline__ void gather_target(Get v, const ScoreArgs& a, int t, int64_t wv_lo,
+                                              int fhalf) {
+  const int64_t tgt = a.ids[t];
+  const int64_t loc = tgt - wv_lo;
+  if (tgt >= 0 && tgt < a.V_true && loc >= 0 && loc < kWaveV) {
+    const int li = (int)loc;
+    const int ti = li >> 5, rr = li & 31;
+    if (((rr >> 2) & 1) == fhalf) {
+      const int tr = ((rr >> 3) << 2) | (rr & 3);
+      float tv = 0.f;
+#pragma unroll
+      for (int i = 0; i < kSubV; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (i == ti && r == tr) tv = v(i, r);
+      a.tval[t] = tv * a.scale2;
+    }
+  }
+}
+
+// Merge of the two 128-row halves of a vocabulary tile, lower half first
+// (m0 is finite: row v0 < V_true lies in the lower half).
+__device__ __forceinline__ void merge_halves(float m0, float s0, float m1, float s1, float& M,
+                                             float& S) {
+  M = fmaxf(m0, m1);
+  S = __builtin_fmaf(s1, fast_exp2(m1 - M), s0 * fast_exp2(m0 - M));  // contraction spelled out
+}
+
+// Does register r of vocabulary sub-tile i hold a row at or past V_true?
+// vlane = first vocabulary row of the wave + 4 * (lane >> 5).
+__device__ __forceinline__ bool past_vocab(int vlane, int i, int r, int V_true) {
+  return vlane + 32 * i + 8 * (r >> 2) + (r & 3) >= V_true;
+}
+
 __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   // LDS: two stages of each operand, 256 rows x 128 B each, the 16-byte chunks
   // of row r XOR-permuted by f(r) (see swz()). Separate objects, so the
@@ -141,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   __shared__ float red_s[2][kTileT];
 
   int vt, tt;
-  tile_of(blockIdx.x, a.n_vt, a.n_tt, vt, tt);
+  tile_of(blockIdx.x, a.n_vt, a.n_tt, kGroupV, vt, tt);
   vt = __builtin_amdgcn_readfirstlane(vt);  // uniform: keep tile state in SGPRs
   tt = __builtin_amdgcn_readfirstlane(tt);
   const int v0 = vt * kTileV, t0 = tt * kTileT;
@@ -309,10 +378,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
 #undef PHASE_FENCE
 
   // ---- Epilogue: per-token online LSE over this wave's 128 vocab rows. ----
-  // MFMA 32x32 output layout: lane l holds column (l & 31) and, in register
-  // r, row 8 * (r >> 2) + 4 * (l >> 5) + (r & 3).
-  const float NEG_INF = -__builtin_inff();
-  const int vlane = v0 + wm * kWaveV + 4 * fhalf;  // + 32 i + 8 (r >> 2) + (r & 3)
+  const int vlane = v0 + wm * kWaveV + 4 * fhalf;
   const bool vtail = v0 + kTileV > a.V_true;
   const int64_t wv_lo = v0 + wm * kWaveV;
 
@@ -322,52 +388,19 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
     for (int i = 0; i < kSubV; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (vlane + 32 * i + 8 * (r >> 2) + (r & 3) >= a.V_true)
+        if (past_vocab(vlane, i, r, a.V_true))
 #pragma unroll
-          for (int j = 0; j < kSubT; ++j) acc[i][j][r] = NEG_INF;
+          for (int j = 0; j < kSubT; ++j) acc[i][j][r] = -__builtin_inff();
   }
 
 #pragma unroll
   for (int j = 0; j < kSubT; ++j) {
     const int tl = wn * kWaveT + j * 32 + frow;
     const int t = t0 + tl;
-    // The scale log2(e)/T is positive, so the max of the scaled logits is the
-    // scaled max; the scale is folded into the exp2 argument with one FMA.
-    float mr = NEG_INF;
-#pragma unroll
-    for (int i = 0; i < kSubV; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mr = fmaxf(mr, acc[i][j][r]);
-    mr = fmaxf(mr, __shfl_xor(mr, 32));
-    const float m = mr * a.scale2;
-    float s = 0.f;
-    if (mr != NEG_INF) {
-#pragma unroll
-      for (int i = 0; i < kSubV; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s += fast_exp2(__builtin_fmaf(acc[i][j][r], a.scale2, -m));
-    }
-    s += __shfl_xor(s, 32);  // s_l + s_{l^32}: identical in both lanes
-
-    // Target gather: exactly one lane of the grid holds (target, t).
-    if (t < a.T) {
-      const int64_t tgt = a.ids[t];
-      const int64_t loc = tgt - wv_lo;
-      if (tgt >= 0 && tgt < a.V_true && loc >= 0 && loc < kWaveV) {
-        const int li = (int)loc;
-        const int ti = li >> 5, rr = li & 31;
-        if (((rr >> 2) & 1) == fhalf) {
-          const int tr = ((rr >> 3) << 2) | (rr & 3);
-          float tv = 0.f;
-#pragma unroll
-          for (int i = 0; i < kSubV; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (i == ti && r == tr) tv = acc[i][j][r];
-          a.tval[t] = tv * a.scale2;
-        }
-      }
-    }
+    auto v = [&](int i, int r) __attribute__((always_inline)) { return acc[i][j][r]; };
+    float m, s;
+    wave_lse(v, a.scale2, m, s);
+    if (t < a.T) gather_target(v, a, t, wv_lo, fhalf);
     if (fhalf == 0) {
       red_m[wm][tl] = m;
       red_s[wm][tl] = s;
@@ -375,20 +408,189 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   }
   __syncthreads();
 
-  // Merge the two vocabulary halves of the tile (lower half first).
   {
     const int tl = tid;
     const int t = t0 + tl;
-    const float m0 = red_m[0][tl], m1 = red_m[1][tl];
-    const float s0 = red_s[0][tl], s1 = red_s[1][tl];
-    const float M = fmaxf(m0, m1);  // m0 is finite: row v0 < V_true is in half 0
-    const float S = s0 * fast_exp2(m0 - M) + s1 * fast_exp2(m1 - M);
+    float M, S;
+    merge_halves(red_m[0][tl], red_s[0][tl], red_m[1][tl], red_s[1][tl], M, S);
     if (t < a.T) {
       a.part_m[(size_t)vt * a.T + t] = M;
       a.part_s[(size_t)vt * a.T + t] = S;
     }
   }
 }
+
+// ---- Streaming kernel for small batches (HBM-bound on W). ----
+// With few rows the product is a stream over W (2 V H bytes) and the 256 x 256
+// tiles would be mostly padding. Here a work item is one 128-row half of a
+// vocabulary tile x 32 ST tokens, computed by a single wave in exactly the
+// placement of the 256 x 256 kernel -- vocabulary row -> (MFMA tile i, lane
+// half, register), token -> MFMA column, the same v_mfma_f32_32x32x16_bf16
+// chain over 16-wide K blocks in ascending order -- and the same per-wave
+// epilogue (wave_lse), so every row's bits match. The wave writes its half's
+// (max, sum) partial; the merge kernel applies merge_halves before folding
+// the tiles, as the 256 x 256 kernel does in LDS.
+//
+// The grid is persistent (a fixed number of one-wave workgroups per CU, each
+// taking items b, b + G, b + 2G, ... with XCD-contiguous numbering, token
+// tiles fastest so the waves of one XCD that share a W half-tile run
+// together). Each wave streams its items' 64-wide K stages (128-byte row
+// segments of W) through a ring of kSmStages LDS slots with direct buffer ->
+// LDS copies, kSmStages - 1 stages in flight, continuing across item
+// boundaries; being alone in its workgroup, a wave only waits on its own
+// vmcnt, never on a barrier. Two slots (four waves per CU) stream faster than
+// deeper rings with fewer waves per CU.
+constexpr int kSmK = 64;                       // hidden elements per stage
+constexpr int kSmStages = 2;                   // ring depth
+constexpr int kSmRowB = kSmK * 2;              // LDS row bytes
+constexpr int kSmNC = kSmRowB / 16;            // 16-byte chunks per row
+constexpr int kSmRPC = 1024 / kSmRowB;         // rows per 1-KiB wave copy
+constexpr int kSmRowsA = kWaveV;               // 128 W rows per item
+constexpr int kSmCopiesA = kSmRowsA * kSmRowB / 1024;
+static_assert(kSmNC == 4 || kSmNC == 8, "64- or 128-byte rows");
+
+// Physical chunk of logical chunk c in row `row`: conflict-free fragment
+// reads for 64-byte rows ((row >> 2) & 3) and 128-byte rows (as in the
+// 256 x 256 kernel).
+__host__ __device__ __forceinline__ int swz_sm(int row, int c) {
+  return kSmNC == 4 ? c ^ ((row >> 2) & 3) : c ^ ((row ^ (row >> 3)) & 7);
+}
+
+template <int ST>
+struct Stream {
+  static constexpr int kTok = 32 * ST;                     // tokens per item
+  static constexpr int kCopiesB = kTok * kSmRowB / 1024;   // 2 ST
+  static constexpr int kCopies = kSmCopiesA + kCopiesB;    // per stage
+  static constexpr int kSlotA = kSmRowsA * kSmRowB;        // 8 KiB
+  static constexpr int kSlotB = kTok * kSmRowB;            // 2 ST KiB
+  static constexpr int kSlot = kSlotA + kSlotB;
+  static constexpr int kLds = kSmStages * kSlot;
+  static_assert((kSmStages - 1) * kCopies <= 63, "vmcnt holds at most 63");
+};
+
+template <int ST>
+__global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_items) {
+  using S = Stream<ST>;
+  __shared__ __attribute__((aligned(1024))) char ring[S::kLds];
+  const int lane = threadIdx.x;
+  const int G = gridDim.x;  // a multiple of 8
+  const int xb = (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3);
+  const int nk = a.H / kSmK;
+  const int n_mine = xb < n_items ? (n_items - xb + G - 1) / G : 0;
+  const int n_stages = n_mine * nk;
+  const uint32_t H2 = (uint32_t)a.H * 2, X2 = (uint32_t)a.ldh * 2;
+  // Copy lane mapping: copy q fills rows kSmRPC q .. + kSmRPC - 1; lane i
+  // writes physical chunk i % kSmNC of row kSmRPC q + i / kSmNC, i.e. the
+  // logical chunk swz_sm(row, i % kSmNC) (the permutation is an involution).
+  const int lrow = lane / kSmNC;
+#define SM_LC(q_) ((uint32_t)(swz_sm(kSmRPC * (q_) + lrow, lane % kSmNC) * 16))
+
+  // Enqueue the copies of flat stage g (item g / nk, K stage g % nk).
+  auto issue = [&](int g) __attribute__((always_inline)) {
+    const int it = g / nk, kt = g - it * nk;
+    const int L = xb + it * G;
+    const int vh = L / a.n_tt, tt = L - vh * a.n_tt;
+    // vh = 2 vt + half. The resource starts at the tile's first row v0 <
+    // V_rows; rows are clamped to the matrix (the upper half of the last
+    // tile may lie wholly past V_rows), results there are discarded.
+    const int v0 = (vh >> 1) * kTileV, t0 = tt * S::kTok;
+    const __amdgpu_buffer_rsrc_t wres =
+        make_rsrc(reinterpret_cast<const char*>(a.w) + (size_t)v0 * H2,
+                  span_bytes((uint64_t)(a.V_rows - v0) * H2));
+    const __amdgpu_buffer_rsrc_t xres =
+        make_rsrc(reinterpret_cast<const char*>(a.x) + (size_t)t0 * X2,
+                  span_bytes((uint64_t)(a.T - t0 - 1) * X2 + H2));
+    lds_char* slot = (lds_char*)ring + (g % kSmStages) * S::kSlot;
+    const int koff = kt * kSmRowB;
+    const int vr0 = (vh & 1) * kWaveV, vmax = a.V_rows - 1 - v0, tmax = a.T - 1 - t0;
+#pragma unroll
+    for (int q = 0; q < kSmCopiesA; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wres, (lds_void*)(slot + q * 1024), 16,
+          (uint32_t)min(vr0 + kSmRPC * q + lrow, vmax) * H2 + SM_LC(q), koff, 0, 0);
+#pragma unroll
+    for (int q = 0; q < S::kCopiesB; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xres, (lds_void*)(slot + S::kSlotA + q * 1024), 16,
+          (uint32_t)min(kSmRPC * q + lrow, tmax) * X2 + SM_LC(q), koff, 0, 0);
+  };
+
+  // Fragment reads: row 32 i + (l & 31) of the half-tile (A) or 32 j + (l & 31)
+  // of the token tile (B), logical chunk 2 s + (l >> 5).
+  const int frow = lane & 31, fhalf = lane >> 5;
+#define SM_RD(row0_, sp_) \
+  ((uint32_t)(((row0_) + frow) * kSmRowB + swz_sm((row0_) + frow, 2 * (sp_) + fhalf) * 16))
+
+  f32x16 acc[kSubV][ST];
+  for (int g = 0; g < kSmStages - 1 && g < n_stages; ++g) issue(g);
+  for (int g = 0; g < n_stages; ++g) {
+    if (g + kSmStages - 1 < n_stages) {
+      issue(g + kSmStages - 1);
+      // Stage g has landed once at most (kSmStages - 1) stages' copies remain.
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (((kSmStages - 1) * S::kCopies) & 15) |
+                                 ((((kSmStages - 1) * S::kCopies) >> 4) << 14));
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
+    const int kt = g % nk;
+    if (kt == 0) {
+#pragma unroll
+      for (int i = 0; i < kSubV; ++i)
+#pragma unroll
+        for (int jj = 0; jj < ST; ++jj)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
+    }
+    const char* slot = ring + (g % kSmStages) * S::kSlot;
+#pragma unroll
+    for (int sp = 0; sp < kSmK / 16; ++sp) {
+      bf16x8 fa[kSubV], fb[ST];
+#pragma unroll
+      for (int i = 0; i < kSubV; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8*>(slot + SM_RD(32 * i, sp));
+#pragma unroll
+      for (int jj = 0; jj < ST; ++jj)
+        fb[jj] = *reinterpret_cast<const bf16x8*>(slot + S::kSlotA + SM_RD(32 * jj, sp));
+#pragma unroll
+      for (int i = 0; i < kSubV; ++i)
+#pragma unroll
+        for (int jj = 0; jj < ST; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[jj], acc[i][jj], 0, 0, 0);
+    }
+    if (kt == nk - 1) {
+      const int L = xb + (g / nk) * G;
+      const int vh = L / a.n_tt, tt = L - vh * a.n_tt;
+      const int vbase = vh * kWaveV, t0 = tt * S::kTok;
+      const int vlane = vbase + 4 * fhalf;
+      if (vbase + kWaveV > a.V_true) {
+#pragma unroll
+        for (int i = 0; i < kSubV; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (past_vocab(vlane, i, r, a.V_true))
+#pragma unroll
+              for (int jj = 0; jj < ST; ++jj) acc[i][jj][r] = -__builtin_inff();
+      }
+#pragma unroll
+      for (int jj = 0; jj < ST; ++jj) {
+        const int t = t0 + 32 * jj + frow;
+        auto v = [&](int i, int r) __attribute__((always_inline)) { return acc[i][jj][r]; };
+        float m, s;
+        wave_lse(v, a.scale2, m, s);
+        if (t < a.T) {
+          gather_target(v, a, t, vbase, fhalf);
+          if (fhalf == 0) {
+            a.part_m[(size_t)vh * a.T + t] = m;
+            a.part_s[(size_t)vh * a.T + t] = s;
+          }
+        }
+      }
+    }
+  }
+}
+
+#undef SM_LC
+#undef SM_RD
 
 // Merge of the per-tile partials. A workgroup takes 64 consecutive tokens
 // (one per lane, so every partial row is read coalesced) and 8 waves; wave w
@@ -399,10 +601,14 @@ constexpr int kMergeSegs = 8;
 
 __device__ __forceinline__ void lse_fold(float& M, float& S, float m, float s) {
   const float Mn = fmaxf(M, m);
-  S = S * fast_exp2(M - Mn) + s * fast_exp2(m - Mn);  // exp2(-inf) = 0 on first use
+  // exp2(-inf) = 0 on first use; the contraction is spelled out.
+  S = __builtin_fmaf(s, fast_exp2(m - Mn), S * fast_exp2(M - Mn));
   M = Mn;
 }
 
+// kHalves: the partials are per 128-row half of each vocabulary tile (rows
+// 2 vt and 2 vt + 1), merged with merge_halves first.
+template <bool kHalves>
 __global__ __launch_bounds__(64 * kMergeSegs) void lse_merge_kernel(ScoreArgs a) {
   __shared__ float seg_m[kMergeSegs][64];
   __shared__ float seg_s[kMergeSegs][64];
@@ -414,9 +620,18 @@ __global__ __launch_bounds__(64 * kMergeSegs) void lse_merge_kernel(ScoreArgs a)
   if (t < a.T) {
     const float* pm = a.part_m + t;
     const float* ps = a.part_s + t;
+    if (kHalves) {
+      for (int vt = lo; vt < hi; ++vt) {
+        float m, s;
+        merge_halves(pm[(size_t)(2 * vt) * a.T], ps[(size_t)(2 * vt) * a.T],
+                     pm[(size_t)(2 * vt + 1) * a.T], ps[(size_t)(2 * vt + 1) * a.T], m, s);
+        lse_fold(M, S, m, s);
+      }
+    } else {
 #pragma unroll 4
-    for (int vt = lo; vt < hi; ++vt)
-      lse_fold(M, S, pm[(size_t)vt * a.T], ps[(size_t)vt * a.T]);
+      for (int vt = lo; vt < hi; ++vt)
+        lse_fold(M, S, pm[(size_t)vt * a.T], ps[(size_t)vt * a.T]);
+    }
   }
   seg_m[seg][lane] = M;
   seg_s[seg][lane] = S;
@@ -437,23 +652,51 @@ __global__ __launch_bounds__(64 * kMergeSegs) void lse_merge_kernel(ScoreArgs a)
 
 }  // namespace
 
+// Streaming kernel choice: items of 32 ST tokens; 0 = the 256 x 256 kernel.
+static int stream_tokens(int64_t T) {
+  if (T <= 32) return 1;
+  if (T <= kSkinnyMaxT) return 2;
+  return 0;
+}
+
 ScoreWorkspace score_workspace_layout(int64_t T, int64_t V_true) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t n_vt = (size_t)((V_true + kTileV - 1) / kTileV);
+  const size_t rows = stream_tokens(T) ? 2 * n_vt : n_vt;  // half-tile partials
   ScoreWorkspace w;
   w.off_m = 0;
-  w.off_s = up(w.off_m + n_vt * (size_t)T * sizeof(float));
-  w.off_t = up(w.off_s + n_vt * (size_t)T * sizeof(float));
+  w.off_s = up(w.off_m + rows * (size_t)T * sizeof(float));
+  w.off_t = up(w.off_s + rows * (size_t)T * sizeof(float));
   w.total = up(w.off_t + (size_t)T * sizeof(float));
   return w;
 }
 
+template <int ST>
+static void launch_stream(ScoreArgs a, hipStream_t stream) {
+  a.n_tt = (a.T + 32 * ST - 1) / (32 * ST);
+  const int n_items = 2 * a.n_vt * a.n_tt;
+  // Workgroups (one wave each) per CU: as many as the LDS ring allows.
+  const int per_cu = (160 * 1024) / Stream<ST>::kLds;
+  const int grid = 256 * (per_cu < 8 ? per_cu : 8);
+  hipLaunchKernelGGL(score_stream_kernel<ST>, dim3(grid), dim3(64), 0, stream, a, n_items);
+}
+
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
-  const unsigned grid = (unsigned)a.n_vt * (unsigned)a.n_tt;
-  hipLaunchKernelGGL(score_tile_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  const int st = stream_tokens(a.T);
+  if (st == 1) launch_stream<1>(a, stream);
+  else if (st == 2) launch_stream<2>(a, stream);
+  else {
+    const unsigned grid = (unsigned)a.n_vt * (unsigned)a.n_tt;
+    hipLaunchKernelGGL(score_tile_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lse_merge_kernel, dim3((a.T + 63) / 64), dim3(64 * kMergeSegs), 0, stream, a);
+  if (st)
+    hipLaunchKernelGGL(lse_merge_kernel<true>, dim3((a.T + 63) / 64), dim3(64 * kMergeSegs), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(lse_merge_kernel<false>, dim3((a.T + 63) / 64), dim3(64 * kMergeSegs), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
