@@ -64,14 +64,19 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-rows", type=int, default=4096,
+    ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="rows of the batch the fp64 oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep-n", type=int, default=4096,
-                    help="sequences in the comparison bandwidth probe (L = 2304)")
-    ap.add_argument("--mode", choices=("bench", "score", "copy"), default="bench",
-                    help="score: only `steps` lp_score calls on the benchmark batch (for "
-                         "profilers); copy: one plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--sweep-n", type=str, default="512,4096",
+                    help="sequence counts of the comparison bandwidth probe (L = 2304)")
+    ap.add_argument("--small-batches", type=str, default="1,7,64",
+                    help="row counts at which lp_score is timed as a stream over W")
+    ap.add_argument("--mode", choices=("bench", "score", "small", "compare", "copy"),
+                    default="bench",
+                    help="score: only `steps` lp_score calls on the benchmark batch; small: "
+                         "`steps` lp_score calls on its first row; compare: `steps` lp_compare "
+                         "calls at N=4096, L=2304 (these three for profilers); copy: one plain "
+                         "1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the scoring path has no cross-GPU "
@@ -130,6 +135,21 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"bench: {args.steps} lp_score calls done")
         return 0
+    if args.mode == "small":
+        for _ in range(args.steps):
+            lp.score(x[:1], w, ids[:1], out=out[:1], workspace=ws)
+        torch.cuda.synchronize()
+        log(f"bench: {args.steps} one-row lp_score calls done")
+        return 0
+    if args.mode == "compare":
+        sc = synth.compare_sweep_case(N=4096)
+        tA, tB, tC, tM = (torch.from_numpy(a).to(dev) for a in (sc.A, sc.B, sc.C, sc.mask))
+        sbuf = torch.empty(3 * sc.N * lp.SEQ_STATS_DTYPE.itemsize, dtype=torch.uint8, device=dev)
+        for _ in range(args.steps):
+            lp.compare_raw(tA, tB, tC, tM, out=sbuf)
+        torch.cuda.synchronize()
+        log(f"bench: {args.steps} lp_compare calls (N=4096, L=2304) done")
+        return 0
 
     def step(ev=None):
         if ev is not None:
@@ -168,25 +188,47 @@ def main() -> int:
         f"{max(score_ms):.3f}) = {achieved:.1f} TFLOP/s = {100 * achieved / PEAK_BF16_TFLOPS:.1f}% "
         f"of bf16 peak; lp_compare {cmp_avg * 1e6:.1f} us")
 
-    # Comparison bandwidth probe at a size that is not launch-latency bound.
-    sweep = None
-    if args.sweep_n > 0:
-        sc = synth.compare_sweep_case(N=args.sweep_n)
-        tA, tB, tC, tM = (torch.from_numpy(a).to(dev) for a in (sc.A, sc.B, sc.C, sc.mask))
-        sbuf = torch.empty(3 * sc.N * lp.SEQ_STATS_DTYPE.itemsize, dtype=torch.uint8, device=dev)
+    def median_us(fn, reps=20):
+        """Median / min / max duration of fn() in microseconds (HIP events on
+        the current stream, 3 untimed calls first)."""
         for _ in range(3):
-            lp.compare_raw(tA, tB, tC, tM, out=sbuf)
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
+            fn()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
         for e in evs:
             e[0].record()
-            lp.compare_raw(tA, tB, tC, tM, out=sbuf)
+            fn()
             e[1].record()
         torch.cuda.synchronize()
-        us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+        t = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in evs)
+        return t[len(t) // 2], t[0], t[-1]
+
+    # Small batches: the product is a stream over W (HBM-bound); report the
+    # algorithmic bytes (W, the rows, ids and outputs) per second.
+    small = []
+    for b in (int(v) for v in args.small_batches.split(",") if v):
+        xs, ids_s = x[:b].contiguous(), ids[:b].contiguous()
+        out_s = torch.empty(b, dtype=torch.float32, device=dev)
+        ws_s = torch.empty(lp.score_workspace_bytes(b, H, V), dtype=torch.uint8, device=dev)
+        med, lo, hi = median_us(lambda: lp.score(xs, w, ids_s, out=out_s, workspace=ws_s))
+        nbytes = 2.0 * V * H + 2.0 * b * H + 16.0 * b
+        small.append({"rows": b, "us": round(med, 2), "min_us": round(lo, 2), "max_us": round(hi, 2),
+                      "GBps": round(nbytes / med / 1e3, 1),
+                      "frac_hbm": round(nbytes / med / 1e3 / PEAK_HBM_GBPS, 4)})
+        log(f"bench: lp_score {b} rows: {med:.1f} us = {nbytes / med / 1e3:.1f} GB/s")
+
+    # Comparison bandwidth probe at sizes that are not launch-latency bound.
+    sweep = []
+    for n_seq in (int(v) for v in args.sweep_n.split(",") if v):
+        sc = synth.compare_sweep_case(N=n_seq)
+        tA, tB, tC, tM = (torch.from_numpy(a).to(dev) for a in (sc.A, sc.B, sc.C, sc.mask))
+        sbuf = torch.empty(3 * sc.N * lp.SEQ_STATS_DTYPE.itemsize, dtype=torch.uint8, device=dev)
+        med, lo, hi = median_us(lambda: lp.compare_raw(tA, tB, tC, tM, out=sbuf))
         nbytes = 13.0 * sc.N * sc.L
-        sweep = {"N": sc.N, "L": sc.L, "us": round(us, 2),
-                 "GBps": round(nbytes / us / 1e3, 1), "bytes_per_token": 13}
-        log(f"bench: lp_compare N={sc.N} L={sc.L}: {us:.1f} us = {nbytes / us / 1e3:.1f} GB/s")
+        sweep.append({"N": sc.N, "L": sc.L, "us": round(med, 2), "min_us": round(lo, 2),
+                      "max_us": round(hi, 2), "GBps": round(nbytes / med / 1e3, 1),
+                      "frac_hbm": round(nbytes / med / 1e3 / PEAK_HBM_GBPS, 4),
+                      "bytes_per_token": 13})
+        log(f"bench: lp_compare N={sc.N} L={sc.L}: {med:.1f} us = {nbytes / med / 1e3:.1f} GB/s")
         del tA, tB, tC, tM
 
     cpu = None
@@ -228,7 +270,11 @@ def main() -> int:
                      "traffic": traffic},
         "cpu_baseline": cpu,
         "kernels": {"lp_score_ms": round(score_avg * 1e3, 4),
+                    "lp_score_ms_median": round(float(np.median(score_ms)), 4),
+                    "lp_score_ms_min": round(min(score_ms), 4),
+                    "lp_score_ms_max": round(max(score_ms), 4),
                     "lp_compare_us": round(cmp_avg * 1e6, 2)},
+        "small_batch": small,
         "compare_sweep": sweep,
     }
     print(json.dumps(rec), flush=True)

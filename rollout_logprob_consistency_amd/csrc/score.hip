@@ -170,15 +170,16 @@ __device__ __forceinline__ void gather_target(Get v, const ScoreArgs& a, int t, 
   const int64_t loc = tgt - wv_lo;
   if (tgt >= 0 && tgt < a.V_true && loc >= 0 && loc < kWaveV) {
     const int li = (int)loc;
-    const int ti = li >> 5, rr = li & 31;
+    const int rr = li & 31;
     if (((rr >> 2) & 1) == fhalf) {
-      const int tr = ((rr >> 3) << 2) | (rr & 3);
+      // Flat (sub-tile, register) index of the target row; a branch-free
+      // select over the lane's values picks it.
+      const int k = (li >> 5) * 16 + (((rr >> 3) << 2) | (rr & 3));
       float tv = 0.f;
 #pragma unroll
       for (int i = 0; i < kSubV; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (i == ti && r == tr) tv = v(i, r);
+        for (int r = 0; r < 16; ++r) tv = (k == i * 16 + r) ? v(i, r) : tv;
       a.tval[t] = tv * a.scale2;
     }
   }
@@ -192,11 +193,13 @@ __device__ __forceinline__ void merge_halves(float m0, float s0, float m1, float
   S = __builtin_fmaf(s1, fast_exp2(m1 - M), s0 * fast_exp2(m0 - M));  // contraction spelled out
 }
 
-// Does register r of vocabulary sub-tile i hold a row at or past V_true?
-// vlane = first vocabulary row of the wave + 4 * (lane >> 5).
-__device__ __forceinline__ bool past_vocab(int vlane, int i, int r, int V_true) {
-  return vlane + 32 * i + 8 * (r >> 2) + (r & 3) >= V_true;
-}
+// Rows at or past V_true (only in the last vocabulary tile) read as -inf:
+// register r of vocabulary sub-tile i holds row vlane + 32 i + 8 (r >> 2) +
+// (r & 3), vlane = first vocabulary row of the wave + 4 (lane >> 5). The
+// epilogue takes this masked view only in that tile (a uniform branch), so
+// the accumulators are never rewritten.
+#define LP_MASKED(x_, vlane_, i_, r_, V_) \
+  (((vlane_) + 32 * (i_) + 8 * ((r_) >> 2) + ((r_) & 3) >= (V_)) ? -__builtin_inff() : (x_))
 
 __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   // LDS: two stages of each operand, 256 rows x 128 B each, the 16-byte chunks
@@ -382,25 +385,18 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   const bool vtail = v0 + kTileV > a.V_true;
   const int64_t wv_lo = v0 + wm * kWaveV;
 
-  // Rows at or past V_true (only in the last vocabulary tile) become -inf.
-  if (vtail) {
-#pragma unroll
-    for (int i = 0; i < kSubV; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (past_vocab(vlane, i, r, a.V_true))
-#pragma unroll
-          for (int j = 0; j < kSubT; ++j) acc[i][j][r] = -__builtin_inff();
-  }
-
 #pragma unroll
   for (int j = 0; j < kSubT; ++j) {
     const int tl = wn * kWaveT + j * 32 + frow;
     const int t = t0 + tl;
     auto v = [&](int i, int r) __attribute__((always_inline)) { return acc[i][j][r]; };
+    auto vm = [&](int i, int r) __attribute__((always_inline)) {
+      return LP_MASKED(acc[i][j][r], vlane, i, r, a.V_true);
+    };
     float m, s;
-    wave_lse(v, a.scale2, m, s);
-    if (t < a.T) gather_target(v, a, t, wv_lo, fhalf);
+    if (vtail) wave_lse(vm, a.scale2, m, s);
+    else wave_lse(v, a.scale2, m, s);
+    if (t < a.T) gather_target(v, a, t, wv_lo, fhalf);  // targets lie below V_true
     if (fhalf == 0) {
       red_m[wm][tl] = m;
       red_s[wm][tl] = s;
@@ -562,23 +558,19 @@ __global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_ite
       const int vh = L / a.n_tt, tt = L - vh * a.n_tt;
       const int vbase = vh * kWaveV, t0 = tt * S::kTok;
       const int vlane = vbase + 4 * fhalf;
-      if (vbase + kWaveV > a.V_true) {
-#pragma unroll
-        for (int i = 0; i < kSubV; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (past_vocab(vlane, i, r, a.V_true))
-#pragma unroll
-              for (int jj = 0; jj < ST; ++jj) acc[i][jj][r] = -__builtin_inff();
-      }
+      const bool vtail = vbase + kWaveV > a.V_true;
 #pragma unroll
       for (int jj = 0; jj < ST; ++jj) {
         const int t = t0 + 32 * jj + frow;
         auto v = [&](int i, int r) __attribute__((always_inline)) { return acc[i][jj][r]; };
+        auto vm = [&](int i, int r) __attribute__((always_inline)) {
+          return LP_MASKED(acc[i][jj][r], vlane, i, r, a.V_true);
+        };
         float m, s;
-        wave_lse(v, a.scale2, m, s);
+        if (vtail) wave_lse(vm, a.scale2, m, s);
+        else wave_lse(v, a.scale2, m, s);
         if (t < a.T) {
-          gather_target(v, a, t, vbase, fhalf);
+          gather_target(v, a, t, vbase, fhalf);  // targets lie below V_true
           if (fhalf == 0) {
             a.part_m[(size_t)vh * a.T + t] = m;
             a.part_s[(size_t)vh * a.T + t] = s;
@@ -621,6 +613,7 @@ __global__ __launch_bounds__(64 * kMergeSegs) void lse_merge_kernel(ScoreArgs a)
     const float* pm = a.part_m + t;
     const float* ps = a.part_s + t;
     if (kHalves) {
+#pragma unroll 8
       for (int vt = lo; vt < hi; ++vt) {
         float m, s;
         merge_halves(pm[(size_t)(2 * vt) * a.T], ps[(size_t)(2 * vt) * a.T],
@@ -628,7 +621,7 @@ __global__ __launch_bounds__(64 * kMergeSegs) void lse_merge_kernel(ScoreArgs a)
         lse_fold(M, S, m, s);
       }
     } else {
-#pragma unroll 4
+#pragma unroll 8
       for (int vt = lo; vt < hi; ++vt)
         lse_fold(M, S, pm[(size_t)vt * a.T], ps[(size_t)vt * a.T]);
     }
