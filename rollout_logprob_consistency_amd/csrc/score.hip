@@ -585,11 +585,12 @@ __global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_ite
 #undef SM_RD
 
 // Merge of the per-tile partials. A workgroup takes 64 consecutive tokens
-// (one per lane, so every partial row is read coalesced) and 8 waves; wave w
-// folds the vocabulary tiles of segment w in ascending order, then the 8
-// segment results are folded in segment order. Segment bounds depend only on
-// the number of vocabulary tiles, so the order is the same for every batch.
-constexpr int kMergeSegs = 8;
+// (one per lane, so every partial row is read coalesced) and kMergeSegs
+// waves; wave w folds the vocabulary tiles of segment w in ascending order,
+// then the segment results are folded in segment order. Segment bounds depend
+// only on the number of vocabulary tiles, so the order is the same for every
+// batch.
+constexpr int kMergeSegs = 16;
 
 __device__ __forceinline__ void lse_fold(float& M, float& S, float m, float s) {
   const float Mn = fmaxf(M, m);
