@@ -188,18 +188,22 @@ def main() -> int:
         f"{max(score_ms):.3f}) = {achieved:.1f} TFLOP/s = {100 * achieved / PEAK_BF16_TFLOPS:.1f}% "
         f"of bf16 peak; lp_compare {cmp_avg * 1e6:.1f} us")
 
-    def median_us(fn, reps=20):
-        """Median / min / max duration of fn() in microseconds (HIP events on
-        the current stream, 3 untimed calls first)."""
+    def median_us(fn, calls=20, reps=7):
+        """Per-call duration of fn() in microseconds: `calls` back-to-back
+        calls between two HIP events on the current stream, repeated `reps`
+        times; returns the median, min and max of the per-call averages (3
+        untimed calls first). Back-to-back calls keep short kernels from being
+        timed together with the host's launch gaps."""
         for _ in range(3):
             fn()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
         for e in evs:
             e[0].record()
-            fn()
+            for _ in range(calls):
+                fn()
             e[1].record()
         torch.cuda.synchronize()
-        t = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in evs)
+        t = sorted(e[0].elapsed_time(e[1]) * 1e3 / calls for e in evs)
         return t[len(t) // 2], t[0], t[-1]
 
     # Small batches: the product is a stream over W (HBM-bound); report the
@@ -222,7 +226,11 @@ def main() -> int:
         sc = synth.compare_sweep_case(N=n_seq)
         tA, tB, tC, tM = (torch.from_numpy(a).to(dev) for a in (sc.A, sc.B, sc.C, sc.mask))
         sbuf = torch.empty(3 * sc.N * lp.SEQ_STATS_DTYPE.itemsize, dtype=torch.uint8, device=dev)
-        med, lo, hi = median_us(lambda: lp.compare_raw(tA, tB, tC, tM, out=sbuf))
+        lp.compare_raw(tA, tB, tC, tM, out=sbuf)  # argument checks once, then the bare C call
+        cargs = (tA.data_ptr(), tB.data_ptr(), tC.data_ptr(), tM.data_ptr(), sc.N, sc.L, sc.L,
+                 2.0, -1.0, sbuf.data_ptr(), None, torch.cuda.current_stream().cuda_stream)
+        c_compare = lp._lib.lib().lp_compare
+        med, lo, hi = median_us(lambda: c_compare(*cargs))
         nbytes = 13.0 * sc.N * sc.L
         sweep.append({"N": sc.N, "L": sc.L, "us": round(med, 2), "min_us": round(lo, 2),
                       "max_us": round(hi, 2), "GBps": round(nbytes / med / 1e3, 1),
