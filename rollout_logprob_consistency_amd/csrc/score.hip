@@ -12,20 +12,24 @@
 // only the invariant is kept here, the kernel is designed for CDNA4:
 //
 //  * One workgroup = 4 waves computes a 256 (vocab) x 256 (token) tile of
-//    Z^T = W . X^T with v_mfma_f32_32x32x16_bf16, fp32 accumulation, the whole
-//    hidden dimension in ascending 64-wide LDS stages (no split-K). Each wave
-//    owns 128 x 128 outputs = 4 x 4 MFMA tiles (256 accumulator registers).
-//    Tokens are the MFMA "N" dimension, so every lane holds one token column
-//    and 16 vocabulary rows per MFMA tile: the vocabulary reduction is mostly
-//    inside a lane.
-//  * Operand tiles are staged global -> registers -> LDS, double buffered,
-//    one barrier per stage; 16-byte chunks are XOR-swizzled per row so that
-//    the ds_read_b128 fragment reads do not collide on LDS banks.
+//    Z^T = W . X^T with v_mfma_f32_16x16x32_bf16, fp32 accumulation, the whole
+//    hidden dimension in ascending 32-wide MFMA steps (no split-K). Each wave
+//    owns 128 x 128 outputs = 8 x 8 MFMA tiles (256 accumulator registers).
+//    Tokens are the MFMA "N" dimension: a lane holds one token column and 32
+//    vocabulary rows, so the vocabulary reduction is mostly inside a lane.
+//    The 16x16x32 shape moves half as many accumulator bytes per flop as
+//    32x32x16; at the same work the chip holds a higher clock with it.
+//  * Operand stages go from HBM/L2 straight into LDS (buffer_load ... lds, no
+//    VGPR round trip) through a ring of 5 units of 32 KiB (one operand's 64-wide
+//    K stage each); the 16-byte chunks of each 128-byte row are XOR-permuted so
+//    the ds_read_b128 fragment reads do not collide on LDS banks. Copies,
+//    fragment reads and MFMAs are issued in a fixed interleave with one
+//    barrier per K stage.
 //  * Epilogue: scale by log2(e)/temperature, mask rows >= V_true to -inf,
-//    per-token max and sum of exp2 over the lane's 64 values, the lane pair
-//    (l, l^32) and the two vocabulary waves, in a fixed order; write one
-//    (max, sum) partial per (vocabulary tile, token); the single lane that
-//    holds the target logit writes it. Logits never reach memory.
+//    per-token max and sum of exp2 over the lane's 32 values, the lanes
+//    (l, l^16, l^32, l^48) and the two vocabulary waves, in a fixed order;
+//    write one (max, sum) partial per (vocabulary tile, token); the single
+//    lane that holds the target logit writes it. Logits never reach memory.
 //  * A second kernel merges the vocabulary tiles of each token in ascending
 //    tile order and writes logprob and log-sum-exp in nats.
 //
@@ -41,33 +45,39 @@ namespace lp {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaveV = 128;                  // vocab rows per wave
 constexpr int kWaveT = 128;                  // token columns per wave
-constexpr int kSubV = kWaveV / 32;           // MFMA tiles along vocab
-constexpr int kSubT = kWaveT / 32;           // MFMA tiles along tokens
-constexpr int kStageBytes = kTileV * kTileK * 2;     // one operand stage: 32 KiB
-constexpr int kLoads = kStageBytes / 16 / kThreads;  // 16-byte copies per thread per operand
+constexpr int kSubV = kWaveV / 16;           // 16-row MFMA tiles along vocab (8)
+constexpr int kSubT = kWaveT / 16;           // 16-column MFMA tiles along tokens (8)
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
 // lgkmcnt [11:8]); only vmcnt is constrained.
 constexpr int kWaitVm0 = 0x0F70;             // vmcnt(0)
+constexpr int kWaitVm8 = 0x0F78;             // vmcnt(8)
 constexpr int kGroupV = 4;                   // vocab tiles per scheduling group
 constexpr float kLn2 = 0.693147180559945309f;
 
-static_assert(kTileV == kTileT, "A and B stages share one layout");
+static_assert(kTileV == kTileT, "W and X stages share one layout");
 static_assert(kTileV == 2 * kWaveV && kTileT == 2 * kWaveT, "2 x 2 waves");
-static_assert(kLoads * kThreads * 16 == kStageBytes, "stage split");
+static_assert(kTileK == 64, "128-byte LDS rows");
 
-// Physical 16-byte chunk of logical chunk `c` in tile row `row`.
-__device__ __forceinline__ int swz(int row, int c) {
-  return c ^ ((row ^ (row >> 3)) & 7);
-}
+// Physical 16-byte chunk of logical chunk `c` (hidden elements 8 c .. 8 c + 7
+// of a 64-wide stage) in LDS row `row`. A fragment read (ds_read_b128) has
+// lane l read row 16 u + (l & 15) at chunk 4 h + (l >> 4); with the chunk
+// XOR-permuted by (row & 7) these reads measure SQ_LDS_BANK_CONFLICT = 0 on
+// gfx950 (the permutation (row ^ (row >> 3)) & 7 measures two-way conflicts
+// on every read for this pattern).
+__host__ __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// One MFMA step: 16 vocabulary rows x 16 tokens x 32 hidden elements.
+__device__ __forceinline__ f32x4 mma(const bf16x8& w, const bf16x8& x, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, x, c, 0, 0, 0);
+}
 
 // Workgroup id -> (vocab tile, token tile). The hardware deals workgroups to
 // the 8 XCDs round-robin; give each XCD a contiguous run of logical tiles, and
@@ -112,33 +122,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
 }
 
-// Enqueue copies j0 <= j < j1 of one K stage of both operands into the LDS
-// stage buffers dstA (W) and dstB (X).
-__device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t wres, __amdgpu_buffer_rsrc_t xres,
-                                            const uint32_t (&offA)[kLoads],
-                                            const uint32_t (&offB)[kLoads], lds_char* dstA,
-                                            lds_char* dstB, int wave, int koff, int j0, int j1) {
-#pragma unroll
-  for (int j = j0; j < j1; ++j) {
-    const int q = 4 * j + wave;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void*)(dstA + q * 1024), 16, offA[j],
-                                             koff, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void*)(dstB + q * 1024), 16, offB[j],
-                                             koff, 0, 0);
-  }
-}
-
 // ---- Epilogue pieces shared by both tile kernels, so that a (token,
 // vocabulary tile) pair goes through the same floating-point operations in the
-// same order whichever kernel scores it. A wave holds kSubV MFMA tiles of 32
-// vocabulary rows for each token column; `v(i, r)` returns the raw accumulator
-// of vocabulary sub-tile i, register r, for the lane's token. MFMA 32x32
-// output layout: lane l holds column (l & 31) and, in register r, row
-// 8 * (r >> 2) + 4 * (l >> 5) + (r & 3).
+// same order whichever kernel scores it. A wave holds kSubV MFMA tiles of 16
+// vocabulary rows for each token column; `v(i, r)` returns the raw
+// accumulator of vocabulary tile i, register r, for the lane's token. MFMA
+// 16x16 output layout: lane l holds column (l & 15) and, in register r, row
+// 4 (l >> 4) + r; the four lanes l & 15 + 16 g (g = 0..3) share a token.
 
-// Per-token max and sum of exp2 over the wave's 128 rows (lane pair l, l^32).
-// The scale log2(e)/T is positive, so the max of the scaled logits is the
-// scaled max; the scale is folded into the exp2 argument with one FMA.
+// Per-token max and sum of exp2 over the wave's 128 rows (lanes l, l^16,
+// l^32, l^48). The scale log2(e)/T is positive, so the max of the scaled
+// logits is the scaled max; the scale is folded into the exp2 argument with
+// one FMA. The butterfly adds the same two values in both lanes of each step,
+// so all four lanes end with the same bits.
 template <class Get>
 __device__ __forceinline__ void wave_lse(Get v, float scale2, float& m_out, float& s_out) {
   const float NEG_INF = -__builtin_inff();
@@ -146,7 +142,8 @@ __device__ __forceinline__ void wave_lse(Get v, float scale2, float& m_out, floa
 #pragma unroll
   for (int i = 0; i < kSubV; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mr = fmaxf(mr, v(i, r));
+    for (int r = 0; r < 4; ++r) mr = fmaxf(mr, v(i, r));
+  mr = fmaxf(mr, __shfl_xor(mr, 16));
   mr = fmaxf(mr, __shfl_xor(mr, 32));
   const float m = mr * scale2;
   float s = 0.f;
@@ -154,32 +151,32 @@ __device__ __forceinline__ void wave_lse(Get v, float scale2, float& m_out, floa
 #pragma unroll
     for (int i = 0; i < kSubV; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s += fast_exp2(__builtin_fmaf(v(i, r), scale2, -m));
+      for (int r = 0; r < 4; ++r) s += fast_exp2(__builtin_fmaf(v(i, r), scale2, -m));
   }
-  s += __shfl_xor(s, 32);  // s_l + s_{l^32}: identical in both lanes
+  s += __shfl_xor(s, 16);
+  s += __shfl_xor(s, 32);
   m_out = m;
   s_out = s;
 }
 
 // Target gather for token t: exactly one lane of the grid holds (target, t);
-// wv_lo is the first vocabulary row of the wave.
+// wv_lo is the first vocabulary row of the wave, lg = lane >> 4.
 template <class Get>
 __device__ __forceinline__ void gather_target(Get v, const ScoreArgs& a, int t, int64_t wv_lo,
-                                              int fhalf) {
+                                              int lg) {
   const int64_t tgt = a.ids[t];
   const int64_t loc = tgt - wv_lo;
   if (tgt >= 0 && tgt < a.V_true && loc >= 0 && loc < kWaveV) {
     const int li = (int)loc;
-    const int rr = li & 31;
-    if (((rr >> 2) & 1) == fhalf) {
-      // Flat (sub-tile, register) index of the target row; a branch-free
-      // select over the lane's values picks it.
-      const int k = (li >> 5) * 16 + (((rr >> 3) << 2) | (rr & 3));
+    if (((li >> 2) & 3) == lg) {
+      // Flat (tile, register) index of the target row; a branch-free select
+      // over the lane's values picks it.
+      const int k = (li >> 4) * 4 + (li & 3);
       float tv = 0.f;
 #pragma unroll
       for (int i = 0; i < kSubV; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tv = (k == i * 16 + r) ? v(i, r) : tv;
+        for (int r = 0; r < 4; ++r) tv = (k == i * 4 + r) ? v(i, r) : tv;
       a.tval[t] = tv * a.scale2;
     }
   }
@@ -194,23 +191,42 @@ __device__ __forceinline__ void merge_halves(float m0, float s0, float m1, float
 }
 
 // Rows at or past V_true (only in the last vocabulary tile) read as -inf:
-// register r of vocabulary sub-tile i holds row vlane + 32 i + 8 (r >> 2) +
-// (r & 3), vlane = first vocabulary row of the wave + 4 (lane >> 5). The
-// epilogue takes this masked view only in that tile (a uniform branch), so
-// the accumulators are never rewritten.
+// register r of vocabulary tile i holds row vlane + 16 i + r, vlane = first
+// vocabulary row of the wave + 4 (lane >> 4). The epilogue takes this masked
+// view only in that tile (a uniform branch), so the accumulators are never
+// rewritten.
 #define LP_MASKED(x_, vlane_, i_, r_, V_) \
-  (((vlane_) + 32 * (i_) + 8 * ((r_) >> 2) + ((r_) & 3) >= (V_)) ? -__builtin_inff() : (x_))
+  (((vlane_) + 16 * (i_) + (r_) >= (V_)) ? -__builtin_inff() : (x_))
+
+// One 1-KiB buffer -> LDS copy (buffer_load_dwordx4 ... lds): lane i moves 16
+// bytes from rsrc + voff + soff to LDS byte address lds + 16 i. Written as
+// inline assembly so that the compiler does not treat the asynchronous LDS
+// write as aliasing every later LDS read (it would wait for every copy in
+// flight before each read); the ring's explicit vmcnt waits and barriers order
+// copies and reads instead. The LDS address goes in M0 (an operand of the
+// statement); an M0 write needs one wait state before an LDS-DMA load.
+__device__ __forceinline__ void copy_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, uint32_t voff,
+                                         uint32_t soff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
+               : "memory");
+}
+
+// Ring geometry of the 256 x 256 kernel: a unit is one operand's K stage
+// (256 rows x 64 hidden elements = 128-byte rows, 32 KiB); unit 2k is the W
+// stage k, unit 2k + 1 the X stage k; unit u lives in slot u mod kSlots.
+constexpr int kSlots = 5;
+constexpr int kRowB = kTileK * 2;            // 128 B
+constexpr int kSlotB = kTileV * kRowB;       // 32 KiB
+constexpr int kCopiesU = kSlotB / 1024 / 4;  // 1-KiB copies per wave per unit
+static_assert(kCopiesU == 8, "copy schedule assumes 8 copies per wave per unit");
+static_assert(kSlots * kSlotB <= 160 * 1024, "LDS");
 
 __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
-  // LDS: two stages of each operand, 256 rows x 128 B each, the 16-byte chunks
-  // of row r XOR-permuted by f(r) (see swz()). Separate objects, so the
-  // compiler can tell the copies into one stage from the reads of the other.
-  __shared__ __attribute__((aligned(1024))) char sA0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char sA1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char sB0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char sB1[kStageBytes];
-  __shared__ float red_m[2][kTileT];
-  __shared__ float red_s[2][kTileT];
+  // Ring of kSlots units; the 16-byte chunks of row r are XOR-permuted by
+  // swz(). After the K loop the first 2 KiB hold the cross-wave reduction.
+  __shared__ __attribute__((aligned(1024))) char ring[kSlots * kSlotB];
 
   int vt, tt;
   tile_of(blockIdx.x, a.n_vt, a.n_tt, kGroupV, vt, tt);
@@ -222,172 +238,152 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
+  const int lcol = lane & 15, lg = lane >> 4;
 
-  // ---- Global -> LDS assignment. Per operand and stage, wave w issues 8
-  // copies; copy j fills LDS rows 8q .. 8q+7 (q = 4 j + w), lane i writing
-  // physical chunk (i & 7) of row 8q + (i >> 3), i.e. logical chunk
-  // (i & 7) ^ f(row). Rows past the matrix are clamped (results discarded).
-  // Buffer resources based at the first row of each operand tile: the copies
-  // then take a 32-bit per-lane offset plus a uniform K offset.
+  // ---- Copies. Per unit, wave w issues 8 copies; copy j fills rows 8 q ..
+  // 8 q + 7 (q = 4 j + w), lane i writing physical chunk (i & 7) of row
+  // 8 q + (i >> 3), i.e. logical chunk swz(row, i & 7). Rows past the matrix
+  // are clamped (their results are discarded). The resources start at the
+  // tile's first row; the K offset of a stage is the uniform soffset.
   const char* wtile = reinterpret_cast<const char*>(a.w) + (size_t)v0 * a.H * 2;
   const char* xtile = reinterpret_cast<const char*>(a.x) + (size_t)t0 * a.ldh * 2;
-  const uint32_t w_span = span_bytes((uint64_t)(a.V_rows - v0) * (uint64_t)a.H * 2);
-  const uint32_t x_span = span_bytes((uint64_t)(a.T - t0 - 1) * (uint64_t)a.ldh * 2 + (uint64_t)a.H * 2);
-  const __amdgpu_buffer_rsrc_t wres = make_rsrc(wtile, w_span);
-  const __amdgpu_buffer_rsrc_t xres = make_rsrc(xtile, x_span);
-  uint32_t offA[kLoads], offB[kLoads];
+  const __amdgpu_buffer_rsrc_t wres =
+      make_rsrc(wtile, span_bytes((uint64_t)(a.V_rows - v0) * (uint64_t)a.H * 2));
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc(
+      xtile, span_bytes((uint64_t)(a.T - t0 - 1) * (uint64_t)a.ldh * 2 + (uint64_t)a.H * 2));
+  uint32_t offW[kCopiesU], offX[kCopiesU];
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) {
-    const int q = 4 * j + wave;
-    const int row = 8 * q + (lane >> 3);
-    const int c = swz(row, lane & 7);  // XOR permutation is its own inverse
-    const int ra = min(row, a.V_rows - 1 - v0);
-    const int rt = min(row, a.T - 1 - t0);
-    offA[j] = (uint32_t)ra * (uint32_t)(a.H * 2) + c * 16;
-    offB[j] = (uint32_t)rt * (uint32_t)(a.ldh * 2) + c * 16;
+  for (int j = 0; j < kCopiesU; ++j) {
+    const int row = 8 * (4 * j + wave) + (lane >> 3);
+    const int c = swz(row, lane & 7);  // the permutation is an involution
+    offW[j] = (uint32_t)min(row, a.V_rows - 1 - v0) * (uint32_t)(a.H * 2) + c * 16;
+    offX[j] = (uint32_t)min(row, a.T - 1 - t0) * (uint32_t)(a.ldh * 2) + c * 16;
   }
-#define ISSUE_PART(kt_, buf_, j0_, j1_)                                                 \
-  issue_stage(wres, xres, offA, offB, (lds_char*)((buf_) ? sA1 : sA0),               \
-              (lds_char*)((buf_) ? sB1 : sB0), wave, (kt_) * (kTileK * 2), (j0_), (j1_))
-#define ISSUE_STAGE(kt_, buf_) ISSUE_PART((kt_), (buf_), 0, kLoads)
+  const uint32_t lds0 =
+      __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_char*)ring));
+  const int nk = a.H / kTileK;
+  // Copy j (0..7) of the W (x_ = false) or X unit of stage k into slot sl. A
+  // stage past the end re-copies the last one into a slot that nothing reads
+  // before it is refilled.
+#define COPY(x_, j_, k_, sl_)                                                                   \
+  copy_lds((x_) ? xres : wres, lds0 + (uint32_t)(sl_) * kSlotB + (4 * (j_) + wave) * 1024,      \
+           (x_) ? offX[(j_)] : offW[(j_)], (uint32_t)min((k_), nk - 1) * kRowB)
 
-  // ---- Fragment reads. Lane l reads row (base + 32 i + (l & 31)), logical
-  // chunk 2 s + (l >> 5). With f(row) = (l & 7) ^ ((l & 31) >> 3) ^ 4 (i & 1)
-  // the physical chunk is 2 (s ^ 2 (i & 1)) ^ c0 with c0 = (l >> 5) ^ f0, so
-  // four addresses per operand cover every (s, i); the rest is immediate.
-  const int frow = lane & 31, fhalf = lane >> 5;
-  const int c0 = fhalf ^ ((frow & 7) ^ (frow >> 3));
-  uint32_t rdA[4], rdB[4];
+  // ---- Fragment reads. Fragment (tile u, half h) of an operand: lane l reads
+  // row base + 16 u + (l & 15), logical chunk 4 h + (l >> 4) (hidden elements
+  // 32 h + 8 (l >> 4) .. + 7 of the stage). swz() depends on the row only
+  // through l & 7, so one address per (operand, h) plus an immediate per tile
+  // suffice.
+  uint32_t rdA[2], rdB[2];
 #pragma unroll
-  for (int sp = 0; sp < 4; ++sp) {
-    rdA[sp] = (uint32_t)((wm * kWaveV + frow) * 128 + (((2 * sp) ^ c0) * 16));
-    rdB[sp] = (uint32_t)((wn * kWaveT + frow) * 128 + (((2 * sp) ^ c0) * 16));
+  for (int h = 0; h < 2; ++h) {
+    const int pc = swz(lcol, 4 * h + lg);
+    rdA[h] = (uint32_t)((wm * kWaveV + lcol) * kRowB + pc * 16);
+    rdB[h] = (uint32_t)((wn * kWaveT + lcol) * kRowB + pc * 16);
   }
-  auto read_frags = [&](bf16x8 (&fa)[kSubV], bf16x8 (&fb)[kSubT], int buf, int s)
-      __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < kSubV; ++i) {
-      const int sp = s ^ (2 * (i & 1));
-      fa[i] = *reinterpret_cast<const bf16x8*>((buf ? sA1 : sA0) + rdA[sp] + i * 4096);
-    }
-#pragma unroll
-    for (int j = 0; j < kSubT; ++j) {
-      const int sp = s ^ (2 * (j & 1));
-      fb[j] = *reinterpret_cast<const bf16x8*>((buf ? sB1 : sB0) + rdB[sp] + j * 4096);
-    }
-  };
+  // Fragment n (0..15) of half h: n == 0 and 9..15 are W tiles 0 and 1..7,
+  // n = 1..8 are X tiles 0..7 -- the order in which the MFMAs of a step first
+  // use them (W tile 0 with every X tile, then W tiles 1..7).
+#define READ(fa_, fb_, n_, h_)                                                                 \
+  do {                                                                                         \
+    if ((n_) >= 1 && (n_) <= 8)                                                                \
+      fb_[(n_) - 1] = *reinterpret_cast<const bf16x8*>(ring + bB + rdB[(h_)] + ((n_) - 1) * 2048); \
+    else {                                                                                     \
+      const int ii_ = (n_) == 0 ? 0 : (n_) - 8;                                                \
+      fa_[ii_] = *reinterpret_cast<const bf16x8*>(ring + bA + rdA[(h_)] + ii_ * 2048);         \
+    }                                                                                          \
+  } while (0)
+#define MFMA(fa_, fb_, u_) \
+  acc[(u_) >> 3][(u_) & 7] = mma(fa_[(u_) >> 3], fb_[(u_) & 7], acc[(u_) >> 3][(u_) & 7])
+#define FENCE() __builtin_amdgcn_sched_barrier(0)
 
-  f32x16 acc[kSubV][kSubT];
+  f32x4 acc[kSubV][kSubT];
 #pragma unroll
   for (int i = 0; i < kSubV; ++i)
 #pragma unroll
     for (int j = 0; j < kSubT; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  auto mma = [&](const bf16x8 (&fa)[kSubV], const bf16x8 (&fb)[kSubT])
-      __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < kSubV; ++i)
-#pragma unroll
-      for (int j = 0; j < kSubT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-  };
-
-  const int nk = a.H / kTileK;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
   bf16x8 fa0[kSubV], fb0[kSubT], fa1[kSubV], fb1[kSubT];
 
-  // Software pipeline over K stages. Phase kt runs between two barriers with
-  // stage kt readable in LDS buffer kt & 1 and four substeps of 16 MFMAs. The
-  // copies of stage kt+1 into the other buffer (freed by the barrier just
-  // passed) are spread one per two MFMAs over the first two substeps: a
-  // 1-KiB copy keeps the CU's address unit busy for several cycles, and
-  // bursts of copies from the four waves (which all leave the barrier
-  // together) would stall their in-order MFMA issue, while copies issued in
-  // the second half of the phase would not land before its end. Fragment
-  // registers alternate per substep so that the LDS reads of substep s+1
-  // (one per two MFMAs) overlap the MFMAs of substep s; the 16 MFMAs of the
-  // last substep are carried into the next phase, where they cover the
-  // latency of its first reads. Each phase ends with vmcnt(0) + barrier, so
-  // no copy is in flight across the loop back-edge. The copy of the next
-  // stage is issued unconditionally (branch-free, so it can be interleaved):
-  // in the last phase it re-copies the final stage into the idle buffer,
-  // which nothing reads. sched_barrier(0) keeps the compiler from re-ordering
-  // the substeps; sched_group_barrier sets the interleave inside one (masks:
-  // 0x008 MFMA, 0x020 VMEM read, 0x100 DS read).
-#define PHASE_FENCE() __builtin_amdgcn_sched_barrier(0)
-#define SGB(mask_, n_) __builtin_amdgcn_sched_group_barrier((mask_), (n_), 0)
-#define MIX_READS()                                  \
-  do {                                               \
-    _Pragma("unroll") for (int u = 0; u < 8; ++u) {  \
-      SGB(0x008, 1);                                 \
-      SGB(0x100, 1);                                 \
-      SGB(0x008, 1);                                 \
-    }                                                \
-  } while (0)
-#define MIX_READS_COPIES()                           \
-  do {                                               \
-    _Pragma("unroll") for (int u = 0; u < 8; ++u) {  \
-      SGB(0x008, 1);                                 \
-      SGB(0x020, 1);                                 \
-      SGB(0x100, 1);                                 \
-      SGB(0x008, 1);                                 \
-    }                                                \
-  } while (0)
-#define PHASE(kt_, buf_, carry_)                                            \
-  do {                                                                      \
-    const int buf = (buf_);                                                 \
-    const int kc = min((kt_) + 1, nk - 1);                                  \
-    ISSUE_PART(kc, buf ^ 1, 0, kLoads / 2);                                 \
-    read_frags(fa0, fb0, buf, 0);                                           \
-    if (carry_) {                                                           \
-      mma(fa1, fb1);                                                        \
-      MIX_READS_COPIES();                                                   \
-    }                                                                       \
-    PHASE_FENCE();                                                          \
-    ISSUE_PART(kc, buf ^ 1, kLoads / 2, kLoads);                            \
-    read_frags(fa1, fb1, buf, 1);                                           \
-    mma(fa0, fb0);                                                          \
-    MIX_READS_COPIES();                                                     \
-    PHASE_FENCE();                                                          \
-    read_frags(fa0, fb0, buf, 2);                                           \
-    mma(fa1, fb1);                                                          \
-    MIX_READS();                                                            \
-    PHASE_FENCE();                                                          \
-    read_frags(fa1, fb1, buf, 3);                                           \
-    mma(fa0, fb0);                                                          \
-    MIX_READS();                                                            \
-    PHASE_FENCE();                                                          \
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);                                   \
-    __syncthreads();                                                        \
-    PHASE_FENCE();                                                          \
+  // One step = 64 MFMAs (all 8 x 8 tiles, 32 hidden elements) on the
+  // fragments (mf, mb) with, interleaved, the 16 fragment reads of half rh_
+  // into (rf, rb) (one per 3 MFMAs from the first, so the last lands well
+  // before the phase barrier) and 8 copies (one per 8 MFMAs) of unit
+  // (cx_, ck_) into slot cs_. The order is fixed instruction by instruction.
+#define STEP(do_mma_, mf_, mb_, rf_, rb_, rh_, cx_, ck_, cs_)                \
+  do {                                                                       \
+    _Pragma("unroll") for (int u = 0; u < 64; ++u) {                         \
+      if (do_mma_) MFMA(mf_, mb_, u);                                        \
+      if (u % 3 == 0 && u / 3 < 16) READ(rf_, rb_, u / 3, (rh_));            \
+      if ((u & 7) == 2) COPY((cx_), (u >> 3), (ck_), (cs_));                 \
+      FENCE();                                                               \
+    }                                                                        \
   } while (0)
 
-  ISSUE_STAGE(0, 0);
+  // Phase k reads units 2k (W, slot s0) and 2k + 1 (X, slot s0 + 1) and
+  // copies units 2k + 3 (X stage k + 1) and 2k + 4 (W stage k + 2) into the
+  // slots freed by the barrier that ended phase k - 1. Unit 2k + 2 (W stage
+  // k + 1) was copied during phase k - 1, so every copy has at least half a
+  // phase to land, and half of them a phase and a half. The first step runs
+  // the MFMAs of the previous stage's second half (carried across the
+  // barrier) while reading this stage's first half; the second step runs the
+  // first half while reading the second. The phase ends once at most the 8
+  // copies of unit 2k + 4 are in flight and every wave is there.
+#define PHASE(carry_)                                                              \
+  do {                                                                             \
+    const uint32_t bA = (uint32_t)s0 * kSlotB;                                     \
+    const uint32_t bB = (uint32_t)(s0 == kSlots - 1 ? 0 : s0 + 1) * kSlotB;         \
+    const int c3 = s0 + 3 >= kSlots ? s0 + 3 - kSlots : s0 + 3;                    \
+    const int c4 = s0 + 4 >= kSlots ? s0 + 4 - kSlots : s0 + 4;                    \
+    STEP((carry_), fa1, fb1, fa0, fb0, 0, true, k + 1, c3);                        \
+    STEP(true, fa0, fb0, fa1, fb1, 1, false, k + 2, c4);                           \
+    __builtin_amdgcn_s_waitcnt(kWaitVm8);                                          \
+    __syncthreads();                                                               \
+    FENCE();                                                                       \
+    s0 = s0 + 2 >= kSlots ? s0 + 2 - kSlots : s0 + 2;                              \
+  } while (0)
+
+  // Prologue: units 0, 1, 2 (W0, X0, W1) into slots 0, 1, 2; wait for 0 and 1.
+#pragma unroll
+  for (int j = 0; j < kCopiesU; ++j) COPY(false, j, 0, 0);
+#pragma unroll
+  for (int j = 0; j < kCopiesU; ++j) COPY(true, j, 0, 1);
+#pragma unroll
+  for (int j = 0; j < kCopiesU; ++j) COPY(false, j, 1, 2);
+  __builtin_amdgcn_s_waitcnt(kWaitVm8);
+  __syncthreads();
+  FENCE();
+
+  int s0 = 0;
+  int k = 0;
+  PHASE(false);
+  for (k = 1; k < nk; ++k) PHASE(true);
+#pragma unroll
+  for (int u = 0; u < 64; ++u) {  // second half of the last stage
+    MFMA(fa1, fb1, u);
+    FENCE();
+  }
+  // Drain the tail copies before the LDS is reused.
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
-  PHASE(0, 0, false);
-  for (int kt = 1; kt < nk; kt += 2) {
-    PHASE(kt, 1, true);
-    if (kt + 1 < nk) PHASE(kt + 1, 0, true);
-  }
-  mma(fa1, fb1);  // last substep of the last stage
-#undef ISSUE_STAGE
-#undef ISSUE_PART
+#undef STEP
 #undef PHASE
-#undef MIX_READS
-#undef MIX_READS_COPIES
-#undef SGB
-#undef PHASE_FENCE
+#undef COPY
+#undef READ
+#undef MFMA
+#undef FENCE
+  float (*red_m)[kTileT] = reinterpret_cast<float (*)[kTileT]>(ring);
+  float (*red_s)[kTileT] = reinterpret_cast<float (*)[kTileT]>(ring + 2 * kTileT * sizeof(float));
 
   // ---- Epilogue: per-token online LSE over this wave's 128 vocab rows. ----
-  const int vlane = v0 + wm * kWaveV + 4 * fhalf;
+  const int vlane = v0 + wm * kWaveV + 4 * lg;
   const bool vtail = v0 + kTileV > a.V_true;
   const int64_t wv_lo = v0 + wm * kWaveV;
 
 #pragma unroll
   for (int j = 0; j < kSubT; ++j) {
-    const int tl = wn * kWaveT + j * 32 + frow;
+    const int tl = wn * kWaveT + j * 16 + lcol;
     const int t = t0 + tl;
     auto v = [&](int i, int r) __attribute__((always_inline)) { return acc[i][j][r]; };
     auto vm = [&](int i, int r) __attribute__((always_inline)) {
@@ -396,8 +392,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
     float m, s;
     if (vtail) wave_lse(vm, a.scale2, m, s);
     else wave_lse(v, a.scale2, m, s);
-    if (t < a.T) gather_target(v, a, t, wv_lo, fhalf);  // targets lie below V_true
-    if (fhalf == 0) {
+    if (t < a.T) gather_target(v, a, t, wv_lo, lg);  // targets lie below V_true
+    if (lg == 0) {
       red_m[wm][tl] = m;
       red_s[wm][tl] = s;
     }
@@ -421,8 +417,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
 // tiles would be mostly padding. Here a work item is one 128-row half of a
 // vocabulary tile x 32 ST tokens, computed by a single wave in exactly the
 // placement of the 256 x 256 kernel -- vocabulary row -> (MFMA tile i, lane
-// half, register), token -> MFMA column, the same v_mfma_f32_32x32x16_bf16
-// chain over 16-wide K blocks in ascending order -- and the same per-wave
+// group, register), token -> MFMA column, the same v_mfma_f32_16x16x32_bf16
+// chain over 32-wide K steps in ascending order -- and the same per-wave
 // epilogue (wave_lse), so every row's bits match. The wave writes its half's
 // (max, sum) partial; the merge kernel applies merge_halves before folding
 // the tiles, as the 256 x 256 kernel does in LDS.
@@ -436,29 +432,22 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
 // boundaries; being alone in its workgroup, a wave only waits on its own
 // vmcnt, never on a barrier. Two slots (four waves per CU) stream faster than
 // deeper rings with fewer waves per CU.
-constexpr int kSmK = 64;                       // hidden elements per stage
+constexpr int kSmK = kTileK;                   // hidden elements per stage
 constexpr int kSmStages = 2;                   // ring depth
-constexpr int kSmRowB = kSmK * 2;              // LDS row bytes
-constexpr int kSmNC = kSmRowB / 16;            // 16-byte chunks per row
-constexpr int kSmRPC = 1024 / kSmRowB;         // rows per 1-KiB wave copy
+constexpr int kSmRowB = kSmK * 2;              // LDS row bytes (128)
+constexpr int kSmNC = kSmRowB / 16;            // 16-byte chunks per row (8)
+constexpr int kSmRPC = 1024 / kSmRowB;         // rows per 1-KiB wave copy (8)
 constexpr int kSmRowsA = kWaveV;               // 128 W rows per item
 constexpr int kSmCopiesA = kSmRowsA * kSmRowB / 1024;
-static_assert(kSmNC == 4 || kSmNC == 8, "64- or 128-byte rows");
-
-// Physical chunk of logical chunk c in row `row`: conflict-free fragment
-// reads for 64-byte rows ((row >> 2) & 3) and 128-byte rows (as in the
-// 256 x 256 kernel).
-__host__ __device__ __forceinline__ int swz_sm(int row, int c) {
-  return kSmNC == 4 ? c ^ ((row >> 2) & 3) : c ^ ((row ^ (row >> 3)) & 7);
-}
 
 template <int ST>
 struct Stream {
   static constexpr int kTok = 32 * ST;                     // tokens per item
-  static constexpr int kCopiesB = kTok * kSmRowB / 1024;   // 2 ST
+  static constexpr int kTilesB = 2 * ST;                   // 16-token MFMA tiles
+  static constexpr int kCopiesB = kTok * kSmRowB / 1024;   // 4 ST
   static constexpr int kCopies = kSmCopiesA + kCopiesB;    // per stage
-  static constexpr int kSlotA = kSmRowsA * kSmRowB;        // 8 KiB
-  static constexpr int kSlotB = kTok * kSmRowB;            // 2 ST KiB
+  static constexpr int kSlotA = kSmRowsA * kSmRowB;        // 16 KiB
+  static constexpr int kSlotB = kTok * kSmRowB;            // 4 ST KiB
   static constexpr int kSlot = kSlotA + kSlotB;
   static constexpr int kLds = kSmStages * kSlot;
   static_assert((kSmStages - 1) * kCopies <= 63, "vmcnt holds at most 63");
@@ -477,9 +466,9 @@ __global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_ite
   const uint32_t H2 = (uint32_t)a.H * 2, X2 = (uint32_t)a.ldh * 2;
   // Copy lane mapping: copy q fills rows kSmRPC q .. + kSmRPC - 1; lane i
   // writes physical chunk i % kSmNC of row kSmRPC q + i / kSmNC, i.e. the
-  // logical chunk swz_sm(row, i % kSmNC) (the permutation is an involution).
+  // logical chunk swz(row, i % kSmNC) (the permutation is an involution).
   const int lrow = lane / kSmNC;
-#define SM_LC(q_) ((uint32_t)(swz_sm(kSmRPC * (q_) + lrow, lane % kSmNC) * 16))
+#define SM_LC(q_) ((uint32_t)(swz(kSmRPC * (q_) + lrow, lane % kSmNC) * 16))
 
   // Enqueue the copies of flat stage g (item g / nk, K stage g % nk).
   auto issue = [&](int g) __attribute__((always_inline)) {
@@ -511,13 +500,13 @@ __global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_ite
           (uint32_t)min(kSmRPC * q + lrow, tmax) * X2 + SM_LC(q), koff, 0, 0);
   };
 
-  // Fragment reads: row 32 i + (l & 31) of the half-tile (A) or 32 j + (l & 31)
-  // of the token tile (B), logical chunk 2 s + (l >> 5).
-  const int frow = lane & 31, fhalf = lane >> 5;
-#define SM_RD(row0_, sp_) \
-  ((uint32_t)(((row0_) + frow) * kSmRowB + swz_sm((row0_) + frow, 2 * (sp_) + fhalf) * 16))
+  // Fragment reads: row 16 i + (l & 15) of the half-tile (W) or 16 jj +
+  // (l & 15) of the token tile (X), logical chunk 4 h + (l >> 4).
+  const int lcol = lane & 15, lg = lane >> 4;
+#define SM_RD(row0_, h_) \
+  ((uint32_t)(((row0_) + lcol) * kSmRowB + swz((row0_) + lcol, 4 * (h_) + lg) * 16))
 
-  f32x16 acc[kSubV][ST];
+  f32x4 acc[kSubV][S::kTilesB];
   for (int g = 0; g < kSmStages - 1 && g < n_stages; ++g) issue(g);
   for (int g = 0; g < n_stages; ++g) {
     if (g + kSmStages - 1 < n_stages) {
@@ -533,35 +522,34 @@ __global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_ite
 #pragma unroll
       for (int i = 0; i < kSubV; ++i)
 #pragma unroll
-        for (int jj = 0; jj < ST; ++jj)
+        for (int jj = 0; jj < S::kTilesB; ++jj)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
+          for (int r = 0; r < 4; ++r) acc[i][jj][r] = 0.f;
     }
     const char* slot = ring + (g % kSmStages) * S::kSlot;
 #pragma unroll
-    for (int sp = 0; sp < kSmK / 16; ++sp) {
-      bf16x8 fa[kSubV], fb[ST];
+    for (int h = 0; h < kSmK / 32; ++h) {
+      bf16x8 fa[kSubV], fb[S::kTilesB];
 #pragma unroll
       for (int i = 0; i < kSubV; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(slot + SM_RD(32 * i, sp));
+        fa[i] = *reinterpret_cast<const bf16x8*>(slot + SM_RD(16 * i, h));
 #pragma unroll
-      for (int jj = 0; jj < ST; ++jj)
-        fb[jj] = *reinterpret_cast<const bf16x8*>(slot + S::kSlotA + SM_RD(32 * jj, sp));
+      for (int jj = 0; jj < S::kTilesB; ++jj)
+        fb[jj] = *reinterpret_cast<const bf16x8*>(slot + S::kSlotA + SM_RD(16 * jj, h));
 #pragma unroll
       for (int i = 0; i < kSubV; ++i)
 #pragma unroll
-        for (int jj = 0; jj < ST; ++jj)
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[jj], acc[i][jj], 0, 0, 0);
+        for (int jj = 0; jj < S::kTilesB; ++jj) acc[i][jj] = mma(fa[i], fb[jj], acc[i][jj]);
     }
     if (kt == nk - 1) {
       const int L = xb + (g / nk) * G;
       const int vh = L / a.n_tt, tt = L - vh * a.n_tt;
       const int vbase = vh * kWaveV, t0 = tt * S::kTok;
-      const int vlane = vbase + 4 * fhalf;
+      const int vlane = vbase + 4 * lg;
       const bool vtail = vbase + kWaveV > a.V_true;
 #pragma unroll
-      for (int jj = 0; jj < ST; ++jj) {
-        const int t = t0 + 32 * jj + frow;
+      for (int jj = 0; jj < S::kTilesB; ++jj) {
+        const int t = t0 + 16 * jj + lcol;
         auto v = [&](int i, int r) __attribute__((always_inline)) { return acc[i][jj][r]; };
         auto vm = [&](int i, int r) __attribute__((always_inline)) {
           return LP_MASKED(acc[i][jj][r], vlane, i, r, a.V_true);
@@ -570,8 +558,8 @@ __global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_ite
         if (vtail) wave_lse(vm, a.scale2, m, s);
         else wave_lse(v, a.scale2, m, s);
         if (t < a.T) {
-          gather_target(v, a, t, vbase, fhalf);  // targets lie below V_true
-          if (fhalf == 0) {
+          gather_target(v, a, t, vbase, lg);  // targets lie below V_true
+          if (lg == 0) {
             a.part_m[(size_t)vh * a.T + t] = m;
             a.part_s[(size_t)vh * a.T + t] = s;
           }
