@@ -87,8 +87,10 @@ __device__ __forceinline__ double exp_f64(double x) {
   return ldexp(p, (int)k);
 }
 
-// 8 waves per SIMD: the few spills this costs sit outside the window loop.
-__global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(8))) void compare_kernel(
+// 7 waves per SIMD: the 68 registers this allows hold the whole state without
+// spilling (at 8 waves the spill area of 24 bytes per lane cost more write
+// traffic than the extra wave saved).
+__global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(7))) void compare_kernel(
     CompareArgs a) {
   const int lane = threadIdx.x & 63;
   const int p = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // pair of this wave
