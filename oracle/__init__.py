@@ -13,5 +13,5 @@ Every function cites the passage of the source pages it writes out:
   [VeX]  "Diagnosing Training Inference Mismatch in LLM Reinforcement Learning"
 """
 
-from .score import bf16_bits_to_f64, score, logits  # noqa: F401
+from .score import bf16_bits_to_f64, score, score_stats, entropy_argmax, logits  # noqa: F401
 from .compare import compare, per_token, PAIRS, STAT_FIELDS  # noqa: F401

@@ -19,6 +19,18 @@ What is computed, per scored row t (rows are independent):
         normaliser covers the true vocabulary range only, so padded LM-head
         rows past it take no part.
 
+The row's entropy and argmax (score_stats):
+
+  [AMD] §"Case 2: A and B Stay Close; C Changes": the trainer's scoring step
+        computes the log probs and the entropy of the same distribution. The
+        entropy here is the plain Shannon entropy of softmax(z / T) over the
+        true vocabulary range, in nats: H = -sum_v p_v ln p_v.
+  [vLLM] §"Metric measurement basis": the full-vocabulary argmax is reported
+        separately from the token metrics; "Diagnosing Training Inference
+        Mismatch ..." (result 1 and its list of practical indicators) counts a
+        top-1 flip when two scorings disagree on it. The argmax is the first
+        (lowest) index of the row's largest logit.
+
 Precision: the bf16 input bits are widened exactly to fp64; every later
 operation is one fp64 operation. The logit row is an fp64 matrix product
 (library matmul; its rounding, at most about H * 2^-53 relative, is far below
@@ -81,3 +93,32 @@ def score(x_bits: np.ndarray, w_bits: np.ndarray, ids: np.ndarray,
     if x_bits.shape[0] == 0:
         return np.zeros(0), np.zeros(0)
     return log_softmax_at(logits(x_bits, w_bits, v_true), ids, temperature)
+
+
+def entropy_argmax(z: np.ndarray, temperature: float = 1.0):
+    """Return (entropy[t] in nats, argmax[t]) for logit rows z [T, V], fp64.
+
+    p = softmax(z / T) row by row; entropy = -sum_v p_v ln p_v with
+    ln p_v = s_v - lse (exact form of the log of the normalised weight);
+    argmax = the lowest v with z[t, v] equal to the row's maximum.
+    """
+    temperature = float(temperature)
+    if not (np.isfinite(temperature) and temperature > 0.0):
+        raise ValueError("temperature must be finite and > 0")
+    s = z / temperature
+    M = s.max(axis=1)
+    lse = M + np.log(np.exp(s - M[:, None]).sum(axis=1))
+    logp = s - lse[:, None]
+    ent = -(np.exp(logp) * logp).sum(axis=1)
+    return ent, np.argmax(z, axis=1).astype(np.int64)
+
+
+def score_stats(x_bits: np.ndarray, w_bits: np.ndarray, ids: np.ndarray,
+                temperature: float = 1.0, v_true: int | None = None):
+    """(logprob, lse, entropy, argmax) of every row: fp64, fp64, fp64, int64."""
+    if x_bits.shape[0] == 0:
+        return np.zeros(0), np.zeros(0), np.zeros(0), np.zeros(0, np.int64)
+    z = logits(x_bits, w_bits, v_true)
+    lp, lse = log_softmax_at(z, ids, temperature)
+    ent, amax = entropy_argmax(z, temperature)
+    return lp, lse, ent, amax
