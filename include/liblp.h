@@ -98,6 +98,44 @@ lp_status lp_score(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
                    hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Selected-token logprob with the row's entropy and argmax
+ *
+ * The same call as lp_score, also returning per row the entropy of the
+ * scored distribution and its most likely token, from the same fused pass
+ * (the logits still never reach memory):
+ *
+ *   entropy[t] = -sum_{v < V_true} p[t, v] ln p[t, v],   p = softmax(s[t, :])
+ *              = lse[t] - sum_v p[t, v] s[t, v]            (nats, fp32)
+ *   argmax[t]  = the lowest v < V_true with z[t, v] = max_{v' < V_true} z[t, v']
+ *                over the fp32 logits as this library computes them (int64)
+ *
+ * Sources: the trainer's scoring step that the AMD blog's Case 2 inspects
+ * computes log probs and entropy together ([AMD] "Case 2: A and B Stay Close;
+ * C Changes"); the full-vocabulary argmax is reported apart from the token
+ * metrics ([vLLM] "Metric measurement basis"), and a top-1 token flip
+ * between two scorings -- argmax differs for the same row -- is one of the
+ * indicators [VeX] lists (result 1 and its list of practical indicators).
+ * Two argmax arrays are compared as integers.
+ *
+ * out_logprob and out_lse hold exactly the bits lp_score writes for the same
+ * arguments. The batch-invariance guarantee of lp_score covers entropy and
+ * argmax too. Ties between logits that compare equal after the temperature
+ * scale go to the lower index. Workspace: lp_score_stats_workspace_bytes (it
+ * is larger than lp_score's). out_entropy [T] fp32 and out_argmax [T] int64
+ * are required; every other argument, layout and error is as for lp_score.
+ * ------------------------------------------------------------------------ */
+size_t lp_score_stats_workspace_bytes(int64_t T, int64_t H, int64_t V_rows,
+                                      int64_t V_true);
+
+lp_status lp_score_stats(const void* hidden_bf16, int64_t ldh,
+                         const void* w_bf16, const int64_t* target_ids,
+                         int64_t T, int64_t H, int64_t V_rows, int64_t V_true,
+                         float temperature, float* out_logprob, float* out_lse,
+                         float* out_entropy, int64_t* out_argmax,
+                         int32_t* bad_rows, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Three-way comparison of generation (A), replay (B) and trainer (C) scores
  *
  * [AMD] "One Response, Three Scores", "Check Whether the Pattern Extends",

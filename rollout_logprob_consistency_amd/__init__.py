@@ -8,6 +8,7 @@ step runs in the library's kernels. PyTorch supplies device memory and
 streams.
 
     score(hidden, w, ids, temperature=1.0, v_true=None)   -> logprob [T] fp32
+    score_stats(hidden, w, ids, ...)                      -> logprob, entropy, argmax
     compare(A, B, C, mask, tis_clip=2.0, atol=None)       -> stats per pair
     align(hidden, input_ids, response_mask)               -> rows, targets, mask
 """
@@ -85,6 +86,51 @@ def score(hidden: torch.Tensor, w: torch.Tensor, ids: torch.Tensor,
     if check and int(bad_rows.item()) != 0:
         raise ValueError(f"{int(bad_rows.item())} row(s) have a target id outside [0, {vt})")
     return out
+
+
+def score_stats_workspace_bytes(T: int, H: int, V_rows: int, V_true: int | None = None) -> int:
+    return int(lib().lp_score_stats_workspace_bytes(T, H, V_rows,
+                                                    V_rows if V_true is None else V_true))
+
+
+def score_stats(hidden: torch.Tensor, w: torch.Tensor, ids: torch.Tensor,
+                temperature: float = 1.0, v_true: int | None = None, *,
+                lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                check: bool = False):
+    """Selected-token logprob plus the row's entropy (nats) and argmax.
+
+    Same arguments as score(); returns (logprob fp32 [T], entropy fp32 [T],
+    argmax int64 [T]). The logprob bits equal score()'s for the same inputs.
+    """
+    _need_cuda("hidden", hidden, torch.bfloat16)
+    _need_cuda("w", w, torch.bfloat16)
+    _need_cuda("ids", ids, torch.int64)
+    if hidden.dim() != 2 or w.dim() != 2 or ids.dim() != 1:
+        raise ValueError("expected hidden [T, H], w [V, H], ids [T]")
+    if hidden.stride(1) != 1 or not w.is_contiguous() or not ids.is_contiguous():
+        raise ValueError("hidden needs unit column stride; w and ids must be contiguous")
+    T, H = hidden.shape
+    V = w.shape[0]
+    if w.shape[1] != H or ids.shape[0] != T:
+        raise ValueError("shape mismatch between hidden, w and ids")
+    vt = V if v_true is None else int(v_true)
+    dev = hidden.device
+    out = torch.empty(T, dtype=torch.float32, device=dev)
+    ent = torch.empty(T, dtype=torch.float32, device=dev)
+    amax = torch.empty(T, dtype=torch.int64, device=dev)
+    need = score_stats_workspace_bytes(T, H, V, vt)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    bad_rows = torch.zeros(1, dtype=torch.int32, device=dev) if check else None
+    st = lib().lp_score_stats(_ptr(hidden), hidden.stride(0) if T else H, _ptr(w), _ptr(ids),
+                              T, H, V, vt, float(temperature), _ptr(out), _ptr(lse), _ptr(ent),
+                              _ptr(amax), _ptr(bad_rows), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(dev))
+    if st != LP_OK:
+        raise LpError(st, "lp_score_stats")
+    if check and int(bad_rows.item()) != 0:
+        raise ValueError(f"{int(bad_rows.item())} row(s) have a target id outside [0, {vt})")
+    return out, ent, amax
 
 
 def compare_raw(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch.Tensor,

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblp.so")
 LP_OK, LP_EINVAL, LP_EUNSUPPORTED, LP_EHIP = 0, 1, 2, 3
 
 # Names of every function include/liblp.h declares.
-EXPORTS = ("lp_status_string", "lp_score_workspace_bytes", "lp_score", "lp_compare")
+EXPORTS = ("lp_status_string", "lp_score_workspace_bytes", "lp_score",
+           "lp_score_stats_workspace_bytes", "lp_score_stats", "lp_compare")
 
 # numpy mirror of `lp_seq_stats` (natural C alignment: 6 int32 then 7 double).
 SEQ_STATS_DTYPE = np.dtype([
@@ -56,6 +57,11 @@ def lib() -> ctypes.CDLL:
     L.lp_score.restype = ctypes.c_int
     L.lp_score.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, f32,
                            vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.lp_score_stats_workspace_bytes.restype = ctypes.c_size_t
+    L.lp_score_stats_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    L.lp_score_stats.restype = ctypes.c_int
+    L.lp_score_stats.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, f32,
+                                 vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.lp_compare.restype = ctypes.c_int
     L.lp_compare.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, f32, vp, vp, vp]
     _lib = L

@@ -31,20 +31,33 @@ const char* lp_status_string(lp_status status) {
 size_t lp_score_workspace_bytes(int64_t T, int64_t H, int64_t V_rows, int64_t V_true) {
   (void)H;
   if (T < 0 || V_rows < 1 || V_true < 1 || V_true > V_rows) return 0;
-  return lp::score_workspace_layout(T, V_true).total;
+  return lp::score_workspace_layout(T, V_true, false).total;
 }
 
-lp_status lp_score(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
-                   const int64_t* target_ids, int64_t T, int64_t H, int64_t V_rows,
-                   int64_t V_true, float temperature, float* out_logprob, float* out_lse,
-                   int32_t* bad_rows, void* workspace, size_t workspace_bytes,
-                   hipStream_t stream) {
+size_t lp_score_stats_workspace_bytes(int64_t T, int64_t H, int64_t V_rows, int64_t V_true) {
+  (void)H;
+  if (T < 0 || V_rows < 1 || V_true < 1 || V_true > V_rows) return 0;
+  return lp::score_workspace_layout(T, V_true, true).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared body of lp_score and lp_score_stats (stats: entropy and argmax
+// requested, both non-NULL).
+lp_status score_impl(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
+                     const int64_t* target_ids, int64_t T, int64_t H, int64_t V_rows,
+                     int64_t V_true, float temperature, float* out_logprob, float* out_lse,
+                     float* out_entropy, int64_t* out_argmax, bool stats, int32_t* bad_rows,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (T < 0 || H < 1 || V_rows < 1 || V_true < 1 || V_true > V_rows || ldh < H)
     return LP_EINVAL;
   if (!(isfinite(temperature) && temperature > 0.0f)) return LP_EINVAL;
   if (T == 0) return LP_OK;
   if (!hidden_bf16 || !w_bf16 || !target_ids || !out_logprob || !workspace) return LP_EINVAL;
-  const lp::ScoreWorkspace ws = lp::score_workspace_layout(T, V_true);
+  if (stats && (!out_entropy || !out_argmax)) return LP_EINVAL;
+  const lp::ScoreWorkspace ws = lp::score_workspace_layout(T, V_true, stats);
   if (workspace_bytes < ws.total || !aligned(workspace, 256)) return LP_EINVAL;
   if (H % lp::kTileK != 0 || ldh % 8 != 0) return LP_EUNSUPPORTED;
   if (!aligned(hidden_bf16, 16) || !aligned(w_bf16, 16)) return LP_EUNSUPPORTED;
@@ -72,7 +85,35 @@ lp_status lp_score(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
   a.out_lp = out_logprob;
   a.out_lse = out_lse;
   a.bad_rows = bad_rows;
+  a.part_q = stats ? reinterpret_cast<float*>(base + ws.off_q) : nullptr;
+  a.part_i = stats ? reinterpret_cast<int32_t*>(base + ws.off_i) : nullptr;
+  a.out_ent = stats ? out_entropy : nullptr;
+  a.out_argmax = stats ? out_argmax : nullptr;
   return lp::launch_score(a, stream) == hipSuccess ? LP_OK : LP_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+lp_status lp_score(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
+                   const int64_t* target_ids, int64_t T, int64_t H, int64_t V_rows,
+                   int64_t V_true, float temperature, float* out_logprob, float* out_lse,
+                   int32_t* bad_rows, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  return score_impl(hidden_bf16, ldh, w_bf16, target_ids, T, H, V_rows, V_true, temperature,
+                    out_logprob, out_lse, nullptr, nullptr, false, bad_rows, workspace,
+                    workspace_bytes, stream);
+}
+
+lp_status lp_score_stats(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
+                         const int64_t* target_ids, int64_t T, int64_t H, int64_t V_rows,
+                         int64_t V_true, float temperature, float* out_logprob, float* out_lse,
+                         float* out_entropy, int64_t* out_argmax, int32_t* bad_rows,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return score_impl(hidden_bf16, ldh, w_bf16, target_ids, T, H, V_rows, V_true, temperature,
+                    out_logprob, out_lse, out_entropy, out_argmax, true, bad_rows, workspace,
+                    workspace_bytes, stream);
 }
 
 lp_status lp_compare(const float* gen_A, const float* replay_B, const float* train_C,

@@ -35,13 +35,19 @@ struct ScoreArgs {
   float* out_lp;          // [T]
   float* out_lse;         // [T] or null
   int32_t* bad_rows;      // or null
+  // Entropy / argmax outputs (lp_score_stats); null for lp_score.
+  float* part_q;          // [rows][T]  per-partial sum 2^d d (log2 units)
+  int32_t* part_i;        // [rows][T]  per-partial argmax (vocabulary row)
+  float* out_ent;         // [T] entropy, nats
+  int64_t* out_argmax;    // [T]
 };
 
 // Workspace layout inside the caller's buffer (offsets in bytes, 256-aligned).
+// With stats, two more planes follow for the entropy term and the argmax.
 struct ScoreWorkspace {
-  size_t off_m, off_s, off_t, total;
+  size_t off_m, off_s, off_t, off_q, off_i, total;
 };
-ScoreWorkspace score_workspace_layout(int64_t T, int64_t V_true);
+ScoreWorkspace score_workspace_layout(int64_t T, int64_t V_true, bool stats);
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream);
 

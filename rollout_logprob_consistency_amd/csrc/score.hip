@@ -135,28 +135,65 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // logits is the scaled max; the scale is folded into the exp2 argument with
 // one FMA. The butterfly adds the same two values in both lanes of each step,
 // so all four lanes end with the same bits.
-template <class Get>
-__device__ __forceinline__ void wave_lse(Get v, float scale2, float& m_out, float& s_out) {
+//
+// kStats adds, for the entropy and the argmax, q = sum 2^d d over the same
+// terms (d = scaled logit - m, log2 units; a masked row has d = -inf and adds
+// nothing) and the wave-local row (0..127) of the maximum, the lowest row on
+// ties (kNoRow for a wave whose rows are all masked). s and m are formed by
+// exactly the same operations as without kStats.
+constexpr int kNoRow = 0x7FFFFFFF;
+
+template <bool kStats, class Get>
+__device__ __forceinline__ void wave_lse(Get v, float scale2, int lg, float& m_out, float& s_out,
+                                         float& q_out, int& i_out) {
   const float NEG_INF = -__builtin_inff();
   float mr = NEG_INF;
 #pragma unroll
   for (int i = 0; i < kSubV; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) mr = fmaxf(mr, v(i, r));
-  mr = fmaxf(mr, __shfl_xor(mr, 16));
-  mr = fmaxf(mr, __shfl_xor(mr, 32));
+  int li = kNoRow;
+  if (kStats) {
+    // Register r of tile i holds row 16 i + 4 lg + r: rows ascend with (i, r),
+    // so the last overwrite in descending order is the lowest matching row.
+#pragma unroll
+    for (int i = kSubV - 1; i >= 0; --i)
+#pragma unroll
+      for (int r = 3; r >= 0; --r) li = (v(i, r) == mr) ? 16 * i + 4 * lg + r : li;
+    if (mr == NEG_INF) li = kNoRow;
+  }
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    const float mo = __shfl_xor(mr, off);
+    if (kStats) {
+      const int lo = __shfl_xor(li, off);
+      li = (mo > mr) ? lo : ((mr > mo) ? li : min(li, lo));
+    }
+    mr = fmaxf(mr, mo);
+  }
   const float m = mr * scale2;
-  float s = 0.f;
+  float s = 0.f, q = 0.f;
   if (mr != NEG_INF) {
 #pragma unroll
     for (int i = 0; i < kSubV; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s += fast_exp2(__builtin_fmaf(v(i, r), scale2, -m));
+      for (int r = 0; r < 4; ++r) {
+        const float d = __builtin_fmaf(v(i, r), scale2, -m);
+        const float e = fast_exp2(d);
+        s += e;
+        if (kStats) q = __builtin_fmaf(e, fmaxf(d, -3.0e38f), q);  // -inf row: 0 * finite
+      }
   }
   s += __shfl_xor(s, 16);
   s += __shfl_xor(s, 32);
+  if (kStats) {
+    q += __shfl_xor(q, 16);
+    q += __shfl_xor(q, 32);
+  }
   m_out = m;
   s_out = s;
+  q_out = q;
+  i_out = li;
 }
 
 // Target gather for token t: exactly one lane of the grid holds (target, t);
@@ -188,6 +225,16 @@ __device__ __forceinline__ void merge_halves(float m0, float s0, float m1, float
                                              float& S) {
   M = fmaxf(m0, m1);
   S = __builtin_fmaf(s1, fast_exp2(m1 - M), s0 * fast_exp2(m0 - M));  // contraction spelled out
+}
+
+// Entropy term of the merge of two (max, sum, q) partials into max M: q is
+// relative to each partial's max, so q_j + (m_j - M) s_j re-bases it (an
+// empty partial, s_j = 0, contributes nothing even when m_j = -inf).
+__device__ __forceinline__ float merge_q(float m0, float s0, float q0, float m1, float s1,
+                                         float q1, float M) {
+  const float t0 = s0 != 0.f ? (m0 - M) * s0 : 0.f;
+  const float t1 = s1 != 0.f ? (m1 - M) * s1 : 0.f;
+  return __builtin_fmaf(fast_exp2(m1 - M), q1 + t1, fast_exp2(m0 - M) * (q0 + t0));
 }
 
 // Rows at or past V_true (only in the last vocabulary tile) read as -inf:
@@ -223,6 +270,7 @@ constexpr int kCopiesU = kSlotB / 1024 / 4;  // 1-KiB copies per wave per unit
 static_assert(kCopiesU == 8, "copy schedule assumes 8 copies per wave per unit");
 static_assert(kSlots * kSlotB <= 160 * 1024, "LDS");
 
+template <bool kStats>
 __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   // Ring of kSlots units; the 16-byte chunks of row r are XOR-permuted by
   // swz(). After the K loop the first 2 KiB hold the cross-wave reduction.
@@ -375,6 +423,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
 #undef FENCE
   float (*red_m)[kTileT] = reinterpret_cast<float (*)[kTileT]>(ring);
   float (*red_s)[kTileT] = reinterpret_cast<float (*)[kTileT]>(ring + 2 * kTileT * sizeof(float));
+  float (*red_q)[kTileT] = reinterpret_cast<float (*)[kTileT]>(ring + 4 * kTileT * sizeof(float));
+  int (*red_i)[kTileT] = reinterpret_cast<int (*)[kTileT]>(ring + 6 * kTileT * sizeof(float));
 
   // ---- Epilogue: per-token online LSE over this wave's 128 vocab rows. ----
   const int vlane = v0 + wm * kWaveV + 4 * lg;
@@ -389,13 +439,18 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
     auto vm = [&](int i, int r) __attribute__((always_inline)) {
       return LP_MASKED(acc[i][j][r], vlane, i, r, a.V_true);
     };
-    float m, s;
-    if (vtail) wave_lse(vm, a.scale2, m, s);
-    else wave_lse(v, a.scale2, m, s);
+    float m, s, q;
+    int li;
+    if (vtail) wave_lse<kStats>(vm, a.scale2, lg, m, s, q, li);
+    else wave_lse<kStats>(v, a.scale2, lg, m, s, q, li);
     if (t < a.T) gather_target(v, a, t, wv_lo, lg);  // targets lie below V_true
     if (lg == 0) {
       red_m[wm][tl] = m;
       red_s[wm][tl] = s;
+      if (kStats) {
+        red_q[wm][tl] = q;
+        red_i[wm][tl] = li == kNoRow ? kNoRow : (int)wv_lo + li;
+      }
     }
   }
   __syncthreads();
@@ -408,6 +463,12 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
     if (t < a.T) {
       a.part_m[(size_t)vt * a.T + t] = M;
       a.part_s[(size_t)vt * a.T + t] = S;
+      if (kStats) {
+        a.part_q[(size_t)vt * a.T + t] = merge_q(red_m[0][tl], red_s[0][tl], red_q[0][tl],
+                                                 red_m[1][tl], red_s[1][tl], red_q[1][tl], M);
+        // The lower half wins ties: its rows come first.
+        a.part_i[(size_t)vt * a.T + t] = red_m[1][tl] > red_m[0][tl] ? red_i[1][tl] : red_i[0][tl];
+      }
     }
   }
 }
@@ -453,7 +514,7 @@ struct Stream {
   static_assert((kSmStages - 1) * kCopies <= 63, "vmcnt holds at most 63");
 };
 
-template <int ST>
+template <int ST, bool kStats>
 __global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_items) {
   using S = Stream<ST>;
   __shared__ __attribute__((aligned(1024))) char ring[S::kLds];
@@ -554,14 +615,19 @@ __global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_ite
         auto vm = [&](int i, int r) __attribute__((always_inline)) {
           return LP_MASKED(acc[i][jj][r], vlane, i, r, a.V_true);
         };
-        float m, s;
-        if (vtail) wave_lse(vm, a.scale2, m, s);
-        else wave_lse(v, a.scale2, m, s);
+        float m, s, q;
+        int li;
+        if (vtail) wave_lse<kStats>(vm, a.scale2, lg, m, s, q, li);
+        else wave_lse<kStats>(v, a.scale2, lg, m, s, q, li);
         if (t < a.T) {
           gather_target(v, a, t, vbase, lg);  // targets lie below V_true
           if (lg == 0) {
             a.part_m[(size_t)vh * a.T + t] = m;
             a.part_s[(size_t)vh * a.T + t] = s;
+            if (kStats) {
+              a.part_q[(size_t)vh * a.T + t] = q;
+              a.part_i[(size_t)vh * a.T + t] = li == kNoRow ? kNoRow : vbase + li;
+            }
           }
         }
       }
@@ -587,48 +653,90 @@ __device__ __forceinline__ void lse_fold(float& M, float& S, float m, float s) {
   M = Mn;
 }
 
+// The same fold with the entropy term q and the argmax i carried along; an
+// equal maximum keeps the earlier (lower) index.
+__device__ __forceinline__ void lse_fold_stats(float& M, float& S, float& Q, int& I, float m,
+                                               float s, float q, int i) {
+  const float Mn = fmaxf(M, m);
+  Q = merge_q(M, S, Q, m, s, q, Mn);
+  I = m > M ? i : I;
+  S = __builtin_fmaf(s, fast_exp2(m - Mn), S * fast_exp2(M - Mn));
+  M = Mn;
+}
+
 // kHalves: the partials are per 128-row half of each vocabulary tile (rows
-// 2 vt and 2 vt + 1), merged with merge_halves first.
-template <bool kHalves>
+// 2 vt and 2 vt + 1), merged with merge_halves first. kStats: also fold the
+// entropy term and the argmax, and write entropy (nats) and argmax.
+template <bool kHalves, bool kStats>
 __global__ __launch_bounds__(64 * kMergeSegs) void lse_merge_kernel(ScoreArgs a) {
   __shared__ float seg_m[kMergeSegs][64];
   __shared__ float seg_s[kMergeSegs][64];
+  __shared__ float seg_q[kStats ? kMergeSegs : 1][64];
+  __shared__ int seg_i[kStats ? kMergeSegs : 1][64];
   const int lane = threadIdx.x & 63, seg = threadIdx.x >> 6;
   const int t = blockIdx.x * 64 + lane;
   const int per = (a.n_vt + kMergeSegs - 1) / kMergeSegs;
   const int lo = min(a.n_vt, seg * per), hi = min(a.n_vt, lo + per);
-  float M = -__builtin_inff(), S = 0.f;
+  float M = -__builtin_inff(), S = 0.f, Q = 0.f;
+  int I = kNoRow;
   if (t < a.T) {
     const float* pm = a.part_m + t;
     const float* ps = a.part_s + t;
+    const float* pq = a.part_q + t;
+    const int* pi = a.part_i + t;
     if (kHalves) {
 #pragma unroll 8
       for (int vt = lo; vt < hi; ++vt) {
+        const size_t r0 = (size_t)(2 * vt) * a.T, r1 = (size_t)(2 * vt + 1) * a.T;
         float m, s;
-        merge_halves(pm[(size_t)(2 * vt) * a.T], ps[(size_t)(2 * vt) * a.T],
-                     pm[(size_t)(2 * vt + 1) * a.T], ps[(size_t)(2 * vt + 1) * a.T], m, s);
-        lse_fold(M, S, m, s);
+        merge_halves(pm[r0], ps[r0], pm[r1], ps[r1], m, s);
+        if (kStats) {
+          const float q = merge_q(pm[r0], ps[r0], pq[r0], pm[r1], ps[r1], pq[r1], m);
+          const int i = pm[r1] > pm[r0] ? pi[r1] : pi[r0];
+          lse_fold_stats(M, S, Q, I, m, s, q, i);
+        } else {
+          lse_fold(M, S, m, s);
+        }
       }
     } else {
 #pragma unroll 8
-      for (int vt = lo; vt < hi; ++vt)
-        lse_fold(M, S, pm[(size_t)vt * a.T], ps[(size_t)vt * a.T]);
+      for (int vt = lo; vt < hi; ++vt) {
+        const size_t r = (size_t)vt * a.T;
+        if (kStats) lse_fold_stats(M, S, Q, I, pm[r], ps[r], pq[r], pi[r]);
+        else lse_fold(M, S, pm[r], ps[r]);
+      }
     }
   }
   seg_m[seg][lane] = M;
   seg_s[seg][lane] = S;
+  if (kStats) {
+    seg_q[seg][lane] = Q;
+    seg_i[seg][lane] = I;
+  }
   __syncthreads();
   if (seg != 0 || t >= a.T) return;
   M = seg_m[0][lane];
   S = seg_s[0][lane];
+  if (kStats) {
+    Q = seg_q[0][lane];
+    I = seg_i[0][lane];
+  }
 #pragma unroll
-  for (int g = 1; g < kMergeSegs; ++g)  // an empty segment (-inf, 0) folds to a no-op
-    lse_fold(M, S, seg_m[g][lane], seg_s[g][lane]);
-  const float lse2 = M + fast_log2(S);
+  for (int g = 1; g < kMergeSegs; ++g) {  // an empty segment (-inf, 0) folds to a no-op
+    if (kStats) lse_fold_stats(M, S, Q, I, seg_m[g][lane], seg_s[g][lane], seg_q[g][lane], seg_i[g][lane]);
+    else lse_fold(M, S, seg_m[g][lane], seg_s[g][lane]);
+  }
+  const float l2s = fast_log2(S);
+  const float lse2 = M + l2s;
   const int64_t id = a.ids[t];
   const bool ok = id >= 0 && id < a.V_true;
   a.out_lp[t] = ok ? (a.tval[t] - lse2) * kLn2 : __builtin_nanf("");
   if (a.out_lse) a.out_lse[t] = lse2 * kLn2;
+  if (kStats) {
+    // H = ln 2 (log2 S - Q / S): the log-sum-exp minus the mean scaled logit.
+    a.out_ent[t] = (l2s - Q / S) * kLn2;
+    a.out_argmax[t] = I;
+  }
   if (!ok && a.bad_rows) atomicAdd(a.bad_rows, 1);
 }
 
@@ -641,45 +749,54 @@ static int stream_tokens(int64_t T) {
   return 0;
 }
 
-ScoreWorkspace score_workspace_layout(int64_t T, int64_t V_true) {
+ScoreWorkspace score_workspace_layout(int64_t T, int64_t V_true, bool stats) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t n_vt = (size_t)((V_true + kTileV - 1) / kTileV);
   const size_t rows = stream_tokens(T) ? 2 * n_vt : n_vt;  // half-tile partials
+  const size_t plane = rows * (size_t)T * sizeof(float);
   ScoreWorkspace w;
   w.off_m = 0;
-  w.off_s = up(w.off_m + rows * (size_t)T * sizeof(float));
-  w.off_t = up(w.off_s + rows * (size_t)T * sizeof(float));
-  w.total = up(w.off_t + (size_t)T * sizeof(float));
+  w.off_s = up(w.off_m + plane);
+  w.off_t = up(w.off_s + plane);
+  w.off_q = up(w.off_t + (size_t)T * sizeof(float));
+  w.off_i = stats ? up(w.off_q + plane) : w.off_q;
+  w.total = stats ? up(w.off_i + plane) : w.off_q;
   return w;
 }
 
-template <int ST>
+template <int ST, bool kStats>
 static void launch_stream(ScoreArgs a, hipStream_t stream) {
   a.n_tt = (a.T + 32 * ST - 1) / (32 * ST);
   const int n_items = 2 * a.n_vt * a.n_tt;
   // Workgroups (one wave each) per CU: as many as the LDS ring allows.
   const int per_cu = (160 * 1024) / Stream<ST>::kLds;
   const int grid = 256 * (per_cu < 8 ? per_cu : 8);
-  hipLaunchKernelGGL(score_stream_kernel<ST>, dim3(grid), dim3(64), 0, stream, a, n_items);
+  hipLaunchKernelGGL((score_stream_kernel<ST, kStats>), dim3(grid), dim3(64), 0, stream, a,
+                     n_items);
 }
 
-hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
+template <bool kStats>
+static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t stream) {
   const int st = stream_tokens(a.T);
-  if (st == 1) launch_stream<1>(a, stream);
-  else if (st == 2) launch_stream<2>(a, stream);
+  if (st == 1) launch_stream<1, kStats>(a, stream);
+  else if (st == 2) launch_stream<2, kStats>(a, stream);
   else {
     const unsigned grid = (unsigned)a.n_vt * (unsigned)a.n_tt;
-    hipLaunchKernelGGL(score_tile_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(score_tile_kernel<kStats>, dim3(grid), dim3(kThreads), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (st)
-    hipLaunchKernelGGL(lse_merge_kernel<true>, dim3((a.T + 63) / 64), dim3(64 * kMergeSegs), 0,
-                       stream, a);
+    hipLaunchKernelGGL((lse_merge_kernel<true, kStats>), dim3((a.T + 63) / 64),
+                       dim3(64 * kMergeSegs), 0, stream, a);
   else
-    hipLaunchKernelGGL(lse_merge_kernel<false>, dim3((a.T + 63) / 64), dim3(64 * kMergeSegs), 0,
-                       stream, a);
+    hipLaunchKernelGGL((lse_merge_kernel<false, kStats>), dim3((a.T + 63) / 64),
+                       dim3(64 * kMergeSegs), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
+  return a.out_ent ? launch_score_t<true>(a, stream) : launch_score_t<false>(a, stream);
 }
 
 }  // namespace lp

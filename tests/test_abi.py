@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["lp_status_string", "lp_score_workspace_bytes", "lp_score", "lp_compare"])
+        ["lp_status_string", "lp_score_workspace_bytes", "lp_score",
+         "lp_score_stats_workspace_bytes", "lp_score_stats", "lp_compare"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -57,6 +58,16 @@ def test_workspace_bytes(L):
         assert got >= 2 * n_vt * T * 4 + T * 4 and got % 256 == 0
     assert L.lp_score_workspace_bytes(-1, 64, 10, 10) == 0
     assert L.lp_score_workspace_bytes(4, 64, 10, 11) == 0
+
+
+def test_stats_workspace_holds_two_more_planes(L):
+    for T, V in ((64, 4096), (8192, 151936), (1, 1), (300, 1000)):
+        n_vt = -(-V // 256)
+        base = L.lp_score_workspace_bytes(T, 4096, V, V)
+        got = L.lp_score_stats_workspace_bytes(T, 4096, V, V)
+        assert got % 256 == 0 and got >= base + 2 * n_vt * T * 4
+    assert L.lp_score_stats_workspace_bytes(-1, 64, 10, 10) == 0
+    assert L.lp_score_stats_workspace_bytes(4, 64, 10, 11) == 0
 
 
 P = ctypes.c_void_p(0x10000)   # aligned, never dereferenced: every call below fails validation
@@ -87,6 +98,27 @@ def test_score_rejects_bad_arguments(L):
     assert score(L, ldh=68) == EUNSUP                                # ldh % 8
     assert score(L, hid=ctypes.c_void_p(0x10008)) == EUNSUP          # 16-byte alignment
     assert score(L, T=0, hid=None, w=None, ids=None, out=None, ws=None) == 0   # empty: no-op
+
+
+def score_stats(L, T=4, H=64, V=300, vt=300, temp=1.0, ent=P, am=P, ws=P, wsb=1 << 30,
+                ids=P, out=P):
+    return L.lp_score_stats(P, H, P, ids, T, H, V, vt, temp, out, None, ent, am, None, ws, wsb,
+                            None)
+
+
+def test_score_stats_rejects_bad_arguments(L):
+    EINVAL, EUNSUP = 1, 2
+    assert score_stats(L, ent=None) == EINVAL                          # entropy output required
+    assert score_stats(L, am=None) == EINVAL                           # argmax output required
+    assert score_stats(L, ids=None) == EINVAL
+    assert score_stats(L, out=None) == EINVAL
+    assert score_stats(L, temp=0.0) == EINVAL
+    assert score_stats(L, vt=301) == EINVAL
+    # a workspace large enough for lp_score but not for the two extra planes
+    need = L.lp_score_stats_workspace_bytes(4, 64, 300, 300)
+    assert score_stats(L, wsb=need - 256) == EINVAL
+    assert score_stats(L, H=96) == EUNSUP
+    assert score_stats(L, T=0, ent=None, am=None, ws=None, ids=None, out=None) == 0
 
 
 def cmp(L, N=2, Lq=5, ld=None, clip=2.0, atol=-1.0, out=P, a=P, m=P):
