@@ -71,9 +71,10 @@ def main() -> int:
                     help="sequence counts of the comparison bandwidth probe (L = 2304)")
     ap.add_argument("--small-batches", type=str, default="1,7,64",
                     help="row counts at which lp_score is timed as a stream over W")
-    ap.add_argument("--mode", choices=("bench", "score", "small", "compare", "copy"),
+    ap.add_argument("--mode", choices=("bench", "score", "stats", "small", "compare", "copy"),
                     default="bench",
-                    help="score: only `steps` lp_score calls on the benchmark batch; small: "
+                    help="score: only `steps` lp_score calls on the benchmark batch; stats: "
+                         "the same with lp_score_stats (entropy and argmax too); small: "
                          "`steps` lp_score calls on its first row; compare: `steps` lp_compare "
                          "calls at N=4096, L=2304 (these three for profilers); copy: one plain "
                          "1 GiB device copy (counter calibration)")
@@ -134,6 +135,26 @@ def main() -> int:
             lp.score(x, w, ids, out=out, workspace=ws)
         torch.cuda.synchronize()
         log(f"bench: {args.steps} lp_score calls done")
+        return 0
+    ent = torch.empty(T, dtype=torch.float32, device=dev)
+    amax = torch.empty(T, dtype=torch.int64, device=dev)
+    ws_stats = torch.empty(lp.score_stats_workspace_bytes(T, H, V), dtype=torch.uint8, device=dev)
+    out_stats = torch.empty(T, dtype=torch.float32, device=dev)
+    stats_args = (x.data_ptr(), H, w.data_ptr(), ids.data_ptr(), T, H, V, V, 1.0,
+                  out_stats.data_ptr(), None, ent.data_ptr(), amax.data_ptr(), None,
+                  ws_stats.data_ptr(), ws_stats.numel(), torch.cuda.current_stream().cuda_stream)
+    c_stats = lp._lib.lib().lp_score_stats
+
+    def score_stats_call():
+        st_ = c_stats(*stats_args)
+        if st_ != 0:
+            raise lp.LpError(st_, "lp_score_stats")
+
+    if args.mode == "stats":
+        for _ in range(args.steps):
+            score_stats_call()
+        torch.cuda.synchronize()
+        log(f"bench: {args.steps} lp_score_stats calls done")
         return 0
     if args.mode == "small":
         for _ in range(args.steps):
@@ -205,6 +226,18 @@ def main() -> int:
         torch.cuda.synchronize()
         t = sorted(e[0].elapsed_time(e[1]) * 1e3 / calls for e in evs)
         return t[len(t) // 2], t[0], t[-1]
+
+    # The same scoring with the row entropy and argmax (lp_score_stats).
+    st_med, st_lo, st_hi = median_us(score_stats_call, calls=3, reps=5)
+    score_stats_call()
+    torch.cuda.synchronize()
+    assert torch.equal(out_stats.view(torch.int32), out.view(torch.int32)), \
+        "lp_score_stats logprob bits differ from lp_score"
+    stats_rec = {"ms": round(st_med / 1e3, 4), "min_ms": round(st_lo / 1e3, 4),
+                 "max_ms": round(st_hi / 1e3, 4),
+                 "TFLOPs": round(flops / st_med / 1e6, 2),
+                 "frac": round(flops / st_med / 1e6 / PEAK_BF16_TFLOPS, 4)}
+    log(f"bench: lp_score_stats {st_med / 1e3:.3f} ms = {flops / st_med / 1e6:.1f} TFLOP/s")
 
     # Small batches: the product is a stream over W (HBM-bound); report the
     # algorithmic bytes (W, the rows, ids and outputs) per second.
@@ -282,6 +315,7 @@ def main() -> int:
                     "lp_score_ms_min": round(min(score_ms), 4),
                     "lp_score_ms_max": round(max(score_ms), 4),
                     "lp_compare_us": round(cmp_avg * 1e6, 2)},
+        "score_stats": stats_rec,
         "small_batch": small,
         "compare_sweep": sweep,
     }
