@@ -14,4 +14,4 @@ Every function cites the passage of the source pages it writes out:
 """
 
 from .score import bf16_bits_to_f64, score, score_stats, entropy_argmax, logits  # noqa: F401
-from .compare import compare, per_token, PAIRS, STAT_FIELDS  # noqa: F401
+from .compare import compare, per_token, tails, nearest_rank, PAIRS, STAT_FIELDS, TAIL_FIELDS  # noqa: F401

@@ -160,3 +160,78 @@ def per_token(A, B, C, mask, tis_clip: float = 2.0) -> np.ndarray:
             o = np.where(act & finite, v, np.where(act, np.nan, 0.0))
             out[p, j] = o.astype(np.float32)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Batch tail statistics of |Delta| per pair (lp_compare_tails)
+#
+#   [vLLM] §"Metric measurement basis": logprob_mae = sum(mask |lp_train -
+#          lp_serve|) / sum(mask) over valid tokens, "also report p95/max and
+#          position"; probability_mae = mean |exp(lp_train) - exp(lp_serve)|
+#          over valid tokens.
+#   [VeX] section 5, its list of practical indicators: record the p50 / p95 /
+#          p99 / max of abs(delta_logprob).
+#
+# Over the whole batch, per pair, the tokens counted are the active ones whose
+# two scores are finite (non-finite ones are reported by compare()).
+#   count          number of such tokens
+#   q50, q95, q99  nearest-rank order statistics of |Delta|: the value at
+#                  1-based rank ceil(p n / 100) of the ascending sort (p = 50,
+#                  95, 99; the rank is formed in integers); 0 when n = 0
+#   max_abs        max |Delta| (0 when n = 0)
+#   max_seq, max_pos  sequence and position (column) of the first token, in
+#                  row-major order, with |Delta| = max_abs (-1, -1 when n = 0)
+#   sum_abs        sum |Delta|                  (logprob_mae numerator)
+#   sum_prob_abs   sum |exp(left) - exp(right)| (probability_mae numerator)
+# and per position i (column) of the rows: the sum of |Delta| over the
+# sequences whose token there is counted, and how many are (pos_sum, pos_count)
+# -- the error-by-position profile.
+# ---------------------------------------------------------------------------
+
+TAIL_FIELDS = ("count", "q50", "q95", "q99", "max_abs", "max_seq", "max_pos",
+               "sum_abs", "sum_prob_abs")
+
+
+def nearest_rank(sorted_vals: np.ndarray, pct: int) -> float:
+    """Value at 1-based rank ceil(pct * n / 100) of an ascending array."""
+    n = sorted_vals.size
+    if n == 0:
+        return 0.0
+    rank = (pct * n + 99) // 100
+    return float(sorted_vals[rank - 1])
+
+
+def tails(A, B, C, mask):
+    """Per pair: dict of TAIL_FIELDS; plus pos_sum [3][L] fp64 and pos_count
+    [3][L] int64. Sums are exactly rounded (math.fsum)."""
+    A, B, C, mask = _check(A, B, C, mask)
+    sides = {"A": A, "B": B, "C": C}
+    N, L = A.shape
+    out = {}
+    pos_sum = np.zeros((3, L))
+    pos_count = np.zeros((3, L), np.int64)
+    for p, (ln, rn) in enumerate(PAIRS):
+        left = sides[ln].astype(np.float64)
+        right = sides[rn].astype(np.float64)
+        keep = (mask != 0) & np.isfinite(left) & np.isfinite(right)
+        delta = np.abs(left - right)
+        vals = delta[keep]                       # row-major order
+        srt = np.sort(vals)
+        rec = {"count": int(vals.size)}
+        for pct in (50, 95, 99):
+            rec[f"q{pct}"] = nearest_rank(srt, pct)
+        if vals.size:
+            mx = float(vals.max())
+            seqs, poss = np.nonzero(keep & (delta == mx))
+            rec.update(max_abs=mx, max_seq=int(seqs[0]), max_pos=int(poss[0]))
+        else:
+            rec.update(max_abs=0.0, max_seq=-1, max_pos=-1)
+        rec["sum_abs"] = math.fsum(vals.tolist())
+        prob = np.abs(np.exp(left) - np.exp(right))[keep]
+        rec["sum_prob_abs"] = math.fsum(prob.tolist())
+        out["".join((ln, rn))] = rec
+        for i in range(L):
+            col = delta[:, i][keep[:, i]]
+            pos_sum[p, i] = math.fsum(col.tolist())
+            pos_count[p, i] = col.size
+    return out, pos_sum, pos_count
