@@ -201,6 +201,62 @@ lp_status lp_compare(const float* gen_A, const float* replay_B,
                      int64_t L, int64_t ld, float tis_clip, float atol,
                      lp_seq_stats* out, float* per_token, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Batch tail statistics of the per-token differences
+ *
+ * For each pair (A,B), (B,C), (A,C) over the whole batch: the counted tokens
+ * are the active ones whose two scores are finite, Delta as for lp_compare.
+ *
+ *   count          number of counted tokens
+ *   q50, q95, q99  nearest-rank order statistics of |Delta|: the value at
+ *                  1-based rank ceil(p * count / 100) of the ascending order
+ *                  (p = 50, 95, 99); exact (a selection, not an estimate);
+ *                  0 when count == 0
+ *   max_abs        max |Delta| (0 when count == 0)
+ *   max_seq, max_pos  sequence and column of the first counted token, in
+ *                  row-major order, with |Delta| = max_abs (-1 when none)
+ *   sum_abs        sum |Delta|                  (logprob_mae = sum_abs / count)
+ *   sum_prob_abs   sum |exp(left) - exp(right)| (probability_mae numerator)
+ *
+ * [vLLM] "Metric measurement basis" (logprob_mae with its p95, max and
+ * position; probability_mae); [VeX] section 5, practical indicators (p50 /
+ * p95 / p99 / max of abs(delta_logprob)).
+ *
+ * pos_abs_sum / pos_count (both NULL or both non-NULL): [3][L] arrays, pair-
+ * major; for column i, the sum of |Delta| over the sequences whose token i
+ * is counted, and how many are -- the error-by-position profile.
+ *
+ * Integer results and the quantile and max values are exact; the fp64 sums
+ * are taken in a fixed order (bitwise reproducible run to run).
+ *
+ * Layout and arguments as for lp_compare; out is [3] lp_tail_stats in device
+ * memory; workspace: lp_compare_tails_workspace_bytes(N, L) bytes, 256-byte
+ * aligned, contents ignored. Errors: LP_EINVAL for N < 0, L < 0, ld < L, a
+ * NULL out or workspace, only one of pos_abs_sum / pos_count given, NULL
+ * inputs with N, L > 0, or a small or misaligned workspace. N == 0 or
+ * L == 0 writes the empty statistics (and zero profiles).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t count;
+  double q50;
+  double q95;
+  double q99;
+  double max_abs;
+  int32_t max_seq;
+  int32_t max_pos;
+  double sum_abs;
+  double sum_prob_abs;
+} lp_tail_stats;
+
+size_t lp_compare_tails_workspace_bytes(int64_t N, int64_t L);
+
+lp_status lp_compare_tails(const float* gen_A, const float* replay_B,
+                           const float* train_C, const uint8_t* mask,
+                           int64_t N, int64_t L, int64_t ld,
+                           lp_tail_stats* out, double* pos_abs_sum,
+                           int32_t* pos_count, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,6 +10,7 @@ streams.
     score(hidden, w, ids, temperature=1.0, v_true=None)   -> logprob [T] fp32
     score_stats(hidden, w, ids, ...)                      -> logprob, entropy, argmax
     compare(A, B, C, mask, tis_clip=2.0, atol=None)       -> stats per pair
+    compare_tails(A, B, C, mask, positions=False)         -> batch tails per pair
     align(hidden, input_ids, response_mask)               -> rows, targets, mask
 """
 
@@ -20,8 +21,8 @@ import ctypes
 import numpy as np
 import torch
 
-from ._lib import (EXPORTS, LP_OK, SEQ_STATS_DTYPE, LpError, lib,  # noqa: F401
-                   status_string)
+from ._lib import (EXPORTS, LP_OK, SEQ_STATS_DTYPE, TAIL_STATS_DTYPE, LpError,  # noqa: F401
+                   lib, status_string)
 
 PAIRS = ("AB", "BC", "AC")
 
@@ -144,9 +145,9 @@ def compare_raw(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch.T
     if not (A.shape == B.shape == C.shape == mask.shape) or A.dim() != 2:
         raise ValueError("A, B, C and mask must share one [N, L] shape")
     N, L = A.shape
-    ld = A.stride(0) if N else L
+    ld = A.stride(0) if A.numel() else L
     for t in (A, B, C, mask):
-        if t.stride(1) != 1 or (N > 1 and t.stride(0) != ld):
+        if t.numel() and (t.stride(1) != 1 or (N > 1 and t.stride(0) != ld)):
             raise ValueError("A, B, C and mask need unit column stride and one row stride")
     dev = A.device
     nbytes = 3 * N * SEQ_STATS_DTYPE.itemsize
@@ -186,6 +187,38 @@ def compare(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch.Tenso
             if np.any(stats[p]["nonfinite"] > 0):
                 raise ValueError(f"non-finite score on an active token ({p})")
     return (stats, pt) if per_token else stats
+
+
+def compare_tails(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch.Tensor,
+                  positions: bool = False):
+    """Batch tail statistics of |left - right| per pair (lp_compare_tails);
+    synchronises. Returns {"AB"|"BC"|"AC": numpy record of TAIL_STATS_DTYPE},
+    plus (pos_sum [3, L] fp64, pos_count [3, L] int32) when positions=True."""
+    for name, t in (("A", A), ("B", B), ("C", C)):
+        _need_cuda(name, t, torch.float32)
+    _need_cuda("mask", mask, torch.uint8)
+    if not (A.shape == B.shape == C.shape == mask.shape) or A.dim() != 2:
+        raise ValueError("A, B, C and mask must share one [N, L] shape")
+    N, L = A.shape
+    ld = A.stride(0) if A.numel() else L
+    for t in (A, B, C, mask):
+        if t.numel() and (t.stride(1) != 1 or (N > 1 and t.stride(0) != ld)):
+            raise ValueError("A, B, C and mask need unit column stride and one row stride")
+    dev = A.device
+    out = torch.empty(3 * TAIL_STATS_DTYPE.itemsize, dtype=torch.uint8, device=dev)
+    ps = torch.empty((3, L), dtype=torch.float64, device=dev) if positions else None
+    pc = torch.empty((3, L), dtype=torch.int32, device=dev) if positions else None
+    need = int(lib().lp_compare_tails_workspace_bytes(N, L))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib().lp_compare_tails(_ptr(A), _ptr(B), _ptr(C), _ptr(mask), N, L, max(ld, L),
+                                _ptr(out), _ptr(ps), _ptr(pc), _ptr(ws), need, _stream(dev))
+    if st != LP_OK:
+        raise LpError(st, "lp_compare_tails")
+    rec = out.cpu().numpy().view(TAIL_STATS_DTYPE)
+    tails = {p: rec[i] for i, p in enumerate(PAIRS)}
+    if positions:
+        return tails, ps.cpu().numpy(), pc.cpu().numpy()
+    return tails
 
 
 def align(hidden: torch.Tensor, input_ids: torch.Tensor, response_mask: torch.Tensor):

@@ -17,7 +17,8 @@ LP_OK, LP_EINVAL, LP_EUNSUPPORTED, LP_EHIP = 0, 1, 2, 3
 
 # Names of every function include/liblp.h declares.
 EXPORTS = ("lp_status_string", "lp_score_workspace_bytes", "lp_score",
-           "lp_score_stats_workspace_bytes", "lp_score_stats", "lp_compare")
+           "lp_score_stats_workspace_bytes", "lp_score_stats", "lp_compare",
+           "lp_compare_tails_workspace_bytes", "lp_compare_tails")
 
 # numpy mirror of `lp_seq_stats` (natural C alignment: 6 int32 then 7 double).
 SEQ_STATS_DTYPE = np.dtype([
@@ -27,6 +28,14 @@ SEQ_STATS_DTYPE = np.dtype([
     ("sum_k3", "<f8"), ("sum_d", "<f8"), ("seq_tis", "<f8"), ("sum_tok_tis", "<f8"),
 ], align=True)
 assert SEQ_STATS_DTYPE.itemsize == 80
+
+# numpy mirror of `lp_tail_stats`.
+TAIL_STATS_DTYPE = np.dtype([
+    ("count", "<i8"), ("q50", "<f8"), ("q95", "<f8"), ("q99", "<f8"),
+    ("max_abs", "<f8"), ("max_seq", "<i4"), ("max_pos", "<i4"),
+    ("sum_abs", "<f8"), ("sum_prob_abs", "<f8"),
+], align=True)
+assert TAIL_STATS_DTYPE.itemsize == 64
 
 
 class LpError(RuntimeError):
@@ -64,6 +73,11 @@ def lib() -> ctypes.CDLL:
                                  vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.lp_compare.restype = ctypes.c_int
     L.lp_compare.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, f32, vp, vp, vp]
+    L.lp_compare_tails_workspace_bytes.restype = ctypes.c_size_t
+    L.lp_compare_tails_workspace_bytes.argtypes = [i64, i64]
+    L.lp_compare_tails.restype = ctypes.c_int
+    L.lp_compare_tails.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp,
+                                   ctypes.c_size_t, vp]
     _lib = L
     return L
 

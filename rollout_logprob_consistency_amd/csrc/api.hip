@@ -143,4 +143,35 @@ lp_status lp_compare(const float* gen_A, const float* replay_B, const float* tra
   return lp::launch_compare(a, stream) == hipSuccess ? LP_OK : LP_EHIP;
 }
 
+size_t lp_compare_tails_workspace_bytes(int64_t N, int64_t L) {
+  if (N < 0 || L < 0 || N > kI32Max || L > kI32Max) return 0;
+  return lp::tails_workspace_bytes(N, L);
+}
+
+lp_status lp_compare_tails(const float* gen_A, const float* replay_B, const float* train_C,
+                           const uint8_t* mask, int64_t N, int64_t L, int64_t ld,
+                           lp_tail_stats* out, double* pos_abs_sum, int32_t* pos_count,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (N < 0 || L < 0 || ld < L) return LP_EINVAL;
+  if (!out || !workspace) return LP_EINVAL;
+  if ((pos_abs_sum == nullptr) != (pos_count == nullptr)) return LP_EINVAL;
+  if (N > 0 && L > 0 && (!gen_A || !replay_B || !train_C || !mask)) return LP_EINVAL;
+  if (L > kI32Max || N > kI32Max) return LP_EUNSUPPORTED;
+  if (workspace_bytes < lp::tails_workspace_bytes(N, L) || !aligned(workspace, 256))
+    return LP_EINVAL;
+  lp::TailArgs a;
+  a.A = gen_A;
+  a.B = replay_B;
+  a.C = train_C;
+  a.mask = mask;
+  a.N = N;
+  a.L = L;
+  a.ld = ld;
+  a.out = out;
+  a.pos_sum = pos_abs_sum;
+  a.pos_count = pos_count;
+  a.workspace = workspace;
+  return lp::launch_tails(a, stream) == hipSuccess ? LP_OK : LP_EHIP;
+}
+
 }  // extern "C"

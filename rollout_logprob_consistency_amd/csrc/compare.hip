@@ -327,3 +327,352 @@ hipError_t launch_compare(const CompareArgs& a, hipStream_t stream) {
 }
 
 }  // namespace lp
+
+namespace lp {
+
+// ---------------------------------------------------------------------------
+// Batch tail statistics of |delta| per pair (lp_compare_tails): the p50 / p95
+// / p99 / max of abs(delta_logprob) that "Diagnosing Training Inference
+// Mismatch in LLM Reinforcement Learning" (section 5, practical indicators)
+// asks to record, and the logprob_mae / probability_mae numerators with the
+// worst token's position of "Fault localization and mismatch bisect" ("Metric
+// measurement basis"), plus the error-by-position profile.
+//
+// Exact order statistics by radix selection on the bit patterns of |delta|
+// (non-negative fp64, so the bits order like the values): 8 passes of one
+// byte, each a histogram pass over the batch -- one workgroup per sequence,
+// LDS counters, integer atomics into 9 global histograms (3 pairs x 3
+// quantiles) -- and a one-workgroup select that keeps, per target, the byte
+// where the wanted rank falls. Every count is an integer, so the result does
+// not depend on the order in which workgroups run. The sums and the first
+// worst token are formed per sequence in a fixed order (pass 0) and reduced
+// in a fixed tree; the position profile folds fixed chunks of sequences in
+// order.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kTailTargets = 9;     // 3 pairs x (p50, p95, p99)
+constexpr int kTailThreads = 256;
+constexpr int kTailChunks = 64;     // sequence chunks of the position profile
+
+struct TailSel {
+  uint64_t prefix;   // bytes of the selected key found so far
+  int64_t rank;      // 1-based rank still wanted below that prefix; 0: none
+};
+
+struct TailPart {    // one (sequence, pair), from pass 0
+  double sum_abs, sum_prob;
+  uint64_t max_key;  // bits of the largest |delta| (0 without tokens)
+  int32_t max_pos;   // its first column, -1 without tokens
+  int32_t count;
+};
+
+struct TailWs {
+  uint32_t* hist;    // [9][256]
+  TailSel* sel;      // [9]
+  int64_t* count;    // [3]
+  TailPart* part;    // [N][3]
+  double* pos_part;  // [nch][3][L]
+  int32_t* pos_cpart;
+  int nch;
+};
+
+__host__ __device__ inline size_t tail_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+TailWs tail_layout(void* base, int64_t N, int64_t L) {
+  char* p = static_cast<char*>(base);
+  TailWs w;
+  size_t o = 0;
+  w.hist = reinterpret_cast<uint32_t*>(p + o); o = tail_up(o + kTailTargets * 256 * sizeof(uint32_t));
+  w.sel = reinterpret_cast<TailSel*>(p + o);   o = tail_up(o + kTailTargets * sizeof(TailSel));
+  w.count = reinterpret_cast<int64_t*>(p + o); o = tail_up(o + 3 * sizeof(int64_t));
+  w.part = reinterpret_cast<TailPart*>(p + o); o = tail_up(o + (size_t)N * 3 * sizeof(TailPart));
+  w.nch = (int)(N < kTailChunks ? (N < 1 ? 1 : N) : kTailChunks);
+  w.pos_part = reinterpret_cast<double*>(p + o); o = tail_up(o + (size_t)w.nch * 3 * L * sizeof(double));
+  w.pos_cpart = reinterpret_cast<int32_t*>(p + o);
+  return w;
+}
+
+size_t tail_bytes(int64_t N, int64_t L) {
+  size_t o = 0;
+  o = tail_up(o + kTailTargets * 256 * sizeof(uint32_t));
+  o = tail_up(o + kTailTargets * sizeof(TailSel));
+  o = tail_up(o + 3 * sizeof(int64_t));
+  o = tail_up(o + (size_t)N * 3 * sizeof(TailPart));
+  const int nch = (int)(N < kTailChunks ? (N < 1 ? 1 : N) : kTailChunks);
+  o = tail_up(o + (size_t)nch * 3 * L * sizeof(double));
+  o = tail_up(o + (size_t)nch * 3 * L * sizeof(int32_t));
+  return o;
+}
+
+// Left and right side of pair p among the three scores (A, B, C).
+__device__ __forceinline__ int pair_left(int p) { return p == 1 ? 1 : 0; }
+__device__ __forceinline__ int pair_right(int p) { return p == 0 ? 1 : 2; }
+
+__global__ __launch_bounds__(kTailThreads) void tails_init_kernel(TailWs w) {
+  for (int i = threadIdx.x; i < kTailTargets * 256; i += kTailThreads) w.hist[i] = 0u;
+  if (threadIdx.x < kTailTargets) w.sel[threadIdx.x] = TailSel{0ull, 0};
+}
+
+// One histogram pass; pass 0 also forms the per-sequence sums and maxima.
+__global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, TailWs w, int pass) {
+  __shared__ uint32_t h[kTailTargets * 256];
+  __shared__ TailPart red[3][kTailThreads];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kTailTargets * 256; i += kTailThreads) h[i] = 0u;
+  const int shift = 56 - 8 * pass;  // this pass's byte: key bits [shift + 7 : shift]
+  uint64_t pre[kTailTargets];
+  bool want[kTailTargets];
+#pragma unroll
+  for (int t = 0; t < kTailTargets; ++t) {
+    pre[t] = pass ? w.sel[t].prefix : 0ull;
+    want[t] = pass == 0 || w.sel[t].rank > 0;
+  }
+  __syncthreads();
+
+  const int64_t n = blockIdx.x;
+  const float* rows[3] = {a.A + n * a.ld, a.B + n * a.ld, a.C + n * a.ld};
+  const uint8_t* M = a.mask + n * a.ld;
+  TailPart mine[3];
+#pragma unroll
+  for (int p = 0; p < 3; ++p) mine[p] = TailPart{0.0, 0.0, 0ull, -1, 0};
+  for (int64_t i = tid; i < a.L; i += kTailThreads) {
+    if (M[i] == 0) continue;
+    const float v[3] = {rows[0][i], rows[1][i], rows[2][i]};
+    double e[3] = {0.0, 0.0, 0.0};
+    if (pass == 0) {
+#pragma unroll
+      for (int s = 0; s < 3; ++s)
+        if (__builtin_isfinite(v[s])) e[s] = exp_f64((double)v[s]);
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const float l = v[pair_left(p)], r = v[pair_right(p)];
+      if (!__builtin_isfinite(l) || !__builtin_isfinite(r)) continue;
+      const double d = fabs((double)l - (double)r);
+      const uint64_t key = (uint64_t)__double_as_longlong(d);
+      const uint32_t digit = (uint32_t)(key >> shift) & 255u;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int t = 3 * p + j;
+        if (want[t] && (pass == 0 || (key >> (shift + 8)) == pre[t])) atomicAdd(&h[t * 256 + digit], 1u);
+      }
+      if (pass == 0) {
+        TailPart& m = mine[p];
+        m.sum_abs += d;
+        m.sum_prob += fabs(e[pair_left(p)] - e[pair_right(p)]);
+        if (m.max_pos < 0 || key > m.max_key) {  // positions ascend: the first one stays
+          m.max_key = key;
+          m.max_pos = (int32_t)i;
+        }
+        m.count += 1;
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kTailTargets * 256; i += kTailThreads)
+    if (h[i]) atomicAdd(&w.hist[i], h[i]);
+  if (pass != 0) return;
+
+  // Fixed tree over the threads (thread t holds the columns = t mod 256).
+#pragma unroll
+  for (int p = 0; p < 3; ++p) red[p][tid] = mine[p];
+  __syncthreads();
+  for (int stride = kTailThreads / 2; stride > 0; stride >>= 1) {
+    if (tid < stride) {
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        TailPart x = red[p][tid];
+        const TailPart y = red[p][tid + stride];
+        x.sum_abs += y.sum_abs;
+        x.sum_prob += y.sum_prob;
+        x.count += y.count;
+        if (y.max_pos >= 0 &&
+            (x.max_pos < 0 || y.max_key > x.max_key || (y.max_key == x.max_key && y.max_pos < x.max_pos))) {
+          x.max_key = y.max_key;
+          x.max_pos = y.max_pos;
+        }
+        red[p][tid] = x;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid < 3) w.part[n * 3 + tid] = red[tid][0];
+}
+
+// Select the byte of each target's key; one wave per target, 4 bins a lane.
+__global__ __launch_bounds__(64 * kTailTargets) void tails_select_kernel(TailWs w, int pass) {
+  const int t = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t* hist = w.hist + t * 256;
+  uint32_t c[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) c[k] = hist[4 * lane + k];
+  const int64_t lsum = (int64_t)c[0] + c[1] + c[2] + c[3];
+  int64_t incl = lsum;  // inclusive scan over lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  const int64_t total = __shfl(incl, 63);
+  int64_t rank;
+  if (pass == 0) {
+    // The pass-0 histogram holds every counted token of the pair.
+    const int64_t pct = (t % 3 == 0) ? 50 : (t % 3 == 1 ? 95 : 99);
+    rank = total > 0 ? (pct * total + 99) / 100 : 0;
+    if (t % 3 == 0 && lane == 0) w.count[t / 3] = total;
+  } else {
+    rank = w.sel[t].rank;
+  }
+  const int64_t excl = incl - lsum;
+  if (rank > 0 && excl < rank && rank <= incl) {
+    int64_t below = excl;
+    int k = 0;
+    while (below + (int64_t)c[k] < rank) below += c[k++];
+    w.sel[t].prefix = (pass ? (w.sel[t].prefix << 8) : 0ull) | (uint64_t)(4 * lane + k);
+    w.sel[t].rank = rank - below;
+  } else if (rank == 0 && lane == 0) {
+    w.sel[t].rank = 0;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) hist[4 * lane + k] = 0u;
+}
+
+// Batch results per pair: fixed chunks of sequences per thread, fixed tree.
+__global__ __launch_bounds__(kTailThreads) void tails_final_kernel(TailArgs a, TailWs w) {
+  __shared__ TailPart red[kTailThreads];
+  __shared__ int32_t red_seq[kTailThreads];
+  const int tid = threadIdx.x;
+  const int64_t per = (a.N + kTailThreads - 1) / kTailThreads;
+  for (int p = 0; p < 3; ++p) {
+    TailPart x{0.0, 0.0, 0ull, -1, 0};
+    int32_t xs = -1;
+    const int64_t lo = tid * per, hi = min(a.N, lo + per);
+    for (int64_t n = lo; n < hi; ++n) {
+      const TailPart y = w.part[n * 3 + p];
+      x.sum_abs += y.sum_abs;
+      x.sum_prob += y.sum_prob;
+      x.count += y.count;
+      if (y.max_pos >= 0 && (x.max_pos < 0 || y.max_key > x.max_key)) {  // n ascends
+        x.max_key = y.max_key;
+        x.max_pos = y.max_pos;
+        xs = (int32_t)n;
+      }
+    }
+    red[tid] = x;
+    red_seq[tid] = xs;
+    __syncthreads();
+    for (int stride = kTailThreads / 2; stride > 0; stride >>= 1) {
+      if (tid < stride) {
+        TailPart u = red[tid];
+        const TailPart v = red[tid + stride];
+        u.sum_abs += v.sum_abs;
+        u.sum_prob += v.sum_prob;
+        u.count += v.count;
+        // After the first steps a thread's sequences interleave with its
+        // partner's, so an equal key is decided by the sequence index.
+        const int32_t us = red_seq[tid], vs = red_seq[tid + stride];
+        if (v.max_pos >= 0 &&
+            (u.max_pos < 0 || v.max_key > u.max_key || (v.max_key == u.max_key && vs < us))) {
+          u.max_key = v.max_key;
+          u.max_pos = v.max_pos;
+          red_seq[tid] = vs;
+        }
+        red[tid] = u;
+      }
+      __syncthreads();
+    }
+    if (tid == 0) {
+      const TailPart& r = red[0];
+      lp_tail_stats o;
+      o.count = w.count[p];
+      const bool any = o.count > 0;
+      o.q50 = any ? __longlong_as_double((long long)w.sel[3 * p].prefix) : 0.0;
+      o.q95 = any ? __longlong_as_double((long long)w.sel[3 * p + 1].prefix) : 0.0;
+      o.q99 = any ? __longlong_as_double((long long)w.sel[3 * p + 2].prefix) : 0.0;
+      o.max_abs = any ? __longlong_as_double((long long)r.max_key) : 0.0;
+      o.max_seq = any ? red_seq[0] : -1;
+      o.max_pos = any ? r.max_pos : -1;
+      o.sum_abs = r.sum_abs;
+      o.sum_prob_abs = r.sum_prob;
+      a.out[p] = o;
+    }
+    __syncthreads();
+  }
+}
+
+// Position profile, stage 1: chunk c of the sequences, column i.
+__global__ __launch_bounds__(kTailThreads) void tails_pos_kernel(TailArgs a, TailWs w) {
+  const int64_t i = (int64_t)blockIdx.x * kTailThreads + threadIdx.x;
+  if (i >= a.L) return;
+  const int c = blockIdx.y;
+  const int64_t per = (a.N + w.nch - 1) / w.nch;
+  const int64_t lo = c * per, hi = min(a.N, lo + per);
+  double s[3] = {0.0, 0.0, 0.0};
+  int32_t k[3] = {0, 0, 0};
+  for (int64_t n = lo; n < hi; ++n) {
+    const int64_t o = n * a.ld + i;
+    if (a.mask[o] == 0) continue;
+    const float v[3] = {a.A[o], a.B[o], a.C[o]};
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const float l = v[pair_left(p)], r = v[pair_right(p)];
+      if (!__builtin_isfinite(l) || !__builtin_isfinite(r)) continue;
+      s[p] += fabs((double)l - (double)r);
+      k[p] += 1;
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    w.pos_part[((size_t)c * 3 + p) * a.L + i] = s[p];
+    w.pos_cpart[((size_t)c * 3 + p) * a.L + i] = k[p];
+  }
+}
+
+// Position profile, stage 2: fold the chunks in order.
+__global__ __launch_bounds__(kTailThreads) void tails_pos_fold_kernel(TailArgs a, TailWs w) {
+  const int64_t idx = (int64_t)blockIdx.x * kTailThreads + threadIdx.x;  // p * L + i
+  if (idx >= 3 * a.L) return;
+  double s = 0.0;
+  int32_t k = 0;
+  for (int c = 0; c < w.nch; ++c) {
+    s += w.pos_part[(size_t)c * 3 * a.L + idx];
+    k += w.pos_cpart[(size_t)c * 3 * a.L + idx];
+  }
+  a.pos_sum[idx] = s;
+  a.pos_count[idx] = k;
+}
+
+}  // namespace
+
+size_t tails_workspace_bytes(int64_t N, int64_t L) { return tail_bytes(N, L); }
+
+hipError_t launch_tails(const TailArgs& a, hipStream_t stream) {
+  const TailWs w = tail_layout(a.workspace, a.N, a.L);
+  hipLaunchKernelGGL(tails_init_kernel, dim3(1), dim3(kTailThreads), 0, stream, w);
+  if (a.N > 0) {
+    // Every pass runs, also with L == 0 (pass 0 then writes empty partials).
+    for (int pass = 0; pass < 8; ++pass) {
+      hipLaunchKernelGGL(tails_hist_kernel, dim3((unsigned)a.N), dim3(kTailThreads), 0, stream,
+                         a, w, pass);
+      hipLaunchKernelGGL(tails_select_kernel, dim3(1), dim3(64 * kTailTargets), 0, stream, w,
+                         pass);
+    }
+  } else {
+    // No sequence: empty histograms give count 0 and no rank to select.
+    hipLaunchKernelGGL(tails_select_kernel, dim3(1), dim3(64 * kTailTargets), 0, stream, w, 0);
+  }
+  hipLaunchKernelGGL(tails_final_kernel, dim3(1), dim3(kTailThreads), 0, stream, a, w);
+  if (a.pos_sum && a.L > 0) {
+    // Stage 1 also runs with N == 0, writing zero partials for the fold.
+    hipLaunchKernelGGL(tails_pos_kernel,
+                       dim3((unsigned)((a.L + kTailThreads - 1) / kTailThreads), (unsigned)w.nch),
+                       dim3(kTailThreads), 0, stream, a, w);
+    hipLaunchKernelGGL(tails_pos_fold_kernel,
+                       dim3((unsigned)((3 * a.L + kTailThreads - 1) / kTailThreads)),
+                       dim3(kTailThreads), 0, stream, a, w);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lp

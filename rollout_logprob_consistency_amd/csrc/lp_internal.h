@@ -67,4 +67,19 @@ struct CompareArgs {
 
 hipError_t launch_compare(const CompareArgs& a, hipStream_t stream);
 
+struct TailArgs {
+  const float* A;
+  const float* B;
+  const float* C;
+  const uint8_t* mask;
+  int64_t N, L, ld;
+  lp_tail_stats* out;     // [3]
+  double* pos_sum;        // [3][L] or null
+  int32_t* pos_count;     // [3][L] or null (null iff pos_sum is)
+  void* workspace;
+};
+
+size_t tails_workspace_bytes(int64_t N, int64_t L);
+hipError_t launch_tails(const TailArgs& a, hipStream_t stream);
+
 }  // namespace lp

@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["lp_status_string", "lp_score_workspace_bytes", "lp_score",
-         "lp_score_stats_workspace_bytes", "lp_score_stats", "lp_compare"])
+         "lp_score_stats_workspace_bytes", "lp_score_stats", "lp_compare",
+         "lp_compare_tails_workspace_bytes", "lp_compare_tails"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -164,3 +165,29 @@ def test_align_shift_on_cpu():
     assert mask.tolist() == [0, 0, 1, 1, 1, 0, 0, 1, 1, 0, 0, 0]
     with pytest.raises(ValueError):
         lp.align(hidden, ids, torch.ones_like(ids))
+
+
+def tails(L, N=2, Lq=5, ld=None, out=P, ws=P, wsb=1 << 30, ps=None, pc=None, a=P):
+    return L.lp_compare_tails(a, P, P, P, N, Lq, Lq if ld is None else ld, out, ps, pc, ws, wsb,
+                              None)
+
+
+def test_compare_tails_rejects_bad_arguments(L):
+    EINVAL = 1
+    assert tails(L, N=-1) == EINVAL
+    assert tails(L, Lq=-1) == EINVAL
+    assert tails(L, ld=3) == EINVAL
+    assert tails(L, out=None) == EINVAL
+    assert tails(L, ws=None) == EINVAL
+    assert tails(L, ps=P) == EINVAL                      # one profile array without the other
+    assert tails(L, a=None) == EINVAL
+    assert tails(L, wsb=L.lp_compare_tails_workspace_bytes(2, 5) - 1) == EINVAL
+    assert tails(L, ws=ctypes.c_void_p(0x10010)) == EINVAL
+    assert L.lp_compare_tails_workspace_bytes(-1, 5) == 0
+
+
+def test_tail_stats_layout():
+    from rollout_logprob_consistency_amd import _lib
+    assert _lib.TAIL_STATS_DTYPE.itemsize == 64
+    assert [_lib.TAIL_STATS_DTYPE.fields[f][1] for f in ("count", "q50", "max_seq", "max_pos", "sum_abs")] == \
+        [0, 8, 40, 44, 48]

@@ -1,0 +1,104 @@
+"""GPU parity of lp_compare_tails (batch tail statistics of |left - right| per
+pair) against the oracle: counts, quantiles, maxima and their positions, and
+the position counts exact; fp64 sums to 1e-9 relative. Every call goes
+through the C ABI (liblp.so)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import rollout_logprob_consistency_amd as lp
+from workloads import synth
+
+from .gpu_helpers import dev
+
+pytestmark = pytest.mark.gpu
+
+EXACT = ("count", "q50", "q95", "q99", "max_abs", "max_seq", "max_pos")
+SUMS = ("sum_abs", "sum_prob_abs")
+
+
+def run(A, B, C, M, positions=True):
+    got, ps, pc = lp.compare_tails(dev(A), dev(B), dev(C), dev(M), positions=True)
+    ref, rps, rpc = oracle.tails(A, B, C, M)
+    for p in lp.PAIRS:
+        for f in EXACT:
+            assert got[p][f] == ref[p][f], (p, f, got[p][f], ref[p][f])
+        for f in SUMS:
+            np.testing.assert_allclose(got[p][f], ref[p][f], rtol=1e-9, atol=1e-300, err_msg=f"{p} {f}")
+    assert np.array_equal(pc.astype(np.int64), rpc)
+    np.testing.assert_allclose(ps, rps, rtol=1e-9, atol=1e-300)
+    return got, ps, pc
+
+
+@pytest.fixture(scope="module")
+def record():
+    return synth.compare_case(N=8, max_resp=2048, prompt=256, seed=0)
+
+
+def test_identical_scores(record):
+    got, _, _ = run(record.A, record.B, record.C, record.mask)
+    assert got["AB"]["max_abs"] == 0.0 and got["AB"]["q99"] == 0.0
+
+
+@pytest.mark.parametrize("fault", ["noise", "shift", "case1", "case2"])
+def test_faults(record, fault):
+    c = record
+    A, C = c.A, c.C
+    if fault == "noise":
+        C = synth.noise_scores(c.C, c.mask, 1e-3, seed=21)
+    elif fault == "shift":
+        C = synth.shift_scores(c.C, seq=3, k=1, fill=-5.0)
+    elif fault == "case1":
+        A = synth.offset_scores(c.A, c.mask, 0.10, first_pos=1)
+    else:
+        C = synth.offset_scores(c.C, c.mask, 0.10)
+    got, _, _ = run(A, c.B, C, c.mask)
+    assert got["AC"]["count"] > 0
+
+
+def test_stale_weights_rescoring():
+    # B scored with W, C with W' = bf16(W + N(0, 1e-3)), both by the oracle.
+    x, w, w_stale, ids = synth.stale_inputs()
+    N, L = 8, 2304
+    B = oracle.score(x, w, ids)[0].astype(np.float32).reshape(N, L)
+    C = oracle.score(x, w_stale, ids)[0].astype(np.float32).reshape(N, L)
+    rec = synth.compare_case(N=N, max_resp=2048, prompt=256, seed=5, B=B)
+    Cm = rec.C.copy()
+    act = rec.mask != 0
+    Cm[act] = C[act]
+    got, _, _ = run(rec.A, rec.B, Cm, rec.mask)
+    assert got["BC"]["q50"] > 0.0
+
+
+def test_masks_nonfinite_and_ties():
+    rng = np.random.default_rng(3)
+    N, L = 37, 301
+    B = rng.standard_normal((N, L)).astype(np.float32) - 3.0
+    A = B + np.round(rng.standard_normal((N, L)), 1).astype(np.float32) * np.float32(0.5)
+    C = B.copy()
+    C[rng.random((N, L)) < 0.3] -= np.float32(0.25)
+    M = (rng.random((N, L)) < 0.8).astype(np.uint8)
+    A[2, 5] = np.nan; C[7, 9] = np.inf; B[11, 300] = -np.inf
+    run(A.astype(np.float32), B, C, M)
+
+
+@pytest.mark.parametrize("N,L", [(0, 5), (3, 0), (1, 1)])
+def test_degenerate_sizes(N, L):
+    A = np.zeros((N, L), np.float32)
+    M = np.ones((N, L), np.uint8)
+    got, ps, pc = lp.compare_tails(dev(A), dev(A), dev(A), dev(M), positions=True)
+    ref, rps, rpc = oracle.tails(A, A, A, M)
+    for p in lp.PAIRS:
+        for f in EXACT + SUMS:
+            assert got[p][f] == ref[p][f], (p, f)
+    assert ps.shape == (3, L) and np.array_equal(pc.astype(np.int64), rpc)
+
+
+def test_sweep_size_and_repeatability():
+    c = synth.compare_sweep_case(N=512)
+    got, ps, pc = run(c.A, c.B, c.C, c.mask)
+    again, ps2, pc2 = lp.compare_tails(dev(c.A), dev(c.B), dev(c.C), dev(c.mask), positions=True)
+    for p in lp.PAIRS:
+        assert got[p].tobytes() == again[p].tobytes()
+    assert ps.tobytes() == ps2.tobytes() and pc.tobytes() == pc2.tobytes()
