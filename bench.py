@@ -255,6 +255,7 @@ def main() -> int:
 
     # Comparison bandwidth probe at sizes that are not launch-latency bound.
     sweep = []
+    tails_rec = None
     for n_seq in (int(v) for v in args.sweep_n.split(",") if v):
         sc = synth.compare_sweep_case(N=n_seq)
         tA, tB, tC, tM = (torch.from_numpy(a).to(dev) for a in (sc.A, sc.B, sc.C, sc.mask))
@@ -270,6 +271,26 @@ def main() -> int:
                       "frac_hbm": round(nbytes / med / 1e3 / PEAK_HBM_GBPS, 4),
                       "bytes_per_token": 13})
         log(f"bench: lp_compare N={sc.N} L={sc.L}: {med:.1f} us = {nbytes / med / 1e3:.1f} GB/s")
+        if sc.N == max(int(v) for v in args.sweep_n.split(",") if v):
+            # Batch tail statistics on the same arrays: 8 selection passes and
+            # the position profile each read the 13 bytes of every position.
+            tw = torch.empty(lp._lib.lib().lp_compare_tails_workspace_bytes(sc.N, sc.L),
+                             dtype=torch.uint8, device=dev)
+            tout = torch.empty(3 * lp.TAIL_STATS_DTYPE.itemsize, dtype=torch.uint8, device=dev)
+            tps = torch.empty((3, sc.L), dtype=torch.float64, device=dev)
+            tpc = torch.empty((3, sc.L), dtype=torch.int32, device=dev)
+            targs = (tA.data_ptr(), tB.data_ptr(), tC.data_ptr(), tM.data_ptr(), sc.N, sc.L,
+                     sc.L, tout.data_ptr(), tps.data_ptr(), tpc.data_ptr(), tw.data_ptr(),
+                     tw.numel(), torch.cuda.current_stream().cuda_stream)
+            c_tails = lp._lib.lib().lp_compare_tails
+            tmed, tlo, thi = median_us(lambda: c_tails(*targs), calls=5, reps=5)
+            tbytes = 9 * 13.0 * sc.N * sc.L
+            tails_rec = {"N": sc.N, "L": sc.L, "us": round(tmed, 2), "min_us": round(tlo, 2),
+                         "max_us": round(thi, 2), "passes": 9,
+                         "GBps": round(tbytes / tmed / 1e3, 1),
+                         "frac_hbm": round(tbytes / tmed / 1e3 / PEAK_HBM_GBPS, 4)}
+            log(f"bench: lp_compare_tails N={sc.N} L={sc.L}: {tmed:.1f} us "
+                f"({tbytes / tmed / 1e3:.1f} GB/s over 9 passes)")
         del tA, tB, tC, tM
 
     cpu = None
@@ -318,6 +339,7 @@ def main() -> int:
         "score_stats": stats_rec,
         "small_batch": small,
         "compare_sweep": sweep,
+        "compare_tails": tails_rec,
     }
     print(json.dumps(rec), flush=True)
     return 0

@@ -409,6 +409,15 @@ size_t tail_bytes(int64_t N, int64_t L) {
 __device__ __forceinline__ int pair_left(int p) { return p == 1 ? 1 : 0; }
 __device__ __forceinline__ int pair_right(int p) { return p == 0 ? 1 : 2; }
 
+// The target whose histogram target t reads: the first target of its pair
+// that is selecting under the same prefix (every one of them in pass 0).
+__device__ __forceinline__ int tail_src(const uint64_t* pre, const bool* want, int t) {
+  const int p0 = 3 * (t / 3);
+  for (int u = p0; u < t; ++u)
+    if (want[u] && pre[u] == pre[t]) return u;
+  return t;
+}
+
 __global__ __launch_bounds__(kTailThreads) void tails_init_kernel(TailWs w) {
   for (int i = threadIdx.x; i < kTailTargets * 256; i += kTailThreads) w.hist[i] = 0u;
   if (threadIdx.x < kTailTargets) w.sel[threadIdx.x] = TailSel{0ull, 0};
@@ -421,6 +430,8 @@ __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, Ta
   const int tid = threadIdx.x;
   for (int i = tid; i < kTailTargets * 256; i += kTailThreads) h[i] = 0u;
   const int shift = 56 - 8 * pass;  // this pass's byte: key bits [shift + 7 : shift]
+  // Targets of one pair whose prefixes agree see the same tokens: only the
+  // first of them counts (tail_src() below names it for the select kernel).
   uint64_t pre[kTailTargets];
   bool want[kTailTargets];
 #pragma unroll
@@ -428,6 +439,9 @@ __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, Ta
     pre[t] = pass ? w.sel[t].prefix : 0ull;
     want[t] = pass == 0 || w.sel[t].rank > 0;
   }
+#pragma unroll
+  for (int t = 0; t < kTailTargets; ++t)
+    if (tail_src(pre, want, t) != t) want[t] = false;
   __syncthreads();
 
   const int64_t n = blockIdx.x;
@@ -436,11 +450,20 @@ __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, Ta
   TailPart mine[3];
 #pragma unroll
   for (int p = 0; p < 3; ++p) mine[p] = TailPart{0.0, 0.0, 0ull, -1, 0};
-  for (int64_t i = tid; i < a.L; i += kTailThreads) {
-    if (M[i] == 0) continue;
-    const float v[3] = {rows[0][i], rows[1][i], rows[2][i]};
+  const int lane = tid & 63;
+  // Rounded up to whole waves so that every lane of a wave takes part in the
+  // ballots below; positions past L are inactive.
+  const int64_t Lw = (a.L + kTailThreads - 1) / kTailThreads * kTailThreads;
+  for (int64_t i = tid; i < Lw; i += kTailThreads) {
+    const bool act = i < a.L && M[i] != 0;
+    float v[3] = {0.f, 0.f, 0.f};
+    if (act) {
+      v[0] = rows[0][i];
+      v[1] = rows[1][i];
+      v[2] = rows[2][i];
+    }
     double e[3] = {0.0, 0.0, 0.0};
-    if (pass == 0) {
+    if (pass == 0 && act) {
 #pragma unroll
       for (int s = 0; s < 3; ++s)
         if (__builtin_isfinite(v[s])) e[s] = exp_f64((double)v[s]);
@@ -448,15 +471,36 @@ __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, Ta
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
       const float l = v[pair_left(p)], r = v[pair_right(p)];
-      if (!__builtin_isfinite(l) || !__builtin_isfinite(r)) continue;
+      const bool ok = act && __builtin_isfinite(l) && __builtin_isfinite(r);
       const double d = fabs((double)l - (double)r);
       const uint64_t key = (uint64_t)__double_as_longlong(d);
       const uint32_t digit = (uint32_t)(key >> shift) & 255u;
+      // After the first passes few tokens share any target's prefix: one
+      // ballot per pair lets a wave with no such token skip the targets.
+      bool any = ok && pass == 0;
+      if (pass != 0) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+          any = any || (ok && want[3 * p + j] && (key >> (shift + 8)) == pre[3 * p + j]);
+      }
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
         const int t = 3 * p + j;
-        if (want[t] && (pass == 0 || (key >> (shift + 8)) == pre[t])) atomicAdd(&h[t * 256 + digit], 1u);
+        if (!want[t] || __ballot(any) == 0) continue;  // uniform
+        const bool hit = ok && (pass == 0 || (key >> (shift + 8)) == pre[t]);
+        const uint64_t hb = __ballot(hit);
+        if (hb == 0) continue;
+        // One atomic for the wave when all its hits share a bin (the common
+        // case: runs of identical scores put every lane in bin 0).
+        const int first = __ffsll((long long)hb) - 1;
+        const uint32_t d0 = (uint32_t)__shfl((int)digit, first);
+        if (__ballot(hit && digit != d0) == 0) {
+          if (lane == first) atomicAdd(&h[t * 256 + d0], (uint32_t)__popcll(hb));
+        } else if (hit) {
+          atomicAdd(&h[t * 256 + digit], 1u);
+        }
       }
+      if (!ok) continue;
       if (pass == 0) {
         TailPart& m = mine[p];
         m.sum_abs += d;
@@ -501,12 +545,26 @@ __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, Ta
 }
 
 // Select the byte of each target's key; one wave per target, 4 bins a lane.
+// A target reads the histogram of tail_src() (the same prefix within its
+// pair); every histogram is read before any is cleared or any prefix moves.
 __global__ __launch_bounds__(64 * kTailTargets) void tails_select_kernel(TailWs w, int pass) {
   const int t = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  uint32_t* hist = w.hist + t * 256;
+  uint64_t pre[kTailTargets];
+  bool want[kTailTargets];
+#pragma unroll
+  for (int u = 0; u < kTailTargets; ++u) {
+    pre[u] = pass ? w.sel[u].prefix : 0ull;
+    want[u] = pass == 0 || w.sel[u].rank > 0;
+  }
+  const int src = tail_src(pre, want, t);
+  const uint32_t* hist = w.hist + src * 256;
   uint32_t c[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) c[k] = hist[4 * lane + k];
+  const int64_t old_rank = pass ? w.sel[t].rank : 0;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w.hist[t * 256 + 4 * lane + k] = 0u;
   const int64_t lsum = (int64_t)c[0] + c[1] + c[2] + c[3];
   int64_t incl = lsum;  // inclusive scan over lanes
 #pragma unroll
@@ -522,20 +580,18 @@ __global__ __launch_bounds__(64 * kTailTargets) void tails_select_kernel(TailWs 
     rank = total > 0 ? (pct * total + 99) / 100 : 0;
     if (t % 3 == 0 && lane == 0) w.count[t / 3] = total;
   } else {
-    rank = w.sel[t].rank;
+    rank = old_rank;
   }
   const int64_t excl = incl - lsum;
   if (rank > 0 && excl < rank && rank <= incl) {
     int64_t below = excl;
     int k = 0;
     while (below + (int64_t)c[k] < rank) below += c[k++];
-    w.sel[t].prefix = (pass ? (w.sel[t].prefix << 8) : 0ull) | (uint64_t)(4 * lane + k);
+    w.sel[t].prefix = (pass ? (pre[t] << 8) : 0ull) | (uint64_t)(4 * lane + k);
     w.sel[t].rank = rank - below;
   } else if (rank == 0 && lane == 0) {
     w.sel[t].rank = 0;
   }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) hist[4 * lane + k] = 0u;
 }
 
 // Batch results per pair: fixed chunks of sequences per thread, fixed tree.
