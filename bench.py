@@ -239,6 +239,48 @@ def main() -> int:
                  "frac": round(flops / st_med / 1e6 / PEAK_BF16_TFLOPS, 4)}
     log(f"bench: lp_score_stats {st_med / 1e3:.3f} ms = {flops / st_med / 1e6:.1f} TFLOP/s")
 
+    # Vocabulary-parallel scoring at its per-GPU shape: rank 0 of 8 canonical
+    # shards scores its rows of W; the merge folds the 16 gathered segment
+    # records. All 8 shards, scored here one after another into one exchange
+    # buffer, must merge to lp_score's bits.
+    n_sh = 8
+    parts = lp.shard_partials(T, False, dev)
+    shards = []
+    for r in range(n_sh):
+        sh = lp.vocab_shard(V, n_sh, r)
+        rows = sh["row_end"] - sh["row_begin"]
+        wsh = torch.empty(lp._lib.lib().lp_score_shard_workspace_bytes(T, V, n_sh, r, 0),
+                          dtype=torch.uint8, device=dev)
+        shards.append((r, rows, w[sh["row_begin"]:sh["row_end"]], wsh))
+
+    def shard_call(k):
+        r, _, w_own, wsh = shards[k]
+        lp.score_shard(x, w_own, ids, V, n_sh, r, parts, workspace=wsh)
+
+    for k in range(n_sh):
+        shard_call(k)
+    merged = lp.merge_shards(parts, ids, V)
+    torch.cuda.synchronize()
+    assert torch.equal(merged.view(torch.int32), out.view(torch.int32)), \
+        "merged vocabulary shards differ from lp_score"
+    sh_med, sh_lo, sh_hi = median_us(lambda: shard_call(0), calls=5, reps=5)
+    all_med, _, _ = median_us(lambda: [shard_call(k) for k in range(n_sh)], calls=2, reps=3)
+    mg_med, _, _ = median_us(lambda: lp.merge_shards(parts, ids, V))
+    sh_flops = 2.0 * T * H * shards[0][1]
+    shard_rec = {"shards": n_sh, "rank": 0, "rows": shards[0][1],
+                 "ms": round(sh_med / 1e3, 4), "min_ms": round(sh_lo / 1e3, 4),
+                 "max_ms": round(sh_hi / 1e3, 4),
+                 "TFLOPs": round(sh_flops / sh_med / 1e6, 2),
+                 "frac": round(sh_flops / sh_med / 1e6 / PEAK_BF16_TFLOPS, 4),
+                 "all_shards_one_gpu_ms": round(all_med / 1e3, 4),
+                 "merge_us": round(mg_med, 2),
+                 "exchange_bytes_per_row_per_rank": 16 * 3 * 4 // n_sh,
+                 "bitwise_equal_lp_score": True}
+    log(f"bench: vocab shard 0/{n_sh} ({shards[0][1]} rows) {sh_med / 1e3:.3f} ms = "
+        f"{sh_flops / sh_med / 1e6:.1f} TFLOP/s; all {n_sh} shards {all_med / 1e3:.3f} ms; "
+        f"merge {mg_med:.1f} us; bitwise equal to lp_score")
+    del parts, shards
+
     # Small batches: the product is a stream over W (HBM-bound); report the
     # algorithmic bytes (W, the rows, ids and outputs) per second.
     small = []
@@ -337,6 +379,7 @@ def main() -> int:
                     "lp_score_ms_max": round(max(score_ms), 4),
                     "lp_compare_us": round(cmp_avg * 1e6, 2)},
         "score_stats": stats_rec,
+        "vocab_parallel": shard_rec,
         "small_batch": small,
         "compare_sweep": sweep,
         "compare_tails": tails_rec,

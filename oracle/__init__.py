@@ -13,5 +13,6 @@ Every function cites the passage of the source pages it writes out:
   [VeX]  "Diagnosing Training Inference Mismatch in LLM Reinforcement Learning"
 """
 
-from .score import bf16_bits_to_f64, score, score_stats, entropy_argmax, logits  # noqa: F401
+from .score import (bf16_bits_to_f64, score, score_stats, entropy_argmax, logits,  # noqa: F401
+                    log_softmax_at, sharded_log_softmax_at)
 from .compare import compare, per_token, tails, nearest_rank, PAIRS, STAT_FIELDS, TAIL_FIELDS  # noqa: F401

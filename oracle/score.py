@@ -95,6 +95,53 @@ def score(x_bits: np.ndarray, w_bits: np.ndarray, ids: np.ndarray,
     return log_softmax_at(logits(x_bits, w_bits, v_true), ids, temperature)
 
 
+def sharded_log_softmax_at(z: np.ndarray, ids: np.ndarray, bounds, temperature: float = 1.0):
+    """log_softmax_at with the vocabulary split into shards, as a
+    vocabulary-parallel LM head computes it.
+
+    [AMD] §"Collect A/B and C" (notes on the trainer's extraction): when the
+    vocabulary is split over shards, one global normaliser must still span
+    all of them; normalising each shard on its own scores a different
+    distribution. The vime / RL-Kernel summary: the cross-rank LSE merge
+    takes the ranks in a fixed order.
+
+    bounds: ascending row indices 0 = b_0 <= b_1 <= ... <= b_n = V (a shard
+    may be empty). Shard r holds rows [b_r, b_{r+1}) and reports
+    M_r = max s_v and S_r = sum exp(s_v - M_r) over its rows (an empty shard
+    reports nothing); the owner of ids[t] reports s[ids[t]]. Then, in shard
+    order, M = max_r M_r and lse = M + ln sum_r S_r exp(M_r - M).
+    Returns (logprob[t], lse[t]) in fp64.
+    """
+    temperature = float(temperature)
+    if not (np.isfinite(temperature) and temperature > 0.0):
+        raise ValueError("temperature must be finite and > 0")
+    b = [int(v) for v in bounds]
+    if b[0] != 0 or b[-1] != z.shape[1] or any(b1 < b0 for b0, b1 in zip(b, b[1:])):
+        raise ValueError("bounds must rise from 0 to V")
+    ids = np.asarray(ids, dtype=np.int64)
+    if ids.shape != (z.shape[0],):
+        raise ValueError("one target id per row")
+    if ids.size and (ids.min() < 0 or ids.max() >= z.shape[1]):
+        raise ValueError("target id outside the true vocabulary range")
+    s = z / temperature
+    parts = []
+    target = np.full(z.shape[0], np.nan)
+    for b0, b1 in zip(b, b[1:]):
+        if b1 == b0:
+            continue
+        sr = s[:, b0:b1]
+        Mr = sr.max(axis=1)
+        parts.append((Mr, np.exp(sr - Mr[:, None]).sum(axis=1)))
+        own = (ids >= b0) & (ids < b1)
+        target[own] = sr[own, ids[own] - b0]
+    M = np.max([Mr for Mr, _ in parts], axis=0)
+    S = np.zeros(z.shape[0])
+    for Mr, Sr in parts:
+        S = S + Sr * np.exp(Mr - M)
+    lse = M + np.log(S)
+    return target - lse, lse
+
+
 def entropy_argmax(z: np.ndarray, temperature: float = 1.0):
     """Return (entropy[t] in nats, argmax[t]) for logit rows z [T, V], fp64.
 

@@ -11,6 +11,7 @@ streams.
     score_stats(hidden, w, ids, ...)                      -> logprob, entropy, argmax
     compare(A, B, C, mask, tis_clip=2.0, atol=None)       -> stats per pair
     compare_tails(A, B, C, mask, positions=False)         -> batch tails per pair
+    vocab_shard / score_shard / merge_shards              -> vocabulary-parallel scoring
     align(hidden, input_ids, response_mask)               -> rows, targets, mask
 """
 
@@ -219,6 +220,84 @@ def compare_tails(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch
     if positions:
         return tails, ps.cpu().numpy(), pc.cpu().numpy()
     return tails
+
+
+def vocab_shard(v_true: int, n_shards: int, rank: int) -> dict:
+    """Canonical vocabulary shard of rank `rank` of `n_shards` (1..16): the
+    merge segments [seg_lo, seg_hi) it owns and their rows [row_begin, row_end)."""
+    from ._lib import VocabShard
+    out = VocabShard()
+    st = lib().lp_vocab_shard_range(int(v_true), int(n_shards), int(rank), ctypes.byref(out))
+    if st != LP_OK:
+        raise LpError(st, "lp_vocab_shard_range")
+    return {"seg_lo": out.seg_lo, "seg_hi": out.seg_hi,
+            "row_begin": out.row_begin, "row_end": out.row_end}
+
+
+def shard_partials(T: int, stats: bool = False, device=None) -> torch.Tensor:
+    """An exchange buffer for T rows: [16, F, T] fp32 (F = 5 with stats, else 3)."""
+    F = 5 if stats else 3
+    assert int(lib().lp_shard_partials_bytes(T, int(stats))) == 16 * F * T * 4
+    return torch.empty((16, F, T), dtype=torch.float32, device=device)
+
+
+def score_shard(hidden: torch.Tensor, w_shard: torch.Tensor, ids: torch.Tensor, v_true: int,
+                n_shards: int, rank: int, partials: torch.Tensor, temperature: float = 1.0,
+                stats: bool = False, *, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Score one vocabulary shard (lp_score_shard): w_shard holds rows
+    [row_begin, row_end) of W; writes this shard's segment records into
+    `partials` (from shard_partials) and returns it. Does not synchronise."""
+    _need_cuda("hidden", hidden, torch.bfloat16)
+    _need_cuda("w_shard", w_shard, torch.bfloat16)
+    _need_cuda("ids", ids, torch.int64)
+    _need_cuda("partials", partials, torch.float32)
+    if hidden.dim() != 2 or w_shard.dim() != 2 or ids.dim() != 1:
+        raise ValueError("expected hidden [T, H], w_shard [rows, H], ids [T]")
+    if hidden.stride(1) != 1 or not w_shard.is_contiguous() or not ids.is_contiguous():
+        raise ValueError("hidden needs unit column stride; w_shard and ids must be contiguous")
+    T, H = hidden.shape
+    sh = vocab_shard(v_true, n_shards, rank)
+    if w_shard.shape != (sh["row_end"] - sh["row_begin"], H) or ids.shape[0] != T:
+        raise ValueError("w_shard must hold the shard's rows [row_begin, row_end) x H")
+    F = 5 if stats else 3
+    if not partials.is_contiguous() or partials.shape != (16, F, T):
+        raise ValueError(f"partials must be a contiguous [16, {F}, T] buffer")
+    need = int(lib().lp_score_shard_workspace_bytes(T, v_true, n_shards, rank, int(stats)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    st = lib().lp_score_shard(_ptr(hidden), hidden.stride(0) if T else H, _ptr(w_shard),
+                              _ptr(ids), T, H, int(v_true), float(temperature), int(n_shards),
+                              int(rank), int(stats), _ptr(partials), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(),
+                              _stream(hidden.device))
+    if st != LP_OK:
+        raise LpError(st, "lp_score_shard")
+    return partials
+
+
+def merge_shards(partials: torch.Tensor, ids: torch.Tensor, v_true: int, stats: bool = False,
+                 *, lse: torch.Tensor | None = None, check: bool = False):
+    """Fold the gathered segment records (lp_merge_shards). Returns logprob
+    fp32 [T], or (logprob, entropy, argmax) with stats; bitwise equal to
+    score() / score_stats() on the whole W."""
+    _need_cuda("partials", partials, torch.float32)
+    _need_cuda("ids", ids, torch.int64)
+    T = ids.shape[0]
+    F = 5 if stats else 3
+    if not partials.is_contiguous() or partials.shape != (16, F, T) or not ids.is_contiguous():
+        raise ValueError(f"partials must be a contiguous [16, {F}, T] buffer and ids [T]")
+    dev = ids.device
+    out = torch.empty(T, dtype=torch.float32, device=dev)
+    ent = torch.empty(T, dtype=torch.float32, device=dev) if stats else None
+    amax = torch.empty(T, dtype=torch.int64, device=dev) if stats else None
+    bad_rows = torch.zeros(1, dtype=torch.int32, device=dev) if check else None
+    st = lib().lp_merge_shards(_ptr(partials), _ptr(ids), T, int(v_true), int(stats), _ptr(out),
+                               _ptr(lse), _ptr(ent), _ptr(amax), _ptr(bad_rows), _stream(dev))
+    if st != LP_OK:
+        raise LpError(st, "lp_merge_shards")
+    if check and int(bad_rows.item()) != 0:
+        raise ValueError(f"{int(bad_rows.item())} row(s) have a target id outside [0, {v_true})")
+    return (out, ent, amax) if stats else out
 
 
 def align(hidden: torch.Tensor, input_ids: torch.Tensor, response_mask: torch.Tensor):

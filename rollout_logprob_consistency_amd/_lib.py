@@ -18,7 +18,17 @@ LP_OK, LP_EINVAL, LP_EUNSUPPORTED, LP_EHIP = 0, 1, 2, 3
 # Names of every function include/liblp.h declares.
 EXPORTS = ("lp_status_string", "lp_score_workspace_bytes", "lp_score",
            "lp_score_stats_workspace_bytes", "lp_score_stats", "lp_compare",
-           "lp_compare_tails_workspace_bytes", "lp_compare_tails")
+           "lp_compare_tails_workspace_bytes", "lp_compare_tails",
+           "lp_vocab_shard_range", "lp_shard_partials_bytes",
+           "lp_score_shard_workspace_bytes", "lp_score_shard", "lp_merge_shards")
+
+MERGE_SEGMENTS = 16  # LP_MERGE_SEGMENTS
+
+
+class VocabShard(ctypes.Structure):
+    """Mirror of `lp_vocab_shard`."""
+    _fields_ = [("seg_lo", ctypes.c_int32), ("seg_hi", ctypes.c_int32),
+                ("row_begin", ctypes.c_int64), ("row_end", ctypes.c_int64)]
 
 # numpy mirror of `lp_seq_stats` (natural C alignment: 6 int32 then 7 double).
 SEQ_STATS_DTYPE = np.dtype([
@@ -78,6 +88,18 @@ def lib() -> ctypes.CDLL:
     L.lp_compare_tails.restype = ctypes.c_int
     L.lp_compare_tails.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp,
                                    ctypes.c_size_t, vp]
+    i32 = ctypes.c_int32
+    L.lp_vocab_shard_range.restype = ctypes.c_int
+    L.lp_vocab_shard_range.argtypes = [i64, i32, i32, ctypes.POINTER(VocabShard)]
+    L.lp_shard_partials_bytes.restype = ctypes.c_size_t
+    L.lp_shard_partials_bytes.argtypes = [i64, i32]
+    L.lp_score_shard_workspace_bytes.restype = ctypes.c_size_t
+    L.lp_score_shard_workspace_bytes.argtypes = [i64, i64, i32, i32, i32]
+    L.lp_score_shard.restype = ctypes.c_int
+    L.lp_score_shard.argtypes = [vp, i64, vp, vp, i64, i64, i64, f32, i32, i32, i32,
+                                 vp, vp, ctypes.c_size_t, vp]
+    L.lp_merge_shards.restype = ctypes.c_int
+    L.lp_merge_shards.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, vp]
     _lib = L
     return L
 

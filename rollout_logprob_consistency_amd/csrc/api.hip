@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <limits>
 
 #include "lp_internal.h"
@@ -13,9 +14,132 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 
 constexpr int64_t kI32Max = std::numeric_limits<int32_t>::max();
 
+// Canonical shard of the merge segments: rank r of n owns segments
+// [16 r / n, 16 (r + 1) / n) and the vocabulary rows they cover.
+lp_vocab_shard shard_of(int64_t V_true, int32_t n_shards, int32_t rank) {
+  const int64_t rows_per_seg = (int64_t)lp::merge_segment_tiles(V_true) * lp::kTileV;
+  lp_vocab_shard s;
+  s.seg_lo = (int32_t)((int64_t)lp::kMergeSegs * rank / n_shards);
+  s.seg_hi = (int32_t)((int64_t)lp::kMergeSegs * (rank + 1) / n_shards);
+  s.row_begin = std::min<int64_t>(V_true, s.seg_lo * rows_per_seg);
+  s.row_end = std::min<int64_t>(V_true, s.seg_hi * rows_per_seg);
+  return s;
+}
+
+bool shard_args_ok(int64_t V_true, int32_t n_shards, int32_t rank) {
+  return V_true >= 1 && V_true <= kI32Max && n_shards >= 1 && n_shards <= lp::kMergeSegs &&
+         rank >= 0 && rank < n_shards;
+}
+
 }  // namespace
 
 extern "C" {
+
+lp_status lp_vocab_shard_range(int64_t V_true, int32_t n_shards, int32_t rank,
+                               lp_vocab_shard* out) {
+  if (!out || !shard_args_ok(V_true, n_shards, rank)) return LP_EINVAL;
+  *out = shard_of(V_true, n_shards, rank);
+  return LP_OK;
+}
+
+size_t lp_shard_partials_bytes(int64_t T, int32_t stats) {
+  if (T < 0 || T > kI32Max) return 0;
+  return (size_t)lp::kMergeSegs * (stats ? 5 : 3) * (size_t)T * sizeof(float);
+}
+
+size_t lp_score_shard_workspace_bytes(int64_t T, int64_t V_true, int32_t n_shards, int32_t rank,
+                                      int32_t stats) {
+  if (T < 0 || T > kI32Max || !shard_args_ok(V_true, n_shards, rank)) return 0;
+  const lp_vocab_shard sh = shard_of(V_true, n_shards, rank);
+  const size_t total = lp::score_workspace_layout(T, sh.row_end - sh.row_begin, stats != 0).total;
+  return total < 256 ? 256 : total;
+}
+
+lp_status lp_score_shard(const void* hidden_bf16, int64_t ldh, const void* w_shard_bf16,
+                         const int64_t* target_ids, int64_t T, int64_t H, int64_t V_true,
+                         float temperature, int32_t n_shards, int32_t rank, int32_t stats,
+                         void* partials, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (T < 0 || H < 1 || ldh < H || !shard_args_ok(V_true, n_shards, rank)) return LP_EINVAL;
+  if (stats != 0 && stats != 1) return LP_EINVAL;
+  if (!(isfinite(temperature) && temperature > 0.0f)) return LP_EINVAL;
+  if (T == 0) return LP_OK;
+  const lp_vocab_shard sh = shard_of(V_true, n_shards, rank);
+  const int64_t rows = sh.row_end - sh.row_begin;
+  if (!target_ids || !partials || !workspace) return LP_EINVAL;
+  if (rows > 0 && (!hidden_bf16 || !w_shard_bf16)) return LP_EINVAL;
+  const lp::ScoreWorkspace ws = lp::score_workspace_layout(T, rows, stats != 0);
+  if (workspace_bytes < ws.total || !aligned(workspace, 256) || !aligned(partials, 4))
+    return LP_EINVAL;
+  if (H % lp::kTileK != 0 || ldh % 8 != 0) return LP_EUNSUPPORTED;
+  if (rows > 0 && (!aligned(hidden_bf16, 16) || !aligned(w_shard_bf16, 16)))
+    return LP_EUNSUPPORTED;
+  const int64_t n_vt = (rows + lp::kTileV - 1) / lp::kTileV;
+  const int64_t n_tt = (T + lp::kTileT - 1) / lp::kTileT;
+  if (T > kI32Max || H > kI32Max || n_vt * n_tt > kI32Max) return LP_EUNSUPPORTED;
+
+  lp::ScoreArgs a;
+  a.x = static_cast<const uint16_t*>(hidden_bf16);
+  a.w = static_cast<const uint16_t*>(w_shard_bf16);
+  a.ids = target_ids;
+  a.ldh = ldh;
+  a.T = (int32_t)T;
+  a.H = (int32_t)H;
+  a.V_rows = (int32_t)rows;
+  a.V_true = (int32_t)rows;
+  a.v_base = (int32_t)sh.row_begin;
+  a.n_vt = (int32_t)n_vt;
+  a.n_tt = (int32_t)n_tt;
+  a.scale2 = (float)(1.4426950408889634 / (double)temperature);
+  char* base = static_cast<char*>(workspace);
+  a.part_m = reinterpret_cast<float*>(base + ws.off_m);
+  a.part_s = reinterpret_cast<float*>(base + ws.off_s);
+  a.tval = reinterpret_cast<float*>(base + ws.off_t);
+  a.out_lp = nullptr;
+  a.out_lse = nullptr;
+  a.bad_rows = nullptr;
+  a.part_q = stats ? reinterpret_cast<float*>(base + ws.off_q) : nullptr;
+  a.part_i = stats ? reinterpret_cast<int32_t*>(base + ws.off_i) : nullptr;
+  a.out_ent = nullptr;
+  a.out_argmax = nullptr;
+
+  lp::ShardArgs s;
+  s.seg_lo = sh.seg_lo;
+  s.n_seg = sh.seg_hi - sh.seg_lo;
+  s.per = lp::merge_segment_tiles(V_true);
+  s.n_vt_glob = (int32_t)((V_true + lp::kTileV - 1) / lp::kTileV);
+  s.tile_base = (int32_t)(sh.row_begin / lp::kTileV);
+  s.V_true_glob = (int32_t)V_true;
+  s.F = stats ? 5 : 3;
+  s.out = static_cast<float*>(partials);
+  if (s.n_seg == 0) return LP_OK;
+  return lp::launch_score_shard(a, s, stream) == hipSuccess ? LP_OK : LP_EHIP;
+}
+
+lp_status lp_merge_shards(const void* partials, const int64_t* target_ids, int64_t T,
+                          int64_t V_true, int32_t stats, float* out_logprob, float* out_lse,
+                          float* out_entropy, int64_t* out_argmax, int32_t* bad_rows,
+                          hipStream_t stream) {
+  if (T < 0 || V_true < 1 || (stats != 0 && stats != 1)) return LP_EINVAL;
+  if (T == 0) return LP_OK;
+  if (!partials || !target_ids || !out_logprob || !aligned(partials, 4)) return LP_EINVAL;
+  if (stats && (!out_entropy || !out_argmax)) return LP_EINVAL;
+  if (T > kI32Max || V_true > kI32Max) return LP_EUNSUPPORTED;
+  lp::ScoreArgs a = {};
+  a.ids = target_ids;
+  a.T = (int32_t)T;
+  a.V_true = (int32_t)V_true;
+  a.out_lp = out_logprob;
+  a.out_lse = out_lse;
+  a.bad_rows = bad_rows;
+  a.out_ent = stats ? out_entropy : nullptr;
+  a.out_argmax = stats ? out_argmax : nullptr;
+  lp::ShardArgs s = {};
+  s.per = lp::merge_segment_tiles(V_true);
+  s.F = stats ? 5 : 3;
+  s.out = static_cast<float*>(const_cast<void*>(partials));
+  return lp::launch_merge_shards(a, s, stream) == hipSuccess ? LP_OK : LP_EHIP;
+}
 
 const char* lp_status_string(lp_status status) {
   switch (status) {
@@ -75,6 +199,7 @@ lp_status score_impl(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
   a.H = (int32_t)H;
   a.V_rows = (int32_t)V_rows;
   a.V_true = (int32_t)V_true;
+  a.v_base = 0;
   a.n_vt = (int32_t)n_vt;
   a.n_tt = (int32_t)n_tt;
   a.scale2 = (float)(1.4426950408889634 / (double)temperature);

@@ -27,6 +27,7 @@ struct ScoreArgs {
   const int64_t* ids;     // [T]
   int64_t ldh;
   int32_t T, H, V_rows, V_true;
+  int32_t v_base;         // vocabulary index of W row 0 (0 unless a shard)
   int32_t n_vt, n_tt;     // vocabulary / token tile counts
   float scale2;           // log2(e) / temperature
   float* part_m;          // [n_vt][T]  per-tile max (log2 units)
@@ -50,6 +51,26 @@ struct ScoreWorkspace {
 ScoreWorkspace score_workspace_layout(int64_t T, int64_t V_true, bool stats);
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream);
+
+// Fixed merge segments of the vocabulary tiles; a vocabulary shard owns whole
+// segments.
+constexpr int kMergeSegs = 16;
+static_assert(kMergeSegs == LP_MERGE_SEGMENTS, "the segment count is part of the C ABI");
+int merge_segment_tiles(int64_t V_true);  // tiles per segment
+
+struct ShardArgs {
+  int32_t seg_lo, n_seg;  // this shard's first segment and segment count
+  int32_t per;            // vocabulary tiles per segment
+  int32_t n_vt_glob;      // vocabulary tiles over the whole true range
+  int32_t tile_base;      // tile index of this shard's first row
+  int32_t V_true_glob;
+  int32_t F;              // planes per segment record: 3, or 5 with stats
+  float* out;             // [kMergeSegs][F][T] segment records
+};
+// ScoreArgs describe the shard's own rows (W = the shard, V_rows = V_true =
+// its row count, v_base = its first row); the merge takes the whole range.
+hipError_t launch_score_shard(const ScoreArgs& a, const ShardArgs& s, hipStream_t stream);
+hipError_t launch_merge_shards(const ScoreArgs& a, const ShardArgs& s, hipStream_t stream);
 
 struct CompareArgs {
   const float* A;

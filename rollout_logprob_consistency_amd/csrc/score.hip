@@ -201,7 +201,7 @@ __device__ __forceinline__ void wave_lse(Get v, float scale2, int lg, float& m_o
 template <class Get>
 __device__ __forceinline__ void gather_target(Get v, const ScoreArgs& a, int t, int64_t wv_lo,
                                               int lg) {
-  const int64_t tgt = a.ids[t];
+  const int64_t tgt = a.ids[t] - a.v_base;  // row of this W buffer
   const int64_t loc = tgt - wv_lo;
   if (tgt >= 0 && tgt < a.V_true && loc >= 0 && loc < kWaveV) {
     const int li = (int)loc;
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
       red_s[wm][tl] = s;
       if (kStats) {
         red_q[wm][tl] = q;
-        red_i[wm][tl] = li == kNoRow ? kNoRow : (int)wv_lo + li;
+        red_i[wm][tl] = li == kNoRow ? kNoRow : a.v_base + (int)wv_lo + li;
       }
     }
   }
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_ite
             a.part_s[(size_t)vh * a.T + t] = s;
             if (kStats) {
               a.part_q[(size_t)vh * a.T + t] = q;
-              a.part_i[(size_t)vh * a.T + t] = li == kNoRow ? kNoRow : vbase + li;
+              a.part_i[(size_t)vh * a.T + t] = li == kNoRow ? kNoRow : a.v_base + vbase + li;
             }
           }
         }
@@ -644,7 +644,6 @@ __global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_ite
 // then the segment results are folded in segment order. Segment bounds depend
 // only on the number of vocabulary tiles, so the order is the same for every
 // batch.
-constexpr int kMergeSegs = 16;
 
 __device__ __forceinline__ void lse_fold(float& M, float& S, float m, float s) {
   const float Mn = fmaxf(M, m);
@@ -664,9 +663,63 @@ __device__ __forceinline__ void lse_fold_stats(float& M, float& S, float& Q, int
   M = Mn;
 }
 
+// Fold of the vocabulary tiles [lo, hi) (indices of the partial planes) of
+// one merge segment for token t, in ascending order, from the empty partial.
 // kHalves: the partials are per 128-row half of each vocabulary tile (rows
-// 2 vt and 2 vt + 1), merged with merge_halves first. kStats: also fold the
-// entropy term and the argmax, and write entropy (nats) and argmax.
+// 2 vt and 2 vt + 1), merged with merge_halves first. kStats: the entropy
+// term and the argmax are carried along.
+template <bool kHalves, bool kStats>
+__device__ __forceinline__ void seg_fold(const ScoreArgs& a, int t, int lo, int hi, float& M,
+                                         float& S, float& Q, int& I) {
+  M = -__builtin_inff();
+  S = 0.f;
+  Q = 0.f;
+  I = kNoRow;
+  const float* pm = a.part_m + t;
+  const float* ps = a.part_s + t;
+  const float* pq = a.part_q + t;
+  const int* pi = a.part_i + t;
+  if (kHalves) {
+#pragma unroll 8
+    for (int vt = lo; vt < hi; ++vt) {
+      const size_t r0 = (size_t)(2 * vt) * a.T, r1 = (size_t)(2 * vt + 1) * a.T;
+      float m, s;
+      merge_halves(pm[r0], ps[r0], pm[r1], ps[r1], m, s);
+      if (kStats) {
+        const float q = merge_q(pm[r0], ps[r0], pq[r0], pm[r1], ps[r1], pq[r1], m);
+        const int i = pm[r1] > pm[r0] ? pi[r1] : pi[r0];
+        lse_fold_stats(M, S, Q, I, m, s, q, i);
+      } else {
+        lse_fold(M, S, m, s);
+      }
+    }
+  } else {
+#pragma unroll 8
+    for (int vt = lo; vt < hi; ++vt) {
+      const size_t r = (size_t)vt * a.T;
+      if (kStats) lse_fold_stats(M, S, Q, I, pm[r], ps[r], pq[r], pi[r]);
+      else lse_fold(M, S, pm[r], ps[r]);
+    }
+  }
+}
+
+// Outputs of row t from its fully folded (M, S[, Q, I]) and its scaled
+// target logit tv (ok: the target id lies in [0, V_true)).
+template <bool kStats>
+__device__ __forceinline__ void finish_row(const ScoreArgs& a, int t, float M, float S, float Q,
+                                           int I, float tv, bool ok) {
+  const float l2s = fast_log2(S);
+  const float lse2 = M + l2s;
+  a.out_lp[t] = ok ? (tv - lse2) * kLn2 : __builtin_nanf("");
+  if (a.out_lse) a.out_lse[t] = lse2 * kLn2;
+  if (kStats) {
+    // H = ln 2 (log2 S - Q / S): the log-sum-exp minus the mean scaled logit.
+    a.out_ent[t] = (l2s - Q / S) * kLn2;
+    a.out_argmax[t] = I;
+  }
+  if (!ok && a.bad_rows) atomicAdd(a.bad_rows, 1);
+}
+
 template <bool kHalves, bool kStats>
 __global__ __launch_bounds__(64 * kMergeSegs) void lse_merge_kernel(ScoreArgs a) {
   __shared__ float seg_m[kMergeSegs][64];
@@ -679,34 +732,7 @@ __global__ __launch_bounds__(64 * kMergeSegs) void lse_merge_kernel(ScoreArgs a)
   const int lo = min(a.n_vt, seg * per), hi = min(a.n_vt, lo + per);
   float M = -__builtin_inff(), S = 0.f, Q = 0.f;
   int I = kNoRow;
-  if (t < a.T) {
-    const float* pm = a.part_m + t;
-    const float* ps = a.part_s + t;
-    const float* pq = a.part_q + t;
-    const int* pi = a.part_i + t;
-    if (kHalves) {
-#pragma unroll 8
-      for (int vt = lo; vt < hi; ++vt) {
-        const size_t r0 = (size_t)(2 * vt) * a.T, r1 = (size_t)(2 * vt + 1) * a.T;
-        float m, s;
-        merge_halves(pm[r0], ps[r0], pm[r1], ps[r1], m, s);
-        if (kStats) {
-          const float q = merge_q(pm[r0], ps[r0], pq[r0], pm[r1], ps[r1], pq[r1], m);
-          const int i = pm[r1] > pm[r0] ? pi[r1] : pi[r0];
-          lse_fold_stats(M, S, Q, I, m, s, q, i);
-        } else {
-          lse_fold(M, S, m, s);
-        }
-      }
-    } else {
-#pragma unroll 8
-      for (int vt = lo; vt < hi; ++vt) {
-        const size_t r = (size_t)vt * a.T;
-        if (kStats) lse_fold_stats(M, S, Q, I, pm[r], ps[r], pq[r], pi[r]);
-        else lse_fold(M, S, pm[r], ps[r]);
-      }
-    }
-  }
+  if (t < a.T) seg_fold<kHalves, kStats>(a, t, lo, hi, M, S, Q, I);
   seg_m[seg][lane] = M;
   seg_s[seg][lane] = S;
   if (kStats) {
@@ -726,18 +752,67 @@ __global__ __launch_bounds__(64 * kMergeSegs) void lse_merge_kernel(ScoreArgs a)
     if (kStats) lse_fold_stats(M, S, Q, I, seg_m[g][lane], seg_s[g][lane], seg_q[g][lane], seg_i[g][lane]);
     else lse_fold(M, S, seg_m[g][lane], seg_s[g][lane]);
   }
-  const float l2s = fast_log2(S);
-  const float lse2 = M + l2s;
   const int64_t id = a.ids[t];
   const bool ok = id >= 0 && id < a.V_true;
-  a.out_lp[t] = ok ? (a.tval[t] - lse2) * kLn2 : __builtin_nanf("");
-  if (a.out_lse) a.out_lse[t] = lse2 * kLn2;
+  finish_row<kStats>(a, t, M, S, Q, I, ok ? a.tval[t] : 0.f, ok);
+}
+
+// ---- Vocabulary-parallel scoring. ----
+// A shard owns whole merge segments (the segment bounds above, fixed by the
+// true vocabulary size alone). It scores its rows with the kernels above
+// (same tiles, same K order, same epilogue) and folds each of its segments
+// exactly as lse_merge_kernel does; after the records of all segments are
+// gathered, shard_merge_kernel folds them in segment order as
+// lse_merge_kernel's second stage does. Every float operation and its order
+// are those of the one-buffer path, so the results are bitwise equal.
+//
+// Record of segment g: s.F planes of T floats at s.out + g F T -- max, sum,
+// target logit (0 unless the target row lies in the segment), and with stats
+// the entropy term and the argmax (int32 bits).
+template <bool kHalves, bool kStats>
+__global__ __launch_bounds__(64) void shard_fold_kernel(ScoreArgs a, ShardArgs s) {
+  const int t = blockIdx.x * 64 + threadIdx.x;
+  if (t >= a.T) return;
+  const int g = s.seg_lo + blockIdx.y;
+  const int lo = min(s.n_vt_glob, g * s.per), hi = min(s.n_vt_glob, lo + s.per);
+  float M, S, Q;
+  int I;
+  seg_fold<kHalves, kStats>(a, t, lo - s.tile_base, hi - s.tile_base, M, S, Q, I);
+  const int64_t id = a.ids[t];
+  const int64_t r0 = (int64_t)lo * kTileV, r1 = min((int64_t)hi * kTileV, (int64_t)s.V_true_glob);
+  float* rec = s.out + (size_t)g * s.F * a.T + t;
+  rec[0] = M;
+  rec[(size_t)a.T] = S;
+  rec[2 * (size_t)a.T] = (id >= r0 && id < r1) ? a.tval[t] : 0.f;
   if (kStats) {
-    // H = ln 2 (log2 S - Q / S): the log-sum-exp minus the mean scaled logit.
-    a.out_ent[t] = (l2s - Q / S) * kLn2;
-    a.out_argmax[t] = I;
+    rec[3 * (size_t)a.T] = Q;
+    reinterpret_cast<int*>(rec)[4 * (size_t)a.T] = I;
   }
-  if (!ok && a.bad_rows) atomicAdd(a.bad_rows, 1);
+}
+
+template <bool kStats>
+__global__ __launch_bounds__(256) void shard_merge_kernel(ScoreArgs a, ShardArgs s) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.T) return;
+  const size_t T = (size_t)a.T, FT = (size_t)s.F * T;
+  const float* rec = s.out + t;
+  float M = rec[0], S = rec[T], Q = 0.f;
+  int I = kNoRow;
+  if (kStats) {
+    Q = rec[3 * T];
+    I = reinterpret_cast<const int*>(rec)[4 * T];
+  }
+#pragma unroll
+  for (int g = 1; g < kMergeSegs; ++g) {
+    const float* r = rec + g * FT;
+    if (kStats) lse_fold_stats(M, S, Q, I, r[0], r[T], r[3 * T], reinterpret_cast<const int*>(r)[4 * T]);
+    else lse_fold(M, S, r[0], r[T]);
+  }
+  const int64_t id = a.ids[t];
+  const bool ok = id >= 0 && id < a.V_true;
+  float tv = 0.f;
+  if (ok) tv = rec[(size_t)((int)(id / kTileV) / s.per) * FT + 2 * T];
+  finish_row<kStats>(a, t, M, S, Q, I, tv, ok);
 }
 
 }  // namespace
@@ -775,8 +850,9 @@ static void launch_stream(ScoreArgs a, hipStream_t stream) {
                      n_items);
 }
 
+// The tile (or streaming) kernel alone; returns the streaming choice.
 template <bool kStats>
-static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t stream) {
+static int launch_tiles(const ScoreArgs& a, hipStream_t stream) {
   const int st = stream_tokens(a.T);
   if (st == 1) launch_stream<1, kStats>(a, stream);
   else if (st == 2) launch_stream<2, kStats>(a, stream);
@@ -784,6 +860,12 @@ static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t stream) {
     const unsigned grid = (unsigned)a.n_vt * (unsigned)a.n_tt;
     hipLaunchKernelGGL(score_tile_kernel<kStats>, dim3(grid), dim3(kThreads), 0, stream, a);
   }
+  return st;
+}
+
+template <bool kStats>
+static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t stream) {
+  const int st = launch_tiles<kStats>(a, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (st)
@@ -795,8 +877,39 @@ static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <bool kStats>
+static hipError_t launch_shard_t(const ScoreArgs& a, const ShardArgs& s, hipStream_t stream) {
+  // A shard with no rows (more shards than segments hold tiles) still writes
+  // the empty records of its segments.
+  const int st = a.n_vt > 0 ? launch_tiles<kStats>(a, stream) : stream_tokens(a.T);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((a.T + 63) / 64), (unsigned)s.n_seg);
+  if (st)
+    hipLaunchKernelGGL((shard_fold_kernel<true, kStats>), grid, dim3(64), 0, stream, a, s);
+  else
+    hipLaunchKernelGGL((shard_fold_kernel<false, kStats>), grid, dim3(64), 0, stream, a, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
   return a.out_ent ? launch_score_t<true>(a, stream) : launch_score_t<false>(a, stream);
+}
+
+int merge_segment_tiles(int64_t V_true) {
+  const int64_t n_vt = (V_true + kTileV - 1) / kTileV;
+  return (int)((n_vt + kMergeSegs - 1) / kMergeSegs);
+}
+
+hipError_t launch_score_shard(const ScoreArgs& a, const ShardArgs& s, hipStream_t stream) {
+  return s.F == 5 ? launch_shard_t<true>(a, s, stream) : launch_shard_t<false>(a, s, stream);
+}
+
+hipError_t launch_merge_shards(const ScoreArgs& a, const ShardArgs& s, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.T + 255) / 256));
+  if (s.F == 5) hipLaunchKernelGGL(shard_merge_kernel<true>, grid, dim3(256), 0, stream, a, s);
+  else hipLaunchKernelGGL(shard_merge_kernel<false>, grid, dim3(256), 0, stream, a, s);
+  return hipGetLastError();
 }
 
 }  // namespace lp

@@ -31,7 +31,9 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["lp_status_string", "lp_score_workspace_bytes", "lp_score",
          "lp_score_stats_workspace_bytes", "lp_score_stats", "lp_compare",
-         "lp_compare_tails_workspace_bytes", "lp_compare_tails"])
+         "lp_compare_tails_workspace_bytes", "lp_compare_tails",
+         "lp_vocab_shard_range", "lp_shard_partials_bytes",
+         "lp_score_shard_workspace_bytes", "lp_score_shard", "lp_merge_shards"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -191,3 +193,63 @@ def test_tail_stats_layout():
     assert _lib.TAIL_STATS_DTYPE.itemsize == 64
     assert [_lib.TAIL_STATS_DTYPE.fields[f][1] for f in ("count", "q50", "max_seq", "max_pos", "sum_abs")] == \
         [0, 8, 40, 44, 48]
+
+
+def shard(L, x=P, w=P, ids=P, T=8, H=64, V=1000, temp=1.0, n=4, r=0, stats=0, parts=P, ws=P,
+          wsb=None, ldh=None):
+    if wsb is None:
+        wsb = L.lp_score_shard_workspace_bytes(T, V, n, r, stats) if T >= 0 else 0
+    return L.lp_score_shard(x, H if ldh is None else ldh, w, ids, T, H, V, temp, n, r, stats,
+                            parts, ws, wsb, None)
+
+
+def test_score_shard_rejects_bad_arguments(L):
+    EINVAL, EUNSUP = 1, 2
+    assert shard(L, T=-1) == EINVAL
+    assert shard(L, H=0) == EINVAL
+    assert shard(L, ldh=32) == EINVAL
+    assert shard(L, V=0) == EINVAL
+    assert shard(L, n=0) == EINVAL
+    assert shard(L, n=17) == EINVAL
+    assert shard(L, r=4) == EINVAL
+    assert shard(L, stats=2) == EINVAL
+    assert shard(L, temp=0.0) == EINVAL
+    assert shard(L, temp=float("inf")) == EINVAL
+    assert shard(L, parts=None) == EINVAL
+    assert shard(L, ids=None) == EINVAL
+    assert shard(L, ws=None) == EINVAL
+    assert shard(L, x=None) == EINVAL                   # rank 0 of 4 owns rows 0..511
+    assert shard(L, wsb=L.lp_score_shard_workspace_bytes(8, 1000, 4, 0, 0) - 1) == EINVAL
+    assert shard(L, ws=ctypes.c_void_p(0x10010)) == EINVAL
+    assert shard(L, parts=ctypes.c_void_p(0x10002)) == EINVAL
+    assert shard(L, H=96, ldh=96) == EUNSUP             # H not a multiple of 64
+    assert shard(L, x=ctypes.c_void_p(0x10008)) == EUNSUP
+    assert shard(L, T=0) == 0                           # nothing to do
+    assert L.lp_score_shard_workspace_bytes(8, 1000, 4, 4, 0) == 0
+    assert L.lp_score_shard_workspace_bytes(-1, 1000, 4, 0, 0) == 0
+
+
+def test_shard_buffers(L):
+    assert L.lp_shard_partials_bytes(100, 0) == 16 * 3 * 100 * 4
+    assert L.lp_shard_partials_bytes(100, 1) == 16 * 5 * 100 * 4
+    assert L.lp_shard_partials_bytes(-1, 0) == 0
+    # A shard's workspace holds the partial planes of its own tiles only.
+    whole = L.lp_score_workspace_bytes(8192, 4096, 151936, 151936)
+    one = L.lp_score_shard_workspace_bytes(8192, 151936, 8, 0, 0)
+    assert one % 256 == 0 and one >= 2 * 76 * 8192 * 4 and one < whole // 6
+    # Shards with no rows (1000 rows, 16 shards) still need a valid buffer.
+    assert L.lp_score_shard_workspace_bytes(8, 1000, 16, 15, 1) >= 256
+
+
+def test_merge_shards_rejects_bad_arguments(L):
+    EINVAL = 1
+    m = L.lp_merge_shards
+    assert m(P, P, -1, 1000, 0, P, None, None, None, None, None) == EINVAL
+    assert m(P, P, 8, 0, 0, P, None, None, None, None, None) == EINVAL
+    assert m(P, P, 8, 1000, 2, P, None, None, None, None, None) == EINVAL
+    assert m(None, P, 8, 1000, 0, P, None, None, None, None, None) == EINVAL
+    assert m(P, None, 8, 1000, 0, P, None, None, None, None, None) == EINVAL
+    assert m(P, P, 8, 1000, 0, None, None, None, None, None, None) == EINVAL
+    assert m(P, P, 8, 1000, 1, P, None, None, P, None, None) == EINVAL   # stats needs both outputs
+    assert m(ctypes.c_void_p(0x10002), P, 8, 1000, 0, P, None, None, None, None, None) == EINVAL
+    assert m(P, P, 0, 1000, 0, None, None, None, None, None, None) == 0
