@@ -98,3 +98,18 @@ def test_library_chunking_rejects_bad_arguments():
     for args in ((0, 1, 0), (100, 0, 0), (100, 17, 0), (100, 4, 4), (100, 4, -1), (2**31, 1, 0)):
         with pytest.raises(lp.LpError):
             lp.vocab_shard(*args)
+
+
+def test_merge_is_stable_across_shards_far_apart():
+    # The normaliser is a stable log-sum-exp ([AMD] "Case 2": computed with a
+    # numerically stable logsumexp): shards whose logits lie 1600 apart
+    # (exp of the gap overflows fp64) still merge to the finite one-buffer
+    # value, whichever shard holds the maximum.
+    z = np.concatenate([np.linspace(-810, -790, 50), np.linspace(790, 810, 50),
+                        np.linspace(-5, 5, 50)])[None, :]
+    for ids in ([10], [60], [120]):
+        ref_lp, ref_lse = oracle.log_softmax_at(z, ids)
+        got_lp, got_lse = oracle.sharded_log_softmax_at(z, ids, [0, 50, 100, 150])
+        assert np.isfinite(got_lse).all()
+        np.testing.assert_allclose(got_lse, ref_lse, rtol=1e-15, atol=0)
+        np.testing.assert_allclose(got_lp, ref_lp, rtol=1e-13, atol=1e-12)
