@@ -298,6 +298,7 @@ def main() -> int:
     # Comparison bandwidth probe at sizes that are not launch-latency bound.
     sweep = []
     tails_rec = None
+    corr_rec = None
     for n_seq in (int(v) for v in args.sweep_n.split(",") if v):
         sc = synth.compare_sweep_case(N=n_seq)
         tA, tB, tC, tM = (torch.from_numpy(a).to(dev) for a in (sc.A, sc.B, sc.C, sc.mask))
@@ -333,6 +334,24 @@ def main() -> int:
                          "frac_hbm": round(tbytes / tmed / 1e3 / PEAK_HBM_GBPS, 4)}
             log(f"bench: lp_compare_tails N={sc.N} L={sc.L}: {tmed:.1f} us "
                 f"({tbytes / tmed / 1e3:.1f} GB/s over 9 passes)")
+            # Correction consumer on the same arrays: rollout = A, trainer = C;
+            # TIS cap, MIS interval and K3 rejection, weights written. Bytes:
+            # 2 x fp32 + mask read, fp32 weight written per position.
+            cw = torch.empty((sc.N, sc.L), dtype=torch.float32, device=dev)
+            cout = torch.empty(sc.N * lp.CORR_SEQ_DTYPE.itemsize, dtype=torch.uint8, device=dev)
+            cargs2 = (tA.data_ptr(), tC.data_ptr(), tM.data_ptr(), sc.N, sc.L, sc.L, 1.001,
+                      -0.003, 0.003, lp.REJECT_K3, float("-inf"), 2e-4, cw.data_ptr(),
+                      cout.data_ptr(), torch.cuda.current_stream().cuda_stream)
+            c_corr = lp._lib.lib().lp_correct
+            cmed, clo, chi = median_us(lambda: c_corr(*cargs2))
+            cbytes = 13.0 * sc.N * sc.L
+            corr_rec = {"N": sc.N, "L": sc.L, "us": round(cmed, 2), "min_us": round(clo, 2),
+                        "max_us": round(chi, 2), "bytes_per_token": 13,
+                        "GBps": round(cbytes / cmed / 1e3, 1),
+                        "frac_hbm": round(cbytes / cmed / 1e3 / PEAK_HBM_GBPS, 4)}
+            log(f"bench: lp_correct N={sc.N} L={sc.L}: {cmed:.1f} us = "
+                f"{cbytes / cmed / 1e3:.1f} GB/s")
+            del cw, cout
         del tA, tB, tC, tM
 
     cpu = None
@@ -383,6 +402,7 @@ def main() -> int:
         "small_batch": small,
         "compare_sweep": sweep,
         "compare_tails": tails_rec,
+        "correct": corr_rec,
     }
     print(json.dumps(rec), flush=True)
     return 0

@@ -330,6 +330,70 @@ lp_status lp_merge_shards(const void* partials, const int64_t* target_ids,
                           float* out_entropy, int64_t* out_argmax,
                           int32_t* bad_rows, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Correction consumers: TIS / MIS token weights and sequence rejection
+ *
+ * For each sequence n and active token i with both scores finite, the
+ * correction ratio is r = pi_train / pi_rollout, taken in the log domain as
+ * d = fp64(train_lp) - fp64(rollout_lp) (one IEEE operation):
+ *
+ *   weight   = 0                 unless mis_log_lo <= d <= mis_log_hi
+ *            = C                 if d >= log C                 (TIS cap)
+ *            = fp32(exp(d))      otherwise
+ *   and weight = 0 on masked and non-finite tokens and in rejected
+ *   sequences.
+ *   stat     = sum over the counted tokens of K(r): K1 = -log r = -d,
+ *              K3 = r - 1 - log r = expm1(d) - d (fp64; an overflowing
+ *              term makes stat +inf); 0 with LP_REJECT_NONE
+ *   accepted = reject_lo <= stat <= reject_hi
+ *
+ * ["Rollout-Training Mismatch in LLM RL"] section 2.1, Eq. (2) and the TIS /
+ * MIS definitions after Eq. (3): w_TIS = min(w, C), w_MIS = w 1[l <= w <= u]
+ * (here l = exp(mis_log_lo), u = exp(mis_log_hi); both may be combined);
+ * [VeX] result 5 and the discussion of how TIS works: r_corr is the old
+ * trainer over the rollout probability, token TIS clamps exp(log r) at C,
+ * sequence rejection filters by sum_t K1(r_t) or sum_t K3(r_t), padding
+ * tokens weigh 0.
+ *
+ * Arguments: rollout_lp, train_lp fp32 and mask uint8, [N, L] with row
+ * stride ld (as for lp_compare); tis_clip C > 0 (+inf: no cap); the MIS
+ * interval on log r (-inf / +inf: no bound); reject_kind LP_REJECT_NONE,
+ * LP_REJECT_K1 or LP_REJECT_K3 and the accepted range of stat (-inf / +inf:
+ * no bound). weights: [N, L] fp32 contiguous, or NULL for the statistics
+ * only; out: [N] lp_corr_seq. Device memory owned by the caller; async on
+ * `stream`.
+ *
+ * kept counts the counted tokens inside the interval whether or not the
+ * sequence is accepted; capped those of them at the cap; sum_weight the
+ * written weights (0 for a rejected sequence). Counts, accepted and the
+ * interval / cap decisions are exact; stat and sum_weight are fp64 sums in a
+ * fixed order (bitwise reproducible, independent of N).
+ *
+ * Errors: LP_EINVAL for N < 0, L < 0, ld < L, C <= 0 or NaN, a NaN or
+ * inverted interval or accepted range, an unknown reject_kind, a NULL out,
+ * or NULL inputs with N, L > 0. N == 0 does nothing.
+ * ------------------------------------------------------------------------ */
+#define LP_REJECT_NONE 0
+#define LP_REJECT_K1 1
+#define LP_REJECT_K3 3
+
+typedef struct {
+  int32_t valid;      /* active tokens */
+  int32_t nonfinite;  /* active tokens with a non-finite score (weight 0) */
+  int32_t kept;       /* counted tokens inside the MIS interval */
+  int32_t capped;     /* kept tokens whose weight is the cap C */
+  int32_t accepted;   /* 1: the sequence is kept; 0: rejected */
+  int32_t reserved;   /* 0 */
+  double stat;        /* sum of K1 or K3 over the counted tokens */
+  double sum_weight;  /* sum of the written weights */
+} lp_corr_seq;
+
+lp_status lp_correct(const float* rollout_lp, const float* train_lp,
+                     const uint8_t* mask, int64_t N, int64_t L, int64_t ld,
+                     double tis_clip, double mis_log_lo, double mis_log_hi,
+                     int32_t reject_kind, double reject_lo, double reject_hi,
+                     float* weights, lp_corr_seq* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

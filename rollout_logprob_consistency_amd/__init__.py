@@ -12,18 +12,20 @@ streams.
     compare(A, B, C, mask, tis_clip=2.0, atol=None)       -> stats per pair
     compare_tails(A, B, C, mask, positions=False)         -> batch tails per pair
     vocab_shard / score_shard / merge_shards              -> vocabulary-parallel scoring
+    correct(rollout, train, mask, ...)                    -> TIS/MIS weights, rejection
     align(hidden, input_ids, response_mask)               -> rows, targets, mask
 """
 
 from __future__ import annotations
 
 import ctypes
+import math
 
 import numpy as np
 import torch
 
-from ._lib import (EXPORTS, LP_OK, SEQ_STATS_DTYPE, TAIL_STATS_DTYPE, LpError,  # noqa: F401
-                   lib, status_string)
+from ._lib import (CORR_SEQ_DTYPE, EXPORTS, LP_OK, REJECT_K1, REJECT_K3,  # noqa: F401
+                   REJECT_NONE, SEQ_STATS_DTYPE, TAIL_STATS_DTYPE, LpError, lib, status_string)
 
 PAIRS = ("AB", "BC", "AC")
 
@@ -298,6 +300,37 @@ def merge_shards(partials: torch.Tensor, ids: torch.Tensor, v_true: int, stats: 
     if check and int(bad_rows.item()) != 0:
         raise ValueError(f"{int(bad_rows.item())} row(s) have a target id outside [0, {v_true})")
     return (out, ent, amax) if stats else out
+
+
+def correct(rollout: torch.Tensor, train: torch.Tensor, mask: torch.Tensor,
+            tis_clip: float = 2.0, mis_log_lo: float = -math.inf, mis_log_hi: float = math.inf,
+            reject: int = REJECT_NONE, reject_lo: float = -math.inf,
+            reject_hi: float = math.inf, weights: bool = True):
+    """Correction weights of r = pi_train / pi_rollout (lp_correct): TIS cap
+    `tis_clip`, MIS interval [mis_log_lo, mis_log_hi] on log r, sequence
+    rejection by sum K1 / K3 outside [reject_lo, reject_hi]. Returns
+    (weights fp32 [N, L] device tensor or None, numpy records of
+    CORR_SEQ_DTYPE [N]); synchronises."""
+    for name, t in (("rollout", rollout), ("train", train)):
+        _need_cuda(name, t, torch.float32)
+    _need_cuda("mask", mask, torch.uint8)
+    if not (rollout.shape == train.shape == mask.shape) or rollout.dim() != 2:
+        raise ValueError("rollout, train and mask must share one [N, L] shape")
+    N, L = rollout.shape
+    ld = rollout.stride(0) if rollout.numel() else L
+    for t in (rollout, train, mask):
+        if t.numel() and (t.stride(1) != 1 or (N > 1 and t.stride(0) != ld)):
+            raise ValueError("rollout, train and mask need unit column stride and one row stride")
+    dev = rollout.device
+    w = torch.empty((N, L), dtype=torch.float32, device=dev) if weights else None
+    out = torch.empty(max(N * CORR_SEQ_DTYPE.itemsize, 1), dtype=torch.uint8, device=dev)
+    st = lib().lp_correct(_ptr(rollout), _ptr(train), _ptr(mask), N, L, max(ld, L),
+                          float(tis_clip), float(mis_log_lo), float(mis_log_hi), int(reject),
+                          float(reject_lo), float(reject_hi), _ptr(w), _ptr(out), _stream(dev))
+    if st != LP_OK:
+        raise LpError(st, "lp_correct")
+    rec = out[:N * CORR_SEQ_DTYPE.itemsize].cpu().numpy().view(CORR_SEQ_DTYPE)
+    return w, rec
 
 
 def align(hidden: torch.Tensor, input_ids: torch.Tensor, response_mask: torch.Tensor):

@@ -20,7 +20,17 @@ EXPORTS = ("lp_status_string", "lp_score_workspace_bytes", "lp_score",
            "lp_score_stats_workspace_bytes", "lp_score_stats", "lp_compare",
            "lp_compare_tails_workspace_bytes", "lp_compare_tails",
            "lp_vocab_shard_range", "lp_shard_partials_bytes",
-           "lp_score_shard_workspace_bytes", "lp_score_shard", "lp_merge_shards")
+           "lp_score_shard_workspace_bytes", "lp_score_shard", "lp_merge_shards",
+           "lp_correct")
+
+REJECT_NONE, REJECT_K1, REJECT_K3 = 0, 1, 3  # LP_REJECT_*
+
+# numpy mirror of `lp_corr_seq` (6 int32 then 2 double).
+CORR_SEQ_DTYPE = np.dtype([
+    ("valid", "<i4"), ("nonfinite", "<i4"), ("kept", "<i4"), ("capped", "<i4"),
+    ("accepted", "<i4"), ("reserved", "<i4"), ("stat", "<f8"), ("sum_weight", "<f8"),
+], align=True)
+assert CORR_SEQ_DTYPE.itemsize == 40
 
 MERGE_SEGMENTS = 16  # LP_MERGE_SEGMENTS
 
@@ -100,6 +110,9 @@ def lib() -> ctypes.CDLL:
                                  vp, vp, ctypes.c_size_t, vp]
     L.lp_merge_shards.restype = ctypes.c_int
     L.lp_merge_shards.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, vp]
+    f64 = ctypes.c_double
+    L.lp_correct.restype = ctypes.c_int
+    L.lp_correct.argtypes = [vp, vp, vp, i64, i64, i64, f64, f64, f64, i32, f64, f64, vp, vp, vp]
     _lib = L
     return L
 

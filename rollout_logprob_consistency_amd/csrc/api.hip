@@ -268,6 +268,42 @@ lp_status lp_compare(const float* gen_A, const float* replay_B, const float* tra
   return lp::launch_compare(a, stream) == hipSuccess ? LP_OK : LP_EHIP;
 }
 
+lp_status lp_correct(const float* rollout_lp, const float* train_lp, const uint8_t* mask,
+                     int64_t N, int64_t L, int64_t ld, double tis_clip, double mis_log_lo,
+                     double mis_log_hi, int32_t reject_kind, double reject_lo, double reject_hi,
+                     float* weights, lp_corr_seq* out, hipStream_t stream) {
+  if (N < 0 || L < 0 || ld < L) return LP_EINVAL;
+  if (isnan(tis_clip) || !(tis_clip > 0.0)) return LP_EINVAL;
+  if (isnan(mis_log_lo) || isnan(mis_log_hi) || mis_log_lo > mis_log_hi) return LP_EINVAL;
+  if (isnan(reject_lo) || isnan(reject_hi) || reject_lo > reject_hi) return LP_EINVAL;
+  if (reject_kind != LP_REJECT_NONE && reject_kind != LP_REJECT_K1 &&
+      reject_kind != LP_REJECT_K3)
+    return LP_EINVAL;
+  if (N == 0) return LP_OK;
+  if (!out) return LP_EINVAL;
+  if (L > 0 && (!rollout_lp || !train_lp || !mask)) return LP_EINVAL;
+  if (L > kI32Max || N > kI32Max) return LP_EUNSUPPORTED;
+  lp::CorrectArgs a;
+  a.rollout = rollout_lp;
+  a.train = train_lp;
+  a.mask = mask;
+  a.N = N;
+  a.L = L;
+  a.ld = ld;
+  a.kind = reject_kind;
+  a.cap = tis_clip;
+  a.log_cap = log(tis_clip);
+  a.log_lo = mis_log_lo;
+  a.log_hi = mis_log_hi;
+  a.rej_lo = reject_lo;
+  a.rej_hi = reject_hi;
+  a.weights = weights;
+  a.out = out;
+  a.vec = ld % 4 == 0 && aligned(rollout_lp, 16) && aligned(train_lp, 16) && aligned(mask, 4) &&
+          aligned(weights, 16);
+  return lp::launch_correct(a, stream) == hipSuccess ? LP_OK : LP_EHIP;
+}
+
 size_t lp_compare_tails_workspace_bytes(int64_t N, int64_t L) {
   if (N < 0 || L < 0 || N > kI32Max || L > kI32Max) return 0;
   return lp::tails_workspace_bytes(N, L);

@@ -88,6 +88,22 @@ struct CompareArgs {
 
 hipError_t launch_compare(const CompareArgs& a, hipStream_t stream);
 
+struct CorrectArgs {
+  const float* rollout;   // [N, ld] log pi_rollout of the sampled tokens
+  const float* train;     // [N, ld] log pi_train (old trainer) of the same tokens
+  const uint8_t* mask;    // [N, ld]
+  int64_t N, L, ld;
+  int32_t kind;           // LP_REJECT_NONE / _K1 / _K3
+  double cap, log_cap;    // TIS cap C and log C (log C = +inf: no cap)
+  double log_lo, log_hi;  // MIS interval on log r
+  double rej_lo, rej_hi;  // accepted range of the sequence statistic
+  bool vec;               // rows 16-byte aligned and ld % 4 == 0
+  float* weights;         // [N, L] or null
+  lp_corr_seq* out;       // [N]
+};
+
+hipError_t launch_correct(const CorrectArgs& a, hipStream_t stream);
+
 struct TailArgs {
   const float* A;
   const float* B;

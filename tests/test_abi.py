@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
          "lp_score_stats_workspace_bytes", "lp_score_stats", "lp_compare",
          "lp_compare_tails_workspace_bytes", "lp_compare_tails",
          "lp_vocab_shard_range", "lp_shard_partials_bytes",
-         "lp_score_shard_workspace_bytes", "lp_score_shard", "lp_merge_shards"])
+         "lp_score_shard_workspace_bytes", "lp_score_shard", "lp_merge_shards",
+         "lp_correct"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -253,3 +254,35 @@ def test_merge_shards_rejects_bad_arguments(L):
     assert m(P, P, 8, 1000, 1, P, None, None, P, None, None) == EINVAL   # stats needs both outputs
     assert m(ctypes.c_void_p(0x10002), P, 8, 1000, 0, P, None, None, None, None, None) == EINVAL
     assert m(P, P, 0, 1000, 0, None, None, None, None, None, None) == 0
+
+
+def corr(L, r=P, t=P, m=P, N=2, Lq=5, ld=None, C=2.0, lo=-1.0, hi=1.0, kind=1, rlo=-1.0, rhi=1.0,
+         w=P, out=P):
+    return L.lp_correct(r, t, m, N, Lq, Lq if ld is None else ld, C, lo, hi, kind, rlo, rhi,
+                        w, out, None)
+
+
+def test_correct_rejects_bad_arguments(L):
+    EINVAL = 1
+    inf, nan = float("inf"), float("nan")
+    assert corr(L, N=-1) == EINVAL
+    assert corr(L, Lq=-1) == EINVAL
+    assert corr(L, ld=3) == EINVAL
+    assert corr(L, C=0.0) == EINVAL
+    assert corr(L, C=-1.0) == EINVAL
+    assert corr(L, C=nan) == EINVAL
+    assert corr(L, lo=nan) == EINVAL
+    assert corr(L, lo=2.0, hi=1.0) == EINVAL
+    assert corr(L, rlo=nan) == EINVAL
+    assert corr(L, rlo=2.0, rhi=1.0) == EINVAL
+    assert corr(L, kind=2) == EINVAL
+    assert corr(L, out=None) == EINVAL
+    assert corr(L, r=None) == EINVAL
+    assert corr(L, m=None) == EINVAL
+    assert corr(L, N=0, C=inf) == 0                      # nothing to do (and C = inf is allowed)
+
+
+def test_corr_seq_layout():
+    from rollout_logprob_consistency_amd import _lib
+    assert _lib.CORR_SEQ_DTYPE.itemsize == 40
+    assert [_lib.CORR_SEQ_DTYPE.fields[f][1] for f in ("accepted", "stat", "sum_weight")] == [16, 24, 32]
