@@ -239,6 +239,25 @@ def main() -> int:
                  "frac": round(flops / st_med / 1e6 / PEAK_BF16_TFLOPS, 4)}
     log(f"bench: lp_score_stats {st_med / 1e3:.3f} ms = {flops / st_med / 1e6:.1f} TFLOP/s")
 
+    # The bf16-logit mode (lp_score_ex): one conversion per logit in the epilogue.
+    out_bf = torch.empty(T, dtype=torch.float32, device=dev)
+    c_ex = lp._lib.lib().lp_score_ex
+    ex_args = (x.data_ptr(), H, w.data_ptr(), ids.data_ptr(), T, H, V, V, 1.0,
+               lp.SCORE_BF16_LOGITS, out_bf.data_ptr(), None, None, None, None, ws.data_ptr(),
+               ws.numel(), torch.cuda.current_stream().cuda_stream)
+
+    def score_bf16_call():
+        st_ = c_ex(*ex_args)
+        if st_ != lp.LP_OK:
+            raise lp.LpError(st_, "lp_score_ex")
+
+    bf_med, bf_lo, bf_hi = median_us(score_bf16_call, calls=3, reps=5)
+    bf16_rec = {"ms": round(bf_med / 1e3, 4), "min_ms": round(bf_lo / 1e3, 4),
+                "max_ms": round(bf_hi / 1e3, 4),
+                "TFLOPs": round(flops / bf_med / 1e6, 2),
+                "frac": round(flops / bf_med / 1e6 / PEAK_BF16_TFLOPS, 4)}
+    log(f"bench: lp_score_ex bf16 logits {bf_med / 1e3:.3f} ms = {flops / bf_med / 1e6:.1f} TFLOP/s")
+
     # Vocabulary-parallel scoring at its per-GPU shape: rank 0 of 8 canonical
     # shards scores its rows of W; the merge folds the 16 gathered segment
     # records. All 8 shards, scored here one after another into one exchange
@@ -398,6 +417,7 @@ def main() -> int:
                     "lp_score_ms_max": round(max(score_ms), 4),
                     "lp_compare_us": round(cmp_avg * 1e6, 2)},
         "score_stats": stats_rec,
+        "score_bf16_logits": bf16_rec,
         "vocab_parallel": shard_rec,
         "small_batch": small,
         "compare_sweep": sweep,

@@ -136,6 +136,41 @@ lp_status lp_score_stats(const void* hidden_bf16, int64_t ldh,
                          size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Scoring with options: lp_score_ex
+ *
+ * flags (bitwise or):
+ *   LP_SCORE_STATS        also write out_entropy and out_argmax, exactly as
+ *                         lp_score_stats (both then required)
+ *   LP_SCORE_BF16_LOGITS  round every fp32-accumulated logit to bf16 (round
+ *                         to nearest even) before the temperature and the
+ *                         log-softmax, which stay fp32: the score a trainer
+ *                         gets when its LM head stores logits in the model's
+ *                         bf16 and only the final log-softmax is cast to fp32
+ *                         ([AMD] "Collect A/B and C", notes on the trainer's
+ *                         extraction: the fp32 cast applies to the final
+ *                         log-softmax, upstream computation keeps its own
+ *                         precision; [vLLM] "Metric measurement basis":
+ *                         align the logits' precision before comparing).
+ * flags = 0 is lp_score and flags = LP_SCORE_STATS is lp_score_stats, bit
+ * for bit. Workspace: lp_score_ex_workspace_bytes(T, H, V_rows, V_true,
+ * flags) (0 for invalid arguments). Errors as for lp_score, plus LP_EINVAL
+ * for unknown flag bits.
+ * ------------------------------------------------------------------------ */
+#define LP_SCORE_STATS 1u
+#define LP_SCORE_BF16_LOGITS 2u
+
+size_t lp_score_ex_workspace_bytes(int64_t T, int64_t H, int64_t V_rows,
+                                   int64_t V_true, uint32_t flags);
+
+lp_status lp_score_ex(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
+                      const int64_t* target_ids, int64_t T, int64_t H,
+                      int64_t V_rows, int64_t V_true, float temperature,
+                      uint32_t flags, float* out_logprob, float* out_lse,
+                      float* out_entropy, int64_t* out_argmax,
+                      int32_t* bad_rows, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Three-way comparison of generation (A), replay (B) and trainer (C) scores
  *
  * [AMD] "One Response, Three Scores", "Check Whether the Pattern Extends",
@@ -279,22 +314,23 @@ lp_status lp_compare_tails(const float* gen_A, const float* replay_B,
  * row_end) of W, contiguous [row_end - row_begin, H] bf16; the other
  * arguments are lp_score's with V_true the WHOLE true vocabulary size. It
  * writes the records of its own segments into `partials`, a buffer of
- * lp_shard_partials_bytes(T, stats) bytes laid out [16][F][T] fp32 (F = 3:
+ * lp_shard_partials_bytes(T, flags) bytes laid out [16][F][T] fp32 (F = 3:
  * max and sum of exp2 in log2 units and the target's scaled logit, 0 where
- * the target is not in the segment; F = 5 with stats: also the entropy term
+ * the target is not in the segment; F = 5 with LP_SCORE_STATS: also the entropy term
  * and the argmax row as int32 bits). A rank's segments are one contiguous
  * byte range, so the exchange is one all-gather of T F 4 16 / n bytes per
  * rank (equal blocks when n divides 16). Workspace:
- * lp_score_shard_workspace_bytes(T, V_true, n, r, stats), 256-byte aligned.
+ * lp_score_shard_workspace_bytes(T, V_true, n, r, flags), 256-byte aligned.
+ * flags are lp_score_ex's (LP_SCORE_STATS, LP_SCORE_BF16_LOGITS).
  *
  * lp_merge_shards folds the 16 records of each row in segment order and
- * writes what lp_score (stats = 0) or lp_score_stats (stats = 1) writes.
- * The results are BITWISE equal to lp_score / lp_score_stats on the whole W
+ * writes what lp_score_ex with the same flags writes.
+ * The results are BITWISE equal to lp_score_ex on the whole W
  * for any n: the tiles, their K order, every fold and its order are the
  * same. A target outside [0, V_true) gives NaN and ++*bad_rows in the merge.
  *
  * Errors: LP_EINVAL for T < 0, H < 1, ldh < H, V_true < 1, n outside
- * [1, 16], rank outside [0, n), stats not 0/1, a bad temperature, NULL
+ * [1, 16], rank outside [0, n), unknown flag bits, a bad temperature, NULL
  * required pointers (hidden and w_shard may be NULL for an empty shard), a
  * small or misaligned workspace or a misaligned partials buffer;
  * LP_EUNSUPPORTED as for lp_score. T == 0 does nothing.
@@ -311,21 +347,21 @@ typedef struct {
 lp_status lp_vocab_shard_range(int64_t V_true, int32_t n_shards, int32_t rank,
                                lp_vocab_shard* out);
 
-size_t lp_shard_partials_bytes(int64_t T, int32_t stats);
+size_t lp_shard_partials_bytes(int64_t T, uint32_t flags);
 
 size_t lp_score_shard_workspace_bytes(int64_t T, int64_t V_true,
                                       int32_t n_shards, int32_t rank,
-                                      int32_t stats);
+                                      uint32_t flags);
 
 lp_status lp_score_shard(const void* hidden_bf16, int64_t ldh,
                          const void* w_shard_bf16, const int64_t* target_ids,
                          int64_t T, int64_t H, int64_t V_true,
                          float temperature, int32_t n_shards, int32_t rank,
-                         int32_t stats, void* partials, void* workspace,
+                         uint32_t flags, void* partials, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
 lp_status lp_merge_shards(const void* partials, const int64_t* target_ids,
-                          int64_t T, int64_t V_true, int32_t stats,
+                          int64_t T, int64_t V_true, uint32_t flags,
                           float* out_logprob, float* out_lse,
                           float* out_entropy, int64_t* out_argmax,
                           int32_t* bad_rows, hipStream_t stream);

@@ -9,6 +9,7 @@ streams.
 
     score(hidden, w, ids, temperature=1.0, v_true=None)   -> logprob [T] fp32
     score_stats(hidden, w, ids, ...)                      -> logprob, entropy, argmax
+    score_ex(hidden, w, ids, ..., stats, bf16_logits)     -> either, optionally bf16 logits
     compare(A, B, C, mask, tis_clip=2.0, atol=None)       -> stats per pair
     compare_tails(A, B, C, mask, positions=False)         -> batch tails per pair
     vocab_shard / score_shard / merge_shards              -> vocabulary-parallel scoring
@@ -137,6 +138,49 @@ def score_stats(hidden: torch.Tensor, w: torch.Tensor, ids: torch.Tensor,
     return out, ent, amax
 
 
+SCORE_STATS, SCORE_BF16_LOGITS = 1, 2  # LP_SCORE_* flags
+
+
+def score_ex(hidden: torch.Tensor, w: torch.Tensor, ids: torch.Tensor,
+             temperature: float = 1.0, v_true: int | None = None, *, stats: bool = False,
+             bf16_logits: bool = False, lse: torch.Tensor | None = None,
+             workspace: torch.Tensor | None = None, check: bool = False):
+    """lp_score_ex: score() (stats=False) or score_stats() (stats=True), with
+    bf16_logits=True rounding every fp32 logit to bf16 before the tempered
+    log-softmax (the score of an LM head that stores bf16 logits). Returns
+    logprob, or (logprob, entropy, argmax) with stats."""
+    _need_cuda("hidden", hidden, torch.bfloat16)
+    _need_cuda("w", w, torch.bfloat16)
+    _need_cuda("ids", ids, torch.int64)
+    if hidden.dim() != 2 or w.dim() != 2 or ids.dim() != 1:
+        raise ValueError("expected hidden [T, H], w [V, H], ids [T]")
+    if hidden.stride(1) != 1 or not w.is_contiguous() or not ids.is_contiguous():
+        raise ValueError("hidden needs unit column stride; w and ids must be contiguous")
+    T, H = hidden.shape
+    V = w.shape[0]
+    if w.shape[1] != H or ids.shape[0] != T:
+        raise ValueError("shape mismatch between hidden, w and ids")
+    vt = V if v_true is None else int(v_true)
+    flags = (SCORE_STATS if stats else 0) | (SCORE_BF16_LOGITS if bf16_logits else 0)
+    dev = hidden.device
+    out = torch.empty(T, dtype=torch.float32, device=dev)
+    ent = torch.empty(T, dtype=torch.float32, device=dev) if stats else None
+    amax = torch.empty(T, dtype=torch.int64, device=dev) if stats else None
+    need = int(lib().lp_score_ex_workspace_bytes(T, H, V, vt, flags))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    bad_rows = torch.zeros(1, dtype=torch.int32, device=dev) if check else None
+    st = lib().lp_score_ex(_ptr(hidden), hidden.stride(0) if T else H, _ptr(w), _ptr(ids),
+                           T, H, V, vt, float(temperature), flags, _ptr(out), _ptr(lse),
+                           _ptr(ent), _ptr(amax), _ptr(bad_rows), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(dev))
+    if st != LP_OK:
+        raise LpError(st, "lp_score_ex")
+    if check and int(bad_rows.item()) != 0:
+        raise ValueError(f"{int(bad_rows.item())} row(s) have a target id outside [0, {vt})")
+    return (out, ent, amax) if stats else out
+
+
 def compare_raw(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch.Tensor,
                 tis_clip: float = 2.0, atol: float | None = None,
                 per_token: bool = False, out: torch.Tensor | None = None):
@@ -239,13 +283,14 @@ def vocab_shard(v_true: int, n_shards: int, rank: int) -> dict:
 def shard_partials(T: int, stats: bool = False, device=None) -> torch.Tensor:
     """An exchange buffer for T rows: [16, F, T] fp32 (F = 5 with stats, else 3)."""
     F = 5 if stats else 3
-    assert int(lib().lp_shard_partials_bytes(T, int(stats))) == 16 * F * T * 4
+    assert int(lib().lp_shard_partials_bytes(T, SCORE_STATS if stats else 0)) == 16 * F * T * 4
     return torch.empty((16, F, T), dtype=torch.float32, device=device)
 
 
 def score_shard(hidden: torch.Tensor, w_shard: torch.Tensor, ids: torch.Tensor, v_true: int,
                 n_shards: int, rank: int, partials: torch.Tensor, temperature: float = 1.0,
-                stats: bool = False, *, workspace: torch.Tensor | None = None) -> torch.Tensor:
+                stats: bool = False, *, bf16_logits: bool = False,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Score one vocabulary shard (lp_score_shard): w_shard holds rows
     [row_begin, row_end) of W; writes this shard's segment records into
     `partials` (from shard_partials) and returns it. Does not synchronise."""
@@ -264,12 +309,13 @@ def score_shard(hidden: torch.Tensor, w_shard: torch.Tensor, ids: torch.Tensor, 
     F = 5 if stats else 3
     if not partials.is_contiguous() or partials.shape != (16, F, T):
         raise ValueError(f"partials must be a contiguous [16, {F}, T] buffer")
-    need = int(lib().lp_score_shard_workspace_bytes(T, v_true, n_shards, rank, int(stats)))
+    flags = (SCORE_STATS if stats else 0) | (SCORE_BF16_LOGITS if bf16_logits else 0)
+    need = int(lib().lp_score_shard_workspace_bytes(T, v_true, n_shards, rank, flags))
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
     st = lib().lp_score_shard(_ptr(hidden), hidden.stride(0) if T else H, _ptr(w_shard),
                               _ptr(ids), T, H, int(v_true), float(temperature), int(n_shards),
-                              int(rank), int(stats), _ptr(partials), _ptr(workspace),
+                              int(rank), flags, _ptr(partials), _ptr(workspace),
                               workspace.numel() * workspace.element_size(),
                               _stream(hidden.device))
     if st != LP_OK:
@@ -293,7 +339,8 @@ def merge_shards(partials: torch.Tensor, ids: torch.Tensor, v_true: int, stats: 
     ent = torch.empty(T, dtype=torch.float32, device=dev) if stats else None
     amax = torch.empty(T, dtype=torch.int64, device=dev) if stats else None
     bad_rows = torch.zeros(1, dtype=torch.int32, device=dev) if check else None
-    st = lib().lp_merge_shards(_ptr(partials), _ptr(ids), T, int(v_true), int(stats), _ptr(out),
+    st = lib().lp_merge_shards(_ptr(partials), _ptr(ids), T, int(v_true),
+                               SCORE_STATS if stats else 0, _ptr(out),
                                _ptr(lse), _ptr(ent), _ptr(amax), _ptr(bad_rows), _stream(dev))
     if st != LP_OK:
         raise LpError(st, "lp_merge_shards")

@@ -21,7 +21,7 @@ EXPORTS = ("lp_status_string", "lp_score_workspace_bytes", "lp_score",
            "lp_compare_tails_workspace_bytes", "lp_compare_tails",
            "lp_vocab_shard_range", "lp_shard_partials_bytes",
            "lp_score_shard_workspace_bytes", "lp_score_shard", "lp_merge_shards",
-           "lp_correct")
+           "lp_correct", "lp_score_ex_workspace_bytes", "lp_score_ex")
 
 REJECT_NONE, REJECT_K1, REJECT_K3 = 0, 1, 3  # LP_REJECT_*
 
@@ -99,17 +99,23 @@ def lib() -> ctypes.CDLL:
     L.lp_compare_tails.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp,
                                    ctypes.c_size_t, vp]
     i32 = ctypes.c_int32
+    u32 = ctypes.c_uint32
+    L.lp_score_ex_workspace_bytes.restype = ctypes.c_size_t
+    L.lp_score_ex_workspace_bytes.argtypes = [i64, i64, i64, i64, u32]
+    L.lp_score_ex.restype = ctypes.c_int
+    L.lp_score_ex.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, f32, u32, vp, vp, vp, vp, vp,
+                              vp, ctypes.c_size_t, vp]
     L.lp_vocab_shard_range.restype = ctypes.c_int
     L.lp_vocab_shard_range.argtypes = [i64, i32, i32, ctypes.POINTER(VocabShard)]
     L.lp_shard_partials_bytes.restype = ctypes.c_size_t
-    L.lp_shard_partials_bytes.argtypes = [i64, i32]
+    L.lp_shard_partials_bytes.argtypes = [i64, u32]
     L.lp_score_shard_workspace_bytes.restype = ctypes.c_size_t
-    L.lp_score_shard_workspace_bytes.argtypes = [i64, i64, i32, i32, i32]
+    L.lp_score_shard_workspace_bytes.argtypes = [i64, i64, i32, i32, u32]
     L.lp_score_shard.restype = ctypes.c_int
-    L.lp_score_shard.argtypes = [vp, i64, vp, vp, i64, i64, i64, f32, i32, i32, i32,
+    L.lp_score_shard.argtypes = [vp, i64, vp, vp, i64, i64, i64, f32, i32, i32, u32,
                                  vp, vp, ctypes.c_size_t, vp]
     L.lp_merge_shards.restype = ctypes.c_int
-    L.lp_merge_shards.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, vp]
+    L.lp_merge_shards.argtypes = [vp, vp, i64, i64, u32, vp, vp, vp, vp, vp, vp]
     f64 = ctypes.c_double
     L.lp_correct.restype = ctypes.c_int
     L.lp_correct.argtypes = [vp, vp, vp, i64, i64, i64, f64, f64, f64, i32, f64, f64, vp, vp, vp]

@@ -13,6 +13,7 @@ namespace {
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 constexpr int64_t kI32Max = std::numeric_limits<int32_t>::max();
+constexpr uint32_t kScoreFlags = LP_SCORE_STATS | LP_SCORE_BF16_LOGITS;
 
 // Canonical shard of the merge segments: rank r of n owns segments
 // [16 r / n, 16 (r + 1) / n) and the vocabulary rows they cover.
@@ -42,33 +43,36 @@ lp_status lp_vocab_shard_range(int64_t V_true, int32_t n_shards, int32_t rank,
   return LP_OK;
 }
 
-size_t lp_shard_partials_bytes(int64_t T, int32_t stats) {
-  if (T < 0 || T > kI32Max) return 0;
-  return (size_t)lp::kMergeSegs * (stats ? 5 : 3) * (size_t)T * sizeof(float);
+size_t lp_shard_partials_bytes(int64_t T, uint32_t flags) {
+  if (T < 0 || T > kI32Max || (flags & ~kScoreFlags)) return 0;
+  return (size_t)lp::kMergeSegs * ((flags & LP_SCORE_STATS) ? 5 : 3) * (size_t)T * sizeof(float);
 }
 
 size_t lp_score_shard_workspace_bytes(int64_t T, int64_t V_true, int32_t n_shards, int32_t rank,
-                                      int32_t stats) {
-  if (T < 0 || T > kI32Max || !shard_args_ok(V_true, n_shards, rank)) return 0;
+                                      uint32_t flags) {
+  if (T < 0 || T > kI32Max || !shard_args_ok(V_true, n_shards, rank) || (flags & ~kScoreFlags))
+    return 0;
   const lp_vocab_shard sh = shard_of(V_true, n_shards, rank);
-  const size_t total = lp::score_workspace_layout(T, sh.row_end - sh.row_begin, stats != 0).total;
+  const size_t total =
+      lp::score_workspace_layout(T, sh.row_end - sh.row_begin, (flags & LP_SCORE_STATS) != 0).total;
   return total < 256 ? 256 : total;
 }
 
 lp_status lp_score_shard(const void* hidden_bf16, int64_t ldh, const void* w_shard_bf16,
                          const int64_t* target_ids, int64_t T, int64_t H, int64_t V_true,
-                         float temperature, int32_t n_shards, int32_t rank, int32_t stats,
+                         float temperature, int32_t n_shards, int32_t rank, uint32_t flags,
                          void* partials, void* workspace, size_t workspace_bytes,
                          hipStream_t stream) {
   if (T < 0 || H < 1 || ldh < H || !shard_args_ok(V_true, n_shards, rank)) return LP_EINVAL;
-  if (stats != 0 && stats != 1) return LP_EINVAL;
+  if (flags & ~kScoreFlags) return LP_EINVAL;
+  const bool stats = (flags & LP_SCORE_STATS) != 0;
   if (!(isfinite(temperature) && temperature > 0.0f)) return LP_EINVAL;
   if (T == 0) return LP_OK;
   const lp_vocab_shard sh = shard_of(V_true, n_shards, rank);
   const int64_t rows = sh.row_end - sh.row_begin;
   if (!target_ids || !partials || !workspace) return LP_EINVAL;
   if (rows > 0 && (!hidden_bf16 || !w_shard_bf16)) return LP_EINVAL;
-  const lp::ScoreWorkspace ws = lp::score_workspace_layout(T, rows, stats != 0);
+  const lp::ScoreWorkspace ws = lp::score_workspace_layout(T, rows, stats);
   if (workspace_bytes < ws.total || !aligned(workspace, 256) || !aligned(partials, 4))
     return LP_EINVAL;
   if (H % lp::kTileK != 0 || ldh % 8 != 0) return LP_EUNSUPPORTED;
@@ -88,6 +92,7 @@ lp_status lp_score_shard(const void* hidden_bf16, int64_t ldh, const void* w_sha
   a.V_rows = (int32_t)rows;
   a.V_true = (int32_t)rows;
   a.v_base = (int32_t)sh.row_begin;
+  a.bf16_logits = (flags & LP_SCORE_BF16_LOGITS) != 0;
   a.n_vt = (int32_t)n_vt;
   a.n_tt = (int32_t)n_tt;
   a.scale2 = (float)(1.4426950408889634 / (double)temperature);
@@ -117,10 +122,11 @@ lp_status lp_score_shard(const void* hidden_bf16, int64_t ldh, const void* w_sha
 }
 
 lp_status lp_merge_shards(const void* partials, const int64_t* target_ids, int64_t T,
-                          int64_t V_true, int32_t stats, float* out_logprob, float* out_lse,
+                          int64_t V_true, uint32_t flags, float* out_logprob, float* out_lse,
                           float* out_entropy, int64_t* out_argmax, int32_t* bad_rows,
                           hipStream_t stream) {
-  if (T < 0 || V_true < 1 || (stats != 0 && stats != 1)) return LP_EINVAL;
+  if (T < 0 || V_true < 1 || (flags & ~kScoreFlags)) return LP_EINVAL;
+  const bool stats = (flags & LP_SCORE_STATS) != 0;
   if (T == 0) return LP_OK;
   if (!partials || !target_ids || !out_logprob || !aligned(partials, 4)) return LP_EINVAL;
   if (stats && (!out_entropy || !out_argmax)) return LP_EINVAL;
@@ -173,8 +179,9 @@ namespace {
 lp_status score_impl(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
                      const int64_t* target_ids, int64_t T, int64_t H, int64_t V_rows,
                      int64_t V_true, float temperature, float* out_logprob, float* out_lse,
-                     float* out_entropy, int64_t* out_argmax, bool stats, int32_t* bad_rows,
-                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                     float* out_entropy, int64_t* out_argmax, bool stats, bool bf16,
+                     int32_t* bad_rows, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
   if (T < 0 || H < 1 || V_rows < 1 || V_true < 1 || V_true > V_rows || ldh < H)
     return LP_EINVAL;
   if (!(isfinite(temperature) && temperature > 0.0f)) return LP_EINVAL;
@@ -200,6 +207,7 @@ lp_status score_impl(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
   a.V_rows = (int32_t)V_rows;
   a.V_true = (int32_t)V_true;
   a.v_base = 0;
+  a.bf16_logits = bf16;
   a.n_vt = (int32_t)n_vt;
   a.n_tt = (int32_t)n_tt;
   a.scale2 = (float)(1.4426950408889634 / (double)temperature);
@@ -227,7 +235,7 @@ lp_status lp_score(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
                    int32_t* bad_rows, void* workspace, size_t workspace_bytes,
                    hipStream_t stream) {
   return score_impl(hidden_bf16, ldh, w_bf16, target_ids, T, H, V_rows, V_true, temperature,
-                    out_logprob, out_lse, nullptr, nullptr, false, bad_rows, workspace,
+                    out_logprob, out_lse, nullptr, nullptr, false, false, bad_rows, workspace,
                     workspace_bytes, stream);
 }
 
@@ -237,8 +245,28 @@ lp_status lp_score_stats(const void* hidden_bf16, int64_t ldh, const void* w_bf1
                          float* out_entropy, int64_t* out_argmax, int32_t* bad_rows,
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return score_impl(hidden_bf16, ldh, w_bf16, target_ids, T, H, V_rows, V_true, temperature,
-                    out_logprob, out_lse, out_entropy, out_argmax, true, bad_rows, workspace,
-                    workspace_bytes, stream);
+                    out_logprob, out_lse, out_entropy, out_argmax, true, false, bad_rows,
+                    workspace, workspace_bytes, stream);
+}
+
+size_t lp_score_ex_workspace_bytes(int64_t T, int64_t H, int64_t V_rows, int64_t V_true,
+                                   uint32_t flags) {
+  if (T < 0 || H < 1 || V_true < 1 || V_true > V_rows || (flags & ~kScoreFlags)) return 0;
+  return lp::score_workspace_layout(T, V_true, (flags & LP_SCORE_STATS) != 0).total;
+}
+
+lp_status lp_score_ex(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
+                      const int64_t* target_ids, int64_t T, int64_t H, int64_t V_rows,
+                      int64_t V_true, float temperature, uint32_t flags, float* out_logprob,
+                      float* out_lse, float* out_entropy, int64_t* out_argmax,
+                      int32_t* bad_rows, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  if (flags & ~kScoreFlags) return LP_EINVAL;
+  const bool stats = (flags & LP_SCORE_STATS) != 0;
+  return score_impl(hidden_bf16, ldh, w_bf16, target_ids, T, H, V_rows, V_true, temperature,
+                    out_logprob, out_lse, stats ? out_entropy : nullptr,
+                    stats ? out_argmax : nullptr, stats, (flags & LP_SCORE_BF16_LOGITS) != 0,
+                    bad_rows, workspace, workspace_bytes, stream);
 }
 
 lp_status lp_compare(const float* gen_A, const float* replay_B, const float* train_C,

@@ -28,6 +28,7 @@ struct ScoreArgs {
   int64_t ldh;
   int32_t T, H, V_rows, V_true;
   int32_t v_base;         // vocabulary index of W row 0 (0 unless a shard)
+  bool bf16_logits;       // round the fp32 logits to bf16 before the scale
   int32_t n_vt, n_tt;     // vocabulary / token tile counts
   float scale2;           // log2(e) / temperature
   float* part_m;          // [n_vt][T]  per-tile max (log2 units)

@@ -242,6 +242,15 @@ __device__ __forceinline__ float merge_q(float m0, float s0, float q0, float m1,
 // vocabulary row of the wave + 4 (lane >> 4). The epilogue takes this masked
 // view only in that tile (a uniform branch), so the accumulators are never
 // rewritten.
+// The logit the epilogue uses: the fp32 accumulator, or with kBf16 that
+// value rounded to bf16 (round to nearest even, v_cvt_pk_bf16_f32) and
+// widened back, as an LM head whose output is stored in bf16 would give it.
+template <bool kBf16>
+__device__ __forceinline__ float logit(float acc) {
+  if (!kBf16) return acc;
+  return static_cast<float>(static_cast<__bf16>(acc));
+}
+
 #define LP_MASKED(x_, vlane_, i_, r_, V_) \
   (((vlane_) + 16 * (i_) + (r_) >= (V_)) ? -__builtin_inff() : (x_))
 
@@ -270,7 +279,7 @@ constexpr int kCopiesU = kSlotB / 1024 / 4;  // 1-KiB copies per wave per unit
 static_assert(kCopiesU == 8, "copy schedule assumes 8 copies per wave per unit");
 static_assert(kSlots * kSlotB <= 160 * 1024, "LDS");
 
-template <bool kStats>
+template <bool kStats, bool kBf16>
 __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   // Ring of kSlots units; the 16-byte chunks of row r are XOR-permuted by
   // swz(). After the K loop the first 2 KiB hold the cross-wave reduction.
@@ -435,9 +444,9 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   for (int j = 0; j < kSubT; ++j) {
     const int tl = wn * kWaveT + j * 16 + lcol;
     const int t = t0 + tl;
-    auto v = [&](int i, int r) __attribute__((always_inline)) { return acc[i][j][r]; };
+    auto v = [&](int i, int r) __attribute__((always_inline)) { return logit<kBf16>(acc[i][j][r]); };
     auto vm = [&](int i, int r) __attribute__((always_inline)) {
-      return LP_MASKED(acc[i][j][r], vlane, i, r, a.V_true);
+      return LP_MASKED(logit<kBf16>(acc[i][j][r]), vlane, i, r, a.V_true);
     };
     float m, s, q;
     int li;
@@ -514,7 +523,7 @@ struct Stream {
   static_assert((kSmStages - 1) * kCopies <= 63, "vmcnt holds at most 63");
 };
 
-template <int ST, bool kStats>
+template <int ST, bool kStats, bool kBf16>
 __global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_items) {
   using S = Stream<ST>;
   __shared__ __attribute__((aligned(1024))) char ring[S::kLds];
@@ -611,9 +620,11 @@ __global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_ite
 #pragma unroll
       for (int jj = 0; jj < S::kTilesB; ++jj) {
         const int t = t0 + 16 * jj + lcol;
-        auto v = [&](int i, int r) __attribute__((always_inline)) { return acc[i][jj][r]; };
+        auto v = [&](int i, int r) __attribute__((always_inline)) {
+          return logit<kBf16>(acc[i][jj][r]);
+        };
         auto vm = [&](int i, int r) __attribute__((always_inline)) {
-          return LP_MASKED(acc[i][jj][r], vlane, i, r, a.V_true);
+          return LP_MASKED(logit<kBf16>(acc[i][jj][r]), vlane, i, r, a.V_true);
         };
         float m, s, q;
         int li;
@@ -839,28 +850,35 @@ ScoreWorkspace score_workspace_layout(int64_t T, int64_t V_true, bool stats) {
   return w;
 }
 
-template <int ST, bool kStats>
+template <int ST, bool kStats, bool kBf16>
 static void launch_stream(ScoreArgs a, hipStream_t stream) {
   a.n_tt = (a.T + 32 * ST - 1) / (32 * ST);
   const int n_items = 2 * a.n_vt * a.n_tt;
   // Workgroups (one wave each) per CU: as many as the LDS ring allows.
   const int per_cu = (160 * 1024) / Stream<ST>::kLds;
   const int grid = 256 * (per_cu < 8 ? per_cu : 8);
-  hipLaunchKernelGGL((score_stream_kernel<ST, kStats>), dim3(grid), dim3(64), 0, stream, a,
+  hipLaunchKernelGGL((score_stream_kernel<ST, kStats, kBf16>), dim3(grid), dim3(64), 0, stream, a,
                      n_items);
 }
 
 // The tile (or streaming) kernel alone; returns the streaming choice.
-template <bool kStats>
-static int launch_tiles(const ScoreArgs& a, hipStream_t stream) {
+template <bool kStats, bool kBf16>
+static int launch_tiles_t(const ScoreArgs& a, hipStream_t stream) {
   const int st = stream_tokens(a.T);
-  if (st == 1) launch_stream<1, kStats>(a, stream);
-  else if (st == 2) launch_stream<2, kStats>(a, stream);
+  if (st == 1) launch_stream<1, kStats, kBf16>(a, stream);
+  else if (st == 2) launch_stream<2, kStats, kBf16>(a, stream);
   else {
     const unsigned grid = (unsigned)a.n_vt * (unsigned)a.n_tt;
-    hipLaunchKernelGGL(score_tile_kernel<kStats>, dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((score_tile_kernel<kStats, kBf16>), dim3(grid), dim3(kThreads), 0, stream,
+                       a);
   }
   return st;
+}
+
+template <bool kStats>
+static int launch_tiles(const ScoreArgs& a, hipStream_t stream) {
+  return a.bf16_logits ? launch_tiles_t<kStats, true>(a, stream)
+                       : launch_tiles_t<kStats, false>(a, stream);
 }
 
 template <bool kStats>

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
          "lp_compare_tails_workspace_bytes", "lp_compare_tails",
          "lp_vocab_shard_range", "lp_shard_partials_bytes",
          "lp_score_shard_workspace_bytes", "lp_score_shard", "lp_merge_shards",
-         "lp_correct"])
+         "lp_correct", "lp_score_ex_workspace_bytes", "lp_score_ex"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -213,7 +213,7 @@ def test_score_shard_rejects_bad_arguments(L):
     assert shard(L, n=0) == EINVAL
     assert shard(L, n=17) == EINVAL
     assert shard(L, r=4) == EINVAL
-    assert shard(L, stats=2) == EINVAL
+    assert shard(L, stats=4) == EINVAL                  # unknown flag bit
     assert shard(L, temp=0.0) == EINVAL
     assert shard(L, temp=float("inf")) == EINVAL
     assert shard(L, parts=None) == EINVAL
@@ -247,7 +247,7 @@ def test_merge_shards_rejects_bad_arguments(L):
     m = L.lp_merge_shards
     assert m(P, P, -1, 1000, 0, P, None, None, None, None, None) == EINVAL
     assert m(P, P, 8, 0, 0, P, None, None, None, None, None) == EINVAL
-    assert m(P, P, 8, 1000, 2, P, None, None, None, None, None) == EINVAL
+    assert m(P, P, 8, 1000, 4, P, None, None, None, None, None) == EINVAL
     assert m(None, P, 8, 1000, 0, P, None, None, None, None, None) == EINVAL
     assert m(P, None, 8, 1000, 0, P, None, None, None, None, None) == EINVAL
     assert m(P, P, 8, 1000, 0, None, None, None, None, None, None) == EINVAL
@@ -286,3 +286,17 @@ def test_corr_seq_layout():
     from rollout_logprob_consistency_amd import _lib
     assert _lib.CORR_SEQ_DTYPE.itemsize == 40
     assert [_lib.CORR_SEQ_DTYPE.fields[f][1] for f in ("accepted", "stat", "sum_weight")] == [16, 24, 32]
+
+
+def test_score_ex_flags_and_workspace(L):
+    EINVAL = 1
+    for T, V in ((64, 4096), (8192, 151936)):
+        assert L.lp_score_ex_workspace_bytes(T, 4096, V, V, 0) == L.lp_score_workspace_bytes(T, 4096, V, V)
+        assert L.lp_score_ex_workspace_bytes(T, 4096, V, V, 1) == \
+            L.lp_score_stats_workspace_bytes(T, 4096, V, V)
+        assert L.lp_score_ex_workspace_bytes(T, 4096, V, V, 2) == L.lp_score_workspace_bytes(T, 4096, V, V)
+    assert L.lp_score_ex_workspace_bytes(8, 64, 10, 10, 4) == 0
+    ex = L.lp_score_ex
+    assert ex(P, 64, P, P, 8, 64, 100, 100, 1.0, 4, P, None, None, None, None, P, 1 << 20, None) == EINVAL
+    assert ex(P, 64, P, P, 8, 64, 100, 100, 1.0, 1, P, None, None, None, None, P, 1 << 20, None) == EINVAL
+    assert ex(P, 64, P, P, 8, 64, 100, 100, 0.0, 2, P, None, None, None, None, P, 1 << 20, None) == EINVAL
