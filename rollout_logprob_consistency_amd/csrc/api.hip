@@ -360,6 +360,8 @@ lp_status lp_compare_tails(const float* gen_A, const float* replay_B, const floa
   a.pos_sum = pos_abs_sum;
   a.pos_count = pos_count;
   a.workspace = workspace;
+  a.vec = ld % 4 == 0 && aligned(gen_A, 16) && aligned(replay_B, 16) && aligned(train_C, 16) &&
+          aligned(mask, 4);
   return lp::launch_tails(a, stream) == hipSuccess ? LP_OK : LP_EHIP;
 }
 

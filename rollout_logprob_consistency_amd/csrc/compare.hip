@@ -354,6 +354,12 @@ namespace {
 constexpr int kTailTargets = 9;     // 3 pairs x (p50, p95, p99)
 constexpr int kTailThreads = 256;
 constexpr int kTailChunks = 64;     // sequence chunks of the position profile
+// Copies of the histograms: workgroup b adds into copy b mod kHistCopies, so
+// no counter takes device-scope atomics from more than N / kHistCopies
+// workgroups (identical rows put every workgroup's count in one bin); the
+// select kernel sums the copies.
+constexpr int kHistCopies = 16;
+constexpr int kHistWords = kTailTargets * 256;
 
 struct TailSel {
   uint64_t prefix;   // bytes of the selected key found so far
@@ -367,9 +373,24 @@ struct TailPart {    // one (sequence, pair), from pass 0
   int32_t count;
 };
 
+// After two passes each target's remaining candidates (the keys under its
+// 16-bit prefix) are few for continuous data; pass 2 copies them into a list
+// and passes 3 .. 7 read only the lists. Targets of one pair under one prefix
+// share a list. A target whose list does not fit the key buffer keeps
+// reading the full batch.
+struct TailList {
+  int64_t off, len;  // region of keys[]
+  int32_t src;       // the target whose region it is; -1: no list
+};
+
 struct TailWs {
-  uint32_t* hist;    // [9][256]
+  uint32_t* hist;    // [kHistCopies][9][256]
   TailSel* sel;      // [9]
+  TailList* list;    // [9]
+  uint64_t* keys;    // [cap]
+  int64_t cap;
+  uint32_t* cnt;     // [9][N] candidates of sequence n in list t (pass 2)
+  uint32_t* koff;    // [9][N] their offset within the list
   int64_t* count;    // [3]
   TailPart* part;    // [N][3]
   double* pos_part;  // [nch][3][L]
@@ -379,12 +400,24 @@ struct TailWs {
 
 __host__ __device__ inline size_t tail_up(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Key buffer: one eighth of the positions (continuous scores leave a few
+// percent of a pair's tokens under each target's 16-bit prefix).
+inline int64_t tail_key_cap(int64_t N, int64_t L) {
+  const int64_t c = N * L / 8;
+  return c < 4096 ? 4096 : (c > 0x7FFFFFFF ? 0x7FFFFFFF : c);
+}
+
 TailWs tail_layout(void* base, int64_t N, int64_t L) {
   char* p = static_cast<char*>(base);
   TailWs w;
   size_t o = 0;
-  w.hist = reinterpret_cast<uint32_t*>(p + o); o = tail_up(o + kTailTargets * 256 * sizeof(uint32_t));
+  w.hist = reinterpret_cast<uint32_t*>(p + o); o = tail_up(o + kHistCopies * kHistWords * sizeof(uint32_t));
   w.sel = reinterpret_cast<TailSel*>(p + o);   o = tail_up(o + kTailTargets * sizeof(TailSel));
+  w.list = reinterpret_cast<TailList*>(p + o); o = tail_up(o + kTailTargets * sizeof(TailList));
+  w.cap = tail_key_cap(N, L);
+  w.keys = reinterpret_cast<uint64_t*>(p + o); o = tail_up(o + (size_t)w.cap * sizeof(uint64_t));
+  w.cnt = reinterpret_cast<uint32_t*>(p + o);  o = tail_up(o + (size_t)N * kTailTargets * sizeof(uint32_t));
+  w.koff = reinterpret_cast<uint32_t*>(p + o); o = tail_up(o + (size_t)N * kTailTargets * sizeof(uint32_t));
   w.count = reinterpret_cast<int64_t*>(p + o); o = tail_up(o + 3 * sizeof(int64_t));
   w.part = reinterpret_cast<TailPart*>(p + o); o = tail_up(o + (size_t)N * 3 * sizeof(TailPart));
   w.nch = (int)(N < kTailChunks ? (N < 1 ? 1 : N) : kTailChunks);
@@ -395,8 +428,12 @@ TailWs tail_layout(void* base, int64_t N, int64_t L) {
 
 size_t tail_bytes(int64_t N, int64_t L) {
   size_t o = 0;
-  o = tail_up(o + kTailTargets * 256 * sizeof(uint32_t));
+  o = tail_up(o + kHistCopies * kHistWords * sizeof(uint32_t));
   o = tail_up(o + kTailTargets * sizeof(TailSel));
+  o = tail_up(o + kTailTargets * sizeof(TailList));
+  o = tail_up(o + (size_t)tail_key_cap(N, L) * sizeof(uint64_t));
+  o = tail_up(o + (size_t)N * kTailTargets * sizeof(uint32_t));
+  o = tail_up(o + (size_t)N * kTailTargets * sizeof(uint32_t));
   o = tail_up(o + 3 * sizeof(int64_t));
   o = tail_up(o + (size_t)N * 3 * sizeof(TailPart));
   const int nch = (int)(N < kTailChunks ? (N < 1 ? 1 : N) : kTailChunks);
@@ -419,106 +456,176 @@ __device__ __forceinline__ int tail_src(const uint64_t* pre, const bool* want, i
 }
 
 __global__ __launch_bounds__(kTailThreads) void tails_init_kernel(TailWs w) {
-  for (int i = threadIdx.x; i < kTailTargets * 256; i += kTailThreads) w.hist[i] = 0u;
-  if (threadIdx.x < kTailTargets) w.sel[threadIdx.x] = TailSel{0ull, 0};
+  for (int i = threadIdx.x; i < kHistCopies * kHistWords; i += kTailThreads) w.hist[i] = 0u;
+  if (threadIdx.x < kTailTargets) {
+    w.sel[threadIdx.x] = TailSel{0ull, 0};
+    w.list[threadIdx.x] = TailList{0, 0, -1};
+  }
 }
 
 // One histogram pass; pass 0 also forms the per-sequence sums and maxima.
+// Scores and mask of the four positions i .. i + 3 of row n (inactive past
+// L); 16-byte loads on the vector path, element loads otherwise.
+template <bool kVec>
+__device__ __forceinline__ void tail_load4(const TailArgs& a, const float* const rows[3],
+                                           const uint8_t* M, int64_t i, float v[4][3],
+                                           bool act[4]) {
+  if (kVec && i + 4 <= a.L) {
+    const uint32_t mv = *reinterpret_cast<const uint32_t*>(M + i);
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      const float4 f = *reinterpret_cast<const float4*>(rows[s] + i);
+      v[0][s] = f.x;
+      v[1][s] = f.y;
+      v[2][s] = f.z;
+      v[3][s] = f.w;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) act[k] = ((mv >> (8 * k)) & 255u) != 0;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      act[k] = i + k < a.L && M[i + k] != 0;
+#pragma unroll
+      for (int s = 0; s < 3; ++s) v[k][s] = act[k] ? rows[s][i + k] : 0.f;
+    }
+  }
+}
+
+// Full pass over the batch. kMode 0: pass 0 (also the per-sequence
+// partials); 1: a later pass, for the targets without a list; 2: pass 2,
+// which also counts each sequence's candidates per list; 3: no histogram,
+// writes each sequence's candidates at the offsets the counts give (a
+// separate pass so that no append needs an atomic on a shared counter).
+template <bool kVec, int kMode>
 __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, TailWs w, int pass) {
-  __shared__ uint32_t h[kTailTargets * 256];
-  __shared__ TailPart red[3][kTailThreads];
+  __shared__ uint32_t h[kHistWords];
+  __shared__ TailPart red[kMode == 0 ? 3 : 1][kMode == 0 ? kTailThreads : 1];
+  __shared__ uint32_t n_found[kTailTargets];
   const int tid = threadIdx.x;
-  for (int i = tid; i < kTailTargets * 256; i += kTailThreads) h[i] = 0u;
   const int shift = 56 - 8 * pass;  // this pass's byte: key bits [shift + 7 : shift]
   // Targets of one pair whose prefixes agree see the same tokens: only the
   // first of them counts (tail_src() below names it for the select kernel).
   uint64_t pre[kTailTargets];
   bool want[kTailTargets];
+  bool src_list[kTailTargets];  // kMode 2, 3: t owns a list region
 #pragma unroll
   for (int t = 0; t < kTailTargets; ++t) {
     pre[t] = pass ? w.sel[t].prefix : 0ull;
-    want[t] = pass == 0 || w.sel[t].rank > 0;
+    want[t] = pass == 0 || (w.sel[t].rank > 0 && (pass <= 2 || w.list[t].src < 0));
   }
+  bool any_want = false;
 #pragma unroll
-  for (int t = 0; t < kTailTargets; ++t)
+  for (int t = 0; t < kTailTargets; ++t) {
     if (tail_src(pre, want, t) != t) want[t] = false;
+    any_want = any_want || want[t];
+    src_list[t] = kMode >= 2 && want[t] && w.list[t].src == t;
+  }
+  if (!any_want) return;  // uniform: every target has a list or is done
+  for (int i = tid; i < kHistWords; i += kTailThreads) h[i] = 0u;
+  if (kMode >= 2 && tid < kTailTargets) n_found[tid] = 0u;
   __syncthreads();
 
   const int64_t n = blockIdx.x;
-  const float* rows[3] = {a.A + n * a.ld, a.B + n * a.ld, a.C + n * a.ld};
+  const float* const rows[3] = {a.A + n * a.ld, a.B + n * a.ld, a.C + n * a.ld};
   const uint8_t* M = a.mask + n * a.ld;
   TailPart mine[3];
 #pragma unroll
   for (int p = 0; p < 3; ++p) mine[p] = TailPart{0.0, 0.0, 0ull, -1, 0};
   const int lane = tid & 63;
-  // Rounded up to whole waves so that every lane of a wave takes part in the
-  // ballots below; positions past L are inactive.
-  const int64_t Lw = (a.L + kTailThreads - 1) / kTailThreads * kTailThreads;
-  for (int64_t i = tid; i < Lw; i += kTailThreads) {
-    const bool act = i < a.L && M[i] != 0;
-    float v[3] = {0.f, 0.f, 0.f};
-    if (act) {
-      v[0] = rows[0][i];
-      v[1] = rows[1][i];
-      v[2] = rows[2][i];
-    }
-    double e[3] = {0.0, 0.0, 0.0};
-    if (pass == 0 && act) {
+  // Groups of four consecutive positions 4 tid + 1024 k; the trip count is
+  // the same for every thread, so every lane of a wave takes part in the
+  // ballots below (positions past L are inactive). Positions ascend within a
+  // thread.
+  constexpr int64_t kStep = 4 * kTailThreads;
+  const int64_t Lw = (a.L + kStep - 1) / kStep * kStep;
+  for (int64_t i0 = 4 * (int64_t)tid; i0 < Lw; i0 += kStep) {
+    float vv[4][3];
+    bool actv[4];
+    tail_load4<kVec>(a, rows, M, i0, vv, actv);
 #pragma unroll
-      for (int s = 0; s < 3; ++s)
-        if (__builtin_isfinite(v[s])) e[s] = exp_f64((double)v[s]);
-    }
+    for (int k = 0; k < 4; ++k) {
+      const int64_t i = i0 + k;
+      const bool act = actv[k];
+      const float* v = vv[k];
+      double e[3] = {0.0, 0.0, 0.0};
+      if (kMode == 0 && act) {
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      const float l = v[pair_left(p)], r = v[pair_right(p)];
-      const bool ok = act && __builtin_isfinite(l) && __builtin_isfinite(r);
-      const double d = fabs((double)l - (double)r);
-      const uint64_t key = (uint64_t)__double_as_longlong(d);
-      const uint32_t digit = (uint32_t)(key >> shift) & 255u;
-      // After the first passes few tokens share any target's prefix: one
-      // ballot per pair lets a wave with no such token skip the targets.
-      bool any = ok && pass == 0;
-      if (pass != 0) {
-#pragma unroll
-        for (int j = 0; j < 3; ++j)
-          any = any || (ok && want[3 * p + j] && (key >> (shift + 8)) == pre[3 * p + j]);
+        for (int s = 0; s < 3; ++s)
+          if (__builtin_isfinite(v[s])) e[s] = exp_f64((double)v[s]);
       }
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const int t = 3 * p + j;
-        if (!want[t] || __ballot(any) == 0) continue;  // uniform
-        const bool hit = ok && (pass == 0 || (key >> (shift + 8)) == pre[t]);
-        const uint64_t hb = __ballot(hit);
-        if (hb == 0) continue;
-        // One atomic for the wave when all its hits share a bin (the common
-        // case: runs of identical scores put every lane in bin 0).
-        const int first = __ffsll((long long)hb) - 1;
-        const uint32_t d0 = (uint32_t)__shfl((int)digit, first);
-        if (__ballot(hit && digit != d0) == 0) {
-          if (lane == first) atomicAdd(&h[t * 256 + d0], (uint32_t)__popcll(hb));
-        } else if (hit) {
-          atomicAdd(&h[t * 256 + digit], 1u);
+      for (int p = 0; p < 3; ++p) {
+        const float l = v[pair_left(p)], r = v[pair_right(p)];
+        const bool ok = act && __builtin_isfinite(l) && __builtin_isfinite(r);
+        const double d = fabs((double)l - (double)r);
+        const uint64_t key = (uint64_t)__double_as_longlong(d);
+        const uint32_t digit = (uint32_t)(key >> shift) & 255u;
+        // After the first passes few tokens share any target's prefix: one
+        // ballot per pair lets a wave with no such token skip the targets.
+        bool any = ok && kMode == 0;
+        if (kMode != 0) {
+#pragma unroll
+          for (int j = 0; j < 3; ++j)
+            any = any || (ok && want[3 * p + j] && (key >> (shift + 8)) == pre[3 * p + j]);
         }
-      }
-      if (!ok) continue;
-      if (pass == 0) {
-        TailPart& m = mine[p];
-        m.sum_abs += d;
-        m.sum_prob += fabs(e[pair_left(p)] - e[pair_right(p)]);
-        if (m.max_pos < 0 || key > m.max_key) {  // positions ascend: the first one stays
-          m.max_key = key;
-          m.max_pos = (int32_t)i;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          const int t = 3 * p + j;
+          if (!want[t] || __ballot(any) == 0) continue;  // uniform
+          const bool hit = ok && (kMode == 0 || (key >> (shift + 8)) == pre[t]);
+          const uint64_t hb = __ballot(hit);
+          if (hb == 0) continue;
+          // One atomic for the wave when all its hits share a bin (the common
+          // case: runs of identical scores put every lane in bin 0).
+          const int first = __ffsll((long long)hb) - 1;
+          if (kMode <= 2) {
+            const uint32_t d0 = (uint32_t)__shfl((int)digit, first);
+            if (__ballot(hit && digit != d0) == 0) {
+              if (lane == first) atomicAdd(&h[t * 256 + d0], (uint32_t)__popcll(hb));
+            } else if (hit) {
+              atomicAdd(&h[t * 256 + digit], 1u);
+            }
+          }
+          if (kMode >= 2 && src_list[t]) {
+            // Consecutive slots for the wave's hits.
+            uint32_t slot = 0u;
+            if (lane == first) slot = atomicAdd(&n_found[t], (uint32_t)__popcll(hb));
+            if (kMode == 3) {
+              slot = (uint32_t)__shfl((int)slot, first);
+              const uint32_t r = (uint32_t)__popcll(hb & ((1ull << lane) - 1ull));
+              const TailList L = w.list[t];
+              const int64_t e = (int64_t)w.koff[t * a.N + n] + slot + r;
+              if (hit && e < L.len) w.keys[L.off + e] = key;
+            }
+          }
         }
-        m.count += 1;
+        if (!ok) continue;
+        if (kMode == 0) {
+          TailPart& m = mine[p];
+          m.sum_abs += d;
+          m.sum_prob += fabs(e[pair_left(p)] - e[pair_right(p)]);
+          if (m.max_pos < 0 || key > m.max_key) {  // positions ascend: the first one stays
+            m.max_key = key;
+            m.max_pos = (int32_t)i;
+          }
+          m.count += 1;
+        }
       }
     }
   }
   __syncthreads();
-  for (int i = tid; i < kTailTargets * 256; i += kTailThreads)
-    if (h[i]) atomicAdd(&w.hist[i], h[i]);
-  if (pass != 0) return;
+  if (kMode == 3) return;
+  uint32_t* hc = w.hist + (blockIdx.x % kHistCopies) * kHistWords;
+  for (int i = tid; i < kHistWords; i += kTailThreads)
+    if (h[i]) atomicAdd(&hc[i], h[i]);
+  if (kMode == 2) {
+    if (tid < kTailTargets) w.cnt[tid * a.N + n] = src_list[tid] ? n_found[tid] : 0u;
+    return;
+  }
+  if (kMode != 0) return;
 
-  // Fixed tree over the threads (thread t holds the columns = t mod 256).
+  // Fixed tree over the threads; equal maxima keep the lower position.
 #pragma unroll
   for (int p = 0; p < 3; ++p) red[p][tid] = mine[p];
   __syncthreads();
@@ -544,11 +651,109 @@ __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, Ta
   if (tid < 3) w.part[n * 3 + tid] = red[tid][0];
 }
 
+// Offsets of each sequence's candidates within each list: an exclusive scan
+// of the pass-2 counts over the sequences, one workgroup per list. Thread j
+// takes the contiguous sequences [j per, (j + 1) per).
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void tails_scan_kernel(TailWs w, int64_t N) {
+  __shared__ uint32_t wsum[kScanThreads / 64];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t* cnt = w.cnt + t * N;
+  uint32_t* koff = w.koff + t * N;
+  const int64_t per = (N + kScanThreads - 1) / kScanThreads;
+  const int64_t lo = min(N, tid * per), hi = min(N, lo + per);
+  uint32_t tot = 0u;
+  for (int64_t n = lo; n < hi; ++n) tot += cnt[n];
+  uint32_t incl = tot;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_up((int)incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0u;
+  for (int v = 0; v < wave; ++v) before += wsum[v];
+  uint32_t run = before + incl - tot;
+  for (int64_t n = lo; n < hi; ++n) {
+    const uint32_t c = cnt[n];
+    koff[n] = run;
+    run += c;
+  }
+}
+
+// Passes 3 .. 7 for the targets with a list: the histogram of this pass's
+// byte over the list's keys under the target's prefix. A grid-stride walk
+// in whole waves (the ballots need every lane); integer counts, so the order
+// of the keys does not matter.
+constexpr int kListBlocks = 512;
+
+__global__ __launch_bounds__(kTailThreads) void tails_list_kernel(TailWs w, int pass) {
+  __shared__ uint32_t h[kHistWords];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int shift = 56 - 8 * pass;
+  uint64_t pre[kTailTargets];
+  bool want[kTailTargets];
+  int lst[kTailTargets];
+#pragma unroll
+  for (int t = 0; t < kTailTargets; ++t) {
+    pre[t] = w.sel[t].prefix;
+    lst[t] = w.list[t].src;
+    want[t] = w.sel[t].rank > 0 && lst[t] >= 0;
+  }
+  bool any_want = false;
+#pragma unroll
+  for (int t = 0; t < kTailTargets; ++t) {
+    if (tail_src(pre, want, t) != t) want[t] = false;
+    any_want = any_want || want[t];
+  }
+  if (!any_want) return;  // uniform
+  for (int i = tid; i < kHistWords; i += kTailThreads) h[i] = 0u;
+  __syncthreads();
+  const int64_t stride = (int64_t)gridDim.x * kTailThreads;
+  for (int u = 0; u < kTailTargets; ++u) {
+    bool used = false;
+#pragma unroll
+    for (int t = 0; t < kTailTargets; ++t) used = used || (want[t] && lst[t] == u);
+    if (!used) continue;  // uniform
+    const TailList L = w.list[u];
+    const int64_t wave0 = (int64_t)blockIdx.x * kTailThreads + (tid - lane);
+    for (int64_t e0 = wave0; e0 < L.len; e0 += stride) {
+      const int64_t e = e0 + lane;
+      const bool in = e < L.len;
+      const uint64_t key = in ? w.keys[L.off + e] : 0ull;
+      const uint32_t digit = (uint32_t)(key >> shift) & 255u;
+#pragma unroll
+      for (int t = 0; t < kTailTargets; ++t) {
+        if (!want[t] || lst[t] != u) continue;  // uniform
+        const bool hit = in && (key >> (shift + 8)) == pre[t];
+        const uint64_t hb = __ballot(hit);
+        if (hb == 0) continue;
+        const int first = __ffsll((long long)hb) - 1;
+        const uint32_t d0 = (uint32_t)__shfl((int)digit, first);
+        if (__ballot(hit && digit != d0) == 0) {
+          if (lane == first) atomicAdd(&h[t * 256 + d0], (uint32_t)__popcll(hb));
+        } else if (hit) {
+          atomicAdd(&h[t * 256 + digit], 1u);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* hc = w.hist + (blockIdx.x % kHistCopies) * kHistWords;
+  for (int i = tid; i < kHistWords; i += kTailThreads)
+    if (h[i]) atomicAdd(&hc[i], h[i]);
+}
+
 // Select the byte of each target's key; one wave per target, 4 bins a lane.
 // A target reads the histogram of tail_src() (the same prefix within its
 // pair); every histogram is read before any is cleared or any prefix moves.
 __global__ __launch_bounds__(64 * kTailTargets) void tails_select_kernel(TailWs w, int pass) {
+  __shared__ uint64_t s_pre[kTailTargets];
+  __shared__ int64_t s_rank[kTailTargets], s_len[kTailTargets];
   const int t = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (threadIdx.x < kTailTargets) s_rank[threadIdx.x] = 0;
   uint64_t pre[kTailTargets];
   bool want[kTailTargets];
 #pragma unroll
@@ -557,14 +762,19 @@ __global__ __launch_bounds__(64 * kTailTargets) void tails_select_kernel(TailWs 
     want[u] = pass == 0 || w.sel[u].rank > 0;
   }
   const int src = tail_src(pre, want, t);
-  const uint32_t* hist = w.hist + src * 256;
-  uint32_t c[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) c[k] = hist[4 * lane + k];
+  uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll 4
+  for (int cp = 0; cp < kHistCopies; ++cp) {
+    const uint4 q = *reinterpret_cast<const uint4*>(w.hist + cp * kHistWords + src * 256 + 4 * lane);
+    c[0] += q.x;
+    c[1] += q.y;
+    c[2] += q.z;
+    c[3] += q.w;
+  }
   const int64_t old_rank = pass ? w.sel[t].rank : 0;
   __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 4; ++k) w.hist[t * 256 + 4 * lane + k] = 0u;
+  for (int cp = 0; cp < kHistCopies; ++cp)
+    *reinterpret_cast<uint4*>(w.hist + cp * kHistWords + t * 256 + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
   const int64_t lsum = (int64_t)c[0] + c[1] + c[2] + c[3];
   int64_t incl = lsum;  // inclusive scan over lanes
 #pragma unroll
@@ -587,77 +797,105 @@ __global__ __launch_bounds__(64 * kTailTargets) void tails_select_kernel(TailWs 
     int64_t below = excl;
     int k = 0;
     while (below + (int64_t)c[k] < rank) below += c[k++];
-    w.sel[t].prefix = (pass ? (pre[t] << 8) : 0ull) | (uint64_t)(4 * lane + k);
-    w.sel[t].rank = rank - below;
+    const uint64_t np = (pass ? (pre[t] << 8) : 0ull) | (uint64_t)(4 * lane + k);
+    // A key whose top byte is 0 is the bit pattern of a double below 2^-1007:
+    // the difference of two fp32 scores is 0 or at least 2^-149 in
+    // magnitude, so every key in bin 0 of pass 0 is 0 and the selection is
+    // done (the prefix, 0, is the key).
+    const int64_t nr = (pass == 0 && 4 * lane + k == 0) ? 0 : rank - below;
+    w.sel[t].prefix = np;
+    w.sel[t].rank = nr;
+    s_pre[t] = np;
+    s_rank[t] = nr;
+    s_len[t] = (int64_t)c[k];
   } else if (rank == 0 && lane == 0) {
     w.sel[t].rank = 0;
+  }
+  if (pass != 1) return;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  // Lists for passes 3 .. 7, in target order while the key buffer lasts.
+  int64_t used = 0;
+  for (int u = 0; u < kTailTargets; ++u) {
+    TailList L{0, 0, -1};
+    if (s_rank[u] > 0) {
+      int src = u;
+      for (int v = 3 * (u / 3); v < u; ++v)
+        if (s_rank[v] > 0 && s_pre[v] == s_pre[u]) {
+          src = v;
+          break;
+        }
+      if (src != u) {
+        L = w.list[src];  // shares that target's list (or its lack of one)
+      } else if (used + s_len[u] <= w.cap) {
+        L = TailList{used, s_len[u], u};
+        used += s_len[u];
+      }
+    }
+    w.list[u] = L;
   }
 }
 
 // Batch results per pair: fixed chunks of sequences per thread, fixed tree.
-__global__ __launch_bounds__(kTailThreads) void tails_final_kernel(TailArgs a, TailWs w) {
-  __shared__ TailPart red[kTailThreads];
-  __shared__ int32_t red_seq[kTailThreads];
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(3 * kTailThreads) void tails_final_kernel(TailArgs a, TailWs w) {
+  __shared__ TailPart red[3][kTailThreads];
+  __shared__ int32_t red_seq[3][kTailThreads];
+  const int p = threadIdx.x / kTailThreads, tid = threadIdx.x % kTailThreads;
   const int64_t per = (a.N + kTailThreads - 1) / kTailThreads;
-  for (int p = 0; p < 3; ++p) {
-    TailPart x{0.0, 0.0, 0ull, -1, 0};
-    int32_t xs = -1;
-    const int64_t lo = tid * per, hi = min(a.N, lo + per);
-    for (int64_t n = lo; n < hi; ++n) {
-      const TailPart y = w.part[n * 3 + p];
-      x.sum_abs += y.sum_abs;
-      x.sum_prob += y.sum_prob;
-      x.count += y.count;
-      if (y.max_pos >= 0 && (x.max_pos < 0 || y.max_key > x.max_key)) {  // n ascends
-        x.max_key = y.max_key;
-        x.max_pos = y.max_pos;
-        xs = (int32_t)n;
-      }
+  TailPart x{0.0, 0.0, 0ull, -1, 0};
+  int32_t xs = -1;
+  const int64_t lo = tid * per, hi = min(a.N, lo + per);
+  for (int64_t n = lo; n < hi; ++n) {
+    const TailPart y = w.part[n * 3 + p];
+    x.sum_abs += y.sum_abs;
+    x.sum_prob += y.sum_prob;
+    x.count += y.count;
+    if (y.max_pos >= 0 && (x.max_pos < 0 || y.max_key > x.max_key)) {  // n ascends
+      x.max_key = y.max_key;
+      x.max_pos = y.max_pos;
+      xs = (int32_t)n;
     }
-    red[tid] = x;
-    red_seq[tid] = xs;
-    __syncthreads();
-    for (int stride = kTailThreads / 2; stride > 0; stride >>= 1) {
-      if (tid < stride) {
-        TailPart u = red[tid];
-        const TailPart v = red[tid + stride];
-        u.sum_abs += v.sum_abs;
-        u.sum_prob += v.sum_prob;
-        u.count += v.count;
-        // After the first steps a thread's sequences interleave with its
-        // partner's, so an equal key is decided by the sequence index.
-        const int32_t us = red_seq[tid], vs = red_seq[tid + stride];
-        if (v.max_pos >= 0 &&
-            (u.max_pos < 0 || v.max_key > u.max_key || (v.max_key == u.max_key && vs < us))) {
-          u.max_key = v.max_key;
-          u.max_pos = v.max_pos;
-          red_seq[tid] = vs;
-        }
-        red[tid] = u;
+  }
+  red[p][tid] = x;
+  red_seq[p][tid] = xs;
+  __syncthreads();
+  for (int stride = kTailThreads / 2; stride > 0; stride >>= 1) {
+    if (tid < stride) {
+      TailPart u = red[p][tid];
+      const TailPart v = red[p][tid + stride];
+      u.sum_abs += v.sum_abs;
+      u.sum_prob += v.sum_prob;
+      u.count += v.count;
+      // After the first steps a thread's sequences interleave with its
+      // partner's, so an equal key is decided by the sequence index.
+      const int32_t us = red_seq[p][tid], vs = red_seq[p][tid + stride];
+      if (v.max_pos >= 0 &&
+          (u.max_pos < 0 || v.max_key > u.max_key || (v.max_key == u.max_key && vs < us))) {
+        u.max_key = v.max_key;
+        u.max_pos = v.max_pos;
+        red_seq[p][tid] = vs;
       }
-      __syncthreads();
-    }
-    if (tid == 0) {
-      const TailPart& r = red[0];
-      lp_tail_stats o;
-      o.count = w.count[p];
-      const bool any = o.count > 0;
-      o.q50 = any ? __longlong_as_double((long long)w.sel[3 * p].prefix) : 0.0;
-      o.q95 = any ? __longlong_as_double((long long)w.sel[3 * p + 1].prefix) : 0.0;
-      o.q99 = any ? __longlong_as_double((long long)w.sel[3 * p + 2].prefix) : 0.0;
-      o.max_abs = any ? __longlong_as_double((long long)r.max_key) : 0.0;
-      o.max_seq = any ? red_seq[0] : -1;
-      o.max_pos = any ? r.max_pos : -1;
-      o.sum_abs = r.sum_abs;
-      o.sum_prob_abs = r.sum_prob;
-      a.out[p] = o;
+      red[p][tid] = u;
     }
     __syncthreads();
   }
+  if (tid == 0) {
+    const TailPart& r = red[p][0];
+    lp_tail_stats o;
+    o.count = w.count[p];
+    const bool any = o.count > 0;
+    o.q50 = any ? __longlong_as_double((long long)w.sel[3 * p].prefix) : 0.0;
+    o.q95 = any ? __longlong_as_double((long long)w.sel[3 * p + 1].prefix) : 0.0;
+    o.q99 = any ? __longlong_as_double((long long)w.sel[3 * p + 2].prefix) : 0.0;
+    o.max_abs = any ? __longlong_as_double((long long)r.max_key) : 0.0;
+    o.max_seq = any ? red_seq[p][0] : -1;
+    o.max_pos = any ? r.max_pos : -1;
+    o.sum_abs = r.sum_abs;
+    o.sum_prob_abs = r.sum_prob;
+    a.out[p] = o;
+  }
 }
 
-// Position profile, stage 1: chunk c of the sequences, column i.
 __global__ __launch_bounds__(kTailThreads) void tails_pos_kernel(TailArgs a, TailWs w) {
   const int64_t i = (int64_t)blockIdx.x * kTailThreads + threadIdx.x;
   if (i >= a.L) return;
@@ -666,16 +904,31 @@ __global__ __launch_bounds__(kTailThreads) void tails_pos_kernel(TailArgs a, Tai
   const int64_t lo = c * per, hi = min(a.N, lo + per);
   double s[3] = {0.0, 0.0, 0.0};
   int32_t k[3] = {0, 0, 0};
-  for (int64_t n = lo; n < hi; ++n) {
-    const int64_t o = n * a.ld + i;
-    if (a.mask[o] == 0) continue;
-    const float v[3] = {a.A[o], a.B[o], a.C[o]};
+  // Eight sequences' loads are issued together (all of them, masked or not);
+  // the sums still take the sequences in ascending order.
+  constexpr int kB = 8;
+  for (int64_t n0 = lo; n0 < hi; n0 += kB) {
+    float v[kB][3];
+    bool act[kB];
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      const float l = v[pair_left(p)], r = v[pair_right(p)];
-      if (!__builtin_isfinite(l) || !__builtin_isfinite(r)) continue;
-      s[p] += fabs((double)l - (double)r);
-      k[p] += 1;
+    for (int b = 0; b < kB; ++b) {
+      const bool in = n0 + b < hi;
+      const int64_t o = (in ? n0 + b : lo) * a.ld + i;
+      act[b] = in && a.mask[o] != 0;
+      v[b][0] = a.A[o];
+      v[b][1] = a.B[o];
+      v[b][2] = a.C[o];
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      if (!act[b]) continue;
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const float l = v[b][pair_left(p)], r = v[b][pair_right(p)];
+        if (!__builtin_isfinite(l) || !__builtin_isfinite(r)) continue;
+        s[p] += fabs((double)l - (double)r);
+        k[p] += 1;
+      }
     }
   }
 #pragma unroll
@@ -691,6 +944,7 @@ __global__ __launch_bounds__(kTailThreads) void tails_pos_fold_kernel(TailArgs a
   if (idx >= 3 * a.L) return;
   double s = 0.0;
   int32_t k = 0;
+#pragma unroll 8
   for (int c = 0; c < w.nch; ++c) {
     s += w.pos_part[(size_t)c * 3 * a.L + idx];
     k += w.pos_cpart[(size_t)c * 3 * a.L + idx];
@@ -703,14 +957,35 @@ __global__ __launch_bounds__(kTailThreads) void tails_pos_fold_kernel(TailArgs a
 
 size_t tails_workspace_bytes(int64_t N, int64_t L) { return tail_bytes(N, L); }
 
+template <int kMode>
+static void launch_hist(const TailArgs& a, const TailWs& w, int pass, hipStream_t stream) {
+  if (a.vec)
+    hipLaunchKernelGGL((tails_hist_kernel<true, kMode>), dim3((unsigned)a.N), dim3(kTailThreads), 0,
+                       stream, a, w, pass);
+  else
+    hipLaunchKernelGGL((tails_hist_kernel<false, kMode>), dim3((unsigned)a.N), dim3(kTailThreads),
+                       0, stream, a, w, pass);
+}
+
 hipError_t launch_tails(const TailArgs& a, hipStream_t stream) {
   const TailWs w = tail_layout(a.workspace, a.N, a.L);
   hipLaunchKernelGGL(tails_init_kernel, dim3(1), dim3(kTailThreads), 0, stream, w);
   if (a.N > 0) {
     // Every pass runs, also with L == 0 (pass 0 then writes empty partials).
     for (int pass = 0; pass < 8; ++pass) {
-      hipLaunchKernelGGL(tails_hist_kernel, dim3((unsigned)a.N), dim3(kTailThreads), 0, stream,
-                         a, w, pass);
+      if (pass == 0) {
+        launch_hist<0>(a, w, pass, stream);
+      } else if (pass == 2) {
+        launch_hist<2>(a, w, pass, stream);
+        hipLaunchKernelGGL(tails_scan_kernel, dim3(kTailTargets), dim3(kScanThreads), 0, stream, w,
+                           a.N);
+        launch_hist<3>(a, w, pass, stream);
+      } else {
+        launch_hist<1>(a, w, pass, stream);  // passes >= 3: targets without a list
+      }
+      if (pass >= 3)
+        hipLaunchKernelGGL(tails_list_kernel, dim3(kListBlocks), dim3(kTailThreads), 0, stream, w,
+                           pass);
       hipLaunchKernelGGL(tails_select_kernel, dim3(1), dim3(64 * kTailTargets), 0, stream, w,
                          pass);
     }
@@ -718,7 +993,7 @@ hipError_t launch_tails(const TailArgs& a, hipStream_t stream) {
     // No sequence: empty histograms give count 0 and no rank to select.
     hipLaunchKernelGGL(tails_select_kernel, dim3(1), dim3(64 * kTailTargets), 0, stream, w, 0);
   }
-  hipLaunchKernelGGL(tails_final_kernel, dim3(1), dim3(kTailThreads), 0, stream, a, w);
+  hipLaunchKernelGGL(tails_final_kernel, dim3(1), dim3(3 * kTailThreads), 0, stream, a, w);
   if (a.pos_sum && a.L > 0) {
     // Stage 1 also runs with N == 0, writing zero partials for the fold.
     hipLaunchKernelGGL(tails_pos_kernel,

@@ -115,6 +115,7 @@ struct TailArgs {
   double* pos_sum;        // [3][L] or null
   int32_t* pos_count;     // [3][L] or null (null iff pos_sum is)
   void* workspace;
+  bool vec;               // rows 16-byte aligned (A, B, C), mask 4-byte aligned, ld % 4 == 0
 };
 
 size_t tails_workspace_bytes(int64_t N, int64_t L);

@@ -41,8 +41,13 @@ def test_identical_scores(record):
     assert got["AB"]["max_abs"] == 0.0 and got["AB"]["q99"] == 0.0
 
 
-@pytest.mark.parametrize("fault", ["noise", "shift", "case1", "case2"])
+@pytest.mark.parametrize("fault", ["noise", "shift", "case1", "case2", "case1_noise"])
 def test_faults(record, fault):
+    # After two passes a target either reads a short list of candidate keys
+    # (continuous differences: noise) or, when its candidates do not fit the
+    # key buffer (an offset puts every |delta| under one 16-bit prefix),
+    # keeps reading the batch; identical pairs stop after one pass. The
+    # faults cover each path and their mix (case1_noise: AB full, BC lists).
     c = record
     A, C = c.A, c.C
     if fault == "noise":
@@ -51,6 +56,9 @@ def test_faults(record, fault):
         C = synth.shift_scores(c.C, seq=3, k=1, fill=-5.0)
     elif fault == "case1":
         A = synth.offset_scores(c.A, c.mask, 0.10, first_pos=1)
+    elif fault == "case1_noise":
+        A = synth.offset_scores(c.A, c.mask, 0.10, first_pos=1)
+        C = synth.noise_scores(c.C, c.mask, 1e-3, seed=22)
     else:
         C = synth.offset_scores(c.C, c.mask, 0.10)
     got, _, _ = run(A, c.B, C, c.mask)
@@ -102,3 +110,20 @@ def test_sweep_size_and_repeatability():
     for p in lp.PAIRS:
         assert got[p].tobytes() == again[p].tobytes()
     assert ps.tobytes() == ps2.tobytes() and pc.tobytes() == pc2.tobytes()
+
+
+def test_vector_and_scalar_paths_agree(record):
+    # Rows with a stride that is not a multiple of 4 take element loads over
+    # the same positions in the same order: bitwise equal results.
+    import torch
+    C = synth.noise_scores(record.C, record.mask, 1e-3, seed=31)
+    N, L = record.N, record.L
+    vec = lp.compare_tails(dev(record.A), dev(record.B), dev(C), dev(record.mask), positions=True)
+    for pad in (1, 3):
+        big = [np.zeros((N, L + pad), a.dtype) for a in (record.A, record.B, C, record.mask)]
+        for b, a in zip(big, (record.A, record.B, C, record.mask)):
+            b[:, :L] = a
+        sca = lp.compare_tails(*[dev(b)[:, :L] for b in big], positions=True)
+        for p in lp.PAIRS:
+            assert vec[0][p].tobytes() == sca[0][p].tobytes(), p
+        assert np.array_equal(vec[1], sca[1]) and np.array_equal(vec[2], sca[2])
