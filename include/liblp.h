@@ -303,8 +303,8 @@ lp_status lp_compare_tails(const float* gen_A, const float* replay_B,
  * cross-rank LSE merge, fixed rank reduction order).
  *
  * lp_score merges its per-tile partials in LP_MERGE_SEGMENTS fixed segments
- * of the 256-row vocabulary tiles (segment g holds tiles [g P, (g + 1) P),
- * P = ceil(ceil(V_true / 256) / 16)), each folded in ascending tile order,
+ * of the 352-row vocabulary tiles (segment g holds tiles [g P, (g + 1) P),
+ * P = ceil(ceil(V_true / 352) / 16)), each folded in ascending tile order,
  * then folds the segments in order. A shard owns whole segments:
  * lp_vocab_shard_range gives rank r of n (1 <= n <= 16) the segments
  * [16 r / n, 16 (r + 1) / n) and the vocabulary rows [row_begin, row_end)
@@ -336,6 +336,7 @@ lp_status lp_compare_tails(const float* gen_A, const float* replay_B,
  * LP_EUNSUPPORTED as for lp_score. T == 0 does nothing.
  * ------------------------------------------------------------------------ */
 #define LP_MERGE_SEGMENTS 16
+#define LP_VOCAB_TILE_ROWS 352  /* vocabulary rows per tile (the chunking unit) */
 
 typedef struct {
   int32_t seg_lo;     /* first merge segment of the shard */

@@ -33,6 +33,7 @@ CORR_SEQ_DTYPE = np.dtype([
 assert CORR_SEQ_DTYPE.itemsize == 40
 
 MERGE_SEGMENTS = 16  # LP_MERGE_SEGMENTS
+VOCAB_TILE_ROWS = 352  # LP_VOCAB_TILE_ROWS
 
 
 class VocabShard(ctypes.Structure):

@@ -4,7 +4,9 @@
 
 Compiles every .hip file under csrc/ into one shared library next to this
 file, with hipcc for gfx950. Packed-fp32 instructions are disabled for all
-device code.
+device code. The device assembly of score.hip is then checked for wait-state
+hazards around its inline-assembly MFMAs (isa_check.py); a violation fails
+the build.
 """
 
 from __future__ import annotations
@@ -66,8 +68,26 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    check_score_isa(objdir, extra, verbose)
     os.replace(tmp, LIB)
     return LIB
+
+
+def check_score_isa(objdir: str, extra: list[str] | None = None, verbose: bool = False) -> None:
+    """Compile score.hip to device assembly with the same flags and run the
+    inline-assembly MFMA hazard check on it."""
+    from rollout_logprob_consistency_amd import isa_check
+    src = os.path.join(CSRC, "score.hip")
+    out = os.path.join(objdir, "score.device.s")
+    cmd = [hipcc(), *compile_flags(), *(extra or []), "--cuda-device-only", "-S", src, "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stdout}\n{r.stderr}")
+    problems = isa_check.check_asm(open(out).read())
+    if problems:
+        raise RuntimeError("inline-assembly MFMA hazard check failed:\n" + "\n".join(problems[:20]))
 
 
 if __name__ == "__main__":

@@ -12,7 +12,7 @@ namespace lp {
 // Fixed tile geometry of the selected-token logprob. These never depend on
 // the number of rows: every row is reduced over H and over the vocabulary in
 // the same order whatever batch it is scored in.
-constexpr int kTileV = 256;   // vocabulary rows per workgroup tile
+constexpr int kTileV = 352;   // vocabulary rows per workgroup tile
 constexpr int kTileT = 256;   // token rows per workgroup tile
 constexpr int kTileK = 64;    // hidden elements per LDS stage
 // Batches of at most this many rows take the streaming kernel (one wave per
@@ -57,6 +57,7 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t stream);
 // segments.
 constexpr int kMergeSegs = 16;
 static_assert(kMergeSegs == LP_MERGE_SEGMENTS, "the segment count is part of the C ABI");
+static_assert(kTileV == LP_VOCAB_TILE_ROWS, "the tile height is part of the C ABI");
 int merge_segment_tiles(int64_t V_true);  // tiles per segment
 
 struct ShardArgs {

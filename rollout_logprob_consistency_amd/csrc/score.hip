@@ -11,22 +11,28 @@
 // report and the VeXact note describe batch-invariant GEMMs on other hardware;
 // only the invariant is kept here, the kernel is designed for CDNA4:
 //
-//  * One workgroup = 4 waves computes a 256 (vocab) x 256 (token) tile of
+//  * One workgroup = 4 waves computes a 352 (vocab) x 256 (token) tile of
 //    Z^T = W . X^T with v_mfma_f32_16x16x32_bf16, fp32 accumulation, the whole
 //    hidden dimension in ascending 32-wide MFMA steps (no split-K). Each wave
-//    owns 128 x 128 outputs = 8 x 8 MFMA tiles (256 accumulator registers).
-//    Tokens are the MFMA "N" dimension: a lane holds one token column and 32
-//    vocabulary rows, so the vocabulary reduction is mostly inside a lane.
-//    The 16x16x32 shape moves half as many accumulator bytes per flop as
-//    32x32x16; at the same work the chip holds a higher clock with it.
+//    owns 176 x 128 outputs = 11 x 8 MFMA tiles: 256 accumulators in AGPRs
+//    and 96 in VGPRs (the largest wave tile the register file holds next to
+//    its fragments). Tokens are the MFMA "N" dimension: a lane holds one
+//    token column and 44 vocabulary rows, so the vocabulary reduction is
+//    mostly inside a lane. The 16x16x32 shape moves half as many accumulator
+//    bytes per flop as 32x32x16.
+//  * The chip runs this product at its power limit, so the data moved per
+//    flop sets the clock: the 176 x 128 wave tile reads 14 % fewer LDS bytes
+//    per flop than 128 x 128, and the 352 x 256 workgroup tile copies 14 %
+//    fewer bytes from L2 into LDS.
 //  * Operand stages go from HBM/L2 straight into LDS (buffer_load ... lds, no
-//    VGPR round trip) through a ring of 5 units of 32 KiB (one operand's 64-wide
-//    K stage each); the 16-byte chunks of each 128-byte row are XOR-permuted so
-//    the ds_read_b128 fragment reads do not collide on LDS banks. Copies,
-//    fragment reads and MFMAs are issued in a fixed interleave with one
-//    barrier per K stage.
+//    VGPR round trip) through two alternating 76 KiB stage buffers (W and X
+//    rows of one 64-wide K slice); the 16-byte chunks of each 128-byte row
+//    are XOR-permuted so the ds_read_b128 fragment reads do not collide on
+//    LDS banks. One barrier per stage; MFMAs of the previous stage's second
+//    half are carried across it, and the next stage's copies are spread over
+//    the whole stage.
 //  * Epilogue: scale by log2(e)/temperature, mask rows >= V_true to -inf,
-//    per-token max and sum of exp2 over the lane's 32 values, the lanes
+//    per-token max and sum of exp2 over the lane's 44 values, the lanes
 //    (l, l^16, l^32, l^48) and the two vocabulary waves, in a fixed order;
 //    write one (max, sum) partial per (vocabulary tile, token); the single
 //    lane that holds the target logit writes it. Logits never reach memory.
@@ -36,7 +42,9 @@
 // Batch invariance: the arithmetic applied to a (token, vocabulary row) pair
 // depends only on the tile shape, H and the vocabulary tile index, never on
 // T, on the token's slot in its tile, on the other tokens or on which CU runs
-// the tile. Rows past T are clamped copies whose results are discarded.
+// the tile. Rows past T or V_rows are never read from memory (the buffer
+// range check; the streaming kernel clamps them) and their results are
+// discarded.
 #include <math.h>
 
 #include "lp_internal.h"
@@ -48,18 +56,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kWaveV = 128;                  // vocab rows per wave
+constexpr int kWaveV = 176;                  // vocab rows per wave
 constexpr int kWaveT = 128;                  // token columns per wave
-constexpr int kSubV = kWaveV / 16;           // 16-row MFMA tiles along vocab (8)
+constexpr int kSubV = kWaveV / 16;           // 16-row MFMA tiles along vocab (11)
 constexpr int kSubT = kWaveT / 16;           // 16-column MFMA tiles along tokens (8)
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
 // lgkmcnt [11:8]); only vmcnt is constrained.
 constexpr int kWaitVm0 = 0x0F70;             // vmcnt(0)
-constexpr int kWaitVm8 = 0x0F78;             // vmcnt(8)
 constexpr int kGroupV = 4;                   // vocab tiles per scheduling group
 constexpr float kLn2 = 0.693147180559945309f;
 
-static_assert(kTileV == kTileT, "W and X stages share one layout");
 static_assert(kTileV == 2 * kWaveV && kTileT == 2 * kWaveT, "2 x 2 waves");
 static_assert(kTileK == 64, "128-byte LDS rows");
 
@@ -130,7 +136,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // 16x16 output layout: lane l holds column (l & 15) and, in register r, row
 // 4 (l >> 4) + r; the four lanes l & 15 + 16 g (g = 0..3) share a token.
 
-// Per-token max and sum of exp2 over the wave's 128 rows (lanes l, l^16,
+// Per-token max and sum of exp2 over the wave's kWaveV rows (lanes l, l^16,
 // l^32, l^48). The scale log2(e)/T is positive, so the max of the scaled
 // logits is the scaled max; the scale is folded into the exp2 argument with
 // one FMA. The butterfly adds the same two values in both lanes of each step,
@@ -219,7 +225,7 @@ __device__ __forceinline__ void gather_target(Get v, const ScoreArgs& a, int t, 
   }
 }
 
-// Merge of the two 128-row halves of a vocabulary tile, lower half first
+// Merge of the two kWaveV-row halves of a vocabulary tile, lower half first
 // (m0 is finite: row v0 < V_true lies in the lower half).
 __device__ __forceinline__ void merge_halves(float m0, float s0, float m1, float s1, float& M,
                                              float& S) {
@@ -269,21 +275,45 @@ __device__ __forceinline__ void copy_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t l
                : "memory");
 }
 
-// Ring geometry of the 256 x 256 kernel: a unit is one operand's K stage
-// (256 rows x 64 hidden elements = 128-byte rows, 32 KiB); unit 2k is the W
-// stage k, unit 2k + 1 the X stage k; unit u lives in slot u mod kSlots.
-constexpr int kSlots = 5;
-constexpr int kRowB = kTileK * 2;            // 128 B
-constexpr int kSlotB = kTileV * kRowB;       // 32 KiB
-constexpr int kCopiesU = kSlotB / 1024 / 4;  // 1-KiB copies per wave per unit
-static_assert(kCopiesU == 8, "copy schedule assumes 8 copies per wave per unit");
-static_assert(kSlots * kSlotB <= 160 * 1024, "LDS");
+// Stage geometry of the tile kernel: a stage is one 64-wide K slice of both
+// operands, the W unit (kTileV rows of 128 bytes) followed by the X unit
+// (kTileT rows); two stage buffers alternate. Wave w issues copy j of a unit
+// for rows 8 (4 j + w) .. + 7.
+constexpr int kRowB = kTileK * 2;               // 128 B
+constexpr int kWUnitB = kTileV * kRowB;         // 44 KiB
+constexpr int kXUnitB = kTileT * kRowB;         // 32 KiB
+constexpr int kStageB = kWUnitB + kXUnitB;      // 76 KiB
+constexpr int kCopiesW = kWUnitB / 1024 / 4;    // 1-KiB copies per wave per W unit (11)
+constexpr int kCopiesX = kXUnitB / 1024 / 4;    // per X unit (8)
+constexpr int kCopies = kCopiesW + kCopiesX;    // per wave per stage (19)
+constexpr int kSubVA = 8;                       // vocab MFMA tiles with AGPR accumulators
+constexpr int kSubVV = kSubV - kSubVA;          // ... with VGPR accumulators (3)
+static_assert(kWUnitB % 4096 == 0 && kXUnitB % 4096 == 0, "whole copies per wave");
+static_assert(2 * kStageB <= 160 * 1024, "LDS");
+constexpr int kCopyEvery = 6;                   // MFMAs per copy across a phase
+static_assert(kCopyEvery * kCopies < 2 * 8 * kSubV, "copies fit in a phase");
+static_assert(kSubT == 8 && kSubVA == 8 && kSubVV <= kSubVA, "read schedule");
+
+// The same MFMA as mma() with the accumulator in VGPRs (the AGPR file holds
+// only kSubVA x kSubT accumulators). Written as assembly, so the compiler
+// cannot see the MFMA's hazards; none arise: the first MFMA of an
+// accumulator takes the inline constant 0 as C (mma_v0), so no VALU write
+// ever precedes an MFMA read of that register; its A and B fragments are
+// written only by LDS reads, which the compiler orders with lgkmcnt waits,
+// and are overwritten only a whole step after their last MFMA; VALU code
+// reads the accumulators only after the K loop, behind explicit wait states.
+__device__ __forceinline__ void mma_v(f32x4& c, const bf16x8& w, const bf16x8& x) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(w), "v"(x));
+}
+__device__ __forceinline__ void mma_v0(f32x4& c, const bf16x8& w, const bf16x8& x) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(c) : "v"(w), "v"(x));
+}
 
 template <bool kStats, bool kBf16>
 __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
-  // Ring of kSlots units; the 16-byte chunks of row r are XOR-permuted by
-  // swz(). After the K loop the first 2 KiB hold the cross-wave reduction.
-  __shared__ __attribute__((aligned(1024))) char ring[kSlots * kSlotB];
+  // Two stage buffers; the 16-byte chunks of row r are XOR-permuted by
+  // swz(). After the K loop the first bytes hold the cross-wave reduction.
+  __shared__ __attribute__((aligned(1024))) char ring[2 * kStageB];
 
   int vt, tt;
   tile_of(blockIdx.x, a.n_vt, a.n_tt, kGroupV, vt, tt);
@@ -297,145 +327,167 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   const int wm = wave & 1, wn = wave >> 1;
   const int lcol = lane & 15, lg = lane >> 4;
 
-  // ---- Copies. Per unit, wave w issues 8 copies; copy j fills rows 8 q ..
-  // 8 q + 7 (q = 4 j + w), lane i writing physical chunk (i & 7) of row
-  // 8 q + (i >> 3), i.e. logical chunk swz(row, i & 7). Rows past the matrix
-  // are clamped (their results are discarded). The resources start at the
-  // tile's first row; the K offset of a stage is the uniform soffset.
+  // Accumulators: vocab MFMA tiles 0..7 in AGPRs, 8..10 in VGPRs. The
+  // first MFMA of each starts from C = 0.
+  f32x4 acc[kSubVA][kSubT], accv[kSubVV][kSubT];
+
+  // ---- Copies. Copy j of a unit: lane i moves the 16 bytes of physical chunk
+  // (i & 7) of row 8 (4 j + w) + (i >> 3), i.e. logical chunk swz(row, i & 7);
+  // row & 7 = (i >> 3) & 7 for every j. The resources start at the tile's
+  // first row and end at the matrix's last byte, so rows past the matrix read
+  // zeros (their results are discarded); the K offset of a stage is the
+  // uniform soffset, which never leaves the row.
   const char* wtile = reinterpret_cast<const char*>(a.w) + (size_t)v0 * a.H * 2;
   const char* xtile = reinterpret_cast<const char*>(a.x) + (size_t)t0 * a.ldh * 2;
   const __amdgpu_buffer_rsrc_t wres =
       make_rsrc(wtile, span_bytes((uint64_t)(a.V_rows - v0) * (uint64_t)a.H * 2));
   const __amdgpu_buffer_rsrc_t xres = make_rsrc(
       xtile, span_bytes((uint64_t)(a.T - t0 - 1) * (uint64_t)a.ldh * 2 + (uint64_t)a.H * 2));
-  uint32_t offW[kCopiesU], offX[kCopiesU];
-#pragma unroll
-  for (int j = 0; j < kCopiesU; ++j) {
-    const int row = 8 * (4 * j + wave) + (lane >> 3);
-    const int c = swz(row, lane & 7);  // the permutation is an involution
-    offW[j] = (uint32_t)min(row, a.V_rows - 1 - v0) * (uint32_t)(a.H * 2) + c * 16;
-    offX[j] = (uint32_t)min(row, a.T - 1 - t0) * (uint32_t)(a.ldh * 2) + c * 16;
-  }
+  const uint32_t H2 = (uint32_t)a.H * 2, X2 = (uint32_t)a.ldh * 2;
+  const uint32_t lrow = (uint32_t)(8 * wave + (lane >> 3));
+  const uint32_t cb = (uint32_t)(swz(lane >> 3, lane & 7) * 16);
+  const uint32_t offW0 = lrow * H2 + cb, offX0 = lrow * X2 + cb;
+  const uint32_t stepW = 32 * H2, stepX = 32 * X2;  // 32 rows per copy index
   const uint32_t lds0 =
       __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_char*)ring));
   const int nk = a.H / kTileK;
-  // Copy j (0..7) of the W (x_ = false) or X unit of stage k into slot sl. A
-  // stage past the end re-copies the last one into a slot that nothing reads
-  // before it is refilled.
-#define COPY(x_, j_, k_, sl_)                                                                   \
-  copy_lds((x_) ? xres : wres, lds0 + (uint32_t)(sl_) * kSlotB + (4 * (j_) + wave) * 1024,      \
-           (x_) ? offX[(j_)] : offW[(j_)], (uint32_t)min((k_), nk - 1) * kRowB)
+  // Copy c (0..18) of stage k into buffer st: c < 11 copies W rows, else X
+  // rows. A stage past the end re-copies the last one (same bytes, into the
+  // buffer that holds it or into one nothing reads before it is refilled).
+// The per-copy row offset is added in place (an opaque add the compiler
+// cannot hoist into 19 loop-invariant registers).
+#define COPY(c_, k_, st_)                                                                      \
+  do {                                                                                         \
+    const uint32_t soff_ = (uint32_t)min((k_), nk - 1) * kRowB;                                 \
+    const bool w_ = (c_) < kCopiesW;                                                           \
+    const uint32_t cc_ = w_ ? (uint32_t)(c_) : (uint32_t)((c_) - kCopiesW);                     \
+    uint32_t voff_;                                                                            \
+    asm volatile("v_add_u32 %0, %1, %2" : "=v"(voff_) : "s"(cc_ * (w_ ? stepW : stepX)),         \
+                 "v"(w_ ? offW0 : offX0));                                                     \
+    copy_lds(w_ ? wres : xres,                                                                 \
+             lds0 + (uint32_t)(st_) * kStageB + (w_ ? 0u : (uint32_t)kWUnitB) + (4 * cc_ + wave) * 1024, \
+             voff_, soff_);                                                                    \
+  } while (0)
+
+  // Stage 0 into buffer 0 before the first phase.
+#define COPY_ALL_PROLOGUE()                                                    \
+  do {                                                                         \
+    _Pragma("unroll") for (int c = 0; c < kCopies; ++c) COPY(c, 0, 0);         \
+  } while (0)
 
   // ---- Fragment reads. Fragment (tile u, half h) of an operand: lane l reads
   // row base + 16 u + (l & 15), logical chunk 4 h + (l >> 4) (hidden elements
   // 32 h + 8 (l >> 4) .. + 7 of the stage). swz() depends on the row only
-  // through l & 7, so one address per (operand, h) plus an immediate per tile
-  // suffice.
+  // through l & 7, so one address per (operand, half, buffer) plus an
+  // immediate per tile suffice.
   uint32_t rdA[2], rdB[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int pc = swz(lcol, 4 * h + lg);
     rdA[h] = (uint32_t)((wm * kWaveV + lcol) * kRowB + pc * 16);
-    rdB[h] = (uint32_t)((wn * kWaveT + lcol) * kRowB + pc * 16);
+    rdB[h] = (uint32_t)(kWUnitB + (wn * kWaveT + lcol) * kRowB + pc * 16);
   }
-  // Fragment n (0..15) of half h: n == 0 and 9..15 are W tiles 0 and 1..7,
-  // n = 1..8 are X tiles 0..7 -- the order in which the MFMAs of a step first
-  // use them (W tile 0 with every X tile, then W tiles 1..7).
-#define READ(fa_, fb_, n_, h_)                                                                 \
-  do {                                                                                         \
-    if ((n_) >= 1 && (n_) <= 8)                                                                \
-      fb_[(n_) - 1] = *reinterpret_cast<const bf16x8*>(ring + bB + rdB[(h_)] + ((n_) - 1) * 2048); \
-    else {                                                                                     \
-      const int ii_ = (n_) == 0 ? 0 : (n_) - 8;                                                \
-      fa_[ii_] = *reinterpret_cast<const bf16x8*>(ring + bA + rdA[(h_)] + ii_ * 2048);         \
-    }                                                                                          \
-  } while (0)
-#define MFMA(fa_, fb_, u_) \
-  acc[(u_) >> 3][(u_) & 7] = mma(fa_[(u_) >> 3], fb_[(u_) & 7], acc[(u_) >> 3][(u_) & 7])
+  // Buffer st (0 or 1, possibly a run-time value) starts at st * kStageB.
+#define RD_A(u_, h_, st_) \
+  *reinterpret_cast<const bf16x8*>(ring + (rdA[(h_)] + (uint32_t)(st_) * kStageB) + (u_) * 2048)
+#define RD_B(u_, h_, st_) \
+  *reinterpret_cast<const bf16x8*>(ring + (rdB[(h_)] + (uint32_t)(st_) * kStageB) + (u_) * 2048)
 #define FENCE() __builtin_amdgcn_sched_barrier(0)
 
-  f32x4 acc[kSubV][kSubT];
-#pragma unroll
-  for (int i = 0; i < kSubV; ++i)
+  // W fragments of MFMA groups 0..7 are single-buffered: fa[g] is reloaded
+  // with the next step's fragment right after group g has used it. Those of
+  // groups 8..10 (the VGPR-accumulator groups, last in a step) and the X
+  // fragments alternate between two buffers, so every read of a step is
+  // issued at least 24 MFMAs before the step ends.
+  bf16x8 fa[kSubVA], fx0[kSubVV], fx1[kSubVV], fb0[kSubT], fb1[kSubT];
+
+  // One step = kSubV groups of 8 MFMAs (W tile g with X tiles 0..7), 32
+  // hidden elements, on (fa, mx_, mb_) (skipped with do_mma_ false); reads
+  // of the next step's fragments from (half rh_, buffer rs_): X tile i into
+  // rb_ after the 4th MFMA of group i, W tile g < 8 into fa[g] after group
+  // g, W tile 8 + i into rx_ after the 6th MFMA of group i. A phase (two
+  // steps, p0_ = 0 or 8 kSubV) issues copy c of stage ck_ into buffer cs_
+  // after its MFMA slot kCopyEvery c + 1. The order is fixed instruction by
+  // instruction.
+#define STEP(do_mma_, z_, do_rd_, mx_, mb_, rx_, rb_, rh_, rs_, p0_, ck_, cs_)       \
+  do {                                                                             \
+    _Pragma("unroll") for (int u = 0; u < 8 * kSubV; ++u) {                        \
+      const int g_ = u >> 3, b_ = u & 7;                                           \
+      if (do_mma_) {                                                               \
+        if (g_ < kSubVA) {                                                         \
+          const int ga_ = g_ < kSubVA ? g_ : 0;                                    \
+          acc[ga_][b_] = mma(fa[ga_], mb_[b_], (z_) ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[ga_][b_]); \
+        } else {                                                                   \
+          const int gv_ = g_ >= kSubVA ? g_ - kSubVA : 0;                          \
+          if (z_) mma_v0(accv[gv_][b_], mx_[gv_], mb_[b_]);                        \
+          else mma_v(accv[gv_][b_], mx_[gv_], mb_[b_]);                            \
+        }                                                                          \
+      }                                                                            \
+      if ((do_rd_) && b_ == 3 && g_ < kSubT) rb_[g_ < kSubT ? g_ : 0] = RD_B(g_, (rh_), (rs_)); \
+      if ((do_rd_) && b_ == 5 && g_ < kSubVV) rx_[g_ < kSubVV ? g_ : 0] =                      \
+          RD_A(kSubVA + g_, (rh_), (rs_));                                         \
+      if ((do_rd_) && b_ == 7 && g_ < kSubVA) fa[g_ < kSubVA ? g_ : 0] = RD_A(g_, (rh_), (rs_)); \
+      {                                                                            \
+        const int pu_ = (p0_) + u;                                                 \
+        if (pu_ % kCopyEvery == 1 && pu_ / kCopyEvery < kCopies)                   \
+          COPY(pu_ / kCopyEvery, (ck_), (cs_));                                    \
+      }                                                                            \
+      FENCE();                                                                     \
+    }                                                                              \
+  } while (0)
+
+  // Phase k: once stage k has landed (its copies were issued during phase
+  // k - 1) and every wave has finished reading stage k - 1, one barrier;
+  // then the first step runs the MFMAs of stage k - 1's second half (their
+  // fragments were read during phase k - 1) while reading stage k's first
+  // half, and the second step runs stage k's first half while reading its
+  // second half. Stage k + 1 is copied, across the whole phase, into the
+  // buffer stage k - 1 has left.
+  COPY_ALL_PROLOGUE();
+  // Phase 0 has no carried MFMAs.
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  __syncthreads();
+  FENCE();
+  STEP(false, false, true, fx1, fb1, fx0, fb0, 0, 0, 0, 1, 1);
+  STEP(true, true, true, fx0, fb0, fx1, fb1, 1, 0, 8 * kSubV, 1, 1);
+  for (int k = 1; k < nk; ++k) {
+    const int sb = k & 1;
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __syncthreads();
+    FENCE();
+    STEP(true, false, true, fx1, fb1, fx0, fb0, 0, sb, 0, k + 1, sb ^ 1);
+    STEP(true, false, true, fx0, fb0, fx1, fb1, 1, sb, 8 * kSubV, k + 1, sb ^ 1);
+  }
+  STEP(true, false, false, fx1, fb1, fx0, fb0, 0, 0, 2 * 8 * kSubV, 0, 0);  // stage nk - 1's second half
+  // Drain the tail copies and reads before the LDS is reused; the wait
+  // states cover the VALU reads of the VGPR accumulators.
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  __syncthreads();
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  // bf16-logit mode: round every accumulator once, in place, so that the
+  // epilogue below holds no second copy of the logits.
+  if (kBf16) {
 #pragma unroll
     for (int j = 0; j < kSubT; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
-  bf16x8 fa0[kSubV], fb0[kSubT], fa1[kSubV], fb1[kSubT];
-
-  // One step = 64 MFMAs (all 8 x 8 tiles, 32 hidden elements) on the
-  // fragments (mf, mb) with, interleaved, the 16 fragment reads of half rh_
-  // into (rf, rb) (one per 3 MFMAs from the first, so the last lands well
-  // before the phase barrier) and 8 copies (one per 8 MFMAs) of unit
-  // (cx_, ck_) into slot cs_. The order is fixed instruction by instruction.
-#define STEP(do_mma_, mf_, mb_, rf_, rb_, rh_, cx_, ck_, cs_)                \
-  do {                                                                       \
-    _Pragma("unroll") for (int u = 0; u < 64; ++u) {                         \
-      if (do_mma_) MFMA(mf_, mb_, u);                                        \
-      if (u % 3 == 0 && u / 3 < 16) READ(rf_, rb_, u / 3, (rh_));            \
-      if ((u & 7) == 2) COPY((cx_), (u >> 3), (ck_), (cs_));                 \
-      FENCE();                                                               \
-    }                                                                        \
-  } while (0)
-
-  // Phase k reads units 2k (W, slot s0) and 2k + 1 (X, slot s0 + 1) and
-  // copies units 2k + 3 (X stage k + 1) and 2k + 4 (W stage k + 2) into the
-  // slots freed by the barrier that ended phase k - 1. Unit 2k + 2 (W stage
-  // k + 1) was copied during phase k - 1, so every copy has at least half a
-  // phase to land, and half of them a phase and a half. The first step runs
-  // the MFMAs of the previous stage's second half (carried across the
-  // barrier) while reading this stage's first half; the second step runs the
-  // first half while reading the second. The phase ends once at most the 8
-  // copies of unit 2k + 4 are in flight and every wave is there.
-#define PHASE(carry_)                                                              \
-  do {                                                                             \
-    const uint32_t bA = (uint32_t)s0 * kSlotB;                                     \
-    const uint32_t bB = (uint32_t)(s0 == kSlots - 1 ? 0 : s0 + 1) * kSlotB;         \
-    const int c3 = s0 + 3 >= kSlots ? s0 + 3 - kSlots : s0 + 3;                    \
-    const int c4 = s0 + 4 >= kSlots ? s0 + 4 - kSlots : s0 + 4;                    \
-    STEP((carry_), fa1, fb1, fa0, fb0, 0, true, k + 1, c3);                        \
-    STEP(true, fa0, fb0, fa1, fb1, 1, false, k + 2, c4);                           \
-    __builtin_amdgcn_s_waitcnt(kWaitVm8);                                          \
-    __syncthreads();                                                               \
-    FENCE();                                                                       \
-    s0 = s0 + 2 >= kSlots ? s0 + 2 - kSlots : s0 + 2;                              \
-  } while (0)
-
-  // Prologue: units 0, 1, 2 (W0, X0, W1) into slots 0, 1, 2; wait for 0 and 1.
+      for (int r = 0; r < 4; ++r) {
 #pragma unroll
-  for (int j = 0; j < kCopiesU; ++j) COPY(false, j, 0, 0);
+        for (int i = 0; i < kSubVA; ++i) acc[i][j][r] = logit<true>(acc[i][j][r]);
 #pragma unroll
-  for (int j = 0; j < kCopiesU; ++j) COPY(true, j, 0, 1);
-#pragma unroll
-  for (int j = 0; j < kCopiesU; ++j) COPY(false, j, 1, 2);
-  __builtin_amdgcn_s_waitcnt(kWaitVm8);
-  __syncthreads();
-  FENCE();
-
-  int s0 = 0;
-  int k = 0;
-  PHASE(false);
-  for (k = 1; k < nk; ++k) PHASE(true);
-#pragma unroll
-  for (int u = 0; u < 64; ++u) {  // second half of the last stage
-    MFMA(fa1, fb1, u);
-    FENCE();
+        for (int i = 0; i < kSubVV; ++i) accv[i][j][r] = logit<true>(accv[i][j][r]);
+      }
   }
-  // Drain the tail copies before the LDS is reused.
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
 #undef STEP
-#undef PHASE
 #undef COPY
-#undef READ
-#undef MFMA
+#undef RD_A
+#undef RD_B
 #undef FENCE
   float (*red_m)[kTileT] = reinterpret_cast<float (*)[kTileT]>(ring);
   float (*red_s)[kTileT] = reinterpret_cast<float (*)[kTileT]>(ring + 2 * kTileT * sizeof(float));
   float (*red_q)[kTileT] = reinterpret_cast<float (*)[kTileT]>(ring + 4 * kTileT * sizeof(float));
   int (*red_i)[kTileT] = reinterpret_cast<int (*)[kTileT]>(ring + 6 * kTileT * sizeof(float));
 
-  // ---- Epilogue: per-token online LSE over this wave's 128 vocab rows. ----
+  // ---- Epilogue: per-token online LSE over this wave's kWaveV vocab rows. ----
   const int vlane = v0 + wm * kWaveV + 4 * lg;
   const bool vtail = v0 + kTileV > a.V_true;
   const int64_t wv_lo = v0 + wm * kWaveV;
@@ -444,9 +496,12 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   for (int j = 0; j < kSubT; ++j) {
     const int tl = wn * kWaveT + j * 16 + lcol;
     const int t = t0 + tl;
-    auto v = [&](int i, int r) __attribute__((always_inline)) { return logit<kBf16>(acc[i][j][r]); };
+    auto raw = [&](int i, int r) __attribute__((always_inline)) {
+      return i < kSubVA ? acc[i < kSubVA ? i : 0][j][r] : accv[i >= kSubVA ? i - kSubVA : 0][j][r];
+    };
+    auto v = [&](int i, int r) __attribute__((always_inline)) { return raw(i, r); };
     auto vm = [&](int i, int r) __attribute__((always_inline)) {
-      return LP_MASKED(logit<kBf16>(acc[i][j][r]), vlane, i, r, a.V_true);
+      return LP_MASKED(raw(i, r), vlane, i, r, a.V_true);
     };
     float m, s, q;
     int li;
@@ -483,15 +538,15 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
 }
 
 // ---- Streaming kernel for small batches (HBM-bound on W). ----
-// With few rows the product is a stream over W (2 V H bytes) and the 256 x 256
-// tiles would be mostly padding. Here a work item is one 128-row half of a
+// With few rows the product is a stream over W (2 V H bytes) and the 352 x 256
+// tiles would be mostly padding. Here a work item is one 176-row half of a
 // vocabulary tile x 32 ST tokens, computed by a single wave in exactly the
-// placement of the 256 x 256 kernel -- vocabulary row -> (MFMA tile i, lane
+// placement of the 352 x 256 kernel -- vocabulary row -> (MFMA tile i, lane
 // group, register), token -> MFMA column, the same v_mfma_f32_16x16x32_bf16
 // chain over 32-wide K steps in ascending order -- and the same per-wave
 // epilogue (wave_lse), so every row's bits match. The wave writes its half's
 // (max, sum) partial; the merge kernel applies merge_halves before folding
-// the tiles, as the 256 x 256 kernel does in LDS.
+// the tiles, as the 352 x 256 kernel does in LDS.
 //
 // The grid is persistent (a fixed number of one-wave workgroups per CU, each
 // taking items b, b + G, b + 2G, ... with XCD-contiguous numbering, token
@@ -500,14 +555,14 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
 // segments of W) through a ring of kSmStages LDS slots with direct buffer ->
 // LDS copies, kSmStages - 1 stages in flight, continuing across item
 // boundaries; being alone in its workgroup, a wave only waits on its own
-// vmcnt, never on a barrier. Two slots (four waves per CU) stream faster than
-// deeper rings with fewer waves per CU.
+// vmcnt, never on a barrier. Two slots per wave, and as many waves per CU as
+// the LDS holds (three with 32-token items, two with 64).
 constexpr int kSmK = kTileK;                   // hidden elements per stage
 constexpr int kSmStages = 2;                   // ring depth
 constexpr int kSmRowB = kSmK * 2;              // LDS row bytes (128)
 constexpr int kSmNC = kSmRowB / 16;            // 16-byte chunks per row (8)
 constexpr int kSmRPC = 1024 / kSmRowB;         // rows per 1-KiB wave copy (8)
-constexpr int kSmRowsA = kWaveV;               // 128 W rows per item
+constexpr int kSmRowsA = kWaveV;               // 176 W rows per item
 constexpr int kSmCopiesA = kSmRowsA * kSmRowB / 1024;
 
 template <int ST>
@@ -516,7 +571,7 @@ struct Stream {
   static constexpr int kTilesB = 2 * ST;                   // 16-token MFMA tiles
   static constexpr int kCopiesB = kTok * kSmRowB / 1024;   // 4 ST
   static constexpr int kCopies = kSmCopiesA + kCopiesB;    // per stage
-  static constexpr int kSlotA = kSmRowsA * kSmRowB;        // 16 KiB
+  static constexpr int kSlotA = kSmRowsA * kSmRowB;        // 22 KiB
   static constexpr int kSlotB = kTok * kSmRowB;            // 4 ST KiB
   static constexpr int kSlot = kSlotA + kSlotB;
   static constexpr int kLds = kSmStages * kSlot;
@@ -676,7 +731,7 @@ __device__ __forceinline__ void lse_fold_stats(float& M, float& S, float& Q, int
 
 // Fold of the vocabulary tiles [lo, hi) (indices of the partial planes) of
 // one merge segment for token t, in ascending order, from the empty partial.
-// kHalves: the partials are per 128-row half of each vocabulary tile (rows
+// kHalves: the partials are per 176-row half of each vocabulary tile (rows
 // 2 vt and 2 vt + 1), merged with merge_halves first. kStats: the entropy
 // term and the argmax are carried along.
 template <bool kHalves, bool kStats>
@@ -828,7 +883,7 @@ __global__ __launch_bounds__(256) void shard_merge_kernel(ScoreArgs a, ShardArgs
 
 }  // namespace
 
-// Streaming kernel choice: items of 32 ST tokens; 0 = the 256 x 256 kernel.
+// Streaming kernel choice: items of 32 ST tokens; 0 = the 352 x 256 kernel.
 static int stream_tokens(int64_t T) {
   if (T <= 32) return 1;
   if (T <= kSkinnyMaxT) return 2;

@@ -1,0 +1,120 @@
+"""Build-time check of the MFMA instructions written as inline assembly.
+
+score_tile_kernel issues part of its MFMAs (those whose accumulators live in
+VGPRs) as inline assembly, where the compiler cannot see the instruction and
+so inserts none of the wait states CDNA requires around it. The kernel is
+written so that none are needed; this check proves it on the code the
+compiler actually produced, for every instantiation, and fails the build
+otherwise. It reads the device assembly of score.hip (our own build) and, for
+every MFMA that came from an inline-assembly block and writes VGPRs, rejects:
+
+  * a VALU instruction writing any of its A, B or C/D registers within the 4
+    instruction slots before it (VALU write -> MFMA read needs 2 wait states);
+  * within the 20 slots after it, a VALU instruction reading or writing its
+    D registers, a store reading them, or an MFMA reading them as A or B (an
+    8-pass XDL result needs about 11 wait states before other readers, and
+    its C read needs them before a VALU overwrite).
+
+Slots are counted conservatively: each instruction is one, `s_nop n` is n+1.
+"""
+
+from __future__ import annotations
+
+import re
+
+_VREG = re.compile(r"v\[(\d+):(\d+)\]|v(\d+)\b")
+_STORES = ("ds_write", "buffer_store", "global_store", "scratch_store", "flat_store")
+BEFORE_SLOTS = 4
+AFTER_SLOTS = 20
+
+
+def _regs(text: str) -> set[int]:
+    out: set[int] = set()
+    for m in _VREG.finditer(text):
+        if m.group(3) is not None:
+            out.add(int(m.group(3)))
+        else:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return out
+
+
+def _split(line: str) -> tuple[str, list[str]]:
+    parts = line.split(None, 1)
+    if len(parts) < 2:
+        return parts[0], []
+    return parts[0], [t.strip() for t in parts[1].split(";")[0].split(",")]
+
+
+def _slots(op: str, ops: list[str]) -> int:
+    if op == "s_nop" and ops:
+        try:
+            return int(ops[0], 0) + 1
+        except ValueError:
+            return 1
+    return 1
+
+
+def _kernel_lines(asm: str, name: str) -> list[tuple[str, bool]]:
+    i = asm.find(name + ":")
+    j = asm.find(".Lfunc_end", i)
+    lines: list[tuple[str, bool]] = []
+    in_asm = False
+    for raw in asm[i:j].split("\n")[1:]:
+        t = raw.strip()
+        if t.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if t.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        if not t or t.startswith((";", ".")) or t.endswith(":"):
+            continue
+        lines.append((t, in_asm))
+    return lines
+
+
+def check_asm(asm: str, kernel_filter: str = "score_tile_kernel") -> list[str]:
+    """Return one message per violation in the kernels whose name contains
+    kernel_filter; an empty list means the code is clean."""
+    problems: list[str] = []
+    names = [k for k in re.findall(r"\.amdhsa_kernel (\S+)", asm) if kernel_filter in k]
+    if not names:
+        problems.append(f"no kernel matching {kernel_filter!r} in the assembly")
+    for name in names:
+        lines = _kernel_lines(asm, name)
+        n_asm_mfma = 0
+        for n, (t, from_asm) in enumerate(lines):
+            op, ops = _split(t)
+            if not (from_asm and op.startswith("v_mfma") and len(ops) >= 4
+                    and ops[0].startswith("v")):
+                continue
+            n_asm_mfma += 1
+            D, A, B = _regs(ops[0]), _regs(ops[1]), _regs(ops[2])
+            slots = 0
+            for m in range(n - 1, -1, -1):
+                pt, _ = lines[m]
+                pop, pops = _split(pt)
+                if (pop.startswith("v_") and not pop.startswith("v_mfma") and pops
+                        and _regs(pops[0]) & (A | B | D)):
+                    problems.append(f"{name}: VALU write '{pt}' just before '{t}'")
+                slots += _slots(pop, pops)
+                if slots >= BEFORE_SLOTS:
+                    break
+            slots = 0
+            for m in range(n + 1, len(lines)):
+                pt, _ = lines[m]
+                pop, pops = _split(pt)
+                used = _regs(",".join(pops))
+                if pop.startswith("v_mfma"):
+                    if len(pops) >= 3 and (_regs(pops[1]) | _regs(pops[2])) & D:
+                        problems.append(f"{name}: '{pt}' reads the result of '{t}' too early")
+                elif pop.startswith("v_") and used & D:
+                    problems.append(f"{name}: VALU '{pt}' touches the result of '{t}' too early")
+                elif pop.startswith(_STORES) and used & D:
+                    problems.append(f"{name}: store '{pt}' reads the result of '{t}' too early")
+                slots += _slots(pop, pops)
+                if slots >= AFTER_SLOTS:
+                    break
+        if n_asm_mfma == 0:
+            problems.append(f"{name}: no inline-assembly MFMA found (check is stale)")
+    return problems

@@ -13,6 +13,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "liblp.h")
 
 
+def header_define(name):
+    return int(re.search(r"#define %s (\d+)" % name, open(HEADER).read()).group(1))
+
+
+TILE_V = header_define("LP_VOCAB_TILE_ROWS")
+
+
 @pytest.fixture(scope="module")
 def L():
     from rollout_logprob_consistency_amd import _lib
@@ -57,7 +64,7 @@ def test_status_strings(L):
 
 def test_workspace_bytes(L):
     for T, V in ((64, 4096), (8192, 151936), (1, 1), (300, 1000)):
-        n_vt = -(-V // 256)
+        n_vt = -(-V // TILE_V)
         got = L.lp_score_workspace_bytes(T, 4096, V, V)
         assert got >= 2 * n_vt * T * 4 + T * 4 and got % 256 == 0
     assert L.lp_score_workspace_bytes(-1, 64, 10, 10) == 0
@@ -66,7 +73,7 @@ def test_workspace_bytes(L):
 
 def test_stats_workspace_holds_two_more_planes(L):
     for T, V in ((64, 4096), (8192, 151936), (1, 1), (300, 1000)):
-        n_vt = -(-V // 256)
+        n_vt = -(-V // TILE_V)
         base = L.lp_score_workspace_bytes(T, 4096, V, V)
         got = L.lp_score_stats_workspace_bytes(T, 4096, V, V)
         assert got % 256 == 0 and got >= base + 2 * n_vt * T * 4
@@ -237,7 +244,8 @@ def test_shard_buffers(L):
     # A shard's workspace holds the partial planes of its own tiles only.
     whole = L.lp_score_workspace_bytes(8192, 4096, 151936, 151936)
     one = L.lp_score_shard_workspace_bytes(8192, 151936, 8, 0, 0)
-    assert one % 256 == 0 and one >= 2 * 76 * 8192 * 4 and one < whole // 6
+    # 432 tiles of 352 rows: 27 per segment, two segments (54 tiles) per shard of 8.
+    assert one % 256 == 0 and one >= 2 * 54 * 8192 * 4 and one < whole // 6
     # Shards with no rows (1000 rows, 16 shards) still need a valid buffer.
     assert L.lp_score_shard_workspace_bytes(8, 1000, 16, 15, 1) >= 256
 
@@ -300,3 +308,9 @@ def test_score_ex_flags_and_workspace(L):
     assert ex(P, 64, P, P, 8, 64, 100, 100, 1.0, 4, P, None, None, None, None, P, 1 << 20, None) == EINVAL
     assert ex(P, 64, P, P, 8, 64, 100, 100, 1.0, 1, P, None, None, None, None, P, 1 << 20, None) == EINVAL
     assert ex(P, 64, P, P, 8, 64, 100, 100, 0.0, 2, P, None, None, None, None, P, 1 << 20, None) == EINVAL
+
+
+def test_python_mirrors_of_header_constants():
+    from rollout_logprob_consistency_amd import _lib
+    assert _lib.MERGE_SEGMENTS == header_define("LP_MERGE_SEGMENTS")
+    assert _lib.VOCAB_TILE_ROWS == header_define("LP_VOCAB_TILE_ROWS")

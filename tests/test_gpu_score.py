@@ -39,10 +39,13 @@ def test_tiny_full_parity(temperature):
 
 @pytest.mark.parametrize("T,H,V,v_true,ldh", [
     (1, 64, 4096, 4096, 64),        # single row, minimum H
-    (7, 128, 1000, 1000, 128),      # ragged vocabulary tail (1000 = 3*256 + 232)
+    (7, 128, 1000, 1000, 128),      # ragged vocabulary tail (1000 = 2*352 + 296, in the upper half)
     (255, 256, 4096, 3000, 256),    # true vocabulary range shorter than the head
-    (257, 192, 513, 513, 200),      # two token tiles, 1-row-deep last vocab tile, strided rows
+    (257, 192, 353, 353, 200),      # two token tiles, 1-row-deep last vocab tile, strided rows
+    (257, 64, 513, 513, 64),        # last vocab tile 161 rows deep: inside its lower half
     (300, 256, 300, 129, 256),      # tail inside the first vocabulary half
+    (300, 128, 400, 177, 128),      # tail one row into the second half of the first tile
+    (300, 128, 704, 528, 128),      # tail exactly at a half boundary (528 = 352 + 176)
     (520, 64, 257, 1, 64),          # one-token vocabulary
 ])
 def test_ragged_shapes(T, H, V, v_true, ldh):

@@ -142,7 +142,7 @@ def test_qwen17b_shaped_sampled_rows(qwen17b):
 
 def test_batch_invariance(qwen17b):
     # 48 probe rows at random positions inside batches of 1, 7, 64 (streaming
-    # kernel) and 300, 4096 rows (256 x 256 tiles): bitwise equal outputs.
+    # kernel) and 300, 4096 rows (352 x 256 tiles): bitwise equal outputs.
     c, wd, _ = qwen17b
     rng = np.random.default_rng(9)
     probes = rng.choice(c.T, 48, replace=False)

@@ -80,7 +80,7 @@ def test_tiny_stream_path_all_shard_counts(stats):
 @pytest.mark.parametrize("T", [1, 33, 300])
 @pytest.mark.parametrize("stats", [False, True])
 def test_ragged_tokens_padded_vocab_temperature(T, stats):
-    # T = 300: 256 x 256 tiles with a ragged token tail; V_true < V_rows, so
+    # T = 300: 352 x 256 tiles with a ragged token tail; V_true < V_rows, so
     # the one-buffer W has padding rows that the shards never hold.
     H, V, v_true, temp = 256, 20000, 19990, 0.7
     c = synth.tiny_case(T=T, H=H, V=V, seed=3, temperature=temp)
@@ -95,7 +95,7 @@ def test_ragged_tokens_padded_vocab_temperature(T, stats):
 
 
 def test_small_vocabulary_with_empty_shards():
-    # 1000 rows = 4 tiles: with 8 or 16 shards most shards own no rows and
+    # 1000 rows = 3 tiles: with 8 or 16 shards most shards own no rows and
     # still write their (empty) segment records.
     c = synth.tiny_case(T=40, H=128, V=1000, seed=4)
     x, w, ids = dev_bf16(c.x_bits), dev_bf16(c.w_bits), dev(c.ids)
@@ -118,7 +118,7 @@ def test_shard_order_and_buffer_reuse():
 
 def test_qwen_shaped_eight_shards():
     # Qwen3-1.7B-shaped head (H = 2048, V = 151 936), 512 rows, 8 shards of
-    # 19 456 rows (the last 15 872): bitwise equal to the one-buffer call;
+    # 19 008 rows (the last 18 880): bitwise equal to the one-buffer call;
     # sampled rows against the oracle.
     c = synth.qwen_case(T=512, H=2048)
     x, w, ids = dev_bf16(c.x_bits), dev_bf16(c.w_bits), dev(c.ids)
@@ -152,9 +152,10 @@ def test_binding_rejects_wrong_shapes():
     c = synth.tiny_case(T=8, seed=7)
     x, w, ids = dev_bf16(c.x_bits), dev_bf16(c.w_bits), dev(c.ids)
     parts = lp.shard_partials(8, False, DEV)
+    rows = lp.vocab_shard(4096, 4, 0)["row_end"]   # shard 0 of 4: its rows start at 0
     with pytest.raises(ValueError):       # rows of another shard
-        lp.score_shard(x, w[:1000].clone(), ids, 4096, 4, 0, parts)
+        lp.score_shard(x, w[:rows - 24].clone(), ids, 4096, 4, 0, parts)
     with pytest.raises(ValueError):       # stats buffer expected
-        lp.score_shard(x, w[:1024].clone(), ids, 4096, 4, 0, parts, stats=True)
+        lp.score_shard(x, w[:rows].clone(), ids, 4096, 4, 0, parts, stats=True)
     with pytest.raises(lp.LpError):
-        lp.score_shard(x, w[:1024].clone(), ids, 4096, 4, 0, parts, temperature=0.0)
+        lp.score_shard(x, w[:rows].clone(), ids, 4096, 4, 0, parts, temperature=0.0)

@@ -1,0 +1,71 @@
+"""The build-time wait-state check of the inline-assembly MFMAs (CPU only).
+
+Each planted hazard below is one of the patterns the check exists to reject;
+the clean snippets are the patterns the tile kernel relies on."""
+
+import os
+
+import pytest
+
+from rollout_logprob_consistency_amd import isa_check
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def kernel(body_lines):
+    body = "\n".join("\t" + l for l in body_lines)
+    return (".amdhsa_kernel _Z17score_tile_kernelv\n.end_amdhsa_kernel\n"
+            "_Z17score_tile_kernelv:\n" + body + "\n.Lfunc_end0:\n")
+
+
+ASM_MFMA = [";;#ASMSTART", "v_mfma_f32_16x16x32_bf16 v[20:23], v[0:3], v[4:7], v[20:23]",
+            ";;#ASMEND"]
+
+
+def test_clean_chain_passes():
+    lines = ["ds_read_b128 v[0:3], v40", "ds_read_b128 v[4:7], v41", "s_waitcnt lgkmcnt(0)",
+             *ASM_MFMA, "v_mfma_f32_16x16x32_bf16 a[0:3], v[0:3], v[4:7], a[0:3]", *ASM_MFMA,
+             "s_nop 7", "s_nop 7", "s_nop 7", "v_max_f32_e32 v30, v20, v21"]
+    assert isa_check.check_asm(kernel(lines)) == []
+
+
+def test_valu_write_just_before_is_caught():
+    lines = ["v_mov_b64_e32 v[20:21], 0", *ASM_MFMA, "s_nop 7", "s_nop 7", "s_nop 7"]
+    assert any("VALU write" in p for p in isa_check.check_asm(kernel(lines)))
+
+
+def test_valu_write_of_a_source_just_before_is_caught():
+    lines = ["v_add_u32_e32 v5, 1, v5", *ASM_MFMA, "s_nop 7", "s_nop 7", "s_nop 7"]
+    assert isa_check.check_asm(kernel(lines))
+
+
+def test_valu_read_of_the_result_too_early_is_caught():
+    lines = [*ASM_MFMA, "s_nop 3", "v_mov_b64_e32 v[30:31], v[22:23]"]
+    assert any("touches the result" in p for p in isa_check.check_asm(kernel(lines)))
+
+
+def test_store_of_the_result_too_early_is_caught():
+    lines = [*ASM_MFMA, "scratch_store_dwordx4 off, v[20:23], off offset:16"]
+    assert any("store" in p for p in isa_check.check_asm(kernel(lines)))
+
+
+def test_mfma_reading_the_result_as_source_is_caught():
+    lines = [*ASM_MFMA, "v_mfma_f32_16x16x32_bf16 a[0:3], v[20:23], v[4:7], a[0:3]"]
+    assert isa_check.check_asm(kernel(lines))
+
+
+def test_enough_wait_states_pass():
+    lines = ["v_mov_b64_e32 v[20:21], 0", "s_nop 3", *ASM_MFMA, "s_nop 7", "s_nop 7", "s_nop 3",
+             "v_mov_b64_e32 v[30:31], v[22:23]"]
+    assert isa_check.check_asm(kernel(lines)) == []
+
+
+def test_a_kernel_without_asm_mfma_is_reported():
+    assert isa_check.check_asm(kernel(["s_endpgm"]))
+
+
+def test_built_score_kernel_is_clean():
+    path = os.path.join(ROOT, "_build", "score.device.s")
+    if not os.path.exists(path):
+        pytest.skip("no device assembly: the library has not been built here")
+    assert isa_check.check_asm(open(path).read()) == []

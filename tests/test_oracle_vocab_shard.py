@@ -73,13 +73,15 @@ def test_empty_shards_and_single_row_shards():
 
 
 def segment_rows(V_true):
-    """Rows per merge segment: 16 segments of P whole 256-row tiles,
-    P = ceil(ceil(V_true / 256) / 16)."""
-    tiles = -(-V_true // 256)
-    return 256 * -(-tiles // 16)
+    """Rows per merge segment: 16 segments of P whole vocabulary tiles of
+    R = LP_VOCAB_TILE_ROWS rows, P = ceil(ceil(V_true / R) / 16)."""
+    R = lp._lib.VOCAB_TILE_ROWS
+    tiles = -(-V_true // R)
+    return R * -(-tiles // 16)
 
 
-@pytest.mark.parametrize("V_true", [1, 255, 256, 1000, 4096, 4097, 151936, 152064, 262144])
+@pytest.mark.parametrize("V_true", [1, 255, 256, 351, 352, 353, 1000, 4096, 4097, 5632, 5633,
+                                    151936, 152064, 262144])
 def test_library_chunking_follows_the_segments(V_true):
     R = segment_rows(V_true)
     for n in range(1, 17):
