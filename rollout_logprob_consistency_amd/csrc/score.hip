@@ -464,6 +464,13 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0070);
   __syncthreads();
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  // Empty statements that claim to rewrite each VGPR accumulator: every later
+  // read of one is ordered after the wait states above (a plain asm is a
+  // fence for memory only, not for register-to-register code).
+#pragma unroll
+  for (int i = 0; i < kSubVV; ++i)
+#pragma unroll
+    for (int j = 0; j < kSubT; ++j) asm volatile("" : "+v"(accv[i][j]));
   // bf16-logit mode: round every accumulator once, in place, so that the
   // epilogue below holds no second copy of the logits.
   if (kBf16) {
