@@ -559,13 +559,11 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
 // taking items b, b + G, b + 2G, ... with XCD-contiguous numbering, token
 // tiles fastest so the waves of one XCD that share a W half-tile run
 // together). Each wave streams its items' 64-wide K stages (128-byte row
-// segments of W) through a ring of kSmStages LDS slots with direct buffer ->
-// LDS copies, kSmStages - 1 stages in flight, continuing across item
+// segments of W) through a ring of S::kStages LDS slots with direct buffer ->
+// LDS copies, S::kStages - 1 stages in flight, continuing across item
 // boundaries; being alone in its workgroup, a wave only waits on its own
-// vmcnt, never on a barrier. Two slots per wave, and as many waves per CU as
-// the LDS holds (three with 32-token items, two with 64).
+// vmcnt, never on a barrier; as many waves per CU as the LDS holds.
 constexpr int kSmK = kTileK;                   // hidden elements per stage
-constexpr int kSmStages = 2;                   // ring depth
 constexpr int kSmRowB = kSmK * 2;              // LDS row bytes (128)
 constexpr int kSmNC = kSmRowB / 16;            // 16-byte chunks per row (8)
 constexpr int kSmRPC = 1024 / kSmRowB;         // rows per 1-KiB wave copy (8)
@@ -581,8 +579,13 @@ struct Stream {
   static constexpr int kSlotA = kSmRowsA * kSmRowB;        // 22 KiB
   static constexpr int kSlotB = kTok * kSmRowB;            // 4 ST KiB
   static constexpr int kSlot = kSlotA + kSlotB;
-  static constexpr int kLds = kSmStages * kSlot;
-  static_assert((kSmStages - 1) * kCopies <= 63, "vmcnt holds at most 63");
+  // Ring depth: the stream is latency-bound, so as many stages in flight as
+  // the LDS allows without dropping below two waves per CU (32-token items:
+  // three 26 KiB stages, two waves per CU, 10 % faster than two stages with
+  // three waves; 64-token items: two 30 KiB stages).
+  static constexpr int kStages = ST == 1 ? 3 : 2;
+  static constexpr int kLds = kStages * kSlot;
+  static_assert((kStages - 1) * kCopies <= 63, "vmcnt holds at most 63");
 };
 
 template <int ST, bool kStats, bool kBf16>
@@ -617,7 +620,7 @@ __global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_ite
     const __amdgpu_buffer_rsrc_t xres =
         make_rsrc(reinterpret_cast<const char*>(a.x) + (size_t)t0 * X2,
                   span_bytes((uint64_t)(a.T - t0 - 1) * X2 + H2));
-    lds_char* slot = (lds_char*)ring + (g % kSmStages) * S::kSlot;
+    lds_char* slot = (lds_char*)ring + (g % S::kStages) * S::kSlot;
     const int koff = kt * kSmRowB;
     const int vr0 = (vh & 1) * kWaveV, vmax = a.V_rows - 1 - v0, tmax = a.T - 1 - t0;
 #pragma unroll
@@ -639,13 +642,13 @@ __global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_ite
   ((uint32_t)(((row0_) + lcol) * kSmRowB + swz((row0_) + lcol, 4 * (h_) + lg) * 16))
 
   f32x4 acc[kSubV][S::kTilesB];
-  for (int g = 0; g < kSmStages - 1 && g < n_stages; ++g) issue(g);
+  for (int g = 0; g < S::kStages - 1 && g < n_stages; ++g) issue(g);
   for (int g = 0; g < n_stages; ++g) {
-    if (g + kSmStages - 1 < n_stages) {
-      issue(g + kSmStages - 1);
-      // Stage g has landed once at most (kSmStages - 1) stages' copies remain.
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (((kSmStages - 1) * S::kCopies) & 15) |
-                                 ((((kSmStages - 1) * S::kCopies) >> 4) << 14));
+    if (g + S::kStages - 1 < n_stages) {
+      issue(g + S::kStages - 1);
+      // Stage g has landed once at most (kStages - 1) stages' copies remain.
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (((S::kStages - 1) * S::kCopies) & 15) |
+                                 ((((S::kStages - 1) * S::kCopies) >> 4) << 14));
     } else {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
     }
@@ -658,7 +661,7 @@ __global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_ite
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[i][jj][r] = 0.f;
     }
-    const char* slot = ring + (g % kSmStages) * S::kSlot;
+    const char* slot = ring + (g % S::kStages) * S::kSlot;
 #pragma unroll
     for (int h = 0; h < kSmK / 32; ++h) {
       bf16x8 fa[kSubV], fb[S::kTilesB];
