@@ -235,3 +235,33 @@ def tails(A, B, C, mask):
             pos_sum[p, i] = math.fsum(col.tolist())
             pos_count[p, i] = col.size
     return out, pos_sum, pos_count
+
+
+def worst_tokens(A, B, C, mask, k: int):
+    """Per pair, the k counted tokens with the largest |Delta|: a list of
+    (abs_delta, seq, pos) tuples, ordered by |Delta| descending and, among
+    equal |Delta|, by row-major position (sequence, then column); shorter
+    than k when fewer tokens are counted.
+
+    [vLLM] "Metric measurement basis": report the worst positions, not only
+    the mean (logprob_mae with its max and where it sits); [VeX] section 5,
+    practical indicators: the tail of abs(delta_logprob). The counted tokens
+    and Delta are those of tails(): active, both scores finite,
+    Delta = fp64(left) - fp64(right). The order is a plain stable sort.
+    """
+    if k < 0:
+        raise ValueError("k must be >= 0")
+    A, B, C, mask = _check(A, B, C, mask)
+    sides = {"A": A, "B": B, "C": C}
+    out = {}
+    for ln, rn in PAIRS:
+        left = sides[ln].astype(np.float64)
+        right = sides[rn].astype(np.float64)
+        keep = (mask != 0) & np.isfinite(left) & np.isfinite(right)
+        delta = np.abs(left - right)
+        seqs, poss = np.nonzero(keep)               # row-major order
+        vals = delta[seqs, poss]
+        order = np.lexsort((poss, seqs, -vals))     # last key is the primary one
+        out["".join((ln, rn))] = [(float(vals[j]), int(seqs[j]), int(poss[j]))
+                                  for j in order[:k]]
+    return out

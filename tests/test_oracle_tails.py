@@ -101,3 +101,73 @@ def test_position_profile_adds_up():
     for p, name in enumerate(("AB", "BC", "AC")):
         assert pos_count[p].sum() == t[name]["count"]
         assert abs(math.fsum(pos_sum[p].tolist()) - t[name]["sum_abs"]) <= 1e-12 * max(1.0, t[name]["sum_abs"])
+
+
+# ---------------------------------------------------------------------------
+# Worst tokens: pinned to a brute force with Python's own tuple ordering,
+# to the maximum and its position, to the order statistics, and to planted
+# ties that only the row-major rule orders.
+# ---------------------------------------------------------------------------
+
+def brute_worst(A, B, C, mask, k):
+    sides = {"A": A, "B": B, "C": C}
+    out = {}
+    for ln, rn in oracle.PAIRS:
+        items = []
+        for n in range(A.shape[0]):
+            for i in range(A.shape[1]):
+                l, r = float(sides[ln][n, i]), float(sides[rn][n, i])
+                if mask[n, i] and math.isfinite(l) and math.isfinite(r):
+                    items.append((-abs(l - r), n, i))
+        items.sort()
+        out[ln + rn] = [(-d, n, i) for d, n, i in items[:k]]
+    return out
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_worst_tokens_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    N, L = int(rng.integers(1, 6)), int(rng.integers(1, 40))
+    A = rng.standard_normal((N, L)).astype(np.float32)
+    B = (A + rng.integers(-3, 4, (N, L)) * 0.25).astype(np.float32)   # many equal |Delta|
+    C = (B + 1e-3 * rng.standard_normal((N, L))).astype(np.float32)
+    mask = (rng.random((N, L)) < 0.8).astype(np.uint8)
+    C[0, 0] = np.nan
+    for k in (0, 1, 5, N * L + 3):
+        got = oracle.worst_tokens(A, B, C, mask, k)
+        assert got == brute_worst(A, B, C, mask, k)
+
+
+def test_worst_one_is_the_tail_maximum():
+    r = synth.compare_case(N=6, max_resp=300, prompt=16, seed=8)
+    C = synth.noise_scores(r.C, r.mask, 1e-3, seed=8)
+    tails, _, _ = oracle.tails(r.A, r.B, C, r.mask)
+    worst = oracle.worst_tokens(r.A, r.B, C, r.mask, 1)
+    for p in ("AB", "BC", "AC"):
+        t = tails[p]
+        if t["count"]:
+            assert worst[p] == [(t["max_abs"], t["max_seq"], t["max_pos"])]
+        else:
+            assert worst[p] == []
+
+
+def test_worst_values_are_the_top_order_statistics():
+    r = synth.compare_case(N=5, max_resp=200, prompt=16, seed=9)
+    C = synth.noise_scores(r.C, r.mask, 1e-2, seed=9)
+    k = 37
+    worst = oracle.worst_tokens(r.A, r.B, C, r.mask, k)["BC"]
+    d = np.abs(r.B.astype(np.float64) - C.astype(np.float64))[r.mask != 0]
+    top = np.sort(d)[::-1][:k]
+    assert [w[0] for w in worst] == top.tolist()
+
+
+def test_worst_ties_follow_row_major_order():
+    N, L = 3, 5
+    A = np.zeros((N, L), np.float32)
+    B = np.zeros((N, L), np.float32)
+    B[2, 1] = B[0, 3] = B[1, 0] = B[0, 1] = 0.5     # four equal |Delta|
+    B[1, 4] = 0.75
+    mask = np.ones((N, L), np.uint8)
+    w = oracle.worst_tokens(A, B, B.copy(), mask, 4)["AB"]
+    assert w == [(0.75, 1, 4), (0.5, 0, 1), (0.5, 0, 3), (0.5, 1, 0)]
+    assert oracle.worst_tokens(A, B, B.copy(), mask, 40)["BC"][:2] == [(0.0, 0, 0), (0.0, 0, 1)]
