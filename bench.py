@@ -353,6 +353,21 @@ def main() -> int:
                          "frac_hbm": round(tbytes / tmed / 1e3 / PEAK_HBM_GBPS, 4)}
             log(f"bench: lp_compare_tails N={sc.N} L={sc.L}: {tmed:.1f} us "
                 f"({tbytes / tmed / 1e3:.1f} GB/s over 9 passes)")
+            # The same call with the 16 worst tokens of each pair
+            # (lp_compare_tails_ex): a fourth selection target per pair, a
+            # counting pass, a writing pass and a 16-row sort.
+            kw = 16
+            tw2 = torch.empty(lp._lib.lib().lp_compare_tails_ex_workspace_bytes(sc.N, sc.L, kw),
+                              dtype=torch.uint8, device=dev)
+            twr = torch.empty(3 * kw * lp.WORST_DTYPE.itemsize, dtype=torch.uint8, device=dev)
+            targs2 = (tA.data_ptr(), tB.data_ptr(), tC.data_ptr(), tM.data_ptr(), sc.N, sc.L,
+                      sc.L, kw, tout.data_ptr(), twr.data_ptr(), tps.data_ptr(), tpc.data_ptr(),
+                      tw2.data_ptr(), tw2.numel(), torch.cuda.current_stream().cuda_stream)
+            c_tails_ex = lp._lib.lib().lp_compare_tails_ex
+            wmed, _, _ = median_us(lambda: c_tails_ex(*targs2), calls=5, reps=5)
+            tails_rec["worst_k"] = kw
+            tails_rec["with_worst_us"] = round(wmed, 2)
+            log(f"bench: lp_compare_tails_ex (16 worst tokens per pair): {wmed:.1f} us")
             # Correction consumer on the same arrays: rollout = A, trainer = C;
             # TIS cap, MIS interval and K3 rejection, weights written. Bytes:
             # 2 x fp32 + mask read, fp32 weight written per position.

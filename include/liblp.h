@@ -293,6 +293,43 @@ lp_status lp_compare_tails(const float* gen_A, const float* replay_B,
                            size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Batch tail statistics with the worst tokens
+ *
+ * lp_compare_tails plus, per pair, the k counted tokens with the largest
+ * |Delta|: worst is [3][k] lp_worst_token in device memory (pair-major),
+ * row j of pair p the (j+1)-th largest, ordered by |Delta| descending and,
+ * among equal |Delta|, by row-major position (sequence, then column); when
+ * the pair counts fewer than k tokens the remaining rows are {0.0, -1, -1}.
+ * [vLLM] "Metric measurement basis": where the largest errors sit, not only
+ * their mean; [VeX] section 5: the tail of abs(delta_logprob).
+ *
+ * The k-th largest |Delta| is selected exactly like the quantiles; the rows
+ * are exact (bit-for-bit |Delta|, and the positions).
+ *
+ * 0 <= k <= LP_WORST_MAX; k == 0 gives lp_compare_tails (worst may be
+ * NULL). Workspace: lp_compare_tails_ex_workspace_bytes(N, L, k) bytes,
+ * 256-byte aligned. Errors as for lp_compare_tails, plus LP_EINVAL for k
+ * outside [0, LP_WORST_MAX] or a NULL worst with k > 0.
+ * ------------------------------------------------------------------------ */
+#define LP_WORST_MAX 4096
+
+typedef struct {
+  double abs_delta;   /* |Delta| of the token */
+  int32_t seq;        /* its sequence, -1 for a fill row */
+  int32_t pos;        /* its column, -1 for a fill row */
+} lp_worst_token;
+
+size_t lp_compare_tails_ex_workspace_bytes(int64_t N, int64_t L, int32_t k);
+
+lp_status lp_compare_tails_ex(const float* gen_A, const float* replay_B,
+                              const float* train_C, const uint8_t* mask,
+                              int64_t N, int64_t L, int64_t ld, int32_t k,
+                              lp_tail_stats* out, lp_worst_token* worst,
+                              double* pos_abs_sum, int32_t* pos_count,
+                              void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Vocabulary-parallel scoring with a canonical chunking
  *
  * With the LM head split over vocabulary shards, the normaliser must still

@@ -26,7 +26,8 @@ import numpy as np
 import torch
 
 from ._lib import (CORR_SEQ_DTYPE, EXPORTS, LP_OK, REJECT_K1, REJECT_K3,  # noqa: F401
-                   REJECT_NONE, SEQ_STATS_DTYPE, TAIL_STATS_DTYPE, LpError, lib, status_string)
+                   REJECT_NONE, SEQ_STATS_DTYPE, TAIL_STATS_DTYPE, WORST_DTYPE, WORST_MAX, LpError,
+                   lib, status_string)
 
 PAIRS = ("AB", "BC", "AC")
 
@@ -237,35 +238,49 @@ def compare(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch.Tenso
 
 
 def compare_tails(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch.Tensor,
-                  positions: bool = False):
-    """Batch tail statistics of |left - right| per pair (lp_compare_tails);
-    synchronises. Returns {"AB"|"BC"|"AC": numpy record of TAIL_STATS_DTYPE},
-    plus (pos_sum [3, L] fp64, pos_count [3, L] int32) when positions=True."""
+                  positions: bool = False, worst_k: int = 0):
+    """Batch tail statistics of |left - right| per pair (lp_compare_tails,
+    or lp_compare_tails_ex with worst_k > 0); synchronises. Returns
+    {"AB"|"BC"|"AC": numpy record of TAIL_STATS_DTYPE}, then, when asked,
+    (pos_sum [3, L] fp64, pos_count [3, L] int32) and the worst tokens
+    {"AB"|"BC"|"AC": numpy array [worst_k] of WORST_DTYPE}."""
     for name, t in (("A", A), ("B", B), ("C", C)):
         _need_cuda(name, t, torch.float32)
     _need_cuda("mask", mask, torch.uint8)
     if not (A.shape == B.shape == C.shape == mask.shape) or A.dim() != 2:
         raise ValueError("A, B, C and mask must share one [N, L] shape")
+    if not 0 <= int(worst_k) <= WORST_MAX:
+        raise ValueError(f"worst_k must lie in [0, {WORST_MAX}]")
     N, L = A.shape
     ld = A.stride(0) if A.numel() else L
     for t in (A, B, C, mask):
         if t.numel() and (t.stride(1) != 1 or (N > 1 and t.stride(0) != ld)):
             raise ValueError("A, B, C and mask need unit column stride and one row stride")
     dev = A.device
+    k = int(worst_k)
     out = torch.empty(3 * TAIL_STATS_DTYPE.itemsize, dtype=torch.uint8, device=dev)
     ps = torch.empty((3, L), dtype=torch.float64, device=dev) if positions else None
     pc = torch.empty((3, L), dtype=torch.int32, device=dev) if positions else None
-    need = int(lib().lp_compare_tails_workspace_bytes(N, L))
+    worst = torch.empty(max(3 * k * WORST_DTYPE.itemsize, 1), dtype=torch.uint8, device=dev)
+    need = int(lib().lp_compare_tails_ex_workspace_bytes(N, L, k))
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    st = lib().lp_compare_tails(_ptr(A), _ptr(B), _ptr(C), _ptr(mask), N, L, max(ld, L),
-                                _ptr(out), _ptr(ps), _ptr(pc), _ptr(ws), need, _stream(dev))
+    if k == 0:
+        st = lib().lp_compare_tails(_ptr(A), _ptr(B), _ptr(C), _ptr(mask), N, L, max(ld, L),
+                                    _ptr(out), _ptr(ps), _ptr(pc), _ptr(ws), need, _stream(dev))
+    else:
+        st = lib().lp_compare_tails_ex(_ptr(A), _ptr(B), _ptr(C), _ptr(mask), N, L, max(ld, L), k,
+                                       _ptr(out), _ptr(worst), _ptr(ps), _ptr(pc), _ptr(ws), need,
+                                       _stream(dev))
     if st != LP_OK:
-        raise LpError(st, "lp_compare_tails")
+        raise LpError(st, "lp_compare_tails" + ("_ex" if k else ""))
     rec = out.cpu().numpy().view(TAIL_STATS_DTYPE)
-    tails = {p: rec[i] for i, p in enumerate(PAIRS)}
+    res = [{p: rec[i] for i, p in enumerate(PAIRS)}]
     if positions:
-        return tails, ps.cpu().numpy(), pc.cpu().numpy()
-    return tails
+        res += [ps.cpu().numpy(), pc.cpu().numpy()]
+    if k:
+        wr = worst.cpu().numpy()[:3 * k * WORST_DTYPE.itemsize].view(WORST_DTYPE).reshape(3, k)
+        res.append({p: wr[i] for i, p in enumerate(PAIRS)})
+    return res[0] if len(res) == 1 else tuple(res)
 
 
 def vocab_shard(v_true: int, n_shards: int, rank: int) -> dict:

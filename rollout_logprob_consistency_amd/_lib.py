@@ -21,7 +21,8 @@ EXPORTS = ("lp_status_string", "lp_score_workspace_bytes", "lp_score",
            "lp_compare_tails_workspace_bytes", "lp_compare_tails",
            "lp_vocab_shard_range", "lp_shard_partials_bytes",
            "lp_score_shard_workspace_bytes", "lp_score_shard", "lp_merge_shards",
-           "lp_correct", "lp_score_ex_workspace_bytes", "lp_score_ex")
+           "lp_correct", "lp_score_ex_workspace_bytes", "lp_score_ex",
+           "lp_compare_tails_ex_workspace_bytes", "lp_compare_tails_ex")
 
 REJECT_NONE, REJECT_K1, REJECT_K3 = 0, 1, 3  # LP_REJECT_*
 
@@ -57,6 +58,11 @@ TAIL_STATS_DTYPE = np.dtype([
     ("sum_abs", "<f8"), ("sum_prob_abs", "<f8"),
 ], align=True)
 assert TAIL_STATS_DTYPE.itemsize == 64
+
+# numpy mirror of `lp_worst_token`.
+WORST_DTYPE = np.dtype([("abs_delta", "<f8"), ("seq", "<i4"), ("pos", "<i4")], align=True)
+assert WORST_DTYPE.itemsize == 16
+WORST_MAX = 4096  # LP_WORST_MAX
 
 
 class LpError(RuntimeError):
@@ -99,6 +105,11 @@ def lib() -> ctypes.CDLL:
     L.lp_compare_tails.restype = ctypes.c_int
     L.lp_compare_tails.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp,
                                    ctypes.c_size_t, vp]
+    L.lp_compare_tails_ex_workspace_bytes.restype = ctypes.c_size_t
+    L.lp_compare_tails_ex_workspace_bytes.argtypes = [i64, i64, ctypes.c_int32]
+    L.lp_compare_tails_ex.restype = ctypes.c_int
+    L.lp_compare_tails_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int32, vp, vp, vp,
+                                      vp, vp, ctypes.c_size_t, vp]
     i32 = ctypes.c_int32
     u32 = ctypes.c_uint32
     L.lp_score_ex_workspace_bytes.restype = ctypes.c_size_t

@@ -333,21 +333,36 @@ lp_status lp_correct(const float* rollout_lp, const float* train_lp, const uint8
 }
 
 size_t lp_compare_tails_workspace_bytes(int64_t N, int64_t L) {
-  if (N < 0 || L < 0 || N > kI32Max || L > kI32Max) return 0;
-  return lp::tails_workspace_bytes(N, L);
+  return lp_compare_tails_ex_workspace_bytes(N, L, 0);
+}
+
+size_t lp_compare_tails_ex_workspace_bytes(int64_t N, int64_t L, int32_t k) {
+  if (N < 0 || L < 0 || N > kI32Max || L > kI32Max || k < 0 || k > LP_WORST_MAX) return 0;
+  return lp::tails_workspace_bytes(N, L, k);
 }
 
 lp_status lp_compare_tails(const float* gen_A, const float* replay_B, const float* train_C,
                            const uint8_t* mask, int64_t N, int64_t L, int64_t ld,
                            lp_tail_stats* out, double* pos_abs_sum, int32_t* pos_count,
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return lp_compare_tails_ex(gen_A, replay_B, train_C, mask, N, L, ld, 0, out, nullptr,
+                             pos_abs_sum, pos_count, workspace, workspace_bytes, stream);
+}
+
+lp_status lp_compare_tails_ex(const float* gen_A, const float* replay_B, const float* train_C,
+                              const uint8_t* mask, int64_t N, int64_t L, int64_t ld, int32_t k,
+                              lp_tail_stats* out, lp_worst_token* worst, double* pos_abs_sum,
+                              int32_t* pos_count, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
   if (N < 0 || L < 0 || ld < L) return LP_EINVAL;
   if (!out || !workspace) return LP_EINVAL;
+  if (k < 0 || k > LP_WORST_MAX || (k > 0 && !worst)) return LP_EINVAL;
   if ((pos_abs_sum == nullptr) != (pos_count == nullptr)) return LP_EINVAL;
   if (N > 0 && L > 0 && (!gen_A || !replay_B || !train_C || !mask)) return LP_EINVAL;
   if (L > kI32Max || N > kI32Max) return LP_EUNSUPPORTED;
-  if (workspace_bytes < lp::tails_workspace_bytes(N, L) || !aligned(workspace, 256))
+  if (workspace_bytes < lp::tails_workspace_bytes(N, L, k) || !aligned(workspace, 256))
     return LP_EINVAL;
+  if (k > 0 && !aligned(worst, 8)) return LP_EINVAL;
   lp::TailArgs a;
   a.A = gen_A;
   a.B = replay_B;
@@ -362,6 +377,8 @@ lp_status lp_compare_tails(const float* gen_A, const float* replay_B, const floa
   a.workspace = workspace;
   a.vec = ld % 4 == 0 && aligned(gen_A, 16) && aligned(replay_B, 16) && aligned(train_C, 16) &&
           aligned(mask, 4);
+  a.worst_k = k;
+  a.worst = worst;
   return lp::launch_tails(a, stream) == hipSuccess ? LP_OK : LP_EHIP;
 }
 

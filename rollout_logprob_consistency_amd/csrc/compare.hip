@@ -341,17 +341,29 @@ namespace lp {
 // Exact order statistics by radix selection on the bit patterns of |delta|
 // (non-negative fp64, so the bits order like the values): 8 passes of one
 // byte, each a histogram pass over the batch -- one workgroup per sequence,
-// LDS counters, integer atomics into 9 global histograms (3 pairs x 3
-// quantiles) -- and a one-workgroup select that keeps, per target, the byte
-// where the wanted rank falls. Every count is an integer, so the result does
-// not depend on the order in which workgroups run. The sums and the first
-// worst token are formed per sequence in a fixed order (pass 0) and reduced
-// in a fixed tree; the position profile folds fixed chunks of sequences in
-// order.
+// LDS counters, integer atomics into 12 global histograms (3 pairs x 3
+// quantiles and the k-th largest) -- and a one-workgroup select that keeps,
+// per target, the byte where the wanted rank falls. Every count is an
+// integer, so the result does not depend on the order in which workgroups
+// run. The sums and the first worst token are formed per sequence in a fixed
+// order (pass 0) and reduced in a fixed tree; the position profile folds
+// fixed chunks of sequences in order.
+//
+// Worst k tokens: the k-th largest key tau of a pair is selected like the
+// quantiles; then every sequence counts its tokens above tau and equal to
+// it, a scan turns the counts into offsets, and a second pass writes the
+// tokens above tau and the first (in row-major order) of those equal to it
+// as candidates; one workgroup per pair sorts its candidates (|delta|
+// descending, then sequence and column ascending).
 // ---------------------------------------------------------------------------
 namespace {
 
-constexpr int kTailTargets = 9;     // 3 pairs x (p50, p95, p99)
+// Targets per pair: p50, p95, p99 and, when worst tokens are asked for, the
+// k-th largest. The kernels are instantiated for 3 and 4 (an idle fourth
+// target would still cost every pass a little); the workspace always has
+// room for 4.
+constexpr int kMaxTP = 4;
+constexpr int kMaxTargets = 3 * kMaxTP;
 constexpr int kTailThreads = 256;
 constexpr int kTailChunks = 64;     // sequence chunks of the position profile
 // Copies of the histograms: workgroup b adds into copy b mod kHistCopies, so
@@ -359,7 +371,7 @@ constexpr int kTailChunks = 64;     // sequence chunks of the position profile
 // workgroups (identical rows put every workgroup's count in one bin); the
 // select kernel sums the copies.
 constexpr int kHistCopies = 16;
-constexpr int kHistWords = kTailTargets * 256;
+constexpr int kHistStride = kMaxTargets * 256;  // words per histogram copy
 
 struct TailSel {
   uint64_t prefix;   // bytes of the selected key found so far
@@ -383,19 +395,28 @@ struct TailList {
   int32_t src;       // the target whose region it is; -1: no list
 };
 
+struct WorstCand {   // a worst-token candidate
+  uint64_t key;      // bits of |delta|
+  int32_t seq, pos;
+};
+
 struct TailWs {
-  uint32_t* hist;    // [kHistCopies][9][256]
-  TailSel* sel;      // [9]
-  TailList* list;    // [9]
+  uint32_t* hist;    // [kHistCopies][kMaxTargets][256]
+  TailSel* sel;      // [kMaxTargets]
+  TailList* list;    // [kMaxTargets]
   uint64_t* keys;    // [cap]
   int64_t cap;
-  uint32_t* cnt;     // [9][N] candidates of sequence n in list t (pass 2)
-  uint32_t* koff;    // [9][N] their offset within the list
+  uint32_t* cnt;     // [kMaxTargets][N] candidates of sequence n in list t (pass 2)
+  uint32_t* koff;    // [kMaxTargets][N] their offset within the list
   int64_t* count;    // [3]
   TailPart* part;    // [N][3]
   double* pos_part;  // [nch][3][L]
   int32_t* pos_cpart;
   int nch;
+  int32_t k;         // worst tokens per pair (0: none)
+  uint32_t* wcnt;    // [2][3][N] tokens above / equal to tau, per pair and sequence
+  int64_t* woff;     // [2][3][N] their offsets (exclusive scan over sequences)
+  WorstCand* cand;   // [3][k]
 };
 
 __host__ __device__ inline size_t tail_up(size_t x) { return (x + 255) & ~size_t(255); }
@@ -407,38 +428,47 @@ inline int64_t tail_key_cap(int64_t N, int64_t L) {
   return c < 4096 ? 4096 : (c > 0x7FFFFFFF ? 0x7FFFFFFF : c);
 }
 
-TailWs tail_layout(void* base, int64_t N, int64_t L) {
+TailWs tail_layout(void* base, int64_t N, int64_t L, int32_t k) {
   char* p = static_cast<char*>(base);
   TailWs w;
   size_t o = 0;
-  w.hist = reinterpret_cast<uint32_t*>(p + o); o = tail_up(o + kHistCopies * kHistWords * sizeof(uint32_t));
-  w.sel = reinterpret_cast<TailSel*>(p + o);   o = tail_up(o + kTailTargets * sizeof(TailSel));
-  w.list = reinterpret_cast<TailList*>(p + o); o = tail_up(o + kTailTargets * sizeof(TailList));
+  w.hist = reinterpret_cast<uint32_t*>(p + o); o = tail_up(o + kHistCopies * kHistStride * sizeof(uint32_t));
+  w.sel = reinterpret_cast<TailSel*>(p + o);   o = tail_up(o + kMaxTargets * sizeof(TailSel));
+  w.list = reinterpret_cast<TailList*>(p + o); o = tail_up(o + kMaxTargets * sizeof(TailList));
   w.cap = tail_key_cap(N, L);
   w.keys = reinterpret_cast<uint64_t*>(p + o); o = tail_up(o + (size_t)w.cap * sizeof(uint64_t));
-  w.cnt = reinterpret_cast<uint32_t*>(p + o);  o = tail_up(o + (size_t)N * kTailTargets * sizeof(uint32_t));
-  w.koff = reinterpret_cast<uint32_t*>(p + o); o = tail_up(o + (size_t)N * kTailTargets * sizeof(uint32_t));
+  w.cnt = reinterpret_cast<uint32_t*>(p + o);  o = tail_up(o + (size_t)N * kMaxTargets * sizeof(uint32_t));
+  w.koff = reinterpret_cast<uint32_t*>(p + o); o = tail_up(o + (size_t)N * kMaxTargets * sizeof(uint32_t));
   w.count = reinterpret_cast<int64_t*>(p + o); o = tail_up(o + 3 * sizeof(int64_t));
   w.part = reinterpret_cast<TailPart*>(p + o); o = tail_up(o + (size_t)N * 3 * sizeof(TailPart));
   w.nch = (int)(N < kTailChunks ? (N < 1 ? 1 : N) : kTailChunks);
   w.pos_part = reinterpret_cast<double*>(p + o); o = tail_up(o + (size_t)w.nch * 3 * L * sizeof(double));
-  w.pos_cpart = reinterpret_cast<int32_t*>(p + o);
+  w.pos_cpart = reinterpret_cast<int32_t*>(p + o); o = tail_up(o + (size_t)w.nch * 3 * L * sizeof(int32_t));
+  w.k = k;
+  w.wcnt = reinterpret_cast<uint32_t*>(p + o); o = tail_up(o + (size_t)(k > 0 ? 6 * N : 0) * sizeof(uint32_t));
+  w.woff = reinterpret_cast<int64_t*>(p + o); o = tail_up(o + (size_t)(k > 0 ? 6 * N : 0) * sizeof(int64_t));
+  w.cand = reinterpret_cast<WorstCand*>(p + o);
   return w;
 }
 
-size_t tail_bytes(int64_t N, int64_t L) {
+size_t tail_bytes(int64_t N, int64_t L, int32_t k) {
   size_t o = 0;
-  o = tail_up(o + kHistCopies * kHistWords * sizeof(uint32_t));
-  o = tail_up(o + kTailTargets * sizeof(TailSel));
-  o = tail_up(o + kTailTargets * sizeof(TailList));
+  o = tail_up(o + kHistCopies * kHistStride * sizeof(uint32_t));
+  o = tail_up(o + kMaxTargets * sizeof(TailSel));
+  o = tail_up(o + kMaxTargets * sizeof(TailList));
   o = tail_up(o + (size_t)tail_key_cap(N, L) * sizeof(uint64_t));
-  o = tail_up(o + (size_t)N * kTailTargets * sizeof(uint32_t));
-  o = tail_up(o + (size_t)N * kTailTargets * sizeof(uint32_t));
+  o = tail_up(o + (size_t)N * kMaxTargets * sizeof(uint32_t));
+  o = tail_up(o + (size_t)N * kMaxTargets * sizeof(uint32_t));
   o = tail_up(o + 3 * sizeof(int64_t));
   o = tail_up(o + (size_t)N * 3 * sizeof(TailPart));
   const int nch = (int)(N < kTailChunks ? (N < 1 ? 1 : N) : kTailChunks);
   o = tail_up(o + (size_t)nch * 3 * L * sizeof(double));
   o = tail_up(o + (size_t)nch * 3 * L * sizeof(int32_t));
+  if (k > 0) {
+    o = tail_up(o + (size_t)6 * N * sizeof(uint32_t));
+    o = tail_up(o + (size_t)6 * N * sizeof(int64_t));
+    o = tail_up(o + (size_t)3 * k * sizeof(WorstCand));
+  }
   return o;
 }
 
@@ -448,16 +478,17 @@ __device__ __forceinline__ int pair_right(int p) { return p == 0 ? 1 : 2; }
 
 // The target whose histogram target t reads: the first target of its pair
 // that is selecting under the same prefix (every one of them in pass 0).
+template <int kTP>
 __device__ __forceinline__ int tail_src(const uint64_t* pre, const bool* want, int t) {
-  const int p0 = 3 * (t / 3);
+  const int p0 = kTP * (t / kTP);
   for (int u = p0; u < t; ++u)
     if (want[u] && pre[u] == pre[t]) return u;
   return t;
 }
 
 __global__ __launch_bounds__(kTailThreads) void tails_init_kernel(TailWs w) {
-  for (int i = threadIdx.x; i < kHistCopies * kHistWords; i += kTailThreads) w.hist[i] = 0u;
-  if (threadIdx.x < kTailTargets) {
+  for (int i = threadIdx.x; i < kHistCopies * kHistStride; i += kTailThreads) w.hist[i] = 0u;
+  if (threadIdx.x < kMaxTargets) {
     w.sel[threadIdx.x] = TailSel{0ull, 0};
     w.list[threadIdx.x] = TailList{0, 0, -1};
   }
@@ -497,33 +528,34 @@ __device__ __forceinline__ void tail_load4(const TailArgs& a, const float* const
 // which also counts each sequence's candidates per list; 3: no histogram,
 // writes each sequence's candidates at the offsets the counts give (a
 // separate pass so that no append needs an atomic on a shared counter).
-template <bool kVec, int kMode>
+template <bool kVec, int kMode, int kTP>
 __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, TailWs w, int pass) {
-  __shared__ uint32_t h[kHistWords];
+  constexpr int kNT = 3 * kTP, kHW = kNT * 256;
+  __shared__ uint32_t h[kHW];
   __shared__ TailPart red[kMode == 0 ? 3 : 1][kMode == 0 ? kTailThreads : 1];
-  __shared__ uint32_t n_found[kTailTargets];
+  __shared__ uint32_t n_found[kNT];
   const int tid = threadIdx.x;
   const int shift = 56 - 8 * pass;  // this pass's byte: key bits [shift + 7 : shift]
   // Targets of one pair whose prefixes agree see the same tokens: only the
   // first of them counts (tail_src() below names it for the select kernel).
-  uint64_t pre[kTailTargets];
-  bool want[kTailTargets];
-  bool src_list[kTailTargets];  // kMode 2, 3: t owns a list region
+  uint64_t pre[kNT];
+  bool want[kNT];
+  bool src_list[kNT];  // kMode 2, 3: t owns a list region
 #pragma unroll
-  for (int t = 0; t < kTailTargets; ++t) {
+  for (int t = 0; t < kNT; ++t) {
     pre[t] = pass ? w.sel[t].prefix : 0ull;
     want[t] = pass == 0 || (w.sel[t].rank > 0 && (pass <= 2 || w.list[t].src < 0));
   }
   bool any_want = false;
 #pragma unroll
-  for (int t = 0; t < kTailTargets; ++t) {
-    if (tail_src(pre, want, t) != t) want[t] = false;
+  for (int t = 0; t < kNT; ++t) {
+    if (tail_src<kTP>(pre, want, t) != t) want[t] = false;
     any_want = any_want || want[t];
     src_list[t] = kMode >= 2 && want[t] && w.list[t].src == t;
   }
   if (!any_want) return;  // uniform: every target has a list or is done
-  for (int i = tid; i < kHistWords; i += kTailThreads) h[i] = 0u;
-  if (kMode >= 2 && tid < kTailTargets) n_found[tid] = 0u;
+  for (int i = tid; i < kHW; i += kTailThreads) h[i] = 0u;
+  if (kMode >= 2 && tid < kNT) n_found[tid] = 0u;
   __syncthreads();
 
   const int64_t n = blockIdx.x;
@@ -566,12 +598,13 @@ __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, Ta
         bool any = ok && kMode == 0;
         if (kMode != 0) {
 #pragma unroll
-          for (int j = 0; j < 3; ++j)
-            any = any || (ok && want[3 * p + j] && (key >> (shift + 8)) == pre[3 * p + j]);
+          for (int j = 0; j < kTP; ++j)
+            any = any || (ok && want[kTP * p + j] &&
+                          (key >> (shift + 8)) == pre[kTP * p + j]);
         }
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
-          const int t = 3 * p + j;
+        for (int j = 0; j < kTP; ++j) {
+          const int t = kTP * p + j;
           if (!want[t] || __ballot(any) == 0) continue;  // uniform
           const bool hit = ok && (kMode == 0 || (key >> (shift + 8)) == pre[t]);
           const uint64_t hb = __ballot(hit);
@@ -616,11 +649,11 @@ __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, Ta
   }
   __syncthreads();
   if (kMode == 3) return;
-  uint32_t* hc = w.hist + (blockIdx.x % kHistCopies) * kHistWords;
-  for (int i = tid; i < kHistWords; i += kTailThreads)
+  uint32_t* hc = w.hist + (blockIdx.x % kHistCopies) * kHistStride;
+  for (int i = tid; i < kHW; i += kTailThreads)
     if (h[i]) atomicAdd(&hc[i], h[i]);
   if (kMode == 2) {
-    if (tid < kTailTargets) w.cnt[tid * a.N + n] = src_list[tid] ? n_found[tid] : 0u;
+    if (tid < kNT) w.cnt[tid * a.N + n] = src_list[tid] ? n_found[tid] : 0u;
     return;
   }
   if (kMode != 0) return;
@@ -689,33 +722,35 @@ __global__ __launch_bounds__(kScanThreads) void tails_scan_kernel(TailWs w, int6
 // of the keys does not matter.
 constexpr int kListBlocks = 512;
 
+template <int kTP>
 __global__ __launch_bounds__(kTailThreads) void tails_list_kernel(TailWs w, int pass) {
-  __shared__ uint32_t h[kHistWords];
+  constexpr int kNT = 3 * kTP, kHW = kNT * 256;
+  __shared__ uint32_t h[kHW];
   const int tid = threadIdx.x, lane = tid & 63;
   const int shift = 56 - 8 * pass;
-  uint64_t pre[kTailTargets];
-  bool want[kTailTargets];
-  int lst[kTailTargets];
+  uint64_t pre[kNT];
+  bool want[kNT];
+  int lst[kNT];
 #pragma unroll
-  for (int t = 0; t < kTailTargets; ++t) {
+  for (int t = 0; t < kNT; ++t) {
     pre[t] = w.sel[t].prefix;
     lst[t] = w.list[t].src;
     want[t] = w.sel[t].rank > 0 && lst[t] >= 0;
   }
   bool any_want = false;
 #pragma unroll
-  for (int t = 0; t < kTailTargets; ++t) {
-    if (tail_src(pre, want, t) != t) want[t] = false;
+  for (int t = 0; t < kNT; ++t) {
+    if (tail_src<kTP>(pre, want, t) != t) want[t] = false;
     any_want = any_want || want[t];
   }
   if (!any_want) return;  // uniform
-  for (int i = tid; i < kHistWords; i += kTailThreads) h[i] = 0u;
+  for (int i = tid; i < kHW; i += kTailThreads) h[i] = 0u;
   __syncthreads();
   const int64_t stride = (int64_t)gridDim.x * kTailThreads;
-  for (int u = 0; u < kTailTargets; ++u) {
+  for (int u = 0; u < kNT; ++u) {
     bool used = false;
 #pragma unroll
-    for (int t = 0; t < kTailTargets; ++t) used = used || (want[t] && lst[t] == u);
+    for (int t = 0; t < kNT; ++t) used = used || (want[t] && lst[t] == u);
     if (!used) continue;  // uniform
     const TailList L = w.list[u];
     const int64_t wave0 = (int64_t)blockIdx.x * kTailThreads + (tid - lane);
@@ -725,7 +760,7 @@ __global__ __launch_bounds__(kTailThreads) void tails_list_kernel(TailWs w, int 
       const uint64_t key = in ? w.keys[L.off + e] : 0ull;
       const uint32_t digit = (uint32_t)(key >> shift) & 255u;
 #pragma unroll
-      for (int t = 0; t < kTailTargets; ++t) {
+      for (int t = 0; t < kNT; ++t) {
         if (!want[t] || lst[t] != u) continue;  // uniform
         const bool hit = in && (key >> (shift + 8)) == pre[t];
         const uint64_t hb = __ballot(hit);
@@ -741,31 +776,33 @@ __global__ __launch_bounds__(kTailThreads) void tails_list_kernel(TailWs w, int 
     }
   }
   __syncthreads();
-  uint32_t* hc = w.hist + (blockIdx.x % kHistCopies) * kHistWords;
-  for (int i = tid; i < kHistWords; i += kTailThreads)
+  uint32_t* hc = w.hist + (blockIdx.x % kHistCopies) * kHistStride;
+  for (int i = tid; i < kHW; i += kTailThreads)
     if (h[i]) atomicAdd(&hc[i], h[i]);
 }
 
 // Select the byte of each target's key; one wave per target, 4 bins a lane.
 // A target reads the histogram of tail_src() (the same prefix within its
 // pair); every histogram is read before any is cleared or any prefix moves.
-__global__ __launch_bounds__(64 * kTailTargets) void tails_select_kernel(TailWs w, int pass) {
-  __shared__ uint64_t s_pre[kTailTargets];
-  __shared__ int64_t s_rank[kTailTargets], s_len[kTailTargets];
+template <int kTP>
+__global__ __launch_bounds__(64 * kMaxTargets) void tails_select_kernel(TailWs w, int pass) {
+  constexpr int kNT = 3 * kTP;
+  __shared__ uint64_t s_pre[kNT];
+  __shared__ int64_t s_rank[kNT], s_len[kNT];
   const int t = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (threadIdx.x < kTailTargets) s_rank[threadIdx.x] = 0;
-  uint64_t pre[kTailTargets];
-  bool want[kTailTargets];
+  if (threadIdx.x < kNT) s_rank[threadIdx.x] = 0;
+  uint64_t pre[kNT];
+  bool want[kNT];
 #pragma unroll
-  for (int u = 0; u < kTailTargets; ++u) {
+  for (int u = 0; u < kNT; ++u) {
     pre[u] = pass ? w.sel[u].prefix : 0ull;
     want[u] = pass == 0 || w.sel[u].rank > 0;
   }
-  const int src = tail_src(pre, want, t);
+  const int src = tail_src<kTP>(pre, want, t);
   uint32_t c[4] = {0u, 0u, 0u, 0u};
 #pragma unroll 4
   for (int cp = 0; cp < kHistCopies; ++cp) {
-    const uint4 q = *reinterpret_cast<const uint4*>(w.hist + cp * kHistWords + src * 256 + 4 * lane);
+    const uint4 q = *reinterpret_cast<const uint4*>(w.hist + cp * kHistStride + src * 256 + 4 * lane);
     c[0] += q.x;
     c[1] += q.y;
     c[2] += q.z;
@@ -774,7 +811,7 @@ __global__ __launch_bounds__(64 * kTailTargets) void tails_select_kernel(TailWs 
   const int64_t old_rank = pass ? w.sel[t].rank : 0;
   __syncthreads();
   for (int cp = 0; cp < kHistCopies; ++cp)
-    *reinterpret_cast<uint4*>(w.hist + cp * kHistWords + t * 256 + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(w.hist + cp * kHistStride + t * 256 + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
   const int64_t lsum = (int64_t)c[0] + c[1] + c[2] + c[3];
   int64_t incl = lsum;  // inclusive scan over lanes
 #pragma unroll
@@ -786,9 +823,16 @@ __global__ __launch_bounds__(64 * kTailTargets) void tails_select_kernel(TailWs 
   int64_t rank;
   if (pass == 0) {
     // The pass-0 histogram holds every counted token of the pair.
-    const int64_t pct = (t % 3 == 0) ? 50 : (t % 3 == 1 ? 95 : 99);
-    rank = total > 0 ? (pct * total + 99) / 100 : 0;
-    if (t % 3 == 0 && lane == 0) w.count[t / 3] = total;
+    const int j = t % kTP;
+    if (j < 3) {
+      const int64_t pct = j == 0 ? 50 : (j == 1 ? 95 : 99);
+      rank = total > 0 ? (pct * total + 99) / 100 : 0;
+    } else {
+      // The k-th largest: rank count - k + 1 (the smallest when fewer are
+      // counted); no target without worst tokens requested.
+      rank = (w.k > 0 && total > 0) ? (total > w.k ? total - w.k + 1 : 1) : 0;
+    }
+    if (j == 0 && lane == 0) w.count[t / kTP] = total;
   } else {
     rank = old_rank;
   }
@@ -816,11 +860,11 @@ __global__ __launch_bounds__(64 * kTailTargets) void tails_select_kernel(TailWs 
   if (threadIdx.x != 0) return;
   // Lists for passes 3 .. 7, in target order while the key buffer lasts.
   int64_t used = 0;
-  for (int u = 0; u < kTailTargets; ++u) {
+  for (int u = 0; u < kNT; ++u) {
     TailList L{0, 0, -1};
     if (s_rank[u] > 0) {
       int src = u;
-      for (int v = 3 * (u / 3); v < u; ++v)
+      for (int v = kTP * (u / kTP); v < u; ++v)
         if (s_rank[v] > 0 && s_pre[v] == s_pre[u]) {
           src = v;
           break;
@@ -837,6 +881,7 @@ __global__ __launch_bounds__(64 * kTailTargets) void tails_select_kernel(TailWs 
 }
 
 // Batch results per pair: fixed chunks of sequences per thread, fixed tree.
+template <int kTP>
 __global__ __launch_bounds__(3 * kTailThreads) void tails_final_kernel(TailArgs a, TailWs w) {
   __shared__ TailPart red[3][kTailThreads];
   __shared__ int32_t red_seq[3][kTailThreads];
@@ -884,9 +929,9 @@ __global__ __launch_bounds__(3 * kTailThreads) void tails_final_kernel(TailArgs 
     lp_tail_stats o;
     o.count = w.count[p];
     const bool any = o.count > 0;
-    o.q50 = any ? __longlong_as_double((long long)w.sel[3 * p].prefix) : 0.0;
-    o.q95 = any ? __longlong_as_double((long long)w.sel[3 * p + 1].prefix) : 0.0;
-    o.q99 = any ? __longlong_as_double((long long)w.sel[3 * p + 2].prefix) : 0.0;
+    o.q50 = any ? __longlong_as_double((long long)w.sel[kTP * p].prefix) : 0.0;
+    o.q95 = any ? __longlong_as_double((long long)w.sel[kTP * p + 1].prefix) : 0.0;
+    o.q99 = any ? __longlong_as_double((long long)w.sel[kTP * p + 2].prefix) : 0.0;
     o.max_abs = any ? __longlong_as_double((long long)r.max_key) : 0.0;
     o.max_seq = any ? red_seq[p][0] : -1;
     o.max_pos = any ? r.max_pos : -1;
@@ -953,47 +998,299 @@ __global__ __launch_bounds__(kTailThreads) void tails_pos_fold_kernel(TailArgs a
   a.pos_count[idx] = k;
 }
 
-}  // namespace
+// ---- Worst k tokens ----------------------------------------------------
 
-size_t tails_workspace_bytes(int64_t N, int64_t L) { return tail_bytes(N, L); }
-
-template <int kMode>
-static void launch_hist(const TailArgs& a, const TailWs& w, int pass, hipStream_t stream) {
-  if (a.vec)
-    hipLaunchKernelGGL((tails_hist_kernel<true, kMode>), dim3((unsigned)a.N), dim3(kTailThreads), 0,
-                       stream, a, w, pass);
-  else
-    hipLaunchKernelGGL((tails_hist_kernel<false, kMode>), dim3((unsigned)a.N), dim3(kTailThreads),
-                       0, stream, a, w, pass);
+// Threshold of pair p: the key its fourth target selected (meaningful when
+// the pair counts any token).
+__device__ __forceinline__ uint64_t worst_tau(const TailWs& w, int p) {
+  return w.sel[kMaxTP * p + 3].prefix;  // only with kTP == 4
 }
 
-hipError_t launch_tails(const TailArgs& a, hipStream_t stream) {
-  const TailWs w = tail_layout(a.workspace, a.N, a.L);
-  hipLaunchKernelGGL(tails_init_kernel, dim3(1), dim3(kTailThreads), 0, stream, w);
+// Per sequence and pair: counted tokens with key > tau and key == tau.
+template <bool kVec>
+__global__ __launch_bounds__(kTailThreads) void tails_worst_count_kernel(TailArgs a, TailWs w) {
+  __shared__ uint32_t tot[6];
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 6) tot[tid] = 0u;
+  __syncthreads();
+  uint64_t tau[3];
+  bool on[3];
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    tau[p] = worst_tau(w, p);
+    on[p] = w.count[p] > 0;
+  }
+  const int64_t n = blockIdx.x;
+  const float* const rows[3] = {a.A + n * a.ld, a.B + n * a.ld, a.C + n * a.ld};
+  const uint8_t* M = a.mask + n * a.ld;
+  uint32_t c[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+  constexpr int64_t kStep = 4 * kTailThreads;
+  for (int64_t i0 = 4 * (int64_t)tid; i0 < a.L; i0 += kStep) {
+    float vv[4][3];
+    bool actv[4];
+    tail_load4<kVec>(a, rows, M, i0, vv, actv);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const float l = vv[k][pair_left(p)], r = vv[k][pair_right(p)];
+        if (!(on[p] && actv[k] && __builtin_isfinite(l) && __builtin_isfinite(r))) continue;
+        const uint64_t key = (uint64_t)__double_as_longlong(fabs((double)l - (double)r));
+        c[p] += key > tau[p] ? 1u : 0u;
+        c[3 + p] += key == tau[p] ? 1u : 0u;
+      }
+  }
+  // Integer sums: the order of the additions does not matter.
+#pragma unroll
+  for (int q = 0; q < 6; ++q) {
+    uint32_t v = c[q];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += (uint32_t)__shfl_xor((int)v, off);
+    if (lane == 0 && v) atomicAdd(&tot[q], v);
+  }
+  __syncthreads();
+  if (tid < 6) w.wcnt[tid * a.N + n] = tot[tid];
+}
+
+// Exclusive scans of the six count rows over the sequences, one workgroup
+// per row, 64-bit offsets. Thread j takes the contiguous sequences
+// [j per, (j + 1) per).
+__global__ __launch_bounds__(kScanThreads) void tails_worst_scan_kernel(TailWs w, int64_t N) {
+  __shared__ int64_t wsum[kScanThreads / 64];
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t* cnt = w.wcnt + q * N;
+  int64_t* off = w.woff + q * N;
+  const int64_t per = (N + kScanThreads - 1) / kScanThreads;
+  const int64_t lo = min(N, tid * per), hi = min(N, lo + per);
+  int64_t tot = 0;
+  for (int64_t n = lo; n < hi; ++n) tot += cnt[n];
+  int64_t incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int64_t run = incl - tot;
+  for (int v = 0; v < wave; ++v) run += wsum[v];
+  for (int64_t n = lo; n < hi; ++n) {
+    off[n] = run;
+    run += cnt[n];
+  }
+}
+
+// Inclusive scan of one value over the workgroup's threads, in thread order;
+// `total` is the workgroup's sum. Every thread must call it.
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t u = (uint32_t)__shfl_up((int)incl, o);
+    if (lane >= o) incl += u;
+  }
+  __syncthreads();  // the previous call's readers are done with wsum
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0u;
+  total = 0u;
+#pragma unroll
+  for (int x = 0; x < kTailThreads / 64; ++x) {
+    before += x < wave ? wsum[x] : 0u;
+    total += wsum[x];
+  }
+  return before + incl;
+}
+
+// Writes the candidates: every token above tau at its slot, and the tokens
+// equal to tau whose row-major rank among them is below what k still needs.
+// Slots follow position order within the sequence (threads take four
+// consecutive positions, in thread order, per 1024-position chunk).
+template <bool kVec>
+__global__ __launch_bounds__(kTailThreads) void tails_worst_write_kernel(TailArgs a, TailWs w) {
+  __shared__ uint32_t wsum[kTailThreads / 64];
+  const int tid = threadIdx.x;
+  const int64_t n = blockIdx.x, N = a.N;
+  uint64_t tau[3];
+  bool on[3];
+  int64_t gt_total[3], need_eq[3], run_g[3], run_e[3], m[3];
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    tau[p] = worst_tau(w, p);
+    on[p] = w.count[p] > 0;
+    m[p] = min((int64_t)w.k, w.count[p]);
+    gt_total[p] = w.woff[p * N + N - 1] + w.wcnt[p * N + N - 1];
+    need_eq[p] = m[p] - gt_total[p];
+    run_g[p] = w.woff[p * N + n];
+    run_e[p] = w.woff[(3 + p) * N + n];
+  }
+  const float* const rows[3] = {a.A + n * a.ld, a.B + n * a.ld, a.C + n * a.ld};
+  const uint8_t* M = a.mask + n * a.ld;
+  constexpr int64_t kStep = 4 * kTailThreads;
+  const int64_t Lw = (a.L + kStep - 1) / kStep * kStep;  // every thread takes every chunk
+  for (int64_t i0 = 4 * (int64_t)tid; i0 < Lw; i0 += kStep) {
+    float vv[4][3];
+    bool actv[4];
+    tail_load4<kVec>(a, rows, M, i0, vv, actv);
+    uint64_t key[4][3];
+    uint32_t fg[3] = {0u, 0u, 0u}, fe[3] = {0u, 0u, 0u};  // bit k: position i0 + k is above / equal
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const float l = vv[k][pair_left(p)], r = vv[k][pair_right(p)];
+        const bool ok = on[p] && actv[k] && __builtin_isfinite(l) && __builtin_isfinite(r);
+        key[k][p] = (uint64_t)__double_as_longlong(fabs((double)l - (double)r));
+        fg[p] |= (ok && key[k][p] > tau[p]) ? 1u << k : 0u;
+        fe[p] |= (ok && key[k][p] == tau[p]) ? 1u << k : 0u;
+      }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      uint32_t tg, te;
+      const uint32_t ig = block_incl_scan((uint32_t)__popc(fg[p]), wsum, tg);
+      const uint32_t ie = block_incl_scan((uint32_t)__popc(fe[p]), wsum, te);
+      int64_t sg = run_g[p] + ig - (uint32_t)__popc(fg[p]);
+      int64_t se = run_e[p] + ie - (uint32_t)__popc(fe[p]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int32_t pos = (int32_t)(i0 + k);
+        if (fg[p] & (1u << k)) {
+          if (sg < m[p]) w.cand[(int64_t)p * w.k + sg] = WorstCand{key[k][p], (int32_t)n, pos};
+          ++sg;
+        }
+        if (fe[p] & (1u << k)) {
+          if (se < need_eq[p])
+            w.cand[(int64_t)p * w.k + gt_total[p] + se] = WorstCand{key[k][p], (int32_t)n, pos};
+          ++se;
+        }
+      }
+      run_g[p] += tg;
+      run_e[p] += te;
+    }
+  }
+}
+
+// One workgroup per pair: bitonic sort of the candidates (|delta| descending,
+// then sequence, then column ascending) and the output rows; rows past the
+// counted tokens get |delta| 0 and sequence and column -1.
+constexpr int kWorstSortThreads = 1024;
+
+__device__ __forceinline__ bool worst_before(const WorstCand& x, const WorstCand& y) {
+  if (x.key != y.key) return x.key > y.key;
+  if (x.seq != y.seq) return x.seq < y.seq;
+  return x.pos < y.pos;
+}
+
+__global__ __launch_bounds__(kWorstSortThreads) void tails_worst_sort_kernel(TailArgs a, TailWs w) {
+  __shared__ WorstCand s[LP_WORST_MAX];
+  const int p = blockIdx.x, tid = threadIdx.x;
+  const int64_t m = min((int64_t)w.k, w.count[p]);
+  int P = 1;
+  while (P < m) P <<= 1;
+  // Padding sorts last: |delta| 0 and the largest sequence index.
+  for (int i = tid; i < P; i += kWorstSortThreads)
+    s[i] = i < m ? w.cand[(int64_t)p * w.k + i] : WorstCand{0ull, 0x7FFFFFFF, 0x7FFFFFFF};
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P; i += kWorstSortThreads) {
+        const int j = i ^ stride;
+        if (j > i) {
+          // Blocks with (i & size) == 0 end in the wanted order, the others
+          // in the reverse; the last merge (size == P) orders everything.
+          const bool fwd = (i & size) == 0;
+          const WorstCand x = s[i], y = s[j];
+          if (worst_before(y, x) == fwd) {
+            s[i] = y;
+            s[j] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = tid; i < w.k; i += kWorstSortThreads) {
+    lp_worst_token o;
+    if (i < m) {
+      o.abs_delta = __longlong_as_double((long long)s[i].key);
+      o.seq = s[i].seq;
+      o.pos = s[i].pos;
+    } else {
+      o.abs_delta = 0.0;
+      o.seq = -1;
+      o.pos = -1;
+    }
+    a.worst[(int64_t)p * w.k + i] = o;
+  }
+}
+
+}  // namespace
+
+size_t tails_workspace_bytes(int64_t N, int64_t L, int32_t k) { return tail_bytes(N, L, k); }
+
+template <int kMode, int kTP>
+static void launch_hist(const TailArgs& a, const TailWs& w, int pass, hipStream_t stream) {
+  if (a.vec)
+    hipLaunchKernelGGL((tails_hist_kernel<true, kMode, kTP>), dim3((unsigned)a.N), dim3(kTailThreads),
+                       0, stream, a, w, pass);
+  else
+    hipLaunchKernelGGL((tails_hist_kernel<false, kMode, kTP>), dim3((unsigned)a.N),
+                       dim3(kTailThreads), 0, stream, a, w, pass);
+}
+
+// The selection passes and the batch results, for kTP targets per pair.
+template <int kTP>
+static void launch_select(const TailArgs& a, const TailWs& w, hipStream_t stream) {
+  constexpr int kNT = 3 * kTP;
   if (a.N > 0) {
     // Every pass runs, also with L == 0 (pass 0 then writes empty partials).
     for (int pass = 0; pass < 8; ++pass) {
       if (pass == 0) {
-        launch_hist<0>(a, w, pass, stream);
+        launch_hist<0, kTP>(a, w, pass, stream);
       } else if (pass == 2) {
-        launch_hist<2>(a, w, pass, stream);
-        hipLaunchKernelGGL(tails_scan_kernel, dim3(kTailTargets), dim3(kScanThreads), 0, stream, w,
-                           a.N);
-        launch_hist<3>(a, w, pass, stream);
+        launch_hist<2, kTP>(a, w, pass, stream);
+        hipLaunchKernelGGL(tails_scan_kernel, dim3(kNT), dim3(kScanThreads), 0, stream, w, a.N);
+        launch_hist<3, kTP>(a, w, pass, stream);
       } else {
-        launch_hist<1>(a, w, pass, stream);  // passes >= 3: targets without a list
+        launch_hist<1, kTP>(a, w, pass, stream);  // passes >= 3: targets without a list
       }
       if (pass >= 3)
-        hipLaunchKernelGGL(tails_list_kernel, dim3(kListBlocks), dim3(kTailThreads), 0, stream, w,
-                           pass);
-      hipLaunchKernelGGL(tails_select_kernel, dim3(1), dim3(64 * kTailTargets), 0, stream, w,
-                         pass);
+        hipLaunchKernelGGL(tails_list_kernel<kTP>, dim3(kListBlocks), dim3(kTailThreads), 0, stream,
+                           w, pass);
+      hipLaunchKernelGGL(tails_select_kernel<kTP>, dim3(1), dim3(64 * kNT), 0, stream, w, pass);
     }
   } else {
     // No sequence: empty histograms give count 0 and no rank to select.
-    hipLaunchKernelGGL(tails_select_kernel, dim3(1), dim3(64 * kTailTargets), 0, stream, w, 0);
+    hipLaunchKernelGGL(tails_select_kernel<kTP>, dim3(1), dim3(64 * kNT), 0, stream, w, 0);
   }
-  hipLaunchKernelGGL(tails_final_kernel, dim3(1), dim3(3 * kTailThreads), 0, stream, a, w);
+  hipLaunchKernelGGL(tails_final_kernel<kTP>, dim3(1), dim3(3 * kTailThreads), 0, stream, a, w);
+}
+
+hipError_t launch_tails(const TailArgs& a, hipStream_t stream) {
+  const TailWs w = tail_layout(a.workspace, a.N, a.L, a.worst_k);
+  hipLaunchKernelGGL(tails_init_kernel, dim3(1), dim3(kTailThreads), 0, stream, w);
+  if (a.worst_k > 0) {
+    launch_select<4>(a, w, stream);
+    if (a.N > 0 && a.L > 0) {
+      if (a.vec) {
+        hipLaunchKernelGGL(tails_worst_count_kernel<true>, dim3((unsigned)a.N), dim3(kTailThreads),
+                           0, stream, a, w);
+        hipLaunchKernelGGL(tails_worst_scan_kernel, dim3(6), dim3(kScanThreads), 0, stream, w, a.N);
+        hipLaunchKernelGGL(tails_worst_write_kernel<true>, dim3((unsigned)a.N), dim3(kTailThreads),
+                           0, stream, a, w);
+      } else {
+        hipLaunchKernelGGL(tails_worst_count_kernel<false>, dim3((unsigned)a.N), dim3(kTailThreads),
+                           0, stream, a, w);
+        hipLaunchKernelGGL(tails_worst_scan_kernel, dim3(6), dim3(kScanThreads), 0, stream, w, a.N);
+        hipLaunchKernelGGL(tails_worst_write_kernel<false>, dim3((unsigned)a.N),
+                           dim3(kTailThreads), 0, stream, a, w);
+      }
+    }
+    // Also with no token: every row is the fill value.
+    hipLaunchKernelGGL(tails_worst_sort_kernel, dim3(3), dim3(kWorstSortThreads), 0, stream, a, w);
+  } else {
+    launch_select<3>(a, w, stream);
+  }
   if (a.pos_sum && a.L > 0) {
     // Stage 1 also runs with N == 0, writing zero partials for the fold.
     hipLaunchKernelGGL(tails_pos_kernel,

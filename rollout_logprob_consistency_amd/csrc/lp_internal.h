@@ -117,9 +117,11 @@ struct TailArgs {
   int32_t* pos_count;     // [3][L] or null (null iff pos_sum is)
   void* workspace;
   bool vec;               // rows 16-byte aligned (A, B, C), mask 4-byte aligned, ld % 4 == 0
+  int32_t worst_k;        // worst tokens per pair (0: none)
+  lp_worst_token* worst;  // [3][worst_k]; null when worst_k == 0
 };
 
-size_t tails_workspace_bytes(int64_t N, int64_t L);
+size_t tails_workspace_bytes(int64_t N, int64_t L, int32_t k);
 hipError_t launch_tails(const TailArgs& a, hipStream_t stream);
 
 }  // namespace lp

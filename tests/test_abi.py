@@ -41,7 +41,8 @@ def test_header_declares_the_boundary():
          "lp_compare_tails_workspace_bytes", "lp_compare_tails",
          "lp_vocab_shard_range", "lp_shard_partials_bytes",
          "lp_score_shard_workspace_bytes", "lp_score_shard", "lp_merge_shards",
-         "lp_correct", "lp_score_ex_workspace_bytes", "lp_score_ex"])
+         "lp_correct", "lp_score_ex_workspace_bytes", "lp_score_ex",
+         "lp_compare_tails_ex_workspace_bytes", "lp_compare_tails_ex"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -194,6 +195,33 @@ def test_compare_tails_rejects_bad_arguments(L):
     assert tails(L, wsb=L.lp_compare_tails_workspace_bytes(2, 5) - 1) == EINVAL
     assert tails(L, ws=ctypes.c_void_p(0x10010)) == EINVAL
     assert L.lp_compare_tails_workspace_bytes(-1, 5) == 0
+
+
+def tails_ex(L, k=4, worst=P, N=2, Lq=5, wsb=1 << 30, ws=P):
+    return L.lp_compare_tails_ex(P, P, P, P, N, Lq, Lq, k, P, worst, None, None, ws, wsb, None)
+
+
+def test_compare_tails_ex_rejects_bad_arguments(L):
+    EINVAL = 1
+    assert tails_ex(L, k=-1) == EINVAL
+    assert tails_ex(L, k=header_define("LP_WORST_MAX") + 1) == EINVAL
+    assert tails_ex(L, worst=None) == EINVAL              # rows requested, no buffer
+    assert tails_ex(L, worst=ctypes.c_void_p(0x10004)) == EINVAL
+    assert tails_ex(L, wsb=L.lp_compare_tails_ex_workspace_bytes(2, 5, 4) - 1) == EINVAL
+    assert tails_ex(L, N=-1) == EINVAL
+    assert L.lp_compare_tails_ex_workspace_bytes(2, 5, -1) == 0
+    assert L.lp_compare_tails_ex_workspace_bytes(2, 5, 4097) == 0
+    # k = 0 is lp_compare_tails; more rows need more workspace.
+    assert L.lp_compare_tails_ex_workspace_bytes(7, 9, 0) == L.lp_compare_tails_workspace_bytes(7, 9)
+    assert (L.lp_compare_tails_ex_workspace_bytes(7, 9, 100)
+            > L.lp_compare_tails_ex_workspace_bytes(7, 9, 1)
+            > L.lp_compare_tails_workspace_bytes(7, 9))
+
+
+def test_worst_token_layout():
+    from rollout_logprob_consistency_amd import _lib
+    assert _lib.WORST_DTYPE.itemsize == 16 and _lib.WORST_DTYPE.fields["pos"][1] == 12
+    assert _lib.WORST_MAX == header_define("LP_WORST_MAX")
 
 
 def test_tail_stats_layout():

@@ -127,3 +127,75 @@ def test_vector_and_scalar_paths_agree(record):
         for p in lp.PAIRS:
             assert vec[0][p].tobytes() == sca[0][p].tobytes(), p
         assert np.array_equal(vec[1], sca[1]) and np.array_equal(vec[2], sca[2])
+
+
+# ---------------------------------------------------------------------------
+# Worst k tokens (lp_compare_tails_ex): every row exact against the oracle
+# (|delta| bit for bit, sequence and column), the tail statistics unchanged.
+# ---------------------------------------------------------------------------
+
+def run_worst(A, B, C, M, k):
+    got, worst = lp.compare_tails(dev(A), dev(B), dev(C), dev(M), worst_k=k)
+    ref = oracle.worst_tokens(A, B, C, M, k)
+    plain = lp.compare_tails(dev(A), dev(B), dev(C), dev(M))
+    for p in lp.PAIRS:
+        assert got[p].tobytes() == plain[p].tobytes(), p      # the rows cost the stats nothing
+        w, r = worst[p], ref[p]
+        assert w.shape == (k,)
+        for j, (d, n, i) in enumerate(r):
+            assert (w[j]["abs_delta"], w[j]["seq"], w[j]["pos"]) == (d, n, i), (p, j, w[j], (d, n, i))
+        for j in range(len(r), k):                            # fewer counted tokens than k
+            assert (w[j]["abs_delta"], w[j]["seq"], w[j]["pos"]) == (0.0, -1, -1), (p, j)
+    return worst
+
+
+@pytest.mark.parametrize("k", [1, 16, 300, 4096])
+def test_worst_tokens_noise(record, k):
+    C = synth.noise_scores(record.C, record.mask, 1e-3, seed=41)
+    A = synth.offset_scores(record.A, record.mask, 0.10, first_pos=1)
+    run_worst(A, record.B, C, record.mask, k)
+
+
+@pytest.mark.parametrize("k", [3, 50, 2000])
+def test_worst_tokens_many_ties(k):
+    # Differences on a coarse grid: the k-th largest |delta| is shared by many
+    # tokens, and only the first of them in row-major order are kept.
+    rng = np.random.default_rng(7)
+    N, L = 23, 517
+    B = (rng.standard_normal((N, L)) - 4.0).astype(np.float32)
+    A = (B + np.round(rng.standard_normal((N, L)), 0).astype(np.float32) * np.float32(0.25))
+    C = B.copy()
+    C[rng.random((N, L)) < 0.5] += np.float32(0.5)
+    M = (rng.random((N, L)) < 0.9).astype(np.uint8)
+    A[1, 2] = np.nan; C[4, 4] = -np.inf
+    run_worst(A.astype(np.float32), B, C, M, k)
+
+
+def test_worst_tokens_identical_scores_keep_row_major_order(record):
+    w = run_worst(record.A, record.B, record.C, record.mask, 10)
+    assert (w["AB"]["abs_delta"] == 0.0).all()
+
+
+@pytest.mark.parametrize("N,L", [(0, 5), (3, 0), (1, 1), (2, 3)])
+def test_worst_tokens_degenerate_sizes(N, L):
+    A = np.zeros((N, L), np.float32)
+    B = np.ones((N, L), np.float32)
+    M = np.ones((N, L), np.uint8)
+    if N * L:
+        M[0, 0] = 0
+    run_worst(A, B, A.copy(), M, 7)
+
+
+def test_worst_tokens_sweep_size_paths_and_repeatability():
+    import torch
+    c = synth.compare_sweep_case(N=512)
+    w1 = run_worst(c.A, c.B, c.C, c.mask, 100)
+    # Strided rows take element loads: the same rows.
+    N, L = c.A.shape
+    big = [np.zeros((N, L + 1), a.dtype) for a in (c.A, c.B, c.C, c.mask)]
+    for b, a in zip(big, (c.A, c.B, c.C, c.mask)):
+        b[:, :L] = a
+    _, w2 = lp.compare_tails(*[dev(b)[:, :L] for b in big], worst_k=100)
+    _, w3 = lp.compare_tails(dev(c.A), dev(c.B), dev(c.C), dev(c.mask), worst_k=100)
+    for p in lp.PAIRS:
+        assert w1[p].tobytes() == w2[p].tobytes() == w3[p].tobytes(), p
