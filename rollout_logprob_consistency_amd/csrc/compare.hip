@@ -1145,6 +1145,9 @@ __global__ __launch_bounds__(kTailThreads) void tails_worst_write_kernel(TailArg
         fg[p] |= (ok && key[k][p] > tau[p]) ? 1u << k : 0u;
         fe[p] |= (ok && key[k][p] == tau[p]) ? 1u << k : 0u;
       }
+    // Few tokens reach tau: a chunk without any skips its scans (the test is
+    // uniform over the workgroup, so every thread takes the same branch).
+    if (!__syncthreads_or((fg[0] | fg[1] | fg[2] | fe[0] | fe[1] | fe[2]) != 0u)) continue;
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
       uint32_t tg, te;
