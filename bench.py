@@ -388,14 +388,44 @@ def main() -> int:
             del cw, cout
         del tA, tB, tC, tM
 
+    # Batch invariance at the headline shape (outside the timed region): the
+    # first 64 rows of the batch scored alone (the streaming kernel), each at
+    # a random position of a 7-row batch of other rows, and inside the whole
+    # batch rolled by 1000 rows (the tile kernel, other tile slots); every
+    # result must equal the timed run's bits.
+    n_probe = 64
+    ref_bits = out[:n_probe].clone().view(torch.int32)
+    alone = lp.score(x[:n_probe], w, ids[:n_probe])
+    rng = np.random.default_rng(synth.BASE_SEED)
+    in7 = torch.empty(n_probe, dtype=torch.float32, device=dev)
+    for j in range(n_probe):
+        rows = torch.from_numpy(rng.choice(np.arange(n_probe, T), 7, replace=False)).to(dev)
+        slot = int(rng.integers(7))
+        rows[slot] = j
+        in7[j] = lp.score(x[rows], w, ids[rows])[slot]
+    rolled = lp.score(torch.roll(x, 1000, 0), w, torch.roll(ids, 1000, 0))[1000:1000 + n_probe]
+    torch.cuda.synchronize()
+    inv_ok = all(torch.equal(t.view(torch.int32), ref_bits) for t in (alone, in7, rolled))
+    assert inv_ok, "batch invariance broken at the headline shape"
+    invariance = {"probe_rows": n_probe, "batches": [n_probe, 7, T], "bitwise_equal": inv_ok}
+    log(f"bench: batch invariance (64 probe rows alone, in 7-row batches, rolled in {T}): "
+        f"{'bitwise equal' if inv_ok else 'DIFFERENT'}")
+
     cpu = None
+    parity = None
     if not args.no_cpu_baseline:
         import oracle
         n = min(args.cpu_rows, T)
         log(f"bench: timing the fp64 oracle on {n} rows ...")
         tc = time.perf_counter()
-        oracle.score(case.x_bits[:n], w_bits, case.ids[:n], 1.0)
+        ref_lp, _ = oracle.score(case.x_bits[:n], w_bits, case.ids[:n], 1.0)
         dt = time.perf_counter() - tc
+        # The same rows of the timed run against the fp64 oracle (the
+        # tolerance is 1e-3 nats).
+        err = float(np.max(np.abs(out[:n].double().cpu().numpy() - ref_lp)))
+        parity = {"rows": n, "max_abs_diff_nats": err, "tolerance_nats": 1e-3,
+                  "within_tolerance": err <= 1e-3}
+        log(f"bench: max |lp_score - fp64 oracle| over {n} rows = {err:.3e} nats")
         cpu = {"value": round(n / dt, 3), "unit": "tokens/s", "cores": blas_threads(),
                "kind": "oracle",
                "sample": f"first {n} of the {T} rows (H={H}, V={V}), fp64 numpy/OpenBLAS, "
@@ -426,6 +456,8 @@ def main() -> int:
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
         "cpu_baseline": cpu,
+        "parity": parity,
+        "batch_invariance": invariance,
         "kernels": {"lp_score_ms": round(score_avg * 1e3, 4),
                     "lp_score_ms_median": round(float(np.median(score_ms)), 4),
                     "lp_score_ms_min": round(min(score_ms), 4),
