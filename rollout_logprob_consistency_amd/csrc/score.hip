@@ -544,25 +544,161 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   }
 }
 
-// ---- Streaming kernel for small batches (HBM-bound on W). ----
+// ---- Streaming kernels for small batches (HBM-bound on W). ----
 // With few rows the product is a stream over W (2 V H bytes) and the 352 x 256
 // tiles would be mostly padding. Here a work item is one 176-row half of a
-// vocabulary tile x 32 ST tokens, computed by a single wave in exactly the
-// placement of the 352 x 256 kernel -- vocabulary row -> (MFMA tile i, lane
-// group, register), token -> MFMA column, the same v_mfma_f32_16x16x32_bf16
-// chain over 32-wide K steps in ascending order -- and the same per-wave
-// epilogue (wave_lse), so every row's bits match. The wave writes its half's
-// (max, sum) partial; the merge kernel applies merge_halves before folding
-// the tiles, as the 352 x 256 kernel does in LDS.
+// vocabulary tile x a few 16-token MFMA tiles, computed by a single wave in
+// exactly the placement of the 352 x 256 kernel -- vocabulary row -> (MFMA
+// tile i, lane group, register), token -> MFMA column, the same
+// v_mfma_f32_16x16x32_bf16 chain over 32-wide K steps in ascending order --
+// and the same per-wave epilogue (wave_lse), so every row's bits match. The
+// wave writes its half's (max, sum) partial; the merge kernel applies
+// merge_halves before folding the tiles, as the 352 x 256 kernel does in LDS.
 //
+// score_stream_kernel (items of 16 or 32 tokens): one wave per item and one
+// item per wave, so the items of a batch (864 at the 151 936-row vocabulary)
+// all run at once, one wave per SIMD, and none is left with a second item
+// after the others finish. Each lane loads its MFMA fragments straight from
+// HBM into registers -- 16 bytes of one W row and of one token row per
+// 32-wide chunk, the two 64-byte halves of each row's 128-byte segment back
+// to back -- with the next 64-wide K stage (22.5 KiB of W per wave) in flight
+// while the current one is multiplied. Measured at the Qwen3-8B head, deeper
+// rings (three stages) and smaller or larger bursts per row run no faster:
+// one-wave-per-item streams of this shape top out near 5.9 TB/s on MI355X
+// (a plain sweep of the same bytes reaches 7 TB/s), and the kernel is within
+// about 12 % of that.
+template <int NT>
+struct Stream {
+  static constexpr int kTok = 16 * NT;  // tokens per item
+  static constexpr int kTilesB = NT;    // 16-token MFMA tiles
+  static constexpr int kRing = 2;       // 64-wide K stages in registers
+};
+
+template <int NT, bool kStats, bool kBf16>
+__global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_items) {
+  using S = Stream<NT>;
+  constexpr int R = S::kRing;
+  const int L = blockIdx.x;
+  if (L >= n_items) return;
+  const int lane = threadIdx.x, lcol = lane & 15, lg = lane >> 4;
+  const int nk = a.H / kTileK;
+  const uint32_t H2 = (uint32_t)a.H * 2, X2 = (uint32_t)a.ldh * 2;
+  const int vh = L / a.n_tt, tt = L - vh * a.n_tt;
+  // vh = 2 vt + half. The resource starts at the tile's first row v0 <
+  // V_rows; rows are clamped to the matrix (the upper half of the last tile
+  // may lie wholly past V_rows), results there are discarded.
+  const int v0 = (vh >> 1) * kTileV, t0 = tt * S::kTok;
+  const __amdgpu_buffer_rsrc_t wres =
+      make_rsrc(reinterpret_cast<const char*>(a.w) + (size_t)v0 * H2,
+                span_bytes((uint64_t)(a.V_rows - v0) * H2));
+  const __amdgpu_buffer_rsrc_t xres =
+      make_rsrc(reinterpret_cast<const char*>(a.x) + (size_t)t0 * X2,
+                span_bytes((uint64_t)(a.T - t0 - 1) * X2 + H2));
+  const int vr0 = (vh & 1) * kWaveV, vmax = a.V_rows - 1 - v0, tmax = a.T - 1 - t0;
+  // Lane l holds row 16 i + (l & 15) (W) or token 16 jj + (l & 15) (X),
+  // hidden elements 32 c + 8 (l >> 4) .. + 7 of each stage's chunk c.
+  uint32_t woff[kSubV], xoff[S::kTilesB];
+#pragma unroll
+  for (int i = 0; i < kSubV; ++i) woff[i] = (uint32_t)min(vr0 + 16 * i + lcol, vmax) * H2 + 16 * lg;
+#pragma unroll
+  for (int jj = 0; jj < S::kTilesB; ++jj) xoff[jj] = (uint32_t)min(16 * jj + lcol, tmax) * X2 + 16 * lg;
+
+  bf16x8 fw[R][2][kSubV], fx[R][2][S::kTilesB];
+  auto ld = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) __attribute__((always_inline)) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+  };
+  // Loads of stage k, clamped to the last stage: the ring's final refills
+  // re-read it, so every iteration issues the same loads and the compiler's
+  // wait counts stay exact.
+  auto issue = [&](bf16x8 (&w)[2][kSubV], bf16x8 (&x)[2][S::kTilesB], int k)
+      __attribute__((always_inline)) {
+    const int soff = min(k, nk - 1) * (kTileK * 2);
+#pragma unroll
+    for (int i = 0; i < kSubV; ++i)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) w[c][i] = ld(wres, woff[i] + 64 * c, soff);
+#pragma unroll
+    for (int jj = 0; jj < S::kTilesB; ++jj)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) x[c][jj] = ld(xres, xoff[jj] + 64 * c, soff);
+  };
+  f32x4 acc[kSubV][S::kTilesB];
+  auto compute = [&](bf16x8 (&w)[2][kSubV], bf16x8 (&x)[2][S::kTilesB])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < kSubV; ++i)
+#pragma unroll
+        for (int jj = 0; jj < S::kTilesB; ++jj) acc[i][jj] = mma(w[c][i], x[c][jj], acc[i][jj]);
+  };
+
+#pragma unroll
+  for (int i = 0; i < kSubV; ++i)
+#pragma unroll
+    for (int jj = 0; jj < S::kTilesB; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][jj][r] = 0.f;
+#pragma unroll
+  for (int u = 0; u < R - 1; ++u) issue(fw[u], fx[u], u);
+  int k0 = 0;
+  for (; k0 + R <= nk; k0 += R) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      // Stage k0 + u + R - 1 goes into the slot stage k0 + u - 1 has left.
+      issue(fw[(u + R - 1) % R], fx[(u + R - 1) % R], k0 + u + R - 1);
+      // Keep the refill ahead of this stage's MFMAs: left alone, the
+      // scheduler sinks each load down to its first use and waits for it.
+      __builtin_amdgcn_sched_barrier(0);
+      compute(fw[u], fx[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // The last nk - k0 < R stages sit in slots 0 .. nk - k0 - 1 already.
+#pragma unroll
+  for (int u = 0; u < R - 1; ++u)
+    if (k0 + u < nk) compute(fw[u], fx[u]);
+
+  const int vbase = vh * kWaveV;
+  const int vlane = vbase + 4 * lg;
+  const bool vtail = vbase + kWaveV > a.V_true;
+#pragma unroll
+  for (int jj = 0; jj < S::kTilesB; ++jj) {
+    const int t = t0 + 16 * jj + lcol;
+    auto v = [&](int i, int r) __attribute__((always_inline)) {
+      return logit<kBf16>(acc[i][jj][r]);
+    };
+    auto vm = [&](int i, int r) __attribute__((always_inline)) {
+      return LP_MASKED(logit<kBf16>(acc[i][jj][r]), vlane, i, r, a.V_true);
+    };
+    float m, s, q;
+    int li;
+    if (vtail) wave_lse<kStats>(vm, a.scale2, lg, m, s, q, li);
+    else wave_lse<kStats>(v, a.scale2, lg, m, s, q, li);
+    if (t < a.T) {
+      gather_target(v, a, t, vbase, lg);  // targets lie below V_true
+      if (lg == 0) {
+        a.part_m[(size_t)vh * a.T + t] = m;
+        a.part_s[(size_t)vh * a.T + t] = s;
+        if (kStats) {
+          a.part_q[(size_t)vh * a.T + t] = q;
+          a.part_i[(size_t)vh * a.T + t] = li == kNoRow ? kNoRow : a.v_base + vbase + li;
+        }
+      }
+    }
+  }
+}
+
+// score_stream_lds_kernel (items of 64 tokens): the 176 x 64 accumulators
+// leave no registers for a ring of W fragments, so the stages go through LDS.
 // The grid is persistent (a fixed number of one-wave workgroups per CU, each
 // taking items b, b + G, b + 2G, ... with XCD-contiguous numbering, token
 // tiles fastest so the waves of one XCD that share a W half-tile run
 // together). Each wave streams its items' 64-wide K stages (128-byte row
-// segments of W) through a ring of S::kStages LDS slots with direct buffer ->
-// LDS copies, S::kStages - 1 stages in flight, continuing across item
-// boundaries; being alone in its workgroup, a wave only waits on its own
-// vmcnt, never on a barrier; as many waves per CU as the LDS holds.
+// segments of W) through a ring of two LDS slots with direct buffer -> LDS
+// copies, one stage in flight, continuing across item boundaries; being alone
+// in its workgroup, a wave only waits on its own vmcnt, never on a barrier;
+// as many waves per CU as the LDS holds.
 constexpr int kSmK = kTileK;                   // hidden elements per stage
 constexpr int kSmRowB = kSmK * 2;              // LDS row bytes (128)
 constexpr int kSmNC = kSmRowB / 16;            // 16-byte chunks per row (8)
@@ -571,7 +707,7 @@ constexpr int kSmRowsA = kWaveV;               // 176 W rows per item
 constexpr int kSmCopiesA = kSmRowsA * kSmRowB / 1024;
 
 template <int ST>
-struct Stream {
+struct StreamLds {
   static constexpr int kTok = 32 * ST;                     // tokens per item
   static constexpr int kTilesB = 2 * ST;                   // 16-token MFMA tiles
   static constexpr int kCopiesB = kTok * kSmRowB / 1024;   // 4 ST
@@ -579,18 +715,16 @@ struct Stream {
   static constexpr int kSlotA = kSmRowsA * kSmRowB;        // 22 KiB
   static constexpr int kSlotB = kTok * kSmRowB;            // 4 ST KiB
   static constexpr int kSlot = kSlotA + kSlotB;
-  // Ring depth: the stream is latency-bound, so as many stages in flight as
-  // the LDS allows without dropping below two waves per CU (32-token items:
-  // three 26 KiB stages, two waves per CU, 10 % faster than two stages with
-  // three waves; 64-token items: two 30 KiB stages).
-  static constexpr int kStages = ST == 1 ? 3 : 2;
+  // Two 30 KiB stages and two waves per CU (three stages would leave one wave
+  // per CU, measured 70 % slower).
+  static constexpr int kStages = 2;
   static constexpr int kLds = kStages * kSlot;
   static_assert((kStages - 1) * kCopies <= 63, "vmcnt holds at most 63");
 };
 
 template <int ST, bool kStats, bool kBf16>
-__global__ __launch_bounds__(64) void score_stream_kernel(ScoreArgs a, int n_items) {
-  using S = Stream<ST>;
+__global__ __launch_bounds__(64) void score_stream_lds_kernel(ScoreArgs a, int n_items) {
+  using S = StreamLds<ST>;
   __shared__ __attribute__((aligned(1024))) char ring[S::kLds];
   const int lane = threadIdx.x;
   const int G = gridDim.x;  // a multiple of 8
@@ -893,10 +1027,12 @@ __global__ __launch_bounds__(256) void shard_merge_kernel(ScoreArgs a, ShardArgs
 
 }  // namespace
 
-// Streaming kernel choice: items of 32 ST tokens; 0 = the 352 x 256 kernel.
+// Streaming kernel choice: 16-token MFMA tiles per item (1, 2: the register
+// kernel; 4: the LDS kernel); 0 = the 352 x 256 kernel.
 static int stream_tokens(int64_t T) {
-  if (T <= 32) return 1;
-  if (T <= kSkinnyMaxT) return 2;
+  if (T <= 16) return 1;
+  if (T <= 32) return 2;
+  if (T <= kSkinnyMaxT) return 4;
   return 0;
 }
 
@@ -915,15 +1051,21 @@ ScoreWorkspace score_workspace_layout(int64_t T, int64_t V_true, bool stats) {
   return w;
 }
 
-template <int ST, bool kStats, bool kBf16>
+template <int NT, bool kStats, bool kBf16>
 static void launch_stream(ScoreArgs a, hipStream_t stream) {
-  a.n_tt = (a.T + 32 * ST - 1) / (32 * ST);
+  a.n_tt = (a.T + 16 * NT - 1) / (16 * NT);
   const int n_items = 2 * a.n_vt * a.n_tt;
-  // Workgroups (one wave each) per CU: as many as the LDS ring allows.
-  const int per_cu = (160 * 1024) / Stream<ST>::kLds;
-  const int grid = 256 * (per_cu < 8 ? per_cu : 8);
-  hipLaunchKernelGGL((score_stream_kernel<ST, kStats, kBf16>), dim3(grid), dim3(64), 0, stream, a,
-                     n_items);
+  if constexpr (NT <= 2) {  // one wave (and workgroup) per item
+    hipLaunchKernelGGL((score_stream_kernel<NT, kStats, kBf16>), dim3(n_items), dim3(64), 0,
+                       stream, a, n_items);
+  } else {
+    // Workgroups (one wave each) per CU: as many as the LDS ring allows.
+    constexpr int ST = NT / 2;
+    const int per_cu = (160 * 1024) / StreamLds<ST>::kLds;
+    const int grid = 256 * (per_cu < 8 ? per_cu : 8);
+    hipLaunchKernelGGL((score_stream_lds_kernel<ST, kStats, kBf16>), dim3(grid), dim3(64), 0,
+                       stream, a, n_items);
+  }
 }
 
 // The tile (or streaming) kernel alone; returns the streaming choice.
@@ -932,6 +1074,7 @@ static int launch_tiles_t(const ScoreArgs& a, hipStream_t stream) {
   const int st = stream_tokens(a.T);
   if (st == 1) launch_stream<1, kStats, kBf16>(a, stream);
   else if (st == 2) launch_stream<2, kStats, kBf16>(a, stream);
+  else if (st == 4) launch_stream<4, kStats, kBf16>(a, stream);
   else {
     const unsigned grid = (unsigned)a.n_vt * (unsigned)a.n_tt;
     hipLaunchKernelGGL((score_tile_kernel<kStats, kBf16>), dim3(grid), dim3(kThreads), 0, stream,

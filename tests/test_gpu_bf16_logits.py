@@ -123,7 +123,8 @@ def test_bf16_mode_is_batch_invariant():
     c = synth.tiny_case(T=700, H=256, V=4096, seed=6)
     x, w, ids = dev_bf16(c.x_bits), dev_bf16(c.w_bits), dev(c.ids)
     full = bits(lp.score_ex(x, w, ids, bf16_logits=True))
-    for lo, hi in ((0, 1), (5, 12), (100, 164), (200, 600), (0, 700)):
+    for lo, hi in ((0, 1), (5, 12), (10, 26), (30, 47), (40, 72), (50, 83), (100, 164),
+                   (200, 600), (0, 700)):
         part = bits(lp.score_ex(x[lo:hi].contiguous(), w, ids[lo:hi].contiguous(),
                                 bf16_logits=True))
         assert np.array_equal(part, full[lo:hi]), (lo, hi)

@@ -162,7 +162,9 @@ def test_qwen8b_shaped_parity_and_repeatability(qwen8b):
 
 # --------------------------------------------------------------------------
 # Batch invariance: 512 fixed probe rows at random positions inside batches
-# of 1, 7, 64, 512 and 8192 rows, twice each.
+# of 1, 7, 64, 512 and 8192 rows, twice each; 16, 17, 32 and 33 rows sit on
+# either side of the streaming kernels' item sizes (16 and 32 tokens in
+# registers, 64 through LDS).
 # --------------------------------------------------------------------------
 
 def test_batch_invariance_sweep(qwen8b):
@@ -172,13 +174,13 @@ def test_batch_invariance_sweep(qwen8b):
     fx, fids = synth.filler_rows(0, 8192, H, V)
     rng = np.random.default_rng(4)
     results = {}
-    for b in (1, 7, 64, 512, 8192):
+    for b in (1, 7, 16, 17, 32, 33, 64, 512, 8192):
         k = min(512, -(-b // 2))
         for rep in range(2):
             got = np.full(512, np.nan, np.float32)
             for start in range(0, 512, k):
-                probes = np.arange(start, start + k)
-                pos = rng.permutation(b)[:k]
+                probes = np.arange(start, min(start + k, 512))
+                pos = rng.permutation(b)[:len(probes)]
                 x = fx[rng.choice(8192, b, replace=False)].copy()
                 ids = fids[rng.choice(8192, b, replace=False)].copy()
                 x[pos], ids[pos] = px[probes], pids[probes]

@@ -141,13 +141,14 @@ def test_qwen17b_shaped_sampled_rows(qwen17b):
 
 
 def test_batch_invariance(qwen17b):
-    # 48 probe rows at random positions inside batches of 1, 7, 64 (streaming
-    # kernel) and 300, 4096 rows (352 x 256 tiles): bitwise equal outputs.
+    # 48 probe rows at random positions inside batches of 1, 7, 16, 17, 32,
+    # 33, 64 (streaming kernels: 16- and 32-token items in registers, 64 in
+    # LDS) and 300, 4096 rows (352 x 256 tiles): bitwise equal outputs.
     c, wd, _ = qwen17b
     rng = np.random.default_rng(9)
     probes = rng.choice(c.T, 48, replace=False)
     res = {}
-    for b in (1, 7, 64, 300, 4096):
+    for b in (1, 7, 16, 17, 32, 33, 64, 300, 4096):
         k = min(48, -(-b // 2))
         g = [np.zeros(48, np.float32), np.zeros(48, np.float32), np.zeros(48, np.int64)]
         for s in range(0, 48, k):
