@@ -67,8 +67,9 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="rows of the batch the fp64 oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep-n", type=str, default="512,4096",
-                    help="sequence counts of the comparison bandwidth probe (L = 2304)")
+    ap.add_argument("--sweep-n", type=str, default="512,4096,32768",
+                    help="sequence counts of the comparison bandwidth probe (L = 2304); the "
+                         "tail statistics and the correction are timed at N = 4096 when listed")
     ap.add_argument("--small-batches", type=str, default="1,7,64",
                     help="row counts at which lp_score is timed as a stream over W")
     ap.add_argument("--mode", choices=("bench", "score", "stats", "small", "compare", "copy"),
@@ -333,7 +334,7 @@ def main() -> int:
                       "frac_hbm": round(nbytes / med / 1e3 / PEAK_HBM_GBPS, 4),
                       "bytes_per_token": 13})
         log(f"bench: lp_compare N={sc.N} L={sc.L}: {med:.1f} us = {nbytes / med / 1e3:.1f} GB/s")
-        if sc.N == max(int(v) for v in args.sweep_n.split(",") if v):
+        if sc.N == 4096:
             # Batch tail statistics on the same arrays: 8 selection passes and
             # the position profile each read the 13 bytes of every position.
             tw = torch.empty(lp._lib.lib().lp_compare_tails_workspace_bytes(sc.N, sc.L),
