@@ -385,6 +385,21 @@ struct TailPart {    // one (sequence, pair), from pass 0
   int32_t count;
 };
 
+// x followed by y: sums added, counts added, the larger |delta| kept (equal
+// maxima keep the lower column). Every operation is commutative, so the two
+// lanes of a butterfly step get the same result.
+__device__ __forceinline__ TailPart tail_part_combine(TailPart x, const TailPart& y) {
+  x.sum_abs += y.sum_abs;
+  x.sum_prob += y.sum_prob;
+  x.count += y.count;
+  if (y.max_pos >= 0 &&
+      (x.max_pos < 0 || y.max_key > x.max_key || (y.max_key == x.max_key && y.max_pos < x.max_pos))) {
+    x.max_key = y.max_key;
+    x.max_pos = y.max_pos;
+  }
+  return x;
+}
+
 // After two passes each target's remaining candidates (the keys under its
 // 16-bit prefix) are few for continuous data; pass 2 copies them into a list
 // and passes 3 .. 7 read only the lists. Targets of one pair under one prefix
@@ -532,7 +547,7 @@ template <bool kVec, int kMode, int kTP>
 __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, TailWs w, int pass) {
   constexpr int kNT = 3 * kTP, kHW = kNT * 256;
   __shared__ uint32_t h[kHW];
-  __shared__ TailPart red[kMode == 0 ? 3 : 1][kMode == 0 ? kTailThreads : 1];
+  __shared__ TailPart red[kMode == 0 ? 3 : 1][kMode == 0 ? kTailThreads / 64 : 1];
   __shared__ uint32_t n_found[kNT];
   const int tid = threadIdx.x;
   const int shift = 56 - 8 * pass;  // this pass's byte: key bits [shift + 7 : shift]
@@ -658,30 +673,32 @@ __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, Ta
   }
   if (kMode != 0) return;
 
-  // Fixed tree over the threads; equal maxima keep the lower position.
+  // Fixed XOR butterfly within each wave, then the waves in order. Only the
+  // histogram and four partials per pair stay in LDS, so that more sequences'
+  // workgroups fit on a CU.
 #pragma unroll
-  for (int p = 0; p < 3; ++p) red[p][tid] = mine[p];
-  __syncthreads();
-  for (int stride = kTailThreads / 2; stride > 0; stride >>= 1) {
-    if (tid < stride) {
+  for (int p = 0; p < 3; ++p) {
+    TailPart x = mine[p];
 #pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        TailPart x = red[p][tid];
-        const TailPart y = red[p][tid + stride];
-        x.sum_abs += y.sum_abs;
-        x.sum_prob += y.sum_prob;
-        x.count += y.count;
-        if (y.max_pos >= 0 &&
-            (x.max_pos < 0 || y.max_key > x.max_key || (y.max_key == x.max_key && y.max_pos < x.max_pos))) {
-          x.max_key = y.max_key;
-          x.max_pos = y.max_pos;
-        }
-        red[p][tid] = x;
-      }
+    for (int m = 1; m < 64; m <<= 1) {
+      TailPart o;
+      o.sum_abs = __shfl_xor(x.sum_abs, m);
+      o.sum_prob = __shfl_xor(x.sum_prob, m);
+      o.max_key = (uint64_t)__shfl_xor((long long)x.max_key, m);
+      o.max_pos = __shfl_xor(x.max_pos, m);
+      o.count = __shfl_xor(x.count, m);
+      x = tail_part_combine(x, o);
     }
-    __syncthreads();
+    if (lane == 0) red[p][tid >> 6] = x;
+    __builtin_amdgcn_sched_barrier(0);  // one pair at a time: fewer live registers
   }
-  if (tid < 3) w.part[n * 3 + tid] = red[tid][0];
+  __syncthreads();
+  if (tid < 3) {
+    TailPart x = red[tid][0];
+#pragma unroll
+    for (int v = 1; v < kTailThreads / 64; ++v) x = tail_part_combine(x, red[tid][v]);
+    w.part[n * 3 + tid] = x;
+  }
 }
 
 // Offsets of each sequence's candidates within each list: an exclusive scan
