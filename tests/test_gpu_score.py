@@ -47,6 +47,9 @@ def test_tiny_full_parity(temperature):
     (300, 128, 400, 177, 128),      # tail one row into the second half of the first tile
     (300, 128, 704, 528, 128),      # tail exactly at a half boundary (528 = 352 + 176)
     (520, 64, 257, 1, 64),          # one-token vocabulary
+    (5, 128, 1000, 1000, 136),      # strided rows, register streaming kernel (16-token items)
+    (29, 64, 705, 700, 72),         # strided rows, register streaming kernel (32-token items)
+    (40, 192, 800, 777, 200),       # strided rows, LDS streaming kernel, tail in the upper half
 ])
 def test_ragged_shapes(T, H, V, v_true, ldh):
     c = synth.tiny_case(T=T, H=H, V=V, seed=T)
