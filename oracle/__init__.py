@@ -15,6 +15,7 @@ Every function cites the passage of the source pages it writes out:
 
 from .score import (bf16_bits_to_f64, score, score_stats, entropy_argmax, logits,  # noqa: F401
                     log_softmax_at, sharded_log_softmax_at, round_to_bf16)
-from .compare import (compare, per_token, tails, worst_tokens, nearest_rank, PAIRS,  # noqa: F401
+from .compare import (compare, per_token, tails, worst_tokens, quantile_linear, seq_quantiles,  # noqa: F401
+                      QUANTILE_PROBS, PAIRS,
                       STAT_FIELDS, TAIL_FIELDS)
 from .correct import correct, CORR_FIELDS, REJECT_NONE, REJECT_K1, REJECT_K3  # noqa: F401

@@ -156,28 +156,37 @@ def per_token(A, B, C, mask, tis_clip: float = 2.0) -> np.ndarray:
             finite = np.isfinite(l64) & np.isfinite(r64)
             d = r64 - l64
             vals = (np.abs(l64 - r64), np.expm1(d) - d, np.minimum(np.exp(d), tis_clip))
-        for j, v in enumerate(vals):
-            o = np.where(act & finite, v, np.where(act, np.nan, 0.0))
-            out[p, j] = o.astype(np.float32)
+            for j, v in enumerate(vals):
+                o = np.where(act & finite, v, np.where(act, np.nan, 0.0))
+                out[p, j] = o.astype(np.float32)    # k3 beyond fp32 range -> inf
     return out
 
 
 # ---------------------------------------------------------------------------
-# Batch tail statistics of |Delta| per pair (lp_compare_tails)
+# Tail statistics of |Delta| per pair (lp_compare_tails, lp_compare_quantiles)
 #
-#   [vLLM] §"Metric measurement basis": logprob_mae = sum(mask |lp_train -
+#   [AMD] "Check Whether the Pattern Extends Across the Response": p95 and p99
+#          are the 95th and 99th percentiles of the absolute error over the
+#          compared arrays, computed by the blog's compare() (section "Case 1:
+#          A Changes; B and C Stay Close") with numpy's np.quantile at its
+#          default settings; compare() takes one record's response-aligned
+#          arrays, and with a single active token every percentile is that
+#          token's |Delta|.
+#   [vLLM] "Metric measurement basis": logprob_mae = sum(mask |lp_train -
 #          lp_serve|) / sum(mask) over valid tokens, "also report p95/max and
 #          position"; probability_mae = mean |exp(lp_train) - exp(lp_serve)|
 #          over valid tokens.
 #   [VeX] section 5, its list of practical indicators: record the p50 / p95 /
 #          p99 / max of abs(delta_logprob).
 #
-# Over the whole batch, per pair, the tokens counted are the active ones whose
-# two scores are finite (non-finite ones are reported by compare()).
-#   count          number of such tokens
-#   q50, q95, q99  nearest-rank order statistics of |Delta|: the value at
-#                  1-based rank ceil(p n / 100) of the ascending sort (p = 50,
-#                  95, 99; the rank is formed in integers); 0 when n = 0
+# The tokens counted are the active ones whose two scores are finite
+# (non-finite ones are reported by compare()). Quantiles follow numpy's
+# default ("linear") rule, see quantile_linear(). tails() pools the whole
+# batch (a run's distribution); seq_quantiles() takes each sequence alone
+# (compare() applied to one record).
+#   count          number of counted tokens
+#   q50, q95, q99  quantile_linear of |Delta| at p = 0.5, 0.95, 0.99; 0 when
+#                  count == 0
 #   max_abs        max |Delta| (0 when n = 0)
 #   max_seq, max_pos  sequence and position (column) of the first token, in
 #                  row-major order, with |Delta| = max_abs (-1, -1 when n = 0)
@@ -190,15 +199,33 @@ def per_token(A, B, C, mask, tis_clip: float = 2.0) -> np.ndarray:
 
 TAIL_FIELDS = ("count", "q50", "q95", "q99", "max_abs", "max_seq", "max_pos",
                "sum_abs", "sum_prob_abs")
+QUANTILE_PROBS = (0.5, 0.95, 0.99)
 
 
-def nearest_rank(sorted_vals: np.ndarray, pct: int) -> float:
-    """Value at 1-based rank ceil(pct * n / 100) of an ascending array."""
+def quantile_linear(sorted_vals: np.ndarray, p: float) -> float:
+    """Quantile p of an ascending array by numpy's default ("linear") rule,
+    evaluated the way numpy evaluates it (fp64, no fused multiply-add).
+
+    With n values x_0 <= ... <= x_{n-1}: the virtual index is h = (n - 1) p
+    (one fp64 product); when h >= n - 1 the result is x_{n-1}; otherwise,
+    with j = floor(h) and g = h - j, it interpolates between a = x_j and
+    b = x_{j+1}: a + (b - a) g when g < 0.5, else b - (b - a)(1 - g) (the
+    same line taken from its nearer end). An empty array gives 0.
+    """
     n = sorted_vals.size
     if n == 0:
         return 0.0
-    rank = (pct * n + 99) // 100
-    return float(sorted_vals[rank - 1])
+    h = float(n - 1) * float(p)
+    j = math.floor(h)
+    if h >= n - 1:
+        return float(sorted_vals[n - 1])
+    g = h - j
+    a = float(sorted_vals[j])
+    b = float(sorted_vals[j + 1])
+    diff = b - a
+    if g < 0.5:
+        return a + diff * g
+    return b - diff * (1.0 - g)
 
 
 def tails(A, B, C, mask):
@@ -218,8 +245,8 @@ def tails(A, B, C, mask):
         vals = delta[keep]                       # row-major order
         srt = np.sort(vals)
         rec = {"count": int(vals.size)}
-        for pct in (50, 95, 99):
-            rec[f"q{pct}"] = nearest_rank(srt, pct)
+        for name, prob in zip(("q50", "q95", "q99"), QUANTILE_PROBS):
+            rec[name] = quantile_linear(srt, prob)
         if vals.size:
             mx = float(vals.max())
             seqs, poss = np.nonzero(keep & (delta == mx))
@@ -235,6 +262,29 @@ def tails(A, B, C, mask):
             pos_sum[p, i] = math.fsum(col.tolist())
             pos_count[p, i] = col.size
     return out, pos_sum, pos_count
+
+
+def seq_quantiles(A, B, C, mask) -> dict:
+    """Per pair and sequence, quantile_linear of |Delta| over the sequence's
+    counted tokens at p = 0.5, 0.95, 0.99: {"AB"|"BC"|"AC": float64 [N, 3]}
+    (0 for a sequence without counted tokens). [AMD] compare() applied to
+    one record's arrays."""
+    A, B, C, mask = _check(A, B, C, mask)
+    sides = {"A": A, "B": B, "C": C}
+    N = A.shape[0]
+    out = {}
+    for ln, rn in PAIRS:
+        left = sides[ln].astype(np.float64)
+        right = sides[rn].astype(np.float64)
+        keep = (mask != 0) & np.isfinite(left) & np.isfinite(right)
+        delta = np.abs(left - right)
+        q = np.zeros((N, 3))
+        for n in range(N):
+            srt = np.sort(delta[n][keep[n]])
+            for j, p in enumerate(QUANTILE_PROBS):
+                q[n, j] = quantile_linear(srt, p)
+        out[ln + rn] = q
+    return out
 
 
 def worst_tokens(A, B, C, mask, k: int):

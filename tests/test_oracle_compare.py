@@ -262,6 +262,90 @@ def test_per_token_layout(record):
             assert abs(row.sum() - res[name]["sum_abs"][n]) <= 1e-5 * max(1, res[name]["sum_abs"][n])
 
 
+def _brute_token(left: float, right: float, clip: float):
+    """One token's per-token values in Python floats, from the definitions:
+    |left - right|, k3 = expm1(d) - d and min(e^d, C) with d = right - left."""
+    d = right - left
+    k3 = math.expm1(d) - d if d < 709.0 else math.inf
+    tis = clip if d >= math.log(clip) else min(math.exp(d), clip)
+    return abs(left - right), k3, tis
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_per_token_columns_brute_force(seed):
+    # Every column of every pair against a token-by-token recount: catches a
+    # flipped d, swapped columns, a missing clip or a k3 without its -d.
+    rng = np.random.default_rng(40 + seed)
+    N, L = 4, 33
+    B = rng.uniform(-12, 0, (N, L)).astype(f32)
+    A = (B + rng.normal(0, 0.3, (N, L))).astype(f32)
+    C = (B + rng.normal(0, 0.8, (N, L))).astype(f32)
+    A[0, 3] = B[0, 3] + 2.5                       # |d| >= ln 2: the clip decides
+    C[1, 4] = np.nan
+    mask = (rng.random((N, L)) < 0.75).astype(np.uint8)
+    clip = 2.0 if seed != 2 else 1.25
+    pt = oracle.per_token(A, B, C, mask, tis_clip=clip)
+    arr = {"A": A, "B": B, "C": C}
+    for p, (ln, rn) in enumerate(oracle.PAIRS):
+        for n in range(N):
+            for i in range(L):
+                l, r = float(arr[ln][n, i]), float(arr[rn][n, i])
+                got = pt[p, :, n, i]
+                if not mask[n, i]:
+                    assert got.tolist() == [0.0, 0.0, 0.0]
+                elif not (math.isfinite(l) and math.isfinite(r)):
+                    assert np.isnan(got).all()
+                else:
+                    want = np.array(_brute_token(l, r, clip), np.float64).astype(f32)
+                    assert got.tolist() == want.tolist(), (ln + rn, n, i, got, want)
+
+
+def test_per_token_ratio_example(golden_dir):
+    # [AMD] "What a Logprob Difference Means": 0.10 -> 0.12 is a ratio of 1.2;
+    # left = rollout, right = trainer, so k3 = r - 1 - ln r and TIS = r.
+    g = json.load(open(os.path.join(golden_dir, "ratio_example.json")))
+    lr = f32(math.log(g["rollout_probability"]))
+    lt = f32(math.log(g["trainer_probability"]))
+    a = np.array([[lr]], f32)
+    b = np.array([[lt]], f32)
+    pt = oracle.per_token(a, b, b, np.ones((1, 1), np.uint8))
+    r = g["trainer_probability"] / g["rollout_probability"]
+    assert abs(float(pt[0, 0, 0, 0]) - math.log(r)) < 1e-6
+    assert abs(float(pt[0, 1, 0, 0]) - (r - 1 - math.log(r))) < 1e-7   # 0.01768, not 0.01565
+    assert abs(float(pt[0, 2, 0, 0]) - r) < 1e-6
+    assert round(float(pt[0, 2, 0, 0]), 2) == g["printed"]["probability_ratio"]
+    # The reverse orientation gives the other k3 (1/r - 1 + ln r): not this.
+    assert abs(float(pt[0, 1, 0, 0]) - (1 / r - 1 + math.log(r))) > 1e-3
+
+
+def test_per_token_overflow_and_clip_closed_forms():
+    # d = +100: e^d overflows fp32, k3 = e^100 - 101 -> inf in fp32, TIS = C.
+    # d = -100: k3 = e^-100 + 99 -> 99.0 exactly in fp32, TIS = e^-100 (a
+    # subnormal fp32). d = ln 3 > ln 2: TIS = 2 exactly, k3 = 2 - ln 3.
+    left = np.array([[0.0, 0.0, 0.0]], f32)
+    right = np.array([[100.0, -100.0, f32(math.log(3.0))]], f32)
+    pt = oracle.per_token(left, right, right, np.ones((1, 3), np.uint8))
+    k3, tis = pt[0, 1, 0], pt[0, 2, 0]
+    assert np.isinf(k3[0]) and k3[0] > 0 and tis[0] == 2.0
+    assert k3[1] == 99.0 and tis[1] == f32(math.exp(-100.0)) and tis[1] > 0
+    d = float(f32(math.log(3.0)))
+    assert tis[2] == 2.0 and abs(float(k3[2]) - (math.exp(d) - 1 - d)) < 1e-6
+
+
+def test_per_token_sums_match_compare(record):
+    # per_token() and compare() are written apart: their k3 and TIS agree.
+    C = synth.noise_scores(record.C, record.mask, 1e-2, seed=5)
+    pt = oracle.per_token(record.A, record.B, C, record.mask)
+    res = oracle.compare(record.A, record.B, C, record.mask)
+    act = record.mask != 0
+    for p, name in enumerate(("AB", "BC", "AC")):
+        for n in range(record.N):
+            k3 = pt[p, 1, n][act[n]].astype(np.float64)
+            tis = pt[p, 2, n][act[n]].astype(np.float64)
+            assert abs(math.fsum(k3) - res[name]["sum_k3"][n]) <= 1e-6 * max(1e-9, res[name]["sum_k3"][n]) + 1e-12
+            assert abs(math.fsum(tis) - res[name]["sum_tok_tis"][n]) <= 1e-6 * max(1.0, res[name]["sum_tok_tis"][n])
+
+
 def test_rejects_bad_arguments():
     a = np.zeros((2, 3), f32)
     with pytest.raises(ValueError):

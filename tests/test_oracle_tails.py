@@ -1,8 +1,10 @@
-"""Pins for the oracle's batch tail statistics (CPU only): the nearest-rank
-quantile against numpy's inverted-CDF percentile, hand-counted ranks, closed
-forms for identical and offset scores, the probability difference of the
-AMD blog's worked example, first-occurrence maxima and position profiles that
-add up to the batch totals."""
+"""Pins for the oracle's tail statistics (CPU only): the quantile rule
+against numpy's np.quantile at its default settings (the estimator the AMD
+blog's compare() uses) on random and heavily tied data, hand-worked lists,
+the one-token and two-token cases, closed forms for identical and offset
+scores, the probability difference of the AMD blog's worked example,
+first-occurrence maxima, position profiles that add up to the batch totals,
+and per-sequence quantiles against np.quantile on each record alone."""
 
 import json
 import math
@@ -14,26 +16,62 @@ import pytest
 import oracle
 from workloads import synth
 
+PROBS = oracle.QUANTILE_PROBS
 
-@pytest.mark.parametrize("seed", range(6))
-def test_nearest_rank_is_the_inverted_cdf_percentile(seed):
+
+@pytest.mark.parametrize("seed", range(8))
+def test_quantile_rule_is_numpys_default(seed):
+    # [AMD] "Case 1: A Changes; B and C Stay Close": compare() returns
+    # np.quantile(error, .95) and np.quantile(error, .99); numpy's routine on
+    # the same sorted values must give the same bits.
     rng = np.random.default_rng(seed)
-    n = int(rng.integers(1, 400))
-    vals = np.sort(np.abs(rng.standard_normal(n)) * 10.0 ** rng.integers(-6, 2, n))
+    n = int(rng.integers(1, 700))
+    vals = np.abs(rng.standard_normal(n)) * 10.0 ** rng.integers(-6, 2, n)
     if seed % 2:
-        vals = np.sort(np.round(vals, 1))            # many ties
-    for pct in (50, 95, 99):
-        assert oracle.nearest_rank(vals, pct) == np.percentile(vals, pct, method="inverted_cdf")
+        vals = np.round(vals, 1)                     # many ties
+    if seed % 4 == 3:
+        vals[: n // 2] = 0.0                         # a block of exact zeros
+    srt = np.sort(vals)
+    for p in PROBS + (0.0, 0.25, 0.75, 1.0):
+        got = oracle.quantile_linear(srt, p)
+        ref = float(np.quantile(vals, p))
+        assert got == ref, (n, p, got, ref)
+        assert float(np.percentile(vals, 100 * p)) == pytest.approx(got, rel=1e-15, abs=0)
 
 
-def test_hand_counted_ranks():
-    v = np.array([0.0, 1.0, 2.0, 3.0])
-    assert oracle.nearest_rank(v, 50) == 1.0          # rank ceil(2)   = 2
-    assert oracle.nearest_rank(v, 95) == 3.0          # rank ceil(3.8) = 4
-    v20 = np.arange(20.0)
-    assert oracle.nearest_rank(v20, 95) == 18.0       # rank 95*20/100 = 19 exactly
-    assert oracle.nearest_rank(v20, 99) == 19.0       # rank ceil(19.8) = 20
-    assert oracle.nearest_rank(np.zeros(0), 50) == 0.0
+def test_hand_worked_lists():
+    v = np.array([0.0, 1.0, 2.0, 3.0])               # h = 3p
+    assert oracle.quantile_linear(v, 0.5) == 1.5
+    assert abs(oracle.quantile_linear(v, 0.95) - 2.85) < 1e-15
+    assert abs(oracle.quantile_linear(v, 0.99) - 2.97) < 1e-15
+    v5 = np.array([10.0, 20.0, 30.0, 40.0, 50.0])    # h = 4p: 2, 3.8, 3.96
+    assert oracle.quantile_linear(v5, 0.5) == 30.0
+    assert abs(oracle.quantile_linear(v5, 0.95) - 48.0) < 1e-12
+    assert abs(oracle.quantile_linear(v5, 0.99) - 49.6) < 1e-12
+    v20 = np.arange(20.0)                             # h = 19p: 9.5, 18.05, 18.81
+    assert oracle.quantile_linear(v20, 0.5) == 9.5
+    assert abs(oracle.quantile_linear(v20, 0.95) - 18.05) < 1e-12
+    assert abs(oracle.quantile_linear(v20, 0.99) - 18.81) < 1e-12
+    assert oracle.quantile_linear(np.zeros(0), 0.5) == 0.0
+
+
+def test_one_and_two_tokens():
+    # The blog: with one active token every percentile equals its |Delta|.
+    for x in (0.0, 2.0 ** -23, 0.017098, 5.5):
+        for p in PROBS:
+            assert oracle.quantile_linear(np.array([x]), p) == x
+    # Two values: the straight line between them, q_p = a + p (b - a).
+    a, b = 0.25, 1.75
+    for p in PROBS:
+        assert abs(oracle.quantile_linear(np.array([a, b]), p) - (a + p * (b - a))) < 1e-15
+
+
+def test_quantile_is_monotone_and_bounded():
+    rng = np.random.default_rng(11)
+    srt = np.sort(np.abs(rng.standard_normal(333)))
+    qs = [oracle.quantile_linear(srt, p) for p in np.linspace(0, 1, 101)]
+    assert all(x <= y for x, y in zip(qs, qs[1:]))
+    assert qs[0] == srt[0] and qs[-1] == srt[-1]
 
 
 def test_identical_scores_closed_form():
@@ -65,9 +103,16 @@ def test_offset_closed_form():
     n = d.size
     srt = np.sort(d)
     assert t["AB"]["count"] == n and np.count_nonzero(srt == 0) == 6
-    for pct in (50, 95, 99):
-        rank = -(-pct * n // 100)
-        assert t["AB"][f"q{pct}"] == srt[rank - 1] and srt[rank - 1] > 0.09
+    # Six zeros then n - 6 tokens at 0.10 rounded through fp32 scores: every
+    # quantile's two neighbours lie among the offsets (h = (n - 1) p >= 6), so
+    # each quantile lies within the offsets' range, one fp32 rounding of 0.10.
+    offs = np.unique(srt[6:])
+    assert np.all(np.abs(offs - 0.10) < 4e-6)
+    for name, p in zip(("q50", "q95", "q99"), PROBS):
+        j = math.floor((n - 1) * p)
+        assert j >= 6
+        assert offs[0] <= t["AB"][name] <= offs[-1]
+        assert t["AB"][name] == float(np.quantile(d, p))
     assert t["BC"]["max_abs"] == 0.0 and t["AC"]["max_abs"] == t["AB"]["max_abs"]
 
 
@@ -171,3 +216,51 @@ def test_worst_ties_follow_row_major_order():
     w = oracle.worst_tokens(A, B, B.copy(), mask, 4)["AB"]
     assert w == [(0.75, 1, 4), (0.5, 0, 1), (0.5, 0, 3), (0.5, 1, 0)]
     assert oracle.worst_tokens(A, B, B.copy(), mask, 40)["BC"][:2] == [(0.0, 0, 0), (0.0, 0, 1)]
+
+
+# ---------------------------------------------------------------------------
+# Per-sequence quantiles: the blog's compare() on one record's arrays.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(3))
+def test_seq_quantiles_are_np_quantile_per_record(seed):
+    r = synth.compare_case(N=6, max_resp=300, prompt=16, seed=20 + seed)
+    C = synth.noise_scores(r.C, r.mask, 1e-3, seed=seed)
+    A = r.A.copy()
+    A[1, 20] = np.nan                                  # not counted
+    mask = r.mask.copy()
+    mask[2, 16:40] = 0                                 # a hole in the record
+    q = oracle.seq_quantiles(A, r.B, C, mask)
+    sides = {"A": A, "B": r.B, "C": C}
+    for ln, rn in oracle.PAIRS:
+        for n in range(A.shape[0]):
+            left = sides[ln][n].astype(np.float64)
+            right = sides[rn][n].astype(np.float64)
+            keep = (mask[n] != 0) & np.isfinite(left) & np.isfinite(right)
+            err = np.abs(left[keep] - right[keep])
+            want = [float(np.quantile(err, p)) for p in PROBS] if err.size else [0.0] * 3
+            assert q[ln + rn][n].tolist() == want, (ln + rn, n)
+
+
+def test_seq_quantiles_worked_token(golden_dir):
+    # One active token (the blog's outlier): p50 = p95 = p99 = |A - B0|.
+    g = json.load(open(os.path.join(golden_dir, "amd_worked_token.json")))["scores"]
+    A = np.array([[np.float32(g["A"]), 0.0]], np.float32)
+    B = np.array([[np.float32(g["B0"]), 5.0]], np.float32)
+    mask = np.array([[1, 0]], np.uint8)
+    q = oracle.seq_quantiles(A, B, B, mask)["AB"][0]
+    d = abs(float(np.float32(g["A"])) - float(np.float32(g["B0"])))
+    assert q.tolist() == [d, d, d] and f"{d:.6f}" == "0.017098"
+    q0 = oracle.seq_quantiles(A, B, B, np.zeros((1, 2), np.uint8))["AB"][0]
+    assert q0.tolist() == [0.0, 0.0, 0.0]
+
+
+def test_batch_quantiles_pool_the_records():
+    # The batch quantile is the quantile of all records' counted tokens
+    # together, not a mean of per-record quantiles.
+    r = synth.compare_case(N=5, max_resp=200, prompt=8, seed=31)
+    C = synth.noise_scores(r.C, r.mask, 1e-2, seed=31)
+    t, _, _ = oracle.tails(r.A, r.B, C, r.mask)
+    d = np.abs(r.B.astype(np.float64) - C.astype(np.float64))[r.mask != 0]
+    for name, p in zip(("q50", "q95", "q99"), PROBS):
+        assert t["BC"][name] == float(np.quantile(d, p))
