@@ -67,6 +67,8 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="rows of the batch the fp64 oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-qwen17b", action="store_true",
+                    help="skip the Qwen3-1.7B-shaped (H=2048) scoring record")
     ap.add_argument("--sweep-n", type=str, default="512,4096,32768",
                     help="sequence counts of the comparison bandwidth probe (L = 2304); the "
                          "tail statistics and the correction are timed at N = 4096 when listed")
@@ -301,6 +303,52 @@ def main() -> int:
         f"merge {mg_med:.1f} us; bitwise equal to lp_score")
     del parts, shards
 
+    # Qwen3-1.7B-shaped scoring: T = 4096 (8 x 512), H = 2048, V = 151 936, at
+    # temperatures 1.0 and 0.7; fp64 oracle parity on every row (outside the
+    # timed region, the logits formed once per 512-row block for both
+    # temperatures).
+    q17 = None
+    if not args.no_qwen17b:
+        T2, H2 = 4096, 2048
+        w2_bits = synth.qwen_weight(H2, V)
+        c2 = synth.qwen_case(T=T2, H=H2, V=V, w_bits=w2_bits)
+        x2, w2 = bf16(c2.x_bits), bf16(w2_bits)
+        ids2 = torch.from_numpy(c2.ids).to(dev)
+        ws2 = torch.empty(lp.score_workspace_bytes(T2, H2, V), dtype=torch.uint8, device=dev)
+        flops2 = 2.0 * T2 * H2 * V
+        q17 = {"T": T2, "H": H2, "V": V, "runs": []}
+        outs2 = {}
+        for temp in (1.0, 0.7):
+            o2 = torch.empty(T2, dtype=torch.float32, device=dev)
+            med, lo, hi = median_us(lambda: lp.score(x2, w2, ids2, temp, out=o2, workspace=ws2),
+                                    calls=5, reps=5)
+            torch.cuda.synchronize()
+            outs2[temp] = o2.cpu().numpy().astype(np.float64)
+            q17["runs"].append({"temperature": temp, "ms": round(med / 1e3, 4),
+                                "min_ms": round(lo / 1e3, 4), "max_ms": round(hi / 1e3, 4),
+                                "tokens_per_s": round(T2 / (med / 1e6), 1),
+                                "TFLOPs": round(flops2 / med / 1e6, 2),
+                                "frac": round(flops2 / med / 1e6 / PEAK_BF16_TFLOPS, 4)})
+            log(f"bench: Qwen3-1.7B shape T={T2} H={H2} temperature {temp}: {med / 1e3:.3f} ms = "
+                f"{flops2 / med / 1e6:.1f} TFLOP/s")
+        if not args.no_cpu_baseline:
+            import oracle
+            errs = {t: 0.0 for t in outs2}
+            for r0 in range(0, T2, 512):
+                z = oracle.logits(c2.x_bits[r0:r0 + 512], w2_bits)
+                for temp in outs2:
+                    ref2, _ = oracle.log_softmax_at(z, c2.ids[r0:r0 + 512], temp)
+                    errs[temp] = max(errs[temp],
+                                     float(np.max(np.abs(outs2[temp][r0:r0 + 512] - ref2))))
+                del z
+            for run in q17["runs"]:
+                e = errs[run["temperature"]]
+                run["parity"] = {"rows": T2, "max_abs_diff_nats": e, "within_tolerance": e <= 1e-3}
+                log(f"bench: Qwen3-1.7B shape temperature {run['temperature']}: max |lp_score - "
+                    f"fp64 oracle| over {T2} rows = {e:.3e} nats")
+                assert e <= 1e-3, "Qwen3-1.7B-shaped parity outside 1e-3 nats"
+        del x2, w2, ids2, ws2
+
     # Small batches: the product is a stream over W (HBM-bound); report the
     # algorithmic bytes (W, the rows, ids and outputs) per second.
     small = []
@@ -369,6 +417,19 @@ def main() -> int:
             tails_rec["worst_k"] = kw
             tails_rec["with_worst_us"] = round(wmed, 2)
             log(f"bench: lp_compare_tails_ex (16 worst tokens per pair): {wmed:.1f} us")
+            # Per-sequence p50 / p95 / p99 (lp_compare_quantiles): one read of
+            # the 13 bytes of every position, selection in LDS.
+            qout = torch.empty((3, sc.N, 3), dtype=torch.float64, device=dev)
+            qargs = (tA.data_ptr(), tB.data_ptr(), tC.data_ptr(), tM.data_ptr(), sc.N, sc.L,
+                     sc.L, qout.data_ptr(), torch.cuda.current_stream().cuda_stream)
+            c_quant = lp._lib.lib().lp_compare_quantiles
+            qmed, qlo, qhi = median_us(lambda: c_quant(*qargs), calls=5, reps=5)
+            qbytes = 13.0 * sc.N * sc.L
+            tails_rec["seq_quantiles_us"] = round(qmed, 2)
+            tails_rec["seq_quantiles_GBps"] = round(qbytes / qmed / 1e3, 1)
+            log(f"bench: lp_compare_quantiles N={sc.N} L={sc.L}: {qmed:.1f} us "
+                f"({qbytes / qmed / 1e3:.1f} GB/s over one read)")
+            del qout
             # Correction consumer on the same arrays: rollout = A, trainer = C;
             # TIS cap, MIS interval and K3 rejection, weights written. Bytes:
             # 2 x fp32 + mask read, fp32 weight written per position.
@@ -467,6 +528,7 @@ def main() -> int:
         "score_stats": stats_rec,
         "score_bf16_logits": bf16_rec,
         "vocab_parallel": shard_rec,
+        "qwen3_1_7b_shape": q17,
         "small_batch": small,
         "compare_sweep": sweep,
         "compare_tails": tails_rec,

@@ -83,8 +83,11 @@ const char* lp_status_string(lp_status status);
  * Errors: LP_EINVAL for T < 0, H < 1, V_rows < 1, V_true outside
  * [1, V_rows], ldh < H, a temperature that is not finite and > 0, a NULL
  * required pointer, or a workspace that is too small or misaligned.
- * LP_EUNSUPPORTED for H % 64 != 0, ldh % 8 != 0 or misaligned hidden/w, and
- * for sizes whose index arithmetic would overflow 32-bit tile counters.
+ * LP_EUNSUPPORTED for H % 64 != 0, ldh % 8 != 0 or misaligned hidden/w; for
+ * sizes whose index arithmetic would overflow 32-bit tile counters; and for
+ * strides the kernels' 32-bit buffer addressing cannot span: 255 * ldh * 2 +
+ * 2 * H or 352 * 2 * H above 0x7FFFFFF0 bytes (at H = 64 the largest
+ * accepted ldh is 4 210 744; the largest accepted H is 3 050 368).
  * T == 0 is a no-op returning LP_OK.
  * ------------------------------------------------------------------------ */
 size_t lp_score_workspace_bytes(int64_t T, int64_t H, int64_t V_rows,
@@ -201,6 +204,14 @@ lp_status lp_score_ex(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
  *
  * Integer fields and max_abs are exact. The fp64 sums are taken in a fixed
  * order, so they are bitwise reproducible run to run and independent of N.
+ * Precision of the k3 and TIS terms: for |d_i| < 0.5 a token's k3 and
+ * exp(d_i) are evaluated in fp32 (k3 by its Taylor series to d^9 / 9!, no
+ * cancellation; exp by the hardware exp2) and added to fp64 sums, which
+ * agree with the exactly rounded sums to about 1e-7 relative (the library's
+ * tests hold them to 1e-6); for |d_i| >= 0.5 both come from one fp64
+ * exponential, k3 = (e^d - 1) - d. The per-token k3 and TIS outputs carry
+ * the same precision. sum_abs, sum_signed, sum_d and seq_tis are fp64 from
+ * the fp64 differences (1e-9 relative is asserted).
  *
  * Layout:
  *   gen_A, replay_B, train_C  [N, L] fp32, row stride ld elements (ld >= L).
@@ -237,16 +248,58 @@ lp_status lp_compare(const float* gen_A, const float* replay_B,
                      lp_seq_stats* out, float* per_token, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Quantiles of |Delta|: the rule used throughout
+ *
+ * p50, p95 and p99 follow numpy's default ("linear") quantile, the estimator
+ * of the AMD blog's compare() (section "Case 1: A Changes; B and C Stay
+ * Close", np.quantile(error, .95) and .99; the p95 / p99 row of "Check
+ * Whether the Pattern Extends Across the Response" refers to it). Over n
+ * counted values sorted ascending, x_0 <= ... <= x_{n-1}, and p = 0.5, 0.95,
+ * 0.99: h = (n - 1) * p (one fp64 product); if h >= n - 1 the quantile is
+ * x_{n-1}; otherwise, with j = floor(h), g = h - j, a = x_j, b = x_{j+1}:
+ *   q = a + (b - a) * g          when g < 0.5
+ *   q = b - (b - a) * (1 - g)    otherwise
+ * each fp64 operation rounded on its own -- the bits np.quantile returns.
+ * x_j and x_{j+1} are selected exactly (radix selection on the bit patterns
+ * of |Delta|); 0 when n == 0.
+ * ------------------------------------------------------------------------ */
+
+/* ------------------------------------------------------------------------
+ * Per-sequence quantiles: the blog's compare() applied to each record
+ *
+ * For each pair p (0: (A,B), 1: (B,C), 2: (A,C)) and sequence n, over the
+ * sequence's counted tokens (active and both scores finite, Delta as for
+ * lp_compare): out[(p * N + n) * 3 + j] = the quantile of |Delta| at
+ * p = 0.5, 0.95, 0.99 for j = 0, 1, 2 (the rule above; 0 for a sequence
+ * without counted tokens). Together with lp_compare's count, signed sum,
+ * |Delta| sum and max_abs this is every field the AMD blog's compare()
+ * returns, per record. With one counted token every quantile is its |Delta|.
+ *
+ * Layout and arguments as for lp_compare; out: [3][N][3] double in device
+ * memory, 8-byte aligned. No workspace: each (sequence, pair) is selected
+ * inside one workgroup. Exact and independent of N and of scheduling.
+ *
+ * Errors: LP_EINVAL for N < 0, L < 0, ld < L, a NULL or misaligned out, or
+ * NULL inputs with N, L > 0; LP_EUNSUPPORTED for N or L above INT32_MAX.
+ * N == 0 does nothing; L == 0 writes zeros.
+ * ------------------------------------------------------------------------ */
+lp_status lp_compare_quantiles(const float* gen_A, const float* replay_B,
+                               const float* train_C, const uint8_t* mask,
+                               int64_t N, int64_t L, int64_t ld, double* out,
+                               hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Batch tail statistics of the per-token differences
  *
  * For each pair (A,B), (B,C), (A,C) over the whole batch: the counted tokens
  * are the active ones whose two scores are finite, Delta as for lp_compare.
+ * The batch pools every sequence's tokens: a run's distribution, which the
+ * blog characterises from full response arrays.
  *
  *   count          number of counted tokens
- *   q50, q95, q99  nearest-rank order statistics of |Delta|: the value at
- *                  1-based rank ceil(p * count / 100) of the ascending order
- *                  (p = 50, 95, 99); exact (a selection, not an estimate);
- *                  0 when count == 0
+ *   q50, q95, q99  quantiles of |Delta| over all counted tokens, by the rule
+ *                  above (exact neighbours, fp64 interpolation); 0 when
+ *                  count == 0
  *   max_abs        max |Delta| (0 when count == 0)
  *   max_seq, max_pos  sequence and column of the first counted token, in
  *                  row-major order, with |Delta| = max_abs (-1 when none)
@@ -255,14 +308,16 @@ lp_status lp_compare(const float* gen_A, const float* replay_B,
  *
  * [vLLM] "Metric measurement basis" (logprob_mae with its p95, max and
  * position; probability_mae); [VeX] section 5, practical indicators (p50 /
- * p95 / p99 / max of abs(delta_logprob)).
+ * p95 / p99 / max of abs(delta_logprob)); [AMD] "Check Whether the Pattern
+ * Extends Across the Response" (p95, p99, maximum, error by position).
  *
  * pos_abs_sum / pos_count (both NULL or both non-NULL): [3][L] arrays, pair-
  * major; for column i, the sum of |Delta| over the sequences whose token i
  * is counted, and how many are -- the error-by-position profile.
  *
- * Integer results and the quantile and max values are exact; the fp64 sums
- * are taken in a fixed order (bitwise reproducible run to run).
+ * Integer results, max values and the quantiles' order statistics are
+ * exact, and the quantiles are np.quantile's bits; the fp64 sums are taken
+ * in a fixed order (bitwise reproducible run to run).
  *
  * Layout and arguments as for lp_compare; out is [3] lp_tail_stats in device
  * memory; workspace: lp_compare_tails_workspace_bytes(N, L) bytes, 256-byte

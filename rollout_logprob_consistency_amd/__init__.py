@@ -11,6 +11,7 @@ streams.
     score_stats(hidden, w, ids, ...)                      -> logprob, entropy, argmax
     score_ex(hidden, w, ids, ..., stats, bf16_logits)     -> either, optionally bf16 logits
     compare(A, B, C, mask, tis_clip=2.0, atol=None)       -> stats per pair
+    compare_quantiles(A, B, C, mask)                      -> p50/p95/p99 per pair and sequence
     compare_tails(A, B, C, mask, positions=False)         -> batch tails per pair
     vocab_shard / score_shard / merge_shards              -> vocabulary-parallel scoring
     correct(rollout, train, mask, ...)                    -> TIS/MIS weights, rejection
@@ -222,9 +223,13 @@ def compare(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch.Tenso
             check: bool = True):
     """Three-way comparison; synchronises and returns per-pair statistics.
 
-    Like the AMD blog's compare(), with check=True it raises ValueError when a
-    sequence has no active token or an active score is non-finite.
+    Like the AMD blog's compare(), with check=True it raises ValueError when
+    the mask holds a value other than 0 or 1, a sequence has no active token
+    or an active score is non-finite. With check=False any non-zero mask
+    byte is active (the library's rule).
     """
+    if check and mask.numel() and bool(((mask != 0) & (mask != 1)).any()):
+        raise ValueError("mask values must be 0 or 1")
     raw, pt = compare_raw(A, B, C, mask, tis_clip, atol, per_token)
     stats = stats_from_bytes(raw, A.shape[0])
     if check:
@@ -235,6 +240,43 @@ def compare(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch.Tenso
             if np.any(stats[p]["nonfinite"] > 0):
                 raise ValueError(f"non-finite score on an active token ({p})")
     return (stats, pt) if per_token else stats
+
+
+def _check_compare_inputs(A, B, C, mask):
+    for name, t in (("A", A), ("B", B), ("C", C)):
+        _need_cuda(name, t, torch.float32)
+    _need_cuda("mask", mask, torch.uint8)
+    if not (A.shape == B.shape == C.shape == mask.shape) or A.dim() != 2:
+        raise ValueError("A, B, C and mask must share one [N, L] shape")
+    N, L = A.shape
+    ld = A.stride(0) if A.numel() else L
+    for t in (A, B, C, mask):
+        if t.numel() and (t.stride(1) != 1 or (N > 1 and t.stride(0) != ld)):
+            raise ValueError("A, B, C and mask need unit column stride and one row stride")
+    return N, L, max(ld, L)
+
+
+def compare_quantiles(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch.Tensor,
+                      *, out: torch.Tensor | None = None, sync: bool = True):
+    """p50 / p95 / p99 of |left - right| per pair and sequence
+    (lp_compare_quantiles): numpy's default quantile over each sequence's
+    counted tokens, as the AMD blog's compare() returns for one record.
+    Returns {"AB"|"BC"|"AC": numpy float64 [N, 3]} (sync=True), else the
+    [3, N, 3] float64 device tensor without synchronising."""
+    N, L, ld = _check_compare_inputs(A, B, C, mask)
+    dev = A.device
+    if out is None:
+        out = torch.empty((3, N, 3), dtype=torch.float64, device=dev)
+    elif out.dtype != torch.float64 or not out.is_contiguous() or out.numel() < 9 * N:
+        raise ValueError("out must be a contiguous float64 tensor of 3 * N * 3 values")
+    st = lib().lp_compare_quantiles(_ptr(A), _ptr(B), _ptr(C), _ptr(mask), N, L, ld, _ptr(out),
+                                    _stream(dev))
+    if st != LP_OK:
+        raise LpError(st, "lp_compare_quantiles")
+    if not sync:
+        return out
+    q = out.reshape(3, N, 3).cpu().numpy()
+    return {p: q[i] for i, p in enumerate(PAIRS)}
 
 
 def compare_tails(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch.Tensor,
@@ -410,8 +452,11 @@ def align(hidden: torch.Tensor, input_ids: torch.Tensor, response_mask: torch.Te
     if hidden.dim() != 3 or input_ids.shape != hidden.shape[:2] or \
             response_mask.shape != input_ids.shape:
         raise ValueError("expected hidden [B, S, H], input_ids and response_mask [B, S]")
+    if bool(((response_mask != 0) & (response_mask != 1)).any()):
+        raise ValueError("response_mask values must be 0 or 1")
     if bool((response_mask[:, 0] != 0).any()):
-        raise ValueError("no preceding prediction row for input position zero")
+        raise ValueError("response_mask[:, 0] must be 0: nothing before the first "
+                         "position predicts it")
     B, S, H = hidden.shape
     targets = torch.zeros_like(input_ids, dtype=torch.int64)
     targets[:, :-1] = input_ids[:, 1:]

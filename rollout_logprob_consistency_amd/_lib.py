@@ -22,7 +22,8 @@ EXPORTS = ("lp_status_string", "lp_score_workspace_bytes", "lp_score",
            "lp_vocab_shard_range", "lp_shard_partials_bytes",
            "lp_score_shard_workspace_bytes", "lp_score_shard", "lp_merge_shards",
            "lp_correct", "lp_score_ex_workspace_bytes", "lp_score_ex",
-           "lp_compare_tails_ex_workspace_bytes", "lp_compare_tails_ex")
+           "lp_compare_tails_ex_workspace_bytes", "lp_compare_tails_ex",
+           "lp_compare_quantiles")
 
 REJECT_NONE, REJECT_K1, REJECT_K3 = 0, 1, 3  # LP_REJECT_*
 
@@ -110,6 +111,8 @@ def lib() -> ctypes.CDLL:
     L.lp_compare_tails_ex.restype = ctypes.c_int
     L.lp_compare_tails_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int32, vp, vp, vp,
                                       vp, vp, ctypes.c_size_t, vp]
+    L.lp_compare_quantiles.restype = ctypes.c_int
+    L.lp_compare_quantiles.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp]
     i32 = ctypes.c_int32
     u32 = ctypes.c_uint32
     L.lp_score_ex_workspace_bytes.restype = ctypes.c_size_t

@@ -13,6 +13,19 @@ namespace {
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 constexpr int64_t kI32Max = std::numeric_limits<int32_t>::max();
+
+// The scoring kernels address a tile's rows through buffer resources with
+// 32-bit byte offsets and a range of at most kSpanMax bytes from the tile's
+// first row: a token tile reaches 255 rows of stride ldh plus one row of H
+// elements, a vocabulary tile 352 rows of H. Larger strides would read rows
+// past the range as zeros, so they are refused.
+constexpr uint64_t kSpanMax = 0x7FFFFFF0ull;
+
+bool spans_ok(int64_t ldh, int64_t H) {
+  if (ldh < 1 || H < 1 || (uint64_t)ldh > kSpanMax || (uint64_t)H > kSpanMax) return false;
+  return (uint64_t)(lp::kTileT - 1) * (uint64_t)ldh * 2 + (uint64_t)H * 2 <= kSpanMax &&
+         (uint64_t)lp::kTileV * (uint64_t)H * 2 <= kSpanMax;
+}
 constexpr uint32_t kScoreFlags = LP_SCORE_STATS | LP_SCORE_BF16_LOGITS;
 
 // Canonical shard of the merge segments: rank r of n owns segments
@@ -80,7 +93,8 @@ lp_status lp_score_shard(const void* hidden_bf16, int64_t ldh, const void* w_sha
     return LP_EUNSUPPORTED;
   const int64_t n_vt = (rows + lp::kTileV - 1) / lp::kTileV;
   const int64_t n_tt = (T + lp::kTileT - 1) / lp::kTileT;
-  if (T > kI32Max || H > kI32Max || n_vt * n_tt > kI32Max) return LP_EUNSUPPORTED;
+  if (T > kI32Max || H > kI32Max || n_vt * n_tt > kI32Max || !spans_ok(ldh, H))
+    return LP_EUNSUPPORTED;
 
   lp::ScoreArgs a;
   a.x = static_cast<const uint16_t*>(hidden_bf16);
@@ -194,7 +208,8 @@ lp_status score_impl(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
   if (!aligned(hidden_bf16, 16) || !aligned(w_bf16, 16)) return LP_EUNSUPPORTED;
   const int64_t n_vt = (V_true + lp::kTileV - 1) / lp::kTileV;
   const int64_t n_tt = (T + lp::kTileT - 1) / lp::kTileT;
-  if (T > kI32Max || H > kI32Max || V_rows > kI32Max || n_vt * n_tt > kI32Max)
+  if (T > kI32Max || H > kI32Max || V_rows > kI32Max || n_vt * n_tt > kI32Max ||
+      !spans_ok(ldh, H))
     return LP_EUNSUPPORTED;
 
   lp::ScoreArgs a;
@@ -330,6 +345,26 @@ lp_status lp_correct(const float* rollout_lp, const float* train_lp, const uint8
   a.vec = ld % 4 == 0 && aligned(rollout_lp, 16) && aligned(train_lp, 16) && aligned(mask, 4) &&
           aligned(weights, 16);
   return lp::launch_correct(a, stream) == hipSuccess ? LP_OK : LP_EHIP;
+}
+
+lp_status lp_compare_quantiles(const float* gen_A, const float* replay_B, const float* train_C,
+                               const uint8_t* mask, int64_t N, int64_t L, int64_t ld, double* out,
+                               hipStream_t stream) {
+  if (N < 0 || L < 0 || ld < L) return LP_EINVAL;
+  if (N == 0) return LP_OK;
+  if (!out || !aligned(out, 8)) return LP_EINVAL;
+  if (L > 0 && (!gen_A || !replay_B || !train_C || !mask)) return LP_EINVAL;
+  if (L > kI32Max || N > kI32Max) return LP_EUNSUPPORTED;
+  lp::QuantArgs a;
+  a.A = gen_A;
+  a.B = replay_B;
+  a.C = train_C;
+  a.mask = mask;
+  a.N = N;
+  a.L = L;
+  a.ld = ld;
+  a.out = out;
+  return lp::launch_seq_quantiles(a, stream) == hipSuccess ? LP_OK : LP_EHIP;
 }
 
 size_t lp_compare_tails_workspace_bytes(int64_t N, int64_t L) {

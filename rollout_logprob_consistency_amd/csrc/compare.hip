@@ -338,14 +338,19 @@ namespace lp {
 // worst token's position of "Fault localization and mismatch bisect" ("Metric
 // measurement basis"), plus the error-by-position profile.
 //
-// Exact order statistics by radix selection on the bit patterns of |delta|
-// (non-negative fp64, so the bits order like the values): 8 passes of one
-// byte, each a histogram pass over the batch -- one workgroup per sequence,
-// LDS counters, integer atomics into 12 global histograms (3 pairs x 3
-// quantiles and the k-th largest) -- and a one-workgroup select that keeps,
-// per target, the byte where the wanted rank falls. Every count is an
-// integer, so the result does not depend on the order in which workgroups
-// run. The sums and the first worst token are formed per sequence in a fixed
+// Quantiles follow numpy's default ("linear") rule, the estimator of the
+// AMD blog's compare(): each lies between two neighbouring order statistics
+// (quantile_ranks), which are selected exactly and interpolated in fp64
+// (quantile_lerp). Exact order statistics by radix selection on the bit
+// patterns of |delta| (non-negative fp64, so the bits order like the
+// values): 8 passes of one byte, each a histogram pass over the batch -- one
+// workgroup per sequence, LDS counters, integer atomics into global
+// histograms (3 pairs x (2 ranks per quantile and the k-th largest)) -- and
+// a one-workgroup select that keeps, per target, the byte where the wanted
+// rank falls. The two ranks of a quantile share one histogram while their
+// prefixes agree, which is every pass unless a bin boundary falls between
+// them. Every count is an integer, so the result does not depend on the
+// order in which workgroups run. The sums and the first worst token are formed per sequence in a fixed
 // order (pass 0) and reduced in a fixed tree; the position profile folds
 // fixed chunks of sequences in order.
 //
@@ -358,11 +363,13 @@ namespace lp {
 // ---------------------------------------------------------------------------
 namespace {
 
-// Targets per pair: p50, p95, p99 and, when worst tokens are asked for, the
-// k-th largest. The kernels are instantiated for 3 and 4 (an idle fourth
-// target would still cost every pass a little); the workspace always has
-// room for 4.
-constexpr int kMaxTP = 4;
+// Targets per pair: the lower and upper neighbouring ranks of p50, p95 and
+// p99 (targets 2q and 2q + 1) and, when worst tokens are asked for, the k-th
+// largest (target 6). The kernels are instantiated for 6 and 7 (an idle
+// seventh target would still cost every pass a little); the workspace always
+// has room for 7.
+constexpr int kMaxTP = 7;
+constexpr int kWorstT = 6;  // index of the k-th-largest target within a pair
 constexpr int kMaxTargets = 3 * kMaxTP;
 constexpr int kTailThreads = 256;
 constexpr int kTailChunks = 64;     // sequence chunks of the position profile
@@ -798,79 +805,101 @@ __global__ __launch_bounds__(kTailThreads) void tails_list_kernel(TailWs w, int 
     if (h[i]) atomicAdd(&hc[i], h[i]);
 }
 
-// Select the byte of each target's key; one wave per target, 4 bins a lane.
-// A target reads the histogram of tail_src() (the same prefix within its
-// pair); every histogram is read before any is cleared or any prefix moves.
+// Select the byte of each target's key. A target reads the histogram of
+// tail_src() (the same prefix within its pair). Phase 1 sums the copies of
+// every target's source histogram into LDS, phase 2 clears the copies (so
+// every histogram is read before any is cleared or any prefix moves), phase
+// 3 finds the bin that holds each target's rank (one wave per target in
+// turn, 4 bins a lane).
+constexpr int kSelThreads = 1024;
+
 template <int kTP>
-__global__ __launch_bounds__(64 * kMaxTargets) void tails_select_kernel(TailWs w, int pass) {
+__global__ __launch_bounds__(kSelThreads) void tails_select_kernel(TailWs w, int pass) {
   constexpr int kNT = 3 * kTP;
-  __shared__ uint64_t s_pre[kNT];
+  constexpr int kWaves = kSelThreads / 64;
+  __shared__ uint32_t cnt[kNT][256];
+  __shared__ uint64_t s_pre[kNT], pre[kNT];   // new / entry prefixes
   __shared__ int64_t s_rank[kNT], s_len[kNT];
-  const int t = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (threadIdx.x < kNT) s_rank[threadIdx.x] = 0;
-  uint64_t pre[kNT];
-  bool want[kNT];
-#pragma unroll
-  for (int u = 0; u < kNT; ++u) {
+  __shared__ bool want[kNT];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (threadIdx.x < kNT) {
+    const int u = threadIdx.x;
+    s_rank[u] = 0;
     pre[u] = pass ? w.sel[u].prefix : 0ull;
     want[u] = pass == 0 || w.sel[u].rank > 0;
   }
-  const int src = tail_src<kTP>(pre, want, t);
-  uint32_t c[4] = {0u, 0u, 0u, 0u};
-#pragma unroll 4
-  for (int cp = 0; cp < kHistCopies; ++cp) {
-    const uint4 q = *reinterpret_cast<const uint4*>(w.hist + cp * kHistStride + src * 256 + 4 * lane);
-    c[0] += q.x;
-    c[1] += q.y;
-    c[2] += q.z;
-    c[3] += q.w;
-  }
-  const int64_t old_rank = pass ? w.sel[t].rank : 0;
   __syncthreads();
-  for (int cp = 0; cp < kHistCopies; ++cp)
-    *reinterpret_cast<uint4*>(w.hist + cp * kHistStride + t * 256 + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
-  const int64_t lsum = (int64_t)c[0] + c[1] + c[2] + c[3];
-  int64_t incl = lsum;  // inclusive scan over lanes
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int64_t o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
-  const int64_t total = __shfl(incl, 63);
-  int64_t rank;
-  if (pass == 0) {
-    // The pass-0 histogram holds every counted token of the pair.
-    const int j = t % kTP;
-    if (j < 3) {
-      const int64_t pct = j == 0 ? 50 : (j == 1 ? 95 : 99);
-      rank = total > 0 ? (pct * total + 99) / 100 : 0;
-    } else {
-      // The k-th largest: rank count - k + 1 (the smallest when fewer are
-      // counted); no target without worst tokens requested.
-      rank = (w.k > 0 && total > 0) ? (total > w.k ? total - w.k + 1 : 1) : 0;
+  for (int t = wave; t < kNT; t += kWaves) {
+    const int src = tail_src<kTP>(pre, want, t);
+    uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll 4
+    for (int cp = 0; cp < kHistCopies; ++cp) {
+      const uint4 q = *reinterpret_cast<const uint4*>(w.hist + cp * kHistStride + src * 256 + 4 * lane);
+      c[0] += q.x;
+      c[1] += q.y;
+      c[2] += q.z;
+      c[3] += q.w;
     }
-    if (j == 0 && lane == 0) w.count[t / kTP] = total;
-  } else {
-    rank = old_rank;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cnt[t][4 * lane + k] = c[k];
   }
-  const int64_t excl = incl - lsum;
-  if (rank > 0 && excl < rank && rank <= incl) {
-    int64_t below = excl;
-    int k = 0;
-    while (below + (int64_t)c[k] < rank) below += c[k++];
-    const uint64_t np = (pass ? (pre[t] << 8) : 0ull) | (uint64_t)(4 * lane + k);
-    // A key whose top byte is 0 is the bit pattern of a double below 2^-1007:
-    // the difference of two fp32 scores is 0 or at least 2^-149 in
-    // magnitude, so every key in bin 0 of pass 0 is 0 and the selection is
-    // done (the prefix, 0, is the key).
-    const int64_t nr = (pass == 0 && 4 * lane + k == 0) ? 0 : rank - below;
-    w.sel[t].prefix = np;
-    w.sel[t].rank = nr;
-    s_pre[t] = np;
-    s_rank[t] = nr;
-    s_len[t] = (int64_t)c[k];
-  } else if (rank == 0 && lane == 0) {
-    w.sel[t].rank = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < kHistCopies * kNT * 64; i += kSelThreads) {
+    const int cp = i / (kNT * 64), r = i % (kNT * 64);
+    *reinterpret_cast<uint4*>(w.hist + cp * kHistStride + 4 * r) = make_uint4(0u, 0u, 0u, 0u);
+  }
+  for (int t = wave; t < kNT; t += kWaves) {
+    uint32_t c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = cnt[t][4 * lane + k];
+    const int64_t old_rank = pass ? w.sel[t].rank : 0;
+    const int64_t lsum = (int64_t)c[0] + c[1] + c[2] + c[3];
+    int64_t incl = lsum;  // inclusive scan over lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    const int64_t total = __shfl(incl, 63);
+    int64_t rank;
+    if (pass == 0) {
+      // The pass-0 histogram holds every counted token of the pair.
+      const int j = t % kTP;
+      if (j < kWorstT) {
+        rank = 0;
+        if (total > 0) {
+          int64_t lo, hi;
+          quantile_ranks(total, quantile_prob(j >> 1), &lo, &hi);
+          rank = (j & 1) ? hi : lo;
+        }
+      } else {
+        // The k-th largest: rank count - k + 1 (the smallest when fewer are
+        // counted); no target without worst tokens requested.
+        rank = (w.k > 0 && total > 0) ? (total > w.k ? total - w.k + 1 : 1) : 0;
+      }
+      if (j == 0 && lane == 0) w.count[t / kTP] = total;
+    } else {
+      rank = old_rank;
+    }
+    const int64_t excl = incl - lsum;
+    if (rank > 0 && excl < rank && rank <= incl) {
+      int64_t below = excl;
+      int k = 0;
+      while (below + (int64_t)c[k] < rank) below += c[k++];
+      const uint64_t np = (pass ? (pre[t] << 8) : 0ull) | (uint64_t)(4 * lane + k);
+      // A key whose top byte is 0 is the bit pattern of a double below 2^-1007:
+      // the difference of two fp32 scores is 0 or at least 2^-149 in
+      // magnitude, so every key in bin 0 of pass 0 is 0 and the selection is
+      // done (the prefix, 0, is the key).
+      const int64_t nr = (pass == 0 && 4 * lane + k == 0) ? 0 : rank - below;
+      w.sel[t].prefix = np;
+      w.sel[t].rank = nr;
+      s_pre[t] = np;
+      s_rank[t] = nr;
+      s_len[t] = (int64_t)c[k];
+    } else if (rank == 0 && lane == 0) {
+      w.sel[t].rank = 0;
+    }
   }
   if (pass != 1) return;
   __syncthreads();
@@ -946,9 +975,16 @@ __global__ __launch_bounds__(3 * kTailThreads) void tails_final_kernel(TailArgs 
     lp_tail_stats o;
     o.count = w.count[p];
     const bool any = o.count > 0;
-    o.q50 = any ? __longlong_as_double((long long)w.sel[kTP * p].prefix) : 0.0;
-    o.q95 = any ? __longlong_as_double((long long)w.sel[kTP * p + 1].prefix) : 0.0;
-    o.q99 = any ? __longlong_as_double((long long)w.sel[kTP * p + 2].prefix) : 0.0;
+    double q[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const double lo = __longlong_as_double((long long)w.sel[kTP * p + 2 * j].prefix);
+      const double hi = __longlong_as_double((long long)w.sel[kTP * p + 2 * j + 1].prefix);
+      q[j] = any ? quantile_lerp(o.count, quantile_prob(j), lo, hi) : 0.0;
+    }
+    o.q50 = q[0];
+    o.q95 = q[1];
+    o.q99 = q[2];
     o.max_abs = any ? __longlong_as_double((long long)r.max_key) : 0.0;
     o.max_seq = any ? red_seq[p][0] : -1;
     o.max_pos = any ? r.max_pos : -1;
@@ -1017,10 +1053,10 @@ __global__ __launch_bounds__(kTailThreads) void tails_pos_fold_kernel(TailArgs a
 
 // ---- Worst k tokens ----------------------------------------------------
 
-// Threshold of pair p: the key its fourth target selected (meaningful when
-// the pair counts any token).
+// Threshold of pair p: the key its k-th-largest target selected (meaningful
+// when the pair counts any token).
 __device__ __forceinline__ uint64_t worst_tau(const TailWs& w, int p) {
-  return w.sel[kMaxTP * p + 3].prefix;  // only with kTP == 4
+  return w.sel[kMaxTP * p + kWorstT].prefix;  // only with kTP == kMaxTP
 }
 
 // Per sequence and pair: counted tokens with key > tau and key == tau.
@@ -1277,11 +1313,11 @@ static void launch_select(const TailArgs& a, const TailWs& w, hipStream_t stream
       if (pass >= 3)
         hipLaunchKernelGGL(tails_list_kernel<kTP>, dim3(kListBlocks), dim3(kTailThreads), 0, stream,
                            w, pass);
-      hipLaunchKernelGGL(tails_select_kernel<kTP>, dim3(1), dim3(64 * kNT), 0, stream, w, pass);
+      hipLaunchKernelGGL(tails_select_kernel<kTP>, dim3(1), dim3(kSelThreads), 0, stream, w, pass);
     }
   } else {
     // No sequence: empty histograms give count 0 and no rank to select.
-    hipLaunchKernelGGL(tails_select_kernel<kTP>, dim3(1), dim3(64 * kNT), 0, stream, w, 0);
+    hipLaunchKernelGGL(tails_select_kernel<kTP>, dim3(1), dim3(kSelThreads), 0, stream, w, 0);
   }
   hipLaunchKernelGGL(tails_final_kernel<kTP>, dim3(1), dim3(3 * kTailThreads), 0, stream, a, w);
 }
@@ -1290,7 +1326,7 @@ hipError_t launch_tails(const TailArgs& a, hipStream_t stream) {
   const TailWs w = tail_layout(a.workspace, a.N, a.L, a.worst_k);
   hipLaunchKernelGGL(tails_init_kernel, dim3(1), dim3(kTailThreads), 0, stream, w);
   if (a.worst_k > 0) {
-    launch_select<4>(a, w, stream);
+    launch_select<kMaxTP>(a, w, stream);
     if (a.N > 0 && a.L > 0) {
       if (a.vec) {
         hipLaunchKernelGGL(tails_worst_count_kernel<true>, dim3((unsigned)a.N), dim3(kTailThreads),
@@ -1309,7 +1345,7 @@ hipError_t launch_tails(const TailArgs& a, hipStream_t stream) {
     // Also with no token: every row is the fill value.
     hipLaunchKernelGGL(tails_worst_sort_kernel, dim3(3), dim3(kWorstSortThreads), 0, stream, a, w);
   } else {
-    launch_select<3>(a, w, stream);
+    launch_select<kWorstT>(a, w, stream);
   }
   if (a.pos_sum && a.L > 0) {
     // Stage 1 also runs with N == 0, writing zero partials for the fold.

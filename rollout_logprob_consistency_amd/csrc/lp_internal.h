@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "liblp.h"
@@ -106,6 +107,39 @@ struct CorrectArgs {
 
 hipError_t launch_correct(const CorrectArgs& a, hipStream_t stream);
 
+// Quantiles p = 0.5, 0.95, 0.99 of n >= 1 values by numpy's default
+// ("linear") rule -- the estimator of the AMD blog's compare() (section
+// "Case 1: A Changes; B and C Stay Close", np.quantile at its defaults).
+// With h = (n - 1) p (one fp64 product) the result lies between the order
+// statistics of 1-based ranks floor(h) + 1 and floor(h) + 2, or is the
+// largest value when h >= n - 1.
+__host__ __device__ inline double quantile_prob(int q) {
+  return q == 0 ? 0.5 : (q == 1 ? 0.95 : 0.99);
+}
+
+__host__ __device__ inline void quantile_ranks(int64_t n, double p, int64_t* lo, int64_t* hi) {
+  const double h = (double)(n - 1) * p;
+  if (h >= (double)(n - 1)) {
+    *lo = *hi = n;
+    return;
+  }
+  const int64_t j = (int64_t)floor(h);
+  *lo = j + 1;
+  *hi = j + 2;
+}
+
+// The quantile from those two order statistics a <= b: the line between
+// them at the fraction g = h - floor(h), taken from a when g < 1/2 and from
+// b otherwise; each fp64 operation is rounded on its own (no contraction).
+__host__ __device__ inline double quantile_lerp(int64_t n, double p, double a, double b) {
+#pragma clang fp contract(off)
+  const double h = (double)(n - 1) * p;
+  if (h >= (double)(n - 1)) return b;
+  const double g = h - floor(h);
+  const double diff = b - a;
+  return g < 0.5 ? a + diff * g : b - diff * (1.0 - g);
+}
+
 struct TailArgs {
   const float* A;
   const float* B;
@@ -123,5 +157,16 @@ struct TailArgs {
 
 size_t tails_workspace_bytes(int64_t N, int64_t L, int32_t k);
 hipError_t launch_tails(const TailArgs& a, hipStream_t stream);
+
+struct QuantArgs {
+  const float* A;
+  const float* B;
+  const float* C;
+  const uint8_t* mask;
+  int64_t N, L, ld;
+  double* out;            // [3][N][3]
+};
+
+hipError_t launch_seq_quantiles(const QuantArgs& a, hipStream_t stream);
 
 }  // namespace lp

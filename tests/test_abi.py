@@ -42,7 +42,8 @@ def test_header_declares_the_boundary():
          "lp_vocab_shard_range", "lp_shard_partials_bytes",
          "lp_score_shard_workspace_bytes", "lp_score_shard", "lp_merge_shards",
          "lp_correct", "lp_score_ex_workspace_bytes", "lp_score_ex",
-         "lp_compare_tails_ex_workspace_bytes", "lp_compare_tails_ex"])
+         "lp_compare_tails_ex_workspace_bytes", "lp_compare_tails_ex",
+         "lp_compare_quantiles"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -112,6 +113,26 @@ def test_score_rejects_bad_arguments(L):
     assert score(L, T=0, hid=None, w=None, ids=None, out=None, ws=None) == 0   # empty: no-op
 
 
+# Largest strides the kernels' 32-bit buffer addressing spans: a token tile
+# reaches 255 rows of ldh plus a row of H, a vocabulary tile 352 rows of H,
+# within 0x7FFFFFF0 bytes.
+SPAN = 0x7FFFFFF0
+LDH_MAX_64 = (SPAN - 2 * 64) // (2 * 255) // 8 * 8      # at H = 64
+H_MAX = SPAN // (2 * 352) // 64 * 64
+
+
+def test_score_refuses_strides_past_the_buffer_span(L):
+    EUNSUP = 2
+    assert LDH_MAX_64 == 4210744 and H_MAX == 3050368
+    assert 255 * 2 * LDH_MAX_64 + 128 <= SPAN < 255 * 2 * (LDH_MAX_64 + 8) + 128
+    assert score(L, ldh=LDH_MAX_64 + 8) == EUNSUP
+    assert score(L, ldh=1 << 40) == EUNSUP
+    assert score(L, H=H_MAX + 64, ldh=H_MAX + 64) == EUNSUP
+    assert score_stats(L, H=H_MAX + 64) == EUNSUP
+    assert shard(L, ldh=LDH_MAX_64 + 8) == EUNSUP
+    assert shard(L, H=H_MAX + 64, ldh=H_MAX + 64) == EUNSUP
+
+
 def score_stats(L, T=4, H=64, V=300, vt=300, temp=1.0, ent=P, am=P, ws=P, wsb=1 << 30,
                 ids=P, out=P):
     return L.lp_score_stats(P, H, P, ids, T, H, V, vt, temp, out, None, ent, am, None, ws, wsb,
@@ -151,6 +172,22 @@ def test_compare_rejects_bad_arguments(L):
     assert cmp(L, N=0, out=None, a=None, m=None) == 0                 # empty: no-op
 
 
+def quant(L, N=2, Lq=5, ld=None, out=P, a=P, m=P):
+    return L.lp_compare_quantiles(a, P, P, m, N, Lq, Lq if ld is None else ld, out, None)
+
+
+def test_compare_quantiles_rejects_bad_arguments(L):
+    EINVAL = 1
+    assert quant(L, N=-1) == EINVAL
+    assert quant(L, Lq=-1) == EINVAL
+    assert quant(L, ld=3) == EINVAL
+    assert quant(L, out=None) == EINVAL
+    assert quant(L, out=ctypes.c_void_p(0x10004)) == EINVAL       # not 8-byte aligned
+    assert quant(L, a=None) == EINVAL
+    assert quant(L, m=None) == EINVAL
+    assert quant(L, N=0, out=None, a=None, m=None) == 0            # empty: no-op
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     import rollout_logprob_consistency_amd as lp
@@ -174,8 +211,12 @@ def test_align_shift_on_cpu():
     # The output after the last prompt position scores the first response token.
     assert tgt.tolist() == [6, 7, 8, 9, 10, 0, 12, 13, 14, 15, 16, 0]
     assert mask.tolist() == [0, 0, 1, 1, 1, 0, 0, 1, 1, 0, 0, 0]
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError, match="must be 0"):
         lp.align(hidden, ids, torch.ones_like(ids))
+    bad = resp.clone()
+    bad[0, 4] = 2                                  # the page's mask is binary
+    with pytest.raises(ValueError, match="0 or 1"):
+        lp.align(hidden, ids, bad)
 
 
 def tails(L, N=2, Lq=5, ld=None, out=P, ws=P, wsb=1 << 30, ps=None, pc=None, a=P):

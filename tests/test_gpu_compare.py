@@ -11,7 +11,7 @@ import oracle
 import rollout_logprob_consistency_amd as lp
 from workloads import synth
 
-from .gpu_helpers import DEV, SCORE_ATOL, check_stats, dev, gpu_score
+from .gpu_helpers import DEV, SCORE_ATOL, check_stats, dev, dev_bf16, gpu_score
 
 pytestmark = pytest.mark.gpu
 
@@ -82,6 +82,33 @@ def test_fault_stale_weights():
     rows = np.flatnonzero(act.reshape(-1))[:4096]
     g = gpu_score(x[rows], w_stale, ids[rows])
     assert np.max(np.abs(g - C.reshape(-1)[rows])) <= SCORE_ATOL
+
+
+def test_fault_stale_weights_scored_on_the_gpu():
+    # [AMD] "Case 3: Agreement Breaks After an Update" at the Qwen3-1.7B head:
+    # every one of the 8 x 2304 positions scored by lp_score with W (B) and
+    # with W' = bf16(W + N(0, 1e-3)) (C), H = 2048, V = 151 936; lp_compare on
+    # those bytes against the oracle, and sampled B and C rows against the
+    # fp64 oracle score.
+    N, L, H = 8, 2304, 2048
+    x, w, w_stale, ids = synth.stale_qwen_inputs(N, L, H)
+    xd = dev_bf16(x)
+    B = gpu_score(xd, w, ids).reshape(N, L)
+    C = gpu_score(xd, w_stale, ids).reshape(N, L)
+    rec = synth.compare_case(N=N, max_resp=2048, prompt=256, seed=5, B=B)
+    act = rec.mask != 0
+    Cm = rec.C.copy()
+    Cm[act] = C[act]
+    got, ref = run(with_c(rec, Cm))
+    assert (got["BC"]["mismatch"] > 0).all() and (got["BC"]["max_abs"] > 0).all()
+    assert not got["AB"]["mismatch"].any()
+    # The update moves scores far more than a repeat would: B - C is the
+    # weight-movement term of the blog's split, A - B (= 0 here) the rest.
+    assert np.array_equal(got["AC"]["sum_signed"], got["BC"]["sum_signed"])
+    rows = np.random.default_rng(55).choice(np.flatnonzero(act.reshape(-1)), 48, replace=False)
+    for Wb, S in ((w, B), (w_stale, C)):
+        ref_rows, _ = oracle.score(x[rows], Wb, ids[rows])
+        assert np.max(np.abs(S.reshape(-1)[rows] - ref_rows)) <= SCORE_ATOL
 
 
 def test_per_token_values(record):

@@ -1,7 +1,8 @@
 """GPU parity of lp_compare_tails (batch tail statistics of |left - right| per
-pair) against the oracle: counts, quantiles, maxima and their positions, and
-the position counts exact; fp64 sums to 1e-9 relative. Every call goes
-through the C ABI (liblp.so)."""
+pair) and lp_compare_quantiles (the same quantiles per sequence) against the
+oracle: counts, quantiles (numpy's default rule, to the bit), maxima and
+their positions, and the position counts exact; fp64 sums to 1e-9 relative.
+Every call goes through the C ABI (liblp.so)."""
 
 import numpy as np
 import pytest
@@ -18,7 +19,18 @@ EXACT = ("count", "q50", "q95", "q99", "max_abs", "max_seq", "max_pos")
 SUMS = ("sum_abs", "sum_prob_abs")
 
 
+def run_seq_quantiles(A, B, C, M):
+    got = lp.compare_quantiles(dev(A), dev(B), dev(C), dev(M))
+    ref = oracle.seq_quantiles(A, B, C, M)
+    for p in lp.PAIRS:
+        assert got[p].shape == ref[p].shape
+        bad = np.argwhere(got[p] != ref[p])
+        assert bad.size == 0, (p, bad[:5], got[p][tuple(bad[0])], ref[p][tuple(bad[0])])
+    return got
+
+
 def run(A, B, C, M, positions=True):
+    run_seq_quantiles(A, B, C, M)
     got, ps, pc = lp.compare_tails(dev(A), dev(B), dev(C), dev(M), positions=True)
     ref, rps, rpc = oracle.tails(A, B, C, M)
     for p in lp.PAIRS:
@@ -91,6 +103,35 @@ def test_masks_nonfinite_and_ties():
     run(A.astype(np.float32), B, C, M)
 
 
+def test_seq_quantiles_one_token_long_rows_and_strides():
+    # One-token and empty records (every quantile is the token's |delta|, or
+    # 0); rows longer than the LDS key cache (recomputed every pass); rows
+    # with a stride that is not a multiple of 4: all exact.
+    rng = np.random.default_rng(17)
+    N, L = 9, 5003
+    B = np.log(1.0 - rng.random((N, L))).astype(np.float32)
+    A = (B + rng.normal(0, 0.01, (N, L))).astype(np.float32)
+    C = (B + np.round(rng.normal(0, 2, (N, L))) * np.float32(1e-3)).astype(np.float32)  # ties
+    M = (rng.random((N, L)) < 0.9).astype(np.uint8)
+    M[0] = 0
+    M[0, 4444] = 1                                   # one token
+    M[1] = 0                                         # none
+    M[2, :4100] = 0                                  # short record in a long row
+    C[3, 7] = np.nan
+    run_seq_quantiles(A, B, C, M)
+    q = lp.compare_quantiles(dev(A), dev(B), dev(C), dev(M))
+    d = abs(float(A[0, 4444]) - float(B[0, 4444]))
+    assert q["AB"][0].tolist() == [d, d, d] and q["AB"][1].tolist() == [0.0, 0.0, 0.0]
+    for pad in (1, 3):
+        big = [np.zeros((N, 700 + pad), a.dtype) for a in (A, B, C, M)]
+        for b_, a_ in zip(big, (A, B, C, M)):
+            b_[:, :700] = a_[:, :700]
+        got = lp.compare_quantiles(*[dev(b_)[:, :700] for b_ in big])
+        ref = oracle.seq_quantiles(A[:, :700], B[:, :700], C[:, :700], M[:, :700])
+        for p in lp.PAIRS:
+            assert np.array_equal(got[p], ref[p]), (pad, p)
+
+
 @pytest.mark.parametrize("N,L", [(0, 5), (3, 0), (1, 1)])
 def test_degenerate_sizes(N, L):
     A = np.zeros((N, L), np.float32)
@@ -101,6 +142,7 @@ def test_degenerate_sizes(N, L):
         for f in EXACT + SUMS:
             assert got[p][f] == ref[p][f], (p, f)
     assert ps.shape == (3, L) and np.array_equal(pc.astype(np.int64), rpc)
+    run_seq_quantiles(A, A, A, M)
 
 
 def test_sweep_size_and_repeatability():

@@ -4,7 +4,8 @@ loads on a row stride that is not a multiple of 4) for lp_compare,
 lp_compare_tails(_ex) and lp_correct; 70 001 scored rows (275 token tiles of
 the 352 x 256 kernel, a ragged last one) and a 1 000 003-row vocabulary (2 841
 vocabulary tiles, a ragged last one) for lp_score, both through the tile kernel
-and through the streaming kernels."""
+and through the streaming kernels; and the largest row stride lp_score
+accepts (its 32-bit buffer addressing spans 255 rows of it)."""
 
 import numpy as np
 import pytest
@@ -13,7 +14,7 @@ import oracle
 import rollout_logprob_consistency_amd as lp
 from workloads import synth
 
-from .gpu_helpers import SCORE_ATOL, check_stats, dev, dev_bf16, gpu_score
+from .gpu_helpers import DEV, SCORE_ATOL, check_stats, dev, dev_bf16, gpu_score
 from .test_gpu_compare_tails import run as run_tails, run_worst
 from .test_gpu_correct import check as check_correct
 
@@ -88,3 +89,29 @@ def test_wide_vocabulary(T):
         x[100:100 + T], ids[100:100 + T] = c.x_bits, c.ids
         inside = gpu_score(x, wd, ids, 1.0)[100:100 + T]
         assert np.array_equal(inside.view(np.int32), got.view(np.int32))
+
+
+def test_largest_accepted_row_stride():
+    # 255 * 2 * ldh + 2 * H <= 0x7FFFFFF0 at H = 64: ldh = 4 210 744 (8.4 MB
+    # per row, 2.5 GB for 300 rows). Everything past column 64 is NaN, so a
+    # read outside the row's H elements would show. Rows 0..4 scored through
+    # the register streaming kernel (T = 5), the LDS streaming kernel (T = 40)
+    # and the tile kernel (T = 300) give the same bits and the oracle's value.
+    import torch
+    H, ldh, T = 64, 4_210_744, 300
+    assert 255 * 2 * ldh + 2 * H <= 0x7FFFFFF0 < 255 * 2 * (ldh + 8) + 2 * H
+    c = synth.tiny_case(T=T, H=H, V=1000, seed=94)
+    buf = torch.full((T, ldh), 0x7FC0, dtype=torch.int16, device=DEV)   # bf16 NaN
+    buf[:, :H] = dev(c.x_bits.view(np.int16))
+    x = buf.view(torch.bfloat16)
+    wd = dev_bf16(c.w_bits)
+    ref, _ = oracle.score(c.x_bits, c.w_bits, c.ids, 1.0)
+    outs = {}
+    for t in (5, 40, T):
+        got = gpu_score(x[:t, :H], wd, c.ids[:t], 1.0)
+        assert np.max(np.abs(got - ref[:t])) <= SCORE_ATOL, t
+        outs[t] = got
+    for t in (5, 40):
+        assert np.array_equal(outs[t].view(np.int32), outs[T][:t].view(np.int32)), t
+    del buf, x
+    torch.cuda.empty_cache()

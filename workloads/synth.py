@@ -297,6 +297,21 @@ def stale_inputs(N: int = 8, L: int = 2304, H: int = 256, V: int = 4096,
     return x, w, w_stale, ids
 
 
+def stale_qwen_inputs(N: int = 8, L: int = 2304, H: int = 2048, V: int = 151936,
+                      noise: float = 1e-3, seed: int = 0):
+    """The skipped-weight-sync fault at the Qwen3-1.7B-shaped head: rms-scaled
+    bf16 rows for every position of an N x L record, W = the Qwen-shaped
+    bf16 N(0, 0.02) weight of qwen_weight(H, V), W' = bf16(W + N(0, noise)),
+    Zipf(1.1) target ids. Returns (x_bits [N*L, H], w_bits, w_stale_bits,
+    ids [N*L])."""
+    b = BASE_SEED + _OFF_STALE + 16 * (seed + 1)
+    x = _hidden_bits(b + _OFF_X, N * L, H, rms=True)
+    w = qwen_weight(H, V)
+    w_stale = bf16_bits_from_f32(f32_from_bf16_bits(w) + normal_f32(b + 5, V * H, noise).reshape(V, H))
+    ids = zipf_ids(b + _OFF_IDS, N * L, V)
+    return x, w, w_stale, ids
+
+
 def compare_sweep_case(N: int, L: int = 2304, prompt: int = 256, seed: int = 0) -> CompareCase:
     """Large comparison batch for bandwidth measurement: A = B, C = B + N(0, 1e-3)."""
     c = compare_case(N=N, max_resp=L - prompt, prompt=prompt, seed=seed + 1)
