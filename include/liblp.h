@@ -101,6 +101,40 @@ lp_status lp_score(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
                    hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * lp_score without a caller workspace
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * call as lp_score, minus workspace and workspace_bytes, with the same
+ * kernels and bit-identical outputs; the workspace is a device array of
+ * LP_NOALLOC_SCRATCH_BYTES inside the library (one per device, held until
+ * the process ends; its address is looked up once per device). No
+ * allocation of any kind happens in the call.
+ *
+ * Limit: the workspace lp_score would need, lp_score_workspace_bytes(T, H,
+ * V_rows, V_true), must fit LP_NOALLOC_SCRATCH_BYTES (32 MiB): at V_true =
+ * 151 936, up to 9 697 rows. Larger calls return LP_EUNSUPPORTED before
+ * anything is enqueued.
+ *
+ * Concurrency: every call on one device uses that device's one array, so
+ * calls that overlap on a device (different streams, different threads)
+ * race; order them (one stream, or events). The array keeps the last call's
+ * contents, which no call reads before writing.
+ *
+ * Errors: as for lp_score (argument errors first), then LP_EUNSUPPORTED for
+ * the scratch limit, LP_EHIP if the stream's device or the array's address
+ * cannot be determined.
+ * ------------------------------------------------------------------------ */
+#define LP_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+lp_status lp_score_noalloc(const void* hidden_bf16, int64_t ldh,
+                           const void* w_bf16, const int64_t* target_ids,
+                           int64_t T, int64_t H, int64_t V_rows,
+                           int64_t V_true, float temperature,
+                           float* out_logprob, float* out_lse,
+                           int32_t* bad_rows, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Selected-token logprob with the row's entropy and argmax
  *
  * The same call as lp_score, also returning per row the entropy of the

@@ -23,7 +23,7 @@ EXPORTS = ("lp_status_string", "lp_score_workspace_bytes", "lp_score",
            "lp_score_shard_workspace_bytes", "lp_score_shard", "lp_merge_shards",
            "lp_correct", "lp_score_ex_workspace_bytes", "lp_score_ex",
            "lp_compare_tails_ex_workspace_bytes", "lp_compare_tails_ex",
-           "lp_compare_quantiles")
+           "lp_compare_quantiles", "lp_score_noalloc")
 
 REJECT_NONE, REJECT_K1, REJECT_K3 = 0, 1, 3  # LP_REJECT_*
 
@@ -64,6 +64,7 @@ assert TAIL_STATS_DTYPE.itemsize == 64
 WORST_DTYPE = np.dtype([("abs_delta", "<f8"), ("seq", "<i4"), ("pos", "<i4")], align=True)
 assert WORST_DTYPE.itemsize == 16
 WORST_MAX = 4096  # LP_WORST_MAX
+NOALLOC_SCRATCH_BYTES = 32 << 20  # LP_NOALLOC_SCRATCH_BYTES
 
 
 class LpError(RuntimeError):
@@ -111,6 +112,8 @@ def lib() -> ctypes.CDLL:
     L.lp_compare_tails_ex.restype = ctypes.c_int
     L.lp_compare_tails_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int32, vp, vp, vp,
                                       vp, vp, ctypes.c_size_t, vp]
+    L.lp_score_noalloc.restype = ctypes.c_int
+    L.lp_score_noalloc.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, f32, vp, vp, vp, vp]
     L.lp_compare_quantiles.restype = ctypes.c_int
     L.lp_compare_quantiles.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp]
     i32 = ctypes.c_int32

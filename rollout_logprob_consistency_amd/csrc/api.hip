@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <limits>
+#include <mutex>
 
 #include "lp_internal.h"
 
@@ -415,6 +416,78 @@ lp_status lp_compare_tails_ex(const float* gen_A, const float* replay_B, const f
   a.worst_k = k;
   a.worst = worst;
   return lp::launch_tails(a, stream) == hipSuccess ? LP_OK : LP_EHIP;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// lp_score_noalloc: lp_score with its workspace in this library's own device
+// memory, for callers that cannot allocate (code under HIP graph capture,
+// tight serving loops, harnesses that forbid hipMalloc).
+//
+// The workspace (per-tile partials and target logits, fully written by the
+// scoring kernels before the merge reads them, so nothing needs clearing)
+// lives in `scratch`, one copy per device for the life of the process. In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// its device address is looked up once per device with hipGetSymbolAddress
+// (with that device current) and only that address reaches a kernel. Calls
+// that overlap on one device share the array and race; the caller orders
+// them (one stream, or events).
+// ---------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[LP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on device `dev`, looked up on first use.
+hipError_t scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (back != hipSuccess) return back;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+lp_status lp_score_noalloc(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
+                           const int64_t* target_ids, int64_t T, int64_t H, int64_t V_rows,
+                           int64_t V_true, float temperature, float* out_logprob,
+                           float* out_lse, int32_t* bad_rows, hipStream_t stream) {
+  // Argument errors first, exactly as lp_score reports them; then the
+  // scratch limit; only then any HIP call.
+  if (T < 0 || H < 1 || V_rows < 1 || V_true < 1 || V_true > V_rows || ldh < H)
+    return LP_EINVAL;
+  if (!(isfinite(temperature) && temperature > 0.0f)) return LP_EINVAL;
+  if (T == 0) return LP_OK;
+  if (!hidden_bf16 || !w_bf16 || !target_ids || !out_logprob) return LP_EINVAL;
+  if (lp::score_workspace_layout(T, V_true, false).total > (size_t)LP_NOALLOC_SCRATCH_BYTES)
+    return LP_EUNSUPPORTED;
+  int dev = 0;
+  if ((stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess)
+    return LP_EHIP;
+  void* ws = nullptr;
+  if (scratch_address(dev, &ws) != hipSuccess) return LP_EHIP;
+  return score_impl(hidden_bf16, ldh, w_bf16, target_ids, T, H, V_rows, V_true, temperature,
+                    out_logprob, out_lse, nullptr, nullptr, false, false, bad_rows, ws,
+                    (size_t)LP_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

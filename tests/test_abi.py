@@ -43,7 +43,7 @@ def test_header_declares_the_boundary():
          "lp_score_shard_workspace_bytes", "lp_score_shard", "lp_merge_shards",
          "lp_correct", "lp_score_ex_workspace_bytes", "lp_score_ex",
          "lp_compare_tails_ex_workspace_bytes", "lp_compare_tails_ex",
-         "lp_compare_quantiles"])
+         "lp_compare_quantiles", "lp_score_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -379,7 +379,36 @@ def test_score_ex_flags_and_workspace(L):
     assert ex(P, 64, P, P, 8, 64, 100, 100, 0.0, 2, P, None, None, None, None, P, 1 << 20, None) == EINVAL
 
 
+def noalloc(L, T=4, H=64, V=300, vt=300, temp=1.0, ldh=None, hid=P, w=P, ids=P, out=P):
+    return L.lp_score_noalloc(hid, H if ldh is None else ldh, w, ids, T, H, V, vt, temp, out,
+                              None, None, None)
+
+
+def test_score_noalloc_rejects_before_any_hip_call(L):
+    # Argument errors as lp_score reports them, then the scratch limit; all
+    # before the library touches a device.
+    EINVAL, EUNSUP = 1, 2
+    assert noalloc(L, T=-1) == EINVAL
+    assert noalloc(L, vt=301) == EINVAL
+    assert noalloc(L, temp=0.0) == EINVAL
+    for k in ("hid", "w", "ids", "out"):
+        assert noalloc(L, **{k: None}) == EINVAL
+    assert noalloc(L, T=0, hid=None, w=None, ids=None, out=None) == 0
+    limit = header_define_expr("LP_NOALLOC_SCRATCH_BYTES")
+    assert limit == 32 << 20
+    # 9697 rows of a 151 936-row head fit the 32 MiB scratch, 9698 do not.
+    assert L.lp_score_workspace_bytes(9697, 4096, 151936, 151936) <= limit
+    assert L.lp_score_workspace_bytes(9698, 4096, 151936, 151936) > limit
+    assert noalloc(L, T=9698, H=4096, V=151936, vt=151936) == EUNSUP
+
+
+def header_define_expr(name):
+    m = re.search(r"#define %s \((\d+)u << (\d+)\)" % name, open(HEADER).read())
+    return int(m.group(1)) << int(m.group(2))
+
+
 def test_python_mirrors_of_header_constants():
     from rollout_logprob_consistency_amd import _lib
+    assert _lib.NOALLOC_SCRATCH_BYTES == header_define_expr("LP_NOALLOC_SCRATCH_BYTES")
     assert _lib.MERGE_SEGMENTS == header_define("LP_MERGE_SEGMENTS")
     assert _lib.VOCAB_TILE_ROWS == header_define("LP_VOCAB_TILE_ROWS")
