@@ -74,12 +74,15 @@ def main() -> int:
                          "tail statistics and the correction are timed at N = 4096 when listed")
     ap.add_argument("--small-batches", type=str, default="1,7,64",
                     help="row counts at which lp_score is timed as a stream over W")
-    ap.add_argument("--mode", choices=("bench", "score", "stats", "small", "compare", "copy"),
+    ap.add_argument("--mode", choices=("bench", "score", "stats", "small", "compare", "tails",
+                                       "quantiles", "copy"),
                     default="bench",
                     help="score: only `steps` lp_score calls on the benchmark batch; stats: "
                          "the same with lp_score_stats (entropy and argmax too); small: "
                          "`steps` lp_score calls on its first row; compare: `steps` lp_compare "
-                         "calls at N=4096, L=2304 (these three for profilers); copy: one plain "
+                         "calls at N=4096, L=2304; tails / quantiles: `steps` lp_compare_tails / "
+                         "lp_compare_quantiles calls on the same arrays (these for profilers); "
+                         "copy: one plain "
                          "1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -165,14 +168,23 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"bench: {args.steps} one-row lp_score calls done")
         return 0
-    if args.mode == "compare":
+    if args.mode in ("compare", "tails", "quantiles"):
         sc = synth.compare_sweep_case(N=4096)
         tA, tB, tC, tM = (torch.from_numpy(a).to(dev) for a in (sc.A, sc.B, sc.C, sc.mask))
-        sbuf = torch.empty(3 * sc.N * lp.SEQ_STATS_DTYPE.itemsize, dtype=torch.uint8, device=dev)
-        for _ in range(args.steps):
-            lp.compare_raw(tA, tB, tC, tM, out=sbuf)
+        if args.mode == "compare":
+            sbuf = torch.empty(3 * sc.N * lp.SEQ_STATS_DTYPE.itemsize, dtype=torch.uint8,
+                               device=dev)
+            for _ in range(args.steps):
+                lp.compare_raw(tA, tB, tC, tM, out=sbuf)
+        elif args.mode == "tails":
+            for _ in range(args.steps):
+                lp.compare_tails(tA, tB, tC, tM, positions=True)
+        else:
+            qout = torch.empty((3, sc.N, 3), dtype=torch.float64, device=dev)
+            for _ in range(args.steps):
+                lp.compare_quantiles(tA, tB, tC, tM, out=qout, sync=False)
         torch.cuda.synchronize()
-        log(f"bench: {args.steps} lp_compare calls (N=4096, L=2304) done")
+        log(f"bench: {args.steps} {args.mode} calls (N=4096, L=2304) done")
         return 0
 
     def step(ev=None):

@@ -314,7 +314,8 @@ lp_status lp_compare(const float* gen_A, const float* replay_B,
  * inside one workgroup. Exact and independent of N and of scheduling.
  *
  * Errors: LP_EINVAL for N < 0, L < 0, ld < L, a NULL or misaligned out, or
- * NULL inputs with N, L > 0; LP_EUNSUPPORTED for N or L above INT32_MAX.
+ * NULL inputs with N, L > 0; LP_EUNSUPPORTED for L above INT32_MAX or N
+ * above 715 827 880 (three workgroups per sequence in one grid row).
  * N == 0 does nothing; L == 0 writes zeros.
  * ------------------------------------------------------------------------ */
 lp_status lp_compare_quantiles(const float* gen_A, const float* replay_B,

@@ -355,7 +355,8 @@ lp_status lp_compare_quantiles(const float* gen_A, const float* replay_B, const 
   if (N == 0) return LP_OK;
   if (!out || !aligned(out, 8)) return LP_EINVAL;
   if (L > 0 && (!gen_A || !replay_B || !train_C || !mask)) return LP_EINVAL;
-  if (L > kI32Max || N > kI32Max) return LP_EUNSUPPORTED;
+  // Three workgroups per sequence, in groups of 8 sequences: one grid row.
+  if (L > kI32Max || N > kI32Max || 3 * ((N + 7) / 8) * 8 > kI32Max) return LP_EUNSUPPORTED;
   lp::QuantArgs a;
   a.A = gen_A;
   a.B = replay_B;
@@ -364,6 +365,8 @@ lp_status lp_compare_quantiles(const float* gen_A, const float* replay_B, const 
   a.N = N;
   a.L = L;
   a.ld = ld;
+  a.vec = ld % 4 == 0 && aligned(gen_A, 16) && aligned(replay_B, 16) && aligned(train_C, 16) &&
+          aligned(mask, 4);
   a.out = out;
   return lp::launch_seq_quantiles(a, stream) == hipSuccess ? LP_OK : LP_EHIP;
 }

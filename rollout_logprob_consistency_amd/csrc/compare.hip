@@ -379,6 +379,7 @@ constexpr int kTailChunks = 64;     // sequence chunks of the position profile
 // select kernel sums the copies.
 constexpr int kHistCopies = 16;
 constexpr int kHistStride = kMaxTargets * 256;  // words per histogram copy
+static_assert(kTailThreads == 256, "one histogram bin per thread");
 
 struct TailSel {
   uint64_t prefix;   // bytes of the selected key found so far
@@ -417,6 +418,20 @@ struct TailList {
   int32_t src;       // the target whose region it is; -1: no list
 };
 
+// What the next pass does, written by the select kernel (the init kernel for
+// pass 0) and read by the pass with a handful of independent loads, so that a
+// pass with nothing to do exits after one. Targets of one pair under one
+// prefix see the same tokens: only the first of them (its "source") takes a
+// histogram, and the others read it.
+struct TailPlan {
+  uint64_t pre[kMaxTargets];  // each target's selected prefix
+  int32_t lsrc[kMaxTargets];  // the list region a list target reads (-1: none)
+  int8_t src[kMaxTargets];    // the target whose histogram target t reads
+  uint32_t full;              // sources that histogram in a full pass over the batch
+  uint32_t list;              // sources that histogram on a list (passes 3 .. 7)
+  uint32_t own;               // pass 2: sources that own a list region
+};
+
 struct WorstCand {   // a worst-token candidate
   uint64_t key;      // bits of |delta|
   int32_t seq, pos;
@@ -426,6 +441,7 @@ struct TailWs {
   uint32_t* hist;    // [kHistCopies][kMaxTargets][256]
   TailSel* sel;      // [kMaxTargets]
   TailList* list;    // [kMaxTargets]
+  TailPlan* plan;
   uint64_t* keys;    // [cap]
   int64_t cap;
   uint32_t* cnt;     // [kMaxTargets][N] candidates of sequence n in list t (pass 2)
@@ -457,6 +473,7 @@ TailWs tail_layout(void* base, int64_t N, int64_t L, int32_t k) {
   w.hist = reinterpret_cast<uint32_t*>(p + o); o = tail_up(o + kHistCopies * kHistStride * sizeof(uint32_t));
   w.sel = reinterpret_cast<TailSel*>(p + o);   o = tail_up(o + kMaxTargets * sizeof(TailSel));
   w.list = reinterpret_cast<TailList*>(p + o); o = tail_up(o + kMaxTargets * sizeof(TailList));
+  w.plan = reinterpret_cast<TailPlan*>(p + o); o = tail_up(o + sizeof(TailPlan));
   w.cap = tail_key_cap(N, L);
   w.keys = reinterpret_cast<uint64_t*>(p + o); o = tail_up(o + (size_t)w.cap * sizeof(uint64_t));
   w.cnt = reinterpret_cast<uint32_t*>(p + o);  o = tail_up(o + (size_t)N * kMaxTargets * sizeof(uint32_t));
@@ -478,6 +495,7 @@ size_t tail_bytes(int64_t N, int64_t L, int32_t k) {
   o = tail_up(o + kHistCopies * kHistStride * sizeof(uint32_t));
   o = tail_up(o + kMaxTargets * sizeof(TailSel));
   o = tail_up(o + kMaxTargets * sizeof(TailList));
+  o = tail_up(o + sizeof(TailPlan));
   o = tail_up(o + (size_t)tail_key_cap(N, L) * sizeof(uint64_t));
   o = tail_up(o + (size_t)N * kMaxTargets * sizeof(uint32_t));
   o = tail_up(o + (size_t)N * kMaxTargets * sizeof(uint32_t));
@@ -498,21 +516,25 @@ size_t tail_bytes(int64_t N, int64_t L, int32_t k) {
 __device__ __forceinline__ int pair_left(int p) { return p == 1 ? 1 : 0; }
 __device__ __forceinline__ int pair_right(int p) { return p == 0 ? 1 : 2; }
 
-// The target whose histogram target t reads: the first target of its pair
-// that is selecting under the same prefix (every one of them in pass 0).
-template <int kTP>
-__device__ __forceinline__ int tail_src(const uint64_t* pre, const bool* want, int t) {
-  const int p0 = kTP * (t / kTP);
-  for (int u = p0; u < t; ++u)
-    if (want[u] && pre[u] == pre[t]) return u;
-  return t;
-}
-
-__global__ __launch_bounds__(kTailThreads) void tails_init_kernel(TailWs w) {
-  for (int i = threadIdx.x; i < kHistCopies * kHistStride; i += kTailThreads) w.hist[i] = 0u;
-  if (threadIdx.x < kMaxTargets) {
-    w.sel[threadIdx.x] = TailSel{0ull, 0};
-    w.list[threadIdx.x] = TailList{0, 0, -1};
+// Workgroup c clears histogram copy c; workgroup 0 also resets the
+// selection state and writes the plan of pass 0: every target of a pair
+// reads the pair's one histogram (prefix 0), kept by its first target.
+__global__ __launch_bounds__(kTailThreads) void tails_init_kernel(TailWs w, int tp) {
+  uint4* h = reinterpret_cast<uint4*>(w.hist + blockIdx.x * kHistStride);
+  for (int i = threadIdx.x; i < kHistStride / 4; i += kTailThreads) h[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (blockIdx.x != 0) return;
+  const int t = threadIdx.x;
+  if (t < kMaxTargets) {
+    w.sel[t] = TailSel{0ull, 0};
+    w.list[t] = TailList{0, 0, -1};
+    w.plan->pre[t] = 0ull;
+    w.plan->lsrc[t] = -1;
+    w.plan->src[t] = (int8_t)(tp * (t / tp));
+  }
+  if (t == 0) {
+    w.plan->full = 1u | (1u << tp) | (1u << (2 * tp));
+    w.plan->list = 0u;
+    w.plan->own = 0u;
   }
 }
 
@@ -558,25 +580,23 @@ __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, Ta
   __shared__ uint32_t n_found[kNT];
   const int tid = threadIdx.x;
   const int shift = 56 - 8 * pass;  // this pass's byte: key bits [shift + 7 : shift]
-  // Targets of one pair whose prefixes agree see the same tokens: only the
-  // first of them counts (tail_src() below names it for the select kernel).
+  // The plan: which sources histogram (want) and, in pass 2, which own a
+  // list region (src_list). A pass with nothing to do exits after one load.
+  const uint32_t full = kMode <= 2 ? w.plan->full : 0u;
+  const uint32_t own = kMode >= 2 ? w.plan->own : 0u;
+  if ((full | own) == 0u) return;  // uniform
   uint64_t pre[kNT];
   bool want[kNT];
-  bool src_list[kNT];  // kMode 2, 3: t owns a list region
+  bool src_list[kNT];
 #pragma unroll
   for (int t = 0; t < kNT; ++t) {
-    pre[t] = pass ? w.sel[t].prefix : 0ull;
-    want[t] = pass == 0 || (w.sel[t].rank > 0 && (pass <= 2 || w.list[t].src < 0));
+    pre[t] = w.plan->pre[t];
+    want[t] = ((full | own) >> t) & 1u;
+    src_list[t] = (own >> t) & 1u;
   }
-  bool any_want = false;
 #pragma unroll
-  for (int t = 0; t < kNT; ++t) {
-    if (tail_src<kTP>(pre, want, t) != t) want[t] = false;
-    any_want = any_want || want[t];
-    src_list[t] = kMode >= 2 && want[t] && w.list[t].src == t;
-  }
-  if (!any_want) return;  // uniform: every target has a list or is done
-  for (int i = tid; i < kHW; i += kTailThreads) h[i] = 0u;
+  for (int t = 0; t < kNT; ++t)
+    if ((full >> t) & 1u) h[t * 256 + tid] = 0u;  // kTailThreads == 256 bins
   if (kMode >= 2 && tid < kNT) n_found[tid] = 0u;
   __syncthreads();
 
@@ -631,11 +651,12 @@ __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, Ta
           const bool hit = ok && (kMode == 0 || (key >> (shift + 8)) == pre[t]);
           const uint64_t hb = __ballot(hit);
           if (hb == 0) continue;
-          // One atomic for the wave when all its hits share a bin (the common
-          // case: runs of identical scores put every lane in bin 0).
+          // One atomic for the wave when all its hits share the bin of its
+          // first lane (the common case: runs of identical scores put every
+          // lane in bin 0); readfirstlane needs no LDS round trip.
           const int first = __ffsll((long long)hb) - 1;
           if (kMode <= 2) {
-            const uint32_t d0 = (uint32_t)__shfl((int)digit, first);
+            const uint32_t d0 = __builtin_amdgcn_readfirstlane(digit);
             if (__ballot(hit && digit != d0) == 0) {
               if (lane == first) atomicAdd(&h[t * 256 + d0], (uint32_t)__popcll(hb));
             } else if (hit) {
@@ -672,8 +693,12 @@ __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, Ta
   __syncthreads();
   if (kMode == 3) return;
   uint32_t* hc = w.hist + (blockIdx.x % kHistCopies) * kHistStride;
-  for (int i = tid; i < kHW; i += kTailThreads)
-    if (h[i]) atomicAdd(&hc[i], h[i]);
+#pragma unroll
+  for (int t = 0; t < kNT; ++t) {
+    if (!((full >> t) & 1u)) continue;  // uniform
+    const uint32_t v = h[t * 256 + tid];
+    if (v) atomicAdd(&hc[t * 256 + tid], v);
+  }
   if (kMode == 2) {
     if (tid < kNT) w.cnt[tid * a.N + n] = src_list[tid] ? n_found[tid] : 0u;
     return;
@@ -752,23 +777,20 @@ __global__ __launch_bounds__(kTailThreads) void tails_list_kernel(TailWs w, int 
   __shared__ uint32_t h[kHW];
   const int tid = threadIdx.x, lane = tid & 63;
   const int shift = 56 - 8 * pass;
+  const uint32_t lm = w.plan->list;
+  if (lm == 0u) return;  // uniform: no target reads a list in this pass
   uint64_t pre[kNT];
   bool want[kNT];
   int lst[kNT];
 #pragma unroll
   for (int t = 0; t < kNT; ++t) {
-    pre[t] = w.sel[t].prefix;
-    lst[t] = w.list[t].src;
-    want[t] = w.sel[t].rank > 0 && lst[t] >= 0;
+    pre[t] = w.plan->pre[t];
+    lst[t] = w.plan->lsrc[t];
+    want[t] = (lm >> t) & 1u;
   }
-  bool any_want = false;
 #pragma unroll
-  for (int t = 0; t < kNT; ++t) {
-    if (tail_src<kTP>(pre, want, t) != t) want[t] = false;
-    any_want = any_want || want[t];
-  }
-  if (!any_want) return;  // uniform
-  for (int i = tid; i < kHW; i += kTailThreads) h[i] = 0u;
+  for (int t = 0; t < kNT; ++t)
+    if (want[t]) h[t * 256 + tid] = 0u;
   __syncthreads();
   const int64_t stride = (int64_t)gridDim.x * kTailThreads;
   for (int u = 0; u < kNT; ++u) {
@@ -790,7 +812,7 @@ __global__ __launch_bounds__(kTailThreads) void tails_list_kernel(TailWs w, int 
         const uint64_t hb = __ballot(hit);
         if (hb == 0) continue;
         const int first = __ffsll((long long)hb) - 1;
-        const uint32_t d0 = (uint32_t)__shfl((int)digit, first);
+        const uint32_t d0 = __builtin_amdgcn_readfirstlane(digit);
         if (__ballot(hit && digit != d0) == 0) {
           if (lane == first) atomicAdd(&h[t * 256 + d0], (uint32_t)__popcll(hb));
         } else if (hit) {
@@ -801,16 +823,20 @@ __global__ __launch_bounds__(kTailThreads) void tails_list_kernel(TailWs w, int 
   }
   __syncthreads();
   uint32_t* hc = w.hist + (blockIdx.x % kHistCopies) * kHistStride;
-  for (int i = tid; i < kHW; i += kTailThreads)
-    if (h[i]) atomicAdd(&hc[i], h[i]);
+#pragma unroll
+  for (int t = 0; t < kNT; ++t) {
+    if (!want[t]) continue;  // uniform
+    const uint32_t v = h[t * 256 + tid];
+    if (v) atomicAdd(&hc[t * 256 + tid], v);
+  }
 }
 
-// Select the byte of each target's key. A target reads the histogram of
-// tail_src() (the same prefix within its pair). Phase 1 sums the copies of
-// every target's source histogram into LDS, phase 2 clears the copies (so
-// every histogram is read before any is cleared or any prefix moves), phase
-// 3 finds the bin that holds each target's rank (one wave per target in
-// turn, 4 bins a lane).
+// Select the byte of each target's key from the histogram of its source
+// (the plan's src: the first target of its pair under the same prefix).
+// Phase 1 sums the copies of every source histogram into LDS, phase 2 clears
+// them (every histogram is read before any is cleared), phase 3 finds the bin
+// that holds each target's rank (one wave per target in turn, 4 bins a lane);
+// then thread 0 assigns the lists (after pass 1) and writes the next plan.
 constexpr int kSelThreads = 1024;
 
 template <int kTP>
@@ -818,23 +844,30 @@ __global__ __launch_bounds__(kSelThreads) void tails_select_kernel(TailWs w, int
   constexpr int kNT = 3 * kTP;
   constexpr int kWaves = kSelThreads / 64;
   __shared__ uint32_t cnt[kNT][256];
-  __shared__ uint64_t s_pre[kNT], pre[kNT];   // new / entry prefixes
+  __shared__ uint64_t pre[kNT], s_pre[kNT];  // entry / new prefixes
   __shared__ int64_t s_rank[kNT], s_len[kNT];
-  __shared__ bool want[kNT];
+  __shared__ int s_src[kNT];
+  __shared__ TailList s_list[kNT];
+  __shared__ uint32_t s_hm;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (threadIdx.x < kNT) {
     const int u = threadIdx.x;
+    pre[u] = w.plan->pre[u];
+    s_pre[u] = pre[u];
+    s_src[u] = w.plan->src[u];
     s_rank[u] = 0;
-    pre[u] = pass ? w.sel[u].prefix : 0ull;
-    want[u] = pass == 0 || w.sel[u].rank > 0;
+    s_len[u] = 0;
+    s_list[u] = w.list[u];
   }
+  if (threadIdx.x == 0) s_hm = w.plan->full | w.plan->list;
   __syncthreads();
+  const uint32_t hm = s_hm;  // the sources that took a histogram
   for (int t = wave; t < kNT; t += kWaves) {
-    const int src = tail_src<kTP>(pre, want, t);
+    if (!((hm >> t) & 1u)) continue;
     uint32_t c[4] = {0u, 0u, 0u, 0u};
 #pragma unroll 4
     for (int cp = 0; cp < kHistCopies; ++cp) {
-      const uint4 q = *reinterpret_cast<const uint4*>(w.hist + cp * kHistStride + src * 256 + 4 * lane);
+      const uint4 q = *reinterpret_cast<const uint4*>(w.hist + cp * kHistStride + t * 256 + 4 * lane);
       c[0] += q.x;
       c[1] += q.y;
       c[2] += q.z;
@@ -846,13 +879,16 @@ __global__ __launch_bounds__(kSelThreads) void tails_select_kernel(TailWs w, int
   __syncthreads();
   for (int i = threadIdx.x; i < kHistCopies * kNT * 64; i += kSelThreads) {
     const int cp = i / (kNT * 64), r = i % (kNT * 64);
-    *reinterpret_cast<uint4*>(w.hist + cp * kHistStride + 4 * r) = make_uint4(0u, 0u, 0u, 0u);
+    if ((hm >> (r >> 6)) & 1u)
+      *reinterpret_cast<uint4*>(w.hist + cp * kHistStride + 4 * r) = make_uint4(0u, 0u, 0u, 0u);
   }
   for (int t = wave; t < kNT; t += kWaves) {
+    int64_t rank = pass ? w.sel[t].rank : 1;  // pass 0: every target, rank from the total below
+    if (rank <= 0) continue;                   // uniform: done, or nothing to select
+    const int src = s_src[t];
     uint32_t c[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) c[k] = cnt[t][4 * lane + k];
-    const int64_t old_rank = pass ? w.sel[t].rank : 0;
+    for (int k = 0; k < 4; ++k) c[k] = cnt[src][4 * lane + k];
     const int64_t lsum = (int64_t)c[0] + c[1] + c[2] + c[3];
     int64_t incl = lsum;  // inclusive scan over lanes
 #pragma unroll
@@ -861,7 +897,6 @@ __global__ __launch_bounds__(kSelThreads) void tails_select_kernel(TailWs w, int
       if (lane >= off) incl += o;
     }
     const int64_t total = __shfl(incl, 63);
-    int64_t rank;
     if (pass == 0) {
       // The pass-0 histogram holds every counted token of the pair.
       const int j = t % kTP;
@@ -878,11 +913,13 @@ __global__ __launch_bounds__(kSelThreads) void tails_select_kernel(TailWs w, int
         rank = (w.k > 0 && total > 0) ? (total > w.k ? total - w.k + 1 : 1) : 0;
       }
       if (j == 0 && lane == 0) w.count[t / kTP] = total;
-    } else {
-      rank = old_rank;
+      if (rank == 0) {
+        if (lane == 0) w.sel[t].rank = 0;
+        continue;
+      }
     }
     const int64_t excl = incl - lsum;
-    if (rank > 0 && excl < rank && rank <= incl) {
+    if (excl < rank && rank <= incl) {
       int64_t below = excl;
       int k = 0;
       while (below + (int64_t)c[k] < rank) below += c[k++];
@@ -897,45 +934,78 @@ __global__ __launch_bounds__(kSelThreads) void tails_select_kernel(TailWs w, int
       s_pre[t] = np;
       s_rank[t] = nr;
       s_len[t] = (int64_t)c[k];
-    } else if (rank == 0 && lane == 0) {
-      w.sel[t].rank = 0;
     }
   }
-  if (pass != 1) return;
   __syncthreads();
   if (threadIdx.x != 0) return;
-  // Lists for passes 3 .. 7, in target order while the key buffer lasts.
-  int64_t used = 0;
+  // Lists for passes 3 .. 7 (after pass 1), in target order while the key
+  // buffer lasts; targets under one prefix share one.
+  if (pass == 1) {
+    int64_t used = 0;
+    for (int u = 0; u < kNT; ++u) {
+      TailList L{0, 0, -1};
+      if (s_rank[u] > 0) {
+        int src = u;
+        for (int v = kTP * (u / kTP); v < u; ++v)
+          if (s_rank[v] > 0 && s_pre[v] == s_pre[u]) {
+            src = v;
+            break;
+          }
+        if (src != u) {
+          L = s_list[src];  // shares that target's list (or its lack of one)
+        } else if (used + s_len[u] <= w.cap) {
+          L = TailList{used, s_len[u], u};
+          used += s_len[u];
+        }
+      }
+      s_list[u] = L;
+      w.list[u] = L;
+    }
+  }
+  // The plan of the next pass: each live target's source, and which sources
+  // histogram over the batch, over a list, or (pass 2) own a list region.
+  const int next = pass + 1;
+  uint32_t full = 0u, list = 0u, own = 0u;
   for (int u = 0; u < kNT; ++u) {
-    TailList L{0, 0, -1};
+    int src = u;
     if (s_rank[u] > 0) {
-      int src = u;
       for (int v = kTP * (u / kTP); v < u; ++v)
         if (s_rank[v] > 0 && s_pre[v] == s_pre[u]) {
           src = v;
           break;
         }
-      if (src != u) {
-        L = w.list[src];  // shares that target's list (or its lack of one)
-      } else if (used + s_len[u] <= w.cap) {
-        L = TailList{used, s_len[u], u};
-        used += s_len[u];
+      if (src == u) {
+        const int32_t ls = next >= 2 ? s_list[u].src : -1;
+        if (next <= 2 || ls < 0) full |= 1u << u;
+        else list |= 1u << u;
+        if (next == 2 && ls == u) own |= 1u << u;
       }
     }
-    w.list[u] = L;
+    w.plan->pre[u] = s_pre[u];
+    w.plan->src[u] = (int8_t)src;
+    w.plan->lsrc[u] = next >= 3 ? s_list[u].src : -1;
   }
+  w.plan->full = full;
+  w.plan->list = list;
+  w.plan->own = own;
 }
 
-// Batch results per pair: fixed chunks of sequences per thread, fixed tree.
+// Batch results, one workgroup per pair: thread j folds the contiguous
+// sequences [j per, (j + 1) per) in order (per depends on N only), then a
+// fixed tree over the threads. The maximum keeps the first sequence (and,
+// within it, the first column) that reaches it.
+constexpr int kFinalThreads = 1024;
+
 template <int kTP>
-__global__ __launch_bounds__(3 * kTailThreads) void tails_final_kernel(TailArgs a, TailWs w) {
-  __shared__ TailPart red[3][kTailThreads];
-  __shared__ int32_t red_seq[3][kTailThreads];
-  const int p = threadIdx.x / kTailThreads, tid = threadIdx.x % kTailThreads;
-  const int64_t per = (a.N + kTailThreads - 1) / kTailThreads;
+__global__ __launch_bounds__(kFinalThreads) void tails_final_kernel(TailArgs a, TailWs w) {
+  __shared__ TailPart red[kFinalThreads];
+  __shared__ int32_t red_seq[kFinalThreads];
+  const int p = blockIdx.x, tid = threadIdx.x;
+  const int64_t per = (a.N + kFinalThreads - 1) / kFinalThreads;
   TailPart x{0.0, 0.0, 0ull, -1, 0};
   int32_t xs = -1;
   const int64_t lo = tid * per, hi = min(a.N, lo + per);
+#pragma unroll 4
   for (int64_t n = lo; n < hi; ++n) {
     const TailPart y = w.part[n * 3 + p];
     x.sum_abs += y.sum_abs;
@@ -947,46 +1017,46 @@ __global__ __launch_bounds__(3 * kTailThreads) void tails_final_kernel(TailArgs 
       xs = (int32_t)n;
     }
   }
-  red[p][tid] = x;
-  red_seq[p][tid] = xs;
+  red[tid] = x;
+  red_seq[tid] = xs;
   __syncthreads();
-  for (int stride = kTailThreads / 2; stride > 0; stride >>= 1) {
+  for (int stride = kFinalThreads / 2; stride > 0; stride >>= 1) {
     if (tid < stride) {
-      TailPart u = red[p][tid];
-      const TailPart v = red[p][tid + stride];
+      TailPart u = red[tid];
+      const TailPart v = red[tid + stride];
       u.sum_abs += v.sum_abs;
       u.sum_prob += v.sum_prob;
       u.count += v.count;
       // After the first steps a thread's sequences interleave with its
       // partner's, so an equal key is decided by the sequence index.
-      const int32_t us = red_seq[p][tid], vs = red_seq[p][tid + stride];
+      const int32_t us = red_seq[tid], vs = red_seq[tid + stride];
       if (v.max_pos >= 0 &&
           (u.max_pos < 0 || v.max_key > u.max_key || (v.max_key == u.max_key && vs < us))) {
         u.max_key = v.max_key;
         u.max_pos = v.max_pos;
-        red_seq[p][tid] = vs;
+        red_seq[tid] = vs;
       }
-      red[p][tid] = u;
+      red[tid] = u;
     }
     __syncthreads();
   }
   if (tid == 0) {
-    const TailPart& r = red[p][0];
+    const TailPart& r = red[0];
     lp_tail_stats o;
     o.count = w.count[p];
     const bool any = o.count > 0;
     double q[3];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      const double lo = __longlong_as_double((long long)w.sel[kTP * p + 2 * j].prefix);
-      const double hi = __longlong_as_double((long long)w.sel[kTP * p + 2 * j + 1].prefix);
-      q[j] = any ? quantile_lerp(o.count, quantile_prob(j), lo, hi) : 0.0;
+      const double qlo = __longlong_as_double((long long)w.sel[kTP * p + 2 * j].prefix);
+      const double qhi = __longlong_as_double((long long)w.sel[kTP * p + 2 * j + 1].prefix);
+      q[j] = any ? quantile_lerp(o.count, quantile_prob(j), qlo, qhi) : 0.0;
     }
     o.q50 = q[0];
     o.q95 = q[1];
     o.q99 = q[2];
     o.max_abs = any ? __longlong_as_double((long long)r.max_key) : 0.0;
-    o.max_seq = any ? red_seq[p][0] : -1;
+    o.max_seq = any ? red_seq[0] : -1;
     o.max_pos = any ? r.max_pos : -1;
     o.sum_abs = r.sum_abs;
     o.sum_prob_abs = r.sum_prob;
@@ -1319,12 +1389,13 @@ static void launch_select(const TailArgs& a, const TailWs& w, hipStream_t stream
     // No sequence: empty histograms give count 0 and no rank to select.
     hipLaunchKernelGGL(tails_select_kernel<kTP>, dim3(1), dim3(kSelThreads), 0, stream, w, 0);
   }
-  hipLaunchKernelGGL(tails_final_kernel<kTP>, dim3(1), dim3(3 * kTailThreads), 0, stream, a, w);
+  hipLaunchKernelGGL(tails_final_kernel<kTP>, dim3(3), dim3(kFinalThreads), 0, stream, a, w);
 }
 
 hipError_t launch_tails(const TailArgs& a, hipStream_t stream) {
   const TailWs w = tail_layout(a.workspace, a.N, a.L, a.worst_k);
-  hipLaunchKernelGGL(tails_init_kernel, dim3(1), dim3(kTailThreads), 0, stream, w);
+  hipLaunchKernelGGL(tails_init_kernel, dim3(kHistCopies), dim3(kTailThreads), 0, stream, w,
+                     a.worst_k > 0 ? kMaxTP : kWorstT);
   if (a.worst_k > 0) {
     launch_select<kMaxTP>(a, w, stream);
     if (a.N > 0 && a.L > 0) {

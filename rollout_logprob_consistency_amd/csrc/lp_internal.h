@@ -164,6 +164,7 @@ struct QuantArgs {
   const float* C;
   const uint8_t* mask;
   int64_t N, L, ld;
+  bool vec;               // rows 16-byte aligned (A, B, C), mask 4-byte aligned, ld % 4 == 0
   double* out;            // [3][N][3]
 };
 

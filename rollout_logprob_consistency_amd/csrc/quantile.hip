@@ -8,14 +8,22 @@
 // One workgroup per (sequence, pair). A key is the bit pattern of the fp64
 // |delta| of a counted token (active, both scores finite); as non-negative
 // doubles the keys order like unsigned integers. The six order statistics
-// the three quantiles interpolate between (quantile_ranks) are found by an
-// 8-pass MSD radix selection, one byte per pass: LDS histograms, the
-// selection inside the workgroup, nothing in global memory but the inputs
-// and the output. Ranks whose selected prefixes agree share one histogram
-// (all six in pass 0). Rows of up to kCache positions keep their keys in LDS
-// after the first read; longer rows recompute them from the scores in every
-// pass. Every count is an integer, so the result does not depend on how the
-// threads are scheduled, and the interpolation is the fp64 quantile_lerp.
+// the three quantiles interpolate between (quantile_ranks) are selected
+// exactly:
+//  1. One read of the scores histograms the keys' top 16 bits. The
+//     difference of two finite fp32 values is 0 or has an fp64 exponent in
+//     [874, 1152] (2^-149 <= |delta| < 2^130), so those 16 bits take 4 465
+//     values (bin 0 holds the key 0); a scan of the 4 465 bins gives every
+//     rank its 16-bit bucket and its rank inside it.
+//  2. The keys of the chosen buckets -- a few percent of the row for
+//     continuous differences -- are read again and gathered in LDS, and each
+//     rank is found by counting: the candidate k of the bucket with
+//     #{j : c_j < k} < r <= #{j : c_j <= k}.
+//  3. When the buckets hold more keys than the gather buffer (many equal or
+//     near-equal differences), the remaining 48 bits are selected by 8-bit
+//     radix passes over the row instead, one byte per pass.
+// Every count is an integer, so the result does not depend on how the
+// threads are scheduled; the interpolation is the fp64 quantile_lerp.
 #include "lp_internal.h"
 
 namespace lp {
@@ -23,134 +31,308 @@ namespace {
 
 constexpr int kQThreads = 256;
 constexpr int kQWaves = kQThreads / 64;
-constexpr int kCache = 4096;           // keys kept in LDS (32 KiB)
-constexpr int kQT = 6;                 // ranks lo / hi of p50, p95, p99
-constexpr uint64_t kNoKey = ~0ull;     // not counted (a real key has bit 63 clear)
+constexpr int kQT = 6;                  // ranks lo / hi of p50, p95, p99
+constexpr uint64_t kNoKey = ~0ull;      // not counted (a real key has bit 63 clear)
+constexpr uint32_t kTop16Lo = 874u << 4;          // top 16 bits of 2^-149
+constexpr uint32_t kTop16Hi = (1152u << 4) | 15u;  // top 16 bits just below 2^130
+constexpr int kBins = (int)(kTop16Hi - kTop16Lo) + 2;  // 4 465 (bin 0: the key 0)
+constexpr int kBinsPerThread = (kBins + kQThreads - 1) / kQThreads;  // 18
+constexpr int kCand = 512;              // gathered candidates
+
+static_assert(kQThreads * kBinsPerThread >= kBins, "every bin belongs to a thread");
 
 __device__ __forceinline__ uint64_t key_of(float l, float r, bool act) {
   if (!act || !__builtin_isfinite(l) || !__builtin_isfinite(r)) return kNoKey;
   return (uint64_t)__double_as_longlong(fabs((double)l - (double)r));
 }
 
+// Bucket of a counted key: 0 for the key 0, else its top 16 bits relative to
+// the smallest nonzero difference (monotone in the key).
+__device__ __forceinline__ uint32_t bucket(uint64_t k) {
+  const uint32_t t = (uint32_t)(k >> 48);
+  return k == 0 ? 0u : min(max(t, kTop16Lo), kTop16Hi) - kTop16Lo + 1u;
+}
+
+// Scores and mask of the four positions i .. i + 3 of a row (inactive past
+// L): one 16-byte load per score array and a 4-byte mask load when the rows
+// allow them, element loads otherwise. Raw values, so that a chunk's loads
+// can be in flight while the previous chunk is processed.
+struct Raw4 {
+  float l[4], r[4];
+  bool act[4];
+};
+
+template <bool kVec>
+__device__ __forceinline__ Raw4 load4(const float* Lp, const float* Rp, const uint8_t* M,
+                                      int64_t L, int64_t i) {
+  Raw4 q;
+  if (kVec && i + 4 <= L) {
+    const float4 l = *reinterpret_cast<const float4*>(Lp + i);
+    const float4 r = *reinterpret_cast<const float4*>(Rp + i);
+    const uint32_t m = *reinterpret_cast<const uint32_t*>(M + i);
+    q.l[0] = l.x; q.l[1] = l.y; q.l[2] = l.z; q.l[3] = l.w;
+    q.r[0] = r.x; q.r[1] = r.y; q.r[2] = r.z; q.r[3] = r.w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q.act[e] = ((m >> (8 * e)) & 0xFFu) != 0;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      q.act[e] = i + e < L && M[i + e] != 0;
+      q.l[e] = q.act[e] ? Lp[i + e] : 0.f;
+      q.r[e] = q.act[e] ? Rp[i + e] : 0.f;
+    }
+  }
+  return q;
+}
+
+__device__ __forceinline__ void keys_of(const Raw4& q, uint64_t (&k)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) k[e] = key_of(q.l[e], q.r[e], q.act[e]);
+}
+
+// Wave-aggregated LDS histogram increment of bin `b` for the lanes with hit:
+// when every hitting lane has the bin of the wave's first lane (read with
+// readfirstlane, no LDS round trip), one atomic adds them all.
+__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t b, bool hit, int lane) {
+  const uint64_t hb = __ballot(hit);
+  if (hb == 0) return;
+  const uint32_t b0 = __builtin_amdgcn_readfirstlane(b);
+  if (__ballot(hit && b != b0) == 0) {
+    if (lane == __ffsll((long long)hb) - 1) atomicAdd(&h[b0], (uint32_t)__popcll(hb));
+  } else if (hit) {
+    atomicAdd(&h[b], 1u);
+  }
+}
+
+template <bool kVec>
 __global__ __launch_bounds__(kQThreads) void seq_quantile_kernel(QuantArgs a) {
-  __shared__ uint64_t keys[kCache];
-  __shared__ uint32_t hist[kQT][256];
-  __shared__ uint64_t s_pre[kQT];
-  __shared__ int64_t s_rank[kQT];
+  // The 4 465-bin histogram of step 1; the 8-bit histograms of step 3 reuse it.
+  __shared__ uint32_t hist[kQThreads * kBinsPerThread];
+  __shared__ uint64_t cand[kCand];
   __shared__ uint32_t s_part[kQWaves];
+  __shared__ uint64_t s_pre[kQT], s_val[kQT];
+  __shared__ int64_t s_rank[kQT];
+  __shared__ uint32_t s_ncand, s_gather;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t n = blockIdx.x;
-  const int p = blockIdx.y;  // pair: 0 (A,B), 1 (B,C), 2 (A,C)
+  // Workgroups are dealt to the 8 XCDs in turn by their index, and each XCD
+  // has its own L2. Index 24 g + 8 p + x takes pair p of sequence 8 g + x, so
+  // the three workgroups of a sequence (each reads two of its three score
+  // arrays) run on one XCD at about the same time and share the reads.
+  const int64_t b = blockIdx.x;
+  const int64_t n = 8 * (b / 24) + (b % 8);
+  const int p = (int)((b % 24) / 8);  // pair: 0 (A,B), 1 (B,C), 2 (A,C)
+  if (n >= a.N) return;
   const float* Lp = (p == 1 ? a.B : a.A) + n * a.ld;
   const float* Rp = (p == 0 ? a.B : a.C) + n * a.ld;
   const uint8_t* M = a.mask + n * a.ld;
-  const bool cached = a.L <= kCache;
-
-  // First read: keys (into LDS when the row fits) and the count.
-  uint32_t mine = 0u;
-  for (int64_t i = tid; i < a.L; i += kQThreads) {
-    const uint64_t k = key_of(Lp[i], Rp[i], M[i] != 0);
-    if (cached) keys[i] = k;
-    mine += k != kNoKey ? 1u : 0u;
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mine += (uint32_t)__shfl_xor((int)mine, off);
-  if (lane == 0) s_part[wave] = mine;
-  __syncthreads();
-  int64_t count = 0;
-#pragma unroll
-  for (int v = 0; v < kQWaves; ++v) count += s_part[v];
   double* out = a.out + ((size_t)p * (size_t)a.N + (size_t)n) * 3;
+  // Every thread takes the same number of steps over the row (four
+  // consecutive positions each), so whole waves reach the ballots; positions
+  // past L hold no key.
+  constexpr int64_t kStep = 4 * kQThreads;
+  const int64_t Lw = (a.L + kStep - 1) / kStep * kStep;
+
+  for (int i = tid; i < kQThreads * kBinsPerThread; i += kQThreads) hist[i] = 0u;
+  if (tid == 0) {
+    s_ncand = 0u;
+    s_gather = 0u;
+  }
+  __syncthreads();
+
+  // Each walk over the row keeps the next chunk's loads in flight while it
+  // processes the current one (the last chunk is loaded twice rather than
+  // branching); `visit` sees the four keys of every position of the row.
+  auto walk = [&](auto&& visit) {
+    Raw4 q = load4<kVec>(Lp, Rp, M, a.L, 4 * tid);
+    for (int64_t i = 4 * tid; i < Lw; i += kStep) {
+      const Raw4 nq = load4<kVec>(Lp, Rp, M, a.L, min(i + kStep, Lw - kStep + 4 * tid));
+      uint64_t k[4];
+      keys_of(q, k);
+      visit(k);
+      q = nq;
+    }
+  };
+
+  // Step 1: the 16-bit bucket histogram.
+  walk([&](const uint64_t (&k)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hist_add(hist, bucket(k[e]), k[e] != kNoKey, lane);
+  });
+  __syncthreads();
+  // Thread j owns bins [18 j, 18 j + 18): their sum, an exclusive scan of the
+  // sums over the threads (the count is the last inclusive value).
+  const int b0 = tid * kBinsPerThread;
+  uint32_t mine = 0u;
+#pragma unroll
+  for (int b = 0; b < kBinsPerThread; ++b) mine += hist[b0 + b];
+  uint32_t incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_up((int)incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) s_part[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0u, count32 = 0u;
+#pragma unroll
+  for (int v = 0; v < kQWaves; ++v) {
+    before += v < wave ? s_part[v] : 0u;
+    count32 += s_part[v];
+  }
+  const int64_t count = count32;
   if (count == 0) {
     if (tid < 3) out[tid] = 0.0;
     return;
   }
-  if (tid < kQT) {
+  const int64_t excl = (int64_t)before + incl - mine;
+  // The thread whose bins hold rank r finds the bucket and the rank within.
+#pragma unroll
+  for (int t = 0; t < kQT; ++t) {
     int64_t lo, hi;
-    quantile_ranks(count, quantile_prob(tid >> 1), &lo, &hi);
-    s_rank[tid] = (tid & 1) ? hi : lo;
-    s_pre[tid] = 0ull;
+    quantile_ranks(count, quantile_prob(t >> 1), &lo, &hi);
+    const int64_t r = (t & 1) ? hi : lo;
+    if (excl < r && r <= excl + mine) {
+      int64_t below = excl;
+      int b = 0;
+      while (below + (int64_t)hist[b0 + b] < r) below += hist[b0 + b++];
+      const uint32_t bk = (uint32_t)(b0 + b);
+      // Bucket 0 holds only the key 0: that rank is settled.
+      s_pre[t] = bk == 0 ? 0ull : (uint64_t)(bk - 1u + kTop16Lo);
+      s_rank[t] = bk == 0 ? 0 : r - below;
+      s_val[t] = 0ull;
+      if (bk != 0) {
+        // Count the bucket's keys once per distinct bucket (the first rank
+        // in it adds them).
+        bool first = true;
+        for (int u = 0; u < t; ++u) {
+          int64_t ulo, uhi;
+          quantile_ranks(count, quantile_prob(u >> 1), &ulo, &uhi);
+          const int64_t ur = (u & 1) ? uhi : ulo;
+          first = first && !(excl < ur && ur <= excl + mine && ur > below &&
+                             ur <= below + (int64_t)hist[bk]);
+        }
+        if (first) atomicAdd(&s_ncand, hist[bk]);
+      }
+    }
   }
   __syncthreads();
+  const bool gather = s_ncand <= (uint32_t)kCand;
+  uint64_t pre[kQT];
+  bool live[kQT];
+#pragma unroll
+  for (int t = 0; t < kQT; ++t) {
+    pre[t] = s_pre[t];
+    live[t] = s_rank[t] > 0;
+  }
 
-  // Every thread takes the same number of steps, so whole waves reach the
-  // ballots (positions past L hold no key).
-  const int64_t Lw = (a.L + kQThreads - 1) / kQThreads * kQThreads;
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
-    uint64_t pre[kQT];
-    int src[kQT];
-    bool use[kQT];  // this target keeps the histogram of its prefix
-    bool any = false;
+  if (gather) {
+    // Step 2: gather the chosen buckets' keys, then rank by counting.
+    walk([&](const uint64_t (&kk)[4]) {
 #pragma unroll
-    for (int t = 0; t < kQT; ++t) pre[t] = s_pre[t];
+      for (int e = 0; e < 4; ++e) {
+        const uint64_t k = kk[e];
+        bool m = false;
 #pragma unroll
-    for (int t = 0; t < kQT; ++t) {
-      const bool live = s_rank[t] > 0;
-      src[t] = t;
-      for (int u = 0; u < t; ++u)
-        if (s_rank[u] > 0 && pre[u] == pre[t]) {
-          src[t] = u;
-          break;
-        }
-      use[t] = live && src[t] == t;
-      any = any || live;
-    }
-    if (!any) break;  // uniform: read from LDS after a barrier
-    for (int i = tid; i < kQT * 256; i += kQThreads) (&hist[0][0])[i] = 0u;
+        for (int t = 0; t < kQT; ++t) m = m || (live[t] && k != kNoKey && (k >> 48) == pre[t]);
+        const uint64_t mb = __ballot(m);
+        if (mb == 0) continue;
+        const int first = __ffsll((long long)mb) - 1;
+        uint32_t base = 0u;
+        if (lane == first) base = atomicAdd(&s_gather, (uint32_t)__popcll(mb));
+        base = (uint32_t)__shfl((int)base, first);
+        if (m) cand[base + (uint32_t)__popcll(mb & ((1ull << lane) - 1ull))] = k;
+      }
+    });
     __syncthreads();
-    for (int64_t i = tid; i < Lw; i += kQThreads) {
-      const uint64_t k = i < a.L ? (cached ? keys[i] : key_of(Lp[i], Rp[i], M[i] != 0)) : kNoKey;
-      const bool ok = k != kNoKey;
-      const uint32_t digit = (uint32_t)(k >> shift) & 255u;
+    const int nc = (int)s_gather;
+    for (int i = tid; i < nc; i += kQThreads) {
+      const uint64_t k = cand[i];
+      const uint64_t top = k >> 48;
+      int32_t less = 0, leq = 0;
+#pragma unroll 8
+      for (int j = 0; j < nc; ++j) {
+        const uint64_t c = cand[j];
+        const bool same = (c >> 48) == top;
+        less += (same && c < k) ? 1 : 0;
+        leq += (same && c <= k) ? 1 : 0;
+      }
+#pragma unroll
+      for (int t = 0; t < kQT; ++t)
+        if (live[t] && top == pre[t] && less < s_rank[t] && s_rank[t] <= leq) s_val[t] = k;
+    }
+    __syncthreads();
+  } else {
+    // Step 3: 8-bit radix passes over the remaining 48 bits, from the row.
+    uint32_t (*h8)[256] = reinterpret_cast<uint32_t (*)[256]>(hist);
+    for (int pass = 2; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
+      int src[kQT];
+      bool use[kQT];
+      bool any = false;
 #pragma unroll
       for (int t = 0; t < kQT; ++t) {
-        if (!use[t]) continue;  // uniform
-        const bool hit = ok && (pass == 0 || (k >> (shift + 8)) == pre[t]);
-        const uint64_t hb = __ballot(hit);
-        if (hb == 0) continue;
-        // One atomic for the wave when all its hits share a bin.
-        const int first = __ffsll((long long)hb) - 1;
-        const uint32_t d0 = (uint32_t)__shfl((int)digit, first);
-        if (__ballot(hit && digit != d0) == 0) {
-          if (lane == first) atomicAdd(&hist[t][d0], (uint32_t)__popcll(hb));
-        } else if (hit) {
-          atomicAdd(&hist[t][digit], 1u);
+        pre[t] = s_pre[t];
+        live[t] = s_rank[t] > 0;
+      }
+#pragma unroll
+      for (int t = 0; t < kQT; ++t) {
+        src[t] = t;
+        for (int u = 0; u < t; ++u)
+          if (live[u] && pre[u] == pre[t]) {
+            src[t] = u;
+            break;
+          }
+        use[t] = live[t] && src[t] == t;
+        any = any || live[t];
+      }
+      if (!any) break;  // uniform: from LDS after a barrier
+      for (int i = tid; i < kQT * 256; i += kQThreads) (&h8[0][0])[i] = 0u;
+      __syncthreads();
+      walk([&](const uint64_t (&kk)[4]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint64_t k = kk[e];
+          const uint32_t digit = (uint32_t)(k >> shift) & 255u;
+#pragma unroll
+          for (int t = 0; t < kQT; ++t) {
+            if (!use[t]) continue;  // uniform
+            hist_add(h8[t], digit, k != kNoKey && (k >> (shift + 8)) == pre[t], lane);
+          }
+        }
+      });
+      __syncthreads();
+      for (int t = wave; t < kQT; t += kQWaves) {
+        const int64_t rank = s_rank[t];
+        if (rank <= 0) continue;  // uniform within the wave
+        uint32_t c[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c[k] = h8[src[t]][4 * lane + k];
+        const uint32_t lsum = c[0] + c[1] + c[2] + c[3];
+        uint32_t inc = lsum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t o = (uint32_t)__shfl_up((int)inc, off);
+          if (lane >= off) inc += o;
+        }
+        const int64_t ex = (int64_t)inc - lsum;
+        if (ex < rank && rank <= (int64_t)inc) {
+          int64_t below = ex;
+          int k = 0;
+          while (below + (int64_t)c[k] < rank) below += c[k++];
+          s_pre[t] = (pre[t] << 8) | (uint64_t)(4 * lane + k);
+          s_rank[t] = rank - below;
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
-    // One wave per target in turn: the bin that holds the target's rank.
-    for (int t = wave; t < kQT; t += kQWaves) {
-      const int64_t rank = s_rank[t];
-      if (rank <= 0) continue;  // uniform within the wave
-      uint32_t c[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) c[k] = hist[src[t]][4 * lane + k];
-      const int64_t lsum = (int64_t)c[0] + c[1] + c[2] + c[3];
-      int64_t incl = lsum;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int64_t o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      const int64_t excl = incl - lsum;
-      if (excl < rank && rank <= incl) {
-        int64_t below = excl;
-        int k = 0;
-        while (below + (int64_t)c[k] < rank) below += c[k++];
-        const uint32_t bin = 4 * lane + k;
-        // A key with a zero top byte is 0: the difference of two fp32 scores
-        // is 0 or at least 2^-149 in magnitude (a top byte of at least 0x36).
-        s_pre[t] = (pass ? (pre[t] << 8) : 0ull) | bin;
-        s_rank[t] = (pass == 0 && bin == 0) ? 0 : rank - below;
-      }
-    }
+    for (int t = 0; t < kQT; ++t)
+      if (tid == t && s_rank[t] > 0) s_val[t] = s_pre[t];  // the full key
     __syncthreads();
   }
   if (tid < 3) {
-    const double lo = __longlong_as_double((long long)s_pre[2 * tid]);
-    const double hi = __longlong_as_double((long long)s_pre[2 * tid + 1]);
+    const double lo = __longlong_as_double((long long)s_val[2 * tid]);
+    const double hi = __longlong_as_double((long long)s_val[2 * tid + 1]);
     out[tid] = quantile_lerp(count, quantile_prob(tid), lo, hi);
   }
 }
@@ -158,7 +340,11 @@ __global__ __launch_bounds__(kQThreads) void seq_quantile_kernel(QuantArgs a) {
 }  // namespace
 
 hipError_t launch_seq_quantiles(const QuantArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(seq_quantile_kernel, dim3((unsigned)a.N, 3), dim3(kQThreads), 0, stream, a);
+  const unsigned blocks = (unsigned)(3 * ((a.N + 7) / 8) * 8);  // 24 per group of 8 sequences
+  if (a.vec)
+    hipLaunchKernelGGL(seq_quantile_kernel<true>, dim3(blocks), dim3(kQThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(seq_quantile_kernel<false>, dim3(blocks), dim3(kQThreads), 0, stream, a);
   return hipGetLastError();
 }
 
