@@ -6,7 +6,8 @@ Compiles every .hip file under csrc/ into one shared library next to this
 file, with hipcc for gfx950. Packed-fp32 instructions are disabled for all
 device code. The device assembly of score.hip is then checked for wait-state
 hazards around its inline-assembly MFMAs (isa_check.py); a violation fails
-the build.
+the build. The comparison kernel's assembly is checked for ds_bpermute (its
+reductions use DPP, ds_swizzle and readlane).
 """
 
 from __future__ import annotations
@@ -69,6 +70,7 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     check_score_isa(objdir, extra, verbose)
+    check_compare_isa(objdir, extra, verbose)
     os.replace(tmp, LIB)
     return LIB
 
@@ -92,3 +94,20 @@ def check_score_isa(objdir: str, extra: list[str] | None = None, verbose: bool =
 
 if __name__ == "__main__":
     print(build(verbose="--verbose" in sys.argv))
+
+
+def check_compare_isa(objdir: str, extra: list[str] | None = None, verbose: bool = False) -> None:
+    """Compile compare.hip to device assembly and check that the comparison
+    kernel's reductions use no ds_bpermute (DPP, ds_swizzle and readlane only)."""
+    from rollout_logprob_consistency_amd import isa_check
+    src = os.path.join(CSRC, "compare.hip")
+    out = os.path.join(objdir, "compare.device.s")
+    cmd = [hipcc(), *compile_flags(), *(extra or []), "--cuda-device-only", "-S", src, "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stdout}\n{r.stderr}")
+    problems = isa_check.check_no_bpermute(open(out).read(), "compare_kernel")
+    if problems:
+        raise RuntimeError("compare_kernel cross-lane check failed:\n" + "\n".join(problems))

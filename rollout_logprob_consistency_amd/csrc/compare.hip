@@ -36,12 +36,68 @@
 // read the mask and each score array twice; the second reads hit in cache.
 #include <math.h>
 
+#include <type_traits>
+
 #include "lp_internal.h"
 
 namespace lp {
 namespace {
 
 constexpr int kWindow = 256;  // positions per wave step (64 lanes x 4)
+
+// ---- Cross-lane steps of the XOR butterflies, without the LDS crossbar.
+// Step m pairs lane l with lane l ^ m. Every step leaves both lanes of a pair
+// with the same value, so after steps 1 and 2 a quad is uniform and the half-
+// row mirror (lane 7 - l of its 8) reads what lane l ^ 4 holds; after step 4
+// the row mirror (lane 15 - l) reads lane l ^ 8's value. Step 16 swaps the
+// 16-lane halves of each 32 with ds_swizzle; after it each 32-lane half is
+// uniform and step 32 reads lanes 0 and 32 (readlane: a wave-uniform value).
+template <int kM>
+__device__ __forceinline__ int xlane(int v) {
+  if constexpr (kM == 1) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  else if constexpr (kM == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  else if constexpr (kM == 4) return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  else if constexpr (kM == 8) return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+  else return __builtin_amdgcn_ds_swizzle(v, 0x401F);  // kM == 16: bit mode, lane ^ 16
+}
+
+template <int kM>
+__device__ __forceinline__ double xlane(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = xlane<kM>((int)(uint32_t)b), hi = xlane<kM>((int)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// The value of lane `l` once each 32-lane half is uniform.
+__device__ __forceinline__ int lane_value(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ double lane_value(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Sum / maximum over the wave by the fixed XOR butterfly; every lane gets the
+// value lane 0 forms, ((x_0 + x_1) + (x_2 + x_3)) + ... (fp64 addition is
+// commutative, so both lanes of a step agree bitwise).
+template <typename T>
+__device__ __forceinline__ T wave_sum(T x) {
+  x += xlane<1>(x);
+  x += xlane<2>(x);
+  x += xlane<4>(x);
+  x += xlane<8>(x);
+  x += xlane<16>(x);
+  return lane_value(x, 0) + lane_value(x, 32);
+}
+
+__device__ __forceinline__ double wave_max(double x) {
+  x = fmax(x, xlane<1>(x));
+  x = fmax(x, xlane<2>(x));
+  x = fmax(x, xlane<4>(x));
+  x = fmax(x, xlane<8>(x));
+  x = fmax(x, xlane<16>(x));
+  return fmax(lane_value(x, 0), lane_value(x, 32));
+}
 
 // Order-sensitive state of one pair over a segment of active tokens.
 struct Runs {
@@ -87,9 +143,10 @@ __device__ __forceinline__ double exp_f64(double x) {
   return ldexp(p, (int)k);
 }
 
-// 7 waves per SIMD: the 68 registers this allows hold the whole state without
-// spilling (at 8 waves the spill area of 24 bytes per lane cost more write
-// traffic than the extra wave saved).
+// Instantiated for per-token output requested or not (kPT) and for the
+// bitwise mismatch test or the atol one (kBitwise), so the common call
+// carries no per-token bookkeeping and no tolerance test.
+template <bool kPT, bool kBitwise>
 __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(7))) void compare_kernel(
     CompareArgs a) {
   const int lane = threadIdx.x & 63;
@@ -99,7 +156,7 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(7))) void c
   const float* Rp = (p == 0 ? a.B : a.C) + n * a.ld;
   const uint8_t* M = a.mask + n * a.ld;
   const size_t plane = (size_t)a.N * (size_t)a.L;
-  float* pt_row = a.per_token ? a.per_token + (size_t)(3 * p) * plane + (size_t)n * a.L : nullptr;
+  float* pt_row = kPT ? a.per_token + (size_t)(3 * p) * plane + (size_t)n * a.L : nullptr;
   const double clip = a.tis_clip;
   const double one_tis = fmin(1.0, clip);  // TIS weight of a token with d = 0
   const float nan = __builtin_nanf("");
@@ -131,10 +188,11 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(7))) void c
           } else {
             const double dl = (double)l - (double)r;  // non-finite iff l or r is
             const double ad = fabs(dl);
-            // atol < 0 (bitwise mode) never holds here, nor does a NaN delta.
-            if (!(ad <= a.atol)) dif |= 1u << e;
+            // Different bits are a mismatch; with atol, unless |delta| <= atol
+            // (never true for a NaN delta).
+            if (kBitwise || !(ad <= a.atol)) dif |= 1u << e;
             if (__builtin_isfinite(dl)) {
-              mx = ad > mx ? ad : mx;
+              mx = fmax(ad, mx);  // both finite and >= 0: the exact maximum
               sa += ad;
               ss += dl;
               o_abs = (float)ad;
@@ -166,7 +224,7 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(7))) void c
             }
           }
         }
-        if (pt_row && i0 + e < a.L) {
+        if (kPT && i0 + e < a.L) {
           pt_row[i0 + e] = o_abs;
           pt_row[plane + i0 + e] = o_k3;
           pt_row[2 * plane + i0 + e] = o_tis;
@@ -201,18 +259,29 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(7))) void c
           }
         }
         int sn = k;
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
+        // Ordered XOR butterfly: the lower lanes' segment is the left operand.
+        auto step = [&](auto m_tag, int m) __attribute__((always_inline)) {
+          constexpr int kM = decltype(m_tag)::value;
           Runs o;
-          o.first = __shfl_xor(s.first, m);
-          o.pre = __shfl_xor(s.pre, m);
-          o.suf = __shfl_xor(s.suf, m);
-          o.best = __shfl_xor(s.best, m);
-          const int on = __shfl_xor(sn, m);
+          o.first = xlane<kM>(s.first);
+          o.pre = xlane<kM>(s.pre);
+          o.suf = xlane<kM>(s.suf);
+          o.best = xlane<kM>(s.best);
+          const int on = xlane<kM>(sn);
           s = (lane & m) ? runs_combine(o, on, s, sn) : runs_combine(s, sn, o, on);
           sn += on;
-        }
-        win = s;
+        };
+        step(std::integral_constant<int, 1>{}, 1);
+        step(std::integral_constant<int, 2>{}, 2);
+        step(std::integral_constant<int, 4>{}, 4);
+        step(std::integral_constant<int, 8>{}, 8);
+        step(std::integral_constant<int, 16>{}, 16);
+        // Step 32: each 32-lane half is uniform; lanes 0 and 32 hold them.
+        const Runs lo = {lane_value(s.first, 0), lane_value(s.pre, 0), lane_value(s.suf, 0),
+                         lane_value(s.best, 0)};
+        const Runs hi = {lane_value(s.first, 32), lane_value(s.pre, 32), lane_value(s.suf, 32),
+                         lane_value(s.best, 32)};
+        win = runs_combine(lo, lane_value(sn, 0), hi, lane_value(sn, 32));
       }
       seq = runs_combine(seq, seq_n, win, wn);
       seq_n += wn;
@@ -278,7 +347,7 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(7))) void c
         const double tis = fmin(E, clip);
         if (__builtin_isfinite(k3)) sk2 += k3; else k3n += 1;
         st2 += tis;
-        if (pt_row) {
+        if (kPT) {
           pt_row[plane + i] = (float)k3;
           pt_row[2 * plane + i] = (float)tis;
         }
@@ -288,18 +357,14 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(7))) void c
     st += st2;
   }
 
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    mism += __shfl_xor(mism, m);
-    nonf += __shfl_xor(nonf, m);
-    k3n += __shfl_xor(k3n, m);
-    const double omx = __shfl_xor(mx, m);
-    mx = omx > mx ? omx : mx;
-    sa += __shfl_xor(sa, m);
-    ss += __shfl_xor(ss, m);
-    sk += __shfl_xor(sk, m);
-    st += __shfl_xor(st, m);
-  }
+  mism = wave_sum(mism);
+  nonf = wave_sum(nonf);
+  k3n = wave_sum(k3n);
+  mx = wave_max(mx);  // |delta| >= 0 and finite: fmax is the exact maximum
+  sa = wave_sum(sa);
+  ss = wave_sum(ss);
+  sk = wave_sum(sk);
+  st = wave_sum(st);
 
   if (lane == 0) {
     lp_seq_stats* o = a.out + (size_t)p * a.N + n;
@@ -322,7 +387,15 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(7))) void c
 }  // namespace
 
 hipError_t launch_compare(const CompareArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(compare_kernel, dim3((unsigned)a.N), dim3(192), 0, stream, a);
+  const dim3 g((unsigned)a.N), b(192);
+  const bool bitwise = a.atol < 0.0;
+  if (a.per_token) {
+    if (bitwise) hipLaunchKernelGGL((compare_kernel<true, true>), g, b, 0, stream, a);
+    else hipLaunchKernelGGL((compare_kernel<true, false>), g, b, 0, stream, a);
+  } else {
+    if (bitwise) hipLaunchKernelGGL((compare_kernel<false, true>), g, b, 0, stream, a);
+    else hipLaunchKernelGGL((compare_kernel<false, false>), g, b, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

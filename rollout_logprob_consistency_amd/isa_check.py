@@ -118,3 +118,31 @@ def check_asm(asm: str, kernel_filter: str = "score_tile_kernel") -> list[str]:
         if n_asm_mfma == 0:
             problems.append(f"{name}: no inline-assembly MFMA found (check is stale)")
     return problems
+
+
+# ---------------------------------------------------------------------------
+# Cross-lane reductions of the comparison kernel: its butterflies run on DPP
+# row operations, ds_swizzle and readlane, never on ds_bpermute (the LDS
+# crossbar), which this check enforces on the built assembly.
+# ---------------------------------------------------------------------------
+
+def kernel_bodies(asm: str, name_part: str) -> dict[str, str]:
+    """Assembly text of every kernel whose symbol contains name_part."""
+    out = {}
+    for m in re.finditer(r"^(_Z\S*%s\S*):" % re.escape(name_part), asm, re.M):
+        end = asm.find(".Lfunc_end", m.end())
+        out[m.group(1)] = asm[m.end():end if end >= 0 else len(asm)]
+    return out
+
+
+def check_no_bpermute(asm: str, name_part: str = "compare_kernel") -> list[str]:
+    """Problems: a missing kernel, or ds_bpermute / ds_permute inside it."""
+    bodies = kernel_bodies(asm, name_part)
+    if not bodies:
+        return [f"no kernel matching {name_part!r} in the assembly"]
+    problems = []
+    for name, body in bodies.items():
+        n = len(re.findall(r"^\s*ds_(?:b)?permute_b32", body, re.M))
+        if n:
+            problems.append(f"{name}: {n} ds_bpermute/ds_permute instruction(s)")
+    return problems

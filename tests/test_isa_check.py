@@ -69,3 +69,30 @@ def test_built_score_kernel_is_clean():
     if not os.path.exists(path):
         pytest.skip("no device assembly: the library has not been built here")
     assert isa_check.check_asm(open(path).read()) == []
+
+
+def cmp_kernel(body_lines):
+    body = "\n".join("\t" + l for l in body_lines)
+    return "_ZN2lp14compare_kernelEv:\n" + body + "\n.Lfunc_end1:\n"
+
+
+def test_compare_kernel_without_bpermute_passes():
+    lines = ["v_mov_b32_dpp v2, v0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf",
+             "ds_swizzle_b32 v3, v0 offset:swizzle(SWAP,16)", "v_readlane_b32 s4, v3, 32"]
+    assert isa_check.check_no_bpermute(cmp_kernel(lines)) == []
+
+
+def test_compare_kernel_with_bpermute_fails():
+    lines = ["v_lshlrev_b32_e32 v1, 2, v1", "ds_bpermute_b32 v2, v1, v0"]
+    assert isa_check.check_no_bpermute(cmp_kernel(lines))
+    assert isa_check.check_no_bpermute("nothing here")     # the kernel must be found
+
+
+def test_built_compare_kernel_has_no_bpermute():
+    # The assembly the last build checked (build() writes it).
+    path = os.path.join(ROOT, "_build", "compare.device.s")
+    if not os.path.exists(path):
+        pytest.skip("no build assembly; run the build first")
+    asm = open(path).read()
+    assert isa_check.kernel_bodies(asm, "compare_kernel")
+    assert isa_check.check_no_bpermute(asm) == []
