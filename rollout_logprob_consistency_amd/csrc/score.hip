@@ -47,6 +47,8 @@
 // discarded.
 #include <math.h>
 
+#include <type_traits>
+
 #include "lp_internal.h"
 
 namespace lp {
@@ -149,6 +151,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // exactly the same operations as without kStats.
 constexpr int kNoRow = 0x7FFFFFFF;
 
+// The value lane l ^ 16 (kOff = 16) or lane l ^ 32 (kOff = 32) holds, by the
+// VALU lane swaps of gfx950 instead of an LDS permute: swapping x with itself
+// puts, in the first result, the even rows' (lower half's) values into the
+// odd rows (upper half) and, in the second, the odd rows' into the even rows.
+template <int kOff>
+__device__ __forceinline__ int xor_lane(int x) {
+  const int lane = (int)__lane_id();
+  if constexpr (kOff == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? (int)r[0] : (int)r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? (int)r[0] : (int)r[1];
+  }
+}
+
+template <int kOff>
+__device__ __forceinline__ float xor_lane(float x) {
+  return __int_as_float(xor_lane<kOff>(__float_as_int(x)));
+}
+
 template <bool kStats, class Get>
 __device__ __forceinline__ void wave_lse(Get v, float scale2, int lg, float& m_out, float& s_out,
                                          float& q_out, int& i_out) {
@@ -168,33 +191,42 @@ __device__ __forceinline__ void wave_lse(Get v, float scale2, int lg, float& m_o
       for (int r = 3; r >= 0; --r) li = (v(i, r) == mr) ? 16 * i + 4 * lg + r : li;
     if (mr == NEG_INF) li = kNoRow;
   }
-#pragma unroll
-  for (int off = 16; off <= 32; off <<= 1) {
-    const float mo = __shfl_xor(mr, off);
+  auto max_step = [&](auto off_tag) __attribute__((always_inline)) {
+    constexpr int kOff = decltype(off_tag)::value;
+    const float mo = xor_lane<kOff>(mr);
     if (kStats) {
-      const int lo = __shfl_xor(li, off);
+      const int lo = xor_lane<kOff>(li);
       li = (mo > mr) ? lo : ((mr > mo) ? li : min(li, lo));
     }
     mr = fmaxf(mr, mo);
-  }
+  };
+  max_step(std::integral_constant<int, 16>{});
+  max_step(std::integral_constant<int, 32>{});
   const float m = mr * scale2;
   float s = 0.f, q = 0.f;
   if (mr != NEG_INF) {
+    // All exponentials first, then the sums in the same order: each exp2
+    // result is used well after it is formed (no wait states between them).
+    float e[kSubV * 4], d[kStats ? kSubV * 4 : 1];
 #pragma unroll
     for (int i = 0; i < kSubV; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float d = __builtin_fmaf(v(i, r), scale2, -m);
-        const float e = fast_exp2(d);
-        s += e;
-        if (kStats) q = __builtin_fmaf(e, fmaxf(d, -3.0e38f), q);  // -inf row: 0 * finite
+        const float di = __builtin_fmaf(v(i, r), scale2, -m);
+        e[4 * i + r] = fast_exp2(di);
+        if (kStats) d[4 * i + r] = di;
       }
+#pragma unroll
+    for (int k = 0; k < kSubV * 4; ++k) {
+      s += e[k];
+      if (kStats) q = __builtin_fmaf(e[k], fmaxf(d[k], -3.0e38f), q);  // -inf row: 0 * finite
+    }
   }
-  s += __shfl_xor(s, 16);
-  s += __shfl_xor(s, 32);
+  s += xor_lane<16>(s);
+  s += xor_lane<32>(s);
   if (kStats) {
-    q += __shfl_xor(q, 16);
-    q += __shfl_xor(q, 32);
+    q += xor_lane<16>(q);
+    q += xor_lane<32>(q);
   }
   m_out = m;
   s_out = s;
