@@ -92,10 +92,6 @@ def check_score_isa(objdir: str, extra: list[str] | None = None, verbose: bool =
         raise RuntimeError("inline-assembly MFMA hazard check failed:\n" + "\n".join(problems[:20]))
 
 
-if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
-
-
 def check_compare_isa(objdir: str, extra: list[str] | None = None, verbose: bool = False) -> None:
     """Compile compare.hip to device assembly and check that the comparison
     kernel's reductions use no ds_bpermute (DPP, ds_swizzle and readlane only)."""
@@ -111,3 +107,7 @@ def check_compare_isa(objdir: str, extra: list[str] | None = None, verbose: bool
     problems = isa_check.check_no_bpermute(open(out).read(), "compare_kernel")
     if problems:
         raise RuntimeError("compare_kernel cross-lane check failed:\n" + "\n".join(problems))
+
+
+if __name__ == "__main__":
+    print(build(verbose="--verbose" in sys.argv))

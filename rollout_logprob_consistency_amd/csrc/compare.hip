@@ -414,18 +414,32 @@ namespace lp {
 // Quantiles follow numpy's default ("linear") rule, the estimator of the
 // AMD blog's compare(): each lies between two neighbouring order statistics
 // (quantile_ranks), which are selected exactly and interpolated in fp64
-// (quantile_lerp). Exact order statistics by radix selection on the bit
-// patterns of |delta| (non-negative fp64, so the bits order like the
-// values): 8 passes of one byte, each a histogram pass over the batch -- one
-// workgroup per sequence, LDS counters, integer atomics into global
-// histograms (3 pairs x (2 ranks per quantile and the k-th largest)) -- and
-// a one-workgroup select that keeps, per target, the byte where the wanted
-// rank falls. The two ranks of a quantile share one histogram while their
-// prefixes agree, which is every pass unless a bin boundary falls between
-// them. Every count is an integer, so the result does not depend on the
-// order in which workgroups run. The sums and the first worst token are formed per sequence in a fixed
-// order (pass 0) and reduced in a fixed tree; the position profile folds
-// fixed chunks of sequences in order.
+// (quantile_lerp). The order statistics are found by radix selection on the
+// keys (the bit patterns of |delta|, which order like the values). A
+// selection target is one rank of one pair: the two ranks of each quantile
+// and, with worst tokens, the k-th largest. Targets of a pair whose known
+// prefixes agree see the same tokens; the first of them (the "source") takes
+// the histogram or the gather, and the others read it.
+//  Pass 0  reads the batch once (one workgroup per sequence): the 4 465-bucket
+//          histogram of the keys' top 16 bits per pair, and the per-sequence
+//          sums and maxima. A one-workgroup select finds every target's
+//          bucket and its rank inside it.
+//  Pass 1  reads the batch again: each source histograms byte [47:40] of the
+//          keys in its bucket and copies those keys into a list region of
+//          the exact size (the bucket's count; the region is split by
+//          histogram copy, so each sequence's workgroup appends to the part
+//          that its copy counted). A source whose bucket holds at most 4 096
+//          keys gathers them instead.
+//  Pass 2 .. 6  select bytes [39:32] .. [7:0] from the lists (the batch, for
+//          a source whose list did not fit the key buffer). Once a source's
+//          prefix holds at most 4 096 keys it gathers them in the next pass
+//          and leaves the passes.
+//  Finish  one workgroup per gathering source selects its targets' remaining
+//          bytes from the gathered keys in LDS.
+// Every count is an integer, so the result does not depend on the order in
+// which workgroups run or append. The sums and the first worst token are
+// formed per sequence in a fixed order (pass 0) and reduced in a fixed tree;
+// the position profile folds fixed chunks of sequences in order.
 //
 // Worst k tokens: the k-th largest key tau of a pair is selected like the
 // quantiles; then every sequence counts its tokens above tau and equal to
@@ -446,17 +460,30 @@ constexpr int kWorstT = 6;  // index of the k-th-largest target within a pair
 constexpr int kMaxTargets = 3 * kMaxTP;
 constexpr int kTailThreads = 256;
 constexpr int kTailChunks = 64;     // sequence chunks of the position profile
-// Copies of the histograms: workgroup b adds into copy b mod kHistCopies, so
-// no counter takes device-scope atomics from more than N / kHistCopies
-// workgroups (identical rows put every workgroup's count in one bin); the
-// select kernel sums the copies.
-constexpr int kHistCopies = 16;
-constexpr int kHistStride = kMaxTargets * 256;  // words per histogram copy
-static_assert(kTailThreads == 256, "one histogram bin per thread");
+// Histogram copies: the workgroup of sequence n adds into copy n mod 8 (with
+// workgroups dealt to the 8 XCDs in turn, each copy is one XCD's), so no
+// counter takes atomics from more than N / 8 workgroups.
+constexpr int kCopies = 8;
+constexpr int kB16Pad = 4480;       // words per pass-0 pair histogram (>= kKeyBuckets)
+constexpr int kHistStride = kMaxTargets * 256;  // words per byte-histogram copy
+constexpr int kGather = 4096;       // keys a source gathers for the finish
+constexpr int kLastPass = 6;        // pass p >= 1 selects key bits [55 - 8p : 48 - 8p]
+// Atomic counters that many workgroups update sit 256 bytes apart, each in
+// a cache line of its own.
+constexpr int kCtrStride64 = 32;    // int64 counters
+constexpr int kCtrStride32 = 64;    // uint32 counters
+static_assert(kTailThreads == 256, "one byte-histogram bin per thread");
+static_assert(kB16Pad >= kKeyBuckets && kB16Pad % 64 == 0, "pass-0 histogram rows");
+
+__device__ __forceinline__ int pass_shift(int pass) { return 48 - 8 * pass; }
 
 struct TailSel {
-  uint64_t prefix;   // bytes of the selected key found so far
-  int64_t rank;      // 1-based rank still wanted below that prefix; 0: none
+  uint64_t prefix;   // known top bits of the selected key (the key itself when done)
+  int64_t rank;      // 1-based rank still wanted under that prefix; 0: done or none
+  int32_t lreg;      // list region that holds its candidates (-1: none, read the batch)
+  int32_t fin_src;   // source whose gathered keys finish it (-1: none)
+  int32_t fin_bits;  // key bits below the prefix when it was gathered
+  int32_t pad;
 };
 
 struct TailPart {    // one (sequence, pair), from pass 0
@@ -481,28 +508,20 @@ __device__ __forceinline__ TailPart tail_part_combine(TailPart x, const TailPart
   return x;
 }
 
-// After two passes each target's remaining candidates (the keys under its
-// 16-bit prefix) are few for continuous data; pass 2 copies them into a list
-// and passes 3 .. 7 read only the lists. Targets of one pair under one prefix
-// share a list. A target whose list does not fit the key buffer keeps
-// reading the full batch.
-struct TailList {
-  int64_t off, len;  // region of keys[]
-  int32_t src;       // the target whose region it is; -1: no list
+struct TailList {    // region of keys[] that a pass-0 source fills in pass 1
+  int64_t off, len;
 };
 
-// What the next pass does, written by the select kernel (the init kernel for
-// pass 0) and read by the pass with a handful of independent loads, so that a
-// pass with nothing to do exits after one. Targets of one pair under one
-// prefix see the same tokens: only the first of them (its "source") takes a
-// histogram, and the others read it.
+// What the next pass does, written by the select before it and read by the
+// pass with a handful of independent loads, so that a pass with nothing to
+// do exits after one.
 struct TailPlan {
-  uint64_t pre[kMaxTargets];  // each target's selected prefix
-  int32_t lsrc[kMaxTargets];  // the list region a list target reads (-1: none)
+  uint64_t pre[kMaxTargets];  // each target's known prefix
+  int32_t lsrc[kMaxTargets];  // the list region its source reads (-1: the batch)
   int8_t src[kMaxTargets];    // the target whose histogram target t reads
-  uint32_t full;              // sources that histogram in a full pass over the batch
-  uint32_t list;              // sources that histogram on a list (passes 3 .. 7)
-  uint32_t own;               // pass 2: sources that own a list region
+  uint32_t hist;              // sources that histogram this pass's byte
+  uint32_t gath;              // sources that gather their keys in this pass
+  uint32_t own;               // pass 1: sources that fill their list region
 };
 
 struct WorstCand {   // a worst-token candidate
@@ -511,14 +530,16 @@ struct WorstCand {   // a worst-token candidate
 };
 
 struct TailWs {
-  uint32_t* hist;    // [kHistCopies][kMaxTargets][256]
+  uint32_t* hist0;   // [kCopies][3][kB16Pad]
+  uint32_t* hist;    // [kCopies][kMaxTargets][256], right after hist0
   TailSel* sel;      // [kMaxTargets]
-  TailList* list;    // [kMaxTargets]
+  TailList* list;    // [kMaxTargets], by owning source
   TailPlan* plan;
-  uint64_t* keys;    // [cap]
+  int64_t* fill;     // [kMaxTargets][kCopies][kCtrStride64] pass-1 write cursors
+  uint32_t* gcnt;    // [kMaxTargets][kCtrStride32] gathered keys per source
+  uint64_t* gbuf;    // [kMaxTargets][kGather]
+  uint64_t* keys;    // [3][cap], one key buffer per pair
   int64_t cap;
-  uint32_t* cnt;     // [kMaxTargets][N] candidates of sequence n in list t (pass 2)
-  uint32_t* koff;    // [kMaxTargets][N] their offset within the list
   int64_t* count;    // [3]
   TailPart* part;    // [N][3]
   double* pos_part;  // [nch][3][L]
@@ -532,86 +553,83 @@ struct TailWs {
 
 __host__ __device__ inline size_t tail_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Key buffer: one eighth of the positions (continuous scores leave a few
-// percent of a pair's tokens under each target's 16-bit prefix).
-inline int64_t tail_key_cap(int64_t N, int64_t L) {
-  const int64_t c = N * L / 8;
-  return c < 4096 ? 4096 : (c > 0x7FFFFFFF ? 0x7FFFFFFF : c);
+// Key buffer of a pair: a quarter of the positions. The sources of a pair
+// sit in different buckets, so their lists are disjoint; a list that does
+// not fit leaves its source reading the batch.
+inline int64_t tail_key_cap(int64_t N, int64_t L) { return (N * L + 3) / 4; }
+
+constexpr size_t kHist0Words = (size_t)kCopies * 3 * kB16Pad;
+constexpr size_t kHistWords = (size_t)kCopies * kHistStride;
+static_assert((kHist0Words * 4) % 256 == 0, "hist follows hist0 contiguously");
+
+// One pass over the layout: with base == nullptr it only sizes it.
+size_t tail_walk(char* p, int64_t N, int64_t L, int32_t k, TailWs* w) {
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    char* q = p ? p + o : nullptr;
+    o = tail_up(o + bytes);
+    return q;
+  };
+  TailWs x;
+  x.hist0 = reinterpret_cast<uint32_t*>(take(kHist0Words * sizeof(uint32_t)));
+  x.hist = reinterpret_cast<uint32_t*>(take(kHistWords * sizeof(uint32_t)));
+  x.sel = reinterpret_cast<TailSel*>(take(kMaxTargets * sizeof(TailSel)));
+  x.list = reinterpret_cast<TailList*>(take(kMaxTargets * sizeof(TailList)));
+  x.plan = reinterpret_cast<TailPlan*>(take(sizeof(TailPlan)));
+  x.fill = reinterpret_cast<int64_t*>(take((size_t)kMaxTargets * kCopies * kCtrStride64 * sizeof(int64_t)));
+  x.gcnt = reinterpret_cast<uint32_t*>(take((size_t)kMaxTargets * kCtrStride32 * sizeof(uint32_t)));
+  x.gbuf = reinterpret_cast<uint64_t*>(take((size_t)kMaxTargets * kGather * sizeof(uint64_t)));
+  x.cap = tail_key_cap(N, L);
+  x.keys = reinterpret_cast<uint64_t*>(take((size_t)3 * x.cap * sizeof(uint64_t)));
+  x.count = reinterpret_cast<int64_t*>(take(3 * sizeof(int64_t)));
+  x.part = reinterpret_cast<TailPart*>(take((size_t)N * 3 * sizeof(TailPart)));
+  x.nch = (int)(N < kTailChunks ? (N < 1 ? 1 : N) : kTailChunks);
+  x.pos_part = reinterpret_cast<double*>(take((size_t)x.nch * 3 * L * sizeof(double)));
+  x.pos_cpart = reinterpret_cast<int32_t*>(take((size_t)x.nch * 3 * L * sizeof(int32_t)));
+  x.k = k;
+  x.wcnt = reinterpret_cast<uint32_t*>(take((size_t)(k > 0 ? 6 * N : 0) * sizeof(uint32_t)));
+  x.woff = reinterpret_cast<int64_t*>(take((size_t)(k > 0 ? 6 * N : 0) * sizeof(int64_t)));
+  x.cand = reinterpret_cast<WorstCand*>(take((size_t)(k > 0 ? 3 * k : 0) * sizeof(WorstCand)));
+  if (w) *w = x;
+  return o;
 }
 
 TailWs tail_layout(void* base, int64_t N, int64_t L, int32_t k) {
-  char* p = static_cast<char*>(base);
   TailWs w;
-  size_t o = 0;
-  w.hist = reinterpret_cast<uint32_t*>(p + o); o = tail_up(o + kHistCopies * kHistStride * sizeof(uint32_t));
-  w.sel = reinterpret_cast<TailSel*>(p + o);   o = tail_up(o + kMaxTargets * sizeof(TailSel));
-  w.list = reinterpret_cast<TailList*>(p + o); o = tail_up(o + kMaxTargets * sizeof(TailList));
-  w.plan = reinterpret_cast<TailPlan*>(p + o); o = tail_up(o + sizeof(TailPlan));
-  w.cap = tail_key_cap(N, L);
-  w.keys = reinterpret_cast<uint64_t*>(p + o); o = tail_up(o + (size_t)w.cap * sizeof(uint64_t));
-  w.cnt = reinterpret_cast<uint32_t*>(p + o);  o = tail_up(o + (size_t)N * kMaxTargets * sizeof(uint32_t));
-  w.koff = reinterpret_cast<uint32_t*>(p + o); o = tail_up(o + (size_t)N * kMaxTargets * sizeof(uint32_t));
-  w.count = reinterpret_cast<int64_t*>(p + o); o = tail_up(o + 3 * sizeof(int64_t));
-  w.part = reinterpret_cast<TailPart*>(p + o); o = tail_up(o + (size_t)N * 3 * sizeof(TailPart));
-  w.nch = (int)(N < kTailChunks ? (N < 1 ? 1 : N) : kTailChunks);
-  w.pos_part = reinterpret_cast<double*>(p + o); o = tail_up(o + (size_t)w.nch * 3 * L * sizeof(double));
-  w.pos_cpart = reinterpret_cast<int32_t*>(p + o); o = tail_up(o + (size_t)w.nch * 3 * L * sizeof(int32_t));
-  w.k = k;
-  w.wcnt = reinterpret_cast<uint32_t*>(p + o); o = tail_up(o + (size_t)(k > 0 ? 6 * N : 0) * sizeof(uint32_t));
-  w.woff = reinterpret_cast<int64_t*>(p + o); o = tail_up(o + (size_t)(k > 0 ? 6 * N : 0) * sizeof(int64_t));
-  w.cand = reinterpret_cast<WorstCand*>(p + o);
+  tail_walk(static_cast<char*>(base), N, L, k, &w);
   return w;
 }
 
-size_t tail_bytes(int64_t N, int64_t L, int32_t k) {
-  size_t o = 0;
-  o = tail_up(o + kHistCopies * kHistStride * sizeof(uint32_t));
-  o = tail_up(o + kMaxTargets * sizeof(TailSel));
-  o = tail_up(o + kMaxTargets * sizeof(TailList));
-  o = tail_up(o + sizeof(TailPlan));
-  o = tail_up(o + (size_t)tail_key_cap(N, L) * sizeof(uint64_t));
-  o = tail_up(o + (size_t)N * kMaxTargets * sizeof(uint32_t));
-  o = tail_up(o + (size_t)N * kMaxTargets * sizeof(uint32_t));
-  o = tail_up(o + 3 * sizeof(int64_t));
-  o = tail_up(o + (size_t)N * 3 * sizeof(TailPart));
-  const int nch = (int)(N < kTailChunks ? (N < 1 ? 1 : N) : kTailChunks);
-  o = tail_up(o + (size_t)nch * 3 * L * sizeof(double));
-  o = tail_up(o + (size_t)nch * 3 * L * sizeof(int32_t));
-  if (k > 0) {
-    o = tail_up(o + (size_t)6 * N * sizeof(uint32_t));
-    o = tail_up(o + (size_t)6 * N * sizeof(int64_t));
-    o = tail_up(o + (size_t)3 * k * sizeof(WorstCand));
-  }
-  return o;
-}
+size_t tail_bytes(int64_t N, int64_t L, int32_t k) { return tail_walk(nullptr, N, L, k, nullptr); }
 
 // Left and right side of pair p among the three scores (A, B, C).
 __device__ __forceinline__ int pair_left(int p) { return p == 1 ? 1 : 0; }
 __device__ __forceinline__ int pair_right(int p) { return p == 0 ? 1 : 2; }
 
-// Workgroup c clears histogram copy c; workgroup 0 also resets the
-// selection state and writes the plan of pass 0: every target of a pair
-// reads the pair's one histogram (prefix 0), kept by its first target.
-__global__ __launch_bounds__(kTailThreads) void tails_init_kernel(TailWs w, int tp) {
-  uint4* h = reinterpret_cast<uint4*>(w.hist + blockIdx.x * kHistStride);
-  for (int i = threadIdx.x; i < kHistStride / 4; i += kTailThreads) h[i] = make_uint4(0u, 0u, 0u, 0u);
+// Clears the histograms (every copy) and the gather counts, and resets the
+// selection state.
+constexpr int kInitBlocks = 64;
+
+__global__ __launch_bounds__(kTailThreads) void tails_init_kernel(TailWs w) {
+  uint4* z = reinterpret_cast<uint4*>(w.hist0);
+  constexpr int64_t kVecs = (int64_t)(kHist0Words + kHistWords) / 4;
+  for (int64_t i = (int64_t)blockIdx.x * kTailThreads + threadIdx.x; i < kVecs;
+       i += (int64_t)gridDim.x * kTailThreads)
+    z[i] = make_uint4(0u, 0u, 0u, 0u);
   if (blockIdx.x != 0) return;
   const int t = threadIdx.x;
   if (t < kMaxTargets) {
-    w.sel[t] = TailSel{0ull, 0};
-    w.list[t] = TailList{0, 0, -1};
-    w.plan->pre[t] = 0ull;
-    w.plan->lsrc[t] = -1;
-    w.plan->src[t] = (int8_t)(tp * (t / tp));
+    w.gcnt[t * kCtrStride32] = 0u;
+    w.sel[t] = TailSel{0ull, 0, -1, -1, 0, 0};
+    w.list[t] = TailList{0, 0};
   }
   if (t == 0) {
-    w.plan->full = 1u | (1u << tp) | (1u << (2 * tp));
-    w.plan->list = 0u;
+    w.plan->hist = 0u;
+    w.plan->gath = 0u;
     w.plan->own = 0u;
   }
 }
 
-// One histogram pass; pass 0 also forms the per-sequence sums and maxima.
 // Scores and mask of the four positions i .. i + 3 of row n (inactive past
 // L); 16-byte loads on the vector path, element loads otherwise.
 template <bool kVec>
@@ -640,37 +658,42 @@ __device__ __forceinline__ void tail_load4(const TailArgs& a, const float* const
   }
 }
 
-// Full pass over the batch. kMode 0: pass 0 (also the per-sequence
-// partials); 1: a later pass, for the targets without a list; 2: pass 2,
-// which also counts each sequence's candidates per list; 3: no histogram,
-// writes each sequence's candidates at the offsets the counts give (a
-// separate pass so that no append needs an atomic on a shared counter).
-template <bool kVec, int kMode, int kTP>
-__global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, TailWs w, int pass) {
-  constexpr int kNT = 3 * kTP, kHW = kNT * 256;
-  __shared__ uint32_t h[kHW];
-  __shared__ TailPart red[kMode == 0 ? 3 : 1][kMode == 0 ? kTailThreads / 64 : 1];
-  __shared__ uint32_t n_found[kNT];
-  const int tid = threadIdx.x;
-  const int shift = 56 - 8 * pass;  // this pass's byte: key bits [shift + 7 : shift]
-  // The plan: which sources histogram (want) and, in pass 2, which own a
-  // list region (src_list). A pass with nothing to do exits after one load.
-  const uint32_t full = kMode <= 2 ? w.plan->full : 0u;
-  const uint32_t own = kMode >= 2 ? w.plan->own : 0u;
-  if ((full | own) == 0u) return;  // uniform
-  uint64_t pre[kNT];
-  bool want[kNT];
-  bool src_list[kNT];
-#pragma unroll
-  for (int t = 0; t < kNT; ++t) {
-    pre[t] = w.plan->pre[t];
-    want[t] = ((full | own) >> t) & 1u;
-    src_list[t] = (own >> t) & 1u;
+// Counted flag and key of pair p at one position.
+__device__ __forceinline__ bool tail_key(const float v[3], bool act, int p, uint64_t* key) {
+  const float l = v[pair_left(p)], r = v[pair_right(p)];
+  *key = (uint64_t)__double_as_longlong(fabs((double)l - (double)r));
+  return act && __builtin_isfinite(l) && __builtin_isfinite(r);
+}
+
+// Pass-0 histogram increment of bucket b: 32-bit counters, or (kWide false,
+// rows of at most 65 535 positions) two 16-bit counters per word, so that
+// the three pairs' histograms take 26.8 KB of LDS instead of 53.6 KB.
+template <bool kWide>
+__device__ __forceinline__ void hist16_add(uint32_t* h, uint32_t b, bool hit, int lane) {
+  const uint64_t hb = __ballot(hit);
+  if (hb == 0) return;
+  const uint32_t b0 = __builtin_amdgcn_readfirstlane(b);
+  uint32_t bin = b, inc = 1u;
+  if (__ballot(hit && b != b0) == 0) {
+    if (lane != __ffsll((long long)hb) - 1) return;
+    bin = b0;
+    inc = (uint32_t)__popcll(hb);
+  } else if (!hit) {
+    return;
   }
-#pragma unroll
-  for (int t = 0; t < kNT; ++t)
-    if ((full >> t) & 1u) h[t * 256 + tid] = 0u;  // kTailThreads == 256 bins
-  if (kMode >= 2 && tid < kNT) n_found[tid] = 0u;
+  if (kWide) atomicAdd(&h[bin], inc);
+  else atomicAdd(&h[bin >> 1], inc << ((bin & 1u) << 4));
+}
+
+// Pass 0: the bucket histogram of every pair, and each sequence's sums and
+// maximum, over one row per workgroup.
+template <bool kVec, bool kWide>
+__global__ __launch_bounds__(kTailThreads) void tails_p0_kernel(TailArgs a, TailWs w) {
+  constexpr int kWords = kWide ? kKeyBuckets : (kKeyBuckets + 1) / 2;
+  __shared__ uint32_t h[3 * kWords];
+  __shared__ TailPart red[3][kTailThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int i = tid; i < 3 * kWords; i += kTailThreads) h[i] = 0u;
   __syncthreads();
 
   const int64_t n = blockIdx.x;
@@ -679,10 +702,9 @@ __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, Ta
   TailPart mine[3];
 #pragma unroll
   for (int p = 0; p < 3; ++p) mine[p] = TailPart{0.0, 0.0, 0ull, -1, 0};
-  const int lane = tid & 63;
   // Groups of four consecutive positions 4 tid + 1024 k; the trip count is
   // the same for every thread, so every lane of a wave takes part in the
-  // ballots below (positions past L are inactive). Positions ascend within a
+  // ballots (positions past L are inactive). Positions ascend within a
   // thread.
   constexpr int64_t kStep = 4 * kTailThreads;
   const int64_t Lw = (a.L + kStep - 1) / kStep * kStep;
@@ -692,95 +714,45 @@ __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, Ta
     tail_load4<kVec>(a, rows, M, i0, vv, actv);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int64_t i = i0 + k;
-      const bool act = actv[k];
       const float* v = vv[k];
       double e[3] = {0.0, 0.0, 0.0};
-      if (kMode == 0 && act) {
+      if (actv[k]) {
 #pragma unroll
         for (int s = 0; s < 3; ++s)
           if (__builtin_isfinite(v[s])) e[s] = exp_f64((double)v[s]);
       }
 #pragma unroll
       for (int p = 0; p < 3; ++p) {
-        const float l = v[pair_left(p)], r = v[pair_right(p)];
-        const bool ok = act && __builtin_isfinite(l) && __builtin_isfinite(r);
-        const double d = fabs((double)l - (double)r);
-        const uint64_t key = (uint64_t)__double_as_longlong(d);
-        const uint32_t digit = (uint32_t)(key >> shift) & 255u;
-        // After the first passes few tokens share any target's prefix: one
-        // ballot per pair lets a wave with no such token skip the targets.
-        bool any = ok && kMode == 0;
-        if (kMode != 0) {
-#pragma unroll
-          for (int j = 0; j < kTP; ++j)
-            any = any || (ok && want[kTP * p + j] &&
-                          (key >> (shift + 8)) == pre[kTP * p + j]);
-        }
-#pragma unroll
-        for (int j = 0; j < kTP; ++j) {
-          const int t = kTP * p + j;
-          if (!want[t] || __ballot(any) == 0) continue;  // uniform
-          const bool hit = ok && (kMode == 0 || (key >> (shift + 8)) == pre[t]);
-          const uint64_t hb = __ballot(hit);
-          if (hb == 0) continue;
-          // One atomic for the wave when all its hits share the bin of its
-          // first lane (the common case: runs of identical scores put every
-          // lane in bin 0); readfirstlane needs no LDS round trip.
-          const int first = __ffsll((long long)hb) - 1;
-          if (kMode <= 2) {
-            const uint32_t d0 = __builtin_amdgcn_readfirstlane(digit);
-            if (__ballot(hit && digit != d0) == 0) {
-              if (lane == first) atomicAdd(&h[t * 256 + d0], (uint32_t)__popcll(hb));
-            } else if (hit) {
-              atomicAdd(&h[t * 256 + digit], 1u);
-            }
-          }
-          if (kMode >= 2 && src_list[t]) {
-            // Consecutive slots for the wave's hits.
-            uint32_t slot = 0u;
-            if (lane == first) slot = atomicAdd(&n_found[t], (uint32_t)__popcll(hb));
-            if (kMode == 3) {
-              slot = (uint32_t)__shfl((int)slot, first);
-              const uint32_t r = (uint32_t)__popcll(hb & ((1ull << lane) - 1ull));
-              const TailList L = w.list[t];
-              const int64_t e = (int64_t)w.koff[t * a.N + n] + slot + r;
-              if (hit && e < L.len) w.keys[L.off + e] = key;
-            }
-          }
-        }
+        uint64_t key;
+        const bool ok = tail_key(v, actv[k], p, &key);
+        hist16_add<kWide>(h + p * kWords, key_bucket(key), ok, lane);
         if (!ok) continue;
-        if (kMode == 0) {
-          TailPart& m = mine[p];
-          m.sum_abs += d;
-          m.sum_prob += fabs(e[pair_left(p)] - e[pair_right(p)]);
-          if (m.max_pos < 0 || key > m.max_key) {  // positions ascend: the first one stays
-            m.max_key = key;
-            m.max_pos = (int32_t)i;
-          }
-          m.count += 1;
+        TailPart& m = mine[p];
+        m.sum_abs += __longlong_as_double((long long)key);
+        m.sum_prob += fabs(e[pair_left(p)] - e[pair_right(p)]);
+        if (m.max_pos < 0 || key > m.max_key) {  // positions ascend: the first one stays
+          m.max_key = key;
+          m.max_pos = (int32_t)(i0 + k);
         }
+        m.count += 1;
       }
     }
   }
   __syncthreads();
-  if (kMode == 3) return;
-  uint32_t* hc = w.hist + (blockIdx.x % kHistCopies) * kHistStride;
-#pragma unroll
-  for (int t = 0; t < kNT; ++t) {
-    if (!((full >> t) & 1u)) continue;  // uniform
-    const uint32_t v = h[t * 256 + tid];
-    if (v) atomicAdd(&hc[t * 256 + tid], v);
+  uint32_t* g = w.hist0 + (size_t)(n % kCopies) * 3 * kB16Pad;
+  for (int i = tid; i < 3 * kWords; i += kTailThreads) {
+    const uint32_t v = h[i];
+    if (v == 0u) continue;
+    const int p = i / kWords, wd = i - p * kWords;
+    if (kWide) {
+      atomicAdd(&g[p * kB16Pad + wd], v);
+    } else {
+      if (v & 0xFFFFu) atomicAdd(&g[p * kB16Pad + 2 * wd], v & 0xFFFFu);
+      if (v >> 16) atomicAdd(&g[p * kB16Pad + 2 * wd + 1], v >> 16);
+    }
   }
-  if (kMode == 2) {
-    if (tid < kNT) w.cnt[tid * a.N + n] = src_list[tid] ? n_found[tid] : 0u;
-    return;
-  }
-  if (kMode != 0) return;
 
-  // Fixed XOR butterfly within each wave, then the waves in order. Only the
-  // histogram and four partials per pair stay in LDS, so that more sequences'
-  // workgroups fit on a CU.
+  // Fixed XOR butterfly within each wave, then the waves in order.
 #pragma unroll
   for (int p = 0; p < 3; ++p) {
     TailPart x = mine[p];
@@ -806,140 +778,327 @@ __global__ __launch_bounds__(kTailThreads) void tails_hist_kernel(TailArgs a, Ta
   }
 }
 
-// Offsets of each sequence's candidates within each list: an exclusive scan
-// of the pass-2 counts over the sequences, one workgroup per list. Thread j
-// takes the contiguous sequences [j per, (j + 1) per).
-constexpr int kScanThreads = 1024;
-
-__global__ __launch_bounds__(kScanThreads) void tails_scan_kernel(TailWs w, int64_t N) {
-  __shared__ uint32_t wsum[kScanThreads / 64];
-  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint32_t* cnt = w.cnt + t * N;
-  uint32_t* koff = w.koff + t * N;
-  const int64_t per = (N + kScanThreads - 1) / kScanThreads;
-  const int64_t lo = min(N, tid * per), hi = min(N, lo + per);
-  uint32_t tot = 0u;
-  for (int64_t n = lo; n < hi; ++n) tot += cnt[n];
-  uint32_t incl = tot;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = (uint32_t)__shfl_up((int)incl, off);
-    if (lane >= off) incl += o;
+// The rank target j of a pair wants among its `total` counted tokens (0:
+// none): the two neighbours of each quantile, or the k-th largest (the
+// smallest when fewer are counted).
+__device__ __forceinline__ int64_t tail_target_rank(int j, int64_t total, int32_t k) {
+  if (total <= 0) return 0;
+  if (j < kWorstT) {
+    int64_t lo, hi;
+    quantile_ranks(total, quantile_prob(j >> 1), &lo, &hi);
+    return (j & 1) ? hi : lo;
   }
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0u;
-  for (int v = 0; v < wave; ++v) before += wsum[v];
-  uint32_t run = before + incl - tot;
-  for (int64_t n = lo; n < hi; ++n) {
-    const uint32_t c = cnt[n];
-    koff[n] = run;
-    run += c;
-  }
+  return k > 0 ? (total > k ? total - k + 1 : 1) : 0;
 }
 
-// Passes 3 .. 7 for the targets with a list: the histogram of this pass's
-// byte over the list's keys under the target's prefix. A grid-stride walk
-// in whole waves (the ballots need every lane); integer counts, so the order
-// of the keys does not matter.
-constexpr int kListBlocks = 512;
+constexpr int kSelThreads = 1024;
+constexpr int kS0Per = (kKeyBuckets + kSelThreads - 1) / kSelThreads;  // 5 buckets a thread
 
+// Select after pass 0, one workgroup per pair: thread j sums the copies of
+// buckets [5 j, 5 j + 5); a scan over the threads gives each target's bucket
+// and its rank inside it. Thread 0 then plans pass 1 for the pair's targets:
+// sources, list regions (each split by copy, at the offsets the copies'
+// counts give) and gathers.
 template <int kTP>
-__global__ __launch_bounds__(kTailThreads) void tails_list_kernel(TailWs w, int pass) {
-  constexpr int kNT = 3 * kTP, kHW = kNT * 256;
-  __shared__ uint32_t h[kHW];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int shift = 56 - 8 * pass;
-  const uint32_t lm = w.plan->list;
-  if (lm == 0u) return;  // uniform: no target reads a list in this pass
-  uint64_t pre[kNT];
-  bool want[kNT];
-  int lst[kNT];
+__global__ __launch_bounds__(kSelThreads) void tails_p0_select_kernel(TailWs w) {
+  constexpr int kWaves = kSelThreads / 64;
+  __shared__ int64_t s_wsum[kWaves], s_total;
+  __shared__ int32_t s_bin[kTP];
+  __shared__ int64_t s_rank[kTP], s_len[kTP], s_trank[kTP];
+  __shared__ uint32_t s_sub[kTP][kCopies];
+  __shared__ int32_t s_lreg[kTP];
+  const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < kTP) s_bin[tid] = -1;
+  uint32_t c[kS0Per];
+  int64_t mine = 0;
 #pragma unroll
-  for (int t = 0; t < kNT; ++t) {
-    pre[t] = w.plan->pre[t];
-    lst[t] = w.plan->lsrc[t];
-    want[t] = (lm >> t) & 1u;
+  for (int j = 0; j < kS0Per; ++j) {
+    const int b = tid * kS0Per + j;
+    uint32_t s = 0u;
+    if (b < kKeyBuckets) {
+#pragma unroll
+      for (int cp = 0; cp < kCopies; ++cp) s += w.hist0[(size_t)(cp * 3 + p) * kB16Pad + b];
+    }
+    c[j] = s;
+    mine += s;
   }
+  int64_t incl = mine;
 #pragma unroll
-  for (int t = 0; t < kNT; ++t)
-    if (want[t]) h[t * 256 + tid] = 0u;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
   __syncthreads();
-  const int64_t stride = (int64_t)gridDim.x * kTailThreads;
-  for (int u = 0; u < kNT; ++u) {
-    bool used = false;
+  if (tid == 0) {  // exclusive prefix of the wave sums, and the pair's total
+    int64_t run = 0;
+    for (int v = 0; v < kWaves; ++v) {
+      const int64_t x = s_wsum[v];
+      s_wsum[v] = run;
+      run += x;
+    }
+    s_total = run;
+    w.count[p] = run;
+  }
+  __syncthreads();
+  incl += s_wsum[wave];
+  if (tid < kTP) s_trank[tid] = tail_target_rank(tid, s_total, w.k);
+  __syncthreads();
+  const int64_t excl = incl - mine;
+  for (int j = 0; j < kTP; ++j) {
+    const int64_t rank = s_trank[j];
+    if (rank > 0 && excl < rank && rank <= incl) {
+      int64_t below = excl;
+      int found = -1;
+      uint32_t len = 0u;
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) used = used || (want[t] && lst[t] == u);
-    if (!used) continue;  // uniform
-    const TailList L = w.list[u];
-    const int64_t wave0 = (int64_t)blockIdx.x * kTailThreads + (tid - lane);
-    for (int64_t e0 = wave0; e0 < L.len; e0 += stride) {
-      const int64_t e = e0 + lane;
-      const bool in = e < L.len;
-      const uint64_t key = in ? w.keys[L.off + e] : 0ull;
-      const uint32_t digit = (uint32_t)(key >> shift) & 255u;
-#pragma unroll
-      for (int t = 0; t < kNT; ++t) {
-        if (!want[t] || lst[t] != u) continue;  // uniform
-        const bool hit = in && (key >> (shift + 8)) == pre[t];
-        const uint64_t hb = __ballot(hit);
-        if (hb == 0) continue;
-        const int first = __ffsll((long long)hb) - 1;
-        const uint32_t d0 = __builtin_amdgcn_readfirstlane(digit);
-        if (__ballot(hit && digit != d0) == 0) {
-          if (lane == first) atomicAdd(&h[t * 256 + d0], (uint32_t)__popcll(hb));
-        } else if (hit) {
-          atomicAdd(&h[t * 256 + digit], 1u);
+      for (int q = 0; q < kS0Per; ++q) {
+        if (found >= 0) continue;
+        if (below + c[q] >= rank) {
+          found = q;
+          len = c[q];
+        } else {
+          below += c[q];
         }
       }
+      const int b = tid * kS0Per + found;
+      s_bin[j] = b;
+      s_rank[j] = rank - below;
+      s_len[j] = len;
+#pragma unroll
+      for (int cp = 0; cp < kCopies; ++cp) s_sub[j][cp] = w.hist0[(size_t)(cp * 3 + p) * kB16Pad + b];
     }
   }
   __syncthreads();
-  uint32_t* hc = w.hist + (blockIdx.x % kHistCopies) * kHistStride;
+  if (tid != 0) return;
+  // Bucket 0 holds only the key 0: a target there is selected. A source's
+  // list region is cut from its pair's key buffer while it lasts.
+  uint32_t hist = 0u, gath = 0u, own = 0u;
+  int64_t used = 0;
+  for (int j = 0; j < kTP; ++j) {
+    const int u = kTP * p + j;
+    const int b = s_bin[j];
+    TailSel s{0ull, 0, -1, -1, 0, 0};
+    int src = j;
+    if (b > 0) {
+      s.prefix = bucket_top16((uint32_t)b);
+      s.rank = s_rank[j];
+      for (int v = 0; v < j; ++v)
+        if (s_bin[v] == b) {
+          src = v;
+          break;
+        }
+      if (src == j) {
+        const int64_t len = s_len[j];
+        if (len <= kGather) {
+          gath |= 1u << u;
+        } else {
+          hist |= 1u << u;
+          if (used + len <= w.cap) {
+            own |= 1u << u;
+            const int64_t off = p * w.cap + used;
+            w.list[u] = TailList{off, len};
+            int64_t o = off;
+            for (int cp = 0; cp < kCopies; ++cp) {
+              w.fill[(u * kCopies + cp) * kCtrStride64] = o;
+              o += s_sub[j][cp];
+            }
+            used += len;
+            s.lreg = u;
+          }
+        }
+      } else {
+        s.lreg = s_lreg[src];
+      }
+    }
+    s_lreg[j] = s.lreg;
+    w.sel[u] = s;
+    w.plan->pre[u] = s.prefix;
+    w.plan->src[u] = (int8_t)(kTP * p + src);
+    w.plan->lsrc[u] = -1;  // pass 1 reads the batch
+  }
+  // The init kernel cleared the masks; each pair adds its sources.
+  if (hist) atomicOr(&w.plan->hist, hist);
+  if (gath) atomicOr(&w.plan->gath, gath);
+  if (own) atomicOr(&w.plan->own, own);
+}
+
+// Appends the hitting lanes' keys to source t's gather buffer (one atomic
+// for the wave). The select only plans a gather for at most kGather keys.
+__device__ __forceinline__ void gather_add(const TailWs& w, int t, uint64_t key, bool hit, int lane) {
+  const uint64_t hb = __ballot(hit);
+  if (hb == 0) return;
+  const int first = __ffsll((long long)hb) - 1;
+  uint32_t base = 0u;
+  if (lane == first) base = atomicAdd(&w.gcnt[t * kCtrStride32], (uint32_t)__popcll(hb));
+  base = (uint32_t)__builtin_amdgcn_readlane((int)base, first);
+  const uint32_t e = base + lanes_below(hb);
+  if (hit && e < (uint32_t)kGather) w.gbuf[(size_t)t * kGather + e] = key;
+}
+
+// Pass 1 over one row per workgroup: each histogram source counts byte
+// [47:40] of the keys in its bucket, each source with a list region copies
+// them into it, each gathering source gathers them. Copies go in chunks of
+// 1 024 positions: every wave numbers its hits per source from its ballots
+// (no atomics), the waves' counts are laid end to end, one atomic per source
+// reserves the chunk's span of the region part that this workgroup's copy
+// counted, and the keys, still in registers, are written.
+template <bool kVec, int kTP>
+__global__ __launch_bounds__(kTailThreads) void tails_p1_kernel(TailArgs a, TailWs w) {
+  constexpr int kNT = 3 * kTP;
+  constexpr int kW = kTailThreads / 64;
+  __shared__ uint32_t h[kNT * 256];
+  __shared__ uint32_t s_wcnt[kW][kNT];
+  __shared__ int64_t s_wbase[kW][kNT], s_lim[kNT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t hist = w.plan->hist, gath = w.plan->gath, own = w.plan->own;
+  const uint32_t act = hist | gath;
+  if (act == 0u) return;  // uniform
+  uint64_t pre[kNT];
+#pragma unroll
+  for (int t = 0; t < kNT; ++t) pre[t] = w.plan->pre[t];
+#pragma unroll
+  for (int t = 0; t < kNT; ++t)
+    if ((hist >> t) & 1u) h[t * 256 + tid] = 0u;
+  if (tid < kNT) {
+    const TailList R = w.list[tid];
+    s_lim[tid] = R.off + R.len;
+  }
+  __syncthreads();
+
+  const int64_t n = blockIdx.x;
+  const int cp = (int)(n % kCopies);
+  const float* const rows[3] = {a.A + n * a.ld, a.B + n * a.ld, a.C + n * a.ld};
+  const uint8_t* M = a.mask + n * a.ld;
+  constexpr int64_t kStep = 4 * kTailThreads;
+  const int64_t Lw = (a.L + kStep - 1) / kStep * kStep;
+  for (int64_t i0 = 4 * (int64_t)tid; i0 < Lw; i0 += kStep) {
+    float vv[4][3];
+    bool actv[4];
+    tail_load4<kVec>(a, rows, M, i0, vv, actv);
+    uint64_t key[4][3];
+    uint32_t okm[3] = {0u, 0u, 0u};
+    uint32_t slot[4][3];  // index among the wave's hits of the source
+    int tsel[4][3];       // the source that copies the key (-1: none)
+    uint32_t wrun[kNT];   // the wave's hits per source so far (uniform)
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) wrun[t] = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        okm[p] |= tail_key(vv[k], actv[k], p, &key[k][p]) ? 1u << k : 0u;
+        tsel[k][p] = -1;
+        slot[k][p] = 0u;
+      }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+#pragma unroll
+      for (int j = 0; j < kTP; ++j) {
+        const int t = kTP * p + j;
+        if (!((act >> t) & 1u)) continue;  // uniform
+        uint32_t hm = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          hm |= (((okm[p] >> k) & 1u) && (key[k][p] >> 48) == pre[t]) ? 1u << k : 0u;
+        if (__ballot(hm != 0u) == 0) continue;  // uniform: no key of the wave in the bucket
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const bool hit = (hm >> k) & 1u;
+          if ((hist >> t) & 1u)
+            wave_hist_add(h + t * 256, (uint32_t)(key[k][p] >> 40) & 255u, hit, lane);
+          if ((gath >> t) & 1u) gather_add(w, t, key[k][p], hit, lane);
+          if ((own >> t) & 1u) {
+            const uint64_t hb = __ballot(hit);
+            if (hit) {
+              slot[k][p] = wrun[t] + lanes_below(hb);
+              tsel[k][p] = t;
+            }
+            wrun[t] += (uint32_t)__popcll(hb);
+          }
+        }
+      }
+    }
+    if (own != 0u) {  // uniform
+      if (lane == 0) {
+#pragma unroll
+        for (int t = 0; t < kNT; ++t)
+          if ((own >> t) & 1u) s_wcnt[wave][t] = wrun[t];
+      }
+      __syncthreads();
+      if (tid < kNT && ((own >> tid) & 1u)) {
+        uint32_t tot = 0u;
+#pragma unroll
+        for (int v = 0; v < kW; ++v) tot += s_wcnt[v][tid];
+        int64_t b = (int64_t)atomicAdd(reinterpret_cast<unsigned long long*>(&w.fill[(tid * kCopies + cp) * kCtrStride64]),
+                                       (unsigned long long)tot);
+#pragma unroll
+        for (int v = 0; v < kW; ++v) {
+          s_wbase[v][tid] = b;
+          b += s_wcnt[v][tid];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          const int t = tsel[k][p];
+          if (t < 0) continue;
+          const int64_t e = s_wbase[wave][t] + slot[k][p];
+          if (e < s_lim[t]) w.keys[e] = key[k][p];
+        }
+    }
+  }
+  __syncthreads();
+  uint32_t* hc = w.hist + (size_t)cp * kHistStride;
 #pragma unroll
   for (int t = 0; t < kNT; ++t) {
-    if (!want[t]) continue;  // uniform
+    if (!((hist >> t) & 1u)) continue;  // uniform
     const uint32_t v = h[t * 256 + tid];
     if (v) atomicAdd(&hc[t * 256 + tid], v);
   }
 }
 
-// Select the byte of each target's key from the histogram of its source
-// (the plan's src: the first target of its pair under the same prefix).
-// Phase 1 sums the copies of every source histogram into LDS, phase 2 clears
-// them (every histogram is read before any is cleared), phase 3 finds the bin
-// that holds each target's rank (one wave per target in turn, 4 bins a lane);
-// then thread 0 assigns the lists (after pass 1) and writes the next plan.
-constexpr int kSelThreads = 1024;
-
-template <int kTP>
-__global__ __launch_bounds__(kSelThreads) void tails_select_kernel(TailWs w, int pass) {
+// Select after pass p >= 1, by one workgroup of kThreads (every thread
+// calls it; cnt is kNT x 256 words of LDS). Phase 1 sums the copies of every
+// histogram source into LDS, phase 2 clears them, phase 3 finds the bin that
+// holds each live target's rank (one wave per target in turn, 4 bins a
+// lane); the targets of a source that gathered in this pass are handed to
+// the finish. Thread 0 then plans the next pass: a source with at most
+// kGather keys under its prefix gathers them, the others histogram.
+template <int kTP, int kThreads>
+__device__ void tails_select_byte(const TailWs& w, int pass, uint32_t (*cnt)[256]) {
   constexpr int kNT = 3 * kTP;
-  constexpr int kWaves = kSelThreads / 64;
-  __shared__ uint32_t cnt[kNT][256];
-  __shared__ uint64_t pre[kNT], s_pre[kNT];  // entry / new prefixes
+  constexpr int kWaves = kThreads / 64;
+  __shared__ uint64_t s_pre[kNT];
   __shared__ int64_t s_rank[kNT], s_len[kNT];
-  __shared__ int s_src[kNT];
-  __shared__ TailList s_list[kNT];
-  __shared__ uint32_t s_hm;
+  __shared__ int s_src[kNT], s_lreg[kNT], s_fin[kNT];
+  __shared__ uint32_t s_hm, s_gm;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int shift = pass_shift(pass);
   if (threadIdx.x < kNT) {
     const int u = threadIdx.x;
-    pre[u] = w.plan->pre[u];
-    s_pre[u] = pre[u];
+    const TailSel x = w.sel[u];
+    s_pre[u] = w.plan->pre[u];
     s_src[u] = w.plan->src[u];
-    s_rank[u] = 0;
+    s_rank[u] = x.rank;
+    s_lreg[u] = x.lreg;
+    s_fin[u] = x.fin_src;
     s_len[u] = 0;
-    s_list[u] = w.list[u];
   }
-  if (threadIdx.x == 0) s_hm = w.plan->full | w.plan->list;
+  if (threadIdx.x == 0) {
+    s_hm = w.plan->hist;
+    s_gm = w.plan->gath;
+  }
   __syncthreads();
-  const uint32_t hm = s_hm;  // the sources that took a histogram
+  const uint32_t hm = s_hm, gm = s_gm;
+  if ((hm | gm) == 0u) return;  // uniform: the pass had nothing to do
   for (int t = wave; t < kNT; t += kWaves) {
     if (!((hm >> t) & 1u)) continue;
     uint32_t c[4] = {0u, 0u, 0u, 0u};
-#pragma unroll 4
-    for (int cp = 0; cp < kHistCopies; ++cp) {
+#pragma unroll
+    for (int cp = 0; cp < kCopies; ++cp) {
       const uint4 q = *reinterpret_cast<const uint4*>(w.hist + cp * kHistStride + t * 256 + 4 * lane);
       c[0] += q.x;
       c[1] += q.y;
@@ -950,15 +1109,24 @@ __global__ __launch_bounds__(kSelThreads) void tails_select_kernel(TailWs w, int
     for (int k = 0; k < 4; ++k) cnt[t][4 * lane + k] = c[k];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < kHistCopies * kNT * 64; i += kSelThreads) {
+  for (int i = threadIdx.x; i < kCopies * kNT * 64; i += kThreads) {
     const int cp = i / (kNT * 64), r = i % (kNT * 64);
     if ((hm >> (r >> 6)) & 1u)
       *reinterpret_cast<uint4*>(w.hist + cp * kHistStride + 4 * r) = make_uint4(0u, 0u, 0u, 0u);
   }
   for (int t = wave; t < kNT; t += kWaves) {
-    int64_t rank = pass ? w.sel[t].rank : 1;  // pass 0: every target, rank from the total below
-    if (rank <= 0) continue;                   // uniform: done, or nothing to select
+    const int64_t rank = s_rank[t];
+    if (rank <= 0 || s_fin[t] >= 0) continue;  // uniform: done, none, or finishing
     const int src = s_src[t];
+    if ((gm >> src) & 1u) {
+      if (lane == 0) {
+        s_fin[t] = src;
+        w.sel[t].fin_src = src;
+        w.sel[t].fin_bits = shift + 8;
+      }
+      continue;
+    }
+    if (!((hm >> src) & 1u)) continue;
     uint32_t c[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) c[k] = cnt[src][4 * lane + k];
@@ -969,100 +1137,224 @@ __global__ __launch_bounds__(kSelThreads) void tails_select_kernel(TailWs w, int
       const int64_t o = __shfl_up(incl, off);
       if (lane >= off) incl += o;
     }
-    const int64_t total = __shfl(incl, 63);
-    if (pass == 0) {
-      // The pass-0 histogram holds every counted token of the pair.
-      const int j = t % kTP;
-      if (j < kWorstT) {
-        rank = 0;
-        if (total > 0) {
-          int64_t lo, hi;
-          quantile_ranks(total, quantile_prob(j >> 1), &lo, &hi);
-          rank = (j & 1) ? hi : lo;
-        }
-      } else {
-        // The k-th largest: rank count - k + 1 (the smallest when fewer are
-        // counted); no target without worst tokens requested.
-        rank = (w.k > 0 && total > 0) ? (total > w.k ? total - w.k + 1 : 1) : 0;
-      }
-      if (j == 0 && lane == 0) w.count[t / kTP] = total;
-      if (rank == 0) {
-        if (lane == 0) w.sel[t].rank = 0;
-        continue;
-      }
-    }
     const int64_t excl = incl - lsum;
     if (excl < rank && rank <= incl) {
       int64_t below = excl;
       int k = 0;
       while (below + (int64_t)c[k] < rank) below += c[k++];
-      const uint64_t np = (pass ? (pre[t] << 8) : 0ull) | (uint64_t)(4 * lane + k);
-      // A key whose top byte is 0 is the bit pattern of a double below 2^-1007:
-      // the difference of two fp32 scores is 0 or at least 2^-149 in
-      // magnitude, so every key in bin 0 of pass 0 is 0 and the selection is
-      // done (the prefix, 0, is the key).
-      const int64_t nr = (pass == 0 && 4 * lane + k == 0) ? 0 : rank - below;
+      const uint64_t np = (s_pre[t] << 8) | (uint64_t)(4 * lane + k);
       w.sel[t].prefix = np;
-      w.sel[t].rank = nr;
+      w.sel[t].rank = rank - below;
       s_pre[t] = np;
-      s_rank[t] = nr;
+      s_rank[t] = rank - below;
       s_len[t] = (int64_t)c[k];
     }
   }
   __syncthreads();
   if (threadIdx.x != 0) return;
-  // Lists for passes 3 .. 7 (after pass 1), in target order while the key
-  // buffer lasts; targets under one prefix share one.
-  if (pass == 1) {
-    int64_t used = 0;
-    for (int u = 0; u < kNT; ++u) {
-      TailList L{0, 0, -1};
-      if (s_rank[u] > 0) {
-        int src = u;
-        for (int v = kTP * (u / kTP); v < u; ++v)
-          if (s_rank[v] > 0 && s_pre[v] == s_pre[u]) {
-            src = v;
-            break;
-          }
-        if (src != u) {
-          L = s_list[src];  // shares that target's list (or its lack of one)
-        } else if (used + s_len[u] <= w.cap) {
-          L = TailList{used, s_len[u], u};
-          used += s_len[u];
-        }
-      }
-      s_list[u] = L;
-      w.list[u] = L;
-    }
-  }
-  // The plan of the next pass: each live target's source, and which sources
-  // histogram over the batch, over a list, or (pass 2) own a list region.
-  const int next = pass + 1;
-  uint32_t full = 0u, list = 0u, own = 0u;
+  uint32_t hist = 0u, gath = 0u;
   for (int u = 0; u < kNT; ++u) {
+    const bool live = s_rank[u] > 0 && s_fin[u] < 0;
     int src = u;
-    if (s_rank[u] > 0) {
+    if (live) {
       for (int v = kTP * (u / kTP); v < u; ++v)
-        if (s_rank[v] > 0 && s_pre[v] == s_pre[u]) {
+        if (s_rank[v] > 0 && s_fin[v] < 0 && s_pre[v] == s_pre[u]) {
           src = v;
           break;
         }
-      if (src == u) {
-        const int32_t ls = next >= 2 ? s_list[u].src : -1;
-        if (next <= 2 || ls < 0) full |= 1u << u;
-        else list |= 1u << u;
-        if (next == 2 && ls == u) own |= 1u << u;
+      if (src == u && pass < kLastPass) {
+        if (s_len[u] <= kGather) gath |= 1u << u;
+        else hist |= 1u << u;
       }
     }
     w.plan->pre[u] = s_pre[u];
     w.plan->src[u] = (int8_t)src;
-    w.plan->lsrc[u] = next >= 3 ? s_list[u].src : -1;
+    w.plan->lsrc[u] = s_lreg[u];
   }
-  w.plan->full = full;
-  w.plan->list = list;
-  w.plan->own = own;
+  w.plan->hist = hist;
+  w.plan->gath = gath;
+  w.plan->own = 0u;
 }
 
+template <int kTP>
+__global__ __launch_bounds__(kSelThreads) void tails_select_kernel(TailWs w, int pass) {
+  __shared__ uint32_t cnt[3 * kTP][256];
+  tails_select_byte<kTP, kSelThreads>(w, pass, cnt);
+}
+
+// Passes 2 .. 6: each histogram source counts this pass's byte of the keys
+// under its prefix, each gathering source gathers them, reading its list
+// region (grid-stride over whole waves: the ballots need every lane), or the
+// batch (sequences dealt to the workgroups in turn) for a source without
+// one. Integer counts, so the order of the keys does not matter.
+constexpr int kListBlocks = 512;
+
+template <bool kVec, int kTP>
+__global__ __launch_bounds__(kTailThreads) void tails_list_kernel(TailArgs a, TailWs w, int pass) {
+  constexpr int kNT = 3 * kTP;
+  __shared__ uint32_t h[kNT * 256];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int shift = pass_shift(pass);
+  const uint32_t hist = w.plan->hist, gath = w.plan->gath;
+  const uint32_t act = hist | gath;
+  if (act == 0u) return;  // uniform: no target left for the passes
+  uint64_t pre[kNT];
+  int lst[kNT];
+  uint32_t batch = 0u;
+#pragma unroll
+  for (int t = 0; t < kNT; ++t) {
+    pre[t] = w.plan->pre[t];
+    lst[t] = w.plan->lsrc[t];
+    if (((act >> t) & 1u) && lst[t] < 0) batch |= 1u << t;
+  }
+#pragma unroll
+  for (int t = 0; t < kNT; ++t)
+    if ((hist >> t) & 1u) h[t * 256 + tid] = 0u;
+  __syncthreads();
+  const int64_t stride = (int64_t)gridDim.x * kTailThreads;
+  const int64_t wave0 = (int64_t)blockIdx.x * kTailThreads + (tid - lane);
+  for (int u = 0; u < kNT; ++u) {
+    bool used = false;
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) used = used || (((act >> t) & 1u) && lst[t] == u);
+    if (!used) continue;  // uniform
+    const TailList R = w.list[u];
+    for (int64_t e0 = wave0; e0 < R.len; e0 += stride) {
+      const int64_t e = e0 + lane;
+      const bool in = e < R.len;
+      const uint64_t key = in ? w.keys[R.off + e] : 0ull;
+      const uint32_t digit = (uint32_t)(key >> shift) & 255u;
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) {
+        if (!((act >> t) & 1u) || lst[t] != u) continue;  // uniform
+        const bool hit = in && (key >> (shift + 8)) == pre[t];
+        if ((hist >> t) & 1u) wave_hist_add(h + t * 256, digit, hit, lane);
+        else gather_add(w, t, key, hit, lane);
+      }
+    }
+  }
+  if (batch != 0u) {  // uniform
+    constexpr int64_t kStep = 4 * kTailThreads;
+    const int64_t Lw = (a.L + kStep - 1) / kStep * kStep;
+    for (int64_t n = blockIdx.x; n < a.N; n += gridDim.x) {
+      const float* const rows[3] = {a.A + n * a.ld, a.B + n * a.ld, a.C + n * a.ld};
+      const uint8_t* M = a.mask + n * a.ld;
+      for (int64_t i0 = 4 * (int64_t)tid; i0 < Lw; i0 += kStep) {
+        float vv[4][3];
+        bool actv[4];
+        tail_load4<kVec>(a, rows, M, i0, vv, actv);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int p = 0; p < 3; ++p) {
+            uint64_t key;
+            const bool ok = tail_key(vv[k], actv[k], p, &key);
+            const uint32_t digit = (uint32_t)(key >> shift) & 255u;
+#pragma unroll
+            for (int j = 0; j < kTP; ++j) {
+              const int t = kTP * p + j;
+              if (!((batch >> t) & 1u)) continue;  // uniform
+              const bool hit = ok && (key >> (shift + 8)) == pre[t];
+              if ((hist >> t) & 1u) wave_hist_add(h + t * 256, digit, hit, lane);
+              else gather_add(w, t, key, hit, lane);
+            }
+          }
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* hc = w.hist + (size_t)(blockIdx.x % kCopies) * kHistStride;
+#pragma unroll
+  for (int t = 0; t < kNT; ++t) {
+    if (!((hist >> t) & 1u)) continue;  // uniform
+    const uint32_t v = h[t * 256 + tid];
+    if (v) atomicAdd(&hc[t * 256 + tid], v);
+  }
+}
+
+// The finish, one workgroup per source (most exit at once): its targets'
+// remaining bytes are selected from its gathered keys, held four to a
+// thread, one byte per round (histograms in LDS, one wave per target).
+constexpr int kFinThreads = 1024;
+static_assert(kFinThreads * 4 == kGather, "four gathered keys a thread");
+
+template <int kTP>
+__global__ __launch_bounds__(kFinThreads) void tails_finish_kernel(TailWs w) {
+  __shared__ uint32_t hh[kTP][256];
+  __shared__ uint64_t s_pre[kTP];
+  __shared__ int64_t s_rank[kTP];
+  __shared__ uint32_t s_mine;
+  __shared__ int s_bits;
+  const int s = blockIdx.x, p = s / kTP, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) {
+    uint32_t m = 0u;
+    int bits = 0;
+    for (int j = 0; j < kTP; ++j) {
+      const TailSel x = w.sel[kTP * p + j];
+      s_pre[j] = x.prefix;
+      s_rank[j] = x.rank;
+      if (x.fin_src == s && x.rank > 0) {
+        m |= 1u << j;
+        bits = x.fin_bits;
+      }
+    }
+    s_mine = m;
+    s_bits = bits;
+  }
+  __syncthreads();
+  const uint32_t mine = s_mine;
+  if (mine == 0u) return;  // uniform
+  const uint32_t g = min(w.gcnt[s * kCtrStride32], (uint32_t)kGather);
+  uint64_t key[4];
+  bool in[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t i = (uint32_t)(tid + m * kFinThreads);
+    in[m] = i < g;
+    key[m] = in[m] ? w.gbuf[(size_t)s * kGather + i] : 0ull;
+  }
+  for (int sh = s_bits - 8; sh >= 0; sh -= 8) {
+    for (int i = tid; i < kTP * 256; i += kFinThreads) hh[i >> 8][i & 255] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kTP; ++j) {
+      if (!((mine >> j) & 1u)) continue;  // uniform
+      const uint64_t pj = s_pre[j];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        wave_hist_add(hh[j], (uint32_t)(key[m] >> sh) & 255u, in[m] && (key[m] >> (sh + 8)) == pj,
+                      lane);
+    }
+    __syncthreads();
+    for (int j = wave; j < kTP; j += kFinThreads / 64) {
+      if (!((mine >> j) & 1u)) continue;
+      const int64_t rank = s_rank[j];
+      uint32_t c[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c[k] = hh[j][4 * lane + k];
+      const int64_t lsum = (int64_t)c[0] + c[1] + c[2] + c[3];
+      int64_t incl = lsum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int64_t o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      const int64_t excl = incl - lsum;
+      if (excl < rank && rank <= incl) {
+        int64_t below = excl;
+        int k = 0;
+        while (below + (int64_t)c[k] < rank) below += c[k++];
+        s_pre[j] = (s_pre[j] << 8) | (uint64_t)(4 * lane + k);
+        s_rank[j] = rank - below;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid < kTP && ((mine >> tid) & 1u)) {
+    w.sel[kTP * p + tid].prefix = s_pre[tid];
+    w.sel[kTP * p + tid].rank = 0;
+  }
+}
 // Batch results, one workgroup per pair: thread j folds the contiguous
 // sequences [j per, (j + 1) per) in order (per depends on N only), then a
 // fixed tree over the threads. The maximum keeps the first sequence (and,
@@ -1251,6 +1543,8 @@ __global__ __launch_bounds__(kTailThreads) void tails_worst_count_kernel(TailArg
 // Exclusive scans of the six count rows over the sequences, one workgroup
 // per row, 64-bit offsets. Thread j takes the contiguous sequences
 // [j per, (j + 1) per).
+constexpr int kScanThreads = 1024;
+
 __global__ __launch_bounds__(kScanThreads) void tails_worst_scan_kernel(TailWs w, int64_t N) {
   __shared__ int64_t wsum[kScanThreads / 64];
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1427,48 +1721,43 @@ __global__ __launch_bounds__(kWorstSortThreads) void tails_worst_sort_kernel(Tai
 
 size_t tails_workspace_bytes(int64_t N, int64_t L, int32_t k) { return tail_bytes(N, L, k); }
 
-template <int kMode, int kTP>
-static void launch_hist(const TailArgs& a, const TailWs& w, int pass, hipStream_t stream) {
-  if (a.vec)
-    hipLaunchKernelGGL((tails_hist_kernel<true, kMode, kTP>), dim3((unsigned)a.N), dim3(kTailThreads),
-                       0, stream, a, w, pass);
-  else
-    hipLaunchKernelGGL((tails_hist_kernel<false, kMode, kTP>), dim3((unsigned)a.N),
-                       dim3(kTailThreads), 0, stream, a, w, pass);
-}
-
 // The selection passes and the batch results, for kTP targets per pair.
 template <int kTP>
 static void launch_select(const TailArgs& a, const TailWs& w, hipStream_t stream) {
   constexpr int kNT = 3 * kTP;
+  const dim3 rows((unsigned)a.N), blk(kTailThreads);
   if (a.N > 0) {
-    // Every pass runs, also with L == 0 (pass 0 then writes empty partials).
-    for (int pass = 0; pass < 8; ++pass) {
-      if (pass == 0) {
-        launch_hist<0, kTP>(a, w, pass, stream);
-      } else if (pass == 2) {
-        launch_hist<2, kTP>(a, w, pass, stream);
-        hipLaunchKernelGGL(tails_scan_kernel, dim3(kNT), dim3(kScanThreads), 0, stream, w, a.N);
-        launch_hist<3, kTP>(a, w, pass, stream);
-      } else {
-        launch_hist<1, kTP>(a, w, pass, stream);  // passes >= 3: targets without a list
-      }
-      if (pass >= 3)
-        hipLaunchKernelGGL(tails_list_kernel<kTP>, dim3(kListBlocks), dim3(kTailThreads), 0, stream,
-                           w, pass);
+    // Also with L == 0: pass 0 writes the empty partials.
+    const bool wide = a.L > 65535;
+    if (a.vec) {
+      if (wide) hipLaunchKernelGGL((tails_p0_kernel<true, true>), rows, blk, 0, stream, a, w);
+      else hipLaunchKernelGGL((tails_p0_kernel<true, false>), rows, blk, 0, stream, a, w);
+    } else {
+      if (wide) hipLaunchKernelGGL((tails_p0_kernel<false, true>), rows, blk, 0, stream, a, w);
+      else hipLaunchKernelGGL((tails_p0_kernel<false, false>), rows, blk, 0, stream, a, w);
+    }
+  }
+  // With no token the histograms are empty: count 0 and no rank to select.
+  hipLaunchKernelGGL(tails_p0_select_kernel<kTP>, dim3(3), dim3(kSelThreads), 0, stream, w);
+  if (a.N > 0 && a.L > 0) {
+    if (a.vec) hipLaunchKernelGGL((tails_p1_kernel<true, kTP>), rows, blk, 0, stream, a, w);
+    else hipLaunchKernelGGL((tails_p1_kernel<false, kTP>), rows, blk, 0, stream, a, w);
+    hipLaunchKernelGGL(tails_select_kernel<kTP>, dim3(1), dim3(kSelThreads), 0, stream, w, 1);
+    for (int pass = 2; pass <= kLastPass; ++pass) {
+      if (a.vec)
+        hipLaunchKernelGGL((tails_list_kernel<true, kTP>), dim3(kListBlocks), blk, 0, stream, a, w, pass);
+      else
+        hipLaunchKernelGGL((tails_list_kernel<false, kTP>), dim3(kListBlocks), blk, 0, stream, a, w, pass);
       hipLaunchKernelGGL(tails_select_kernel<kTP>, dim3(1), dim3(kSelThreads), 0, stream, w, pass);
     }
-  } else {
-    // No sequence: empty histograms give count 0 and no rank to select.
-    hipLaunchKernelGGL(tails_select_kernel<kTP>, dim3(1), dim3(kSelThreads), 0, stream, w, 0);
+    hipLaunchKernelGGL(tails_finish_kernel<kTP>, dim3(kNT), dim3(kFinThreads), 0, stream, w);
   }
   hipLaunchKernelGGL(tails_final_kernel<kTP>, dim3(3), dim3(kFinalThreads), 0, stream, a, w);
 }
 
 hipError_t launch_tails(const TailArgs& a, hipStream_t stream) {
   const TailWs w = tail_layout(a.workspace, a.N, a.L, a.worst_k);
-  hipLaunchKernelGGL(tails_init_kernel, dim3(kHistCopies), dim3(kTailThreads), 0, stream, w,
-                     a.worst_k > 0 ? kMaxTP : kWorstT);
+  hipLaunchKernelGGL(tails_init_kernel, dim3(kInitBlocks), dim3(kTailThreads), 0, stream, w);
   if (a.worst_k > 0) {
     launch_select<kMaxTP>(a, w, stream);
     if (a.N > 0 && a.L > 0) {

@@ -140,6 +140,46 @@ __host__ __device__ inline double quantile_lerp(int64_t n, double p, double a, d
   return g < 0.5 ? a + diff * g : b - diff * (1.0 - g);
 }
 
+// Keys of |delta|: the bit pattern of the fp64 |l - r| of two finite fp32
+// scores. As non-negative doubles the keys order like unsigned integers. The
+// difference is 0 or has an fp64 exponent in [874, 1152] (2^-149 <= |delta|
+// < 2^130), so the top 16 bits (exponent and four mantissa bits) take 4 464
+// values; with the key 0 as bucket 0 that is 4 465 buckets, monotone in the
+// key.
+constexpr uint32_t kKeyTop16Lo = 874u << 4;          // top 16 bits of 2^-149
+constexpr uint32_t kKeyTop16Hi = (1152u << 4) | 15u;  // top 16 bits just below 2^130
+constexpr int kKeyBuckets = (int)(kKeyTop16Hi - kKeyTop16Lo) + 2;  // 4 465
+
+__device__ __forceinline__ uint32_t key_bucket(uint64_t k) {
+  const uint32_t t = (uint32_t)(k >> 48);
+  return k == 0 ? 0u : min(max(t, kKeyTop16Lo), kKeyTop16Hi) - kKeyTop16Lo + 1u;
+}
+
+// The top 16 bits of the keys in bucket b > 0.
+__device__ __forceinline__ uint64_t bucket_top16(uint32_t b) {
+  return (uint64_t)(b - 1u + kKeyTop16Lo);
+}
+
+// Number of lanes below this one whose bit is set in m.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Wave-aggregated LDS histogram increment of bin b for the lanes with hit
+// (every lane of the wave calls it): when every hitting lane has the bin of
+// the wave's first lane (read with readfirstlane, no LDS round trip), one
+// atomic adds them all -- the common case for runs of equal keys.
+__device__ __forceinline__ void wave_hist_add(uint32_t* h, uint32_t b, bool hit, int lane) {
+  const uint64_t hb = __ballot(hit);
+  if (hb == 0) return;
+  const uint32_t b0 = __builtin_amdgcn_readfirstlane(b);
+  if (__ballot(hit && b != b0) == 0) {
+    if (lane == __ffsll((long long)hb) - 1) atomicAdd(&h[b0], (uint32_t)__popcll(hb));
+  } else if (hit) {
+    atomicAdd(&h[b], 1u);
+  }
+}
+
 struct TailArgs {
   const float* A;
   const float* B;

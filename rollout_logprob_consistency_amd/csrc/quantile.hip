@@ -33,24 +33,14 @@ constexpr int kQThreads = 256;
 constexpr int kQWaves = kQThreads / 64;
 constexpr int kQT = 6;                  // ranks lo / hi of p50, p95, p99
 constexpr uint64_t kNoKey = ~0ull;      // not counted (a real key has bit 63 clear)
-constexpr uint32_t kTop16Lo = 874u << 4;          // top 16 bits of 2^-149
-constexpr uint32_t kTop16Hi = (1152u << 4) | 15u;  // top 16 bits just below 2^130
-constexpr int kBins = (int)(kTop16Hi - kTop16Lo) + 2;  // 4 465 (bin 0: the key 0)
-constexpr int kBinsPerThread = (kBins + kQThreads - 1) / kQThreads;  // 18
+constexpr int kBinsPerThread = (kKeyBuckets + kQThreads - 1) / kQThreads;  // 18
 constexpr int kCand = 512;              // gathered candidates
 
-static_assert(kQThreads * kBinsPerThread >= kBins, "every bin belongs to a thread");
+static_assert(kQThreads * kBinsPerThread >= kKeyBuckets, "every bin belongs to a thread");
 
 __device__ __forceinline__ uint64_t key_of(float l, float r, bool act) {
   if (!act || !__builtin_isfinite(l) || !__builtin_isfinite(r)) return kNoKey;
   return (uint64_t)__double_as_longlong(fabs((double)l - (double)r));
-}
-
-// Bucket of a counted key: 0 for the key 0, else its top 16 bits relative to
-// the smallest nonzero difference (monotone in the key).
-__device__ __forceinline__ uint32_t bucket(uint64_t k) {
-  const uint32_t t = (uint32_t)(k >> 48);
-  return k == 0 ? 0u : min(max(t, kTop16Lo), kTop16Hi) - kTop16Lo + 1u;
 }
 
 // Scores and mask of the four positions i .. i + 3 of a row (inactive past
@@ -88,20 +78,6 @@ __device__ __forceinline__ Raw4 load4(const float* Lp, const float* Rp, const ui
 __device__ __forceinline__ void keys_of(const Raw4& q, uint64_t (&k)[4]) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) k[e] = key_of(q.l[e], q.r[e], q.act[e]);
-}
-
-// Wave-aggregated LDS histogram increment of bin `b` for the lanes with hit:
-// when every hitting lane has the bin of the wave's first lane (read with
-// readfirstlane, no LDS round trip), one atomic adds them all.
-__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t b, bool hit, int lane) {
-  const uint64_t hb = __ballot(hit);
-  if (hb == 0) return;
-  const uint32_t b0 = __builtin_amdgcn_readfirstlane(b);
-  if (__ballot(hit && b != b0) == 0) {
-    if (lane == __ffsll((long long)hb) - 1) atomicAdd(&h[b0], (uint32_t)__popcll(hb));
-  } else if (hit) {
-    atomicAdd(&h[b], 1u);
-  }
 }
 
 template <bool kVec>
@@ -156,7 +132,7 @@ __global__ __launch_bounds__(kQThreads) void seq_quantile_kernel(QuantArgs a) {
   // Step 1: the 16-bit bucket histogram.
   walk([&](const uint64_t (&k)[4]) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) hist_add(hist, bucket(k[e]), k[e] != kNoKey, lane);
+    for (int e = 0; e < 4; ++e) wave_hist_add(hist, key_bucket(k[e]), k[e] != kNoKey, lane);
   });
   __syncthreads();
   // Thread j owns bins [18 j, 18 j + 18): their sum, an exclusive scan of the
@@ -197,7 +173,7 @@ __global__ __launch_bounds__(kQThreads) void seq_quantile_kernel(QuantArgs a) {
       while (below + (int64_t)hist[b0 + b] < r) below += hist[b0 + b++];
       const uint32_t bk = (uint32_t)(b0 + b);
       // Bucket 0 holds only the key 0: that rank is settled.
-      s_pre[t] = bk == 0 ? 0ull : (uint64_t)(bk - 1u + kTop16Lo);
+      s_pre[t] = bk == 0 ? 0ull : (uint64_t)(bk - 1u + kKeyTop16Lo);
       s_rank[t] = bk == 0 ? 0 : r - below;
       s_val[t] = 0ull;
       if (bk != 0) {
@@ -296,7 +272,7 @@ __global__ __launch_bounds__(kQThreads) void seq_quantile_kernel(QuantArgs a) {
 #pragma unroll
           for (int t = 0; t < kQT; ++t) {
             if (!use[t]) continue;  // uniform
-            hist_add(h8[t], digit, k != kNoKey && (k >> (shift + 8)) == pre[t], lane);
+            wave_hist_add(h8[t], digit, k != kNoKey && (k >> (shift + 8)) == pre[t], lane);
           }
         }
       });

@@ -132,6 +132,36 @@ def test_seq_quantiles_one_token_long_rows_and_strides():
             assert np.array_equal(got[p], ref[p]), (pad, p)
 
 
+@pytest.mark.parametrize("case", ["ties_in_lists", "ties_beyond_key_buffer", "one_bucket"])
+def test_selection_paths(case):
+    # The selection's paths, each exact against the oracle:
+    #  ties_in_lists: |delta| takes eight values k / 1024 (exact in fp32),
+    #    about 18 000 tokens each. Every quantile's bucket fits its list, but
+    #    more than 4 096 keys share every prefix down to the last byte: the
+    #    lists are read in every pass and nothing is gathered.
+    #  ties_beyond_key_buffer: two values 0.25 and 0.25 + 2^-20 in one
+    #    16-bit bucket holding every token: too many for the pair's key
+    #    buffer (a quarter of the positions), so the batch is read in every
+    #    pass.
+    #  one_bucket: |delta| continuous in [1, 1.0625), one bucket, too many
+    #    for the key buffer: the batch is read until a prefix holds at most
+    #    4 096 keys, which are then gathered from the batch.
+    rng = np.random.default_rng({"ties_in_lists": 5, "ties_beyond_key_buffer": 6, "one_bucket": 7}[case])
+    N, L = (64, 2304) if case == "ties_in_lists" else (16, 2304)
+    B = -np.floor(rng.uniform(1.0, 8.0, (N, L))).astype(np.float32)   # integers: exact differences
+    if case == "ties_in_lists":
+        d = rng.integers(1, 9, (N, L)).astype(np.float32) / np.float32(1024.0)
+    elif case == "ties_beyond_key_buffer":
+        d = np.where(rng.random((N, L)) < 0.6, np.float32(0.25), np.float32(0.25 + 2.0 ** -20))
+    else:
+        d = (1.0 + rng.random((N, L)) / 16.0).astype(np.float32)
+    A = (B - d).astype(np.float32)
+    C = (B + np.float32(0.5) * d).astype(np.float32)
+    M = (rng.random((N, L)) < 0.97).astype(np.uint8)
+    run(A, B, C, M)
+    run_worst(A, B, C, M, 64)
+
+
 @pytest.mark.parametrize("N,L", [(0, 5), (3, 0), (1, 1)])
 def test_degenerate_sizes(N, L):
     A = np.zeros((N, L), np.float32)
