@@ -29,6 +29,18 @@ bool spans_ok(int64_t ldh, int64_t H) {
 }
 constexpr uint32_t kScoreFlags = LP_SCORE_STATS | LP_SCORE_BF16_LOGITS;
 
+// The scoring dispatches fit 2^32 - 1 work-items: n_vt x n_tt tile
+// workgroups, and the merge's workgroup of 64 x 16 threads per 64 rows.
+bool score_grid_ok(int64_t T, int64_t n_vt, int64_t n_tt) {
+  return n_vt * n_tt <= lp::kMaxDispatchItems / lp::kScoreTileThreads &&
+         (T + 63) / 64 <= lp::kMaxDispatchItems / (64 * lp::kMergeSegs);
+}
+
+// Sequences whose workgroups (wg_per_row of `threads` each) fit one dispatch.
+bool rows_fit(int64_t N, int64_t wg_per_row, int64_t threads) {
+  return N <= lp::kMaxDispatchItems / (wg_per_row * threads);
+}
+
 // Canonical shard of the merge segments: rank r of n owns segments
 // [16 r / n, 16 (r + 1) / n) and the vocabulary rows they cover.
 lp_vocab_shard shard_of(int64_t V_true, int32_t n_shards, int32_t rank) {
@@ -94,7 +106,7 @@ lp_status lp_score_shard(const void* hidden_bf16, int64_t ldh, const void* w_sha
     return LP_EUNSUPPORTED;
   const int64_t n_vt = (rows + lp::kTileV - 1) / lp::kTileV;
   const int64_t n_tt = (T + lp::kTileT - 1) / lp::kTileT;
-  if (T > kI32Max || H > kI32Max || n_vt * n_tt > kI32Max || !spans_ok(ldh, H))
+  if (T > kI32Max || H > kI32Max || !score_grid_ok(T, n_vt, n_tt) || !spans_ok(ldh, H))
     return LP_EUNSUPPORTED;
 
   lp::ScoreArgs a;
@@ -209,7 +221,7 @@ lp_status score_impl(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
   if (!aligned(hidden_bf16, 16) || !aligned(w_bf16, 16)) return LP_EUNSUPPORTED;
   const int64_t n_vt = (V_true + lp::kTileV - 1) / lp::kTileV;
   const int64_t n_tt = (T + lp::kTileT - 1) / lp::kTileT;
-  if (T > kI32Max || H > kI32Max || V_rows > kI32Max || n_vt * n_tt > kI32Max ||
+  if (T > kI32Max || H > kI32Max || V_rows > kI32Max || !score_grid_ok(T, n_vt, n_tt) ||
       !spans_ok(ldh, H))
     return LP_EUNSUPPORTED;
 
@@ -293,7 +305,7 @@ lp_status lp_compare(const float* gen_A, const float* replay_B, const float* tra
   if (N == 0) return LP_OK;
   if (!out) return LP_EINVAL;
   if (L > 0 && (!gen_A || !replay_B || !train_C || !mask)) return LP_EINVAL;
-  if (L > kI32Max || N > kI32Max) return LP_EUNSUPPORTED;
+  if (L > kI32Max || !rows_fit(N, 1, lp::kCompareThreads)) return LP_EUNSUPPORTED;
   lp::CompareArgs a;
   a.A = gen_A;
   a.B = replay_B;
@@ -326,7 +338,7 @@ lp_status lp_correct(const float* rollout_lp, const float* train_lp, const uint8
   if (N == 0) return LP_OK;
   if (!out) return LP_EINVAL;
   if (L > 0 && (!rollout_lp || !train_lp || !mask)) return LP_EINVAL;
-  if (L > kI32Max || N > kI32Max) return LP_EUNSUPPORTED;
+  if (L > kI32Max || !rows_fit(N, 1, lp::kRowThreads)) return LP_EUNSUPPORTED;
   lp::CorrectArgs a;
   a.rollout = rollout_lp;
   a.train = train_lp;
@@ -355,8 +367,8 @@ lp_status lp_compare_quantiles(const float* gen_A, const float* replay_B, const 
   if (N == 0) return LP_OK;
   if (!out || !aligned(out, 8)) return LP_EINVAL;
   if (L > 0 && (!gen_A || !replay_B || !train_C || !mask)) return LP_EINVAL;
-  // Three workgroups per sequence, in groups of 8 sequences: one grid row.
-  if (L > kI32Max || N > kI32Max || 3 * ((N + 7) / 8) * 8 > kI32Max) return LP_EUNSUPPORTED;
+  // Three workgroups per sequence, in groups of 8 sequences.
+  if (L > kI32Max || !rows_fit((N + 7) / 8 * 8, 3, lp::kRowThreads)) return LP_EUNSUPPORTED;
   lp::QuantArgs a;
   a.A = gen_A;
   a.B = replay_B;
@@ -398,7 +410,9 @@ lp_status lp_compare_tails_ex(const float* gen_A, const float* replay_B, const f
   if (k < 0 || k > LP_WORST_MAX || (k > 0 && !worst)) return LP_EINVAL;
   if ((pos_abs_sum == nullptr) != (pos_count == nullptr)) return LP_EINVAL;
   if (N > 0 && L > 0 && (!gen_A || !replay_B || !train_C || !mask)) return LP_EINVAL;
-  if (L > kI32Max || N > kI32Max) return LP_EUNSUPPORTED;
+  // One workgroup per sequence; 32-bit histogram counters (N L tokens at most).
+  if (L > kI32Max || !rows_fit(N, 1, lp::kRowThreads) || N * L > lp::kMaxDispatchItems)
+    return LP_EUNSUPPORTED;
   if (workspace_bytes < lp::tails_workspace_bytes(N, L, k) || !aligned(workspace, 256))
     return LP_EINVAL;
   if (k > 0 && !aligned(worst, 8)) return LP_EINVAL;

@@ -387,7 +387,7 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(7))) void c
 }  // namespace
 
 hipError_t launch_compare(const CompareArgs& a, hipStream_t stream) {
-  const dim3 g((unsigned)a.N), b(192);
+  const dim3 g((unsigned)a.N), b(kCompareThreads);
   const bool bitwise = a.atol < 0.0;
   if (a.per_token) {
     if (bitwise) hipLaunchKernelGGL((compare_kernel<true, true>), g, b, 0, stream, a);
@@ -458,7 +458,7 @@ namespace {
 constexpr int kMaxTP = 7;
 constexpr int kWorstT = 6;  // index of the k-th-largest target within a pair
 constexpr int kMaxTargets = 3 * kMaxTP;
-constexpr int kTailThreads = 256;
+constexpr int kTailThreads = kRowThreads;
 constexpr int kTailChunks = 64;     // sequence chunks of the position profile
 // Histogram copies: the workgroup of sequence n adds into copy n mod 8 (with
 // workgroups dealt to the 8 XCDs in turn, each copy is one XCD's), so no
@@ -606,17 +606,64 @@ size_t tail_bytes(int64_t N, int64_t L, int32_t k) { return tail_walk(nullptr, N
 __device__ __forceinline__ int pair_left(int p) { return p == 1 ? 1 : 0; }
 __device__ __forceinline__ int pair_right(int p) { return p == 0 ? 1 : 2; }
 
+// Position profile, stage 1: thread i of chunk c sums column i over the
+// chunk's sequences (fixed chunks, sequences in order); the final kernel
+// folds the chunks in order.
+__device__ void tails_pos_chunk(const TailArgs& a, const TailWs& w, int64_t i, int c) {
+  if (i >= a.L) return;
+  const int64_t per = (a.N + w.nch - 1) / w.nch;
+  const int64_t lo = c * per, hi = min(a.N, lo + per);
+  double s[3] = {0.0, 0.0, 0.0};
+  int32_t k[3] = {0, 0, 0};
+  // Eight sequences' loads are issued together (all of them, masked or not);
+  // the sums still take the sequences in ascending order.
+  constexpr int kB = 8;
+  for (int64_t n0 = lo; n0 < hi; n0 += kB) {
+    float v[kB][3];
+    bool act[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const bool in = n0 + b < hi;
+      const int64_t o = (in ? n0 + b : lo) * a.ld + i;
+      act[b] = in && a.mask[o] != 0;
+      v[b][0] = a.A[o];
+      v[b][1] = a.B[o];
+      v[b][2] = a.C[o];
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      if (!act[b]) continue;
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const float l = v[b][pair_left(p)], r = v[b][pair_right(p)];
+        if (!__builtin_isfinite(l) || !__builtin_isfinite(r)) continue;
+        s[p] += fabs((double)l - (double)r);
+        k[p] += 1;
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    w.pos_part[((size_t)c * 3 + p) * a.L + i] = s[p];
+    w.pos_cpart[((size_t)c * 3 + p) * a.L + i] = k[p];
+  }
+}
+
 // Clears the histograms (every copy) and the gather counts, and resets the
-// selection state.
+// selection state; with the position profile asked for (pos true, grid
+// ceil(L / 256) x chunks), workgroup (x, c) also forms stage 1 of the
+// profile for columns [256 x, 256 x + 256) of chunk c.
 constexpr int kInitBlocks = 64;
 
-__global__ __launch_bounds__(kTailThreads) void tails_init_kernel(TailWs w) {
+__global__ __launch_bounds__(kTailThreads) void tails_init_kernel(TailArgs a, TailWs w, bool pos) {
   uint4* z = reinterpret_cast<uint4*>(w.hist0);
   constexpr int64_t kVecs = (int64_t)(kHist0Words + kHistWords) / 4;
-  for (int64_t i = (int64_t)blockIdx.x * kTailThreads + threadIdx.x; i < kVecs;
-       i += (int64_t)gridDim.x * kTailThreads)
+  const int64_t wg = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  for (int64_t i = wg * kTailThreads + threadIdx.x; i < kVecs;
+       i += (int64_t)gridDim.x * gridDim.y * kTailThreads)
     z[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (blockIdx.x != 0) return;
+  if (pos) tails_pos_chunk(a, w, (int64_t)blockIdx.x * kTailThreads + threadIdx.x, (int)blockIdx.y);
+  if (wg != 0) return;
   const int t = threadIdx.x;
   if (t < kMaxTargets) {
     w.gcnt[t * kCtrStride32] = 0u;
@@ -1272,20 +1319,22 @@ __global__ __launch_bounds__(kTailThreads) void tails_list_kernel(TailArgs a, Ta
   }
 }
 
-// The finish, one workgroup per source (most exit at once): its targets'
-// remaining bytes are selected from its gathered keys, held four to a
-// thread, one byte per round (histograms in LDS, one wave per target).
 constexpr int kFinThreads = 1024;
 static_assert(kFinThreads * 4 == kGather, "four gathered keys a thread");
 
+// The finish of source s (every thread of a kFinThreads workgroup calls it):
+// its targets' remaining bytes are selected from its gathered keys, held
+// four to a thread, one byte per round (histograms in LDS, one wave per
+// target). Does nothing unless a target of s was handed to it.
 template <int kTP>
-__global__ __launch_bounds__(kFinThreads) void tails_finish_kernel(TailWs w) {
+__device__ void tails_finish_source(const TailWs& w, int s) {
   __shared__ uint32_t hh[kTP][256];
   __shared__ uint64_t s_pre[kTP];
   __shared__ int64_t s_rank[kTP];
   __shared__ uint32_t s_mine;
   __shared__ int s_bits;
-  const int s = blockIdx.x, p = s / kTP, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int p = s / kTP, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __syncthreads();  // the previous source's readers are done with the LDS
   if (tid == 0) {
     uint32_t m = 0u;
     int bits = 0;
@@ -1355,18 +1404,43 @@ __global__ __launch_bounds__(kFinThreads) void tails_finish_kernel(TailWs w) {
     w.sel[kTP * p + tid].rank = 0;
   }
 }
-// Batch results, one workgroup per pair: thread j folds the contiguous
-// sequences [j per, (j + 1) per) in order (per depends on N only), then a
-// fixed tree over the threads. The maximum keeps the first sequence (and,
-// within it, the first column) that reaches it.
-constexpr int kFinalThreads = 1024;
 
+// One workgroup per source (most exit at once).
 template <int kTP>
-__global__ __launch_bounds__(kFinalThreads) void tails_final_kernel(TailArgs a, TailWs w) {
-  __shared__ TailPart red[kFinalThreads];
-  __shared__ int32_t red_seq[kFinalThreads];
-  const int p = blockIdx.x, tid = threadIdx.x;
-  const int64_t per = (a.N + kFinalThreads - 1) / kFinalThreads;
+__global__ __launch_bounds__(kFinThreads) void tails_finish_kernel(TailWs w) {
+  tails_finish_source<kTP>(w, blockIdx.x);
+}
+
+// Batch results. Workgroup p < 3 reduces pair p's per-sequence partials
+// (after the finish): thread j folds the
+// contiguous sequences [j per, (j + 1) per) in order (per depends on N
+// only), then a fixed XOR butterfly within each wave and the waves in order.
+// The maximum keeps the first sequence (and, within it, the first column)
+// that reaches it. Workgroups 3, 4, ... fold the position profile's chunks
+// in order.
+template <int kTP>
+__global__ __launch_bounds__(kFinThreads) void tails_final_kernel(TailArgs a, TailWs w) {
+  if (blockIdx.x >= 3) {
+    for (int64_t idx = (int64_t)(blockIdx.x - 3) * kFinThreads + threadIdx.x; idx < 3 * a.L;
+         idx += (int64_t)(gridDim.x - 3) * kFinThreads) {  // p * L + i
+      double s = 0.0;
+      int32_t k = 0;
+#pragma unroll 8
+      for (int c = 0; c < w.nch; ++c) {
+        s += w.pos_part[(size_t)c * 3 * a.L + idx];
+        k += w.pos_cpart[(size_t)c * 3 * a.L + idx];
+      }
+      a.pos_sum[idx] = s;
+      a.pos_count[idx] = k;
+    }
+    return;
+  }
+  constexpr int kWaves = kFinThreads / 64;
+  __shared__ TailPart red[kWaves];
+  __shared__ int32_t red_seq[kWaves];
+  const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+
+  const int64_t per = (a.N + kFinThreads - 1) / kFinThreads;
   TailPart x{0.0, 0.0, 0ull, -1, 0};
   int32_t xs = -1;
   const int64_t lo = tid * per, hi = min(a.N, lo + per);
@@ -1382,108 +1456,66 @@ __global__ __launch_bounds__(kFinalThreads) void tails_final_kernel(TailArgs a, 
       xs = (int32_t)n;
     }
   }
-  red[tid] = x;
-  red_seq[tid] = xs;
+  // Both lanes of a butterfly step get the same result: sums are added in
+  // either order to the same value, and equal maxima keep the lower sequence.
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    TailPart o;
+    o.sum_abs = __shfl_xor(x.sum_abs, m);
+    o.sum_prob = __shfl_xor(x.sum_prob, m);
+    o.count = __shfl_xor(x.count, m);
+    o.max_key = (uint64_t)__shfl_xor((long long)x.max_key, m);
+    o.max_pos = __shfl_xor(x.max_pos, m);
+    const int32_t os = __shfl_xor(xs, m);
+    x.sum_abs += o.sum_abs;
+    x.sum_prob += o.sum_prob;
+    x.count += o.count;
+    if (o.max_pos >= 0 &&
+        (x.max_pos < 0 || o.max_key > x.max_key || (o.max_key == x.max_key && os < xs))) {
+      x.max_key = o.max_key;
+      x.max_pos = o.max_pos;
+      xs = os;
+    }
+  }
+  if (lane == 0) {
+    red[tid >> 6] = x;
+    red_seq[tid >> 6] = xs;
+  }
   __syncthreads();
-  for (int stride = kFinalThreads / 2; stride > 0; stride >>= 1) {
-    if (tid < stride) {
-      TailPart u = red[tid];
-      const TailPart v = red[tid + stride];
-      u.sum_abs += v.sum_abs;
-      u.sum_prob += v.sum_prob;
-      u.count += v.count;
-      // After the first steps a thread's sequences interleave with its
-      // partner's, so an equal key is decided by the sequence index.
-      const int32_t us = red_seq[tid], vs = red_seq[tid + stride];
-      if (v.max_pos >= 0 &&
-          (u.max_pos < 0 || v.max_key > u.max_key || (v.max_key == u.max_key && vs < us))) {
-        u.max_key = v.max_key;
-        u.max_pos = v.max_pos;
-        red_seq[tid] = vs;
-      }
-      red[tid] = u;
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    const TailPart& r = red[0];
-    lp_tail_stats o;
-    o.count = w.count[p];
-    const bool any = o.count > 0;
-    double q[3];
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const double qlo = __longlong_as_double((long long)w.sel[kTP * p + 2 * j].prefix);
-      const double qhi = __longlong_as_double((long long)w.sel[kTP * p + 2 * j + 1].prefix);
-      q[j] = any ? quantile_lerp(o.count, quantile_prob(j), qlo, qhi) : 0.0;
-    }
-    o.q50 = q[0];
-    o.q95 = q[1];
-    o.q99 = q[2];
-    o.max_abs = any ? __longlong_as_double((long long)r.max_key) : 0.0;
-    o.max_seq = any ? red_seq[0] : -1;
-    o.max_pos = any ? r.max_pos : -1;
-    o.sum_abs = r.sum_abs;
-    o.sum_prob_abs = r.sum_prob;
-    a.out[p] = o;
-  }
-}
-
-__global__ __launch_bounds__(kTailThreads) void tails_pos_kernel(TailArgs a, TailWs w) {
-  const int64_t i = (int64_t)blockIdx.x * kTailThreads + threadIdx.x;
-  if (i >= a.L) return;
-  const int c = blockIdx.y;
-  const int64_t per = (a.N + w.nch - 1) / w.nch;
-  const int64_t lo = c * per, hi = min(a.N, lo + per);
-  double s[3] = {0.0, 0.0, 0.0};
-  int32_t k[3] = {0, 0, 0};
-  // Eight sequences' loads are issued together (all of them, masked or not);
-  // the sums still take the sequences in ascending order.
-  constexpr int kB = 8;
-  for (int64_t n0 = lo; n0 < hi; n0 += kB) {
-    float v[kB][3];
-    bool act[kB];
-#pragma unroll
-    for (int b = 0; b < kB; ++b) {
-      const bool in = n0 + b < hi;
-      const int64_t o = (in ? n0 + b : lo) * a.ld + i;
-      act[b] = in && a.mask[o] != 0;
-      v[b][0] = a.A[o];
-      v[b][1] = a.B[o];
-      v[b][2] = a.C[o];
-    }
-#pragma unroll
-    for (int b = 0; b < kB; ++b) {
-      if (!act[b]) continue;
-#pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        const float l = v[b][pair_left(p)], r = v[b][pair_right(p)];
-        if (!__builtin_isfinite(l) || !__builtin_isfinite(r)) continue;
-        s[p] += fabs((double)l - (double)r);
-        k[p] += 1;
-      }
+  if (tid != 0) return;
+  TailPart r = red[0];
+  int32_t rs = red_seq[0];
+  for (int v = 1; v < kWaves; ++v) {  // waves in order: lower sequences first
+    const TailPart& y = red[v];
+    r.sum_abs += y.sum_abs;
+    r.sum_prob += y.sum_prob;
+    r.count += y.count;
+    if (y.max_pos >= 0 &&
+        (r.max_pos < 0 || y.max_key > r.max_key || (y.max_key == r.max_key && red_seq[v] < rs))) {
+      r.max_key = y.max_key;
+      r.max_pos = y.max_pos;
+      rs = red_seq[v];
     }
   }
+  lp_tail_stats o;
+  o.count = w.count[p];
+  const bool any = o.count > 0;
+  double q[3];
 #pragma unroll
-  for (int p = 0; p < 3; ++p) {
-    w.pos_part[((size_t)c * 3 + p) * a.L + i] = s[p];
-    w.pos_cpart[((size_t)c * 3 + p) * a.L + i] = k[p];
+  for (int j = 0; j < 3; ++j) {
+    const double qlo = __longlong_as_double((long long)w.sel[kTP * p + 2 * j].prefix);
+    const double qhi = __longlong_as_double((long long)w.sel[kTP * p + 2 * j + 1].prefix);
+    q[j] = any ? quantile_lerp(o.count, quantile_prob(j), qlo, qhi) : 0.0;
   }
-}
-
-// Position profile, stage 2: fold the chunks in order.
-__global__ __launch_bounds__(kTailThreads) void tails_pos_fold_kernel(TailArgs a, TailWs w) {
-  const int64_t idx = (int64_t)blockIdx.x * kTailThreads + threadIdx.x;  // p * L + i
-  if (idx >= 3 * a.L) return;
-  double s = 0.0;
-  int32_t k = 0;
-#pragma unroll 8
-  for (int c = 0; c < w.nch; ++c) {
-    s += w.pos_part[(size_t)c * 3 * a.L + idx];
-    k += w.pos_cpart[(size_t)c * 3 * a.L + idx];
-  }
-  a.pos_sum[idx] = s;
-  a.pos_count[idx] = k;
+  o.q50 = q[0];
+  o.q95 = q[1];
+  o.q99 = q[2];
+  o.max_abs = any ? __longlong_as_double((long long)r.max_key) : 0.0;
+  o.max_seq = any ? rs : -1;
+  o.max_pos = any ? r.max_pos : -1;
+  o.sum_abs = r.sum_abs;
+  o.sum_prob_abs = r.sum_prob;
+  a.out[p] = o;
 }
 
 // ---- Worst k tokens ----------------------------------------------------
@@ -1724,7 +1756,6 @@ size_t tails_workspace_bytes(int64_t N, int64_t L, int32_t k) { return tail_byte
 // The selection passes and the batch results, for kTP targets per pair.
 template <int kTP>
 static void launch_select(const TailArgs& a, const TailWs& w, hipStream_t stream) {
-  constexpr int kNT = 3 * kTP;
   const dim3 rows((unsigned)a.N), blk(kTailThreads);
   if (a.N > 0) {
     // Also with L == 0: pass 0 writes the empty partials.
@@ -1750,14 +1781,22 @@ static void launch_select(const TailArgs& a, const TailWs& w, hipStream_t stream
         hipLaunchKernelGGL((tails_list_kernel<false, kTP>), dim3(kListBlocks), blk, 0, stream, a, w, pass);
       hipLaunchKernelGGL(tails_select_kernel<kTP>, dim3(1), dim3(kSelThreads), 0, stream, w, pass);
     }
-    hipLaunchKernelGGL(tails_finish_kernel<kTP>, dim3(kNT), dim3(kFinThreads), 0, stream, w);
+    hipLaunchKernelGGL(tails_finish_kernel<kTP>, dim3(3 * kTP), dim3(kFinThreads), 0, stream, w);
   }
-  hipLaunchKernelGGL(tails_final_kernel<kTP>, dim3(3), dim3(kFinalThreads), 0, stream, a, w);
+  // Also the position profile's fold.
+  const int64_t fold_all = a.pos_sum && a.L > 0 ? (3 * a.L + kFinThreads - 1) / kFinThreads : 0;
+  const unsigned fold = (unsigned)(fold_all < 65536 ? fold_all : 65536);  // then a grid-stride loop
+  hipLaunchKernelGGL(tails_final_kernel<kTP>, dim3(3 + fold), dim3(kFinThreads), 0, stream, a, w);
 }
 
 hipError_t launch_tails(const TailArgs& a, hipStream_t stream) {
   const TailWs w = tail_layout(a.workspace, a.N, a.L, a.worst_k);
-  hipLaunchKernelGGL(tails_init_kernel, dim3(kInitBlocks), dim3(kTailThreads), 0, stream, w);
+  // With the position profile asked for, its stage 1 (also with N == 0:
+  // zero partials for the fold) runs in the init kernel.
+  const bool pos = a.pos_sum && a.L > 0;
+  const dim3 init_grid = pos ? dim3((unsigned)((a.L + kTailThreads - 1) / kTailThreads), (unsigned)w.nch)
+                             : dim3(kInitBlocks);
+  hipLaunchKernelGGL(tails_init_kernel, init_grid, dim3(kTailThreads), 0, stream, a, w, pos);
   if (a.worst_k > 0) {
     launch_select<kMaxTP>(a, w, stream);
     if (a.N > 0 && a.L > 0) {
@@ -1779,15 +1818,6 @@ hipError_t launch_tails(const TailArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(tails_worst_sort_kernel, dim3(3), dim3(kWorstSortThreads), 0, stream, a, w);
   } else {
     launch_select<kWorstT>(a, w, stream);
-  }
-  if (a.pos_sum && a.L > 0) {
-    // Stage 1 also runs with N == 0, writing zero partials for the fold.
-    hipLaunchKernelGGL(tails_pos_kernel,
-                       dim3((unsigned)((a.L + kTailThreads - 1) / kTailThreads), (unsigned)w.nch),
-                       dim3(kTailThreads), 0, stream, a, w);
-    hipLaunchKernelGGL(tails_pos_fold_kernel,
-                       dim3((unsigned)((3 * a.L + kTailThreads - 1) / kTailThreads)),
-                       dim3(kTailThreads), 0, stream, a, w);
   }
   return hipGetLastError();
 }

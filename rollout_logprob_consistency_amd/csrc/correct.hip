@@ -23,7 +23,7 @@
 namespace lp {
 namespace {
 
-constexpr int kCorrThreads = 256;
+constexpr int kCorrThreads = kRowThreads;
 constexpr int kCorrWaves = kCorrThreads / 64;
 
 struct CorrPart {

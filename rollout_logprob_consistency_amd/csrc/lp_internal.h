@@ -21,6 +21,7 @@ constexpr int kTileK = 64;    // hidden elements per LDS stage
 // arithmetic), which streams W at HBM rate instead of computing 256-token
 // tiles that are mostly padding.
 constexpr int kSkinnyMaxT = 64;
+constexpr int kScoreTileThreads = 256;  // threads of a tile workgroup
 
 struct ScoreArgs {
   const uint16_t* x;      // [T, ldh] bf16 bits
@@ -74,6 +75,13 @@ struct ShardArgs {
 // its row count, v_base = its first row); the merge takes the whole range.
 hipError_t launch_score_shard(const ScoreArgs& a, const ShardArgs& s, hipStream_t stream);
 hipError_t launch_merge_shards(const ScoreArgs& a, const ShardArgs& s, hipStream_t stream);
+
+// Row-parallel launches: one workgroup per sequence (three for the
+// per-sequence quantiles), of these many threads. A dispatch holds at most
+// 2^32 - 1 work-items, which bounds the sequences of one call.
+constexpr int kCompareThreads = 192;
+constexpr int kRowThreads = 256;  // correction, batch tails, per-sequence quantiles
+constexpr int64_t kMaxDispatchItems = 0xFFFFFFFFll;
 
 struct CompareArgs {
   const float* A;

@@ -29,7 +29,7 @@
 namespace lp {
 namespace {
 
-constexpr int kQThreads = 256;
+constexpr int kQThreads = kRowThreads;
 constexpr int kQWaves = kQThreads / 64;
 constexpr int kQT = 6;                  // ranks lo / hi of p50, p95, p99
 constexpr uint64_t kNoKey = ~0ull;      // not counted (a real key has bit 63 clear)

@@ -57,7 +57,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kScoreTileThreads;
 constexpr int kWaveV = 176;                  // vocab rows per wave
 constexpr int kWaveT = 128;                  // token columns per wave
 constexpr int kSubV = kWaveV / 16;           // 16-row MFMA tiles along vocab (11)

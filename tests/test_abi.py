@@ -412,3 +412,26 @@ def test_python_mirrors_of_header_constants():
     assert _lib.NOALLOC_SCRATCH_BYTES == header_define_expr("LP_NOALLOC_SCRATCH_BYTES")
     assert _lib.MERGE_SEGMENTS == header_define("LP_MERGE_SEGMENTS")
     assert _lib.VOCAB_TILE_ROWS == header_define("LP_VOCAB_TILE_ROWS")
+
+
+def test_dispatch_size_limits(L):
+    # Row-parallel entry points launch one workgroup per sequence (three for
+    # the per-sequence quantiles) and a dispatch holds at most 2^32 - 1
+    # work-items; the tails' histogram counters are 32-bit (N L tokens at
+    # most); the scoring tiles and merge are bounded the same way. Each
+    # limit is refused with LP_EUNSUPPORTED before anything is launched.
+    EUNSUP = 2
+    lim = 0xFFFFFFFF
+    n_cmp = lim // 192
+    assert cmp(L, N=n_cmp + 1) == EUNSUP
+    n_rows = lim // 256
+    assert tails(L, N=n_rows + 1) == EUNSUP
+    assert tails(L, N=3, Lq=(1 << 31) - 1) == EUNSUP                 # N L > 2^32 - 1
+    assert corr(L, N=n_rows + 1) == EUNSUP
+    n_q = lim // (3 * 256) // 8 * 8                                  # groups of 8 sequences
+    assert quant(L, N=n_q + 1) == EUNSUP
+    # lp_score: 432 vocabulary tiles at V = 151 936; 256-row token tiles.
+    V = 151936
+    tiles_max = lim // 256
+    T_bad = (tiles_max // 432 + 1) * 256
+    assert score(L, T=T_bad, V=V, vt=V, wsb=1 << 62) == EUNSUP
