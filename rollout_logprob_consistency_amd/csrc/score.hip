@@ -527,13 +527,24 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   int (*red_i)[kTileT] = reinterpret_cast<int (*)[kTileT]>(ring + 6 * kTileT * sizeof(float));
 
   // ---- Epilogue: per-token online LSE over this wave's kWaveV vocab rows. ----
-  const int vlane = v0 + wm * kWaveV + 4 * lg;
+  // Without the statistics, the lane-derived indices are formed again from a
+  // lane id that a volatile asm produces (the compiler cannot merge it with
+  // the prologue's), so none of the prologue's per-lane values stays live
+  // across the K loop, where every VGPR is taken (they would be spilled). The
+  // statistics variants keep the prologue's values: with theirs, the
+  // allocation that results passes the MFMA hazard check.
+  int lane_e = lane;
+  if (!kStats)
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+  const int tid_e = kStats ? tid : wave * 64 + lane_e;
+  const int lcol_e = kStats ? lcol : lane_e & 15, lg_e = kStats ? lg : lane_e >> 4;
+  const int vlane = v0 + wm * kWaveV + 4 * lg_e;
   const bool vtail = v0 + kTileV > a.V_true;
   const int64_t wv_lo = v0 + wm * kWaveV;
 
 #pragma unroll
   for (int j = 0; j < kSubT; ++j) {
-    const int tl = wn * kWaveT + j * 16 + lcol;
+    const int tl = wn * kWaveT + j * 16 + lcol_e;
     const int t = t0 + tl;
     auto raw = [&](int i, int r) __attribute__((always_inline)) {
       return i < kSubVA ? acc[i < kSubVA ? i : 0][j][r] : accv[i >= kSubVA ? i - kSubVA : 0][j][r];
@@ -544,10 +555,10 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
     };
     float m, s, q;
     int li;
-    if (vtail) wave_lse<kStats>(vm, a.scale2, lg, m, s, q, li);
-    else wave_lse<kStats>(v, a.scale2, lg, m, s, q, li);
-    if (t < a.T) gather_target(v, a, t, wv_lo, lg);  // targets lie below V_true
-    if (lg == 0) {
+    if (vtail) wave_lse<kStats>(vm, a.scale2, lg_e, m, s, q, li);
+    else wave_lse<kStats>(v, a.scale2, lg_e, m, s, q, li);
+    if (t < a.T) gather_target(v, a, t, wv_lo, lg_e);  // targets lie below V_true
+    if (lg_e == 0) {
       red_m[wm][tl] = m;
       red_s[wm][tl] = s;
       if (kStats) {
@@ -559,7 +570,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_tile_kernel(ScoreArgs a) {
   __syncthreads();
 
   {
-    const int tl = tid;
+    const int tl = tid_e;
     const int t = t0 + tl;
     float M, S;
     merge_halves(red_m[0][tl], red_s[0][tl], red_m[1][tl], red_s[1][tl], M, S);
