@@ -240,11 +240,12 @@ lp_status lp_score_ex(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
  * order, so they are bitwise reproducible run to run and independent of N.
  * Precision of the k3 and TIS terms: for |d_i| < 0.5 a token's k3 and
  * exp(d_i) are evaluated in fp32 (k3 by its Taylor series to d^9 / 9!, no
- * cancellation; exp by the hardware exp2) and added to fp64 sums, which
- * agree with the exactly rounded sums to about 1e-7 relative (the library's
- * tests hold them to 1e-6); for |d_i| >= 0.5 both come from one fp64
- * exponential, k3 = (e^d - 1) - d. The per-token k3 and TIS outputs carry
- * the same precision. sum_abs, sum_signed, sum_d and seq_tis are fp64 from
+ * cancellation; exp(d) as 1 + d + k3 from the same series), the terms of
+ * each group of four consecutive positions are added in fp32 and the group
+ * sums in fp64; the sums agree with the exactly rounded ones to about 1e-7
+ * relative (the library's tests hold them to 1e-6). For |d_i| >= 0.5 both
+ * come from one fp64 exponential, k3 = (e^d - 1) - d, summed in fp64. The
+ * per-token k3 and TIS outputs carry the same per-term precision. sum_abs, sum_signed, sum_d and seq_tis are fp64 from
  * the fp64 differences (1e-9 relative is asserted).
  *
  * Layout:

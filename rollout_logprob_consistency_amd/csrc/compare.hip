@@ -158,7 +158,8 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(7))) void c
   const size_t plane = (size_t)a.N * (size_t)a.L;
   float* pt_row = kPT ? a.per_token + (size_t)(3 * p) * plane + (size_t)n * a.L : nullptr;
   const double clip = a.tis_clip;
-  const double one_tis = fmin(1.0, clip);  // TIS weight of a token with d = 0
+  const float clip_f = (float)clip;  // exact: the cap is given in fp32
+  const float one_tis = fminf(1.0f, clip_f);  // TIS weight of a token with d = 0
   const float nan = __builtin_nanf("");
 
   int seq_n = 0;  // active tokens folded so far (same in every lane)
@@ -170,6 +171,9 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(7))) void c
   // Folds the window holding positions i0 .. i0 + 3 of this lane.
   auto fold = [&](int64_t i0, const float (&vl)[4], const float (&vr)[4], unsigned amask) {
       unsigned dif = 0, bad = 0;  // bit e: mismatch / non-finite
+      // The window's k3 and TIS terms (all >= 0) are summed in fp32 and
+      // added to the fp64 sums once: at most 3 roundings of 2^-24 relative.
+      float wk = 0.f, wt = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float o_abs = 0.f, o_k3 = 0.f, o_tis = 0.f;
@@ -179,8 +183,8 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(7))) void c
             // Identical bits: never a mismatch; a finite token adds delta = 0,
             // k3 = 0 and a TIS weight of min(1, C), so no arithmetic is needed.
             if (__builtin_isfinite(l)) {
-              st += one_tis;
-              o_tis = (float)one_tis;
+              wt += one_tis;
+              o_tis = one_tis;
             } else {
               bad |= 1u << e;
               o_abs = o_k3 = o_tis = nan;
@@ -192,29 +196,36 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(7))) void c
             // (never true for a NaN delta).
             if (kBitwise || !(ad <= a.atol)) dif |= 1u << e;
             if (__builtin_isfinite(dl)) {
-              mx = fmax(ad, mx);  // both finite and >= 0: the exact maximum
+              // Both finite and >= 0: one v_max is the exact maximum (fmax
+              // would first canonicalize both operands).
+              asm("v_max_f64 %0, |%1|, %2" : "=v"(mx) : "v"(dl), "v"(mx));
               sa += ad;
               ss += dl;
               o_abs = (float)ad;
               if (ad < 0.5) {
-                // fp32 is enough: k3 = expm1(d) - d by its Taylor series (no
-                // cancellation; truncation after d^9/9! < 2e-9 relative).
+                // fp32 is enough: k3 = expm1(x) - x = x^2 g(x) with g(x) =
+                // sum_k x^k / (k + 2)! (no cancellation), g by a degree-5
+                // polynomial fitted on [-0.5, 0.5] (Chebyshev nodes, then
+                // least squares reweighted toward equal relative error):
+                // 2.5e-8 relative in exact arithmetic, below fp32 rounding.
                 const float x = (float)-dl;
-                float t = 1.0f / 362880.0f;
-                t = __builtin_fmaf(t, x, 1.0f / 40320.0f);
-                t = __builtin_fmaf(t, x, 1.0f / 5040.0f);
-                t = __builtin_fmaf(t, x, 1.0f / 720.0f);
-                t = __builtin_fmaf(t, x, 1.0f / 120.0f);
-                t = __builtin_fmaf(t, x, 1.0f / 24.0f);
-                t = __builtin_fmaf(t, x, 1.0f / 6.0f);
-                t = __builtin_fmaf(t, x, 0.5f);
+                float t = 1.9875631549451514e-4f;
+                t = __builtin_fmaf(t, x, 1.3982032161686808e-3f);
+                t = __builtin_fmaf(t, x, 8.333452311488566e-3f);
+                t = __builtin_fmaf(t, x, 4.166579533613375e-2f);
+                t = __builtin_fmaf(t, x, 1.666666545420338e-1f);
+                t = __builtin_fmaf(t, x, 5.000000120251578e-1f);
                 const float k3 = t * x * x;
-                const double tis =
-                    fmin((double)__builtin_amdgcn_exp2f(x * 1.44269504088896341f), clip);
-                sk += (double)k3;
-                st += tis;
+                // e^x = 1 + x + (expm1(x) - x): from the same series, with no
+                // exponential instruction (rounding about 1e-7 relative).
+                // min(e^x, C): both finite, so one v_min (fminf would first
+                // canonicalize both operands for signalling NaNs).
+                float tis;
+                asm("v_min_f32 %0, %1, %2" : "=v"(tis) : "v"(1.0f + (x + k3)), "v"(clip_f));
+                wk += k3;
+                wt += tis;
                 o_k3 = k3;
-                o_tis = (float)tis;
+                o_tis = tis;
               } else {
                 slow = true;  // k3 and TIS in the second pass
               }
@@ -230,6 +241,8 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(7))) void c
           pt_row[2 * plane + i0 + e] = o_tis;
         }
       }
+      sk += (double)wk;
+      st += (double)wt;
       mism += __popc(dif);
       nonf += __popc(bad);
 

@@ -123,6 +123,28 @@ def test_per_token_values(record):
     np.testing.assert_allclose(got[:, 1:][fin[:, 1:]], ref[:, 1:][fin[:, 1:]], rtol=1e-6, atol=1e-30)
 
 
+def test_per_token_k3_tis_across_the_small_range():
+    # |d| < 0.5 takes the fp32 path (k3 from a fitted polynomial, e^d from the
+    # same series): d swept densely over (-0.5, 0.5) on both sides of each
+    # pair, also at the edges and very near 0, against the fp64 oracle; the
+    # sums to the documented 1e-6 relative. TIS cap below and above e^d.
+    rng = np.random.default_rng(77)
+    N, L = 16, 4096
+    B = -rng.uniform(0.5, 6.0, (N, L)).astype(np.float32)
+    d = np.linspace(-0.4999, 0.4999, N * L).reshape(N, L)
+    d[0, :64] = np.float32(2.0) ** -np.arange(1, 65)            # tiny, both signs
+    d[1, :64] = -d[0, :64]
+    A = (B.astype(np.float64) + d).astype(np.float32)
+    C = (B.astype(np.float64) - 0.5 * d).astype(np.float32)
+    M = np.ones((N, L), np.uint8)
+    for clip in (2.0, 1.25, 0.875):  # fp32 caps (the C ABI takes tis_clip as float)
+        (stats, pt), _ = run((A, B, C, M), per_token=True, tis_clip=clip)
+        ref = oracle.per_token(A, B, C, M, tis_clip=clip)
+        got = pt.cpu().numpy()
+        assert np.array_equal(got[:, 0], ref[:, 0])
+        np.testing.assert_allclose(got[:, 1:], ref[:, 1:], rtol=1e-6, atol=1e-30)
+
+
 def test_special_values_and_atol():
     f = np.float32
     A = np.array([[0.0, -1.0, np.nan, np.inf, -1000.0, -2.0, -3.0, -4.0]], f)
