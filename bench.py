@@ -72,6 +72,8 @@ def main() -> int:
     ap.add_argument("--sweep-n", type=str, default="512,4096,32768",
                     help="sequence counts of the comparison bandwidth probe (L = 2304); the "
                          "tail statistics and the correction are timed at N = 4096 when listed")
+    ap.add_argument("--compare-n", type=int, default=4096,
+                    help="sequences (L = 2304) of the compare / tails / quantiles profiler modes")
     ap.add_argument("--small-batches", type=str, default="1,7,64",
                     help="row counts at which lp_score is timed as a stream over W")
     ap.add_argument("--mode", choices=("bench", "score", "stats", "small", "compare", "tails",
@@ -80,7 +82,7 @@ def main() -> int:
                     help="score: only `steps` lp_score calls on the benchmark batch; stats: "
                          "the same with lp_score_stats (entropy and argmax too); small: "
                          "`steps` lp_score calls on its first row; compare: `steps` lp_compare "
-                         "calls at N=4096, L=2304; tails / quantiles: `steps` lp_compare_tails / "
+                         "calls at N=--compare-n, L=2304; tails / quantiles: `steps` lp_compare_tails / "
                          "lp_compare_quantiles calls on the same arrays (these for profilers); "
                          "copy: one plain "
                          "1 GiB device copy (counter calibration)")
@@ -169,7 +171,7 @@ def main() -> int:
         log(f"bench: {args.steps} one-row lp_score calls done")
         return 0
     if args.mode in ("compare", "tails", "quantiles"):
-        sc = synth.compare_sweep_case(N=4096)
+        sc = synth.compare_sweep_case(N=args.compare_n)
         tA, tB, tC, tM = (torch.from_numpy(a).to(dev) for a in (sc.A, sc.B, sc.C, sc.mask))
         if args.mode == "compare":
             sbuf = torch.empty(3 * sc.N * lp.SEQ_STATS_DTYPE.itemsize, dtype=torch.uint8,
@@ -184,7 +186,7 @@ def main() -> int:
             for _ in range(args.steps):
                 lp.compare_quantiles(tA, tB, tC, tM, out=qout, sync=False)
         torch.cuda.synchronize()
-        log(f"bench: {args.steps} {args.mode} calls (N=4096, L=2304) done")
+        log(f"bench: {args.steps} {args.mode} calls (N={sc.N}, L={sc.L}) done")
         return 0
 
     def step(ev=None):
@@ -395,8 +397,9 @@ def main() -> int:
                       "bytes_per_token": 13})
         log(f"bench: lp_compare N={sc.N} L={sc.L}: {med:.1f} us = {nbytes / med / 1e3:.1f} GB/s")
         if sc.N == 4096:
-            # Batch tail statistics on the same arrays: 8 selection passes and
-            # the position profile each read the 13 bytes of every position.
+            # Batch tail statistics on the same arrays: selection passes 0
+            # and 1 and the position profile each read the 13 bytes of every
+            # position; the later passes read only the candidate lists.
             tw = torch.empty(lp._lib.lib().lp_compare_tails_workspace_bytes(sc.N, sc.L),
                              dtype=torch.uint8, device=dev)
             tout = torch.empty(3 * lp.TAIL_STATS_DTYPE.itemsize, dtype=torch.uint8, device=dev)
@@ -407,13 +410,13 @@ def main() -> int:
                      tw.numel(), torch.cuda.current_stream().cuda_stream)
             c_tails = lp._lib.lib().lp_compare_tails
             tmed, tlo, thi = median_us(lambda: c_tails(*targs), calls=5, reps=5)
-            tbytes = 9 * 13.0 * sc.N * sc.L
+            tbytes = 3 * 13.0 * sc.N * sc.L
             tails_rec = {"N": sc.N, "L": sc.L, "us": round(tmed, 2), "min_us": round(tlo, 2),
-                         "max_us": round(thi, 2), "passes": 9,
+                         "max_us": round(thi, 2), "passes": 3,
                          "GBps": round(tbytes / tmed / 1e3, 1),
                          "frac_hbm": round(tbytes / tmed / 1e3 / PEAK_HBM_GBPS, 4)}
             log(f"bench: lp_compare_tails N={sc.N} L={sc.L}: {tmed:.1f} us "
-                f"({tbytes / tmed / 1e3:.1f} GB/s over 9 passes)")
+                f"({tbytes / tmed / 1e3:.1f} GB/s over 3 reads of the batch)")
             # The same call with the 16 worst tokens of each pair
             # (lp_compare_tails_ex): a fourth selection target per pair, a
             # counting pass, a writing pass and a 16-row sort.

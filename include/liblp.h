@@ -84,7 +84,8 @@ const char* lp_status_string(lp_status status);
  * [1, V_rows], ldh < H, a temperature that is not finite and > 0, a NULL
  * required pointer, or a workspace that is too small or misaligned.
  * LP_EUNSUPPORTED for H % 64 != 0, ldh % 8 != 0 or misaligned hidden/w; for
- * sizes whose index arithmetic would overflow 32-bit tile counters; and for
+ * sizes whose dispatches would exceed 2^32 - 1 work-items (more than
+ * 16 777 215 tiles of 352 x 256, or T above 268 435 455); and for
  * strides the kernels' 32-bit buffer addressing cannot span: 255 * ldh * 2 +
  * 2 * H or 352 * 2 * H above 0x7FFFFFF0 bytes (at H = 64 the largest
  * accepted ldh is 4 210 744; the largest accepted H is 3 050 368).
@@ -258,8 +259,10 @@ lp_status lp_score_ex(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
  *                             NaN for active non-finite ones.
  *
  * Errors: LP_EINVAL for N < 0, L < 0, ld < L, tis_clip not finite and > 0,
- * atol NaN, or a NULL required pointer. N == 0 or L == 0 is a no-op (with
- * L == 0 and N > 0 the stats are still written, all empty).
+ * atol NaN, or a NULL required pointer; LP_EUNSUPPORTED for L above
+ * INT32_MAX or N above 22 369 621 (one 192-thread workgroup per sequence in
+ * one dispatch of at most 2^32 - 1 work-items). N == 0 or L == 0 is a no-op
+ * (with L == 0 and N > 0 the stats are still written, all empty).
  * ------------------------------------------------------------------------ */
 typedef struct {
   int32_t valid;
@@ -316,7 +319,8 @@ lp_status lp_compare(const float* gen_A, const float* replay_B,
  *
  * Errors: LP_EINVAL for N < 0, L < 0, ld < L, a NULL or misaligned out, or
  * NULL inputs with N, L > 0; LP_EUNSUPPORTED for L above INT32_MAX or N
- * above 715 827 880 (three workgroups per sequence in one grid row).
+ * above 5 592 400 (three 256-thread workgroups per sequence, in groups of 8
+ * sequences, in one dispatch of at most 2^32 - 1 work-items).
  * N == 0 does nothing; L == 0 writes zeros.
  * ------------------------------------------------------------------------ */
 lp_status lp_compare_quantiles(const float* gen_A, const float* replay_B,
@@ -359,8 +363,11 @@ lp_status lp_compare_quantiles(const float* gen_A, const float* replay_B,
  * memory; workspace: lp_compare_tails_workspace_bytes(N, L) bytes, 256-byte
  * aligned, contents ignored. Errors: LP_EINVAL for N < 0, L < 0, ld < L, a
  * NULL out or workspace, only one of pos_abs_sum / pos_count given, NULL
- * inputs with N, L > 0, or a small or misaligned workspace. N == 0 or
- * L == 0 writes the empty statistics (and zero profiles).
+ * inputs with N, L > 0, or a small or misaligned workspace; LP_EUNSUPPORTED
+ * for L above INT32_MAX, N above 16 777 215 (one 256-thread workgroup per
+ * sequence in one dispatch of at most 2^32 - 1 work-items) or N * L above
+ * 2^32 - 1 (32-bit histogram counters). N == 0 or L == 0 writes the empty
+ * statistics (and zero profiles).
  * ------------------------------------------------------------------------ */
 typedef struct {
   int64_t count;
@@ -536,7 +543,9 @@ lp_status lp_merge_shards(const void* partials, const int64_t* target_ids,
  *
  * Errors: LP_EINVAL for N < 0, L < 0, ld < L, C <= 0 or NaN, a NaN or
  * inverted interval or accepted range, an unknown reject_kind, a NULL out,
- * or NULL inputs with N, L > 0. N == 0 does nothing.
+ * or NULL inputs with N, L > 0; LP_EUNSUPPORTED for L above INT32_MAX or N
+ * above 16 777 215 (one 256-thread workgroup per sequence in one dispatch).
+ * N == 0 does nothing.
  * ------------------------------------------------------------------------ */
 #define LP_REJECT_NONE 0
 #define LP_REJECT_K1 1
