@@ -472,7 +472,7 @@ constexpr int kMaxTP = 7;
 constexpr int kWorstT = 6;  // index of the k-th-largest target within a pair
 constexpr int kMaxTargets = 3 * kMaxTP;
 constexpr int kTailThreads = kRowThreads;
-constexpr int kTailChunks = 64;     // sequence chunks of the position profile
+constexpr int kTailChunks = 128;    // sequence chunks of the position profile
 // Histogram copies: the workgroup of sequence n adds into copy n mod 8 (with
 // workgroups dealt to the 8 XCDs in turn, each copy is one XCD's), so no
 // counter takes atomics from more than N / 8 workgroups.
@@ -619,55 +619,89 @@ size_t tail_bytes(int64_t N, int64_t L, int32_t k) { return tail_walk(nullptr, N
 __device__ __forceinline__ int pair_left(int p) { return p == 1 ? 1 : 0; }
 __device__ __forceinline__ int pair_right(int p) { return p == 0 ? 1 : 2; }
 
-// Position profile, stage 1: thread i of chunk c sums column i over the
-// chunk's sequences (fixed chunks, sequences in order); the final kernel
-// folds the chunks in order.
-__device__ void tails_pos_chunk(const TailArgs& a, const TailWs& w, int64_t i, int c) {
-  if (i >= a.L) return;
+// Position profile, stage 1: each thread sums its columns over chunk c's
+// sequences (fixed chunks, sequences in ascending order); the final kernel
+// folds the chunks in order. kVec: four consecutive columns per thread
+// (16-byte loads, each load instruction one contiguous KiB; the last partial
+// group by elements), else one column per thread. A column's sum takes the
+// same operations in the same order either way.
+template <bool kVec>
+__device__ void tails_pos_chunk(const TailArgs& a, const TailWs& w, int64_t g, int c) {
+  constexpr int kW = kVec ? 4 : 1;
+  const int64_t i0 = g * kW;
+  if (i0 >= a.L) return;
   const int64_t per = (a.N + w.nch - 1) / w.nch;
   const int64_t lo = c * per, hi = min(a.N, lo + per);
-  double s[3] = {0.0, 0.0, 0.0};
-  int32_t k[3] = {0, 0, 0};
-  // Eight sequences' loads are issued together (all of them, masked or not);
-  // the sums still take the sequences in ascending order.
-  constexpr int kB = 8;
+  double s[kW][3] = {};
+  int32_t k[kW][3] = {};
+  const bool whole = kVec && i0 + 4 <= a.L;
+  // Four sequences' loads are issued together (all of them, masked or not).
+  constexpr int kB = 4;
   for (int64_t n0 = lo; n0 < hi; n0 += kB) {
-    float v[kB][3];
-    bool act[kB];
+    float v[kB][kW][3];
+    bool act[kB][kW];
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
       const bool in = n0 + b < hi;
-      const int64_t o = (in ? n0 + b : lo) * a.ld + i;
-      act[b] = in && a.mask[o] != 0;
-      v[b][0] = a.A[o];
-      v[b][1] = a.B[o];
-      v[b][2] = a.C[o];
-    }
+      const int64_t o = (in ? n0 + b : lo) * a.ld + i0;
+      if (kVec && whole) {
+        const uint32_t m = *reinterpret_cast<const uint32_t*>(a.mask + o);
+        const float4 fa = *reinterpret_cast<const float4*>(a.A + o);
+        const float4 fb = *reinterpret_cast<const float4*>(a.B + o);
+        const float4 fc = *reinterpret_cast<const float4*>(a.C + o);
+        const float va[4] = {fa.x, fa.y, fa.z, fa.w}, vb[4] = {fb.x, fb.y, fb.z, fb.w},
+                    vc[4] = {fc.x, fc.y, fc.z, fc.w};
 #pragma unroll
-    for (int b = 0; b < kB; ++b) {
-      if (!act[b]) continue;
+        for (int e = 0; e < kW; ++e) {
+          act[b][e] = in && ((m >> (8 * e)) & 255u) != 0;
+          v[b][e][0] = va[e];
+          v[b][e][1] = vb[e];
+          v[b][e][2] = vc[e];
+        }
+      } else {
 #pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        const float l = v[b][pair_left(p)], r = v[b][pair_right(p)];
-        if (!__builtin_isfinite(l) || !__builtin_isfinite(r)) continue;
-        s[p] += fabs((double)l - (double)r);
-        k[p] += 1;
+        for (int e = 0; e < kW; ++e) {
+          const bool col = i0 + e < a.L;
+          act[b][e] = in && col && a.mask[o + e] != 0;
+          v[b][e][0] = act[b][e] ? a.A[o + e] : 0.f;
+          v[b][e][1] = act[b][e] ? a.B[o + e] : 0.f;
+          v[b][e][2] = act[b][e] ? a.C[o + e] : 0.f;
+        }
       }
     }
+#pragma unroll
+    for (int b = 0; b < kB; ++b)
+#pragma unroll
+      for (int e = 0; e < kW; ++e) {
+        if (!act[b][e]) continue;
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          const float l = v[b][e][pair_left(p)], r = v[b][e][pair_right(p)];
+          if (!__builtin_isfinite(l) || !__builtin_isfinite(r)) continue;
+          s[e][p] += fabs((double)l - (double)r);
+          k[e][p] += 1;
+        }
+      }
   }
 #pragma unroll
-  for (int p = 0; p < 3; ++p) {
-    w.pos_part[((size_t)c * 3 + p) * a.L + i] = s[p];
-    w.pos_cpart[((size_t)c * 3 + p) * a.L + i] = k[p];
+  for (int e = 0; e < kW; ++e) {
+    if (i0 + e >= a.L) continue;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      w.pos_part[((size_t)c * 3 + p) * a.L + i0 + e] = s[e][p];
+      w.pos_cpart[((size_t)c * 3 + p) * a.L + i0 + e] = k[e][p];
+    }
   }
 }
 
 // Clears the histograms (every copy) and the gather counts, and resets the
 // selection state; with the position profile asked for (pos true, grid
-// ceil(L / 256) x chunks), workgroup (x, c) also forms stage 1 of the
-// profile for columns [256 x, 256 x + 256) of chunk c.
+// ceil(L / (256 W)) x chunks, W = 4 columns a thread on the vector path, else
+// 1), workgroup (x, c) also forms stage 1 of the profile for columns
+// [256 W x, 256 W (x + 1)) of chunk c.
 constexpr int kInitBlocks = 64;
 
+template <bool kVec>
 __global__ __launch_bounds__(kTailThreads) void tails_init_kernel(TailArgs a, TailWs w, bool pos) {
   uint4* z = reinterpret_cast<uint4*>(w.hist0);
   constexpr int64_t kVecs = (int64_t)(kHist0Words + kHistWords) / 4;
@@ -675,7 +709,7 @@ __global__ __launch_bounds__(kTailThreads) void tails_init_kernel(TailArgs a, Ta
   for (int64_t i = wg * kTailThreads + threadIdx.x; i < kVecs;
        i += (int64_t)gridDim.x * gridDim.y * kTailThreads)
     z[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (pos) tails_pos_chunk(a, w, (int64_t)blockIdx.x * kTailThreads + threadIdx.x, (int)blockIdx.y);
+  if (pos) tails_pos_chunk<kVec>(a, w, (int64_t)blockIdx.x * kTailThreads + threadIdx.x, (int)blockIdx.y);
   if (wg != 0) return;
   const int t = threadIdx.x;
   if (t < kMaxTargets) {
@@ -1429,22 +1463,40 @@ __global__ __launch_bounds__(kFinThreads) void tails_finish_kernel(TailWs w) {
 // contiguous sequences [j per, (j + 1) per) in order (per depends on N
 // only), then a fixed XOR butterfly within each wave and the waves in order.
 // The maximum keeps the first sequence (and, within it, the first column)
-// that reaches it. Workgroups 3, 4, ... fold the position profile's chunks
-// in order.
+// that reaches it. Workgroups 3, 4, ... fold the position profile's chunks:
+// four fixed groups of consecutive chunks, each in order, then the groups in
+// order.
 template <int kTP>
 __global__ __launch_bounds__(kFinThreads) void tails_final_kernel(TailArgs a, TailWs w) {
   if (blockIdx.x >= 3) {
-    for (int64_t idx = (int64_t)(blockIdx.x - 3) * kFinThreads + threadIdx.x; idx < 3 * a.L;
-         idx += (int64_t)(gridDim.x - 3) * kFinThreads) {  // p * L + i
+    // Thread (q, o) of a workgroup folds the chunks [q G, (q + 1) G) of output
+    // o of its 256 (G = ceil(nch / 4)); thread (0, o) then adds the four
+    // partials in order.
+    __shared__ double fs[4][kFinThreads / 4];
+    __shared__ int32_t fk[4][kFinThreads / 4];
+    const int q = threadIdx.x / (kFinThreads / 4), o = threadIdx.x % (kFinThreads / 4);
+    const int G = (w.nch + 3) / 4;
+    const int c0 = q * G, c1 = min(w.nch, c0 + G);
+    for (int64_t base = (int64_t)(blockIdx.x - 3) * (kFinThreads / 4); base < 3 * a.L;
+         base += (int64_t)(gridDim.x - 3) * (kFinThreads / 4)) {  // uniform
+      const int64_t idx = base + o;  // p * L + i
       double s = 0.0;
       int32_t k = 0;
+      if (idx < 3 * a.L) {
 #pragma unroll 8
-      for (int c = 0; c < w.nch; ++c) {
-        s += w.pos_part[(size_t)c * 3 * a.L + idx];
-        k += w.pos_cpart[(size_t)c * 3 * a.L + idx];
+        for (int c = c0; c < c1; ++c) {
+          s += w.pos_part[(size_t)c * 3 * a.L + idx];
+          k += w.pos_cpart[(size_t)c * 3 * a.L + idx];
+        }
       }
-      a.pos_sum[idx] = s;
-      a.pos_count[idx] = k;
+      fs[q][o] = s;
+      fk[q][o] = k;
+      __syncthreads();
+      if (q == 0 && idx < 3 * a.L) {
+        a.pos_sum[idx] = ((fs[0][o] + fs[1][o]) + fs[2][o]) + fs[3][o];
+        a.pos_count[idx] = fk[0][o] + fk[1][o] + fk[2][o] + fk[3][o];
+      }
+      __syncthreads();
     }
     return;
   }
@@ -1797,7 +1849,7 @@ static void launch_select(const TailArgs& a, const TailWs& w, hipStream_t stream
     hipLaunchKernelGGL(tails_finish_kernel<kTP>, dim3(3 * kTP), dim3(kFinThreads), 0, stream, w);
   }
   // Also the position profile's fold.
-  const int64_t fold_all = a.pos_sum && a.L > 0 ? (3 * a.L + kFinThreads - 1) / kFinThreads : 0;
+  const int64_t fold_all = a.pos_sum && a.L > 0 ? (3 * a.L + kFinThreads / 4 - 1) / (kFinThreads / 4) : 0;
   const unsigned fold = (unsigned)(fold_all < 65536 ? fold_all : 65536);  // then a grid-stride loop
   hipLaunchKernelGGL(tails_final_kernel<kTP>, dim3(3 + fold), dim3(kFinThreads), 0, stream, a, w);
 }
@@ -1807,9 +1859,10 @@ hipError_t launch_tails(const TailArgs& a, hipStream_t stream) {
   // With the position profile asked for, its stage 1 (also with N == 0:
   // zero partials for the fold) runs in the init kernel.
   const bool pos = a.pos_sum && a.L > 0;
-  const dim3 init_grid = pos ? dim3((unsigned)((a.L + kTailThreads - 1) / kTailThreads), (unsigned)w.nch)
-                             : dim3(kInitBlocks);
-  hipLaunchKernelGGL(tails_init_kernel, init_grid, dim3(kTailThreads), 0, stream, a, w, pos);
+  const int64_t cols = a.vec ? 4 * kTailThreads : kTailThreads;  // columns per workgroup
+  const dim3 init_grid = pos ? dim3((unsigned)((a.L + cols - 1) / cols), (unsigned)w.nch) : dim3(kInitBlocks);
+  if (a.vec) hipLaunchKernelGGL(tails_init_kernel<true>, init_grid, dim3(kTailThreads), 0, stream, a, w, pos);
+  else hipLaunchKernelGGL(tails_init_kernel<false>, init_grid, dim3(kTailThreads), 0, stream, a, w, pos);
   if (a.worst_k > 0) {
     launch_select<kMaxTP>(a, w, stream);
     if (a.N > 0 && a.L > 0) {

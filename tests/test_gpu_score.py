@@ -123,10 +123,14 @@ def test_empty_batch_is_a_noop():
 # --------------------------------------------------------------------------
 
 def sample_rows(T, n, seed):
+    """Tile edges, one random row of every 256-row token tile (so a fault in
+    any tile shows), and random rows up to n."""
     rng = np.random.default_rng(seed)
     fixed = [0, 1, 255, 256, T - 257, T - 256, T - 1]
-    rest = rng.choice(T, size=n - len(fixed), replace=False)
-    return np.unique(np.concatenate([fixed, rest]))
+    per_tile = np.arange(0, T, 256) + rng.integers(0, 256, size=-(-T // 256))
+    per_tile = per_tile[per_tile < T]
+    rest = rng.choice(T, size=max(0, n - len(fixed) - len(per_tile)), replace=False)
+    return np.unique(np.concatenate([fixed, per_tile, rest]))
 
 
 @pytest.fixture(scope="module")
@@ -158,7 +162,7 @@ def test_qwen8b_shaped_parity_and_repeatability(qwen8b):
     again = gpu_score(xd, wd, c.ids)
     assert np.array_equal(got.view(np.int32), again.view(np.int32))   # run to run
     assert np.isfinite(got).all() and (got <= 0).all()
-    rows = sample_rows(c.T, 64, seed=8)
+    rows = sample_rows(c.T, 96, seed=8)          # every one of the 32 token tiles
     ref, _ = oracle_f64(c, rows)
     assert np.max(np.abs(got[rows] - ref)) <= SCORE_ATOL
 
