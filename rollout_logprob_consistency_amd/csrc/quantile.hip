@@ -87,7 +87,8 @@ __global__ __launch_bounds__(kQThreads) void seq_quantile_kernel(QuantArgs a) {
   __shared__ uint64_t cand[kCand];
   __shared__ uint32_t s_part[kQWaves];
   __shared__ uint64_t s_pre[kQT], s_val[kQT];
-  __shared__ int64_t s_rank[kQT];
+  __shared__ int64_t s_rank[kQT], s_r[kQT];
+  __shared__ uint32_t s_bk[kQT];
   __shared__ uint32_t s_ncand, s_gather;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Workgroups are dealt to the 8 XCDs in turn by their index, and each XCD
@@ -161,12 +162,17 @@ __global__ __launch_bounds__(kQThreads) void seq_quantile_kernel(QuantArgs a) {
     return;
   }
   const int64_t excl = (int64_t)before + incl - mine;
+  // The six ranks, once per workgroup.
+  if (tid < kQT) {
+    int64_t lo, hi;
+    quantile_ranks(count, quantile_prob(tid >> 1), &lo, &hi);
+    s_r[tid] = (tid & 1) ? hi : lo;
+  }
+  __syncthreads();
   // The thread whose bins hold rank r finds the bucket and the rank within.
 #pragma unroll
   for (int t = 0; t < kQT; ++t) {
-    int64_t lo, hi;
-    quantile_ranks(count, quantile_prob(t >> 1), &lo, &hi);
-    const int64_t r = (t & 1) ? hi : lo;
+    const int64_t r = s_r[t];
     if (excl < r && r <= excl + mine) {
       int64_t below = excl;
       int b = 0;
@@ -175,21 +181,20 @@ __global__ __launch_bounds__(kQThreads) void seq_quantile_kernel(QuantArgs a) {
       // Bucket 0 holds only the key 0: that rank is settled.
       s_pre[t] = bk == 0 ? 0ull : (uint64_t)(bk - 1u + kKeyTop16Lo);
       s_rank[t] = bk == 0 ? 0 : r - below;
+      s_bk[t] = bk;
       s_val[t] = 0ull;
-      if (bk != 0) {
-        // Count the bucket's keys once per distinct bucket (the first rank
-        // in it adds them).
-        bool first = true;
-        for (int u = 0; u < t; ++u) {
-          int64_t ulo, uhi;
-          quantile_ranks(count, quantile_prob(u >> 1), &ulo, &uhi);
-          const int64_t ur = (u & 1) ? uhi : ulo;
-          first = first && !(excl < ur && ur <= excl + mine && ur > below &&
-                             ur <= below + (int64_t)hist[bk]);
-        }
-        if (first) atomicAdd(&s_ncand, hist[bk]);
-      }
     }
+  }
+  __syncthreads();
+  // The chosen buckets' keys, each distinct bucket counted once.
+  if (tid == 0) {
+    uint32_t nc = 0u;
+    for (int t = 0; t < kQT; ++t) {
+      bool first = s_bk[t] != 0u;
+      for (int u = 0; u < t; ++u) first = first && s_bk[u] != s_bk[t];
+      if (first) nc += hist[s_bk[t]];
+    }
+    s_ncand = nc;
   }
   __syncthreads();
   const bool gather = s_ncand <= (uint32_t)kCand;

@@ -162,6 +162,47 @@ def test_selection_paths(case):
     run_worst(A, B, C, M, 64)
 
 
+def random_case(seed):
+    """A seeded batch whose shape, mask density and |delta| distribution are
+    drawn at random: continuous noise of one of several scales, quantized
+    differences (many ties), a constant offset (one bucket), identical
+    scores, or a mix, with a few non-finite scores."""
+    rng = np.random.default_rng(1000 + seed)
+    N = int(rng.integers(1, 48))
+    L = int(rng.integers(1, 2600))
+    B = np.log(1.0 - rng.random((N, L))).astype(np.float32)
+    def delta(kind):
+        if kind == "noise":
+            return rng.normal(0.0, 10.0 ** rng.uniform(-6, 0), (N, L))
+        if kind == "ties":
+            return np.round(rng.normal(0.0, 3.0, (N, L))) * 2.0 ** -int(rng.integers(4, 12))
+        if kind == "offset":
+            return np.full((N, L), rng.uniform(0.01, 1.0))
+        if kind == "same":
+            return np.zeros((N, L))
+        return np.where(rng.random((N, L)) < 0.5, rng.normal(0.0, 1e-3, (N, L)),
+                        np.round(rng.normal(0.0, 2.0, (N, L))) * 2.0 ** -8)
+    kinds = ("noise", "ties", "offset", "same", "mix")
+    A = (B + delta(kinds[rng.integers(5)])).astype(np.float32)
+    C = (B + delta(kinds[rng.integers(5)])).astype(np.float32)
+    M = (rng.random((N, L)) < rng.uniform(0.05, 1.0)).astype(np.uint8)
+    for arr in (A, B, C):
+        if rng.random() < 0.3:
+            arr[rng.integers(N), rng.integers(L)] = rng.choice([np.nan, np.inf, -np.inf])
+    return A, B, C, M, int(rng.choice([0, 1, 7, 300]))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_batches(seed):
+    # Every selection path on random shapes: sources shared or split, gathers
+    # after pass 0, 1 or later, lists, the batch read when a bucket does not
+    # fit, ties down to the last byte; exact against the oracle.
+    A, B, C, M, k = random_case(seed)
+    run(A, B, C, M)
+    if k:
+        run_worst(A, B, C, M, k)
+
+
 @pytest.mark.parametrize("N,L", [(0, 5), (3, 0), (1, 1)])
 def test_degenerate_sizes(N, L):
     A = np.zeros((N, L), np.float32)
