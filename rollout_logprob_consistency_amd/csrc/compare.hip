@@ -1036,12 +1036,15 @@ __device__ __forceinline__ void gather_add(const TailWs& w, int t, uint64_t key,
 // 1 024 positions: every wave numbers its hits per source from its ballots
 // (no atomics), the waves' counts are laid end to end, one atomic per source
 // reserves the chunk's span of the region part that this workgroup's copy
-// counted, and the keys, still in registers, are written.
-template <bool kVec, int kTP>
+// counted, and the keys, still in registers, are written. The byte
+// histograms are 16-bit counters, two to a word, for rows of at most 65 535
+// positions (kWide false; a bin counts at most L keys), else 32-bit.
+template <bool kVec, bool kWide, int kTP>
 __global__ __launch_bounds__(kTailThreads) void tails_p1_kernel(TailArgs a, TailWs w) {
   constexpr int kNT = 3 * kTP;
   constexpr int kW = kTailThreads / 64;
-  __shared__ uint32_t h[kNT * 256];
+  constexpr int kRow = kWide ? 256 : 128;  // words per source histogram
+  __shared__ uint32_t h[kNT * kRow];
   __shared__ uint32_t s_wcnt[kW][kNT];
   __shared__ int64_t s_wbase[kW][kNT], s_lim[kNT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1053,7 +1056,7 @@ __global__ __launch_bounds__(kTailThreads) void tails_p1_kernel(TailArgs a, Tail
   for (int t = 0; t < kNT; ++t) pre[t] = w.plan->pre[t];
 #pragma unroll
   for (int t = 0; t < kNT; ++t)
-    if ((hist >> t) & 1u) h[t * 256 + tid] = 0u;
+    if (((hist >> t) & 1u) && tid < kRow) h[t * kRow + tid] = 0u;
   if (tid < kNT) {
     const TailList R = w.list[tid];
     s_lim[tid] = R.off + R.len;
@@ -1100,7 +1103,7 @@ __global__ __launch_bounds__(kTailThreads) void tails_p1_kernel(TailArgs a, Tail
         for (int k = 0; k < 4; ++k) {
           const bool hit = (hm >> k) & 1u;
           if ((hist >> t) & 1u)
-            wave_hist_add(h + t * 256, (uint32_t)(key[k][p] >> 40) & 255u, hit, lane);
+            hist16_add<kWide>(h + t * kRow, (uint32_t)(key[k][p] >> 40) & 255u, hit, lane);
           if ((gath >> t) & 1u) gather_add(w, t, key[k][p], hit, lane);
           if ((own >> t) & 1u) {
             const uint64_t hb = __ballot(hit);
@@ -1149,8 +1152,14 @@ __global__ __launch_bounds__(kTailThreads) void tails_p1_kernel(TailArgs a, Tail
 #pragma unroll
   for (int t = 0; t < kNT; ++t) {
     if (!((hist >> t) & 1u)) continue;  // uniform
-    const uint32_t v = h[t * 256 + tid];
-    if (v) atomicAdd(&hc[t * 256 + tid], v);
+    if (kWide) {
+      const uint32_t v = h[t * kRow + tid];
+      if (v) atomicAdd(&hc[t * 256 + tid], v);
+    } else {
+      // Bin tid is half (tid & 1) of word tid >> 1.
+      const uint32_t v = (h[t * kRow + (tid >> 1)] >> ((tid & 1) << 4)) & 0xFFFFu;
+      if (v) atomicAdd(&hc[t * 256 + tid], v);
+    }
   }
 }
 
@@ -1836,8 +1845,14 @@ static void launch_select(const TailArgs& a, const TailWs& w, hipStream_t stream
   // With no token the histograms are empty: count 0 and no rank to select.
   hipLaunchKernelGGL(tails_p0_select_kernel<kTP>, dim3(3), dim3(kSelThreads), 0, stream, w);
   if (a.N > 0 && a.L > 0) {
-    if (a.vec) hipLaunchKernelGGL((tails_p1_kernel<true, kTP>), rows, blk, 0, stream, a, w);
-    else hipLaunchKernelGGL((tails_p1_kernel<false, kTP>), rows, blk, 0, stream, a, w);
+    const bool wide = a.L > 65535;
+    if (a.vec) {
+      if (wide) hipLaunchKernelGGL((tails_p1_kernel<true, true, kTP>), rows, blk, 0, stream, a, w);
+      else hipLaunchKernelGGL((tails_p1_kernel<true, false, kTP>), rows, blk, 0, stream, a, w);
+    } else {
+      if (wide) hipLaunchKernelGGL((tails_p1_kernel<false, true, kTP>), rows, blk, 0, stream, a, w);
+      else hipLaunchKernelGGL((tails_p1_kernel<false, false, kTP>), rows, blk, 0, stream, a, w);
+    }
     hipLaunchKernelGGL(tails_select_kernel<kTP>, dim3(1), dim3(kSelThreads), 0, stream, w, 1);
     for (int pass = 2; pass <= kLastPass; ++pass) {
       if (a.vec)
