@@ -1721,6 +1721,15 @@ __global__ __launch_bounds__(kTailThreads) void tails_worst_write_kernel(TailArg
     run_g[p] = w.woff[p * N + n];
     run_e[p] = w.woff[(3 + p) * N + n];
   }
+  // A sequence with no token above tau, and none equal to it that k still
+  // needs (its first one would rank at or past need_eq), writes nothing and
+  // skips its row (every thread reads the same counts: uniform).
+  bool any = false;
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+    any = any || (on[p] && (w.wcnt[p * N + n] > 0u ||
+                            (w.wcnt[(3 + p) * N + n] > 0u && run_e[p] < need_eq[p])));
+  if (!any) return;
   const float* const rows[3] = {a.A + n * a.ld, a.B + n * a.ld, a.C + n * a.ld};
   const uint8_t* M = a.mask + n * a.ld;
   constexpr int64_t kStep = 4 * kTailThreads;
