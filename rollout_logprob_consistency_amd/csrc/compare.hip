@@ -1609,12 +1609,27 @@ __global__ __launch_bounds__(kTailThreads) void tails_worst_count_kernel(TailArg
   __syncthreads();
   uint64_t tau[3];
   bool on[3];
+  uint32_t known[3];  // the equal count when the row need not be read
+  const int64_t n = blockIdx.x;
 #pragma unroll
   for (int p = 0; p < 3; ++p) {
     tau[p] = worst_tau(w, p);
-    on[p] = w.count[p] > 0;
+    // Pass 0 kept the sequence's largest key and its token count: with the
+    // largest key below tau no token counts; with tau and the largest key
+    // both 0, every counted token equals tau and none is above it.
+    const TailPart q = w.part[n * 3 + p];
+    const bool any = w.count[p] > 0 && q.max_pos >= 0 && q.max_key >= tau[p];
+    const bool zeros = any && tau[p] == 0ull && q.max_key == 0ull;
+    on[p] = any && !zeros;
+    known[p] = zeros ? (uint32_t)q.count : 0u;
   }
-  const int64_t n = blockIdx.x;
+  if (!(on[0] || on[1] || on[2])) {  // uniform: nothing to read
+    if (tid < 3) {
+      w.wcnt[tid * a.N + n] = 0u;
+      w.wcnt[(3 + tid) * a.N + n] = known[tid];
+    }
+    return;
+  }
   const float* const rows[3] = {a.A + n * a.ld, a.B + n * a.ld, a.C + n * a.ld};
   const uint8_t* M = a.mask + n * a.ld;
   uint32_t c[6] = {0u, 0u, 0u, 0u, 0u, 0u};
@@ -1643,7 +1658,10 @@ __global__ __launch_bounds__(kTailThreads) void tails_worst_count_kernel(TailArg
     if (lane == 0 && v) atomicAdd(&tot[q], v);
   }
   __syncthreads();
-  if (tid < 6) w.wcnt[tid * a.N + n] = tot[tid];
+  if (tid < 6) {
+    const uint32_t kn = tid < 3 ? 0u : (tid == 3 ? known[0] : (tid == 4 ? known[1] : known[2]));
+    w.wcnt[tid * a.N + n] = tot[tid] + kn;  // a pair not read has tot 0
+  }
 }
 
 // Exclusive scans of the six count rows over the sequences, one workgroup
