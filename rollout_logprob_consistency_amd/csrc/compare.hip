@@ -809,12 +809,19 @@ __global__ __launch_bounds__(kTailThreads) void tails_p0_kernel(TailArgs a, Tail
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float* v = vv[k];
-      double e[3] = {0.0, 0.0, 0.0};
-      if (actv[k]) {
-#pragma unroll
-        for (int s = 0; s < 3; ++s)
-          if (__builtin_isfinite(v[s])) e[s] = exp_f64((double)v[s]);
-      }
+      // e^A, e^B, e^C of an active token (0 if not finite). When every active
+      // lane of the wave has bitwise equal B and A (or C and B), e^B (e^C) is
+      // the exponential already formed (a uniform test).
+      const bool act = actv[k];
+      const bool ab = __float_as_uint(v[0]) == __float_as_uint(v[1]);
+      const bool bc = __float_as_uint(v[1]) == __float_as_uint(v[2]);
+      const bool same_ab = __ballot(act && !ab) == 0, same_bc = __ballot(act && !bc) == 0;
+      double e[3];
+      e[0] = act && __builtin_isfinite(v[0]) ? exp_f64((double)v[0]) : 0.0;
+      if (same_ab) e[1] = e[0];
+      else e[1] = act && __builtin_isfinite(v[1]) ? exp_f64((double)v[1]) : 0.0;
+      if (same_bc) e[2] = e[1];
+      else e[2] = act && __builtin_isfinite(v[2]) ? exp_f64((double)v[2]) : 0.0;
 #pragma unroll
       for (int p = 0; p < 3; ++p) {
         uint64_t key;
