@@ -12,6 +12,7 @@ reductions use DPP, ds_swizzle and readlane).
 
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import shutil
@@ -50,9 +51,10 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
         raise RuntimeError("no HIP sources under " + CSRC)
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
-    for s in srcs:
-        o = os.path.join(objdir, os.path.basename(s) + ".o")
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
+
+    def compile_one(src_obj):
+        s, o = src_obj
         cmd = [hipcc(), *compile_flags(), *(extra or []), "-c", s, "-o", o]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -61,7 +63,16 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
             raise RuntimeError(f"hipcc failed for {s}:\n{r.stdout}\n{r.stderr}")
         if verbose and (r.stdout or r.stderr):
             print(r.stdout + r.stderr, flush=True)
-        objs.append(o)
+
+    # The translation units and the two assembly checks are independent:
+    # run them side by side (hipcc is single-threaded per file).
+    jobs = max(1, min(8, os.cpu_count() or 1))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        futs = [ex.submit(compile_one, so) for so in zip(srcs, objs)]
+        futs.append(ex.submit(check_score_isa, objdir, extra, verbose))
+        futs.append(ex.submit(check_compare_isa, objdir, extra, verbose))
+        for f in futs:
+            f.result()
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
@@ -69,8 +80,6 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    check_score_isa(objdir, extra, verbose)
-    check_compare_isa(objdir, extra, verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -218,4 +218,34 @@ struct QuantArgs {
 
 hipError_t launch_seq_quantiles(const QuantArgs& a, hipStream_t stream);
 
+// e^x in fp64 for finite x (the comparison's rare tokens with |d| >= 0.5 and
+// the tail statistics' probabilities). Cody-Waite reduction x = k ln2 + r
+// with ln2 split into a 32-bit head (k * head is exact for |k| < 2^21) and a
+// tail, |r| <= ln2 / 2; e^r by its Taylor series to degree 12 (truncation
+// < 2e-16 relative); then the exact scaling by 2^k, which overflows to +inf
+// and underflows to 0 as the true value does. x is clamped to [-800, 800]
+// first, beyond which e^x is already inf or 0.
+__device__ __forceinline__ double exp_f64(double x) {
+  constexpr double kLog2e = 0x1.71547652b82fep+0;
+  constexpr double kLn2Hi = 0x1.62e42feep-1;
+  constexpr double kLn2Lo = 0x1.a39ef35793c76p-33;
+  x = fmin(fmax(x, -800.0), 800.0);
+  const double k = rint(x * kLog2e);
+  const double r = fma(-k, kLn2Lo, fma(-k, kLn2Hi, x));
+  double p = 1.0 / 479001600.0;  // 1/12!
+  p = fma(p, r, 1.0 / 39916800.0);
+  p = fma(p, r, 1.0 / 3628800.0);
+  p = fma(p, r, 1.0 / 362880.0);
+  p = fma(p, r, 1.0 / 40320.0);
+  p = fma(p, r, 1.0 / 5040.0);
+  p = fma(p, r, 1.0 / 720.0);
+  p = fma(p, r, 1.0 / 120.0);
+  p = fma(p, r, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return ldexp(p, (int)k);
+}
+
 }  // namespace lp
