@@ -7,7 +7,9 @@ file, with hipcc for gfx950. Packed-fp32 instructions are disabled for all
 device code. The device assembly of score.hip is then checked for wait-state
 hazards around its inline-assembly MFMAs (isa_check.py); a violation fails
 the build. The comparison kernel's assembly is checked for ds_bpermute (its
-reductions use DPP, ds_swizzle and readlane).
+reductions use DPP, ds_swizzle and readlane). Both files' buffer -> LDS copies
+(inline assembly) are checked for VALU writes of their SGPR operands fewer than
+5 wait states before them.
 """
 
 from __future__ import annotations
@@ -96,9 +98,13 @@ def check_score_isa(objdir: str, extra: list[str] | None = None, verbose: bool =
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stdout}\n{r.stderr}")
-    problems = isa_check.check_asm(open(out).read())
+    text = open(out).read()
+    problems = isa_check.check_asm(text)
     if problems:
         raise RuntimeError("inline-assembly MFMA hazard check failed:\n" + "\n".join(problems[:20]))
+    problems = isa_check.check_lds_dma_sgpr(text)
+    if problems:
+        raise RuntimeError("buffer -> LDS copy SGPR hazard check failed:\n" + "\n".join(problems[:20]))
 
 
 def check_compare_isa(objdir: str, extra: list[str] | None = None, verbose: bool = False) -> None:
@@ -113,9 +119,13 @@ def check_compare_isa(objdir: str, extra: list[str] | None = None, verbose: bool
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stdout}\n{r.stderr}")
-    problems = isa_check.check_no_bpermute(open(out).read(), "compare_kernel")
+    text = open(out).read()
+    problems = isa_check.check_no_bpermute(text, "compare_kernel")
     if problems:
         raise RuntimeError("compare_kernel cross-lane check failed:\n" + "\n".join(problems))
+    problems = isa_check.check_lds_dma_sgpr(text, "compare_kernel")
+    if problems:
+        raise RuntimeError("buffer -> LDS copy SGPR hazard check failed:\n" + "\n".join(problems[:20]))
 
 
 if __name__ == "__main__":

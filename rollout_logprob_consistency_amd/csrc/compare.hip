@@ -54,10 +54,12 @@ constexpr int kWindow = 256;  // positions per wave step (64 lanes x 4)
 // uniform and step 32 reads lanes 0 and 32 (readlane: a wave-uniform value).
 template <int kM>
 __device__ __forceinline__ int xlane(int v) {
-  if constexpr (kM == 1) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-  else if constexpr (kM == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-  else if constexpr (kM == 4) return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
-  else if constexpr (kM == 8) return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+  // Every source lane of these patterns exists and every row and bank is
+  // enabled, so no lane keeps an old value (mov_dpp: none is materialised).
+  if constexpr (kM == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  else if constexpr (kM == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  else if constexpr (kM == 4) return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  else if constexpr (kM == 8) return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);  // row_mirror
   else return __builtin_amdgcn_ds_swizzle(v, 0x401F);  // kM == 16: bit mode, lane ^ 16
 }
 
@@ -164,18 +166,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uin
 // rsrc + voff + soff to LDS byte lds + 16 i (or 4 i). Inline assembly, so the
 // compiler does not take the asynchronous LDS write as aliasing every LDS
 // read that follows (it would wait for all copies in flight); the ring's
-// vmcnt waits and barriers order copies and reads. M0 holds the LDS address;
-// an M0 write needs one wait state before an LDS-DMA load.
+// vmcnt waits and barriers order copies and reads. M0 holds the LDS address.
+// The compiler inserts no wait states before an inline-assembly instruction,
+// so the statement carries its own: 5, which covers both an M0 write (1) and
+// a VALU write of the resource or offset SGPRs (5; e.g. a v_readlane that
+// restores a spilled resource), and the build checks the result.
 template <bool kDw4>
 __device__ __forceinline__ void ring_copy(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, uint32_t voff,
                                           uint32_t soff) {
   if (kDw4)
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
                  : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
                  : "memory");
   else
-    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+    asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds"
                  :
                  : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
                  : "memory");
@@ -190,7 +195,15 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(8))) void c
   __shared__ __attribute__((aligned(1024))) char ring[kRing * kSlotB];
   const int lane = threadIdx.x & 63;
   const int p = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // pair of this wave
-  const int64_t n = blockIdx.x;
+  // Workgroups are dealt to the 8 XCDs in turn; XCD x takes the x-th
+  // contiguous eighth of the sequences, so that the 80-byte records of
+  // neighbouring sequences (and their rows) meet in one L2 and leave it as
+  // whole lines rather than as partial lines from several XCDs.
+  int64_t n;
+  {
+    const int64_t b = blockIdx.x, xcd = b & 7, idx = b >> 3, per = a.N >> 3, rem = a.N & 7;
+    n = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  }
   const float* Lp = (p == 1 ? a.B : a.A) + n * a.ld;
   const float* Rp = (p == 0 ? a.B : a.C) + n * a.ld;
   const uint8_t* M = a.mask + n * a.ld;
@@ -210,6 +223,7 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(8))) void c
   int seq_n = 0;  // active tokens folded so far (same in every lane)
   Runs seq = {-1, 0, 0, 0};
   int mism = 0, nonf = 0, k3n = 0;
+  int mism_w = 0;  // mismatches counted a whole window at a time (wave-uniform)
   double mx = 0.0, sa = 0.0, ss = 0.0, sk = 0.0, st = 0.0;
   bool slow = false;  // this lane has a finite token with |d| >= 0.5
 
@@ -383,16 +397,10 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(8))) void c
       const float vr[4] = {qr[0], qr[1], qr[2], qr[3]};
       // Three wave-uniform shortcuts for the common windows; the folds they
       // make are exactly the general fold's for those windows, term by term
-      // and in the same order.
-      //  * No active position (prompt, padding): nothing to fold (an empty
-      //    segment is the identity of the run monoid).
-      //  * Every position active, mismatching and with |delta| < 0.5 (so
-      //    finite): straight-line arithmetic, and the window is one run of
-      //    256 mismatches.
-      //  * Every position active with identical finite scores: nothing but
-      //    the count (and the capped unit weights below e^0.5).
-      // Conditions are gathered as wave masks (one compare each, combined in
-      // scalar registers); all 64 lanes run this loop.
+      // and in the same order. Conditions are gathered as wave masks (one
+      // compare each, combined in scalar registers); all 64 lanes run this
+      // loop. First: no active position (prompt, padding), nothing to fold
+      // (an empty segment is the identity of the run monoid).
       if (__ballot(qm != 0u) == 0) {
         if (kPT) {
 #pragma unroll
@@ -404,34 +412,50 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(8))) void c
         }
         continue;
       }
-      const uint64_t act = __ballot(((qm - 0x01010101u) & ~qm & 0x80808080u) == 0u);  // no zero byte
+      // am[e]: lanes whose position w + 4 lane + e is active.
+      uint64_t am[4], all_act = ~0ull;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        am[e] = __ballot(((qm >> (8 * e)) & 0xFFu) != 0u);
+        all_act &= am[e];
+      }
+      const int wn = __popcll(am[0]) + __popcll(am[1]) + __popcll(am[2]) + __popcll(am[3]);
       // The differing test is on the fp32 difference y = left - right, with
       // a margin: |y| < 0.4995 implies |delta| < 0.5 in fp64; then
       // d = right - left = -y exactly. (With a tolerance instead of the
-      // bitwise test, that shortcut is not taken.)
+      // bitwise test, that shortcut is not taken.) Inactive positions pass
+      // both tests; the shortcuts give them no contribution (a zero delta,
+      // k3 and weight, which leave every sum and the maximum unchanged).
       float ys[4];
-      uint64_t neq[4], differ = kBitwise ? act : 0;
+      uint64_t neq[4], differ = kBitwise ? ~0ull : 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         ys[e] = vl[e] - vr[e];
         neq[e] = __ballot(__float_as_uint(vl[e]) != __float_as_uint(vr[e]));
-        differ &= neq[e] & __ballot(fabsf(ys[e]) < 0.49951171875f);
+        differ &= ~am[e] | (neq[e] & __ballot(fabsf(ys[e]) < 0.49951171875f));
       }
-      if (differ == ~0ull) {
+      // Every active position mismatches with |delta| < 0.5: straight-line
+      // arithmetic (with selects when some positions are inactive), and the
+      // window's active tokens form one run of mismatches.
+      auto differ_fold = [&](auto masked_tag) __attribute__((always_inline)) {
+        constexpr bool kM = decltype(masked_tag)::value;
         const int64_t i0 = w + l4;
         float wk = 0.f, wt = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const double dl = (double)vl[e] - (double)vr[e];
+          const bool ae = !kM || ((qm >> (8 * e)) & 0xFFu) != 0u;
+          double dl = (double)vl[e] - (double)vr[e];
+          if (kM) dl = ae ? dl : 0.0;
           const double ad = fabs(dl);
           asm("v_max_f64 %0, |%1|, %2" : "=v"(mx) : "v"(dl), "v"(mx));
           sa += ad;
           ss += dl;
-          const float x = -ys[e];
+          const float x = kM ? (ae ? -ys[e] : 0.f) : -ys[e];
           const float tx = small_tx(x);
           wk = __builtin_fmaf(tx, x, wk);
           if (kPT || !tis_count) {
-            const float tis = small_tis(tx, x, clip_f);
+            float tis = small_tis(tx, x, clip_f);
+            if (kM) tis = ae ? tis : 0.f;
             wt += tis;
             if (kPT) {
               pt_row[i0 + e] = (float)ad;
@@ -442,19 +466,25 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(8))) void c
         }
         sk += (double)wk;
         if (!tis_count) st += (double)wt;
-        mism += 4;
-        seq = runs_combine(seq, seq_n, Runs{0, kWindow, kWindow, kWindow}, kWindow);
-        seq_n += kWindow;
+      };
+      if (differ == ~0ull) {
+        if (all_act == ~0ull) differ_fold(std::false_type{});
+        else differ_fold(std::true_type{});
+        mism_w += wn;
+        seq = runs_combine(seq, seq_n, Runs{0, wn, wn, wn}, wn);
+        seq_n += wn;
         continue;
       }
-      uint64_t same = act;
+      // Every active position has identical finite scores: nothing but the
+      // count (and the capped unit weights below e^0.5).
+      uint64_t same = ~0ull;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) same &= ~neq[e] & __ballot(fabsf(vl[e]) < __builtin_inff());
+      for (int e = 0; e < 4; ++e) same &= ~am[e] | (~neq[e] & __ballot(fabsf(vl[e]) < __builtin_inff()));
       if (same == ~0ull) {
         if (!tis_count) {
           float wt = 0.f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) wt += one_tis;
+          for (int e = 0; e < 4; ++e) wt += ((qm >> (8 * e)) & 0xFFu) != 0u ? one_tis : 0.f;
           st += (double)wt;
         }
         if (kPT) {
@@ -463,11 +493,11 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(8))) void c
           for (int e = 0; e < 4; ++e) {
             pt_row[i0 + e] = 0.f;
             pt_row[plane + i0 + e] = 0.f;
-            pt_row[2 * plane + i0 + e] = one_tis;
+            pt_row[2 * plane + i0 + e] = ((qm >> (8 * e)) & 0xFFu) != 0u ? one_tis : 0.f;
           }
         }
-        seq = runs_combine(seq, seq_n, Runs{-1, 0, 0, 0}, kWindow);
-        seq_n += kWindow;
+        seq = runs_combine(seq, seq_n, Runs{-1, 0, 0, 0}, wn);
+        seq_n += wn;
         continue;
       }
       unsigned amask = 0;  // bit e: position w + l4 + e is active
@@ -501,7 +531,8 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(8))) void c
   const double sk_small = sk;  // k3 of the tokens with |d| < 0.5
   double st2 = 0.0, sd2 = 0.0;
   int n2 = 0;
-  if (__ballot(slow) != 0) {
+  const bool any_slow = __ballot(slow) != 0;
+  if (any_slow) {
     double sk2 = 0.0;
     for (int64_t w = 0; w < a.L; w += kWindow) {
 #pragma unroll 1
@@ -528,37 +559,53 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(8))) void c
     if (!tis_count) st += st2;
   }
 
-  mism = wave_sum(mism);
-  nonf = wave_sum(nonf);
-  k3n = wave_sum(k3n);
+  // Wave reductions; a count that is zero in every lane (the usual case for
+  // the non-finite counts, and for the per-lane mismatch count when every
+  // window took a shortcut) needs none.
+  auto isum = [&](int v) __attribute__((always_inline)) { return __ballot(v != 0) ? wave_sum(v) : 0; };
+  mism = isum(mism) + mism_w;
+  nonf = isum(nonf);
+  k3n = isum(k3n);
   mx = wave_max(mx);  // |delta| >= 0 and finite: fmax is the exact maximum
   sa = wave_sum(sa);
   ss = wave_sum(ss);
   sk = wave_sum(sk);
   if (tis_count) {
     // (#finite active - #|d| >= 0.5) + sum d over |d| < 0.5 + their k3 sum
-    // + the capped weights of the others, in this order.
-    const int n_small = seq_n - nonf - wave_sum(n2);
-    st = (((double)n_small + (-ss - wave_sum(sd2))) + wave_sum(sk_small)) + wave_sum(st2);
+    // + the capped weights of the others, in this order. Without tokens of
+    // |d| >= 0.5 the terms of the others are zeros and the k3 sum is sk:
+    // the same bits with three reductions fewer.
+    if (any_slow) {
+      const int n_small = seq_n - nonf - wave_sum(n2);
+      st = (((double)n_small + (-ss - wave_sum(sd2))) + wave_sum(sk_small)) + wave_sum(st2);
+    } else {
+      st = ((double)(seq_n - nonf) + (-ss)) + sk;
+    }
   } else {
     st = wave_sum(st);
   }
 
-  if (lane == 0) {
-    lp_seq_stats* o = a.out + (size_t)p * a.N + n;
-    o->valid = seq_n;
-    o->mismatch = mism;
-    o->first_div = seq.first;
-    o->longest_run = seq.best;
-    o->nonfinite = nonf;
-    o->k3_nonfinite = k3n;
-    o->max_abs = mx;
-    o->sum_abs = sa;
-    o->sum_signed = ss;
-    o->sum_k3 = sk;
-    o->sum_d = -ss;  // d = -delta termwise, summed in the same order
-    o->seq_tis = fmin(exp(-ss), clip);
-    o->sum_tok_tis = st;
+  // The 80-byte record goes out as one store instruction (lane i < 10 writes
+  // its 8-byte word), not as a lane's several partial stores: the records of
+  // a pair are N x 80 bytes apart from those of the other pairs, and many
+  // small writes into lines that other workgroups fill later cost the
+  // streaming reads about 5 % at large N.
+  static_assert(sizeof(lp_seq_stats) == 80, "ten 8-byte words");
+  auto pack = [](int lo, int hi) __attribute__((always_inline)) {
+    return (uint64_t)(uint32_t)lo | ((uint64_t)(uint32_t)hi << 32);
+  };
+  const uint64_t words[10] = {
+      pack(seq_n, mism), pack(seq.first, seq.best), pack(nonf, k3n),
+      (uint64_t)__double_as_longlong(mx), (uint64_t)__double_as_longlong(sa),
+      (uint64_t)__double_as_longlong(ss), (uint64_t)__double_as_longlong(sk),
+      (uint64_t)__double_as_longlong(-ss),  // sum_d: d = -delta termwise, same order
+      (uint64_t)__double_as_longlong(fmin(exp(-ss), clip)),  // seq_tis
+      (uint64_t)__double_as_longlong(st)};
+  if (lane < 10) {
+    uint64_t v = words[0];
+#pragma unroll
+    for (int i = 1; i < 10; ++i) v = lane == i ? words[i] : v;
+    reinterpret_cast<uint64_t*>(a.out + (size_t)p * a.N + n)[lane] = v;
   }
 }
 

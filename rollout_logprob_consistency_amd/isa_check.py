@@ -146,3 +146,53 @@ def check_no_bpermute(asm: str, name_part: str = "compare_kernel") -> list[str]:
         if n:
             problems.append(f"{name}: {n} ds_bpermute/ds_permute instruction(s)")
     return problems
+
+
+# ---------------------------------------------------------------------------
+# Buffer -> LDS copies written as inline assembly (both tile kernels' operand
+# stages, the comparison kernel's window ring): the compiler inserts no wait
+# states around an inline-assembly instruction, and CDNA requires 5 between a
+# VALU instruction that writes an SGPR (v_readlane restoring a spilled
+# resource, a v_cmp writing a lane mask) and a vector memory instruction that
+# reads that SGPR as its resource or offset. The copies carry their own
+# s_nop; this check proves on the built code that no such write sits closer.
+# ---------------------------------------------------------------------------
+
+VMEM_SGPR_SLOTS = 5
+_SREG = re.compile(r"s\[(\d+):(\d+)\]|\bs(\d+)\b")
+
+
+def _sregs(text: str) -> set[int]:
+    out: set[int] = set()
+    for m in _SREG.finditer(text):
+        if m.group(3) is not None:
+            out.add(int(m.group(3)))
+        else:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return out
+
+
+def check_lds_dma_sgpr(asm: str, name_part: str = "") -> list[str]:
+    """Problems: a VALU write of an SGPR that a buffer -> LDS load reads,
+    fewer than 5 wait states before it, in any kernel whose symbol contains
+    name_part."""
+    problems: list[str] = []
+    names = [k for k in re.findall(r"\.amdhsa_kernel (\S+)", asm) if name_part in k]
+    for name in names:
+        lines = _kernel_lines(asm, name)
+        for n, (t, _) in enumerate(lines):
+            op, ops = _split(t)
+            if not (op.startswith("buffer_load") and " lds" in t and len(ops) >= 3):
+                continue
+            used = _sregs(ops[1]) | _sregs(ops[2])
+            slots = 0
+            for m in range(n - 1, -1, -1):
+                pt, _ = lines[m]
+                pop, pops = _split(pt)
+                if pop.startswith("v_") and pops and _sregs(pops[0]) & used:
+                    problems.append(f"{name}: VALU '{pt}' writes an SGPR that '{t}' reads "
+                                    f"fewer than {VMEM_SGPR_SLOTS} wait states later")
+                slots += _slots(pop, pops)
+                if slots >= VMEM_SGPR_SLOTS:
+                    break
+    return problems

@@ -96,3 +96,45 @@ def test_built_compare_kernel_has_no_bpermute():
     asm = open(path).read()
     assert isa_check.kernel_bodies(asm, "compare_kernel")
     assert isa_check.check_no_bpermute(asm) == []
+
+
+def dma_kernel(body_lines):
+    body = "\n".join("\t" + l for l in body_lines)
+    return (".amdhsa_kernel _ZN2lp14compare_kernelEv\n.end_amdhsa_kernel\n"
+            "_ZN2lp14compare_kernelEv:\n" + body + "\n.Lfunc_end2:\n")
+
+
+COPY = [";;#ASMSTART", "s_nop 4", "buffer_load_dwordx4 v18, s[12:15], s8 offen lds", ";;#ASMEND"]
+
+
+def test_lds_copy_with_its_wait_states_passes():
+    lines = ["v_readlane_b32 s15, v63, 19", "s_add_i32 m0, s6, s2", *COPY]
+    assert isa_check.check_lds_dma_sgpr(dma_kernel(lines)) == []
+
+
+def test_spilled_resource_restored_just_before_an_lds_copy_is_caught():
+    # the faulting pattern: a v_readlane restoring the resource, then the copy
+    # with only one wait state of its own
+    lines = ["v_readlane_b32 s15, v63, 19", ";;#ASMSTART", "s_nop 0",
+             "buffer_load_dwordx4 v18, s[12:15], s8 offen lds", ";;#ASMEND"]
+    assert any("writes an SGPR" in p for p in isa_check.check_lds_dma_sgpr(dma_kernel(lines)))
+
+
+def test_valu_write_of_the_offset_sgpr_is_caught():
+    lines = ["v_cmp_ne_u32_e64 s[8:9], v1, v2", ";;#ASMSTART", "s_nop 1",
+             "buffer_load_dword v8, s[20:23], s8 offen lds", ";;#ASMEND"]
+    assert isa_check.check_lds_dma_sgpr(dma_kernel(lines))
+
+
+def test_salu_writes_and_other_registers_pass():
+    lines = ["s_lshl_b32 s8, s3, 10", "v_readlane_b32 s30, v63, 2", ";;#ASMSTART", "s_nop 0",
+             "buffer_load_dword v8, s[20:23], s8 offen lds", ";;#ASMEND"]
+    assert isa_check.check_lds_dma_sgpr(dma_kernel(lines)) == []
+
+
+@pytest.mark.parametrize("name", ["score.device.s", "compare.device.s"])
+def test_built_lds_copies_have_their_wait_states(name):
+    path = os.path.join(ROOT, "_build", name)
+    if not os.path.exists(path):
+        pytest.skip("no build assembly; run the build first")
+    assert isa_check.check_lds_dma_sgpr(open(path).read()) == []
