@@ -239,15 +239,24 @@ lp_status lp_score_ex(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
  *
  * Integer fields and max_abs are exact. The fp64 sums are taken in a fixed
  * order, so they are bitwise reproducible run to run and independent of N.
- * Precision of the k3 and TIS terms: for |d_i| < 0.5 a token's k3 and
- * exp(d_i) are evaluated in fp32 (k3 by its Taylor series to d^9 / 9!, no
- * cancellation; exp(d) as 1 + d + k3 from the same series), the terms of
- * each group of four consecutive positions are added in fp32 and the group
- * sums in fp64; the sums agree with the exactly rounded ones to about 1e-7
- * relative (the library's tests hold them to 1e-6). For |d_i| >= 0.5 both
- * come from one fp64 exponential, k3 = (e^d - 1) - d, summed in fp64. The
- * per-token k3 and TIS outputs carry the same per-term precision. sum_abs, sum_signed, sum_d and seq_tis are fp64 from
- * the fp64 differences (1e-9 relative is asserted).
+ * sum_abs, sum_signed, sum_d and seq_tis are fp64 from the fp64 differences
+ * (the library's tests hold them to 1e-9 relative of the exactly rounded
+ * sums). Precision of the k3 and TIS terms:
+ *   - |d_i| < 0.5: k3 = d^2 g(d) in fp32, with d the fp32 difference
+ *     right - left (within an ulp of d_i) and g(d) = sum_k d^k / (k + 2)!
+ *     by a degree-5 polynomial fitted on [-0.5, 0.5] (2.5e-8 relative, so
+ *     no cancellation); the terms of each group of four consecutive
+ *     positions are added in fp32 and the group sums in fp64. When
+ *     tis_clip > e^0.5 (no such token reaches the cap), these tokens' share
+ *     of sum_tok_tis is their count + their fp64 sum of d + their k3 sum
+ *     (e^d = 1 + d + k3); otherwise each weight min(1 + d + k3, tis_clip) is
+ *     rounded to fp32 and summed like k3.
+ *   - |d_i| >= 0.5: both from one fp64 exponential, k3 = (e^d - 1) - d and
+ *     min(e^d, tis_clip), summed in fp64.
+ * sum_k3 and sum_tok_tis agree with the exactly rounded sums to about 1e-7
+ * relative (the library's tests hold them to 1e-6). The per-token k3 and TIS
+ * outputs carry the same per-term precision (fp32 weights 1 + d + k3 below
+ * 0.5).
  *
  * Layout:
  *   gen_A, replay_B, train_C  [N, L] fp32, row stride ld elements (ld >= L).

@@ -12,28 +12,32 @@
 //    logprob_mae; the blog's signed mean);
 //  * Schulman k3 = expm1(d) - d with d = right - left, overflow counted and
 //    never clipped ("Metric measurement basis"); for |d| < 0.5 the
-//    exponential terms are evaluated in fp32 (k3 by its Taylor series), beyond
-//    that in fp64 from one exponential, (e^d - 1) - d;
+//    exponential terms are evaluated in fp32 (k3 by a fitted polynomial of
+//    its series), beyond that in fp64 from one exponential, (e^d - 1) - d;
 //  * token and sequence truncated importance weights min(exp(d), C) and
 //    min(exp(sum d), C) ("Diagnosing Training Inference Mismatch in LLM
 //    Reinforcement Learning", section 3 on verl's rollout correction;
 //    "Rollout-Training Mismatch in LLM RL", section 2.1).
 //
 // Design: one workgroup per sequence, one wave per pair, so each wave keeps
-// the state of a single pair (few registers, high occupancy). A wave walks its
-// sequence in windows of 256 positions; lane l folds positions w + 4l ..
-// w + 4l + 3 (one 16-byte load per score array and a 4-byte mask load, so
-// every load instruction reads one contiguous KiB), with the next window's
-// loads in flight. Statistics that do not depend on order -- counts, max and
-// the fp64 sums -- accumulate per lane across windows. The order-sensitive
-// ones (first mismatch and runs, a segment monoid over the active tokens) are
-// formed per window -- from ballots when the window is all-equal or
-// all-different, else by an ordered XOR butterfly whose lower half is always
-// the left operand -- and folded into the sequence state in window order. The
-// per-lane accumulators are reduced at the end by a fixed XOR butterfly (each
-// step adds the same two values in both lanes). Everything depends only on L,
-// so results are bitwise reproducible and independent of N. The three waves
-// read the mask and each score array twice; the second reads hit in cache.
+// the state of a single pair (few registers, high occupancy). The sequence is
+// walked in windows of 256 positions; lane l folds positions w + 4l ..
+// w + 4l + 3. Each wave copies one of the three score arrays (and the mask)
+// of a window from memory straight into a four-window LDS ring (buffer ->
+// LDS loads, every array read once, three windows in flight, no VGPR held by
+// a load), and the pair waves read their two arrays from the ring. Most
+// windows are empty (prompt, padding), all-mismatching with small
+// differences, or all-identical, and take wave-uniform shortcuts; the others
+// take the general fold. Statistics that do not depend on order -- counts,
+// max and the fp64 sums -- accumulate per lane across windows. The
+// order-sensitive ones (first mismatch and runs, a segment monoid over the
+// active tokens) are formed per window -- from ballots when the window's
+// active tokens all agree or all differ, else by an ordered XOR butterfly
+// whose lower half is always the left operand -- and folded into the
+// sequence state in window order. The per-lane accumulators are reduced at
+// the end by a fixed XOR butterfly (each step adds the same two values in
+// both lanes). Everything depends only on L, so results are bitwise
+// reproducible and independent of N.
 #include <math.h>
 
 #include <type_traits>

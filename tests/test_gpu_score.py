@@ -167,6 +167,21 @@ def test_qwen8b_shaped_parity_and_repeatability(qwen8b):
     assert np.max(np.abs(got[rows] - ref)) <= SCORE_ATOL
 
 
+def test_qwen8b_shaped_parity_every_row(qwen8b):
+    """All 8192 rows of the Qwen3-8B-shaped batch against the fp64 oracle
+    (in 512-row blocks of fp64 logits), so a fault confined to some token or
+    vocabulary tiles cannot pass on sampled rows."""
+    c, wd, xd = qwen8b
+    got = gpu_score(xd, wd, c.ids)
+    worst = 0.0
+    for r0 in range(0, c.T, 512):
+        z = oracle.logits(c.x_bits[r0:r0 + 512], c.w_bits)
+        ref, _ = oracle.log_softmax_at(z, c.ids[r0:r0 + 512], c.temperature)
+        worst = max(worst, float(np.max(np.abs(got[r0:r0 + 512] - ref))))
+        del z
+    assert worst <= SCORE_ATOL, worst
+
+
 # --------------------------------------------------------------------------
 # Batch invariance: 512 fixed probe rows at random positions inside batches
 # of 1, 7, 64, 512 and 8192 rows, twice each; 16, 17, 32 and 33 rows sit on
