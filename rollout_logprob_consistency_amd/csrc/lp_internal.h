@@ -248,4 +248,61 @@ __device__ __forceinline__ double exp_f64(double x) {
   return ldexp(p, (int)k);
 }
 
+// ---- Cross-lane steps of the XOR butterflies, without the LDS crossbar
+// (the comparison and correction kernels' reductions).
+// Step m pairs lane l with lane l ^ m. Every step leaves both lanes of a pair
+// with the same value, so after steps 1 and 2 a quad is uniform and the half-
+// row mirror (lane 7 - l of its 8) reads what lane l ^ 4 holds; after step 4
+// the row mirror (lane 15 - l) reads lane l ^ 8's value. Step 16 swaps the
+// 16-lane halves of each 32 with ds_swizzle; after it each 32-lane half is
+// uniform and step 32 reads lanes 0 and 32 (readlane: a wave-uniform value).
+template <int kM>
+__device__ __forceinline__ int xlane(int v) {
+  // Every source lane of these patterns exists and every row and bank is
+  // enabled, so no lane keeps an old value (mov_dpp: none is materialised).
+  if constexpr (kM == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  else if constexpr (kM == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  else if constexpr (kM == 4) return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  else if constexpr (kM == 8) return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);  // row_mirror
+  else return __builtin_amdgcn_ds_swizzle(v, 0x401F);  // kM == 16: bit mode, lane ^ 16
+}
+
+template <int kM>
+__device__ __forceinline__ double xlane(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = xlane<kM>((int)(uint32_t)b), hi = xlane<kM>((int)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// The value of lane `l` once each 32-lane half is uniform.
+__device__ __forceinline__ int lane_value(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ double lane_value(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Sum / maximum over the wave by the fixed XOR butterfly; every lane gets the
+// value lane 0 forms, ((x_0 + x_1) + (x_2 + x_3)) + ... (fp64 addition is
+// commutative, so both lanes of a step agree bitwise).
+template <typename T>
+__device__ __forceinline__ T wave_sum(T x) {
+  x += xlane<1>(x);
+  x += xlane<2>(x);
+  x += xlane<4>(x);
+  x += xlane<8>(x);
+  x += xlane<16>(x);
+  return lane_value(x, 0) + lane_value(x, 32);
+}
+
+__device__ __forceinline__ double wave_max(double x) {
+  x = fmax(x, xlane<1>(x));
+  x = fmax(x, xlane<2>(x));
+  x = fmax(x, xlane<4>(x));
+  x = fmax(x, xlane<8>(x));
+  x = fmax(x, xlane<16>(x));
+  return fmax(lane_value(x, 0), lane_value(x, 32));
+}
+
 }  // namespace lp
