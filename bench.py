@@ -89,7 +89,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the scoring path has no cross-GPU "
-              "exchange and this build runs on a single MI355X (use --gpus 1).",
+              "exchange, and the library and its benchmark run on a single MI355X "
+              "(use --gpus 1).",
               file=sys.stderr)
         return 2
 

@@ -34,7 +34,7 @@ extern "C" {
 typedef enum {
   LP_OK = 0,
   LP_EINVAL = 1,       /* an argument is invalid; nothing was enqueued        */
-  LP_EUNSUPPORTED = 2, /* valid, but a shape/alignment this build does not
+  LP_EUNSUPPORTED = 2, /* valid, but a shape/alignment the library does not
                           handle; nothing was enqueued                        */
   LP_EHIP = 3          /* a HIP runtime call or kernel launch failed          */
 } lp_status;
