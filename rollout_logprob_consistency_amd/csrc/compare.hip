@@ -534,10 +534,9 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(8))) void c
   }
 
   // The 80-byte record goes out as one store instruction (lane i < 10 writes
-  // its 8-byte word), not as a lane's several partial stores: the records of
-  // a pair are N x 80 bytes apart from those of the other pairs, and many
-  // small writes into lines that other workgroups fill later cost the
-  // streaming reads about 5 % at large N.
+  // its 8-byte word), not as one lane's several partial stores. (The
+  // records' writes cost the streaming reads about 5 % at large N however
+  // they are cut.)
   static_assert(sizeof(lp_seq_stats) == 80, "ten 8-byte words");
   auto pack = [](int lo, int hi) __attribute__((always_inline)) {
     return (uint64_t)(uint32_t)lo | ((uint64_t)(uint32_t)hi << 32);

@@ -250,3 +250,21 @@ def test_large_differences_and_overflow():
         assert np.array_equal(got[:, 0][fin[:, 0]], ref[:, 0][fin[:, 0]])
         np.testing.assert_allclose(got[:, 1:][fin[:, 1:]], ref[:, 1:][fin[:, 1:]],
                                    rtol=1e-6, atol=1e-30)
+
+
+def test_records_at_an_8_byte_aligned_address(record):
+    """lp_seq_stats records need only their natural 8-byte alignment: an
+    output buffer 8 bytes past a 16-byte boundary gets the same bytes."""
+    C = synth.noise_scores(record.C, record.mask, 1e-3, seed=31)
+    A, B, M = dev(record.A), dev(record.B), dev(record.mask)
+    Cd = dev(C)
+    nbytes = 3 * record.A.shape[0] * lp.SEQ_STATS_DTYPE.itemsize
+    aligned = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    shifted = torch.zeros(nbytes + 8, dtype=torch.uint8, device=DEV)
+    lp.compare_raw(A, B, Cd, M, out=aligned)
+    lp.compare_raw(A, B, Cd, M, out=shifted[8:])
+    torch.cuda.synchronize()
+    assert aligned.data_ptr() % 16 == 0 and shifted[8:].data_ptr() % 16 == 8
+    assert torch.equal(aligned, shifted[8:])
+    check_stats(lp.stats_from_bytes(aligned, record.A.shape[0]),
+                oracle.compare(record.A, record.B, C, record.mask))
