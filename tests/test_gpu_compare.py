@@ -268,3 +268,73 @@ def test_records_at_an_8_byte_aligned_address(record):
     assert torch.equal(aligned, shifted[8:])
     check_stats(lp.stats_from_bytes(aligned, record.A.shape[0]),
                 oracle.compare(record.A, record.B, C, record.mask))
+
+
+def window_mix_rows(seed, N=24, windows=12, tail=77):
+    """Rows built window by window (256 positions) from every kind of window
+    the comparison kernel treats apart: empty, fully or partly active, all
+    mismatching with small differences, all identical, one large |d|, one
+    NaN, one 1-ulp difference, signed zeros, and mixes; plus a partial tail."""
+    rng = np.random.default_rng(seed)
+    L = 256 * windows + tail
+    B = (-rng.exponential(2.0, (N, L))).astype(np.float32)
+    A, C = B.copy(), B.copy()
+    M = np.zeros((N, L), np.uint8)
+    for n in range(N):
+        for w0 in range(0, L, 256):
+            w1 = min(L, w0 + 256)
+            sl = slice(w0, w1)
+            kind = rng.integers(0, 9)
+            if kind == 0:
+                continue
+            act = np.ones(w1 - w0, bool)
+            if kind in (2, 8):
+                cut = sorted(rng.integers(0, w1 - w0, 2))
+                act[:] = False
+                act[cut[0]:cut[1] + 1] = True
+                act &= rng.random(w1 - w0) < (0.5 if kind == 8 else 1.0)
+            M[n, sl] = act
+            noise = rng.normal(0.0, 1e-3, w1 - w0).astype(np.float32)
+            if kind in (1, 2, 4, 5, 8):
+                C[n, sl] = B[n, sl] + noise
+            if kind == 4:
+                C[n, w0 + rng.integers(0, w1 - w0)] += np.float32(0.7)
+            if kind == 5:
+                C[n, w0 + rng.integers(0, w1 - w0)] = np.nan
+            if kind == 6:
+                j = w0 + rng.integers(0, w1 - w0)
+                C[n, j] = np.nextafter(B[n, j], np.float32(0.0))
+            if kind == 7:
+                js = w0 + rng.integers(0, w1 - w0, 3)
+                B[n, js] = np.float32(0.0)
+                A[n, js] = np.float32(0.0)
+                C[n, js] = np.float32(-0.0)
+            if kind == 8:
+                same = rng.random(w1 - w0) < 0.5
+                C[n, sl] = np.where(same, B[n, sl], C[n, sl])
+            if rng.random() < 0.5:
+                A[n, sl] = B[n, sl] + rng.normal(0.0, 1e-3, w1 - w0).astype(np.float32)
+    return A, B, C, M
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_window_shortcuts_against_the_oracle_and_the_element_path(seed):
+    A, B, C, M = window_mix_rows(seed)
+    N, L = A.shape
+    for clip, atol in ((2.0, None), (1.25, None), (2.0, 5e-4)):
+        (stats, pt), _ = run((A, B, C, M), tis_clip=clip, atol=atol, per_token=True)
+        ref = oracle.per_token(A, B, C, M, tis_clip=clip)
+        got = pt.cpu().numpy()
+        assert np.array_equal(np.isnan(got), np.isnan(ref))
+        fin = ~np.isnan(ref)
+        assert np.array_equal(got[:, 0][fin[:, 0]], ref[:, 0][fin[:, 0]])
+        np.testing.assert_allclose(got[:, 1:][fin[:, 1:]], ref[:, 1:][fin[:, 1:]],
+                                   rtol=1e-6, atol=1e-30)
+        # Rows of stride L + 1 take element loads for every window.
+        big = [np.zeros((N, L + 1), a.dtype) for a in (A, B, C, M)]
+        for b, a in zip(big, (A, B, C, M)):
+            b[:, :L] = a
+        vec = lp.compare(dev(A), dev(B), dev(C), dev(M), clip, atol, check=False)
+        sca = lp.compare(*[dev(b)[:, :L] for b in big], clip, atol, check=False)
+        for p in lp.PAIRS:
+            assert vec[p].tobytes() == sca[p].tobytes(), (p, clip, atol)
