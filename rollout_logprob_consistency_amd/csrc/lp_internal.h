@@ -188,6 +188,26 @@ __device__ __forceinline__ void wave_hist_add(uint32_t* h, uint32_t b, bool hit,
   }
 }
 
+// The same add into 16-bit counters packed two to a 32-bit word (bin b in
+// the low half of word b / 2 for even b) unless kWide: for rows of at most
+// 65 535 positions no bin can overflow, and the histogram takes half the LDS.
+template <bool kWide>
+__device__ __forceinline__ void hist16_add(uint32_t* h, uint32_t b, bool hit, int lane) {
+  const uint64_t hb = __ballot(hit);
+  if (hb == 0) return;
+  const uint32_t b0 = __builtin_amdgcn_readfirstlane(b);
+  uint32_t bin = b, inc = 1u;
+  if (__ballot(hit && b != b0) == 0) {
+    if (lane != __ffsll((long long)hb) - 1) return;
+    bin = b0;
+    inc = (uint32_t)__popcll(hb);
+  } else if (!hit) {
+    return;
+  }
+  if (kWide) atomicAdd(&h[bin], inc);
+  else atomicAdd(&h[bin >> 1], inc << ((bin & 1u) << 4));
+}
+
 struct TailArgs {
   const float* A;
   const float* B;

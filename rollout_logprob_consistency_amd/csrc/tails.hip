@@ -354,25 +354,9 @@ __device__ __forceinline__ bool tail_key(const float v[3], bool act, int p, uint
   return act && __builtin_isfinite(l) && __builtin_isfinite(r);
 }
 
-// Pass-0 histogram increment of bucket b: 32-bit counters, or (kWide false,
-// rows of at most 65 535 positions) two 16-bit counters per word, so that
-// the three pairs' histograms take 26.8 KB of LDS instead of 53.6 KB.
-template <bool kWide>
-__device__ __forceinline__ void hist16_add(uint32_t* h, uint32_t b, bool hit, int lane) {
-  const uint64_t hb = __ballot(hit);
-  if (hb == 0) return;
-  const uint32_t b0 = __builtin_amdgcn_readfirstlane(b);
-  uint32_t bin = b, inc = 1u;
-  if (__ballot(hit && b != b0) == 0) {
-    if (lane != __ffsll((long long)hb) - 1) return;
-    bin = b0;
-    inc = (uint32_t)__popcll(hb);
-  } else if (!hit) {
-    return;
-  }
-  if (kWide) atomicAdd(&h[bin], inc);
-  else atomicAdd(&h[bin >> 1], inc << ((bin & 1u) << 4));
-}
+// Pass 0's histogram increments are hist16_add: 32-bit counters, or (kWide
+// false, rows of at most 65 535 positions) two 16-bit counters per word, so
+// that the three pairs' histograms take 26.8 KB of LDS instead of 53.6 KB.
 
 // Pass 0: the bucket histogram of every pair, and each sequence's sums and
 // maximum, over one row per workgroup.
