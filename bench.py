@@ -183,7 +183,7 @@ def main() -> int:
             for _ in range(args.steps):
                 lp.compare_tails(tA, tB, tC, tM, positions=True)
         else:
-            qout = torch.empty((3, sc.N, 3), dtype=torch.float64, device=dev)
+            qout = torch.empty((sc.N, 3, 3), dtype=torch.float64, device=dev)
             for _ in range(args.steps):
                 lp.compare_quantiles(tA, tB, tC, tM, out=qout, sync=False)
         torch.cuda.synchronize()
@@ -435,7 +435,7 @@ def main() -> int:
             log(f"bench: lp_compare_tails_ex (16 worst tokens per pair): {wmed:.1f} us")
             # Per-sequence p50 / p95 / p99 (lp_compare_quantiles): one read of
             # the 13 bytes of every position, selection in LDS.
-            qout = torch.empty((3, sc.N, 3), dtype=torch.float64, device=dev)
+            qout = torch.empty((sc.N, 3, 3), dtype=torch.float64, device=dev)
             qargs = (tA.data_ptr(), tB.data_ptr(), tC.data_ptr(), tM.data_ptr(), sc.N, sc.L,
                      sc.L, qout.data_ptr(), torch.cuda.current_stream().cuda_stream)
             c_quant = lp._lib.lib().lp_compare_quantiles

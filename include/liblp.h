@@ -261,7 +261,9 @@ lp_status lp_score_ex(const void* hidden_bf16, int64_t ldh, const void* w_bf16,
  * Layout:
  *   gen_A, replay_B, train_C  [N, L] fp32, row stride ld elements (ld >= L).
  *   mask                      [N, L] uint8, same row stride ld.
- *   out                       [3][N] lp_seq_stats (pair-major), device memory.
+ *   out                       [N][3] lp_seq_stats, sequence-major: out[3 n + p]
+ *                             is pair p (0: (A,B), 1: (B,C), 2: (A,C)) of
+ *                             sequence n. Device memory, 8-byte aligned.
  *   per_token                 NULL, or [3 pairs][3][N][L] fp32 contiguous with
  *                             values |delta|, k3, min(exp(d), tis_clip) for
  *                             active finite tokens, 0 for inactive tokens and
@@ -316,13 +318,13 @@ lp_status lp_compare(const float* gen_A, const float* replay_B,
  *
  * For each pair p (0: (A,B), 1: (B,C), 2: (A,C)) and sequence n, over the
  * sequence's counted tokens (active and both scores finite, Delta as for
- * lp_compare): out[(p * N + n) * 3 + j] = the quantile of |Delta| at
+ * lp_compare): out[(n * 3 + p) * 3 + j] = the quantile of |Delta| at
  * p = 0.5, 0.95, 0.99 for j = 0, 1, 2 (the rule above; 0 for a sequence
  * without counted tokens). Together with lp_compare's count, signed sum,
  * |Delta| sum and max_abs this is every field the AMD blog's compare()
  * returns, per record. With one counted token every quantile is its |Delta|.
  *
- * Layout and arguments as for lp_compare; out: [3][N][3] double in device
+ * Layout and arguments as for lp_compare; out: [N][3][3] double in device
  * memory, 8-byte aligned. No workspace: each (sequence, pair) is selected
  * inside one workgroup. Exact and independent of N and of scheduling.
  *

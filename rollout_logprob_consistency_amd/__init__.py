@@ -212,10 +212,11 @@ def compare_raw(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch.T
 
 
 def stats_from_bytes(raw: torch.Tensor, N: int) -> dict:
-    """Device stats bytes -> {"AB"|"BC"|"AC": numpy structured array [N]}."""
+    """Device stats bytes (lp_compare's [N][3] records) -> {"AB"|"BC"|"AC":
+    numpy structured array [N]}."""
     host = raw[: 3 * N * SEQ_STATS_DTYPE.itemsize].cpu().numpy()
-    rec = host.view(SEQ_STATS_DTYPE).reshape(3, N) if N else np.zeros((3, 0), SEQ_STATS_DTYPE)
-    return {p: rec[i] for i, p in enumerate(PAIRS)}
+    rec = host.view(SEQ_STATS_DTYPE).reshape(N, 3) if N else np.zeros((0, 3), SEQ_STATS_DTYPE)
+    return {p: np.ascontiguousarray(rec[:, i]) for i, p in enumerate(PAIRS)}
 
 
 def compare(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch.Tensor,
@@ -262,11 +263,12 @@ def compare_quantiles(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: t
     (lp_compare_quantiles): numpy's default quantile over each sequence's
     counted tokens, as the AMD blog's compare() returns for one record.
     Returns {"AB"|"BC"|"AC": numpy float64 [N, 3]} (sync=True), else the
-    [3, N, 3] float64 device tensor without synchronising."""
+    [N, 3, 3] float64 device tensor (sequence, pair, quantile) without
+    synchronising."""
     N, L, ld = _check_compare_inputs(A, B, C, mask)
     dev = A.device
     if out is None:
-        out = torch.empty((3, N, 3), dtype=torch.float64, device=dev)
+        out = torch.empty((N, 3, 3), dtype=torch.float64, device=dev)
     elif out.dtype != torch.float64 or not out.is_contiguous() or out.numel() < 9 * N:
         raise ValueError("out must be a contiguous float64 tensor of 3 * N * 3 values")
     st = lib().lp_compare_quantiles(_ptr(A), _ptr(B), _ptr(C), _ptr(mask), N, L, ld, _ptr(out),
@@ -275,8 +277,8 @@ def compare_quantiles(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: t
         raise LpError(st, "lp_compare_quantiles")
     if not sync:
         return out
-    q = out.reshape(3, N, 3).cpu().numpy()
-    return {p: q[i] for i, p in enumerate(PAIRS)}
+    q = out.reshape(N, 3, 3).cpu().numpy()
+    return {p: np.ascontiguousarray(q[:, i]) for i, p in enumerate(PAIRS)}
 
 
 def compare_tails(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, mask: torch.Tensor,

@@ -144,9 +144,9 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(8))) void c
   const int lane = threadIdx.x & 63;
   const int p = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // pair of this wave
   // Workgroups are dealt to the 8 XCDs in turn; XCD x takes the x-th
-  // contiguous eighth of the sequences, so that the 80-byte records of
-  // neighbouring sequences (and their rows) meet in one L2 and leave it as
-  // whole lines rather than as partial lines from several XCDs.
+  // contiguous eighth of the sequences, so that the records of neighbouring
+  // sequences (and their rows) meet in one L2 and leave it as whole lines
+  // rather than as partial lines from several XCDs.
   int64_t n;
   {
     const int64_t b = blockIdx.x, xcd = b & 7, idx = b >> 3, per = a.N >> 3, rem = a.N & 7;
@@ -534,9 +534,11 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(8))) void c
   }
 
   // The 80-byte record goes out as one store instruction (lane i < 10 writes
-  // its 8-byte word), not as one lane's several partial stores. (The
-  // records' writes cost the streaming reads about 5 % at large N however
-  // they are cut.)
+  // its 8-byte word), not as one lane's several partial stores. The three
+  // records of a sequence are adjacent (sequence-major output), so a
+  // workgroup writes 240 contiguous bytes: interleaved with the streaming
+  // reads, writes into three planes N records apart cost about 2 % more time
+  // at large N than the same bytes in one place.
   static_assert(sizeof(lp_seq_stats) == 80, "ten 8-byte words");
   auto pack = [](int lo, int hi) __attribute__((always_inline)) {
     return (uint64_t)(uint32_t)lo | ((uint64_t)(uint32_t)hi << 32);
@@ -552,7 +554,7 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(8))) void c
     uint64_t v = words[0];
 #pragma unroll
     for (int i = 1; i < 10; ++i) v = lane == i ? words[i] : v;
-    reinterpret_cast<uint64_t*>(a.out + (size_t)p * a.N + n)[lane] = v;
+    reinterpret_cast<uint64_t*>(a.out + (size_t)n * 3 + p)[lane] = v;
   }
 }
 

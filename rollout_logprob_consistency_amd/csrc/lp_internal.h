@@ -93,7 +93,7 @@ struct CompareArgs {
   double log_clip;        // log(tis_clip)
   double atol;            // < 0: bitwise mode
   bool vec;               // rows 16-byte aligned (A, B, C) and 4-byte aligned (mask)
-  lp_seq_stats* out;      // [3][N]
+  lp_seq_stats* out;      // [N][3]: pair p of sequence n at 3 n + p
   float* per_token;       // [3][3][N][L] or null
 };
 
@@ -233,7 +233,7 @@ struct QuantArgs {
   const uint8_t* mask;
   int64_t N, L, ld;
   bool vec;               // rows 16-byte aligned (A, B, C), mask 4-byte aligned, ld % 4 == 0
-  double* out;            // [3][N][3]
+  double* out;            // [N][3][3]: sequence, pair, quantile
 };
 
 hipError_t launch_seq_quantiles(const QuantArgs& a, hipStream_t stream);

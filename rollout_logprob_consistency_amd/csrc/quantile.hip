@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kQThreads) void seq_quantile_kernel(QuantArgs a) {
   const float* Lp = (p == 1 ? a.B : a.A) + n * a.ld;
   const float* Rp = (p == 0 ? a.B : a.C) + n * a.ld;
   const uint8_t* M = a.mask + n * a.ld;
-  double* out = a.out + ((size_t)p * (size_t)a.N + (size_t)n) * 3;
+  double* out = a.out + ((size_t)n * 3 + (size_t)p) * 3;
   // Every thread takes the same number of steps over the row (four
   // consecutive positions each), so whole waves reach the ballots; positions
   // past L hold no key.

@@ -270,6 +270,31 @@ def test_records_at_an_8_byte_aligned_address(record):
                 oracle.compare(record.A, record.B, C, record.mask))
 
 
+def test_record_layout_is_sequence_major():
+    """The C ABI's output is [N][3]: record 3 n + p is pair p (AB, BC, AC) of
+    sequence n. Sequences with 1 .. 5 active tokens and pairs that differ in
+    a known way make every record distinguishable in the raw bytes."""
+    N, L = 5, 300
+    B = synth.normal_f32(40, N * L).reshape(N, L)
+    A = B.copy()
+    A[:, 0] += 1.0      # A differs from B (and C) at position 0 only
+    C = B.copy()
+    C[:, 1] -= 2.0      # C differs from B (and A) at position 1 only
+    M = np.zeros((N, L), np.uint8)
+    for n in range(N):
+        M[n, : n + 1] = 1   # sequence n has n + 1 active tokens
+    raw, _ = lp.compare_raw(dev(A), dev(B), dev(C), dev(M))
+    rec = raw.cpu().numpy()[: 3 * N * lp.SEQ_STATS_DTYPE.itemsize].view(lp.SEQ_STATS_DTYPE)
+    ref = oracle.compare(A, B, C, M)
+    for n in range(N):
+        assert rec[3 * n]["valid"] == n + 1
+        assert (rec[3 * n]["mismatch"], rec[3 * n + 1]["mismatch"], rec[3 * n + 2]["mismatch"]) \
+            == (1, int(n >= 1), 1 + int(n >= 1))
+        for i, pair in enumerate(lp.PAIRS):
+            for f in ("valid", "mismatch", "first_div", "longest_run", "max_abs"):
+                assert rec[3 * n + i][f] == ref[pair][f][n], (n, pair, f)
+
+
 def window_mix_rows(seed, N=24, windows=12, tail=77):
     """Rows built window by window (256 positions) from every kind of window
     the comparison kernel treats apart: empty, fully or partly active, all
