@@ -99,17 +99,6 @@ typedef __attribute__((address_space(3))) char lds_char;
 constexpr int kRing = 4;
 constexpr int kSlotB = 3 * 1024 + 3 * 256;  // A, B, C (256 fp32 each), one mask copy per wave
 
-// Buffer resource (raw, 32-bit data format) over `bytes` bytes from `base`;
-// wave-uniform, so it stays in SGPRs. Reads past the end return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-  return __builtin_amdgcn_make_buffer_rsrc(
-      reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), 0,
-      (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
-}
-
 // One buffer -> LDS copy: lane i moves 16 bytes (kDw4) or 4 bytes from
 // rsrc + voff + soff to LDS byte lds + 16 i (or 4 i). Inline assembly, so the
 // compiler does not take the asynchronous LDS write as aliasing every LDS

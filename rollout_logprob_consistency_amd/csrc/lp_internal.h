@@ -168,6 +168,17 @@ __device__ __forceinline__ uint64_t bucket_top16(uint32_t b) {
   return (uint64_t)(b - 1u + kKeyTop16Lo);
 }
 
+// Buffer resource (raw, 32-bit data format) over `bytes` bytes from `base`;
+// wave-uniform, so it stays in SGPRs. Reads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), 0,
+      (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
 // Number of lanes below this one whose bit is set in m.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));

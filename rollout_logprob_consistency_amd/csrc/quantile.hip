@@ -318,11 +318,326 @@ __global__ __launch_bounds__(kQThreads) void seq_quantile_kernel(QuantArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Rows of at most 2 304 positions: one wave per (sequence, pair) holding the
+// row's keys in registers (kJ chunks of four positions per lane), so the row
+// is read once and no step waits for another wave.
+//  1. A histogram of 4 096 buckets: the key 0; the keys below 2^-126 (top 16
+//     bits under kWLo) together; one bucket per top-16 value from kWLo up.
+//     Its scan gives each rank a key range and the rank inside that range.
+//  2. While a range holds more than kWGroup keys (many equal or near-equal
+//     differences), a histogram of the next 12 bits below the range's common
+//     prefix narrows it; a range narrowed to one key value is settled.
+//  3. The keys of the remaining ranges are gathered in LDS, grouped by range,
+//     and each rank is found by counting within its group: the key c with
+//     #{keys < c} < rank <= #{keys <= c}.
+// All counts are integers, so the selected keys are exact and the result
+// does not depend on scheduling; the same fp64 quantile_lerp follows.
+// ---------------------------------------------------------------------------
+constexpr int kWBins = 4096;                           // 16-bit counters, two per word
+constexpr uint32_t kWLo = kKeyTop16Hi - (kWBins - 3);  // top-16 value of bucket 2
+constexpr int kWGroup = 64;                            // ranges up to this size are counted
+constexpr int kWMaxJ = 9;                              // 9 x 256 = 2 304 positions
+
+__device__ __forceinline__ uint32_t wbucket(uint64_t k) {
+  const uint32_t t = (uint32_t)(k >> 48);
+  return k == 0 ? 0u : (t < kWLo ? 1u : min(t, kKeyTop16Hi) - kWLo + 2u);
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_up((int)v, off);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Lane l owns bins [64 l, 64 l + 64) of the 16-bit histogram (words
+// [32 l, 32 l + 32)); `mine` is their sum and the result its inclusive
+// prefix over the lanes. The lanes start at different 16-byte chunks of
+// their 128 bytes, which spreads the reads over the LDS banks.
+__device__ __forceinline__ uint32_t hist_prefix(const uint32_t* h, int lane, uint32_t& mine) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const uint4* h4 = reinterpret_cast<const uint4*>(h) + 8 * lane;
+  uint32_t s = 0u;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const uint4 v = h4[(w + lane) & 7];
+    const u16x2 one = {1, 1};
+    s = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, v.x), one, s, false);
+    s = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, v.y), one, s, false);
+    s = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, v.z), one, s, false);
+    s = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, v.w), one, s, false);
+  }
+  mine = s;
+  return wave_incl_scan(s, lane);
+}
+
+// The bin of the r-th counted key (1 <= r <= total); `below` keys lie in
+// lower bins and `cnt` in this one. r is wave-uniform.
+__device__ __forceinline__ uint32_t hist_find(const uint32_t* h, int lane, uint32_t incl,
+                                              uint32_t mine, uint32_t r, uint32_t& below,
+                                              uint32_t& cnt) {
+  const int o = __ffsll((long long)__ballot(incl >= r)) - 1;  // lane holding the bin
+  const uint32_t ex = (uint32_t)__builtin_amdgcn_readlane((int)(incl - mine), o);
+  const uint32_t bin = 64u * (uint32_t)o + (uint32_t)lane;
+  const uint32_t c = (h[bin >> 1] >> ((bin & 1u) << 4)) & 0xFFFFu;
+  const uint32_t inc = wave_incl_scan(c, lane);
+  const int j = __ffsll((long long)__ballot(ex + inc >= r)) - 1;
+  below = ex + (uint32_t)__builtin_amdgcn_readlane((int)(inc - c), j);
+  cnt = (uint32_t)__builtin_amdgcn_readlane((int)c, j);
+  return 64u * (uint32_t)o + (uint32_t)j;
+}
+
+template <bool kVec, int kJ>
+__global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
+  constexpr int kK = 4 * kJ;
+  // The histogram (4 096 16-bit bins); afterwards the gathered keys.
+  __shared__ __attribute__((aligned(16))) uint32_t h[kWBins / 2];
+  uint64_t* cand = reinterpret_cast<uint64_t*>(h);
+  static_assert(kQT * kWGroup * sizeof(uint64_t) <= sizeof(h), "candidates fit");
+  const int lane = threadIdx.x;
+  // Same placement as the workgroup kernel: index 24 g + 8 p + x takes pair p
+  // of sequence 8 g + x, so a sequence's three waves share its rows in L2.
+  const int64_t b = blockIdx.x;
+  const int64_t n = 8 * (b / 24) + (b % 8);
+  const int p = (int)((b % 24) / 8);
+  if (n >= a.N) return;
+  const float* Lp = (p == 1 ? a.B : a.A) + n * a.ld;
+  const float* Rp = (p == 0 ? a.B : a.C) + n * a.ld;
+  const uint8_t* M = a.mask + n * a.ld;
+  double* out = a.out + ((size_t)n * 3 + (size_t)p) * 3;
+  const uint32_t L = (uint32_t)a.L;
+  // Range-checked buffer loads: positions past the row read as zeros and are
+  // not counted, so the last chunk needs no branch.
+  const __amdgpu_buffer_rsrc_t lr = row_rsrc(Lp, 4u * L), rr = row_rsrc(Rp, 4u * L);
+  const __amdgpu_buffer_rsrc_t mr = row_rsrc(M, L);
+
+  uint4* h4 = reinterpret_cast<uint4*>(h);
+  auto zero_hist = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h4[64 * i + lane] = make_uint4(0u, 0u, 0u, 0u);
+  };
+  zero_hist();
+
+  // Every chunk's loads are issued before any key is formed.
+  float lv[kK], rv[kK];
+  uint32_t mv[kK];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const uint32_t i = 256u * (uint32_t)j + 4u * (uint32_t)lane;
+    if (kVec) {
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 l4 = __builtin_amdgcn_raw_buffer_load_b128(lr, 4u * i, 0, 0);
+      const u32x4 r4 = __builtin_amdgcn_raw_buffer_load_b128(rr, 4u * i, 0, 0);
+      const uint32_t m4 = __builtin_amdgcn_raw_buffer_load_b32(mr, i, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lv[4 * j + e] = __uint_as_float(l4[e]);
+        rv[4 * j + e] = __uint_as_float(r4[e]);
+        mv[4 * j + e] = (m4 >> (8 * e)) & 0xFFu;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lv[4 * j + e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lr, 4u * (i + e), 0, 0));
+        rv[4 * j + e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, 4u * (i + e), 0, 0));
+        mv[4 * j + e] = __builtin_amdgcn_raw_buffer_load_b8(mr, i + e, 0, 0);
+      }
+    }
+  }
+  uint64_t k[kK];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t i = 256u * (uint32_t)j + 4u * (uint32_t)lane + (uint32_t)e;
+      k[4 * j + e] = key_of(lv[4 * j + e], rv[4 * j + e], i < L && mv[4 * j + e] != 0u);
+    }
+
+  // Step 1.
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kK; ++e) hist16_add<false>(h, wbucket(k[e]), k[e] != kNoKey, lane);
+  __syncthreads();
+  uint32_t mine;
+  const uint32_t incl = hist_prefix(h, lane, mine);
+  const uint32_t count = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  if (count == 0u) {
+    if (lane < 3) out[lane] = 0.0;
+    return;
+  }
+  // Per rank (wave-uniform): its key range [lo, hi), the bit above which
+  // every key of the range agrees (64: none), its rank and size there.
+  uint64_t lo[kQT], hi[kQT], val[kQT];
+  int sh[kQT];
+  uint32_t rk[kQT], m[kQT];
+  bool done[kQT];
+#pragma unroll
+  for (int t = 0; t < kQT; ++t) {
+    int64_t rl, rh;
+    quantile_ranks((int64_t)count, quantile_prob(t >> 1), &rl, &rh);
+    uint32_t below, cnt;
+    const uint32_t bk = hist_find(h, lane, incl, mine, (uint32_t)((t & 1) ? rh : rl), below, cnt);
+    rk[t] = (uint32_t)((t & 1) ? rh : rl) - below;
+    m[t] = cnt;
+    done[t] = bk == 0u;
+    val[t] = 0ull;
+    if (bk == 1u) {
+      lo[t] = 1ull;
+      hi[t] = (uint64_t)kWLo << 48;
+      sh[t] = 64;
+    } else {
+      const uint64_t top = (uint64_t)(bk - 2u + kWLo);
+      lo[t] = top << 48;
+      hi[t] = (top + 1ull) << 48;
+      sh[t] = 48;
+    }
+  }
+
+  // Step 2: each pass narrows every rank that shares the first oversized
+  // range by 12 bits (or to its last bits), so at most 6 passes per range.
+  for (int pass = 0; pass < 6 * kQT; ++pass) {
+    int t0 = -1;
+#pragma unroll
+    for (int t = 0; t < kQT; ++t)
+      if (t0 < 0 && !done[t] && m[t] > (uint32_t)kWGroup) t0 = t;
+    if (t0 < 0) break;
+    uint64_t rlo = 0ull, rhi = 0ull;
+    int rsh = 0;
+#pragma unroll
+    for (int t = 0; t < kQT; ++t)
+      if (t == t0) {
+        rlo = lo[t];
+        rhi = hi[t];
+        rsh = sh[t];
+      }
+    const int ds = rsh > 12 ? rsh - 12 : 0;
+    const uint32_t dmask = (1u << (rsh - ds)) - 1u;  // the bits in [ds, rsh): 12, or 4 at the end
+    const uint64_t base = rsh >= 64 ? 0ull : (rlo >> rsh) << rsh;
+    __syncthreads();  // the previous scan's reads are done
+    zero_hist();
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kK; ++e)
+      hist16_add<false>(h, (uint32_t)(k[e] >> ds) & dmask, k[e] >= rlo && k[e] < rhi, lane);
+    __syncthreads();
+    uint32_t mine2;
+    const uint32_t incl2 = hist_prefix(h, lane, mine2);
+#pragma unroll
+    for (int t = 0; t < kQT; ++t) {
+      if (done[t] || lo[t] != rlo || hi[t] != rhi) continue;
+      uint32_t below, cnt;
+      const uint32_t bin = hist_find(h, lane, incl2, mine2, rk[t], below, cnt);
+      const uint64_t sub = base + ((uint64_t)bin << ds);
+      lo[t] = sub > rlo ? sub : rlo;
+      hi[t] = sub + (1ull << ds) < rhi ? sub + (1ull << ds) : rhi;
+      sh[t] = ds;
+      rk[t] -= below;
+      m[t] = cnt;
+      if (ds == 0) {  // one key value
+        done[t] = true;
+        val[t] = lo[t];
+      }
+    }
+  }
+
+  // Step 3: groups of equal ranges, in target order; g[t] = the first target
+  // of t's group.
+  int g[kQT];
+  uint32_t goff[kQT];
+  uint32_t nc = 0u, maxm = 0u;
+#pragma unroll
+  for (int t = 0; t < kQT; ++t) {
+    g[t] = t;
+#pragma unroll
+    for (int u = 0; u < t; ++u)
+      if (g[t] == t && !done[u] && lo[u] == lo[t] && hi[u] == hi[t]) g[t] = u;
+    goff[t] = nc;
+    if (!done[t] && g[t] == t) {
+      nc += m[t];
+      maxm = m[t] > maxm ? m[t] : maxm;
+    }
+  }
+  if (nc > 0u) {
+    __syncthreads();  // the last scan's reads of the histogram are done
+#pragma unroll
+    for (int t = 0; t < kQT; ++t) {
+      if (done[t] || g[t] != t) continue;
+      uint32_t off = goff[t];
+#pragma unroll
+      for (int e = 0; e < kK; ++e) {
+        const bool hit = k[e] >= lo[t] && k[e] < hi[t];
+        const uint64_t mb = __ballot(hit);
+        if (mb == 0) continue;
+        if (hit) cand[off + lanes_below(mb)] = k[e];
+        off += (uint32_t)__popcll(mb);
+      }
+    }
+    __syncthreads();
+    for (uint32_t c0 = 0u; c0 < nc; c0 += 64u) {
+      const uint32_t i = c0 + (uint32_t)lane;
+      const bool has = i < nc;
+      // This candidate's group: the last group starting at or below i.
+      int mg = -1;
+      uint32_t moff = 0u, mm = 0u;
+#pragma unroll
+      for (int t = 0; t < kQT; ++t)
+        if (!done[t] && g[t] == t && goff[t] <= i) {
+          mg = t;
+          moff = goff[t];
+          mm = m[t];
+        }
+      const uint64_t c = has ? cand[i] : 0ull;
+      uint32_t less = 0u, leq = 0u;
+      for (uint32_t j = 0u; j < maxm; ++j) {
+        const uint64_t cj = cand[moff + j];  // below nc + 64: inside the array
+        const bool v = has && j < mm;
+        less += (v && cj < c) ? 1u : 0u;
+        leq += (v && cj <= c) ? 1u : 0u;
+      }
+#pragma unroll
+      for (int t = 0; t < kQT; ++t) {
+        if (done[t]) continue;
+        const uint64_t hb = __ballot(has && mg == g[t] && less < rk[t] && rk[t] <= leq);
+        if (hb == 0) continue;
+        const int src = __ffsll((long long)hb) - 1;
+        const uint32_t vlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)c, src);
+        const uint32_t vhi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(c >> 32), src);
+        val[t] = ((uint64_t)vhi << 32) | vlo;
+      }
+    }
+  }
+  if (lane < 3) {
+    uint64_t vl = val[0], vh = val[1];
+#pragma unroll
+    for (int q = 1; q < 3; ++q)
+      if (lane == q) {
+        vl = val[2 * q];
+        vh = val[2 * q + 1];
+      }
+    out[lane] = quantile_lerp((int64_t)count, quantile_prob(lane),
+                              __longlong_as_double((long long)vl), __longlong_as_double((long long)vh));
+  }
+}
+
+template <int kJ>
+void launch_wave(const QuantArgs& a, unsigned blocks, hipStream_t stream) {
+  if (a.vec)
+    hipLaunchKernelGGL((seq_quantile_wave_kernel<true, kJ>), dim3(blocks), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((seq_quantile_wave_kernel<false, kJ>), dim3(blocks), dim3(64), 0, stream, a);
+}
+
 }  // namespace
 
 hipError_t launch_seq_quantiles(const QuantArgs& a, hipStream_t stream) {
   const unsigned blocks = (unsigned)(3 * ((a.N + 7) / 8) * 8);  // 24 per group of 8 sequences
-  if (a.vec)
+  if (a.L <= 256 * 3) launch_wave<3>(a, blocks, stream);
+  else if (a.L <= 256 * 6) launch_wave<6>(a, blocks, stream);
+  else if (a.L <= 256 * kWMaxJ) launch_wave<kWMaxJ>(a, blocks, stream);
+  else if (a.vec)
     hipLaunchKernelGGL(seq_quantile_kernel<true>, dim3(blocks), dim3(kQThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(seq_quantile_kernel<false>, dim3(blocks), dim3(kQThreads), 0, stream, a);

@@ -132,6 +132,59 @@ def test_seq_quantiles_one_token_long_rows_and_strides():
             assert np.array_equal(got[p], ref[p]), (pad, p)
 
 
+def quantile_rows(kind, N, L, seed):
+    """Rows whose |delta| exercise each way the per-sequence selection
+    narrows a rank: continuous noise, a constant offset (every difference in
+    one 16-bit bucket), mostly zeros, 1-ulp differences, differences below
+    2^-126, one repeated non-zero difference, and a mix with NaN and Inf."""
+    rng = np.random.default_rng(seed)
+    B = rng.standard_normal((N, L)).astype(np.float32)
+    if kind == "noise":
+        C = (B + rng.standard_normal((N, L)) * 1e-3).astype(np.float32)
+    elif kind == "offset":
+        C = (B + np.float32(0.01)).astype(np.float32)
+    elif kind == "zeros":
+        C = B.copy()
+        C[rng.random((N, L)) < 0.3] += np.float32(1e-3)
+    elif kind == "ulp":
+        C = (B * np.float32(1 + 1e-7)).astype(np.float32)
+    elif kind == "tiny":
+        B = (rng.standard_normal((N, L)) * 1e-38).astype(np.float32)
+        C = (B + np.float32(1e-44) * rng.integers(0, 50, (N, L))).astype(np.float32)
+    elif kind == "equal":
+        B = np.zeros((N, L), np.float32)
+        C = np.full((N, L), np.float32(0.3))
+    else:
+        C = (B + rng.standard_normal((N, L)) * np.float32(10) ** rng.integers(-30, 3, (N, L))).astype(np.float32)
+        C[rng.random((N, L)) < 0.05] = np.nan
+        B[rng.random((N, L)) < 0.02] = np.inf
+    A = (B + rng.standard_normal((N, L)) * 1e-2).astype(np.float32)
+    M = (rng.random((N, L)) < rng.uniform(0.05, 1.0, (N, 1))).astype(np.uint8)
+    M[0] = 0                 # no counted token
+    M[1] = 0
+    M[1, L // 2] = 1         # one
+    return A, B, C, M
+
+
+@pytest.mark.parametrize("L", [1, 300, 768, 769, 1536, 1537, 2304, 2305])
+@pytest.mark.parametrize("kind", ["noise", "offset", "zeros", "ulp", "tiny", "equal", "mixed"])
+def test_seq_quantiles_every_row_length_and_kind(L, kind):
+    # Row lengths on both sides of each register-held key count (4, 8 or 12
+    # chunks of 256 positions; longer rows take the workgroup kernel), every
+    # kind of difference, rows with 16-byte vector loads and with element
+    # loads (a stride that is not a multiple of 4): all exact.
+    N = 12
+    A, B, C, M = quantile_rows(kind, N, L, seed=L)
+    run_seq_quantiles(A, B, C, M)
+    big = [np.zeros((N, L + 1), a.dtype) for a in (A, B, C, M)]
+    for b_, a_ in zip(big, (A, B, C, M)):
+        b_[:, :L] = a_
+    got = lp.compare_quantiles(*[dev(b_)[:, :L] for b_ in big])
+    ref = oracle.seq_quantiles(A, B, C, M)
+    for p in lp.PAIRS:
+        assert np.array_equal(got[p], ref[p]), p
+
+
 @pytest.mark.parametrize("case", ["ties_in_lists", "ties_beyond_key_buffer", "one_bucket"])
 def test_selection_paths(case):
     # The selection's paths, each exact against the oracle:
