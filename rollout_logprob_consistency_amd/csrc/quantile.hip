@@ -339,17 +339,23 @@ constexpr uint32_t kWLo = kKeyTop16Hi - (kWBins - 3);  // top-16 value of bucket
 constexpr int kWGroup = 64;                            // ranges up to this size are counted
 constexpr int kWMaxJ = 9;                              // 9 x 256 = 2 304 positions
 
-__device__ __forceinline__ uint32_t wbucket(uint64_t k) {
-  const uint32_t t = (uint32_t)(k >> 48);
-  return k == 0 ? 0u : (t < kWLo ? 1u : min(t, kKeyTop16Hi) - kWLo + 2u);
+// Bucket of a non-zero counted key (bucket 0, the key 0, is counted apart).
+__device__ __forceinline__ uint32_t wbucket_nz(uint64_t k) {
+  const uint32_t t = (uint32_t)(k >> 48);  // at most kKeyTop16Hi for a finite difference
+  return max(t, kWLo - 1u) - (kWLo - 2u);
 }
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = (uint32_t)__shfl_up((int)v, off);
-    if (lane >= off) v += o;
-  }
+// Inclusive prefix sum over the wave's lanes on DPP: shifts by 1, 2, 4 and 8
+// inside each row of 16 (lanes with no source add 0), then the last lane of
+// row 0 (and 2) is broadcast into row 1 (and 3), and the last lane of row 1
+// into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return v;
 }
 
@@ -371,7 +377,7 @@ __device__ __forceinline__ uint32_t hist_prefix(const uint32_t* h, int lane, uin
     s = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, v.w), one, s, false);
   }
   mine = s;
-  return wave_incl_scan(s, lane);
+  return wave_incl_scan(s);
 }
 
 // The bin of the r-th counted key (1 <= r <= total); `below` keys lie in
@@ -383,7 +389,7 @@ __device__ __forceinline__ uint32_t hist_find(const uint32_t* h, int lane, uint3
   const uint32_t ex = (uint32_t)__builtin_amdgcn_readlane((int)(incl - mine), o);
   const uint32_t bin = 64u * (uint32_t)o + (uint32_t)lane;
   const uint32_t c = (h[bin >> 1] >> ((bin & 1u) << 4)) & 0xFFFFu;
-  const uint32_t inc = wave_incl_scan(c, lane);
+  const uint32_t inc = wave_incl_scan(c);
   const int j = __ffsll((long long)__ballot(ex + inc >= r)) - 1;
   below = ex + (uint32_t)__builtin_amdgcn_readlane((int)(inc - c), j);
   cnt = (uint32_t)__builtin_amdgcn_readlane((int)c, j);
@@ -456,10 +462,21 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
       k[4 * j + e] = key_of(lv[4 * j + e], rv[4 * j + e], i < L && mv[4 * j + e] != 0u);
     }
 
-  // Step 1.
+  // Step 1. Zero differences (identical scores, often most of a row) are
+  // counted with ballots; every other counted key adds 1 to its 16-bit bin.
   __syncthreads();
+  uint32_t zeros = 0u;
 #pragma unroll
-  for (int e = 0; e < kK; ++e) hist16_add<false>(h, wbucket(k[e]), k[e] != kNoKey, lane);
+  for (int e = 0; e < kK; ++e) {
+    zeros += (uint32_t)__popcll(__ballot(k[e] == 0ull));
+    const bool hit = k[e] != 0ull && k[e] != kNoKey;
+    if (__ballot(hit) == 0) continue;
+    if (hit) {
+      const uint32_t bin = wbucket_nz(k[e]);
+      atomicAdd(&h[bin >> 1], 1u << ((bin & 1u) << 4));
+    }
+  }
+  if (lane == 0) atomicAdd(&h[0], zeros);  // bin 0: the low half of word 0
   __syncthreads();
   uint32_t mine;
   const uint32_t incl = hist_prefix(h, lane, mine);
@@ -469,11 +486,11 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
     return;
   }
   // Per rank (wave-uniform): its key range [lo, hi), the bit above which
-  // every key of the range agrees (64: none), its rank and size there.
-  uint64_t lo[kQT], hi[kQT], val[kQT];
+  // every key of the range agrees (64: none), its rank and size there. A
+  // range settled on one key value has sh == 0, and lo is that key.
+  uint64_t lo[kQT], hi[kQT];
   int sh[kQT];
   uint32_t rk[kQT], m[kQT];
-  bool done[kQT];
 #pragma unroll
   for (int t = 0; t < kQT; ++t) {
     int64_t rl, rh;
@@ -482,9 +499,10 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
     const uint32_t bk = hist_find(h, lane, incl, mine, (uint32_t)((t & 1) ? rh : rl), below, cnt);
     rk[t] = (uint32_t)((t & 1) ? rh : rl) - below;
     m[t] = cnt;
-    done[t] = bk == 0u;
-    val[t] = 0ull;
-    if (bk == 1u) {
+    if (bk == 0u) {
+      lo[t] = hi[t] = 0ull;
+      sh[t] = 0;
+    } else if (bk == 1u) {
       lo[t] = 1ull;
       hi[t] = (uint64_t)kWLo << 48;
       sh[t] = 64;
@@ -502,7 +520,7 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
     int t0 = -1;
 #pragma unroll
     for (int t = 0; t < kQT; ++t)
-      if (t0 < 0 && !done[t] && m[t] > (uint32_t)kWGroup) t0 = t;
+      if (t0 < 0 && sh[t] != 0 && m[t] > (uint32_t)kWGroup) t0 = t;
     if (t0 < 0) break;
     uint64_t rlo = 0ull, rhi = 0ull;
     int rsh = 0;
@@ -527,7 +545,7 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
     const uint32_t incl2 = hist_prefix(h, lane, mine2);
 #pragma unroll
     for (int t = 0; t < kQT; ++t) {
-      if (done[t] || lo[t] != rlo || hi[t] != rhi) continue;
+      if (sh[t] == 0 || lo[t] != rlo || hi[t] != rhi) continue;
       uint32_t below, cnt;
       const uint32_t bin = hist_find(h, lane, incl2, mine2, rk[t], below, cnt);
       const uint64_t sub = base + ((uint64_t)bin << ds);
@@ -536,10 +554,6 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
       sh[t] = ds;
       rk[t] -= below;
       m[t] = cnt;
-      if (ds == 0) {  // one key value
-        done[t] = true;
-        val[t] = lo[t];
-      }
     }
   }
 
@@ -553,18 +567,25 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
     g[t] = t;
 #pragma unroll
     for (int u = 0; u < t; ++u)
-      if (g[t] == t && !done[u] && lo[u] == lo[t] && hi[u] == hi[t]) g[t] = u;
+      if (g[t] == t && sh[u] != 0 && lo[u] == lo[t] && hi[u] == hi[t]) g[t] = u;
     goff[t] = nc;
-    if (!done[t] && g[t] == t) {
+    if (sh[t] != 0 && g[t] == t) {
       nc += m[t];
       maxm = m[t] > maxm ? m[t] : maxm;
     }
+  }
+  // The group structure is fixed before any rank is settled below.
+  bool open3[kQT], ldr[kQT];
+#pragma unroll
+  for (int t = 0; t < kQT; ++t) {
+    open3[t] = sh[t] != 0;
+    ldr[t] = open3[t] && g[t] == t;
   }
   if (nc > 0u) {
     __syncthreads();  // the last scan's reads of the histogram are done
 #pragma unroll
     for (int t = 0; t < kQT; ++t) {
-      if (done[t] || g[t] != t) continue;
+      if (!ldr[t]) continue;
       uint32_t off = goff[t];
 #pragma unroll
       for (int e = 0; e < kK; ++e) {
@@ -584,7 +605,7 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
       uint32_t moff = 0u, mm = 0u;
 #pragma unroll
       for (int t = 0; t < kQT; ++t)
-        if (!done[t] && g[t] == t && goff[t] <= i) {
+        if (ldr[t] && goff[t] <= i) {
           mg = t;
           moff = goff[t];
           mm = m[t];
@@ -597,25 +618,27 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
         less += (v && cj < c) ? 1u : 0u;
         leq += (v && cj <= c) ? 1u : 0u;
       }
+      // A rank's key (equal keys may answer it in several rounds: the same
+      // value) replaces the range's lower end, which the rounds no longer read.
 #pragma unroll
       for (int t = 0; t < kQT; ++t) {
-        if (done[t]) continue;
+        if (!open3[t]) continue;
         const uint64_t hb = __ballot(has && mg == g[t] && less < rk[t] && rk[t] <= leq);
         if (hb == 0) continue;
         const int src = __ffsll((long long)hb) - 1;
         const uint32_t vlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)c, src);
         const uint32_t vhi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(c >> 32), src);
-        val[t] = ((uint64_t)vhi << 32) | vlo;
+        lo[t] = ((uint64_t)vhi << 32) | vlo;
       }
     }
   }
   if (lane < 3) {
-    uint64_t vl = val[0], vh = val[1];
+    uint64_t vl = lo[0], vh = lo[1];
 #pragma unroll
     for (int q = 1; q < 3; ++q)
       if (lane == q) {
-        vl = val[2 * q];
-        vh = val[2 * q + 1];
+        vl = lo[2 * q];
+        vh = lo[2 * q + 1];
       }
     out[lane] = quantile_lerp((int64_t)count, quantile_prob(lane),
                               __longlong_as_double((long long)vl), __longlong_as_double((long long)vh));
