@@ -396,6 +396,18 @@ __device__ __forceinline__ uint32_t hist_find(const uint32_t* h, int lane, uint3
   return 64u * (uint32_t)o + (uint32_t)j;
 }
 
+// Lane masks of 64-bit key comparisons, formed in scalar registers (a ballot
+// of a combined condition would first materialise it per lane).
+__device__ __forceinline__ uint64_t mask_eq(uint64_t x, uint64_t y) {
+  return __builtin_amdgcn_uicmpl(x, y, 32);  // ICMP_EQ
+}
+__device__ __forceinline__ uint64_t mask_ne(uint64_t x, uint64_t y) {
+  return __builtin_amdgcn_uicmpl(x, y, 33);  // ICMP_NE
+}
+__device__ __forceinline__ uint64_t mask_in(uint64_t x, uint64_t lo, uint64_t hi) {
+  return __builtin_amdgcn_uicmpl(x, lo, 35) & __builtin_amdgcn_uicmpl(x, hi, 36);  // UGE, ULT
+}
+
 template <bool kVec, int kJ>
 __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
   constexpr int kK = 4 * kJ;
@@ -453,13 +465,16 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
       }
     }
   }
+  // Keys: the fp64 difference is finite exactly when both scores are.
   uint64_t k[kK];
 #pragma unroll
   for (int j = 0; j < kJ; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t i = 256u * (uint32_t)j + 4u * (uint32_t)lane + (uint32_t)e;
-      k[4 * j + e] = key_of(lv[4 * j + e], rv[4 * j + e], i < L && mv[4 * j + e] != 0u);
+      const double dl = (double)lv[4 * j + e] - (double)rv[4 * j + e];
+      const bool ok = i < L && mv[4 * j + e] != 0u && __builtin_isfinite(dl);
+      k[4 * j + e] = ok ? (uint64_t)__double_as_longlong(fabs(dl)) : kNoKey;
     }
 
   // Step 1. Zero differences (identical scores, often most of a row) are
@@ -468,10 +483,10 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
   uint32_t zeros = 0u;
 #pragma unroll
   for (int e = 0; e < kK; ++e) {
-    zeros += (uint32_t)__popcll(__ballot(k[e] == 0ull));
-    const bool hit = k[e] != 0ull && k[e] != kNoKey;
-    if (__ballot(hit) == 0) continue;
-    if (hit) {
+    zeros += (uint32_t)__popcll(mask_eq(k[e], 0ull));
+    const uint64_t hm = mask_ne(k[e], 0ull) & mask_ne(k[e], kNoKey);
+    if (hm == 0) continue;
+    if (__builtin_amdgcn_inverse_ballot_w64(hm)) {
       const uint32_t bin = wbucket_nz(k[e]);
       atomicAdd(&h[bin >> 1], 1u << ((bin & 1u) << 4));
     }
@@ -537,9 +552,21 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
     __syncthreads();  // the previous scan's reads are done
     zero_hist();
     __syncthreads();
+    // The keys of a crowded range often share a bin: when every key of the
+    // wave in the range does, one lane adds them all.
 #pragma unroll
-    for (int e = 0; e < kK; ++e)
-      hist16_add<false>(h, (uint32_t)(k[e] >> ds) & dmask, k[e] >= rlo && k[e] < rhi, lane);
+    for (int e = 0; e < kK; ++e) {
+      const uint64_t hm = mask_in(k[e], rlo, rhi);
+      if (hm == 0) continue;
+      const uint32_t bin = (uint32_t)(k[e] >> ds) & dmask;
+      const int first = __ffsll((long long)hm) - 1;
+      const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)bin, first);
+      if ((hm & __builtin_amdgcn_uicmp(bin, b0, 32)) == hm) {
+        if (lane == first) atomicAdd(&h[b0 >> 1], (uint32_t)__popcll(hm) << ((b0 & 1u) << 4));
+      } else if (__builtin_amdgcn_inverse_ballot_w64(hm)) {
+        atomicAdd(&h[bin >> 1], 1u << ((bin & 1u) << 4));
+      }
+    }
     __syncthreads();
     uint32_t mine2;
     const uint32_t incl2 = hist_prefix(h, lane, mine2);
@@ -589,10 +616,9 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
       uint32_t off = goff[t];
 #pragma unroll
       for (int e = 0; e < kK; ++e) {
-        const bool hit = k[e] >= lo[t] && k[e] < hi[t];
-        const uint64_t mb = __ballot(hit);
+        const uint64_t mb = mask_in(k[e], lo[t], hi[t]);
         if (mb == 0) continue;
-        if (hit) cand[off + lanes_below(mb)] = k[e];
+        if (__builtin_amdgcn_inverse_ballot_w64(mb)) cand[off + lanes_below(mb)] = k[e];
         off += (uint32_t)__popcll(mb);
       }
     }
