@@ -414,9 +414,12 @@ __global__ __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(8))) void c
       }
       // Every active position has identical finite scores: nothing but the
       // count (and the capped unit weights below e^0.5).
+      // (The finiteness mask comes straight from the compare: a ballot of it
+      // would first materialise it per lane.)
       uint64_t same = ~0ull;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) same &= ~am[e] | (~neq[e] & __ballot(fabsf(vl[e]) < __builtin_inff()));
+      for (int e = 0; e < 4; ++e)
+        same &= ~am[e] | (~neq[e] & __builtin_amdgcn_fcmpf(fabsf(vl[e]), __builtin_inff(), 4));  // FCMP_OLT
       if (same == ~0ull) {
         if (!tis_count) {
           float wt = 0.f;
