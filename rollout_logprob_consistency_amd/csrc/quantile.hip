@@ -409,7 +409,7 @@ __device__ __forceinline__ uint64_t mask_in(uint64_t x, uint64_t lo, uint64_t hi
 }
 
 template <bool kVec, int kJ>
-__global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
+__device__ __forceinline__ void seq_quantile_wave(const QuantArgs& a) {
   constexpr int kK = 4 * kJ;
   // The histogram (4 096 16-bit bins); afterwards the gathered keys.
   __shared__ __attribute__((aligned(16))) uint32_t h[kWBins / 2];
@@ -439,9 +439,10 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
   };
   zero_hist();
 
-  // Every chunk's loads are issued before any key is formed.
+  // Every chunk's loads are issued before any key is formed. The mask bytes
+  // of a chunk stay packed in one word (byte e: position i + e).
   float lv[kK], rv[kK];
-  uint32_t mv[kK];
+  uint32_t mw[kJ];
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
     const uint32_t i = 256u * (uint32_t)j + 4u * (uint32_t)lane;
@@ -449,19 +450,19 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
       const u32x4 l4 = __builtin_amdgcn_raw_buffer_load_b128(lr, 4u * i, 0, 0);
       const u32x4 r4 = __builtin_amdgcn_raw_buffer_load_b128(rr, 4u * i, 0, 0);
-      const uint32_t m4 = __builtin_amdgcn_raw_buffer_load_b32(mr, i, 0, 0);
+      mw[j] = __builtin_amdgcn_raw_buffer_load_b32(mr, i, 0, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         lv[4 * j + e] = __uint_as_float(l4[e]);
         rv[4 * j + e] = __uint_as_float(r4[e]);
-        mv[4 * j + e] = (m4 >> (8 * e)) & 0xFFu;
       }
     } else {
+      mw[j] = 0u;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         lv[4 * j + e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lr, 4u * (i + e), 0, 0));
         rv[4 * j + e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, 4u * (i + e), 0, 0));
-        mv[4 * j + e] = __builtin_amdgcn_raw_buffer_load_b8(mr, i + e, 0, 0);
+        mw[j] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(mr, i + e, 0, 0) << (8 * e);
       }
     }
   }
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
     for (int e = 0; e < 4; ++e) {
       const uint32_t i = 256u * (uint32_t)j + 4u * (uint32_t)lane + (uint32_t)e;
       const double dl = (double)lv[4 * j + e] - (double)rv[4 * j + e];
-      const bool ok = i < L && mv[4 * j + e] != 0u && __builtin_isfinite(dl);
+      const bool ok = i < L && ((mw[j] >> (8 * e)) & 0xFFu) != 0u && __builtin_isfinite(dl);
       k[4 * j + e] = ok ? (uint64_t)__double_as_longlong(fabs(dl)) : kNoKey;
     }
 
@@ -671,12 +672,26 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_kernel(QuantArgs a) {
   }
 }
 
+// Rows with 16-byte loads: at most 96 VGPRs, so 5 waves share a SIMD (at the
+// compiler's own choice of 100 it would be 4; the selection is issue-bound).
+// The element-load form keeps its registers (capped, it would spill).
+template <int kJ>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void seq_quantile_wave_kernel(
+    QuantArgs a) {
+  seq_quantile_wave<true, kJ>(a);
+}
+
+template <int kJ>
+__global__ __launch_bounds__(64) void seq_quantile_wave_elem_kernel(QuantArgs a) {
+  seq_quantile_wave<false, kJ>(a);
+}
+
 template <int kJ>
 void launch_wave(const QuantArgs& a, unsigned blocks, hipStream_t stream) {
   if (a.vec)
-    hipLaunchKernelGGL((seq_quantile_wave_kernel<true, kJ>), dim3(blocks), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((seq_quantile_wave_kernel<kJ>), dim3(blocks), dim3(64), 0, stream, a);
   else
-    hipLaunchKernelGGL((seq_quantile_wave_kernel<false, kJ>), dim3(blocks), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((seq_quantile_wave_elem_kernel<kJ>), dim3(blocks), dim3(64), 0, stream, a);
 }
 
 }  // namespace
