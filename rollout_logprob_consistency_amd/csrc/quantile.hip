@@ -322,8 +322,9 @@ __global__ __launch_bounds__(kQThreads) void seq_quantile_kernel(QuantArgs a) {
 // Rows of at most 2 304 positions: one wave per (sequence, pair) holding the
 // row's keys in registers (kJ chunks of four positions per lane), so the row
 // is read once and no step waits for another wave.
-//  1. A histogram of 4 096 buckets: the key 0; the keys below 2^-126 (top 16
-//     bits under kWLo) together; one bucket per top-16 value from kWLo up.
+//  1. A histogram of 4 096 buckets: the key 0; the keys whose top 16 bits
+//     are under kWLo (below 1.125 * 2^-126) together; one bucket per top-16
+//     value from kWLo up.
 //     Its scan gives each rank a key range and the rank inside that range.
 //  2. While a range holds more than kWGroup keys (many equal or near-equal
 //     differences), a histogram of the next 12 bits below the range's common
