@@ -429,7 +429,8 @@ __device__ __forceinline__ void seq_quantile_wave(const QuantArgs& a) {
   double* out = a.out + ((size_t)n * 3 + (size_t)p) * 3;
   const uint32_t L = (uint32_t)a.L;
   // Range-checked buffer loads: positions past the row read as zeros and are
-  // not counted, so the last chunk needs no branch.
+  // not counted, so the last chunk needs no branch (the vector form runs only
+  // on rows of a multiple of 4 positions: see launch_wave).
   const __amdgpu_buffer_rsrc_t lr = row_rsrc(Lp, 4u * L), rr = row_rsrc(Rp, 4u * L);
   const __amdgpu_buffer_rsrc_t mr = row_rsrc(M, L);
 
@@ -687,9 +688,12 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_elem_kernel(QuantArgs a)
   seq_quantile_wave<false, kJ>(a);
 }
 
+// A 16-byte buffer load that reaches past the resource's end returns zeros
+// as a whole (not per dword), so rows take the vector loads only when every
+// group of four positions lies inside the row.
 template <int kJ>
 void launch_wave(const QuantArgs& a, unsigned blocks, hipStream_t stream) {
-  if (a.vec)
+  if (a.vec && (a.L & 3) == 0)
     hipLaunchKernelGGL((seq_quantile_wave_kernel<kJ>), dim3(blocks), dim3(64), 0, stream, a);
   else
     hipLaunchKernelGGL((seq_quantile_wave_elem_kernel<kJ>), dim3(blocks), dim3(64), 0, stream, a);

@@ -11,7 +11,7 @@ import oracle
 import rollout_logprob_consistency_amd as lp
 from workloads import synth
 
-from .gpu_helpers import dev
+from .gpu_helpers import check_stats, dev
 
 pytestmark = pytest.mark.gpu
 
@@ -183,6 +183,35 @@ def test_seq_quantiles_every_row_length_and_kind(L, kind):
     ref = oracle.seq_quantiles(A, B, C, M)
     for p in lp.PAIRS:
         assert np.array_equal(got[p], ref[p]), p
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 5, 767, 1535, 2303])
+def test_vector_rows_with_a_partial_last_group(L):
+    # Rows 16-byte aligned with a stride that is a multiple of 4 take the
+    # vector loads even when L is not a multiple of 4: the last group of four
+    # positions reaches past the row into its padding, which holds values
+    # that must not be read as scores (NaN, huge, non-zero mask bytes).
+    # Per-sequence quantiles, batch tails and the comparison: all exact.
+    N = 10
+    A, B, C, M = quantile_rows("mixed", N, L, seed=L)
+    ld = (L + 3) // 4 * 4 + 4
+    big = []
+    for a_, fill in zip((A, B, C, M), (np.float32(3e38), np.float32(np.nan), np.float32(-7.5), 1)):
+        b_ = np.full((N, ld), fill, a_.dtype)
+        b_[:, :L] = a_
+        big.append(b_)
+    views = [dev(b_)[:, :L] for b_ in big]
+    assert views[0].stride(0) == ld and ld % 4 == 0 and views[0].data_ptr() % 16 == 0
+    got = lp.compare_quantiles(*views)
+    ref = oracle.seq_quantiles(A, B, C, M)
+    for p in lp.PAIRS:
+        assert np.array_equal(got[p], ref[p]), p
+    tg = lp.compare_tails(*views)
+    tr = oracle.tails(A, B, C, M)[0]
+    for p in lp.PAIRS:
+        for f in EXACT:
+            assert tg[p][f] == tr[p][f], (p, f)
+    check_stats(lp.compare(*views, check=False), oracle.compare(A, B, C, M))
 
 
 @pytest.mark.parametrize("case", ["ties_in_lists", "ties_beyond_key_buffer", "one_bucket"])
