@@ -920,7 +920,10 @@ __device__ __forceinline__ void lse_fold_stats(float& M, float& S, float& Q, int
 // one merge segment for token t, in ascending order, from the empty partial.
 // kHalves: the partials are per 176-row half of each vocabulary tile (rows
 // 2 vt and 2 vt + 1), merged with merge_halves first. kStats: the entropy
-// term and the argmax are carried along.
+// term and the argmax are carried along. The partials of kB tiles are loaded
+// before any of them is folded (the fold is a dependent chain; loaded one
+// tile at a time, a one-row merge waited a memory round trip per tile);
+// loads past hi repeat tile hi - 1 and are not folded.
 template <bool kHalves, bool kStats>
 __device__ __forceinline__ void seg_fold(const ScoreArgs& a, int t, int lo, int hi, float& M,
                                          float& S, float& Q, int& I) {
@@ -932,26 +935,43 @@ __device__ __forceinline__ void seg_fold(const ScoreArgs& a, int t, int lo, int 
   const float* ps = a.part_s + t;
   const float* pq = a.part_q + t;
   const int* pi = a.part_i + t;
-  if (kHalves) {
-#pragma unroll 8
-    for (int vt = lo; vt < hi; ++vt) {
-      const size_t r0 = (size_t)(2 * vt) * a.T, r1 = (size_t)(2 * vt + 1) * a.T;
-      float m, s;
-      merge_halves(pm[r0], ps[r0], pm[r1], ps[r1], m, s);
-      if (kStats) {
-        const float q = merge_q(pm[r0], ps[r0], pq[r0], pm[r1], ps[r1], pq[r1], m);
-        const int i = pm[r1] > pm[r0] ? pi[r1] : pi[r0];
-        lse_fold_stats(M, S, Q, I, m, s, q, i);
-      } else {
-        lse_fold(M, S, m, s);
+  constexpr int kP = kHalves ? 2 : 1;  // partial rows per tile
+  constexpr int kB = kStats ? 8 : 16;  // tiles per block of loads
+  for (int v0 = lo; v0 < hi; v0 += kB) {
+    float bm[kB][kP], bs[kB][kP], bq[kStats ? kB : 1][kP];
+    int bi[kStats ? kB : 1][kP];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const int vt = min(v0 + j, hi - 1);
+#pragma unroll
+      for (int h = 0; h < kP; ++h) {
+        const size_t r = (size_t)(kP * vt + h) * a.T;
+        bm[j][h] = pm[r];
+        bs[j][h] = ps[r];
+        if (kStats) {
+          bq[kStats ? j : 0][h] = pq[r];
+          bi[kStats ? j : 0][h] = pi[r];
+        }
       }
     }
-  } else {
-#pragma unroll 8
-    for (int vt = lo; vt < hi; ++vt) {
-      const size_t r = (size_t)vt * a.T;
-      if (kStats) lse_fold_stats(M, S, Q, I, pm[r], ps[r], pq[r], pi[r]);
-      else lse_fold(M, S, pm[r], ps[r]);
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      if (v0 + j >= hi) continue;  // uniform: past the segment
+      const int js = kStats ? j : 0;
+      if (kHalves) {
+        float m, s;
+        merge_halves(bm[j][0], bs[j][0], bm[j][1], bs[j][1], m, s);
+        if (kStats) {
+          const float q = merge_q(bm[j][0], bs[j][0], bq[js][0], bm[j][1], bs[j][1], bq[js][1], m);
+          const int i = bm[j][1] > bm[j][0] ? bi[js][1] : bi[js][0];
+          lse_fold_stats(M, S, Q, I, m, s, q, i);
+        } else {
+          lse_fold(M, S, m, s);
+        }
+      } else {
+        if (kStats) lse_fold_stats(M, S, Q, I, bm[j][0], bs[j][0], bq[js][0], bi[js][0]);
+        else lse_fold(M, S, bm[j][0], bs[j][0]);
+      }
     }
   }
 }
