@@ -214,89 +214,57 @@ size_t tail_bytes(int64_t N, int64_t L, int32_t k) { return tail_walk(nullptr, N
 __device__ __forceinline__ int pair_left(int p) { return p == 1 ? 1 : 0; }
 __device__ __forceinline__ int pair_right(int p) { return p == 0 ? 1 : 2; }
 
-// Position profile, stage 1: each thread sums its columns over chunk c's
+// Position profile, stage 1: each thread sums its column over chunk c's
 // sequences (fixed chunks, sequences in ascending order); the final kernel
-// folds the chunks in order. kVec: four consecutive columns per thread
-// (16-byte loads, each load instruction one contiguous KiB; the last partial
-// group by elements), else one column per thread. A column's sum takes the
-// same operations in the same order either way.
-template <bool kVec>
-__device__ void tails_pos_chunk(const TailArgs& a, const TailWs& w, int64_t g, int c) {
-  constexpr int kW = kVec ? 4 : 1;
-  const int64_t i0 = g * kW;
+// folds the chunks in order. One column per thread: with 4-byte loads the
+// launch has four times the waves of a 4-column form (16-byte loads), whose
+// 1.5 waves per SIMD left the reads latency-bound (the call took 1.5 % longer);
+// a column's sum is the same either way.
+__device__ void tails_pos_chunk(const TailArgs& a, const TailWs& w, int64_t i0, int c) {
   if (i0 >= a.L) return;
   const int64_t per = (a.N + w.nch - 1) / w.nch;
   const int64_t lo = c * per, hi = min(a.N, lo + per);
-  double s[kW][3] = {};
-  int32_t k[kW][3] = {};
-  const bool whole = kVec && i0 + 4 <= a.L;
+  double s[3] = {};
+  int32_t k[3] = {};
   // Four sequences' loads are issued together (all of them, masked or not).
   constexpr int kB = 4;
   for (int64_t n0 = lo; n0 < hi; n0 += kB) {
-    float v[kB][kW][3];
-    bool act[kB][kW];
+    float v[kB][3];
+    bool act[kB];
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
       const bool in = n0 + b < hi;
       const int64_t o = (in ? n0 + b : lo) * a.ld + i0;
-      if (kVec && whole) {
-        const uint32_t m = *reinterpret_cast<const uint32_t*>(a.mask + o);
-        const float4 fa = *reinterpret_cast<const float4*>(a.A + o);
-        const float4 fb = *reinterpret_cast<const float4*>(a.B + o);
-        const float4 fc = *reinterpret_cast<const float4*>(a.C + o);
-        const float va[4] = {fa.x, fa.y, fa.z, fa.w}, vb[4] = {fb.x, fb.y, fb.z, fb.w},
-                    vc[4] = {fc.x, fc.y, fc.z, fc.w};
-#pragma unroll
-        for (int e = 0; e < kW; ++e) {
-          act[b][e] = in && ((m >> (8 * e)) & 255u) != 0;
-          v[b][e][0] = va[e];
-          v[b][e][1] = vb[e];
-          v[b][e][2] = vc[e];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < kW; ++e) {
-          const bool col = i0 + e < a.L;
-          act[b][e] = in && col && a.mask[o + e] != 0;
-          v[b][e][0] = act[b][e] ? a.A[o + e] : 0.f;
-          v[b][e][1] = act[b][e] ? a.B[o + e] : 0.f;
-          v[b][e][2] = act[b][e] ? a.C[o + e] : 0.f;
-        }
-      }
+      act[b] = in && a.mask[o] != 0;
+      v[b][0] = act[b] ? a.A[o] : 0.f;
+      v[b][1] = act[b] ? a.B[o] : 0.f;
+      v[b][2] = act[b] ? a.C[o] : 0.f;
     }
 #pragma unroll
-    for (int b = 0; b < kB; ++b)
+    for (int b = 0; b < kB; ++b) {
+      if (!act[b]) continue;
 #pragma unroll
-      for (int e = 0; e < kW; ++e) {
-        if (!act[b][e]) continue;
-#pragma unroll
-        for (int p = 0; p < 3; ++p) {
-          const float l = v[b][e][pair_left(p)], r = v[b][e][pair_right(p)];
-          if (!__builtin_isfinite(l) || !__builtin_isfinite(r)) continue;
-          s[e][p] += fabs((double)l - (double)r);
-          k[e][p] += 1;
-        }
+      for (int p = 0; p < 3; ++p) {
+        const float l = v[b][pair_left(p)], r = v[b][pair_right(p)];
+        if (!__builtin_isfinite(l) || !__builtin_isfinite(r)) continue;
+        s[p] += fabs((double)l - (double)r);
+        k[p] += 1;
       }
+    }
   }
 #pragma unroll
-  for (int e = 0; e < kW; ++e) {
-    if (i0 + e >= a.L) continue;
-#pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      w.pos_part[((size_t)c * 3 + p) * a.L + i0 + e] = s[e][p];
-      w.pos_cpart[((size_t)c * 3 + p) * a.L + i0 + e] = k[e][p];
-    }
+  for (int p = 0; p < 3; ++p) {
+    w.pos_part[((size_t)c * 3 + p) * a.L + i0] = s[p];
+    w.pos_cpart[((size_t)c * 3 + p) * a.L + i0] = k[p];
   }
 }
 
 // Clears the histograms (every copy) and the gather counts, and resets the
 // selection state; with the position profile asked for (pos true, grid
-// ceil(L / (256 W)) x chunks, W = 4 columns a thread on the vector path, else
-// 1), workgroup (x, c) also forms stage 1 of the profile for columns
-// [256 W x, 256 W (x + 1)) of chunk c.
+// ceil(L / 256) x chunks), workgroup (x, c) also forms stage 1 of the profile
+// for columns [256 x, 256 (x + 1)) of chunk c.
 constexpr int kInitBlocks = 64;
 
-template <bool kVec>
 __global__ __launch_bounds__(kTailThreads) void tails_init_kernel(TailArgs a, TailWs w, bool pos) {
   uint4* z = reinterpret_cast<uint4*>(w.hist0);
   constexpr int64_t kVecs = (int64_t)(kHist0Words + kHistWords) / 4;
@@ -304,7 +272,7 @@ __global__ __launch_bounds__(kTailThreads) void tails_init_kernel(TailArgs a, Ta
   for (int64_t i = wg * kTailThreads + threadIdx.x; i < kVecs;
        i += (int64_t)gridDim.x * gridDim.y * kTailThreads)
     z[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (pos) tails_pos_chunk<kVec>(a, w, (int64_t)blockIdx.x * kTailThreads + threadIdx.x, (int)blockIdx.y);
+  if (pos) tails_pos_chunk(a, w, (int64_t)blockIdx.x * kTailThreads + threadIdx.x, (int)blockIdx.y);
   if (wg != 0) return;
   const int t = threadIdx.x;
   if (t < kMaxTargets) {
@@ -1487,10 +1455,9 @@ hipError_t launch_tails(const TailArgs& a, hipStream_t stream) {
   // With the position profile asked for, its stage 1 (also with N == 0:
   // zero partials for the fold) runs in the init kernel.
   const bool pos = a.pos_sum && a.L > 0;
-  const int64_t cols = a.vec ? 4 * kTailThreads : kTailThreads;  // columns per workgroup
-  const dim3 init_grid = pos ? dim3((unsigned)((a.L + cols - 1) / cols), (unsigned)w.nch) : dim3(kInitBlocks);
-  if (a.vec) hipLaunchKernelGGL(tails_init_kernel<true>, init_grid, dim3(kTailThreads), 0, stream, a, w, pos);
-  else hipLaunchKernelGGL(tails_init_kernel<false>, init_grid, dim3(kTailThreads), 0, stream, a, w, pos);
+  const dim3 init_grid =
+      pos ? dim3((unsigned)((a.L + kTailThreads - 1) / kTailThreads), (unsigned)w.nch) : dim3(kInitBlocks);
+  hipLaunchKernelGGL(tails_init_kernel, init_grid, dim3(kTailThreads), 0, stream, a, w, pos);
   if (a.worst_k > 0) {
     launch_select<kMaxTP>(a, w, stream);
     if (a.N > 0 && a.L > 0) {
