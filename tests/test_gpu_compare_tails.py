@@ -214,6 +214,31 @@ def test_vector_rows_with_a_partial_last_group(L):
     check_stats(lp.compare(*views, check=False), oracle.compare(A, B, C, M))
 
 
+def test_seq_quantiles_random_shapes():
+    # Seeded random shapes across both per-sequence kernels and every key
+    # count: N in [1, 40], L in [1, 3000], row padding 0 .. 5 (so vector and
+    # element loads both occur), a random kind of difference per case.
+    rng = np.random.default_rng(2024)
+    kinds = ["noise", "offset", "zeros", "ulp", "tiny", "equal", "mixed"]
+    for case in range(24):
+        N, L = int(rng.integers(1, 41)), int(rng.integers(1, 3001))
+        pad = int(rng.integers(0, 6))
+        kind = kinds[case % len(kinds)]
+        A, B, C, M = quantile_rows(kind, N, L, seed=1000 + case) if N >= 2 else \
+            tuple(x[:1] for x in quantile_rows(kind, 2, L, seed=1000 + case))
+        if pad:
+            big = [np.zeros((N, L + pad), a_.dtype) for a_ in (A, B, C, M)]
+            for b_, a_ in zip(big, (A, B, C, M)):
+                b_[:, :L] = a_
+            views = [dev(b_)[:, :L] for b_ in big]
+        else:
+            views = [dev(x) for x in (A, B, C, M)]
+        got = lp.compare_quantiles(*views)
+        ref = oracle.seq_quantiles(A, B, C, M)
+        for p in lp.PAIRS:
+            assert np.array_equal(got[p], ref[p]), (case, N, L, pad, kind, p)
+
+
 @pytest.mark.parametrize("case", ["ties_in_lists", "ties_beyond_key_buffer", "one_bucket"])
 def test_selection_paths(case):
     # The selection's paths, each exact against the oracle:
