@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kQThreads) void seq_quantile_kernel(QuantArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Rows of at most 2 304 positions: one wave per (sequence, pair) holding the
+// Rows of at most 3 072 positions: one wave per (sequence, pair) holding the
 // row's keys in registers (kJ chunks of four positions per lane), so the row
 // is read once and no step waits for another wave.
 //  1. A histogram of 4 096 buckets: the key 0; the keys whose top 16 bits
@@ -688,6 +688,23 @@ __global__ __launch_bounds__(64) void seq_quantile_wave_elem_kernel(QuantArgs a)
   seq_quantile_wave<false, kJ>(a);
 }
 
+// Rows of 2 305 to 3 072 positions: 12 chunks of keys per lane, with no
+// register cap (the keys alone take 96 VGPRs; 129 in all, 3 waves per SIMD).
+// With 16 chunks (rows up to 4 096) the wave form ran slower than the
+// workgroup kernel at 2 waves per SIMD, so longer rows take that kernel.
+template <bool kVec, int kJ>
+__global__ __launch_bounds__(64) void seq_quantile_wave_long_kernel(QuantArgs a) {
+  seq_quantile_wave<kVec, kJ>(a);
+}
+
+template <int kJ>
+void launch_wave_long(const QuantArgs& a, unsigned blocks, hipStream_t stream) {
+  if (a.vec && (a.L & 3) == 0)
+    hipLaunchKernelGGL((seq_quantile_wave_long_kernel<true, kJ>), dim3(blocks), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((seq_quantile_wave_long_kernel<false, kJ>), dim3(blocks), dim3(64), 0, stream, a);
+}
+
 // A 16-byte buffer load that reaches past the resource's end returns zeros
 // as a whole (not per dword), so rows take the vector loads only when every
 // group of four positions lies inside the row.
@@ -706,6 +723,7 @@ hipError_t launch_seq_quantiles(const QuantArgs& a, hipStream_t stream) {
   if (a.L <= 256 * 3) launch_wave<3>(a, blocks, stream);
   else if (a.L <= 256 * 6) launch_wave<6>(a, blocks, stream);
   else if (a.L <= 256 * kWMaxJ) launch_wave<kWMaxJ>(a, blocks, stream);
+  else if (a.L <= 256 * 12) launch_wave_long<12>(a, blocks, stream);
   else if (a.vec)
     hipLaunchKernelGGL(seq_quantile_kernel<true>, dim3(blocks), dim3(kQThreads), 0, stream, a);
   else

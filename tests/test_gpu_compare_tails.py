@@ -166,11 +166,11 @@ def quantile_rows(kind, N, L, seed):
     return A, B, C, M
 
 
-@pytest.mark.parametrize("L", [1, 300, 768, 769, 1536, 1537, 2304, 2305])
+@pytest.mark.parametrize("L", [1, 300, 768, 769, 1536, 1537, 2304, 2305, 3072, 3073, 4096, 4097])
 @pytest.mark.parametrize("kind", ["noise", "offset", "zeros", "ulp", "tiny", "equal", "mixed"])
 def test_seq_quantiles_every_row_length_and_kind(L, kind):
-    # Row lengths on both sides of each register-held key count (4, 8 or 12
-    # chunks of 256 positions; longer rows take the workgroup kernel), every
+    # Row lengths on both sides of each register-held key count (3, 6, 9 or
+    # 12 chunks of 256 positions; longer rows take the workgroup kernel), every
     # kind of difference, rows with 16-byte vector loads and with element
     # loads (a stride that is not a multiple of 4): all exact.
     N = 12
